@@ -1,0 +1,148 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) chunked Gated DeltaNet forward.
+ *
+ * The method. Per batch row b and value head h, with a dk x dv state S:
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t
+ * (Gated DeltaNet linear attention: one small recurrent state per head, named in
+ * hyper-parallel PR #1035 "linear attention cp", section "What does this PR do").
+ * It is evaluated in chunks of 64 tokens; issue #320 of the same project (the
+ * test report for PR #1114, section 3.1) fixes chunk size 64 and head dim 128
+ * for the fused backend. This library accepts chunk == 64 and
+ * dk, dv in {16, 32, 64, 128}; the bf16 matrix-core path serves dk == 128.
+ *
+ * The segment calls follow the same PR's p2p and all_gather modes: each
+ * segment of a sequence is summarised by the affine map H_out = M @ H_in + S,
+ * the summaries are combined in order into each segment's incoming state, and
+ * the segment's token outputs are then computed from its prepared chunk
+ * intermediates. Here the segments are pieces of one sequence on one GPU.
+ *
+ * Conventions shared by every call:
+ *   - Layouts are row-major and contiguous:
+ *       q, k    [B, T, Hqk, dk]   io dtype
+ *       v, o    [B, T, H, dv]     io dtype
+ *       g, beta [B, T, H]         fp32 (g is the per-token log-decay, beta the
+ *                                  delta-rule step)
+ *       h0, hT  [B, H, dk, dv]    fp32
+ *       M       [B, H, P, dk, dk] fp32;   S, H_in [B, H, P, dk, dv] fp32
+ *   - Heads: H % Hqk == 0 and value head h reads query/key head h / (H / Hqk);
+ *     this is the grouped copy of 16 query/key heads to 32 value heads that
+ *     issue #320, section 4.1 describes, done as an index map instead of a copy.
+ *   - Every pointer is device memory owned by the caller (except `p` and `bytes`,
+ *     which are host pointers). The library allocates no memory and keeps no
+ *     state between calls; calls are reentrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *     the call returns after enqueueing. Results are visible after the caller
+ *     synchronises that stream.
+ *   - Inputs are read-only. Outputs are fully overwritten; the output of a
+ *     padded token is written as +0.0. hT may alias h0; no other aliasing.
+ *   - Padding (issue #320, section 5.2): token t of row b is valid when
+ *     t < valid_len[b] (clamped to [0, T]); invalid tokens are treated as
+ *     beta = 0, g = 0 with zero q, k, v, so they give zero output and leave the
+ *     state unchanged. T need not be a multiple of 64.
+ *   - Errors: arguments are checked before anything is launched; a failed check
+ *     returns a status and enqueues nothing. A failed launch returns GDN_EHIP.
+ *     Faults inside kernels surface at the caller's stream synchronisation.
+ *     No C++ exception crosses this interface. gdn_last_error() gives a
+ *     human-readable detail of the last failure on the calling thread.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_EINVAL = 1,        /* bad argument: null required pointer, negative size, H % Hqk != 0 */
+    GDN_EUNSUPPORTED = 2,  /* well-formed but not implemented: chunk != 64, head dim, dtype */
+    GDN_EWORKSPACE = 3,    /* workspace pointer null or smaller than the sizing call says */
+    GDN_EHIP = 4           /* the HIP runtime refused a launch or a query */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct gdn_problem {
+    int32_t B, T, H, Hqk, dk, dv;  /* sizes; B, T may be 0 */
+    int32_t chunk;                 /* must be 64 */
+    int32_t io_dtype;              /* gdn_dtype of q, k, v and o */
+    const int32_t* valid_len;      /* device int32[B] or NULL (all T tokens valid) */
+} gdn_problem;
+
+/* Text for a status code (static storage). */
+const char* gdn_status_string(gdn_status s);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* gdn_last_error(void);
+
+/*
+ * Workspace for gdn_chunk_fwd, in bytes, written to *bytes. The workspace holds
+ * the per-chunk intermediates (the triangular-solve factor, the masked intra-chunk
+ * q.k block and the chunk decay factors); its contents are undefined on entry.
+ */
+gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes);
+
+/*
+ * Full-sequence chunked forward: o (all tokens) and, when hT != NULL, the final
+ * state. h0 == NULL starts from the zero state (the stateless use of issue #320,
+ * section 4.1); otherwise h0 is the initial state (the stateful use).
+ * ws must be 256-byte aligned and at least gdn_chunk_fwd_workspace() bytes.
+ */
+gdn_status gdn_chunk_fwd(const gdn_problem* p,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* h0,
+                         void* o, float* hT,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace for the segment calls (gdn_segment_summary, then
+ * gdn_apply_initial_state on the same workspace). seg_len must be a positive
+ * multiple of 64 that divides T; P = T / seg_len segments.
+ */
+gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes);
+
+/*
+ * Per-segment affine summary (PR #1035, p2p mode: H_out = M @ H_in + S):
+ *   S[b,h,p] = the state reached over segment p from a zero state,
+ *   M[b,h,p] = the product of the segment's token transitions
+ *              exp(g_t)(I - beta_t k_t k_t^T), later tokens on the left.
+ * Either output may be NULL to skip it. Leaves in ws the chunk intermediates that
+ * gdn_apply_initial_state reuses. valid_len must be NULL (GDN_EUNSUPPORTED).
+ */
+gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len,
+                               const void* q, const void* k, const void* v,
+                               const float* g, const float* beta,
+                               float* M, float* S,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Prefix combine of the summaries in segment order (PR #1035, all_gather mode):
+ *   H_{-1} = h0 (zero if NULL);  H_in[p] = H_{p-1};  H_p = M_p H_{p-1} + S_p.
+ * hT (nullable) receives H_{P-1}. M_prefix (nullable) receives M_p ... M_0.
+ * All fp32; H_in and M_prefix use the [B,H,P,...] layouts above.
+ */
+gdn_status gdn_summary_combine(int32_t B, int32_t H, int32_t P, int32_t dk, int32_t dv,
+                               const float* M, const float* S, const float* h0,
+                               float* H_in, float* M_prefix, float* hT, void* stream);
+
+/*
+ * Token outputs of every segment from its incoming state H_in[b,h,p] (PR #1035,
+ * p2p mode: once the initial state arrives, the local outputs come from the
+ * prepared chunk intermediates). ws must be the workspace that
+ * gdn_segment_summary filled for the same problem, seg_len and inputs. hT
+ * (nullable) receives the state at the end of the last segment.
+ */
+gdn_status gdn_apply_initial_state(const gdn_problem* p, int32_t seg_len,
+                                   const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   const float* H_in, void* o, float* hT,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

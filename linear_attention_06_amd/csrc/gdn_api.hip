@@ -1,0 +1,305 @@
+// gdn_api.hip -- the C ABI declared in include/gdn.h: argument checks,
+// workspace sizing and kernel selection. Every check runs before anything is
+// enqueued; no exception leaves this file.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+gdn_status hip_fail(hipError_t e, const char* what) {
+    return fail(GDN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Chunk intermediates: one record per (b, h, chunk). Element size of the two
+// 64x64 matrices: 4 bytes (fp32 arithmetic path).
+struct Plan {
+    int64_t NT = 0, nch = 0;
+    size_t that_off = 0, pmat_off = 0, gates_off = 0, bytes = 0;
+};
+
+Plan make_plan(const gdn_problem& p) {
+    Plan pl;
+    pl.NT = (static_cast<int64_t>(p.T) + gdn::kChunk - 1) / gdn::kChunk;
+    pl.nch = static_cast<int64_t>(p.B) * p.H * pl.NT;
+    const size_t elt = sizeof(float);
+    const size_t mat = align256(static_cast<size_t>(pl.nch) * 64 * 64 * elt);
+    pl.that_off = 0;
+    pl.pmat_off = mat;
+    pl.gates_off = 2 * mat;
+    pl.bytes = 2 * mat + align256(static_cast<size_t>(pl.nch) * 128 * sizeof(float));
+    return pl;
+}
+
+gdn::Workspace carve(const Plan& pl, void* ws) {
+    char* base = static_cast<char*>(ws);
+    gdn::Workspace w;
+    w.that = base + pl.that_off;
+    w.pmat = base + pl.pmat_off;
+    w.gates = reinterpret_cast<float*>(base + pl.gates_off);
+    return w;
+}
+
+gdn_status check_problem(const gdn_problem* p) {
+    if (!p) return fail(GDN_EINVAL, "problem pointer is NULL");
+    if (p->B < 0 || p->T < 0) return fail(GDN_EINVAL, "B=%d and T=%d must be >= 0", p->B, p->T);
+    if (p->H <= 0 || p->Hqk <= 0) return fail(GDN_EINVAL, "H=%d and Hqk=%d must be > 0", p->H, p->Hqk);
+    if (p->H % p->Hqk) return fail(GDN_EINVAL, "H=%d is not a multiple of Hqk=%d", p->H, p->Hqk);
+    if (p->H > 65535) return fail(GDN_EUNSUPPORTED, "H=%d exceeds 65535", p->H);
+    if (p->chunk != gdn::kChunk) return fail(GDN_EUNSUPPORTED, "chunk=%d: only 64 is supported", p->chunk);
+    if (p->dk <= 0 || p->dv <= 0) return fail(GDN_EINVAL, "dk=%d and dv=%d must be > 0", p->dk, p->dv);
+    if (!head_dim_ok(p->dk) || !head_dim_ok(p->dv))
+        return fail(GDN_EUNSUPPORTED, "dk=%d, dv=%d: head dims must be 16, 32, 64 or 128", p->dk, p->dv);
+    if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16)
+        return fail(GDN_EUNSUPPORTED, "io_dtype=%d: only GDN_F32 and GDN_BF16", p->io_dtype);
+    return GDN_OK;
+}
+
+gdn_status check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
+    if (pl.bytes == 0) return GDN_OK;
+    if (!ws) return fail(GDN_EWORKSPACE, "workspace is NULL, %zu bytes needed", pl.bytes);
+    if (ws_bytes < pl.bytes)
+        return fail(GDN_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, pl.bytes);
+    if (reinterpret_cast<uintptr_t>(ws) % 256)
+        return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
+    return GDN_OK;
+}
+
+gdn_status check_segments(const gdn_problem& p, int32_t seg_len, int64_t* P) {
+    if (seg_len <= 0 || seg_len % gdn::kChunk)
+        return fail(GDN_EINVAL, "seg_len=%d must be a positive multiple of 64", seg_len);
+    if (p.T % seg_len) return fail(GDN_EINVAL, "seg_len=%d does not divide T=%d", seg_len, p.T);
+    if (p.valid_len) return fail(GDN_EUNSUPPORTED, "valid_len is not supported by the segment calls");
+    *P = p.T / seg_len;
+    if (static_cast<int64_t>(p.B) * *P > 65535)
+        return fail(GDN_EUNSUPPORTED, "B * P = %lld exceeds 65535", static_cast<long long>(p.B * *P));
+    return GDN_OK;
+}
+
+gdn_status run_prep(const gdn_problem& p, const Plan& pl, const void* q, const void* k,
+                    const float* g, const float* beta, const gdn::Workspace& w, hipStream_t s) {
+    if (pl.nch == 0) return GDN_OK;
+    gdn::PrepArgs a;
+    a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.NT = static_cast<int>(pl.NT);
+    a.q = q; a.k = k; a.g = g; a.beta = beta; a.valid_len = p.valid_len; a.ws = w;
+    hipError_t e = gdn::launch_prep_f32path(a, p.io_dtype == GDN_BF16, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "prepare kernel launch");
+}
+
+gdn::StateArgs state_args(const gdn_problem& p, const Plan& pl, const void* q, const void* k,
+                          const void* v, const gdn::Workspace& w) {
+    gdn::StateArgs a;
+    a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.ncols = p.dv;
+    a.NT = static_cast<int>(pl.NT);
+    a.P = 1; a.Lc = static_cast<int>(pl.NT);
+    a.q = q; a.k = k; a.v = v; a.valid_len = p.valid_len; a.ws = w;
+    a.init_mode = gdn::kInitZero; a.s_init = nullptr; a.s_init_per_segment = 0;
+    a.o = nullptr; a.s_out = nullptr; a.store_mode = gdn::kStoreNone;
+    return a;
+}
+
+gdn_status run_state(const gdn_problem& p, const gdn::StateArgs& a, hipStream_t s) {
+    if (p.B == 0 || a.P == 0) return GDN_OK;
+    hipError_t e = gdn::launch_state_f32path(a, p.io_dtype == GDN_BF16, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "state kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_EINVAL: return "GDN_EINVAL: invalid argument";
+        case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: unsupported shape, dtype or option";
+        case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace missing, misaligned or too small";
+        case GDN_EHIP: return "GDN_EHIP: HIP runtime error";
+    }
+    return "unknown gdn_status";
+}
+
+const char* gdn_last_error(void) { return g_last_error.c_str(); }
+
+gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    *bytes = make_plan(*p).bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* h0, void* o, float* hT,
+                         void* ws, size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !v || !g || !beta || !o))
+            return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+        const Plan pl = make_plan(*p);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (p->B == 0) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const gdn::Workspace w = carve(pl, ws);
+        st = run_prep(*p, pl, q, k, g, beta, w, s);
+        if (st != GDN_OK) return st;
+        gdn::StateArgs a = state_args(*p, pl, q, k, v, w);
+        a.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+        a.s_init = h0;
+        a.o = o;
+        a.s_out = hT;
+        a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+        return run_state(*p, a, s);
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    int64_t P = 0;
+    st = check_segments(*p, seg_len, &P);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    *bytes = make_plan(*p).bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, float* M, float* S,
+                               void* ws, size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        int64_t P = 0;
+        st = check_segments(*p, seg_len, &P);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !g || !beta || (S && !v)))
+            return fail(GDN_EINVAL, "q, k, g, beta (and v when S is wanted) must be non-NULL");
+        const Plan pl = make_plan(*p);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (!tokens) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const gdn::Workspace w = carve(pl, ws);
+        st = run_prep(*p, pl, q, k, g, beta, w, s);
+        if (st != GDN_OK) return st;
+        gdn::StateArgs a = state_args(*p, pl, q, k, v, w);
+        a.P = static_cast<int>(P);
+        a.Lc = seg_len / gdn::kChunk;
+        a.store_mode = gdn::kStoreEverySegment;
+        if (S) {
+            a.init_mode = gdn::kInitZero;
+            a.s_out = S;
+            st = run_state(*p, a, s);
+            if (st != GDN_OK) return st;
+        }
+        if (M) {
+            a.v = nullptr;
+            a.ncols = p->dk;
+            a.init_mode = gdn::kInitIdentity;
+            a.s_out = M;
+            st = run_state(*p, a, s);
+            if (st != GDN_OK) return st;
+        }
+        return GDN_OK;
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_summary_combine(int32_t B, int32_t H, int32_t P, int32_t dk, int32_t dv, const float* M,
+                               const float* S, const float* h0, float* H_in, float* M_prefix, float* hT,
+                               void* stream) {
+    try {
+        if (B < 0 || H < 0 || P < 0) return fail(GDN_EINVAL, "B, H and P must be >= 0");
+        if (!head_dim_ok(dk) || !head_dim_ok(dv))
+            return fail(GDN_EUNSUPPORTED, "dk=%d, dv=%d: head dims must be 16, 32, 64 or 128", dk, dv);
+        if (B > 65535 || H > 65535) return fail(GDN_EUNSUPPORTED, "B or H exceeds 65535");
+        const bool work = static_cast<int64_t>(B) * H > 0;
+        if (work && P > 0 && (!M || !S || !H_in))
+            return fail(GDN_EINVAL, "M, S and H_in must be non-NULL");
+        if (!work) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        gdn::ScanArgs a;
+        a.B = B; a.H = H; a.P = P; a.dk = dk; a.ncols = dv;
+        a.M = M; a.S = S;
+        a.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+        a.init = h0;
+        a.x_before = H_in; a.x_after = nullptr; a.x_final = hT;
+        hipError_t e = gdn::launch_scan(a, s);
+        if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+        if (M_prefix && P > 0) {
+            a.ncols = dk; a.S = nullptr;
+            a.init_mode = gdn::kInitIdentity; a.init = nullptr;
+            a.x_before = nullptr; a.x_after = M_prefix; a.x_final = nullptr;
+            e = gdn::launch_scan(a, s);
+            if (e != hipSuccess) return hip_fail(e, "prefix-product kernel launch");
+        }
+        return GDN_OK;
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_apply_initial_state(const gdn_problem* p, int32_t seg_len, const void* q, const void* k,
+                                   const void* v, const float* g, const float* beta, const float* H_in,
+                                   void* o, float* hT, void* ws, size_t ws_bytes, void* stream) {
+    try {
+        (void)g;
+        (void)beta;
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        int64_t P = 0;
+        st = check_segments(*p, seg_len, &P);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !v || !H_in || !o))
+            return fail(GDN_EINVAL, "q, k, v, H_in and o must be non-NULL");
+        const Plan pl = make_plan(*p);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (!tokens) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const gdn::Workspace w = carve(pl, ws);
+        gdn::StateArgs a = state_args(*p, pl, q, k, v, w);
+        a.P = static_cast<int>(P);
+        a.Lc = seg_len / gdn::kChunk;
+        a.init_mode = gdn::kInitLoad;
+        a.s_init = H_in;
+        a.s_init_per_segment = 1;
+        a.o = o;
+        a.s_out = hT;
+        a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+        return run_state(*p, a, s);
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+}  // extern "C"

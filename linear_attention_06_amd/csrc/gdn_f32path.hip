@@ -1,0 +1,339 @@
+// gdn_f32path.hip -- fp32-arithmetic kernels of the chunked Gated DeltaNet
+// forward for gfx950. They serve fp32 I/O (where the fp32 tolerance rules out
+// bf16 matrix cores) and head dims the matrix-core path does not cover. All
+// arithmetic is fp32 on the vector ALUs; q, k, v, o may be fp32 or bf16.
+//
+// Chunk algebra (chunk of C = 64 tokens, incoming state S, Gam = chunk-local
+// cumulative sum of g; see the method statement in include/gdn.h):
+//   A_ij  = beta_i exp(Gam_i - Gam_j) k_i.k_j  (i > j),  Tinv = (I + A)^{-1}
+//   U     = Tinv diag(beta) (V - diag(exp Gam) K S)        delta-rule errors
+//   O     = diag(exp Gam) Q S + P U,   P_ij = (q_i.k_j) exp(Gam_i - Gam_j), j <= i
+//   S'    = exp(Gam_C) S + (diag(exp(Gam_C - Gam)) K)^T U
+// This is the UT/WY chunk form of the Gated DeltaNet recurrence; the decay
+// factors used are all exp of non-positive numbers, so nothing overflows.
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+__device__ __forceinline__ float ld_io(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_io(const uint16_t* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+__device__ __forceinline__ void st_io(float* p, int64_t i, float x) { p[i] = x; }
+__device__ __forceinline__ void st_io(uint16_t* p, int64_t i, float x) {
+    p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));  // round to nearest even
+}
+
+__device__ __forceinline__ int64_t valid_tokens(const int32_t* vl, int b, int64_t T) {
+    if (!vl) return T;
+    int64_t n = vl[b];
+    return n < 0 ? 0 : (n > T ? T : n);
+}
+
+// One wave per (b, h, chunk): cumulative decay, A, the unit-lower-triangular
+// inverse by forward substitution, P and the decay factors.
+template <typename IO, int DK>
+__global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
+    constexpr int KP = DK + 1;
+    constexpr int KT = (64 * KP > 64 * 65) ? 64 * KP : 64 * 65;
+    __shared__ float kt_s[KT];          // K rows, later the inverse
+    __shared__ float a_s[64 * 65];
+    __shared__ float gam_s[64];
+
+    const int64_t ch = blockIdx.x;
+    const int n = static_cast<int>(ch % a.NT);
+    const int bh = static_cast<int>(ch / a.NT);
+    const int h = bh % a.H, b = bh / a.H;
+    const int hq = h / (a.H / a.Hqk);
+    const int i = threadIdx.x;
+    const int64_t t = static_cast<int64_t>(n) * kChunk + i;
+    const bool valid = t < valid_tokens(a.valid_len, b, a.T);
+    const IO* q = static_cast<const IO*>(a.q);
+    const IO* k = static_cast<const IO*>(a.k);
+
+    const int64_t gi_idx = (static_cast<int64_t>(b) * a.T + t) * a.H + h;
+    const float gi = valid ? a.g[gi_idx] : 0.f;
+    const float bi = valid ? a.beta[gi_idx] : 0.f;
+    float gam = gi;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(gam, off, 64);
+        if (i >= off) gam += y;
+    }
+    gam_s[i] = gam;
+    const int64_t row = ((static_cast<int64_t>(b) * a.T + t) * a.Hqk + hq) * DK;
+    float qreg[DK];
+#pragma unroll
+    for (int d = 0; d < DK; ++d) {
+        kt_s[i * KP + d] = valid ? ld_io(k, row + d) : 0.f;
+        qreg[d] = valid ? ld_io(q, row + d) : 0.f;
+    }
+    __syncthreads();
+
+    float* that = static_cast<float*>(a.ws.that) + ch * 4096;
+    float* pm = static_cast<float*>(a.ws.pmat) + ch * 4096;
+    for (int j = 0; j < 64; ++j) {
+        float av = 0.f, pv = 0.f;
+        if (j <= i) {
+            float kk = 0.f, qk = 0.f;
+#pragma unroll 8
+            for (int d = 0; d < DK; ++d) {
+                const float kj = kt_s[j * KP + d];
+                kk += kt_s[i * KP + d] * kj;
+                qk += qreg[d] * kj;
+            }
+            const float decay = expf(gam - gam_s[j]);
+            pv = decay * qk;
+            if (j < i) av = bi * decay * kk;
+        }
+        a_s[i * 65 + j] = av;
+        pm[i * 64 + j] = pv;
+    }
+    __syncthreads();
+
+    // Forward substitution, lane c owns column c of Tinv.
+    float* t_s = kt_s;
+    const int c = i;
+    for (int r = 0; r < 64; ++r) {
+        float acc = (r == c) ? 1.f : 0.f;
+        for (int j = 0; j < r; ++j) acc -= a_s[r * 65 + j] * t_s[j * 65 + c];
+        t_s[r * 65 + c] = acc;
+    }
+    for (int r = 0; r < 64; ++r) that[r * 64 + c] = t_s[r * 65 + c] * bi;
+    const float gam_c = __shfl(gam, 63, 64);
+    float* gates = a.ws.gates + ch * 128;
+    gates[i] = expf(gam);
+    gates[64 + i] = expf(gam_c - gam);
+}
+
+// One block of 256 threads per (b, h, segment, 16 state columns): the
+// sequential pass over the segment's chunks with the state tile in LDS.
+template <typename IO, int DK>
+__global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
+    constexpr int KP = DK + 1;
+    constexpr int BV = 16;
+    __shared__ float k_s[64 * KP];
+    __shared__ float s_s[DK * (BV + 1)];
+    __shared__ float x_s[64 * (BV + 1)];
+    __shared__ float u_s[64 * (BV + 1)];
+    __shared__ float g_s[128];
+
+    const int col0 = blockIdx.x * BV;
+    const int h = blockIdx.y;
+    const int b = blockIdx.z / a.P, seg = blockIdx.z % a.P;
+    const int hq = h / (a.H / a.Hqk);
+    const int tid = threadIdx.x;
+    const int64_t nvalid = valid_tokens(a.valid_len, b, a.T);
+    const int ncols = a.ncols;
+    const IO* q = static_cast<const IO*>(a.q);
+    const IO* k = static_cast<const IO*>(a.k);
+    const IO* v = static_cast<const IO*>(a.v);
+    IO* o = static_cast<IO*>(a.o);
+    const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    const int64_t tile = static_cast<int64_t>(DK) * ncols;
+
+    for (int e = tid; e < DK * BV; e += 256) {
+        const int i = e / BV, c = e % BV;
+        float s0 = 0.f;
+        if (a.init_mode == kInitLoad) {
+            const int64_t blk = a.s_init_per_segment ? bh * a.P + seg : bh;
+            s0 = a.s_init[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c];
+        } else if (a.init_mode == kInitIdentity) {
+            s0 = (i == col0 + c) ? 1.f : 0.f;
+        }
+        s_s[i * (BV + 1) + c] = s0;
+    }
+
+    const int r = tid / 4;             // token row within the chunk
+    const int c4 = (tid % 4) * 4;      // first of this thread's 4 columns
+    const int n0 = seg * a.Lc;
+    const int n1 = min(n0 + a.Lc, a.NT);
+    for (int n = n0; n < n1; ++n) {
+        const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+        const int64_t ch = bh * a.NT + n;
+        __syncthreads();
+        for (int e = tid; e < 64 * DK; e += 256) {
+            const int rr = e / DK, d = e % DK;
+            const int64_t tok = t0 + rr;
+            k_s[rr * KP + d] =
+                tok < nvalid ? ld_io(k, ((static_cast<int64_t>(b) * a.T + tok) * a.Hqk + hq) * DK + d)
+                             : 0.f;
+        }
+        if (tid < 128) g_s[tid] = a.ws.gates[ch * 128 + tid];
+        __syncthreads();
+
+        const int64_t tok = t0 + r;
+        const bool valid = tok < nvalid;
+        const int64_t qrow = ((static_cast<int64_t>(b) * a.T + tok) * a.Hqk + hq) * DK;
+        float ks[4] = {0.f, 0.f, 0.f, 0.f}, qs[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < DK; ++i) {
+            const float kv = k_s[r * KP + i];
+            const float qv = valid ? ld_io(q, qrow + i) : 0.f;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float sv = s_s[i * (BV + 1) + c4 + c];
+                ks[c] += kv * sv;
+                qs[c] += qv * sv;
+            }
+        }
+        const float eg = g_s[r];
+        const int64_t vrow = ((static_cast<int64_t>(b) * a.T + tok) * a.H + h) * ncols + col0 + c4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float vv = (v && valid) ? ld_io(v, vrow + c) : 0.f;
+            x_s[r * (BV + 1) + c4 + c] = vv - eg * ks[c];
+        }
+        __syncthreads();
+
+        const float* that = static_cast<const float*>(a.ws.that) + ch * 4096;
+        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s <= r; ++s) {
+            const float tv = that[r * 64 + s];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) u[c] += tv * x_s[s * (BV + 1) + c4 + c];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) u_s[r * (BV + 1) + c4 + c] = u[c];
+        __syncthreads();
+
+        if (o && tok < a.T) {
+            const float* pm = static_cast<const float*>(a.ws.pmat) + ch * 4096;
+            float ov[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ov[c] = eg * qs[c];
+            for (int s = 0; s <= r; ++s) {
+                const float pv = pm[r * 64 + s];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ov[c] += pv * u_s[s * (BV + 1) + c4 + c];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) st_io(o, vrow + c, valid ? ov[c] : 0.f);
+        }
+
+        const float egC = g_s[63];
+        for (int e = tid; e < DK * BV; e += 256) {
+            const int i = e / BV, c = e % BV;
+            float acc = egC * s_s[i * (BV + 1) + c];
+            for (int s = 0; s < 64; ++s) acc += g_s[64 + s] * k_s[s * KP + i] * u_s[s * (BV + 1) + c];
+            s_s[i * (BV + 1) + c] = acc;
+        }
+    }
+    __syncthreads();
+
+    if (a.store_mode == kStoreNone) return;
+    if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
+    const int64_t blk = (a.store_mode == kStoreEverySegment) ? bh * a.P + seg : bh;
+    for (int e = tid; e < DK * BV; e += 256) {
+        const int i = e / BV, c = e % BV;
+        a.s_out[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = s_s[i * (BV + 1) + c];
+    }
+}
+
+// X_p = M_p X_{p-1} + S_p over the segments of one (b, h), 16 columns per block.
+__global__ __launch_bounds__(256) void affine_scan(ScanArgs a) {
+    constexpr int BV = 16;
+    extern __shared__ float x_s[];       // [dk][BV]
+    const int col0 = blockIdx.x * BV;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int dk = a.dk, ncols = a.ncols;
+    const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    const int64_t tile = static_cast<int64_t>(dk) * ncols;
+    const int tid = threadIdx.x;
+
+    for (int e = tid; e < dk * BV; e += 256) {
+        const int i = e / BV, c = e % BV;
+        float x0 = 0.f;
+        if (a.init_mode == kInitLoad) x0 = a.init[bh * tile + static_cast<int64_t>(i) * ncols + col0 + c];
+        else if (a.init_mode == kInitIdentity) x0 = (i == col0 + c) ? 1.f : 0.f;
+        x_s[e] = x0;
+    }
+    __syncthreads();
+    float acc[8];
+    const int per = (dk * BV + 255) / 256;   // outputs per thread (<= 8)
+    for (int p = 0; p < a.P; ++p) {
+        const int64_t blk = bh * a.P + p;
+        const float* M = a.M + blk * static_cast<int64_t>(dk) * dk;
+        for (int m = 0; m < per; ++m) {
+            const int e = tid + m * 256;
+            acc[m] = 0.f;
+            if (e < dk * BV) {
+                const int i = e / BV, c = e % BV;
+                if (a.x_before) a.x_before[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = x_s[e];
+                float s = a.S ? a.S[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] : 0.f;
+                float dot = 0.f;
+                for (int l = 0; l < dk; ++l) dot += M[static_cast<int64_t>(i) * dk + l] * x_s[l * BV + c];
+                acc[m] = dot + s;
+            }
+        }
+        __syncthreads();
+        for (int m = 0; m < per; ++m) {
+            const int e = tid + m * 256;
+            if (e < dk * BV) {
+                x_s[e] = acc[m];
+                if (a.x_after) {
+                    const int i = e / BV, c = e % BV;
+                    a.x_after[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = acc[m];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (a.x_final) {
+        for (int e = tid; e < dk * BV; e += 256) {
+            const int i = e / BV, c = e % BV;
+            a.x_final[bh * tile + static_cast<int64_t>(i) * ncols + col0 + c] = x_s[e];
+        }
+    }
+}
+
+template <typename IO>
+hipError_t prep_dispatch(const PrepArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.NT));
+    void* args[] = {const_cast<PrepArgs*>(&a)};
+    const void* fn = nullptr;
+    switch (a.dk) {
+        case 16: fn = reinterpret_cast<const void*>(&prep_f32path<IO, 16>); break;
+        case 32: fn = reinterpret_cast<const void*>(&prep_f32path<IO, 32>); break;
+        case 64: fn = reinterpret_cast<const void*>(&prep_f32path<IO, 64>); break;
+        case 128: fn = reinterpret_cast<const void*>(&prep_f32path<IO, 128>); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, grid, dim3(64), args, 0, s);
+}
+
+template <typename IO>
+hipError_t state_dispatch(const StateArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H),
+                    static_cast<unsigned>(a.B * a.P));
+    void* args[] = {const_cast<StateArgs*>(&a)};
+    const void* fn = nullptr;
+    switch (a.dk) {
+        case 16: fn = reinterpret_cast<const void*>(&state_f32path<IO, 16>); break;
+        case 32: fn = reinterpret_cast<const void*>(&state_f32path<IO, 32>); break;
+        case 64: fn = reinterpret_cast<const void*>(&state_f32path<IO, 64>); break;
+        case 128: fn = reinterpret_cast<const void*>(&state_f32path<IO, 128>); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_prep_f32path(const PrepArgs& a, bool io_bf16, hipStream_t s) {
+    return io_bf16 ? prep_dispatch<uint16_t>(a, s) : prep_dispatch<float>(a, s);
+}
+
+hipError_t launch_state_f32path(const StateArgs& a, bool io_bf16, hipStream_t s) {
+    return io_bf16 ? state_dispatch<uint16_t>(a, s) : state_dispatch<float>(a, s);
+}
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H),
+                    static_cast<unsigned>(a.B));
+    void* args[] = {const_cast<ScanArgs*>(&a)};
+    const size_t lds = static_cast<size_t>(a.dk) * 16 * sizeof(float);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&affine_scan), grid, dim3(256), args, lds, s);
+}
+
+}  // namespace gdn

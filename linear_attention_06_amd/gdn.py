@@ -1,0 +1,218 @@
+"""Thin ctypes binding of ``libgdn.so`` (the C ABI in ``include/gdn.h``).
+
+Argument marshalling only: torch tensors are checked for device, dtype and
+contiguity, turned into device pointers, and passed with the current HIP
+stream. Every step of the computation runs in the HIP kernels; there is no
+other implementation behind these functions, and they raise if the library
+is missing. Importing this module does not load the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = range(5)
+GDN_F32, GDN_BF16 = 0, 1
+CHUNK = 64
+
+# The functions include/gdn.h declares.
+EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd",
+           "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
+           "gdn_apply_initial_state")
+
+
+class GdnProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("Hqk", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("valid_len", ctypes.c_void_p)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (where, _status_text(status), detail))
+
+
+_lib = None
+
+
+def lib():
+    """Load libgdn.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdn.so is not built: run `python -m linear_attention_06_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        pp = ctypes.POINTER(GdnProblem)
+        L.gdn_status_string.argtypes = [ctypes.c_int]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error.argtypes = []
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_chunk_fwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
+        L.gdn_segment_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
+        L.gdn_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd",
+                     "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _status_text(status: int) -> str:
+    return lib().gdn_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != GDN_OK:
+        raise GdnError(status, where, lib().gdn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def problem(q: torch.Tensor, v: torch.Tensor, valid_len: Optional[torch.Tensor] = None,
+            chunk: int = CHUNK) -> GdnProblem:
+    """Problem sizes from q [B,T,Hqk,dk] and v [B,T,H,dv]."""
+    B, T, Hqk, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
+    io = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}.get(q.dtype, -1)
+    vl = None
+    if valid_len is not None:
+        _dev(valid_len, "valid_len", torch.int32)
+        vl = valid_len.data_ptr()
+    return GdnProblem(B, T, H, Hqk, dk, dv, chunk, io, vl)
+
+
+def gdn_chunk_fwd_workspace(p: GdnProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(n)), "gdn_chunk_fwd_workspace")
+    return n.value
+
+
+def gdn_segment_workspace(p: GdnProblem, seg_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_segment_workspace(ctypes.byref(p), seg_len, ctypes.byref(n)),
+           "gdn_segment_workspace")
+    return n.value
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _io_checks(q, k, v, g, beta):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype)
+    _dev(g, "g", torch.float32)
+    _dev(beta, "beta", torch.float32)
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, h0=None, valid_len=None, o=None, hT=None, want_state=True,
+                  ws=None, stream=None):
+    """Chunked forward. Returns (o, hT or None); allocates what is not given."""
+    _io_checks(q, k, v, g, beta)
+    _dev(h0, "h0", torch.float32)
+    p = problem(q, v, valid_len)
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    _dev(o, "o", v.dtype)
+    if hT is None and want_state:
+        hT = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=v.device)
+    _dev(hT, "hT", torch.float32)
+    need = gdn_chunk_fwd_workspace(p)
+    if ws is None:
+        ws = workspace(need, v.device)
+    _check(lib().gdn_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                               _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_chunk_fwd")
+    return o, hT
+
+
+def gdn_segment_summary(q, k, v, g, beta, seg_len, M=None, S=None, want_m=True, want_s=True,
+                        ws=None, stream=None):
+    """Per-segment (M, S). Returns (M, S, ws); ws is needed by gdn_apply_initial_state."""
+    _io_checks(q, k, v, g, beta)
+    p = problem(q, v)
+    P = p.T // seg_len if seg_len > 0 else 0
+    dev = v.device
+    if M is None and want_m:
+        M = torch.empty((p.B, p.H, P, p.dk, p.dk), dtype=torch.float32, device=dev)
+    if S is None and want_s:
+        S = torch.empty((p.B, p.H, P, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _dev(M, "M", torch.float32)
+    _dev(S, "S", torch.float32)
+    need = gdn_segment_workspace(p, seg_len)
+    if ws is None:
+        ws = workspace(need, dev)
+    _check(lib().gdn_segment_summary(ctypes.byref(p), seg_len, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _ptr(beta), _ptr(M), _ptr(S), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "gdn_segment_summary")
+    return M, S, ws
+
+
+def gdn_summary_combine(M, S, h0=None, H_in=None, want_prefix=False, M_prefix=None, hT=None,
+                        want_state=True, stream=None):
+    """Prefix combine. Returns (H_in, M_prefix or None, hT or None)."""
+    for t, n in ((M, "M"), (S, "S"), (h0, "h0")):
+        _dev(t, n, torch.float32)
+    B, H, P, dk, dv = S.shape
+    if H_in is None:
+        H_in = torch.empty_like(S)
+    if M_prefix is None and want_prefix:
+        M_prefix = torch.empty_like(M)
+    if hT is None and want_state:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=S.device)
+    for t, n in ((H_in, "H_in"), (M_prefix, "M_prefix"), (hT, "hT")):
+        _dev(t, n, torch.float32)
+    _check(lib().gdn_summary_combine(B, H, P, dk, dv, _ptr(M), _ptr(S), _ptr(h0), _ptr(H_in),
+                                     _ptr(M_prefix), _ptr(hT), _stream(stream)),
+           "gdn_summary_combine")
+    return H_in, M_prefix, hT
+
+
+def gdn_apply_initial_state(q, k, v, g, beta, H_in, seg_len, ws, o=None, hT=None, want_state=True,
+                            stream=None):
+    """Segment outputs from their incoming states. Returns (o, hT or None)."""
+    _io_checks(q, k, v, g, beta)
+    _dev(H_in, "H_in", torch.float32)
+    p = problem(q, v)
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    if hT is None and want_state:
+        hT = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=v.device)
+    _dev(o, "o", v.dtype)
+    _dev(hT, "hT", torch.float32)
+    _check(lib().gdn_apply_initial_state(ctypes.byref(p), seg_len, _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(g), _ptr(beta), _ptr(H_in), _ptr(o), _ptr(hT),
+                                         _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_apply_initial_state")
+    return o, hT

@@ -1,0 +1,61 @@
+"""Helpers for the GPU parity tests: seeded inputs to device tensors, cached
+oracle results, and the tolerances."""
+import functools
+import json
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from linear_attention_06_amd.inputs import WORKLOADS, make_inputs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+with open(os.path.join(HERE, "golden", "page_constants.json")) as _f:
+    PAGE = json.load(_f)
+
+# bf16 inputs with fp32 state: the pages' acceptance bound on relative L2.
+TOL_BF16 = PAGE["rel_l2_bound_bf16"]["value"]
+# fp32 inputs: the arithmetic is fp32 throughout; 1e-4 leaves about two orders
+# of magnitude over the rounding of 64-term fp32 dot products chained over chunks.
+TOL_F32 = 1e-4
+
+
+def dev():
+    if not torch.cuda.is_available():
+        raise RuntimeError("the GPU tests need a GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(inp):
+    """Device tensors (q, k, v, g, beta, h0, valid_len) from an Inputs record."""
+    d = dev()
+
+    def io(x):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        if inp.w.io == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(d)
+
+    f = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(d)
+    return io(inp.q), io(inp.k), io(inp.v), f(inp.g), f(inp.beta), f(inp.h0), f(inp.valid_len)
+
+
+def np_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+@functools.lru_cache(maxsize=4)
+def workload_inputs(name, T=None, B=None):
+    return make_inputs(WORKLOADS[name], T=T, B=B)
+
+
+@functools.lru_cache(maxsize=4)
+def oracle_fwd(name, T=None, B=None):
+    inp = workload_inputs(name, T, B)
+    q, k, v, g, beta, h0 = inp.f64()
+    return oracle.gdn_fwd(q, k, v, g, beta, h0, valid_len=inp.valid_len)
+
+
+def sync():
+    torch.cuda.synchronize()

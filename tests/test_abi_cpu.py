@@ -1,0 +1,137 @@
+"""The C-ABI library without a GPU: it loads, exports what include/gdn.h
+declares, sizes workspaces, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from linear_attention_06_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert set(declared_functions()) == set(gdn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = gdn.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+def test_header_compiles_as_c():
+    src = '#include "gdn.h"\nint main(void){ return (int)sizeof(gdn_problem); }\n'
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                          "-x", "c", "-", "-fsyntax-only"], input=src, text=True, capture_output=True)
+    assert res.returncode == 0, res.stderr
+
+
+def P(**kw):
+    base = dict(B=1, T=128, H=8, Hqk=4, dk=16, dv=16, chunk=64, io_dtype=gdn.GDN_F32, valid_len=None)
+    base.update(kw)
+    return gdn.GdnProblem(**base)
+
+
+def ws_status(p):
+    n = ctypes.c_size_t(0)
+    return gdn.lib().gdn_chunk_fwd_workspace(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+def test_status_strings():
+    for s in range(5):
+        assert gdn.lib().gdn_status_string(s).decode().startswith("GDN_")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk=32), gdn.GDN_EUNSUPPORTED),
+    (dict(dk=48), gdn.GDN_EUNSUPPORTED),
+    (dict(dv=256), gdn.GDN_EUNSUPPORTED),
+    (dict(io_dtype=7), gdn.GDN_EUNSUPPORTED),
+    (dict(H=6, Hqk=4), gdn.GDN_EINVAL),
+    (dict(Hqk=0), gdn.GDN_EINVAL),
+    (dict(B=-1), gdn.GDN_EINVAL),
+    (dict(T=-5), gdn.GDN_EINVAL),
+    (dict(dk=0), gdn.GDN_EINVAL),
+])
+def test_bad_problems_are_rejected(kw, status):
+    st, _ = ws_status(P(**kw))
+    assert st == status
+    assert gdn.lib().gdn_last_error().decode()
+
+
+def test_workspace_sizes():
+    st, n = ws_status(P())
+    assert st == gdn.GDN_OK
+    nch = 1 * 8 * 2
+    assert n >= nch * (2 * 64 * 64 * 2 + 128 * 4)
+    st, n0 = ws_status(P(T=0))
+    assert st == gdn.GDN_OK and n0 == 0
+
+
+def call_fwd(p, q=1, k=1, v=1, g=1, b=1, h0=None, o=1, hT=None, ws=None, nbytes=0):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return gdn.lib().gdn_chunk_fwd(ctypes.byref(p) if p is not None else None, vp(q), vp(k), vp(v),
+                                   vp(g), vp(b), vp(h0), vp(o), vp(hT), vp(ws), nbytes, None)
+
+
+def test_fwd_argument_checks_return_before_launch():
+    p = P()
+    _, need = ws_status(p)
+    assert call_fwd(None) == gdn.GDN_EINVAL
+    assert call_fwd(p, q=None, ws=256, nbytes=need) == gdn.GDN_EINVAL
+    assert call_fwd(p, o=None, ws=256, nbytes=need) == gdn.GDN_EINVAL
+    assert call_fwd(p, ws=None, nbytes=0) == gdn.GDN_EWORKSPACE
+    assert call_fwd(p, ws=256, nbytes=need - 1) == gdn.GDN_EWORKSPACE
+    assert call_fwd(p, ws=258, nbytes=need) == gdn.GDN_EWORKSPACE       # misaligned
+    assert call_fwd(P(chunk=128), ws=256, nbytes=need) == gdn.GDN_EUNSUPPORTED
+
+
+def test_segment_argument_checks():
+    L = gdn.lib()
+    n = ctypes.c_size_t(0)
+    assert L.gdn_segment_workspace(ctypes.byref(P()), 48, ctypes.byref(n)) == gdn.GDN_EINVAL
+    assert L.gdn_segment_workspace(ctypes.byref(P(T=192)), 128, ctypes.byref(n)) == gdn.GDN_EINVAL
+    assert L.gdn_segment_workspace(ctypes.byref(P()), 0, ctypes.byref(n)) == gdn.GDN_EINVAL
+    assert L.gdn_segment_workspace(ctypes.byref(P()), 64, ctypes.byref(n)) == gdn.GDN_OK
+    p = P(valid_len=1234)
+    assert L.gdn_segment_workspace(ctypes.byref(p), 64, ctypes.byref(n)) == gdn.GDN_EUNSUPPORTED
+    vp = ctypes.c_void_p
+    st = L.gdn_segment_summary(ctypes.byref(P()), 64, None, vp(1), vp(1), vp(1), vp(1), vp(1), vp(1),
+                               vp(256), 1 << 30, None)
+    assert st == gdn.GDN_EINVAL
+    st = L.gdn_apply_initial_state(ctypes.byref(P()), 64, vp(1), vp(1), vp(1), vp(1), vp(1), None,
+                                   vp(1), None, vp(256), 1 << 30, None)
+    assert st == gdn.GDN_EINVAL
+
+
+def test_combine_argument_checks():
+    L = gdn.lib()
+    vp = ctypes.c_void_p
+    assert L.gdn_summary_combine(1, 2, 3, 24, 16, vp(1), vp(1), None, vp(1), None, None, None) == \
+        gdn.GDN_EUNSUPPORTED
+    assert L.gdn_summary_combine(1, 2, 3, 16, 16, None, vp(1), None, vp(1), None, None, None) == \
+        gdn.GDN_EINVAL
+    assert L.gdn_summary_combine(-1, 2, 3, 16, 16, vp(1), vp(1), None, vp(1), None, None, None) == \
+        gdn.GDN_EINVAL
+    # nothing to do: no launch, OK
+    assert L.gdn_summary_combine(0, 2, 3, 16, 16, None, None, None, None, None, None, None) == gdn.GDN_OK
+
+
+def test_importing_the_package_does_not_load_the_library():
+    code = ("import linear_attention_06_amd, linear_attention_06_amd.gdn as g, "
+            "linear_attention_06_amd.inputs; print(g._lib is None)")
+    out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "True"
