@@ -1,0 +1,207 @@
+"""Benchmark of the chunked Gated DeltaNet forward on one MI355X.
+
+One step = one gdn_chunk_fwd call (chunk prepare + sequential state pass with
+outputs) over the stateful 32K-token workload: B = 1, T = 32768, 16 query/key
+heads read by 32 value heads, dk = dv = 128, bf16 q/k/v/o, fp32 g, beta and
+state, h0 ~ 0.1 N(0,1). Inputs are seeded synthetic tensors resident in HBM
+before timing starts.
+
+Prints one JSON line with the throughput, the roofline of the dominant kernel
+(its average duration measured with HIP events on the stream it runs on) and
+the fp64 CPU oracle timed on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd tokens/s at H=32,d=128,T=32K bf16; MFMA util % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+WORKLOAD = "stateful_32k"
+
+
+def algorithmic_bytes(B, T, H, Hqk, dk, dv, io_bytes=2, stateful=True):
+    """Bytes the method must move: q, k (Hqk heads), v, g, beta read once, o written
+    once, h0 read and hT written once."""
+    qk = 2 * B * T * Hqk * dk * io_bytes
+    vo = 2 * B * T * H * dv * io_bytes
+    gb = 2 * B * T * H * 4
+    st = (2 if stateful else 0) * B * H * dk * dv * 4
+    return qk + vo + gb + st
+
+
+def flops_per_token_head(C=64, d=128):
+    """Triangle-aware chunk-form flops per token and head: A and P (lower
+    triangles, 2 x C d), That X and P U (lower triangles, 2 x C d), K S, Q S and
+    K^T V'' (3 x 2 d^2), ignoring the O(C^2) solve."""
+    return 5 * C * d + 6 * d * d
+
+
+def cpu_baseline(inp, budget_s=30.0):
+    """The fp64 oracle on the host cores: whole heads of the same workload, as
+    many as fit the time budget (measured on one head first)."""
+    import oracle
+
+    q, k, v, g, beta, h0 = inp.f64()
+    w = inp.w
+    rep = w.H // w.Hqk
+    t0 = time.perf_counter()
+    oracle.gdn_fwd(q[:, :, :1], k[:, :, :1], v[:, :, :rep], g[:, :, :rep], beta[:, :, :rep],
+                   None if h0 is None else h0[:, :rep])
+    one = time.perf_counter() - t0   # rep heads on up to rep threads
+    threads = oracle.num_threads()
+    heads = w.H
+    est = one * (heads / rep) / max(1, min(threads, heads) / rep)
+    if est > budget_s:
+        heads = max(rep, int(w.H * budget_s / est) // rep * rep)
+    hq = heads // rep
+    t0 = time.perf_counter()
+    oracle.gdn_fwd(q[:, :, :hq], k[:, :, :hq], v[:, :, :heads], g[:, :, :heads], beta[:, :, :heads],
+                   None if h0 is None else h0[:, :heads])
+    dt = time.perf_counter() - t0
+    tokens_per_s = w.B * w.T * (heads / w.H) / dt
+    used = min(threads, w.B * heads)   # the oracle runs one (row, head) unit per thread
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": "%d of %d heads x %d tokens (B=%d), fp64 token loop, %.1f s"
+                      % (heads, w.H, w.T, w.B, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_06_amd import gdn
+    from linear_attention_06_amd.inputs import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+
+    w = WORKLOADS[WORKLOAD]
+    inp = make_inputs(w)
+
+    def io(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.int16).view(torch.bfloat16).to(dev)
+
+    q, k, v = io(inp.q), io(inp.k), io(inp.v)
+    g = torch.from_numpy(inp.g).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    h0 = torch.from_numpy(inp.h0).to(dev)
+    p = gdn.problem(q, v)
+    path = gdn.gdn_kernel_path(p)
+    o = torch.empty_like(v)
+    hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
+
+    def step():
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, o=o, hT=hT, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel durations. The prepare kernel alone: the segment summary with a
+    # single segment and no outputs runs only the prepare pass into the workspace.
+    # The state pass alone: gdn_apply_initial_state on that workspace.
+    H_in = h0.reshape(w.B, w.H, 1, w.dk, w.dv).contiguous()
+    seg_ws = gdn.workspace(gdn.gdn_segment_workspace(p, w.T), dev)
+
+    def prep_only():
+        gdn.gdn_segment_summary(q, k, v, g, beta, w.T, want_m=False, want_s=False, ws=seg_ws,
+                                stream=stream)
+
+    def state_only():
+        gdn.gdn_apply_initial_state(q, k, v, g, beta, H_in, w.T, seg_ws, o=o, hT=hT, stream=stream)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    prep_ms = timed(prep_only, args.steps)
+    state_ms = timed(state_only, args.steps)
+    dominant, dom_ms = ("state", state_ms) if state_ms >= prep_ms else ("prepare", prep_ms)
+
+    tokens = w.B * w.T
+    value = tokens / (ms * 1e-3)
+    alg_bytes = algorithmic_bytes(w.B, w.T, w.H, w.Hqk, w.dk, w.dv)
+    flops = flops_per_token_head(64, w.dk) * tokens * w.H
+    achieved_gbs = alg_bytes / (dom_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if path == "bf16-mfma" else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": w.B, "T": w.T, "H": w.H, "Hqk": w.Hqk, "dk": w.dk,
+                   "dv": w.dv, "chunk": 64, "h0": "0.1*N(0,1)", "kernel_path": path},
+        "mfma_util_pct": 100.0 * flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "algorithmic_gbs_per_step": alg_bytes / (ms * 1e-3) / 1e9,
+        "kernels_ms": {"prepare": prep_ms, "state": state_ms},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": None},
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -79,6 +79,14 @@ const char* gdn_status_string(gdn_status s);
 const char* gdn_last_error(void);
 
 /*
+ * Kernel path a problem runs on (static string), or NULL for an invalid problem:
+ *   "bf16-mfma" -- bf16 I/O with dk == 128 (and dv % 32 == 0): bf16 matrix-core
+ *                  contractions with fp32 accumulation and an fp32 state;
+ *   "f32-valu"  -- every other problem: fp32 arithmetic on the vector ALUs.
+ */
+const char* gdn_kernel_path(const gdn_problem* p);
+
+/*
  * Workspace for gdn_chunk_fwd, in bytes, written to *bytes. The workspace holds
  * the per-chunk intermediates (the triangular-solve factor, the masked intra-chunk
  * q.k block and the chunk decay factors); its contents are undefined on entry.

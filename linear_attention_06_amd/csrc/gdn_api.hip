@@ -31,23 +31,36 @@ bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Kernel path: bf16 I/O with dk == 128 runs on the bf16 matrix cores; every
+// other problem runs on the fp32 vector-ALU kernels.
+bool use_mfma(const gdn_problem& p) { return p.io_dtype == GDN_BF16 && p.dk == 128 && p.dv % 32 == 0; }
+
 // Chunk intermediates: one record per (b, h, chunk). Element size of the two
-// 64x64 matrices: 4 bytes (fp32 arithmetic path).
+// 64x64 matrices: 2 bytes (bf16) on the matrix-core path, 4 bytes otherwise.
+// The segment calls on the matrix-core path also keep the bf16 remainder of
+// That (used by the summary-matrix pass).
 struct Plan {
     int64_t NT = 0, nch = 0;
-    size_t that_off = 0, pmat_off = 0, gates_off = 0, bytes = 0;
+    size_t that_off = 0, pmat_off = 0, gates_off = 0, that_lo_off = 0, bytes = 0;
+    bool lo = false;
 };
 
-Plan make_plan(const gdn_problem& p) {
+Plan make_plan(const gdn_problem& p, bool segments) {
     Plan pl;
     pl.NT = (static_cast<int64_t>(p.T) + gdn::kChunk - 1) / gdn::kChunk;
     pl.nch = static_cast<int64_t>(p.B) * p.H * pl.NT;
-    const size_t elt = sizeof(float);
+    const bool mfma = use_mfma(p);
+    const size_t elt = mfma ? 2 : sizeof(float);
     const size_t mat = align256(static_cast<size_t>(pl.nch) * 64 * 64 * elt);
     pl.that_off = 0;
     pl.pmat_off = mat;
     pl.gates_off = 2 * mat;
     pl.bytes = 2 * mat + align256(static_cast<size_t>(pl.nch) * 128 * sizeof(float));
+    pl.lo = mfma && segments;
+    if (pl.lo) {
+        pl.that_lo_off = pl.bytes;
+        pl.bytes += mat;
+    }
     return pl;
 }
 
@@ -57,6 +70,7 @@ gdn::Workspace carve(const Plan& pl, void* ws) {
     w.that = base + pl.that_off;
     w.pmat = base + pl.pmat_off;
     w.gates = reinterpret_cast<float*>(base + pl.gates_off);
+    w.that_lo = pl.lo ? base + pl.that_lo_off : nullptr;
     return w;
 }
 
@@ -72,6 +86,13 @@ gdn_status check_problem(const gdn_problem* p) {
         return fail(GDN_EUNSUPPORTED, "dk=%d, dv=%d: head dims must be 16, 32, 64 or 128", p->dk, p->dv);
     if (p->io_dtype != GDN_F32 && p->io_dtype != GDN_BF16)
         return fail(GDN_EUNSUPPORTED, "io_dtype=%d: only GDN_F32 and GDN_BF16", p->io_dtype);
+    if (use_mfma(*p)) {
+        // the matrix-core kernels address one batch row of q, k, v, o with 32-bit byte offsets
+        const int64_t row_qk = static_cast<int64_t>(p->T + gdn::kChunk) * p->Hqk * p->dk * 2;
+        const int64_t row_vo = static_cast<int64_t>(p->T + gdn::kChunk) * p->H * p->dv * 2;
+        if (row_qk >= (int64_t(1) << 31) || row_vo >= (int64_t(1) << 31))
+            return fail(GDN_EUNSUPPORTED, "one batch row of q/k or v/o exceeds 2 GiB on the bf16 path");
+    }
     return GDN_OK;
 }
 
@@ -102,7 +123,8 @@ gdn_status run_prep(const gdn_problem& p, const Plan& pl, const void* q, const v
     gdn::PrepArgs a;
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.NT = static_cast<int>(pl.NT);
     a.q = q; a.k = k; a.g = g; a.beta = beta; a.valid_len = p.valid_len; a.ws = w;
-    hipError_t e = gdn::launch_prep_f32path(a, p.io_dtype == GDN_BF16, s);
+    hipError_t e = use_mfma(p) ? gdn::launch_prep_mfma(a, s)
+                               : gdn::launch_prep_f32path(a, p.io_dtype == GDN_BF16, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "prepare kernel launch");
 }
 
@@ -120,7 +142,8 @@ gdn::StateArgs state_args(const gdn_problem& p, const Plan& pl, const void* q, c
 
 gdn_status run_state(const gdn_problem& p, const gdn::StateArgs& a, hipStream_t s) {
     if (p.B == 0 || a.P == 0) return GDN_OK;
-    hipError_t e = gdn::launch_state_f32path(a, p.io_dtype == GDN_BF16, s);
+    hipError_t e = use_mfma(p) ? gdn::launch_state_mfma(a, s)
+                               : gdn::launch_state_f32path(a, p.io_dtype == GDN_BF16, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "state kernel launch");
 }
 
@@ -141,11 +164,16 @@ const char* gdn_status_string(gdn_status s) {
 
 const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
+const char* gdn_kernel_path(const gdn_problem* p) {
+    if (check_problem(p) != GDN_OK) return nullptr;
+    return use_mfma(*p) ? "bf16-mfma" : "f32-valu";
+}
+
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
-    *bytes = make_plan(*p).bytes;
+    *bytes = make_plan(*p, false).bytes;
     return GDN_OK;
 }
 
@@ -158,7 +186,7 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !o))
             return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
-        const Plan pl = make_plan(*p);
+        const Plan pl = make_plan(*p, false);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
         if (p->B == 0) return GDN_OK;
@@ -185,7 +213,7 @@ gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* 
     st = check_segments(*p, seg_len, &P);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
-    *bytes = make_plan(*p).bytes;
+    *bytes = make_plan(*p, true).bytes;
     return GDN_OK;
 }
 
@@ -201,7 +229,7 @@ gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !g || !beta || (S && !v)))
             return fail(GDN_EINVAL, "q, k, g, beta (and v when S is wanted) must be non-NULL");
-        const Plan pl = make_plan(*p);
+        const Plan pl = make_plan(*p, true);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
         if (!tokens) return GDN_OK;
@@ -281,7 +309,7 @@ gdn_status gdn_apply_initial_state(const gdn_problem* p, int32_t seg_len, const 
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !H_in || !o))
             return fail(GDN_EINVAL, "q, k, v, H_in and o must be non-NULL");
-        const Plan pl = make_plan(*p);
+        const Plan pl = make_plan(*p, true);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
         if (!tokens) return GDN_OK;

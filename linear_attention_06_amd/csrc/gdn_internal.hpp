@@ -27,6 +27,7 @@ struct Workspace {
     void* that;
     void* pmat;
     float* gates;
+    void* that_lo;   // matrix-core path, segment calls only: bf16 remainder That - bf16(That), or NULL
 };
 
 struct PrepArgs {
@@ -71,5 +72,7 @@ struct ScanArgs {
 hipError_t launch_prep_f32path(const PrepArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_state_f32path(const StateArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s);
+hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s);
 
 }  // namespace gdn

@@ -22,7 +22,8 @@ GDN_F32, GDN_BF16 = 0, 1
 CHUNK = 64
 
 # The functions include/gdn.h declares.
-EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd",
+EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
+           "gdn_chunk_fwd",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
            "gdn_apply_initial_state")
 
@@ -56,6 +57,8 @@ def lib():
         L.gdn_status_string.restype = ctypes.c_char_p
         L.gdn_last_error.argtypes = []
         L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_kernel_path.argtypes = [pp]
+        L.gdn_kernel_path.restype = ctypes.c_char_p
         L.gdn_chunk_fwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
         L.gdn_segment_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
         L.gdn_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -110,6 +113,14 @@ def problem(q: torch.Tensor, v: torch.Tensor, valid_len: Optional[torch.Tensor] 
         _dev(valid_len, "valid_len", torch.int32)
         vl = valid_len.data_ptr()
     return GdnProblem(B, T, H, Hqk, dk, dv, chunk, io, vl)
+
+
+def gdn_kernel_path(p: GdnProblem) -> str:
+    """Name of the kernel path the library runs for this problem."""
+    r = lib().gdn_kernel_path(ctypes.byref(p))
+    if r is None:
+        raise GdnError(GDN_EINVAL, "gdn_kernel_path", lib().gdn_last_error().decode())
+    return r.decode()
 
 
 def gdn_chunk_fwd_workspace(p: GdnProblem) -> int:

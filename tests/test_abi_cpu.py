@@ -135,3 +135,13 @@ def test_importing_the_package_does_not_load_the_library():
             "linear_attention_06_amd.inputs; print(g._lib is None)")
     out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
     assert out.stdout.strip() == "True"
+
+
+def test_kernel_path_selection():
+    path = lambda **kw: gdn.gdn_kernel_path(P(**kw))
+    assert path(io_dtype=gdn.GDN_BF16, dk=128, dv=128) == "bf16-mfma"
+    assert path(io_dtype=gdn.GDN_BF16, dk=128, dv=64) == "bf16-mfma"
+    assert path(io_dtype=gdn.GDN_BF16, dk=64, dv=64) == "f32-valu"
+    assert path(io_dtype=gdn.GDN_F32, dk=128, dv=128) == "f32-valu"
+    with pytest.raises(gdn.GdnError):
+        path(chunk=32)

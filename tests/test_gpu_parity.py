@@ -52,6 +52,12 @@ def test_stateless_8k_matches_oracle():
     assert_close(np_f64(o), o_ref, TOL_BF16, "stateless_8k o")
 
 
+def test_bf16_head_dim_128_uses_the_matrix_core_path():
+    inp = workload_inputs("stateful_32k")
+    q, k, v, g, beta, h0, _ = to_dev(inp)
+    assert gdn.gdn_kernel_path(gdn.problem(q, v)) == "bf16-mfma"
+
+
 def test_stateful_32k_matches_oracle():
     inp = workload_inputs("stateful_32k")
     o_ref, hT_ref = oracle_fwd("stateful_32k")
