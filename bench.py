@@ -14,6 +14,7 @@ the fp64 CPU oracle timed on this host.
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -46,6 +47,26 @@ def flops_per_token_head(C=64, d=128):
     triangles, 2 x C d), That X and P U (lower triangles, 2 x C d), K S, Q S and
     K^T V'' (3 x 2 d^2), ignoring the O(C^2) solve."""
     return 5 * C * d + 6 * d * d
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gdn_state_and_prepare_stateful_32k_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "linear_attention_06_amd", "csrc", "gdn_mfma.hip")
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when that summary was taken on a different version of the kernel source."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("machine-readable:"):
+            kv = dict(item.split("=", 1) for item in line.split()[1:])
+            if kv.get("kernel") == kernel and kv.get("source_sha256_prefix") == sha:
+                return int(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def cpu_baseline(inp, budget_s=30.0):
@@ -195,7 +216,9 @@ def main():
         "kernels_ms": {"prepare": prep_ms, "state": state_ms},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": None},
+                     "traffic": recorded_traffic(dominant), "traffic_unit": "bytes/launch",
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "kernel_ms": dom_ms},
         "wall_s_timed_region": wall,
     }
     if not args.no_cpu_baseline:

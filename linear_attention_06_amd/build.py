@@ -34,9 +34,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Per-source flags. The matrix-core kernels keep MFMA accumulators in ordinary
+# VGPRs: their results feed VALU code every chunk, and accumulation registers
+# would cost a copy each way.
+SOURCE_FLAGS = {"gdn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, extra: list) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIP_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))

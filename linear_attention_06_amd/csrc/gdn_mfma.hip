@@ -304,6 +304,11 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
 //   stage 2: waves 0,1: U rows 32w.. = That X
 //   stage 3: every wave: S rows 32w.. <- exp(Gam_C) S + K^T V'', V'' = diag(exp(Gam_C - Gam)) U
 //            waves 2,3: O rows = diag(exp Gam) Q S + P U
+// Tiles in LDS are unpadded and XOR-swizzled per 16-byte granule so that the
+// staging writes, the MFMA fragment reads and the transposing reads of K (which
+// give the K^T fragments of the state update without a transposed copy) are all
+// free of bank conflicts. The operands exchanged between waves (S, X, U, V'')
+// go through LDS in MFMA B-fragment order.
 // q, k, v are read through buffer descriptors whose range ends at the row's
 // last valid token, so padded and out-of-range tokens read as zero without any
 // per-element test; o is written through a descriptor that ends at T.
@@ -319,6 +324,9 @@ struct Stage {
     uint32_t v[4];
 };
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
 __device__ __forceinline__ void split8(const f32x16& v, int i0, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -326,6 +334,49 @@ __device__ __forceinline__ void split8(const f32x16& v, int i0, bf16x8& hi, bf16
         hi[u] = h;
         lo[u] = static_cast<__bf16>(v[i0 + u] - static_cast<float>(h));
     }
+}
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+    return bf16_bits(a) | (static_cast<uint32_t>(bf16_bits(b)) << 16);
+}
+
+// 128-wide bf16 tile (K, Q): granule g (8 elements) of row r sits at g ^ swz_k(r).
+__device__ __forceinline__ int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int off_k(int r, int g) { return r * 128 + 8 * (g ^ swz_k(r)); }
+// 64-wide bf16 tile (That, P): granule g of row r sits at g ^ swz_c(r).
+__device__ __forceinline__ int swz_c(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int off_c(int r, int g) { return r * 64 + 8 * (g ^ swz_c(r)); }
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
+// i/4, 4 + i/4, 8 + i/4, 12 + i/4 of its group.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+    lds_bf16x4* lp = (lds_bf16x4*)(const_cast<uint16_t*>(p));   // generic to LDS address space
+#pragma clang diagnostic pop
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
+}
+
+// Writes registers i0 .. i0+7 of a 32x32 C tile (rows 16h + {4q..4q+3, 8+4q..8+4q+3},
+// h = i0 / 8, column r) into the B-fragment slots of k-step ks (rows in order).
+__device__ __forceinline__ void put_frag(bf16x8* buf, int ks, int lane, u32x2 first, u32x2 second) {
+    uint16_t* slot = reinterpret_cast<uint16_t*>(buf + ks * 64 + (lane & 31));
+    const int e = 4 * (lane >> 5);
+    *reinterpret_cast<u32x2*>(slot + e) = first;
+    *reinterpret_cast<u32x2*>(slot + 32 * 8 + e) = second;
+}
+__device__ __forceinline__ void put_tile(bf16x8* buf, int ks0, int lane, const f32x16& v) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+        put_frag(buf, ks0 + hh, lane, u32x2{pk2(v[8 * hh], v[8 * hh + 1]), pk2(v[8 * hh + 2], v[8 * hh + 3])},
+                 u32x2{pk2(v[8 * hh + 4], v[8 * hh + 5]), pk2(v[8 * hh + 6], v[8 * hh + 7])});
+}
+__device__ __forceinline__ void put_tile_split(bf16x8* hi, bf16x8* lo, int ks0, int lane, const f32x16& v) {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = v[i] - bf16_to_f32(bf16_bits(v[i]));
+    put_tile(hi, ks0, lane, v);
+    put_tile(lo, ks0, lane, r);
 }
 
 constexpr int kBufferFlags = 0x00020000;   // raw buffer descriptor word 3 on gfx9-family GPUs
@@ -348,17 +399,16 @@ template <bool kHasV, bool kSplit, bool kOut>
 __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int groups) {
     constexpr int NL = kSplit ? 1 : 0;   // extra lo buffers only in split mode
     constexpr bool outputs = kHasV && kOut;
-    __shared__ __align__(16) uint16_t k_s[64 * KP];
-    __shared__ __align__(16) uint16_t q_s[outputs ? 64 * KP : 8];
-    __shared__ __align__(16) uint16_t kt_s[DK * CP];
-    __shared__ __align__(16) uint16_t th_s[64 * CP];
-    __shared__ __align__(16) uint16_t tl_s[kSplit ? 64 * CP : 8];
-    __shared__ __align__(16) uint16_t p_s[outputs ? 64 * CP : 8];
+    __shared__ __align__(16) uint16_t k_s[64 * DK];
+    __shared__ __align__(16) uint16_t q_s[outputs ? 64 * DK : 8];
+    __shared__ __align__(16) uint16_t th_s[64 * 64];
+    __shared__ __align__(16) uint16_t tl_s[kSplit ? 64 * 64 : 8];
+    __shared__ __align__(16) uint16_t p_s[outputs ? 64 * 64 : 8];
     __shared__ __align__(16) uint16_t vt_s[kHasV ? 32 * CP : 8];    // V^T: [column][token]
     __shared__ __align__(16) uint16_t ot_s[outputs ? 32 * CP : 8];  // O^T: [column][token]
     __shared__ __align__(16) float g_s[128];
     __shared__ __align__(16) bf16x8 sbuf[(1 + NL) * 8 * 64];
-    __shared__ __align__(16) bf16x8 xbuf[(1 + NL) * 2 * 64];
+    __shared__ __align__(16) bf16x8 xbuf[(1 + NL) * 4 * 64];
     __shared__ __align__(16) bf16x8 ubuf[outputs ? 4 * 64 : 1];
     __shared__ __align__(16) bf16x8 vbuf[(1 + NL) * 4 * 64];
 
@@ -405,29 +455,19 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
         }
     }
     auto put_state = [&]() {
-        if constexpr (kSplit) {
-            bf16x8 hi, lo;
-            split8(S, 0, hi, lo);
-            sbuf[(2 * wave) * 64 + lane] = hi;
-            sbuf[512 + (2 * wave) * 64 + lane] = lo;
-            split8(S, 8, hi, lo);
-            sbuf[(2 * wave + 1) * 64 + lane] = hi;
-            sbuf[512 + (2 * wave + 1) * 64 + lane] = lo;
-        } else {
-            sbuf[(2 * wave) * 64 + lane] = pack8(S, 0);
-            sbuf[(2 * wave + 1) * 64 + lane] = pack8(S, 8);
-        }
+        if constexpr (kSplit) put_tile_split(sbuf, sbuf + 512, 2 * wave, lane, S);
+        else put_tile(sbuf, 2 * wave, lane, S);
     };
     put_state();
 
-    // staging maps. K/Q: 4 rows x 8 cols per thread. That/P: 2 pieces of 8 cols.
-    // V (and O on the way out): rows 4*(tid/16) .. +3, columns 2*(tid%16) .. +1.
-    const int kb = tid >> 1, krb = kb >> 4, kcb = kb & 15, khf = tid & 1;
+    // staging maps. K/Q: granule p&15 of row p>>4 (p = tid + 256u). That/P: granule p&7
+    // of row p>>3. V (and O on the way out): rows 4*(tid/16) .. +3, columns 2*(tid%16) .. +1.
     const int vrow0 = 4 * (tid >> 4), vcol = 2 * (tid & 15);
     uint32_t koff[4], voff[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        koff[r] = static_cast<uint32_t>(((8 * krb + 4 * khf + r) * qk_row + hq * DK + 8 * kcb) * 2);
+        const int p = tid + 256 * r;
+        koff[r] = static_cast<uint32_t>(((p >> 4) * qk_row + hq * DK + 8 * (p & 15)) * 2);
         voff[r] = static_cast<uint32_t>(((vrow0 + r) * vo_row + h * ncols + col0 + vcol) * 2);
     }
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
@@ -446,38 +486,28 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
             if (outputs) st.q[r] = buf_load16(rq, koff[r] + kc);
             if (kHasV) st.v[r] = buf_load4(rv, voff[r] + vc);
         }
-        const uint16_t* th = th_bh + n * 4096;
-        const uint16_t* pm = pm_bh + n * 4096;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            st.th[u] = *reinterpret_cast<const u32x4*>(th + 8 * (2 * tid + u));
-            if (outputs) st.pm[u] = *reinterpret_cast<const u32x4*>(pm + 8 * (2 * tid + u));
-            if constexpr (kSplit) st.tl[u] = *reinterpret_cast<const u32x4*>(tl_bh + n * 4096 + 8 * (2 * tid + u));
+            const int e = 8 * (tid + 256 * u);
+            st.th[u] = *reinterpret_cast<const u32x4*>(th_bh + n * 4096 + e);
+            if (outputs) st.pm[u] = *reinterpret_cast<const u32x4*>(pm_bh + n * 4096 + e);
+            if constexpr (kSplit) st.tl[u] = *reinterpret_cast<const u32x4*>(tl_bh + n * 4096 + e);
         }
         st.gate = *reinterpret_cast<const u32x4*>(gt_bh + n * 128 + 4 * (tid & 31));
     };
     auto store_stage = [&](const Stage<kSplit>& st) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 8 * krb + 4 * khf + r;
-            store8_perm(k_s + row * KP, 16 * (kcb >> 1), kcb & 1, st.k[r]);
-            if (outputs) store8_perm(q_s + row * KP, 16 * (kcb >> 1), kcb & 1, st.q[r]);
-        }
-        // K^T: feature 8*kcb + e, tokens 8*krb + 4*khf + 0..3 (token index permuted)
-        const int tpos = 16 * (krb >> 1) + 8 * khf + 4 * (krb & 1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int sh = (e & 1) * 16;
-            const uint32_t r0 = (st.k[0][e >> 1] >> sh) & 0xFFFFu, r1 = (st.k[1][e >> 1] >> sh) & 0xFFFFu;
-            const uint32_t r2 = (st.k[2][e >> 1] >> sh) & 0xFFFFu, r3 = (st.k[3][e >> 1] >> sh) & 0xFFFFu;
-            *reinterpret_cast<u32x2*>(kt_s + (8 * kcb + e) * CP + tpos) = u32x2{r0 | (r1 << 16), r2 | (r3 << 16)};
+            const int p = tid + 256 * r;
+            *reinterpret_cast<u32x4*>(k_s + off_k(p >> 4, p & 15)) = st.k[r];
+            if (outputs) *reinterpret_cast<u32x4*>(q_s + off_k(p >> 4, p & 15)) = st.q[r];
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int p = 2 * tid + u, row = p >> 3, cb = p & 7;
-            store8_perm(th_s + row * CP, 16 * (cb >> 1), cb & 1, st.th[u]);
-            if (outputs) store8_perm(p_s + row * CP, 16 * (cb >> 1), cb & 1, st.pm[u]);
-            if constexpr (kSplit) store8_perm(tl_s + row * CP, 16 * (cb >> 1), cb & 1, st.tl[u]);
+            const int p = tid + 256 * u;
+            *reinterpret_cast<u32x4*>(th_s + off_c(p >> 3, p & 7)) = st.th[u];
+            if (outputs) *reinterpret_cast<u32x4*>(p_s + off_c(p >> 3, p & 7)) = st.pm[u];
+            if constexpr (kSplit) *reinterpret_cast<u32x4*>(tl_s + off_c(p >> 3, p & 7)) = st.tl[u];
         }
         if (kHasV) {
             // V^T: columns vcol, vcol+1, tokens vrow0 .. vrow0+3
@@ -502,6 +532,16 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
 #pragma unroll
         for (int r = 0; r < 4; ++r) buf_store4(ro, voff[r] + vc, (t0 + r < nvalid) ? w[r] : 0u);
     };
+    // K^T fragment of k-step c for state rows 32*wave .. : features 32*wave + (lane % 32),
+    // tokens 16c + 8q .. +7, read from the natural K tile with two transposing reads.
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int kt_f = 32 * wave + 16 * (g16 & 1) + 4 * (s16 & 3);
+    auto kt_frag = [&](int c) {
+        const int row = 16 * c + 8 * (g16 >> 1) + (s16 >> 2);
+        const u32x2 lo = lds_read_tr(k_s + off_k(row, kt_f >> 3) + (kt_f & 7));
+        const u32x2 hi = lds_read_tr(k_s + off_k(row + 4, kt_f >> 3) + (kt_f & 7));
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
 
     Stage<kSplit> st;
     if (n0 < n1) load_stage(n0, st);
@@ -516,13 +556,12 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
 
         // ---- stage 1: K S (waves 0,1) or Q S (waves 2,3, only with outputs), rows 32m..32m+31
         f32x16 xs = zero16();   // waves 0,1: X;  waves 2,3: diag(exp Gam) Q S
-        bf16x8 xf0, xf1, xl0, xl1;
         if (wave < 2 || outputs) {
             const uint16_t* X = (wave < 2) ? k_s : q_s;
             f32x16 acc = zero16();
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const bf16x8 av = lds_frag(X + (32 * m + lr) * KP + 16 * c + 8 * q);
+                const bf16x8 av = lds_frag(X + off_k(32 * m + lr, 2 * c + q));
                 acc = mfma32(av, sbuf[c * 64 + lane], acc);
                 if constexpr (kSplit) acc = mfma32(av, sbuf[512 + c * 64 + lane], acc);
             }
@@ -542,20 +581,9 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
                 for (int j = 0; j < 4; ++j)
                     xs[4 * i4 + j] = (wave < 2) ? v4[j] - e4[j] * acc[4 * i4 + j] : e4[j] * acc[4 * i4 + j];
             }
-        }
-        if constexpr (kSplit) {
-            split8(xs, 0, xf0, xl0);
-            split8(xs, 8, xf1, xl1);
-        } else {
-            xf0 = pack8(xs, 0);
-            xf1 = pack8(xs, 8);
-        }
-        if (wave == 0) {
-            xbuf[lane] = xf0;
-            xbuf[64 + lane] = xf1;
-            if constexpr (kSplit) {
-                xbuf[128 + lane] = xl0;
-                xbuf[192 + lane] = xl1;
+            if (wave < 2) {
+                if constexpr (kSplit) put_tile_split(xbuf, xbuf + 256, 2 * m, lane, xs);
+                else put_tile(xbuf, 2 * m, lane, xs);
             }
         }
         lds_sync();
@@ -563,34 +591,16 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
         // ---- stage 2: U rows 32m.. = That X (waves 0,1)
         if (wave < 2) {
             f32x16 u = zero16();
-            const uint16_t* trow = th_s + (32 * m + lr) * CP + 8 * q;
-            const uint16_t* lrow = tl_s + (32 * m + lr) * CP + 8 * q;
-            auto tx = [&](int c, bf16x8 xh, bf16x8 xl) {
-                const bf16x8 th = lds_frag(trow + 16 * c);
-                u = mfma32(th, xh, u);
+            const int kst = 2 * m + 2;   // That is lower triangular: k-steps past the rows are zero
+            for (int c = 0; c < kst; ++c) {
+                const bf16x8 th = lds_frag(th_s + off_c(32 * m + lr, 2 * c + q));
+                u = mfma32(th, xbuf[c * 64 + lane], u);
                 if constexpr (kSplit) {
-                    u = mfma32(th, xl, u);
-                    u = mfma32(lds_frag(lrow + 16 * c), xh, u);
+                    u = mfma32(th, xbuf[256 + c * 64 + lane], u);
+                    u = mfma32(lds_frag(tl_s + off_c(32 * m + lr, 2 * c + q)), xbuf[c * 64 + lane], u);
                 }
-            };
-            if (wave == 0) {
-                tx(0, xf0, xl0);
-                tx(1, xf1, xl1);
-            } else {
-                if constexpr (kSplit) {
-                    tx(0, xbuf[lane], xbuf[128 + lane]);
-                    tx(1, xbuf[64 + lane], xbuf[192 + lane]);
-                } else {
-                    tx(0, xbuf[lane], xl0);
-                    tx(1, xbuf[64 + lane], xl1);
-                }
-                tx(2, xf0, xl0);
-                tx(3, xf1, xl1);
             }
-            if (outputs) {
-                ubuf[(2 * m) * 64 + lane] = pack8(u, 0);
-                ubuf[(2 * m + 1) * 64 + lane] = pack8(u, 8);
-            }
+            if (outputs) put_tile(ubuf, 2 * m, lane, u);
             f32x16 vv;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
@@ -598,18 +608,8 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
 #pragma unroll
                 for (int j = 0; j < 4; ++j) vv[4 * i4 + j] = e4[j] * u[4 * i4 + j];
             }
-            if constexpr (kSplit) {
-                bf16x8 hi, lo;
-                split8(vv, 0, hi, lo);
-                vbuf[(2 * m) * 64 + lane] = hi;
-                vbuf[256 + (2 * m) * 64 + lane] = lo;
-                split8(vv, 8, hi, lo);
-                vbuf[(2 * m + 1) * 64 + lane] = hi;
-                vbuf[256 + (2 * m + 1) * 64 + lane] = lo;
-            } else {
-                vbuf[(2 * m) * 64 + lane] = pack8(vv, 0);
-                vbuf[(2 * m + 1) * 64 + lane] = pack8(vv, 8);
-            }
+            if constexpr (kSplit) put_tile_split(vbuf, vbuf + 256, 2 * m, lane, vv);
+            else put_tile(vbuf, 2 * m, lane, vv);
         }
         lds_sync();
 
@@ -619,10 +619,9 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
             f32x16 sn;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sn[i] = egC * S[i];
-            const uint16_t* krow = kt_s + (32 * wave + lr) * CP + 8 * q;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bf16x8 kv = lds_frag(krow + 16 * c);
+                const bf16x8 kv = kt_frag(c);
                 sn = mfma32(kv, vbuf[c * 64 + lane], sn);
                 if constexpr (kSplit) sn = mfma32(kv, vbuf[256 + c * 64 + lane], sn);
             }
@@ -630,20 +629,14 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
         }
         if (outputs && wave >= 2) {
             f32x16 o = xs;
-            const uint16_t* prow = p_s + (32 * m + lr) * CP + 8 * q;
-            o = mfma32(lds_frag(prow), ubuf[lane], o);
-            o = mfma32(lds_frag(prow + 16), ubuf[64 + lane], o);
-            if (m == 1) {
-                o = mfma32(lds_frag(prow + 32), ubuf[128 + lane], o);
-                o = mfma32(lds_frag(prow + 48), ubuf[192 + lane], o);
-            }
+            const int kst = 2 * m + 2;
+            for (int c = 0; c < kst; ++c)
+                o = mfma32(lds_frag(p_s + off_c(32 * m + lr, 2 * c + q)), ubuf[c * 64 + lane], o);
             // O^T into LDS: column lr, 4 consecutive tokens per register group
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const uint32_t w0 = bf16_bits(o[4 * i4]) | (static_cast<uint32_t>(bf16_bits(o[4 * i4 + 1])) << 16);
-                const uint32_t w1 = bf16_bits(o[4 * i4 + 2]) | (static_cast<uint32_t>(bf16_bits(o[4 * i4 + 3])) << 16);
-                *reinterpret_cast<u32x2*>(ot_s + lr * CP + 32 * m + 8 * i4 + 4 * q) = u32x2{w0, w1};
-            }
+            for (int i4 = 0; i4 < 4; ++i4)
+                *reinterpret_cast<u32x2*>(ot_s + lr * CP + 32 * m + 8 * i4 + 4 * q) =
+                    u32x2{pk2(o[4 * i4], o[4 * i4 + 1]), pk2(o[4 * i4 + 2], o[4 * i4 + 3])};
         }
         put_state();
     }
