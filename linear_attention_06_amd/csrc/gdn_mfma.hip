@@ -76,6 +76,11 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+// Barrier for the state pass: LDS writes of this wave complete, then s_barrier.
+// Written as one asm statement with a memory clobber (so the compiler keeps LDS
+// accesses on their side of it) instead of a fence, because a fence would also wait
+// for the direct-to-LDS loads of the next chunk that are meant to stay in flight.
+__device__ __forceinline__ void stage_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Position of index x inside its 16-block after swapping bits 2 and 3.
 __device__ __forceinline__ int perm16(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
@@ -304,10 +309,13 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
 //   stage 2: waves 0,1: U rows 32w.. = That X
 //   stage 3: every wave: S rows 32w.. <- exp(Gam_C) S + K^T V'', V'' = diag(exp(Gam_C - Gam)) U
 //            waves 2,3: O rows = diag(exp Gam) Q S + P U
-// Tiles in LDS are unpadded and XOR-swizzled per 16-byte granule so that the
-// staging writes, the MFMA fragment reads and the transposing reads of K (which
-// give the K^T fragments of the state update without a transposed copy) are all
-// free of bank conflicts. The operands exchanged between waves (S, X, U, V'')
+// The chunk operands (K, Q, That, P, decay factors) are loaded straight from
+// global memory into LDS (buffer loads with the lds bit), one chunk ahead, into
+// one of two stage buffers. Tiles in LDS are unpadded and XOR-swizzled per
+// 16-byte granule -- each lane of a direct load picks the global granule that
+// belongs at its LDS slot -- so that the MFMA fragment reads and the transposing
+// reads of K (which give the K^T fragments of the state update without a
+// transposed copy) are free of bank conflicts. The operands exchanged between waves (S, X, U, V'')
 // go through LDS in MFMA B-fragment order.
 // q, k, v are read through buffer descriptors whose range ends at the row's
 // last valid token, so padded and out-of-range tokens read as zero without any
@@ -317,13 +325,6 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
 // V'' and That enter the MFMAs as bf16 hi + lo pairs (x = hi + lo, lo the bf16 of
 // the remainder), the products taken as hi*hi + hi*lo + lo*hi.
 // ----------------------------------------------------------------------------
-template <bool kSplit>
-struct Stage {
-    u32x4 k[4], q[4], th[2], pm[2], tl[kSplit ? 2 : 1];
-    u32x4 gate;
-    uint32_t v[4];
-};
-
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
@@ -395,18 +396,43 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t of
     __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
 }
 
+// Raw buffer descriptor (base, range in bytes) as four uniform words.
+__device__ __forceinline__ u32x4 make_desc(const void* base, int64_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    const uint32_t n = static_cast<uint32_t>(bytes < 0 ? 0 : bytes);
+    const auto rfl = [](uint32_t x) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(x)); };
+    return u32x4{rfl(static_cast<uint32_t>(p)), rfl(static_cast<uint32_t>(p >> 32) & 0xFFFFu), rfl(n),
+                 static_cast<uint32_t>(kBufferFlags)};
+}
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+#pragma clang diagnostic pop
+}
+// Direct global-to-LDS load of 16 bytes per lane: lane l writes LDS byte address
+// lds + 16 l (lds wave-uniform). Issued as asm so that the compiler does not make later
+// LDS reads of the other stage buffer wait for it; the chunk loop waits for these loads
+// explicitly (s_waitcnt vmcnt(0)).
+__device__ __forceinline__ void lds_dma16(const u32x4& desc, uint32_t lds, uint32_t off) {
+    const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(off), "s"(desc)
+                 : "memory", "m0");
+}
+
 template <bool kHasV, bool kSplit, bool kOut>
 __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int groups) {
     constexpr int NL = kSplit ? 1 : 0;   // extra lo buffers only in split mode
     constexpr bool outputs = kHasV && kOut;
-    __shared__ __align__(16) uint16_t k_s[64 * DK];
-    __shared__ __align__(16) uint16_t q_s[outputs ? 64 * DK : 8];
-    __shared__ __align__(16) uint16_t th_s[64 * 64];
-    __shared__ __align__(16) uint16_t tl_s[kSplit ? 64 * 64 : 8];
-    __shared__ __align__(16) uint16_t p_s[outputs ? 64 * 64 : 8];
-    __shared__ __align__(16) uint16_t vt_s[kHasV ? 32 * CP : 8];    // V^T: [column][token]
-    __shared__ __align__(16) uint16_t ot_s[outputs ? 32 * CP : 8];  // O^T: [column][token]
-    __shared__ __align__(16) float g_s[128];
+    // one stage buffer: K [64x128], Q [64x128] (outputs), That [64x64], P [64x64] (outputs),
+    // That remainder [64x64] (split), decay factors (1 KiB: 512 B used)
+    constexpr int KB = 64 * DK * 2, QB = outputs ? 64 * DK * 2 : 0, TB = 64 * 64 * 2;
+    constexpr int PB = outputs ? 64 * 64 * 2 : 0, LB = kSplit ? 64 * 64 * 2 : 0, GB = 1024;
+    constexpr int SB = KB + QB + TB + PB + LB + GB;
+    __shared__ __align__(16) unsigned char stage_s[2 * SB];
+    __shared__ __align__(16) uint16_t vt_s[kHasV ? 2 * 32 * CP : 8];  // V^T: [buffer][column][token]
+    __shared__ __align__(16) uint16_t ot_s[outputs ? 32 * CP : 8];    // O^T: [column][token]
     __shared__ __align__(16) bf16x8 sbuf[(1 + NL) * 8 * 64];
     __shared__ __align__(16) bf16x8 xbuf[(1 + NL) * 4 * 64];
     __shared__ __align__(16) bf16x8 ubuf[outputs ? 4 * 64 : 1];
@@ -423,23 +449,31 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
     const int b = bz / a.P, seg = bz % a.P;
     const int hq = h / (a.H / a.Hqk);
     const int col0 = 32 * tile;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 5, lr = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 5, lr = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int ncols = a.ncols;
     const int64_t nvalid = valid_tokens(a.valid_len, b, a.T);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     const int64_t stile = static_cast<int64_t>(DK) * ncols;
 
-    // descriptors over row b: q/k/v end at the last valid token, o at T
+    // descriptors over row b: q/k/v end at the last valid token, o at T; the
+    // workspace records of (b, h) as one descriptor
     const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK;       // elements per token
     const int64_t vo_row = static_cast<int64_t>(a.H) * ncols;
     const uint16_t* kin = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(b) * a.T * qk_row;
     const uint16_t* qin = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.T * qk_row;
     const uint16_t* vin = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(b) * a.T * vo_row;
     uint16_t* oout = static_cast<uint16_t*>(a.o) + static_cast<int64_t>(b) * a.T * vo_row;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin, nvalid * qk_row * 2);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(outputs ? qin : kin, nvalid * qk_row * 2);
+    const u32x4 rk = make_desc(kin, nvalid * qk_row * 2);
+    const u32x4 rq = make_desc(outputs ? qin : kin, nvalid * qk_row * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(outputs ? oout : kin, outputs ? static_cast<int64_t>(a.T) * vo_row * 2 : 0);
+    const int64_t rec = static_cast<int64_t>(a.NT) * 4096 * 2;        // bytes of one head's 64x64 records
+    const u32x4 rth = make_desc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * 4096, rec);
+    const u32x4 rpm = make_desc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * 4096, rec);
+    const u32x4 rtl =
+        make_desc(kSplit ? static_cast<const uint16_t*>(a.ws.that_lo) + bh * a.NT * 4096 : static_cast<const uint16_t*>(a.ws.that), rec);
+    const u32x4 rgt = make_desc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
 
     // state rows 32*wave .. 32*wave+31, columns col0 .. col0+31, fp32, C layout
     f32x16 S;
@@ -460,63 +494,62 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
     };
     put_state();
 
-    // staging maps. K/Q: granule p&15 of row p>>4 (p = tid + 256u). That/P: granule p&7
-    // of row p>>3. V (and O on the way out): rows 4*(tid/16) .. +3, columns 2*(tid%16) .. +1.
-    const int vrow0 = 4 * (tid >> 4), vcol = 2 * (tid & 15);
-    uint32_t koff[4], voff[4];
+    // Direct loads. Each 1 KiB block of a tile is written by one wave instruction,
+    // lane l at byte 16 l. For the 128-wide tiles block j holds rows 4j .. 4j+3; for the
+    // 64-wide tiles rows 8j .. 8j+7. Wave w loads blocks w, w+4, w+8, w+12 (K, Q) and
+    // w, w+4 (That, P, That remainder); wave 0 also the decay factors.
+    uint32_t koff[4], toff[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int p = tid + 256 * r;
-        koff[r] = static_cast<uint32_t>(((p >> 4) * qk_row + hq * DK + 8 * (p & 15)) * 2);
-        voff[r] = static_cast<uint32_t>(((vrow0 + r) * vo_row + h * ncols + col0 + vcol) * 2);
+    for (int u = 0; u < 4; ++u) {
+        const int row = 4 * (wave + 4 * u) + (lane >> 4), g = (lane & 15) ^ swz_k(row);
+        koff[u] = static_cast<uint32_t>((row * qk_row + hq * DK + 8 * g) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int row = 8 * (wave + 4 * u) + (lane >> 3), g = (lane & 7) ^ swz_c(row);
+        toff[u] = static_cast<uint32_t>((row * 64 + 8 * g) * 2);
     }
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
-    const int n0 = seg * a.Lc, n1 = min(n0 + a.Lc, a.NT);
-    const uint16_t* th_bh = static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * 4096;
-    const uint16_t* pm_bh = static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * 4096;
-    const uint16_t* tl_bh = kSplit ? static_cast<const uint16_t*>(a.ws.that_lo) + bh * a.NT * 4096 : nullptr;
-    const float* gt_bh = a.ws.gates + bh * a.NT * 128;
-
-    auto load_stage = [&](int n, Stage<kSplit>& st) {
-        const uint32_t kc = static_cast<uint32_t>(n) * kstep, vc = static_cast<uint32_t>(n) * vstep;
+    const uint32_t stage_base = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds_addr(stage_s)));
+    auto issue_stage = [&](int n) {
+        const uint32_t sb = stage_base + static_cast<uint32_t>((n & 1) * SB) + static_cast<uint32_t>(wave) * 1024u;
+        const uint32_t kc = static_cast<uint32_t>(n) * kstep, tc = static_cast<uint32_t>(n) * 8192u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            st.k[r] = buf_load16(rk, koff[r] + kc);
-            if (outputs) st.q[r] = buf_load16(rq, koff[r] + kc);
-            if (kHasV) st.v[r] = buf_load4(rv, voff[r] + vc);
+        for (int u = 0; u < 4; ++u) {
+            lds_dma16(rk, sb + u * 4096, koff[u] + kc);
+            if constexpr (outputs) lds_dma16(rq, sb + KB + u * 4096, koff[u] + kc);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int e = 8 * (tid + 256 * u);
-            st.th[u] = *reinterpret_cast<const u32x4*>(th_bh + n * 4096 + e);
-            if (outputs) st.pm[u] = *reinterpret_cast<const u32x4*>(pm_bh + n * 4096 + e);
-            if constexpr (kSplit) st.tl[u] = *reinterpret_cast<const u32x4*>(tl_bh + n * 4096 + e);
+            lds_dma16(rth, sb + KB + QB + u * 4096, toff[u] + tc);
+            if constexpr (outputs) lds_dma16(rpm, sb + KB + QB + TB + u * 4096, toff[u] + tc);
+            if constexpr (kSplit) lds_dma16(rtl, sb + KB + QB + TB + PB + u * 4096, toff[u] + tc);
         }
-        st.gate = *reinterpret_cast<const u32x4*>(gt_bh + n * 128 + 4 * (tid & 31));
+        if (wave == 0) lds_dma16(rgt, sb + SB - GB, static_cast<uint32_t>(n) * 512u + 16u * (lane & 31));
     };
-    auto store_stage = [&](const Stage<kSplit>& st) {
+    // V (columns vcol, vcol+1 of tokens vrow0 .. vrow0+3) goes through registers into V^T;
+    // O leaves the same way.
+    const int vrow0 = 4 * (tid >> 4), vcol = 2 * (tid & 15);
+    uint32_t voff[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int p = tid + 256 * r;
-            *reinterpret_cast<u32x4*>(k_s + off_k(p >> 4, p & 15)) = st.k[r];
-            if (outputs) *reinterpret_cast<u32x4*>(q_s + off_k(p >> 4, p & 15)) = st.q[r];
-        }
+    for (int r = 0; r < 4; ++r) voff[r] = static_cast<uint32_t>(((vrow0 + r) * vo_row + h * ncols + col0 + vcol) * 2);
+    uint32_t vreg[4] = {0u, 0u, 0u, 0u};
+    auto load_v = [&](int n) {
+        if constexpr (kHasV) {
+            const uint32_t vc = static_cast<uint32_t>(n) * vstep;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int p = tid + 256 * u;
-            *reinterpret_cast<u32x4*>(th_s + off_c(p >> 3, p & 7)) = st.th[u];
-            if (outputs) *reinterpret_cast<u32x4*>(p_s + off_c(p >> 3, p & 7)) = st.pm[u];
-            if constexpr (kSplit) *reinterpret_cast<u32x4*>(tl_s + off_c(p >> 3, p & 7)) = st.tl[u];
+            for (int r = 0; r < 4; ++r) vreg[r] = buf_load4(rv, voff[r] + vc);
         }
-        if (kHasV) {
-            // V^T: columns vcol, vcol+1, tokens vrow0 .. vrow0+3
-            const uint32_t lo0 = (st.v[0] & 0xFFFFu) | (st.v[1] << 16), lo1 = (st.v[2] & 0xFFFFu) | (st.v[3] << 16);
-            const uint32_t hi0 = (st.v[0] >> 16) | (st.v[1] & 0xFFFF0000u), hi1 = (st.v[2] >> 16) | (st.v[3] & 0xFFFF0000u);
-            *reinterpret_cast<u32x2*>(vt_s + vcol * CP + vrow0) = u32x2{lo0, lo1};
-            *reinterpret_cast<u32x2*>(vt_s + (vcol + 1) * CP + vrow0) = u32x2{hi0, hi1};
+    };
+    auto put_v = [&](int n) {
+        if constexpr (kHasV) {
+            uint16_t* vt = vt_s + (n & 1) * 32 * CP;
+            const uint32_t lo0 = (vreg[0] & 0xFFFFu) | (vreg[1] << 16), lo1 = (vreg[2] & 0xFFFFu) | (vreg[3] << 16);
+            const uint32_t hi0 = (vreg[0] >> 16) | (vreg[1] & 0xFFFF0000u), hi1 = (vreg[2] >> 16) | (vreg[3] & 0xFFFF0000u);
+            *reinterpret_cast<u32x2*>(vt + vcol * CP + vrow0) = u32x2{lo0, lo1};
+            *reinterpret_cast<u32x2*>(vt + (vcol + 1) * CP + vrow0) = u32x2{hi0, hi1};
         }
-        if (tid < 32) *reinterpret_cast<u32x4*>(g_s + 4 * tid) = st.gate;
     };
     // O^T of chunk n from LDS to o (rows past the valid length written as zero)
     auto flush_o = [&](int n) {
@@ -532,38 +565,51 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
 #pragma unroll
         for (int r = 0; r < 4; ++r) buf_store4(ro, voff[r] + vc, (t0 + r < nvalid) ? w[r] : 0u);
     };
-    // K^T fragment of k-step c for state rows 32*wave .. : features 32*wave + (lane % 32),
-    // tokens 16c + 8q .. +7, read from the natural K tile with two transposing reads.
+
+    const int n0 = seg * a.Lc, n1 = min(n0 + a.Lc, a.NT);
     const int g16 = lane >> 4, s16 = lane & 15;
     const int kt_f = 32 * wave + 16 * (g16 & 1) + 4 * (s16 & 3);
-    auto kt_frag = [&](int c) {
-        const int row = 16 * c + 8 * (g16 >> 1) + (s16 >> 2);
-        const u32x2 lo = lds_read_tr(k_s + off_k(row, kt_f >> 3) + (kt_f & 7));
-        const u32x2 hi = lds_read_tr(k_s + off_k(row + 4, kt_f >> 3) + (kt_f & 7));
-        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    };
-
-    Stage<kSplit> st;
-    if (n0 < n1) load_stage(n0, st);
+    if (n0 < n1) {
+        issue_stage(n0);
+        load_v(n0);
+    }
     for (int n = n0; n < n1; ++n) {
-        lds_sync();   // every LDS read of the previous chunk is done
+        const unsigned char* sb = stage_s + (n & 1) * SB;
+        const uint16_t* k_s = reinterpret_cast<const uint16_t*>(sb);
+        const uint16_t* q_s = reinterpret_cast<const uint16_t*>(sb + KB);
+        const uint16_t* th_s = reinterpret_cast<const uint16_t*>(sb + KB + QB);
+        const uint16_t* p_s = reinterpret_cast<const uint16_t*>(sb + KB + QB + TB);
+        const uint16_t* tl_s = reinterpret_cast<const uint16_t*>(sb + KB + QB + TB + PB);
+        const float* g_s = reinterpret_cast<const float*>(sb + SB - GB);
+        const uint16_t* vt = vt_s + (n & 1) * 32 * CP;
+
+        __builtin_amdgcn_s_waitcnt(0);   // this chunk's direct loads and V have landed
+        put_v(n);
+        lds_sync();                      // ... in every wave; the other stage buffer is free
         if (outputs && n > n0) flush_o(n - 1);
-        store_stage(st);
-        lds_sync();
-        // the last chunk reloads its own data: the loads stay unconditional
-        load_stage((n + 1 < n1) ? n + 1 : n, st);
+        {
+            // the last chunk reloads its own data: the loads stay unconditional
+            const int nn = (n + 1 < n1) ? n + 1 : n;
+            if (nn != n) issue_stage(nn);
+            load_v(nn);
+        }
         const int m = wave & 1;
 
         // ---- stage 1: K S (waves 0,1) or Q S (waves 2,3, only with outputs), rows 32m..32m+31
         f32x16 xs = zero16();   // waves 0,1: X;  waves 2,3: diag(exp Gam) Q S
         if (wave < 2 || outputs) {
             const uint16_t* X = (wave < 2) ? k_s : q_s;
-            f32x16 acc = zero16();
+            f32x16 acc0 = zero16(), acc1 = zero16();
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const bf16x8 av = lds_frag(X + off_k(32 * m + lr, 2 * c + q));
-                acc = mfma32(av, sbuf[c * 64 + lane], acc);
-                if constexpr (kSplit) acc = mfma32(av, sbuf[512 + c * 64 + lane], acc);
+            for (int c = 0; c < 8; c += 2) {
+                const bf16x8 a0 = lds_frag(X + off_k(32 * m + lr, 2 * c + q));
+                const bf16x8 a1 = lds_frag(X + off_k(32 * m + lr, 2 * c + 2 + q));
+                acc0 = mfma32(a0, sbuf[c * 64 + lane], acc0);
+                acc1 = mfma32(a1, sbuf[(c + 1) * 64 + lane], acc1);
+                if constexpr (kSplit) {
+                    acc0 = mfma32(a0, sbuf[512 + c * 64 + lane], acc0);
+                    acc1 = mfma32(a1, sbuf[512 + (c + 1) * 64 + lane], acc1);
+                }
             }
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
@@ -571,22 +617,24 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
                 const f32x4 e4 = *reinterpret_cast<const f32x4*>(g_s + row);
                 float v4[4] = {0.f, 0.f, 0.f, 0.f};
                 if (kHasV && wave < 2) {
-                    const u32x2 vv = *reinterpret_cast<const u32x2*>(vt_s + lr * CP + row);
+                    const u32x2 vv = *reinterpret_cast<const u32x2*>(vt + lr * CP + row);
                     v4[0] = __uint_as_float(vv[0] << 16);
                     v4[1] = __uint_as_float(vv[0] & 0xFFFF0000u);
                     v4[2] = __uint_as_float(vv[1] << 16);
                     v4[3] = __uint_as_float(vv[1] & 0xFFFF0000u);
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    xs[4 * i4 + j] = (wave < 2) ? v4[j] - e4[j] * acc[4 * i4 + j] : e4[j] * acc[4 * i4 + j];
+                for (int j = 0; j < 4; ++j) {
+                    const float ks = acc0[4 * i4 + j] + acc1[4 * i4 + j];
+                    xs[4 * i4 + j] = (wave < 2) ? v4[j] - e4[j] * ks : e4[j] * ks;
+                }
             }
             if (wave < 2) {
                 if constexpr (kSplit) put_tile_split(xbuf, xbuf + 256, 2 * m, lane, xs);
                 else put_tile(xbuf, 2 * m, lane, xs);
             }
         }
-        lds_sync();
+        stage_sync();
 
         // ---- stage 2: U rows 32m.. = That X (waves 0,1)
         if (wave < 2) {
@@ -611,21 +659,29 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
             if constexpr (kSplit) put_tile_split(vbuf, vbuf + 256, 2 * m, lane, vv);
             else put_tile(vbuf, 2 * m, lane, vv);
         }
-        lds_sync();
+        stage_sync();
 
         // ---- stage 3: state rows 32*wave.. and (waves 2,3) the outputs
         {
             const float egC = g_s[63];
-            f32x16 sn;
+            f32x16 s0, s1 = zero16();
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sn[i] = egC * S[i];
+            for (int i = 0; i < 16; ++i) s0[i] = egC * S[i];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bf16x8 kv = kt_frag(c);
-                sn = mfma32(kv, vbuf[c * 64 + lane], sn);
-                if constexpr (kSplit) sn = mfma32(kv, vbuf[256 + c * 64 + lane], sn);
+                const int row = 16 * c + 8 * (g16 >> 1) + (s16 >> 2);
+                const u32x2 lo = lds_read_tr(k_s + off_k(row, kt_f >> 3) + (kt_f & 7));
+                const u32x2 hi = lds_read_tr(k_s + off_k(row + 4, kt_f >> 3) + (kt_f & 7));
+                const bf16x8 kv = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                if (c & 1) s1 = mfma32(kv, vbuf[c * 64 + lane], s1);
+                else s0 = mfma32(kv, vbuf[c * 64 + lane], s0);
+                if constexpr (kSplit) {
+                    if (c & 1) s1 = mfma32(kv, vbuf[256 + c * 64 + lane], s1);
+                    else s0 = mfma32(kv, vbuf[256 + c * 64 + lane], s0);
+                }
             }
-            S = sn;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) S[i] = s0[i] + s1[i];
         }
         if (outputs && wave >= 2) {
             f32x16 o = xs;
@@ -644,6 +700,7 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
         lds_sync();
         flush_o(n1 - 1);
     }
+    __builtin_amdgcn_s_waitcnt(0);   // no direct load may still be writing LDS when the block ends
 
     if (a.store_mode == kStoreNone) return;
     if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
