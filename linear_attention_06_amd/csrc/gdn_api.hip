@@ -33,10 +33,11 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Kernel path: bf16 I/O with dk == 128 runs on the bf16 matrix cores; every
 // other problem runs on the fp32 vector-ALU kernels.
-bool use_mfma(const gdn_problem& p) { return p.io_dtype == GDN_BF16 && p.dk == 128 && p.dv % 32 == 0; }
+bool use_mfma(const gdn_problem& p) { return p.io_dtype == GDN_BF16 && p.dk == 128; }
 
-// Chunk intermediates: one record per (b, h, chunk). Element size of the two
-// 64x64 matrices: 2 bytes (bf16) on the matrix-core path, 4 bytes otherwise.
+// Chunk intermediates: one record per (b, h, chunk). The two 64x64 matrices take
+// their 6 lower-triangle 16x32 blocks in bf16 on the matrix-core path, and are
+// stored whole in fp32 otherwise.
 // The segment calls on the matrix-core path also keep the bf16 remainder of
 // That (used by the summary-matrix pass).
 struct Plan {
@@ -50,8 +51,8 @@ Plan make_plan(const gdn_problem& p, bool segments) {
     pl.NT = (static_cast<int64_t>(p.T) + gdn::kChunk - 1) / gdn::kChunk;
     pl.nch = static_cast<int64_t>(p.B) * p.H * pl.NT;
     const bool mfma = use_mfma(p);
-    const size_t elt = mfma ? 2 : sizeof(float);
-    const size_t mat = align256(static_cast<size_t>(pl.nch) * 64 * 64 * elt);
+    const size_t rec = mfma ? static_cast<size_t>(gdn::kTriRecordElems) * 2 : 64 * 64 * sizeof(float);
+    const size_t mat = align256(static_cast<size_t>(pl.nch) * rec);
     pl.that_off = 0;
     pl.pmat_off = mat;
     pl.gates_off = 2 * mat;

@@ -9,6 +9,8 @@
 namespace gdn {
 
 constexpr int kChunk = 64;
+// bf16 elements of one That or P record on the matrix-core path (6 blocks of 64 x 8)
+constexpr int kTriRecordElems = 6 * 512;
 
 // How a state pass starts.
 enum InitMode : int { kInitZero = 0, kInitLoad = 1, kInitIdentity = 2 };

@@ -37,6 +37,11 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int DK = 128;
 constexpr int KP = DK + 8;   // LDS pitch (bf16) of 128-wide rows: 272 B, conflict-free fragment reads
 constexpr int CP = 64 + 8;   // LDS pitch (bf16) of 64-wide rows: 144 B
+// That and P leave the prepare kernel as the 6 lower-triangle 16x32 blocks (r, s),
+// s <= r / 2, of 64 lanes x 8 bf16 each; block (r, s) sits at position tri_block(r, s).
+constexpr int kTriRecord = kTriRecordElems;
+constexpr bool kEnablePrefetch = true;   // L2 prefetch of chunk operands by the output wave
+__host__ __device__ constexpr int tri_block(int r, int s) { return r < 2 ? r : 2 + 2 * (r - 2) + s; }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -271,55 +276,64 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         }
         lds_sync();
     }
-    // outputs: That = Tinv diag(beta) and P, bf16 row-major 64x64
-    {
-        const int r = tid >> 2, c0 = 16 * (tid & 3);
-        uint16_t* that = static_cast<uint16_t*>(a.ws.that) + ch * 4096 + r * 64 + c0;
-        uint16_t* pm = static_cast<uint16_t*>(a.ws.pmat) + ch * 4096 + r * 64 + c0;
-        u32x4 w[2], wl[2];
+    // outputs: That = Tinv diag(beta), P and the bf16 remainder of That, in the
+    // fragment order of the state pass: lane l of block (r, s) holds row 16r + l % 16
+    // at tokens 32s + 4 (l / 16) + (e % 4) + 16 (e / 4), e = 0..7
+    for (int p = tid; p < 6 * 64; p += 256) {
+        const int blk = p >> 6, l = p & 63;
+        const int r = blk < 2 ? blk : 2 + ((blk - 2) >> 1);
+        const int s = blk < 2 ? 0 : ((blk - 2) & 1);
+        const int i = 16 * r + (l & 15), g = l >> 4;
+        u32x4 w, wl, wp;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = c0 + 8 * hh + 2 * e;
-                const float x0 = t_s[r * AP + c] * beta_s[c];
-                const float x1 = t_s[r * AP + c + 1] * beta_s[c + 1];
-                const uint16_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
-                w[hh][e] = h0 | (static_cast<uint32_t>(h1) << 16);
-                const uint16_t l0 = bf16_bits(x0 - bf16_to_f32(h0)), l1 = bf16_bits(x1 - bf16_to_f32(h1));
-                wl[hh][e] = l0 | (static_cast<uint32_t>(l1) << 16);
-            }
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const int j0 = 32 * s + 4 * g + 2 * (e2 & 1) + 16 * (e2 >> 1), j1 = j0 + 1;
+            const float x0 = t_s[i * AP + j0] * beta_s[j0], x1 = t_s[i * AP + j1] * beta_s[j1];
+            const uint16_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+            w[e2] = h0 | (static_cast<uint32_t>(h1) << 16);
+            wl[e2] = bf16_bits(x0 - bf16_to_f32(h0)) | (static_cast<uint32_t>(bf16_bits(x1 - bf16_to_f32(h1))) << 16);
+            wp[e2] = p_s[i * CP + j0] | (static_cast<uint32_t>(p_s[i * CP + j1]) << 16);
         }
-        *reinterpret_cast<u32x4*>(that) = w[0];
-        *reinterpret_cast<u32x4*>(that + 8) = w[1];
-        if (a.ws.that_lo) {
-            uint16_t* tl = static_cast<uint16_t*>(a.ws.that_lo) + ch * 4096 + r * 64 + c0;
-            *reinterpret_cast<u32x4*>(tl) = wl[0];
-            *reinterpret_cast<u32x4*>(tl + 8) = wl[1];
-        }
-        *reinterpret_cast<u32x4*>(pm) = *reinterpret_cast<const u32x4*>(p_s + r * CP + c0);
-        *reinterpret_cast<u32x4*>(pm + 8) = *reinterpret_cast<const u32x4*>(p_s + r * CP + c0 + 8);
+        const int64_t off = ch * kTriRecord + blk * 512 + l * 8;
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.that) + off) = w;
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.pmat) + off) = wp;
+        if (a.ws.that_lo) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.that_lo) + off) = wl;
     }
 }
 
 // ----------------------------------------------------------------------------
-// State pass: one block of 4 waves per (b, h, segment, 32 state columns).
-//   stage 1: waves 0,1: K S for token rows 32w..;  waves 2,3: Q S for rows 32(w-2)..
-//            waves 0,1: X = V - diag(exp Gam) K S
-//   stage 2: waves 0,1: U rows 32w.. = That X
-//   stage 3: every wave: S rows 32w.. <- exp(Gam_C) S + K^T V'', V'' = diag(exp(Gam_C - Gam)) U
-//            waves 2,3: O rows = diag(exp Gam) Q S + P U
-// The chunk operands (K, Q, That, P, decay factors) are loaded straight from
-// global memory into LDS (buffer loads with the lds bit), one chunk ahead, into
-// one of two stage buffers. Tiles in LDS are unpadded and XOR-swizzled per
-// 16-byte granule -- each lane of a direct load picks the global granule that
-// belongs at its LDS slot -- so that the MFMA fragment reads and the transposing
-// reads of K (which give the K^T fragments of the state update without a
-// transposed copy) are free of bank conflicts. The operands exchanged between waves (S, X, U, V'')
-// go through LDS in MFMA B-fragment order.
-// q, k, v are read through buffer descriptors whose range ends at the row's
-// last valid token, so padded and out-of-range tokens read as zero without any
-// per-element test; o is written through a descriptor that ends at T.
+// State pass. One block of 8 waves per (b, h, segment, 16 state columns):
+//   wave 0, the chain wave, carries the 128 x 16 state slice in registers and runs
+//     the sequential part of every chunk:
+//       X = V - diag(exp Gam) K S,   U = That X,   S <- exp(Gam_C) S + K^T diag(exp(Gam_C - Gam)) U
+//     on v_mfma_f32_16x16x32_bf16. Each product's 16x16 result tiles feed the next
+//     product as its B operand straight from the accumulators: the contraction
+//     index of a k-step is ordered as the rows the lanes of the result tiles hold
+//     (4 rows of one tile and the same 4 rows of the next), and every operand
+//     contracted against it is laid out with the same order. The chain wave issues
+//     no global memory instruction (issuing one stalls the issuing wave for tens of
+//     cycles).
+//   wave 1, the output wave (forward only), computes one chunk behind the chain
+//     wave O = diag(exp Gam) Q S + P U from the state and U the chain wave leaves in
+//     LDS, transposed (O^T = S^T Q^T + U^T P^T) so that each lane ends up holding
+//     four consecutive columns of one token, and writes o.
+//   the other waves load the chunk operands straight from global memory into LDS
+//     (buffer loads with the lds bit): K, That (and its remainder), V and the decay
+//     factors two chunks ahead of the chain wave, Q and P one chunk ahead of the
+//     output wave, in rings of three buffers.
+// One barrier per chunk.
+//
+// Layouts. A 1 KiB fragment block holds one 16x32 bf16 MFMA operand, lane l's 16
+// bytes at byte 16 l (row l % 16, contraction slots 8 (l / 16) .. +7):
+//   K, Q: 4-row blocks, swizzled (see below) so that one direct load moves 4 whole rows;
+//   That, P: blocks (r, s) of the lower triangle, (0,0) (1,0) (2,0) (2,1) (3,0) (3,1),
+//     rows = tokens 16r .., slot 8g + e = token 32s + 4g + (e % 4) + 16 (e / 4);
+//   V: [64 tokens][16 columns], read with transposing reads into accumulator order.
+// State register t (t = 0..7) of lane (c = l % 16, g = l / 16), element j holds
+// S[32 (t / 2) + 8g + 4 (t % 2) + j][c], so that the pair of registers 2s, 2s+1 is
+// the B fragment of k-step s of K S, and the transposing reads of K give the A
+// fragments of K^T for the state update in that same row order.
+//
 // kSplit (used for the summary matrix M, a product of thousands of near
 // projections whose relative error grows with every rounding): the state, X,
 // V'' and That enter the MFMAs as bf16 hi + lo pairs (x = hi + lo, lo the bf16 of
@@ -328,56 +342,49 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ void split8(const f32x16& v, int i0, bf16x8& hi, bf16x8& lo) {
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// Two accumulator tiles (4 rows each per lane) as one bf16 B fragment.
+__device__ __forceinline__ bf16x8 pack_frag(const f32x4& a, const f32x4& b) {
+    bf16x8 f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const __bf16 h = static_cast<__bf16>(v[i0 + u]);
-        hi[u] = h;
-        lo[u] = static_cast<__bf16>(v[i0 + u] - static_cast<float>(h));
+    for (int u = 0; u < 4; ++u) {
+        f[u] = static_cast<__bf16>(a[u]);
+        f[4 + u] = static_cast<__bf16>(b[u]);
+    }
+    return f;
+}
+// hi + lo split of the same pair: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void pack_frag_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const __bf16 ha = static_cast<__bf16>(a[u]), hb = static_cast<__bf16>(b[u]);
+        hi[u] = ha;
+        hi[4 + u] = hb;
+        lo[u] = static_cast<__bf16>(a[u] - static_cast<float>(ha));
+        lo[4 + u] = static_cast<__bf16>(b[u] - static_cast<float>(hb));
     }
 }
 __device__ __forceinline__ uint32_t pk2(float a, float b) {
     return bf16_bits(a) | (static_cast<uint32_t>(bf16_bits(b)) << 16);
 }
-
-// 128-wide bf16 tile (K, Q): granule g (8 elements) of row r sits at g ^ swz_k(r).
-__device__ __forceinline__ int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int off_k(int r, int g) { return r * 128 + 8 * (g ^ swz_k(r)); }
-// 64-wide bf16 tile (That, P): granule g of row r sits at g ^ swz_c(r).
-__device__ __forceinline__ int swz_c(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int off_c(int r, int g) { return r * 64 + 8 * (g ^ swz_c(r)); }
+__device__ __forceinline__ bf16x8 lds_frag_b(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
 // lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
 // i/4, 4 + i/4, 8 + i/4, 12 + i/4 of its group.
-__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* p) {
+__device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
-    lds_bf16x4* lp = (lds_bf16x4*)(const_cast<uint16_t*>(p));   // generic to LDS address space
+    lds_bf16x4* lp = (lds_bf16x4*)(const_cast<unsigned char*>(p));   // generic to LDS address space
 #pragma clang diagnostic pop
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
 }
-
-// Writes registers i0 .. i0+7 of a 32x32 C tile (rows 16h + {4q..4q+3, 8+4q..8+4q+3},
-// h = i0 / 8, column r) into the B-fragment slots of k-step ks (rows in order).
-__device__ __forceinline__ void put_frag(bf16x8* buf, int ks, int lane, u32x2 first, u32x2 second) {
-    uint16_t* slot = reinterpret_cast<uint16_t*>(buf + ks * 64 + (lane & 31));
-    const int e = 4 * (lane >> 5);
-    *reinterpret_cast<u32x2*>(slot + e) = first;
-    *reinterpret_cast<u32x2*>(slot + 32 * 8 + e) = second;
-}
-__device__ __forceinline__ void put_tile(bf16x8* buf, int ks0, int lane, const f32x16& v) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-        put_frag(buf, ks0 + hh, lane, u32x2{pk2(v[8 * hh], v[8 * hh + 1]), pk2(v[8 * hh + 2], v[8 * hh + 3])},
-                 u32x2{pk2(v[8 * hh + 4], v[8 * hh + 5]), pk2(v[8 * hh + 6], v[8 * hh + 7])});
-}
-__device__ __forceinline__ void put_tile_split(bf16x8* hi, bf16x8* lo, int ks0, int lane, const f32x16& v) {
-    f32x16 r;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = v[i] - bf16_to_f32(bf16_bits(v[i]));
-    put_tile(hi, ks0, lane, v);
-    put_tile(lo, ks0, lane, r);
+__device__ __forceinline__ f32x4 bf16x4_to_f32(u32x2 v) {
+    return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                 __uint_as_float(v[1] & 0xFFFF0000u)};
 }
 
 constexpr int kBufferFlags = 0x00020000;   // raw buffer descriptor word 3 on gfx9-family GPUs
@@ -386,16 +393,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     const int32_t n = static_cast<int32_t>(bytes < 0 ? 0 : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
 }
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
-}
-
 // Raw buffer descriptor (base, range in bytes) as four uniform words.
 __device__ __forceinline__ u32x4 make_desc(const void* base, int64_t bytes) {
     const uint64_t p = reinterpret_cast<uint64_t>(base);
@@ -411,32 +408,42 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
 #pragma clang diagnostic pop
 }
-// Direct global-to-LDS load of 16 bytes per lane: lane l writes LDS byte address
-// lds + 16 l (lds wave-uniform). Issued as asm so that the compiler does not make later
-// LDS reads of the other stage buffer wait for it; the chunk loop waits for these loads
-// explicitly (s_waitcnt vmcnt(0)).
-__device__ __forceinline__ void lds_dma16(const u32x4& desc, uint32_t lds, uint32_t off) {
+// Direct global-to-LDS load of 16 bytes per lane from byte voff + soff of the
+// buffer: lane l writes LDS byte address lds + 16 l (lds wave-uniform). Issued as asm
+// so that the compiler does not make LDS reads of other buffers wait for it; the
+// loading waves wait for these loads explicitly before the chunk barrier.
+__device__ __forceinline__ void lds_dma16(const u32x4& desc, uint32_t lds, uint32_t voff, uint32_t soff) {
     const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(off), "s"(desc)
+    const uint32_t so = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(soff));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(desc),
+                 "s"(so)
                  : "memory", "m0");
+}
+// Barrier of the state pass: this wave's LDS accesses complete, then s_barrier.
+// The loading waves first wait for their direct loads (vm_wait). One asm statement
+// with a memory clobber, so the compiler keeps LDS accesses on their side of it.
+__device__ __forceinline__ void chunk_barrier(bool vm_wait) {
+    if (vm_wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <bool kHasV, bool kSplit, bool kOut>
-__global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int groups) {
-    constexpr int NL = kSplit ? 1 : 0;   // extra lo buffers only in split mode
+__global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int groups) {
     constexpr bool outputs = kHasV && kOut;
-    // one stage buffer: K [64x128], Q [64x128] (outputs), That [64x64], P [64x64] (outputs),
-    // That remainder [64x64] (split), decay factors (1 KiB: 512 B used)
-    constexpr int KB = 64 * DK * 2, QB = outputs ? 64 * DK * 2 : 0, TB = 64 * 64 * 2;
-    constexpr int PB = outputs ? 64 * 64 * 2 : 0, LB = kSplit ? 64 * 64 * 2 : 0, GB = 1024;
-    constexpr int SB = KB + QB + TB + PB + LB + GB;
-    __shared__ __align__(16) unsigned char stage_s[2 * SB];
-    __shared__ __align__(16) uint16_t vt_s[kHasV ? 2 * 32 * CP : 8];  // V^T: [buffer][column][token]
-    __shared__ __align__(16) uint16_t ot_s[outputs ? 32 * CP : 8];    // O^T: [column][token]
-    __shared__ __align__(16) bf16x8 sbuf[(1 + NL) * 8 * 64];
-    __shared__ __align__(16) bf16x8 xbuf[(1 + NL) * 4 * 64];
-    __shared__ __align__(16) bf16x8 ubuf[outputs ? 4 * 64 : 1];
-    __shared__ __align__(16) bf16x8 vbuf[(1 + NL) * 4 * 64];
+    // K-side stage buffer: K, That, That remainder (split), V; Q-side: Q, P.
+    // K-side operands are loaded two chunks ahead (three buffers), Q-side operands
+    // one chunk ahead of the output wave, which runs one chunk behind (three buffers);
+    // the decay factors of a chunk live from their load to the output wave (ring of four).
+    constexpr int KB = 64 * DK * 2, TB = kTriRecord * 2, LB = kSplit ? kTriRecord * 2 : 0;
+    constexpr int VB = kHasV ? 64 * 16 * 2 : 0;
+    constexpr int KSB = KB + TB + LB + VB;
+    constexpr int QSB = outputs ? KB + TB : 0;
+    constexpr int HB = 6 * 1024;   // hand-off: S fragments (4 blocks), U fragments (2 blocks)
+    __shared__ __align__(16) unsigned char kst[3 * KSB];
+    __shared__ __align__(16) unsigned char qst[outputs ? 3 * QSB : 16];
+    __shared__ __align__(16) unsigned char gst[4 * 1024];
+    __shared__ __align__(16) unsigned char hst[outputs ? 2 * HB : 16];
+    __shared__ __align__(16) unsigned char pf_s[outputs ? 256 : 16];   // sink of the L2 prefetches
 
     // XCD-aware block order: the column tiles of one (b, h, segment) share an XCD.
     const int L = blockIdx.x;
@@ -448,268 +455,364 @@ __global__ __launch_bounds__(256) void state_mfma(StateArgs a, int tiles, int gr
     const int bz = grp / a.H;
     const int b = bz / a.P, seg = bz % a.P;
     const int hq = h / (a.H / a.Hqk);
-    const int col0 = 32 * tile;
-    const int tid = threadIdx.x, lane = tid & 63, q = lane >> 5, lr = lane & 31;
+    const int col0 = 16 * tile;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int ncols = a.ncols;
     const int64_t nvalid = valid_tokens(a.valid_len, b, a.T);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     const int64_t stile = static_cast<int64_t>(DK) * ncols;
+    const int n0 = seg * a.Lc, n1 = min(n0 + a.Lc, a.NT);
 
-    // descriptors over row b: q/k/v end at the last valid token, o at T; the
-    // workspace records of (b, h) as one descriptor
-    const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK;       // elements per token
+    const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK;   // elements per token
     const int64_t vo_row = static_cast<int64_t>(a.H) * ncols;
-    const uint16_t* kin = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(b) * a.T * qk_row;
-    const uint16_t* qin = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.T * qk_row;
-    const uint16_t* vin = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(b) * a.T * vo_row;
-    uint16_t* oout = static_cast<uint16_t*>(a.o) + static_cast<int64_t>(b) * a.T * vo_row;
-    const u32x4 rk = make_desc(kin, nvalid * qk_row * 2);
-    const u32x4 rq = make_desc(outputs ? qin : kin, nvalid * qk_row * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(outputs ? oout : kin, outputs ? static_cast<int64_t>(a.T) * vo_row * 2 : 0);
-    const int64_t rec = static_cast<int64_t>(a.NT) * 4096 * 2;        // bytes of one head's 64x64 records
-    const u32x4 rth = make_desc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * 4096, rec);
-    const u32x4 rpm = make_desc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * 4096, rec);
-    const u32x4 rtl =
-        make_desc(kSplit ? static_cast<const uint16_t*>(a.ws.that_lo) + bh * a.NT * 4096 : static_cast<const uint16_t*>(a.ws.that), rec);
-    const u32x4 rgt = make_desc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
+    const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
+    const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
+    const int first_loader = outputs ? 2 : 1;
+    // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule
+    // (row 4j + rho, dk 32s + 8g .. +7) at 16-byte slot 16 s + ((4 (j % 4) + rho) ^ 4g).
+    // A direct load fills one quad block from 4 whole rows; the fragment reads and the
+    // transposing reads below are free of bank conflicts.
+    const int frag_lane = (l16 >> 2) * 1024 + 16 * (l16 ^ (4 * g4));   // + 4096 r + 256 s: fragment (r, s)
 
-    // state rows 32*wave .. 32*wave+31, columns col0 .. col0+31, fp32, C layout
-    f32x16 S;
+    if (wave >= first_loader) {
+        // ---------------- loading waves ----------------
+        // q/k/v descriptors over row b end at the last valid token: padded and
+        // out-of-range tokens load as zero
+        const uint16_t* kin = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(b) * a.T * qk_row;
+        const uint16_t* qin = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.T * qk_row;
+        const uint16_t* vin = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(b) * a.T * vo_row;
+        const u32x4 rk = make_desc(kin, nvalid * qk_row * 2);
+        const u32x4 rq = make_desc(outputs ? qin : kin, nvalid * qk_row * 2);
+        const u32x4 rv = make_desc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
+        const int64_t rec = static_cast<int64_t>(a.NT) * kTriRecord * 2;   // bytes of one head's records
+        const u32x4 rth = make_desc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * kTriRecord, rec);
+        const u32x4 rpm = make_desc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * kTriRecord, rec);
+        const u32x4 rtl = make_desc(
+            kSplit ? static_cast<const uint16_t*>(a.ws.that_lo) + bh * a.NT * kTriRecord : static_cast<const uint16_t*>(a.ws.that),
+            rec);
+        const u32x4 rgt = make_desc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
+
+        // lane l of a quad-block load: slot l = 16 s + c, row 4j + (c & 3), granule g = (c >> 2) ^ (j & 3)
+        uint32_t voff_k[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            voff_k[jj] = static_cast<uint32_t>(((lane & 3) * qk_row + hq * DK + 32 * (lane >> 4) +
+                                                8 * (((lane >> 2) & 3) ^ jj)) * 2);
+        const uint32_t voff_l = static_cast<uint32_t>(16 * lane);
+        uint32_t voff_v[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * vo_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
+        const uint32_t kbase = lds_addr(kst), qbase = lds_addr(qst), gbase = lds_addr(gst);
+        const int me = wave - first_loader;
+        constexpr int nl = 8 - (outputs ? 2 : 1);
+        constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + (kHasV ? 2 : 0) + 1;
+        constexpr int NQ = outputs ? 22 : 0;
+        constexpr int NI = NK + NQ;   // loads of one full iteration, dealt round-robin over the loading waves
+
+        // K-side operands of chunk n into stage buffer n % 3 (decay factors into ring slot n % 4)
+        auto issue_k = [&](int n) {
+            const uint32_t dst = kbase + static_cast<uint32_t>((n % 3) * KSB);
+            const uint32_t tr = static_cast<uint32_t>(n) * (kTriRecord * 2);
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                if (i % nl != me) continue;
+                if (i < 16) {
+                    lds_dma16(rk, dst + i * 1024, voff_k[i & 3],
+                              static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
+                } else if (i < 22) {
+                    lds_dma16(rth, dst + KB + (i - 16) * 1024, voff_l, tr + (i - 16) * 1024);
+                } else if (kSplit && i < 28) {
+                    lds_dma16(rtl, dst + KB + TB + (i - 22) * 1024, voff_l, tr + (i - 22) * 1024);
+                } else if (kHasV && i < NK - 1) {
+                    const int m = i - (NK - 3);
+                    lds_dma16(rv, dst + KB + TB + LB + m * 1024, voff_v[m], static_cast<uint32_t>(n) * vstep);
+                } else {
+                    lds_dma16(rgt, gbase + (n % 4) * 1024, voff_l, static_cast<uint32_t>(n) * 512u);
+                }
+            }
+        };
+        // Q-side operands of chunk n into buffer n % 3
+        auto issue_q = [&](int n) {
+            const uint32_t dst = qbase + static_cast<uint32_t>((n % 3) * QSB);
+            const uint32_t tr = static_cast<uint32_t>(n) * (kTriRecord * 2);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                if ((NK + j) % nl != me) continue;
+                if (j < 16) {
+                    lds_dma16(rq, dst + j * 1024, voff_k[j & 3],
+                              static_cast<uint32_t>(4 * j * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
+                } else {
+                    lds_dma16(rpm, dst + KB + (j - 16) * 1024, voff_l, tr + (j - 16) * 1024);
+                }
+            }
+        };
+        // In iteration m the waves issue K(m + 2) and Q(m + 1); the barrier that opens
+        // iteration n needs the loads issued in iteration n - 2, so each wave first waits
+        // until no more than its share of iteration n - 1 is outstanding (loads of one
+        // wave complete in order). A partial set (near the end) waits for everything.
+        constexpr int cnt_hi = NI / nl + 1, cnt_lo = NI / nl;
+        const bool hi_share = me < NI % nl;
+        auto wait_older = [&](bool full) {
+            if (!full) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            else if (hi_share) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(cnt_hi) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(cnt_lo) : "memory");
+        };
+        auto issue_iter = [&](int m) {   // the loads of iteration m
+            if (m + 2 < n1) issue_k(m + 2);
+            if (outputs && m + 1 < n1) issue_q(m + 1);
+        };
+        if (n0 < n1) issue_k(n0);
+        issue_iter(n0 - 1);
+        for (int n = n0; n <= n1; ++n) {
+            wait_older(n + 1 < n1);
+            chunk_barrier(false);
+            issue_iter(n);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+
+    if (outputs && wave == 1) {
+        // ---------------- output wave: chunk n - 1 during chunk n ----------------
+        uint16_t* oout = static_cast<uint16_t*>(a.o) + static_cast<int64_t>(b) * a.T * vo_row;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(oout, static_cast<int64_t>(a.T) * vo_row * 2);
+        const uint32_t ooff = static_cast<uint32_t>((l16 * vo_row + h * ncols + col0 + 4 * g4) * 2);
+        // L2 prefetch, kPrefetch chunks ahead of the chain: the column tiles of a head
+        // split the 128-byte lines of its chunk operands between them (lanes 0..31: k and
+        // q rows, 32..47: v rows, 48..59: That and P records, 60..63: decay factors);
+        // the data lands in a scratch LDS word per lane that nothing reads.
+        constexpr int kPrefetch = 4;
+        const unsigned char* pf_base;
+        int64_t pf_stride;      // bytes per chunk
+        int pf_row = -1;        // token row inside the chunk for q/k/v lines, else -1
+        {
+            const int64_t bT = static_cast<int64_t>(b) * a.T;
+            if (lane < 32) {
+                const int lam = 32 * tile + lane;
+                const uint16_t* src = static_cast<const uint16_t*>(lam < 128 ? a.k : a.q);
+                pf_row = (lam & 127) >> 1;
+                pf_base = reinterpret_cast<const unsigned char*>(src + bT * qk_row + hq * DK + 64 * (lam & 1));
+                pf_stride = qk_row * 2;
+            } else if (lane < 48) {
+                const int lam = 16 * tile + lane - 32;
+                const int c = (64 * (lam & 1) < ncols) ? 64 * (lam & 1) : 0;
+                pf_row = lam >> 1;
+                pf_base = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.v) + bT * vo_row +
+                                                                  h * ncols + c);
+                pf_stride = vo_row * 2;
+            } else if (lane < 60) {
+                const int lam = (12 * tile + lane - 48) % 96;
+                const uint16_t* rec = static_cast<const uint16_t*>(lam < 48 ? a.ws.that : a.ws.pmat);
+                pf_base = reinterpret_cast<const unsigned char*>(rec + bh * a.NT * kTriRecord) + 128 * (lam % 48);
+                pf_stride = kTriRecord * 2;
+            } else {
+                pf_base = reinterpret_cast<const unsigned char*>(a.ws.gates + bh * a.NT * 128) + 128 * (lane - 60);
+                pf_stride = 512;
+            }
+        }
+        const uint32_t pf_lds = lds_addr(pf_s);
+        auto prefetch = [&](int c) {
+            const unsigned char* p;
+            if (pf_row >= 0) {
+                int64_t t = static_cast<int64_t>(c) * kChunk + pf_row;
+                if (t > a.T - 1) t = a.T - 1;
+                p = pf_base + t * pf_stride;
+            } else {
+                p = pf_base + static_cast<int64_t>(c) * pf_stride;
+            }
+            const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pf_lds));
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(p) : "memory", "m0");
+        };
+        if (kEnablePrefetch)
+            for (int c = n0 + 2; c < n0 + kPrefetch && c < n1; ++c) prefetch(c);
+        for (int n = n0; n <= n1; ++n) {
+            chunk_barrier(false);
+            if (kEnablePrefetch && n + kPrefetch < n1) prefetch(n + kPrefetch);
+            if (n == n0) continue;
+            const int m = n - 1;
+            const unsigned char* hb = hst + (m & 1) * HB;
+            const unsigned char* qs = qst + (m % 3) * QSB;
+            const unsigned char* ps = qs + KB;
+            const float* gs = reinterpret_cast<const float*>(gst + (m % 4) * 1024);
+            bf16x8 sb[4], ub[2];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) sb[s] = lds_frag_b(hb + s * 1024 + 16 * lane);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) ub[s] = lds_frag_b(hb + (4 + s) * 1024 + 16 * lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                f32x4 o0 = zero4(), o1 = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; s += 2) {
+                    o0 = mfma16(sb[s], lds_frag_b(qs + r * 4096 + s * 256 + frag_lane), o0);
+                    o1 = mfma16(sb[s + 1], lds_frag_b(qs + r * 4096 + (s + 1) * 256 + frag_lane), o1);
+                }
+                const float e = gs[16 * r + l16];
+                f32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = e * (o0[j] + o1[j]);
+                o = mfma16(ub[0], lds_frag_b(ps + tri_block(r, 0) * 1024 + 16 * lane), o);
+                if (r >= 2) o = mfma16(ub[1], lds_frag_b(ps + tri_block(r, 1) * 1024 + 16 * lane), o);
+                const int64_t t = static_cast<int64_t>(m) * kChunk + 16 * r + l16;
+                const bool ok = t < nvalid;
+                const uint32_t w0 = ok ? pk2(o[0], o[1]) : 0u, w1 = ok ? pk2(o[2], o[3]) : 0u;
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro,
+                                                      ooff + static_cast<uint32_t>(m) * vstep +
+                                                          static_cast<uint32_t>(16 * r * vo_row * 2),
+                                                      0, 0);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+    if (wave != 0) {
+        for (int n = n0; n <= n1; ++n) chunk_barrier(false);
+        return;
+    }
+
+    // ---------------- chain wave ----------------
+    f32x4 S[8];
     {
         const int64_t blk = a.s_init_per_segment ? bh * a.P + seg : bh;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 32 * wave + 8 * (i / 4) + 4 * q + (i % 4);
-            float s0 = 0.f;
-            if (a.init_mode == kInitLoad) s0 = a.s_init[blk * stile + static_cast<int64_t>(row) * ncols + col0 + lr];
-            else if (a.init_mode == kInitIdentity) s0 = (row == col0 + lr) ? 1.f : 0.f;
-            S[i] = s0;
-        }
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + j;
+                float s0 = 0.f;
+                if (a.init_mode == kInitLoad) s0 = a.s_init[blk * stile + static_cast<int64_t>(row) * ncols + col0 + l16];
+                else if (a.init_mode == kInitIdentity) s0 = (row == col0 + l16) ? 1.f : 0.f;
+                S[t][j] = s0;
+            }
     }
-    auto put_state = [&]() {
-        if constexpr (kSplit) put_tile_split(sbuf, sbuf + 512, 2 * wave, lane, S);
-        else put_tile(sbuf, 2 * wave, lane, S);
-    };
-    put_state();
+    bf16x8 sb[4], sbl[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (kSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
+        else sb[s] = pack_frag(S[2 * s], S[2 * s + 1]);
+    }
+    // Transposing reads of K: lane (c, g) of k-step s, half hf reads the 8-byte piece of
+    // token 32s + 16hf + 4g + c / 4 at dk 32 (t / 2) + 8 (c % 4) + 4 (t % 2): quad block
+    // 8s + 4hf + g, slot 16 (t / 2) + ((4g + c / 4) ^ 4 (c % 4)), byte 8 (t % 2).
+    const int tr_lane = g4 * 1024 + 16 * ((4 * g4 + (l16 >> 2)) ^ (4 * (l16 & 3)));
+    const int v_lane = 2 * (16 * (4 * g4 + (l16 >> 2)) + 4 * (l16 & 3));
 
-    // Direct loads. Each 1 KiB block of a tile is written by one wave instruction,
-    // lane l at byte 16 l. For the 128-wide tiles block j holds rows 4j .. 4j+3; for the
-    // 64-wide tiles rows 8j .. 8j+7. Wave w loads blocks w, w+4, w+8, w+12 (K, Q) and
-    // w, w+4 (That, P, That remainder); wave 0 also the decay factors.
-    uint32_t koff[4], toff[2];
+    for (int n = n0; n <= n1; ++n) {
+        chunk_barrier(false);
+        if (n == n1) break;
+        const unsigned char* ks = kst + (n % 3) * KSB;
+        const unsigned char* ts = ks + KB;
+        const unsigned char* tls = ks + KB + TB;
+        const unsigned char* vs = ks + KB + TB + LB;
+        const float* gs = reinterpret_cast<const float*>(gst + (n % 4) * 1024);
+        unsigned char* hb = hst + (n & 1) * HB;
+        if constexpr (outputs) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int row = 4 * (wave + 4 * u) + (lane >> 4), g = (lane & 15) ^ swz_k(row);
-        koff[u] = static_cast<uint32_t>((row * qk_row + hq * DK + 8 * g) * 2);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int row = 8 * (wave + 4 * u) + (lane >> 3), g = (lane & 7) ^ swz_c(row);
-        toff[u] = static_cast<uint32_t>((row * 64 + 8 * g) * 2);
-    }
-    const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
-    const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
-    const uint32_t stage_base = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds_addr(stage_s)));
-    auto issue_stage = [&](int n) {
-        const uint32_t sb = stage_base + static_cast<uint32_t>((n & 1) * SB) + static_cast<uint32_t>(wave) * 1024u;
-        const uint32_t kc = static_cast<uint32_t>(n) * kstep, tc = static_cast<uint32_t>(n) * 8192u;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            lds_dma16(rk, sb + u * 4096, koff[u] + kc);
-            if constexpr (outputs) lds_dma16(rq, sb + KB + u * 4096, koff[u] + kc);
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(hb + s * 1024 + 16 * lane) = sb[s];
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            lds_dma16(rth, sb + KB + QB + u * 4096, toff[u] + tc);
-            if constexpr (outputs) lds_dma16(rpm, sb + KB + QB + TB + u * 4096, toff[u] + tc);
-            if constexpr (kSplit) lds_dma16(rtl, sb + KB + QB + TB + PB + u * 4096, toff[u] + tc);
-        }
-        if (wave == 0) lds_dma16(rgt, sb + SB - GB, static_cast<uint32_t>(n) * 512u + 16u * (lane & 31));
-    };
-    // V (columns vcol, vcol+1 of tokens vrow0 .. vrow0+3) goes through registers into V^T;
-    // O leaves the same way.
-    const int vrow0 = 4 * (tid >> 4), vcol = 2 * (tid & 15);
-    uint32_t voff[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) voff[r] = static_cast<uint32_t>(((vrow0 + r) * vo_row + h * ncols + col0 + vcol) * 2);
-    uint32_t vreg[4] = {0u, 0u, 0u, 0u};
-    auto load_v = [&](int n) {
-        if constexpr (kHasV) {
-            const uint32_t vc = static_cast<uint32_t>(n) * vstep;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vreg[r] = buf_load4(rv, voff[r] + vc);
-        }
-    };
-    auto put_v = [&](int n) {
-        if constexpr (kHasV) {
-            uint16_t* vt = vt_s + (n & 1) * 32 * CP;
-            const uint32_t lo0 = (vreg[0] & 0xFFFFu) | (vreg[1] << 16), lo1 = (vreg[2] & 0xFFFFu) | (vreg[3] << 16);
-            const uint32_t hi0 = (vreg[0] >> 16) | (vreg[1] & 0xFFFF0000u), hi1 = (vreg[2] >> 16) | (vreg[3] & 0xFFFF0000u);
-            *reinterpret_cast<u32x2*>(vt + vcol * CP + vrow0) = u32x2{lo0, lo1};
-            *reinterpret_cast<u32x2*>(vt + (vcol + 1) * CP + vrow0) = u32x2{hi0, hi1};
-        }
-    };
-    // O^T of chunk n from LDS to o (rows past the valid length written as zero)
-    auto flush_o = [&](int n) {
-        const u32x2 c0 = *reinterpret_cast<const u32x2*>(ot_s + vcol * CP + vrow0);
-        const u32x2 c1 = *reinterpret_cast<const u32x2*>(ot_s + (vcol + 1) * CP + vrow0);
-        const uint32_t vc = static_cast<uint32_t>(n) * vstep;
-        const int64_t t0 = static_cast<int64_t>(n) * kChunk + vrow0;
-        uint32_t w[4];
-        w[0] = (c0[0] & 0xFFFFu) | (c1[0] << 16);
-        w[1] = (c0[0] >> 16) | (c1[0] & 0xFFFF0000u);
-        w[2] = (c0[1] & 0xFFFFu) | (c1[1] << 16);
-        w[3] = (c0[1] >> 16) | (c1[1] & 0xFFFF0000u);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) buf_store4(ro, voff[r] + vc, (t0 + r < nvalid) ? w[r] : 0u);
-    };
 
-    const int n0 = seg * a.Lc, n1 = min(n0 + a.Lc, a.NT);
-    const int g16 = lane >> 4, s16 = lane & 15;
-    const int kt_f = 32 * wave + 16 * (g16 & 1) + 4 * (s16 & 3);
-    if (n0 < n1) {
-        issue_stage(n0);
-        load_v(n0);
-    }
-    for (int n = n0; n < n1; ++n) {
-        const unsigned char* sb = stage_s + (n & 1) * SB;
-        const uint16_t* k_s = reinterpret_cast<const uint16_t*>(sb);
-        const uint16_t* q_s = reinterpret_cast<const uint16_t*>(sb + KB);
-        const uint16_t* th_s = reinterpret_cast<const uint16_t*>(sb + KB + QB);
-        const uint16_t* p_s = reinterpret_cast<const uint16_t*>(sb + KB + QB + TB);
-        const uint16_t* tl_s = reinterpret_cast<const uint16_t*>(sb + KB + QB + TB + PB);
-        const float* g_s = reinterpret_cast<const float*>(sb + SB - GB);
-        const uint16_t* vt = vt_s + (n & 1) * 32 * CP;
-
-        __builtin_amdgcn_s_waitcnt(0);   // this chunk's direct loads and V have landed
-        put_v(n);
-        lds_sync();                      // ... in every wave; the other stage buffer is free
-        if (outputs && n > n0) flush_o(n - 1);
+        // K S: token tiles r, k-steps s (two accumulators per tile)
+        f32x4 x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f32x4 c0 = zero4(), c1 = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; s += 2) {
+                const bf16x8 k0 = lds_frag_b(ks + r * 4096 + s * 256 + frag_lane);
+                const bf16x8 k1 = lds_frag_b(ks + r * 4096 + (s + 1) * 256 + frag_lane);
+                c0 = mfma16(k0, sb[s], c0);
+                c1 = mfma16(k1, sb[s + 1], c1);
+                if constexpr (kSplit) {
+                    c0 = mfma16(k0, sbl[s], c0);
+                    c1 = mfma16(k1, sbl[s + 1], c1);
+                }
+            }
+            // X = V - diag(exp Gam) K S for tokens 16r + 4g + j, column l16
+            const f32x4 e4 = *reinterpret_cast<const f32x4*>(gs + 16 * r + 4 * g4);
+            f32x4 v4 = zero4();
+            if constexpr (kHasV) v4 = bf16x4_to_f32(lds_read_tr(vs + 16 * r * 32 + v_lane));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[r][j] = v4[j] - e4[j] * (c0[j] + c1[j]);
+        }
+        bf16x8 xb[2], xbl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            if constexpr (kSplit) pack_frag_split(x[2 * s], x[2 * s + 1], xb[s], xbl[s]);
+            else xb[s] = pack_frag(x[2 * s], x[2 * s + 1]);
+        }
+        // U = That X (lower triangular: k-steps s <= r / 2)
+        f32x4 u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            u[r] = zero4();
+#pragma unroll
+            for (int s = 0; s <= r / 2; ++s) {
+                const bf16x8 th = lds_frag_b(ts + tri_block(r, s) * 1024 + 16 * lane);
+                u[r] = mfma16(th, xb[s], u[r]);
+                if constexpr (kSplit) {
+                    u[r] = mfma16(th, xbl[s], u[r]);
+                    u[r] = mfma16(lds_frag_b(tls + tri_block(r, s) * 1024 + 16 * lane), xb[s], u[r]);
+                }
+            }
+        }
+        if constexpr (outputs) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                *reinterpret_cast<bf16x8*>(hb + (4 + s) * 1024 + 16 * lane) = pack_frag(u[2 * s], u[2 * s + 1]);
+        }
+        // V'' = diag(exp(Gam_C - Gam)) U
+        bf16x8 vb[2], vbl[2];
         {
-            // the last chunk reloads its own data: the loads stay unconditional
-            const int nn = (n + 1 < n1) ? n + 1 : n;
-            if (nn != n) issue_stage(nn);
-            load_v(nn);
-        }
-        const int m = wave & 1;
-
-        // ---- stage 1: K S (waves 0,1) or Q S (waves 2,3, only with outputs), rows 32m..32m+31
-        f32x16 xs = zero16();   // waves 0,1: X;  waves 2,3: diag(exp Gam) Q S
-        if (wave < 2 || outputs) {
-            const uint16_t* X = (wave < 2) ? k_s : q_s;
-            f32x16 acc0 = zero16(), acc1 = zero16();
+            f32x4 w[4];
 #pragma unroll
-            for (int c = 0; c < 8; c += 2) {
-                const bf16x8 a0 = lds_frag(X + off_k(32 * m + lr, 2 * c + q));
-                const bf16x8 a1 = lds_frag(X + off_k(32 * m + lr, 2 * c + 2 + q));
-                acc0 = mfma32(a0, sbuf[c * 64 + lane], acc0);
-                acc1 = mfma32(a1, sbuf[(c + 1) * 64 + lane], acc1);
-                if constexpr (kSplit) {
-                    acc0 = mfma32(a0, sbuf[512 + c * 64 + lane], acc0);
-                    acc1 = mfma32(a1, sbuf[512 + (c + 1) * 64 + lane], acc1);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 e4 = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[r][j] = e4[j] * u[r][j];
             }
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int row = 32 * m + 8 * i4 + 4 * q;
-                const f32x4 e4 = *reinterpret_cast<const f32x4*>(g_s + row);
-                float v4[4] = {0.f, 0.f, 0.f, 0.f};
-                if (kHasV && wave < 2) {
-                    const u32x2 vv = *reinterpret_cast<const u32x2*>(vt + lr * CP + row);
-                    v4[0] = __uint_as_float(vv[0] << 16);
-                    v4[1] = __uint_as_float(vv[0] & 0xFFFF0000u);
-                    v4[2] = __uint_as_float(vv[1] << 16);
-                    v4[3] = __uint_as_float(vv[1] & 0xFFFF0000u);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float ks = acc0[4 * i4 + j] + acc1[4 * i4 + j];
-                    xs[4 * i4 + j] = (wave < 2) ? v4[j] - e4[j] * ks : e4[j] * ks;
-                }
-            }
-            if (wave < 2) {
-                if constexpr (kSplit) put_tile_split(xbuf, xbuf + 256, 2 * m, lane, xs);
-                else put_tile(xbuf, 2 * m, lane, xs);
+            for (int s = 0; s < 2; ++s) {
+                if constexpr (kSplit) pack_frag_split(w[2 * s], w[2 * s + 1], vb[s], vbl[s]);
+                else vb[s] = pack_frag(w[2 * s], w[2 * s + 1]);
             }
         }
-        stage_sync();
-
-        // ---- stage 2: U rows 32m.. = That X (waves 0,1)
-        if (wave < 2) {
-            f32x16 u = zero16();
-            const int kst = 2 * m + 2;   // That is lower triangular: k-steps past the rows are zero
-            for (int c = 0; c < kst; ++c) {
-                const bf16x8 th = lds_frag(th_s + off_c(32 * m + lr, 2 * c + q));
-                u = mfma32(th, xbuf[c * 64 + lane], u);
-                if constexpr (kSplit) {
-                    u = mfma32(th, xbuf[256 + c * 64 + lane], u);
-                    u = mfma32(lds_frag(tl_s + off_c(32 * m + lr, 2 * c + q)), xbuf[c * 64 + lane], u);
-                }
+        // S <- exp(Gam_C) S + K^T V'': state tiles t, token k-steps s
+        const float egC = gs[63];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            f32x4 acc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = egC * S[t][j];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int o0 = 8 * s * 1024 + 256 * (t >> 1) + 8 * (t & 1) + tr_lane;
+                const u32x2 lo = lds_read_tr(ks + o0);
+                const u32x2 hi = lds_read_tr(ks + o0 + 4 * 1024);
+                const bf16x8 kt = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                acc = mfma16(kt, vb[s], acc);
+                if constexpr (kSplit) acc = mfma16(kt, vbl[s], acc);
             }
-            if (outputs) put_tile(ubuf, 2 * m, lane, u);
-            f32x16 vv;
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const f32x4 e4 = *reinterpret_cast<const f32x4*>(g_s + 64 + 32 * m + 8 * i4 + 4 * q);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) vv[4 * i4 + j] = e4[j] * u[4 * i4 + j];
-            }
-            if constexpr (kSplit) put_tile_split(vbuf, vbuf + 256, 2 * m, lane, vv);
-            else put_tile(vbuf, 2 * m, lane, vv);
+            S[t] = acc;
         }
-        stage_sync();
-
-        // ---- stage 3: state rows 32*wave.. and (waves 2,3) the outputs
-        {
-            const float egC = g_s[63];
-            f32x16 s0, s1 = zero16();
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s0[i] = egC * S[i];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int row = 16 * c + 8 * (g16 >> 1) + (s16 >> 2);
-                const u32x2 lo = lds_read_tr(k_s + off_k(row, kt_f >> 3) + (kt_f & 7));
-                const u32x2 hi = lds_read_tr(k_s + off_k(row + 4, kt_f >> 3) + (kt_f & 7));
-                const bf16x8 kv = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                if (c & 1) s1 = mfma32(kv, vbuf[c * 64 + lane], s1);
-                else s0 = mfma32(kv, vbuf[c * 64 + lane], s0);
-                if constexpr (kSplit) {
-                    if (c & 1) s1 = mfma32(kv, vbuf[256 + c * 64 + lane], s1);
-                    else s0 = mfma32(kv, vbuf[256 + c * 64 + lane], s0);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) S[i] = s0[i] + s1[i];
+        for (int s = 0; s < 4; ++s) {
+            if constexpr (kSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
+            else sb[s] = pack_frag(S[2 * s], S[2 * s + 1]);
         }
-        if (outputs && wave >= 2) {
-            f32x16 o = xs;
-            const int kst = 2 * m + 2;
-            for (int c = 0; c < kst; ++c)
-                o = mfma32(lds_frag(p_s + off_c(32 * m + lr, 2 * c + q)), ubuf[c * 64 + lane], o);
-            // O^T into LDS: column lr, 4 consecutive tokens per register group
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-                *reinterpret_cast<u32x2*>(ot_s + lr * CP + 32 * m + 8 * i4 + 4 * q) =
-                    u32x2{pk2(o[4 * i4], o[4 * i4 + 1]), pk2(o[4 * i4 + 2], o[4 * i4 + 3])};
-        }
-        put_state();
     }
-    if (outputs && n0 < n1) {
-        lds_sync();
-        flush_o(n1 - 1);
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // no direct load may still be writing LDS when the block ends
 
     if (a.store_mode == kStoreNone) return;
     if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
     const int64_t blk = (a.store_mode == kStoreEverySegment) ? bh * a.P + seg : bh;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = 32 * wave + 8 * (i / 4) + 4 * q + (i % 4);
-        a.s_out[blk * stile + static_cast<int64_t>(row) * ncols + col0 + lr] = S[i];
-    }
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + j;
+            a.s_out[blk * stile + static_cast<int64_t>(row) * ncols + col0 + l16] = S[t][j];
+        }
 }
 
 }  // namespace
@@ -721,7 +824,7 @@ hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
-    int tiles = a.ncols / 32;
+    int tiles = a.ncols / 16;
     int groups = a.H * a.B * a.P;
     const unsigned nblk = static_cast<unsigned>(((groups + 7) / 8) * 8 * tiles);
     void* args[] = {const_cast<StateArgs*>(&a), &tiles, &groups};
@@ -729,7 +832,7 @@ hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
     const void* fn = !a.v ? reinterpret_cast<const void*>(&state_mfma<false, true, false>)
                    : a.o  ? reinterpret_cast<const void*>(&state_mfma<true, false, true>)
                           : reinterpret_cast<const void*>(&state_mfma<true, false, false>);
-    return hipLaunchKernel(fn, dim3(nblk), dim3(256), args, 0, s);
+    return hipLaunchKernel(fn, dim3(nblk), dim3(512), args, 0, s);
 }
 
 }  // namespace gdn
