@@ -101,19 +101,34 @@ __device__ __forceinline__ void store8_perm(uint16_t* row, int base16, int h8, u
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     constexpr int AP = 68;  // fp32 pitch of the 64x64 A and Tinv tiles
-    __shared__ __align__(16) unsigned char smem[2 * 64 * KP * 2 + 64 * AP * 4 + 512];
+    // 34.5 KiB, four blocks per CU: K and Q (bf16, 256-byte rows) fill the first 32 KiB
+    // until the products are done; then A lives at the start and Tinv behind it; once
+    // the solve is done P (bf16) takes the place of A. The decay scan and beta follow.
+    constexpr int TS_OFF = 64 * AP * 4, GB_OFF = 2 * 64 * AP * 4;
+    __shared__ __align__(16) unsigned char smem[GB_OFF + 512];
     uint16_t* k_s = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* q_s = k_s + 64 * KP;
-    float* t_s = reinterpret_cast<float*>(smem);                       // after the products
-    uint16_t* p_s = reinterpret_cast<uint16_t*>(smem + 64 * AP * 4);    // after the products
-    float* a_s = reinterpret_cast<float*>(smem + 2 * 64 * KP * 2);
-    float* gam_s = a_s + 64 * AP;
+    uint16_t* q_s = k_s + 64 * DK;
+    float* a_s = reinterpret_cast<float*>(smem);              // after the products
+    float* t_s = reinterpret_cast<float*>(smem + TS_OFF);     // after the products
+    uint16_t* p_s = reinterpret_cast<uint16_t*>(smem);        // after the solve
+    float* gam_s = reinterpret_cast<float*>(smem + GB_OFF);
     float* beta_s = gam_s + 64;
+    // K / Q element offset of granule g (8 bf16) of row r: XOR-swizzled by the row so
+    // that the fragment reads of 16 consecutive rows hit 16 different bank groups
+    const auto kq_at = [](int r, int g) { return r * DK + 8 * (g ^ (r & 15)); };
 
-    const int64_t ch = blockIdx.x;
-    const int n = static_cast<int>(ch % a.NT);
-    const int bh = static_cast<int>(ch / a.NT);
-    const int h = bh % a.H, b = bh / a.H;
+    // Block order: chunk-major, the heads of one (b, chunk) back to back on one XCD
+    // (workgroups go round-robin over the 8 XCDs), so that its L2 serves the q/k rows
+    // shared by the value heads of a query/key head and the g / beta lines shared by
+    // all heads. ch is the (b, h, chunk) record index.
+    const int64_t L = blockIdx.x;
+    const int xcd = static_cast<int>(L & 7);
+    const int64_t u = L >> 3;
+    const int h = static_cast<int>(u % a.H);
+    const int64_t pair = (u / a.H) * 8 + xcd;
+    if (pair >= static_cast<int64_t>(a.B) * a.NT) return;
+    const int b = static_cast<int>(pair / a.NT), n = static_cast<int>(pair % a.NT);
+    const int64_t ch = (static_cast<int64_t>(b) * a.H + h) * a.NT + n;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 5, lr = lane & 31;
     const int64_t t0 = static_cast<int64_t>(n) * kChunk;
@@ -124,6 +139,19 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     // Loads are unconditional from a clamped, in-bounds token (row 0 of the
     // sequence for padded tokens) and masked afterwards, so that no load waits
     // behind a branch.
+    // the q/k loads go out first; the decay scan of wave 0 runs while they are in flight
+    u32x4 kv[4], qv[4];
+    {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
+            const int64_t t = t0 + row;
+            const int64_t off =
+                ((static_cast<int64_t>(b) * a.T + (t < nvalid ? t : 0)) * a.Hqk + hq) * DK + 8 * cb;
+            kv[u] = *reinterpret_cast<const u32x4*>(kin + off);
+            qv[u] = *reinterpret_cast<const u32x4*>(qin + off);
+        }
+    }
     if (wave == 0) {
         const int64_t t = t0 + lane;
         const bool valid = t < nvalid;
@@ -143,23 +171,13 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         a.ws.gates[ch * 128 + 64 + lane] = __expf(gam_c - gam);
     }
     {
-        u32x4 kv[4], qv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
-            const int64_t t = t0 + row;
-            const int64_t off =
-                ((static_cast<int64_t>(b) * a.T + (t < nvalid ? t : 0)) * a.Hqk + hq) * DK + 8 * cb;
-            kv[u] = *reinterpret_cast<const u32x4*>(kin + off);
-            qv[u] = *reinterpret_cast<const u32x4*>(qin + off);
-        }
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
             const bool valid = t0 + row < nvalid;
-            *reinterpret_cast<u32x4*>(k_s + row * KP + 8 * cb) = valid ? kv[u] : z;
-            *reinterpret_cast<u32x4*>(q_s + row * KP + 8 * cb) = valid ? qv[u] : z;
+            *reinterpret_cast<u32x4*>(k_s + kq_at(row, cb)) = valid ? kv[u] : z;
+            *reinterpret_cast<u32x4*>(q_s + kq_at(row, cb)) = valid ? qv[u] : z;
         }
     }
     lds_sync();
@@ -170,8 +188,8 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         f32x16 acc = zero16();
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const bf16x8 av = lds_frag(X + (32 * mi + lr) * KP + 16 * c + 8 * q);
-            const bf16x8 bv = lds_frag(k_s + (32 * nj + lr) * KP + 16 * c + 8 * q);
+            const bf16x8 av = lds_frag(X + kq_at(32 * mi + lr, 2 * c + q));
+            const bf16x8 bv = lds_frag(k_s + kq_at(32 * nj + lr, 2 * c + q));
             acc = mfma32(av, bv, acc);
         }
         return acc;
@@ -187,14 +205,23 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     } else {
         acc0 = tile(q_s, wave - 2, wave - 2);
     }
-    // A (fp32) into LDS
+    lds_sync();   // K and Q are dead from here on; A takes their place
+    // A (fp32) into LDS. The decay and beta values of the lane's 16 rows are read
+    // into registers first: the A stores share the LDS array, and reads placed
+    // between them would be issued one at a time.
     auto emit_a = [&](const f32x16& acc, int mi, int nj) {
         const int s = 32 * nj + lr;
         const float gs = gam_s[s];
+        f32x4 gt[4], bt[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            gt[i4] = *reinterpret_cast<const f32x4*>(gam_s + 32 * mi + 8 * i4 + 4 * q);
+            bt[i4] = *reinterpret_cast<const f32x4*>(beta_s + 32 * mi + 8 * i4 + 4 * q);
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 32 * mi + 8 * (i / 4) + 4 * q + (i % 4);
-            a_s[t * AP + s] = (t > s) ? beta_s[t] * __expf(gam_s[t] - gs) * acc[i] : 0.f;
+            a_s[t * AP + s] = (t > s) ? bt[i / 4][i % 4] * __expf(gt[i / 4][i % 4] - gs) * acc[i] : 0.f;
         }
     };
     if (wave == 0) emit_a(acc0, 1, 0);
@@ -209,25 +236,16 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     if (has_p) {
         const int s = 32 * p_nj + lr;
         const float gs = gam_s[s];
+        f32x4 gt[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) gt[i4] = *reinterpret_cast<const f32x4*>(gam_s + 32 * p_mi + 8 * i4 + 4 * q);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 32 * p_mi + 8 * (i / 4) + 4 * q + (i % 4);
-            pq[i] = (t >= s) ? __expf(gam_s[t] - gs) * pq[i] : 0.f;
+            pq[i] = (t >= s) ? __expf(gt[i / 4][i % 4] - gs) * pq[i] : 0.f;
         }
     }
-    lds_sync();   // K and Q are dead from here on; their space holds Tinv and P
-
-    if (has_p) {
-        const int s = 32 * p_nj + lr;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = 32 * p_mi + 8 * (i / 4) + 4 * q + (i % 4);
-            p_s[t * CP + s] = bf16_bits(pq[i]);
-        }
-    } else {
-        // wave 1: the all-zero upper tile of P (rows 0..31, cols 32..63)
-        for (int e = lane; e < 32 * 32; e += 64) p_s[(e >> 5) * CP + 32 + (e & 31)] = 0;
-    }
+    lds_sync();   // A is complete; P stays in registers until A is dead
     // zero the strictly upper 16x16 blocks of Tinv
     for (int e = tid; e < 6 * 256; e += 256) {
         const int blk = e >> 8, w = e & 255;
@@ -238,16 +256,23 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     // diagonal 16x16 blocks: unit lower-triangular inverse by forward
     // substitution, wave w inverts block w, lane c < 16 owns column c
     if (lane < 16) {
+        // column sweep: once x[j] is final it is eliminated from every later row, so
+        // the dependency chain is 15 steps long instead of one FMA per matrix entry
         const int c = lane, o = 16 * wave;
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == c) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int j = 0; j < r; ++j) acc -= a_s[(o + r) * AP + o + j] * x[j];
-            x[r] = acc;
-            t_s[(o + r) * AP + o + c] = acc;
+        for (int j = 0; j < 15; ++j) {
+            float col[16];
+#pragma unroll
+            for (int r = j + 1; r < 16; ++r) col[r] = a_s[(o + r) * AP + o + j];
+#pragma unroll
+            for (int r = j + 1; r < 16; ++r) x[r] -= col[r] * x[j];
         }
+        // stored after the substitution, so that no store sits between its LDS reads
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t_s[(o + r) * AP + o + c] = x[r];
     }
     lds_sync();
     // off-diagonal blocks, one block row per level: T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj
@@ -276,6 +301,19 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         }
         lds_sync();
     }
+    // P into the space of A
+    if (has_p) {
+        const int s = 32 * p_nj + lr;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = 32 * p_mi + 8 * (i / 4) + 4 * q + (i % 4);
+            p_s[t * CP + s] = bf16_bits(pq[i]);
+        }
+    } else {
+        // wave 1: the all-zero upper tile of P (rows 0..31, cols 32..63)
+        for (int e = lane; e < 32 * 32; e += 64) p_s[(e >> 5) * CP + 32 + (e & 31)] = 0;
+    }
+    lds_sync();
     // outputs: That = Tinv diag(beta), P and the bf16 remainder of That, in the
     // fragment order of the state pass: lane l of block (r, s) holds row 16r + l % 16
     // at tokens 32s + 4 (l / 16) + (e % 4) + 16 (e / 4), e = 0..7
@@ -428,7 +466,7 @@ __device__ __forceinline__ void chunk_barrier(bool vm_wait) {
 }
 
 template <bool kHasV, bool kSplit, bool kOut>
-__global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int groups) {
+__global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk_groups) {
     constexpr bool outputs = kHasV && kOut;
     // K-side stage buffer: K, That, That remainder (split), V; Q-side: Q, P.
     // K-side operands are loaded two chunks ahead (three buffers), Q-side operands
@@ -445,16 +483,19 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int gr
     __shared__ __align__(16) unsigned char hst[outputs ? 2 * HB : 16];
     __shared__ __align__(16) unsigned char pf_s[outputs ? 256 : 16];   // sink of the L2 prefetches
 
-    // XCD-aware block order: the column tiles of one (b, h, segment) share an XCD.
+    // XCD-aware block order (workgroups go round-robin over the 8 XCDs): every column
+    // tile of the value heads that read one query/key head of one (b, segment) runs on
+    // the same XCD, so that its L2 holds that head's q, k and chunk records once.
     const int L = blockIdx.x;
     const int xcd = L & 7, slot = L >> 3;
     const int tile = slot % tiles;
-    const int grp = (slot / tiles) * 8 + xcd;
-    if (grp >= groups) return;
-    const int h = grp % a.H;
-    const int bz = grp / a.H;
+    const int rep = a.H / a.Hqk;
+    const int kk = slot / tiles;
+    const int qg = (kk / rep) * 8 + xcd;   // (b, segment, query/key head) group
+    if (qg >= qk_groups) return;
+    const int bz = qg / a.Hqk, hq = qg % a.Hqk;
+    const int h = hq * rep + kk % rep;
     const int b = bz / a.P, seg = bz % a.P;
-    const int hq = h / (a.H / a.Hqk);
     const int col0 = 16 * tile;
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
@@ -708,33 +749,76 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int gr
         const unsigned char* vs = ks + KB + TB + LB;
         const float* gs = reinterpret_cast<const float*>(gst + (n % 4) * 1024);
         unsigned char* hb = hst + (n & 1) * HB;
+
+        // Phase 0: every LDS operand of K S, X and U, read at once.
+        bf16x8 kf[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) kf[i] = lds_frag_b(ks + (i >> 2) * 4096 + (i & 3) * 256 + frag_lane);
+        f32x4 eg[4];
+        u32x2 vraw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            eg[r] = *reinterpret_cast<const f32x4*>(gs + 16 * r + 4 * g4);
+            if constexpr (kHasV) vraw[r] = lds_read_tr(vs + 16 * r * 32 + v_lane);
+        }
+        bf16x8 th[6], thl[6];
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+            th[j] = lds_frag_b(ts + j * 1024 + 16 * lane);
+            if constexpr (kSplit) thl[j] = lds_frag_b(tls + j * 1024 + 16 * lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Phase 1: K S for token tiles r (two accumulators per tile, k-steps interleaved
+        // across tiles so that no MFMA waits for the previous one).
+        f32x4 c0[4], c1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            c0[r] = mfma16(kf[4 * r], sb[0], zero4());
+            c1[r] = mfma16(kf[4 * r + 1], sb[1], zero4());
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            c0[r] = mfma16(kf[4 * r + 2], sb[2], c0[r]);
+            c1[r] = mfma16(kf[4 * r + 3], sb[3], c1[r]);
+        }
+        if constexpr (kSplit) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int s = 0; s < 4; s += 2) {
+                    c0[r] = mfma16(kf[4 * r + s], sbl[s], c0[r]);
+                    c1[r] = mfma16(kf[4 * r + s + 1], sbl[s + 1], c1[r]);
+                }
+            }
+        }
+        // the transposing reads of K for the state update go out while K S runs
+        u32x2 ktr[8][2][2];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int o0 = 8 * s * 1024 + 256 * (t >> 1) + 8 * (t & 1) + tr_lane;
+                ktr[t][s][0] = lds_read_tr(ks + o0);
+                ktr[t][s][1] = lds_read_tr(ks + o0 + 4 * 1024);
+            }
+        f32x4 egc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) egc[r] = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
+        const float egC = gs[63];
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (outputs) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(hb + s * 1024 + 16 * lane) = sb[s];
         }
 
-        // K S: token tiles r, k-steps s (two accumulators per tile)
+        // Phase 2: X = V - diag(exp Gam) K S for tokens 16r + 4g + j, column l16
         f32x4 x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            f32x4 c0 = zero4(), c1 = zero4();
+            const f32x4 v4 = kHasV ? bf16x4_to_f32(vraw[r]) : zero4();
 #pragma unroll
-            for (int s = 0; s < 4; s += 2) {
-                const bf16x8 k0 = lds_frag_b(ks + r * 4096 + s * 256 + frag_lane);
-                const bf16x8 k1 = lds_frag_b(ks + r * 4096 + (s + 1) * 256 + frag_lane);
-                c0 = mfma16(k0, sb[s], c0);
-                c1 = mfma16(k1, sb[s + 1], c1);
-                if constexpr (kSplit) {
-                    c0 = mfma16(k0, sbl[s], c0);
-                    c1 = mfma16(k1, sbl[s + 1], c1);
-                }
-            }
-            // X = V - diag(exp Gam) K S for tokens 16r + 4g + j, column l16
-            const f32x4 e4 = *reinterpret_cast<const f32x4*>(gs + 16 * r + 4 * g4);
-            f32x4 v4 = zero4();
-            if constexpr (kHasV) v4 = bf16x4_to_f32(lds_read_tr(vs + 16 * r * 32 + v_lane));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) x[r][j] = v4[j] - e4[j] * (c0[j] + c1[j]);
+            for (int j = 0; j < 4; ++j) x[r][j] = v4[j] - eg[r][j] * (c0[r][j] + c1[r][j]);
         }
         bf16x8 xb[2], xbl[2];
 #pragma unroll
@@ -749,14 +833,19 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int gr
             u[r] = zero4();
 #pragma unroll
             for (int s = 0; s <= r / 2; ++s) {
-                const bf16x8 th = lds_frag_b(ts + tri_block(r, s) * 1024 + 16 * lane);
-                u[r] = mfma16(th, xb[s], u[r]);
+                u[r] = mfma16(th[tri_block(r, s)], xb[s], u[r]);
                 if constexpr (kSplit) {
-                    u[r] = mfma16(th, xbl[s], u[r]);
-                    u[r] = mfma16(lds_frag_b(tls + tri_block(r, s) * 1024 + 16 * lane), xb[s], u[r]);
+                    u[r] = mfma16(th[tri_block(r, s)], xbl[s], u[r]);
+                    u[r] = mfma16(thl[tri_block(r, s)], xb[s], u[r]);
                 }
             }
         }
+        // the scaled old state, off the dependency chain
+        f32x4 sacc[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sacc[t][j] = egC * S[t][j];
         if constexpr (outputs) {
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -767,11 +856,9 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int gr
         {
             f32x4 w[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const f32x4 e4 = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) w[r][j] = e4[j] * u[r][j];
-            }
+                for (int j = 0; j < 4; ++j) w[r][j] = egc[r][j] * u[r][j];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 if constexpr (kSplit) pack_frag_split(w[2 * s], w[2 * s + 1], vb[s], vbl[s]);
@@ -779,23 +866,17 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int gr
             }
         }
         // S <- exp(Gam_C) S + K^T V'': state tiles t, token k-steps s
-        const float egC = gs[63];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            f32x4 acc;
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = egC * S[t][j];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int o0 = 8 * s * 1024 + 256 * (t >> 1) + 8 * (t & 1) + tr_lane;
-                const u32x2 lo = lds_read_tr(ks + o0);
-                const u32x2 hi = lds_read_tr(ks + o0 + 4 * 1024);
-                const bf16x8 kt = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                acc = mfma16(kt, vb[s], acc);
-                if constexpr (kSplit) acc = mfma16(kt, vbl[s], acc);
+            for (int t = 0; t < 8; ++t) {
+                const bf16x8 kt = __builtin_bit_cast(
+                    bf16x8, u32x4{ktr[t][s][0][0], ktr[t][s][0][1], ktr[t][s][1][0], ktr[t][s][1][1]});
+                sacc[t] = mfma16(kt, vb[s], sacc[t]);
+                if constexpr (kSplit) sacc[t] = mfma16(kt, vbl[s], sacc[t]);
             }
-            S[t] = acc;
-        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = sacc[t];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             if constexpr (kSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
@@ -818,16 +899,17 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int gr
 }  // namespace
 
 hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.NT));
+    const int64_t pairs = static_cast<int64_t>(a.B) * a.NT;
+    const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * a.H));
     void* args[] = {const_cast<PrepArgs*>(&a)};
     return hipLaunchKernel(reinterpret_cast<const void*>(&prep_mfma), grid, dim3(256), args, 0, s);
 }
 
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
     int tiles = a.ncols / 16;
-    int groups = a.H * a.B * a.P;
-    const unsigned nblk = static_cast<unsigned>(((groups + 7) / 8) * 8 * tiles);
-    void* args[] = {const_cast<StateArgs*>(&a), &tiles, &groups};
+    int qk_groups = a.Hqk * a.B * a.P;
+    const unsigned nblk = static_cast<unsigned>(((qk_groups + 7) / 8) * 8 * (a.H / a.Hqk) * tiles);
+    void* args[] = {const_cast<StateArgs*>(&a), &tiles, &qk_groups};
     // Without values (the summary matrix M) the pass runs with split operands.
     const void* fn = !a.v ? reinterpret_cast<const void*>(&state_mfma<false, true, false>)
                    : a.o  ? reinterpret_cast<const void*>(&state_mfma<true, false, true>)
