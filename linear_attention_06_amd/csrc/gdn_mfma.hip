@@ -8,21 +8,17 @@
 //   That = Tinv diag(beta),  P_ij = (q_i.k_j) exp(Gam_i - Gam_j) (j <= i)
 //   X  = V - diag(exp Gam) K S          U = That X            (delta-rule errors)
 //   O  = diag(exp Gam) Q S + P U        S' = exp(Gam_C) S + K^T diag(exp(Gam_C - Gam)) U
-// All contractions run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the
-// state stays fp32 and is rounded to bf16 only as an MFMA operand. The
-// triangular solve stays fp32 (VALU substitution on the 16x16 diagonal blocks,
-// v_mfma_f32_16x16x4_f32 for the off-diagonal blocks).
+// The contractions run on bf16 MFMAs with fp32 accumulation; the state stays fp32
+// and is rounded to bf16 only as an MFMA operand. The triangular solve stays fp32
+// (column sweep on the 16x16 diagonal blocks, v_mfma_f32_16x16x4_f32 for the
+// off-diagonal blocks).
 //
-// MFMA operand layouts used below (lane l, q = l / 32, r = l % 32):
-//   32x32x16 A: row r, k = 8q .. 8q+7;  B: col r, k = 8q .. 8q+7;
-//   C/D: 16 fp32, register i holds row 8(i/4) + 4q + (i%4), col r.
-//   16x16x4 f32 A: row l%16, k = l/16;  B: col l%16, k = l/16;  C: rows 4(l/16)+i, col l%16.
-// A 32x32 C tile feeds the next MFMA as its B operand without leaving the
-// registers if the contraction index of k-step h (rows 16h..16h+15 of the tile)
-// is ordered so that k-slot 8q + u stands for row 16h + 4q + 8(u/4) + u%4. Every
-// operand that is contracted against such a tile is stored in LDS with its
-// contraction index permuted the same way inside each 16-block (swap of index
-// bits 2 and 3), so that each lane still reads one 16-byte fragment.
+// MFMA operand layouts used below (lane l):
+//   32x32x16 bf16 (prepare pass), q = l / 32, r = l % 32: A row r, k = 8q .. 8q+7;
+//     B col r, k = 8q .. 8q+7; C register i holds row 8(i/4) + 4q + (i%4), col r.
+//   16x16x32 bf16 (state pass), g = l / 16: A row l%16, k = 8g .. 8g+7; B col l%16,
+//     k = 8g .. 8g+7; C register j holds row 4g + j, col l%16.
+//   16x16x4 f32: A row l%16, k = l/16;  B col l%16, k = l/16;  C rows 4(l/16)+j, col l%16.
 #include "gdn_internal.hpp"
 
 namespace gdn {
@@ -35,7 +31,6 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int DK = 128;
-constexpr int KP = DK + 8;   // LDS pitch (bf16) of 128-wide rows: 272 B, conflict-free fragment reads
 constexpr int CP = 64 + 8;   // LDS pitch (bf16) of 64-wide rows: 144 B
 // That and P leave the prepare kernel as the 6 lower-triangle 16x32 blocks (r, s),
 // s <= r / 2, of 64 lanes x 8 bf16 each; block (r, s) sits at position tri_block(r, s).
@@ -65,13 +60,6 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-// Eight fp32 values (registers i0 .. i0+7 of a C tile) as a bf16 B fragment.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int i0) {
-    bf16x8 f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) f[u] = static_cast<__bf16>(v[i0 + u]);
-    return f;
-}
 // Workgroup barrier that orders LDS only. __syncthreads() also waits for every
 // outstanding global load and store of the wave, which would stall the loads
 // issued one chunk ahead at every barrier; the waves here exchange data through
@@ -81,20 +69,7 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-// Barrier for the state pass: LDS writes of this wave complete, then s_barrier.
-// Written as one asm statement with a memory clobber (so the compiler keeps LDS
-// accesses on their side of it) instead of a fence, because a fence would also wait
-// for the direct-to-LDS loads of the next chunk that are meant to stay in flight.
-__device__ __forceinline__ void stage_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Position of index x inside its 16-block after swapping bits 2 and 3.
-__device__ __forceinline__ int perm16(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-// Writes 8 consecutive bf16 (natural index 8*h8 .. 8*h8+7 inside a 16-block that
-// starts at base) in permuted order: two 8-byte pieces.
-__device__ __forceinline__ void store8_perm(uint16_t* row, int base16, int h8, u32x4 w) {
-    *reinterpret_cast<u32x2*>(row + base16 + 4 * h8) = u32x2{w[0], w[1]};
-    *reinterpret_cast<u32x2*>(row + base16 + 8 + 4 * h8) = u32x2{w[2], w[3]};
-}
 
 // ----------------------------------------------------------------------------
 // Prepare: one block of 4 waves per (b, h, chunk).
