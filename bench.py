@@ -10,7 +10,7 @@ Prints one JSON line with the throughput, the roofline of the dominant kernel
 (its average duration measured with HIP events on the stream it runs on) and
 the fp64 CPU oracle timed on this host.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
 """
 import argparse
@@ -98,6 +98,81 @@ def cpu_baseline(inp, budget_s=30.0):
                       % (heads, w.H, w.T, w.B, dt)}
 
 
+def segmented_timing(gdn, q, k, v, g, beta, h0, stream, timed):
+    """The stateful sequence cut into 8 segments of 4096 tokens: per-segment summary (M, S),
+    prefix combine, then the outputs of every segment from its incoming state."""
+    seg_len = 4096
+    p = gdn.problem(q, v)
+    ws = gdn.workspace(gdn.gdn_segment_workspace(p, seg_len), q.device)
+    B, T, H = v.shape[0], v.shape[1], v.shape[2]
+    P = T // seg_len
+    M = torch_empty((B, H, P, p.dk, p.dk), q.device)
+    S = torch_empty((B, H, P, p.dk, p.dv), q.device)
+    H_in = torch_empty((B, H, P, p.dk, p.dv), q.device)
+    hT = torch_empty((B, H, p.dk, p.dv), q.device)
+    o = torch_empty_like_v(v)
+
+    def summary():
+        gdn.gdn_segment_summary(q, k, v, g, beta, seg_len, M=M, S=S, ws=ws, stream=stream)
+
+    def combine():
+        gdn.gdn_summary_combine(M, S, h0, H_in=H_in, hT=hT, stream=stream)
+
+    def apply():
+        gdn.gdn_apply_initial_state(q, k, v, g, beta, H_in, seg_len, ws, o=o, hT=hT, stream=stream)
+
+    def whole():
+        summary()
+        combine()
+        apply()
+
+    res = {"segments": P, "seg_len": seg_len, "summary_ms": timed(summary, 5),
+           "combine_ms": timed(combine, 5), "apply_ms": timed(apply, 5), "step_ms": timed(whole, 5)}
+    res["tokens_per_s"] = B * T / (res["step_ms"] * 1e-3)
+    return res
+
+
+def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
+    """gdn_chunk_fwd step time on the stateless 8K and padded 8K workloads."""
+    import torch
+
+    out = {}
+    for name in ("stateless_8k", "padded_8k"):
+        w = workloads[name]
+        inp = make_inputs(w)
+
+        def io(x):
+            return torch.from_numpy(np.ascontiguousarray(x)).view(torch.int16).view(torch.bfloat16).to(dev)
+
+        q, k, v = io(inp.q), io(inp.k), io(inp.v)
+        g = torch.from_numpy(inp.g).to(dev)
+        beta = torch.from_numpy(inp.beta).to(dev)
+        vl = None if inp.valid_len is None else torch.from_numpy(inp.valid_len).to(dev)
+        p = gdn.problem(q, v, vl)
+        ws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
+        o = torch.empty_like(v)
+        hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+        def step():
+            gdn.gdn_chunk_fwd(q, k, v, g, beta, None, valid_len=vl, o=o, hT=hT, ws=ws, stream=stream)
+
+        ms = timed(step, 10)
+        out[name] = {"B": w.B, "T": w.T, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
+    return out
+
+
+def torch_empty(shape, dev):
+    import torch
+
+    return torch.empty(shape, dtype=torch.float32, device=dev)
+
+
+def torch_empty_like_v(v):
+    import torch
+
+    return torch.empty_like(v)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +180,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the segmented-path and other-workload timings")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
@@ -152,15 +229,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # events between the steps give per-step durations without any synchronisation
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for i in range(args.steps):
         step()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    step_stats = {"median": per_step[len(per_step) // 2], "min": per_step[0],
+                  "p90": per_step[min(len(per_step) - 1, int(0.9 * len(per_step)))]}
 
     # Per-kernel durations. The prepare kernel alone: the segment summary with a
     # single segment and no outputs runs only the prepare pass into the workspace.
@@ -219,8 +300,13 @@ def main():
                      "traffic": recorded_traffic(dominant), "traffic_unit": "bytes/launch",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "kernel_ms": dom_ms},
+        "step_ms_stats": step_stats,
+        "workspace_bytes": int(ws.numel()),
         "wall_s_timed_region": wall,
     }
+    if not args.no_extra:
+        line["segmented_32k"] = segmented_timing(gdn, q, k, v, g, beta, h0, stream, timed)
+        line["other_workloads"] = other_workloads(gdn, WORKLOADS, make_inputs, dev, stream, timed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line))

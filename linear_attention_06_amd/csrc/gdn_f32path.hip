@@ -231,12 +231,17 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
 }
 
 // X_p = M_p X_{p-1} + S_p over the segments of one (b, h), 16 columns per block.
+// Thread t < 2 dk owns row t / 2 and columns 8 (t % 2) .. +7 of the 16: it streams
+// row t / 2 of M_p once per step with 16-byte loads against X_{p-1} held in LDS.
+// fp32 throughout (the summary products must stay accurate).
+template <int DKT>
 __global__ __launch_bounds__(256) void affine_scan(ScanArgs a) {
     constexpr int BV = 16;
-    extern __shared__ float x_s[];       // [dk][BV]
+    constexpr int dk = DKT;
+    __shared__ float x_s[DKT * BV];
     const int col0 = blockIdx.x * BV;
     const int h = blockIdx.y, b = blockIdx.z;
-    const int dk = a.dk, ncols = a.ncols;
+    const int ncols = a.ncols;
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     const int64_t tile = static_cast<int64_t>(dk) * ncols;
     const int tid = threadIdx.x;
@@ -249,41 +254,48 @@ __global__ __launch_bounds__(256) void affine_scan(ScanArgs a) {
         x_s[e] = x0;
     }
     __syncthreads();
-    float acc[8];
-    const int per = (dk * BV + 255) / 256;   // outputs per thread (<= 8)
+    const bool active = tid < 2 * dk;
+    const int i = tid >> 1, c0 = 8 * (tid & 1);
+    const int64_t out0 = static_cast<int64_t>(i) * ncols + col0 + c0;   // this thread's 8 outputs
     for (int p = 0; p < a.P; ++p) {
         const int64_t blk = bh * a.P + p;
-        const float* M = a.M + blk * static_cast<int64_t>(dk) * dk;
-        for (int m = 0; m < per; ++m) {
-            const int e = tid + m * 256;
-            acc[m] = 0.f;
-            if (e < dk * BV) {
-                const int i = e / BV, c = e % BV;
-                if (a.x_before) a.x_before[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = x_s[e];
-                float s = a.S ? a.S[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] : 0.f;
-                float dot = 0.f;
-                for (int l = 0; l < dk; ++l) dot += M[static_cast<int64_t>(i) * dk + l] * x_s[l * BV + c];
-                acc[m] = dot + s;
-            }
-        }
-        __syncthreads();
-        for (int m = 0; m < per; ++m) {
-            const int e = tid + m * 256;
-            if (e < dk * BV) {
-                x_s[e] = acc[m];
-                if (a.x_after) {
-                    const int i = e / BV, c = e % BV;
-                    a.x_after[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = acc[m];
+        float acc[8];
+        if (active) {
+            if (a.x_before)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) a.x_before[blk * tile + out0 + c] = x_s[i * BV + c0 + c];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = a.S ? a.S[blk * tile + out0 + c] : 0.f;
+            const float4* mrow = reinterpret_cast<const float4*>(a.M + blk * static_cast<int64_t>(dk) * dk +
+                                                                 static_cast<int64_t>(i) * dk);
+            float4 mr[dk / 4];   // the whole row in flight at once
+#pragma unroll
+            for (int l4 = 0; l4 < dk / 4; ++l4) mr[l4] = mrow[l4];
+#pragma unroll
+            for (int l4 = 0; l4 < dk / 4; ++l4) {
+                const float4 m4 = mr[l4];
+                const float mv[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float* xr = x_s + (4 * l4 + u) * BV + c0;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[c] += mv[u] * xr[c];
                 }
             }
         }
         __syncthreads();
-    }
-    if (a.x_final) {
-        for (int e = tid; e < dk * BV; e += 256) {
-            const int i = e / BV, c = e % BV;
-            a.x_final[bh * tile + static_cast<int64_t>(i) * ncols + col0 + c] = x_s[e];
+        if (active) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                x_s[i * BV + c0 + c] = acc[c];
+                if (a.x_after) a.x_after[blk * tile + out0 + c] = acc[c];
+            }
         }
+        __syncthreads();
+    }
+    if (a.x_final && active) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a.x_final[bh * tile + out0 + c] = x_s[i * BV + c0 + c];
     }
 }
 
@@ -332,8 +344,15 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H),
                     static_cast<unsigned>(a.B));
     void* args[] = {const_cast<ScanArgs*>(&a)};
-    const size_t lds = static_cast<size_t>(a.dk) * 16 * sizeof(float);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&affine_scan), grid, dim3(256), args, lds, s);
+    const void* fn = nullptr;
+    switch (a.dk) {
+        case 16: fn = reinterpret_cast<const void*>(&affine_scan<16>); break;
+        case 32: fn = reinterpret_cast<const void*>(&affine_scan<32>); break;
+        case 64: fn = reinterpret_cast<const void*>(&affine_scan<64>); break;
+        case 128: fn = reinterpret_cast<const void*>(&affine_scan<128>); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
 }
 
 }  // namespace gdn
