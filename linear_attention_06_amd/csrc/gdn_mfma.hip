@@ -485,11 +485,15 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
     const int first_loader = outputs ? 2 : 1;
-    // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule
-    // (row 4j + rho, dk 32s + 8g .. +7) at 16-byte slot 16 s + ((4 (j % 4) + rho) ^ 4g).
-    // A direct load fills one quad block from 4 whole rows; the fragment reads and the
-    // transposing reads below are free of bank conflicts.
-    const int frag_lane = (l16 >> 2) * 1024 + 16 * (l16 ^ (4 * g4));   // + 4096 r + 256 s: fragment (r, s)
+    // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
+    // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 (j % 4) + rho)). A direct load fills one
+    // quad block with 16 lanes per row, so that each group of 4 lanes reads one 64-byte piece
+    // (lanes of a quad spread over different rows cost the load path 3x as much); the
+    // fragment reads and the transposing reads below are free of bank conflicts.
+    // Fragment (r, s) of lane (l16, g4): byte 4096 r + frag_lane[s].
+    int frag_lane[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) frag_lane[s] = (l16 >> 2) * 1024 + 256 * (l16 & 3) + 16 * ((4 * s + g4) ^ l16);
 
     if (wave >= first_loader) {
         // ---------------- loading waves ----------------
@@ -509,12 +513,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             rec);
         const u32x4 rgt = make_desc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
 
-        // lane l of a quad-block load: slot l = 16 s + c, row 4j + (c & 3), granule g = (c >> 2) ^ (j & 3)
+        // lane l of a quad-block load: slot l = 16 rho + c, row 4j + rho, granule c ^ (4 (j % 4) + rho)
         uint32_t voff_k[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-            voff_k[jj] = static_cast<uint32_t>(((lane & 3) * qk_row + hq * DK + 32 * (lane >> 4) +
-                                                8 * (((lane >> 2) & 3) ^ jj)) * 2);
+            voff_k[jj] = static_cast<uint32_t>(((lane >> 4) * qk_row + hq * DK +
+                                                8 * ((lane & 15) ^ (4 * jj + (lane >> 4)))) * 2);
         const uint32_t voff_l = static_cast<uint32_t>(16 * lane);
         uint32_t voff_v[2];
 #pragma unroll
@@ -662,8 +666,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 f32x4 o0 = zero4(), o1 = zero4();
 #pragma unroll
                 for (int s = 0; s < 4; s += 2) {
-                    o0 = mfma16(sb[s], lds_frag_b(qs + r * 4096 + s * 256 + frag_lane), o0);
-                    o1 = mfma16(sb[s + 1], lds_frag_b(qs + r * 4096 + (s + 1) * 256 + frag_lane), o1);
+                    o0 = mfma16(sb[s], lds_frag_b(qs + r * 4096 + frag_lane[s]), o0);
+                    o1 = mfma16(sb[s + 1], lds_frag_b(qs + r * 4096 + frag_lane[s + 1]), o1);
                 }
                 const float e = gs[16 * r + l16];
                 f32x4 o;
@@ -711,8 +715,11 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     }
     // Transposing reads of K: lane (c, g) of k-step s, half hf reads the 8-byte piece of
     // token 32s + 16hf + 4g + c / 4 at dk 32 (t / 2) + 8 (c % 4) + 4 (t % 2): quad block
-    // 8s + 4hf + g, slot 16 (t / 2) + ((4g + c / 4) ^ 4 (c % 4)), byte 8 (t % 2).
-    const int tr_lane = g4 * 1024 + 16 * ((4 * g4 + (l16 >> 2)) ^ (4 * (l16 & 3)));
+    // 8s + 4hf + g, row c / 4 in it, granule 4 (t / 2) + c % 4, byte 8 (t % 2) of the granule.
+    int tr_lane[4];
+#pragma unroll
+    for (int th = 0; th < 4; ++th)
+        tr_lane[th] = g4 * 1024 + 256 * (l16 >> 2) + 16 * ((4 * th + (l16 & 3)) ^ (4 * g4 + (l16 >> 2)));
     const int v_lane = 2 * (16 * (4 * g4 + (l16 >> 2)) + 4 * (l16 & 3));
 
     for (int n = n0; n <= n1; ++n) {
@@ -728,7 +735,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // Phase 0: every LDS operand of K S, X and U, read at once.
         bf16x8 kf[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) kf[i] = lds_frag_b(ks + (i >> 2) * 4096 + (i & 3) * 256 + frag_lane);
+        for (int i = 0; i < 16; ++i) kf[i] = lds_frag_b(ks + (i >> 2) * 4096 + frag_lane[i & 3]);
         f32x4 eg[4];
         u32x2 vraw[4];
 #pragma unroll
@@ -742,6 +749,10 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             th[j] = lds_frag_b(ts + j * 1024 + 16 * lane);
             if constexpr (kSplit) thl[j] = lds_frag_b(tls + j * 1024 + 16 * lane);
         }
+        f32x4 egc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) egc[r] = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
+        const float egC = gs[63];
         __builtin_amdgcn_sched_barrier(0);
 
         // Phase 1: K S for token tiles r (two accumulators per tile, k-steps interleaved
@@ -767,20 +778,6 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 }
             }
         }
-        // the transposing reads of K for the state update go out while K S runs
-        u32x2 ktr[8][2][2];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int o0 = 8 * s * 1024 + 256 * (t >> 1) + 8 * (t & 1) + tr_lane;
-                ktr[t][s][0] = lds_read_tr(ks + o0);
-                ktr[t][s][1] = lds_read_tr(ks + o0 + 4 * 1024);
-            }
-        f32x4 egc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) egc[r] = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
-        const float egC = gs[63];
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (outputs) {
 #pragma unroll
@@ -815,6 +812,20 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // The transposing reads of K for the state update go out once U is issued. Issued
+        // earlier they would sit ahead of the That reads in the LDS counter, which counts
+        // at most 15 outstanding reads, and U would wait for them.
+        u32x2 ktr[8][2][2];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int o0 = 8 * s * 1024 + 8 * (t & 1) + tr_lane[t >> 1];
+                ktr[t][s][0] = lds_read_tr(ks + o0);
+                ktr[t][s][1] = lds_read_tr(ks + o0 + 4 * 1024);
+            }
+        __builtin_amdgcn_sched_barrier(0);
         // the scaled old state, off the dependency chain
         f32x4 sacc[8];
 #pragma unroll
