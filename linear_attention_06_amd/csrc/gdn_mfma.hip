@@ -359,6 +359,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+template <int V>
+struct IntTag {
+    static constexpr int value = V;
+};
 // Two accumulator tiles (4 rows each per lane) as one bf16 B fragment.
 __device__ __forceinline__ bf16x8 pack_frag(const f32x4& a, const f32x4& b) {
     bf16x8 f;
@@ -525,12 +529,17 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         for (int m = 0; m < 2; ++m)
             voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * vo_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
         const uint32_t kbase = lds_addr(kst), qbase = lds_addr(qst), gbase = lds_addr(gst);
-        const int me = wave - first_loader;
         constexpr int nl = 8 - (outputs ? 2 : 1);
         constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + (kHasV ? 2 : 0) + 1;
         constexpr int NQ = outputs ? 22 : 0;
         constexpr int NI = NK + NQ;   // loads of one full iteration, dealt round-robin over the loading waves
 
+        // The loads are dealt round-robin over the loading waves; the loop below is
+        // compiled once per wave index, so that each wave runs its own loads as
+        // straight-line code (a compare-and-branch per load slot costs the loading waves
+        // a large share of their time).
+        auto loader = [&](auto me_tag) {
+        constexpr int me = decltype(me_tag)::value;
         // K-side operands of chunk n into stage buffer n % 3 (decay factors into ring slot n % 4)
         auto issue_k = [&](int n) {
             const uint32_t dst = kbase + static_cast<uint32_t>((n % 3) * KSB);
@@ -572,12 +581,10 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // iteration n needs the loads issued in iteration n - 2, so each wave first waits
         // until no more than its share of iteration n - 1 is outstanding (loads of one
         // wave complete in order). A partial set (near the end) waits for everything.
-        constexpr int cnt_hi = NI / nl + 1, cnt_lo = NI / nl;
-        const bool hi_share = me < NI % nl;
+        constexpr int cnt = NI / nl + (me < NI % nl ? 1 : 0);
         auto wait_older = [&](bool full) {
             if (!full) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else if (hi_share) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(cnt_hi) : "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(cnt_lo) : "memory");
+            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(cnt) : "memory");
         };
         auto issue_iter = [&](int m) {   // the loads of iteration m
             if (m + 2 < n1) issue_k(m + 2);
@@ -589,6 +596,16 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             wait_older(n + 1 < n1);
             chunk_barrier(false);
             issue_iter(n);
+        }
+        };
+        switch (wave - first_loader) {
+            case 0: loader(IntTag<0>{}); break;
+            case 1: loader(IntTag<1>{}); break;
+            case 2: loader(IntTag<2>{}); break;
+            case 3: loader(IntTag<3>{}); break;
+            case 4: loader(IntTag<4>{}); break;
+            case 5: loader(IntTag<5>{}); break;
+            default: if constexpr (nl > 6) loader(IntTag<6>{}); break;
         }
         __builtin_amdgcn_s_waitcnt(0);
         return;
@@ -755,28 +772,20 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const float egC = gs[63];
         __builtin_amdgcn_sched_barrier(0);
 
-        // Phase 1: K S for token tiles r (two accumulators per tile, k-steps interleaved
-        // across tiles so that no MFMA waits for the previous one).
-        f32x4 c0[4], c1[4];
+        // Phase 1: K S for token tiles r, one accumulator per tile; the k-steps go
+        // round the four tiles, so each MFMA's predecessor on its tile is four back.
+        f32x4 c0[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            c0[r] = mfma16(kf[4 * r], sb[0], zero4());
-            c1[r] = mfma16(kf[4 * r + 1], sb[1], zero4());
-        }
+        for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * r], sb[0], zero4());
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            c0[r] = mfma16(kf[4 * r + 2], sb[2], c0[r]);
-            c1[r] = mfma16(kf[4 * r + 3], sb[3], c1[r]);
-        }
+        for (int s = 1; s < 4; ++s)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * r + s], sb[s], c0[r]);
         if constexpr (kSplit) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int s = 0; s < 4; s += 2) {
-                    c0[r] = mfma16(kf[4 * r + s], sbl[s], c0[r]);
-                    c1[r] = mfma16(kf[4 * r + s + 1], sbl[s + 1], c1[r]);
-                }
-            }
+                for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * r + s], sbl[s], c0[r]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (outputs) {
@@ -790,7 +799,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         for (int r = 0; r < 4; ++r) {
             const f32x4 v4 = kHasV ? bf16x4_to_f32(vraw[r]) : zero4();
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[r][j] = v4[j] - eg[r][j] * (c0[r][j] + c1[r][j]);
+            for (int j = 0; j < 4; ++j) x[r][j] = v4[j] - eg[r][j] * c0[r][j];
         }
         bf16x8 xb[2], xbl[2];
 #pragma unroll
