@@ -127,6 +127,11 @@ SMALL = [
     ("bf16_d64", "bf16", 1, 300, 2, 4, 64, 64),
     ("bf16_one_token", "bf16", 1, 1, 1, 2, 128, 128),
     ("bf16_tail_only", "bf16", 1, 63, 2, 2, 128, 128),
+    # matrix-core path with fewer than 8 column tiles per head, value/query-key head
+    # ratios 1 and 3 and batch rows that leave the block grid's last XCD slots empty
+    ("bf16_dv16_ratio3", "bf16", 1, 260, 1, 3, 128, 16),
+    ("bf16_dv32_ratio1_B3", "bf16", 3, 190, 3, 3, 128, 32),
+    ("bf16_dv64_B2", "bf16", 2, 700, 2, 4, 128, 64),
 ]
 
 
@@ -220,6 +225,24 @@ def test_slow_decay_segments_exercise_the_combine():
     assert_close(np_f64(S), S_ref, TOL_BF16, "slow S")
     assert_close(np_f64(o), o_ref, TOL_BF16, "slow o")
     assert_close(np_f64(hT), hT_ref, TOL_BF16, "slow hT")
+
+
+def test_summary_bf16_narrow_heads_matches_oracle():
+    """Segment calls on the matrix-core path with dv = 32 and three value heads per
+    query/key head: summaries, prefix products, combine and apply against the oracle."""
+    inp = small_inputs("seg_bf16_dv32", "bf16", 1, 512, 1, 3, 128, 32, seed=8)
+    q64, k64, v64, g64, b64, h064 = inp.f64()
+    M_ref, S_ref = oracle.gdn_segment_summary(q64, k64, v64, g64, b64, 128)
+    Hin_ref, Mp_ref, hTc_ref = oracle.gdn_summary_combine(M_ref, S_ref, h064, want_prefix=True)
+    o_ref, hT_ref = oracle.gdn_apply_initial_state(q64, k64, v64, g64, b64, Hin_ref, 128)
+    q, k, v, g, beta, h0, _ = to_dev(inp)
+    M, S, ws = gdn.gdn_segment_summary(q, k, v, g, beta, 128)
+    H_in, Mp, hTc = gdn.gdn_summary_combine(M, S, h0, want_prefix=True)
+    o, hT = gdn.gdn_apply_initial_state(q, k, v, g, beta, H_in, 128, ws)
+    sync()
+    for x, r, n in ((M, M_ref, "M"), (S, S_ref, "S"), (H_in, Hin_ref, "H_in"), (Mp, Mp_ref, "M_prefix"),
+                    (hTc, hTc_ref, "combined hT"), (o, o_ref, "o"), (hT, hT_ref, "hT")):
+        assert_close(np_f64(x), r, TOL_BF16, "bf16 dv32 segments " + n)
 
 
 def test_summary_f32_small_matches_oracle():
