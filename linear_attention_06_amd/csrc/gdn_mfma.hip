@@ -410,14 +410,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
     const int32_t n = static_cast<int32_t>(bytes < 0 ? 0 : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
 }
-// Raw buffer descriptor (base, range in bytes) as four uniform words.
-__device__ __forceinline__ u32x4 make_desc(const void* base, int64_t bytes) {
-    const uint64_t p = reinterpret_cast<uint64_t>(base);
-    const uint32_t n = static_cast<uint32_t>(bytes < 0 ? 0 : bytes);
-    const auto rfl = [](uint32_t x) { return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(x)); };
-    return u32x4{rfl(static_cast<uint32_t>(p)), rfl(static_cast<uint32_t>(p >> 32) & 0xFFFFu), rfl(n),
-                 static_cast<uint32_t>(kBufferFlags)};
-}
 // LDS byte address of a __shared__ object.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #pragma clang diagnostic push
@@ -425,39 +417,50 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
 #pragma clang diagnostic pop
 }
-// Direct global-to-LDS load of 16 bytes per lane from byte voff + soff of the
-// buffer: lane l writes LDS byte address lds + 16 l (lds wave-uniform). Issued as asm
-// so that the compiler does not make LDS reads of other buffers wait for it; the
-// loading waves wait for these loads explicitly before the chunk barrier.
-__device__ __forceinline__ void lds_dma16(const u32x4& desc, uint32_t lds, uint32_t voff, uint32_t soff) {
-    const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(lds));
-    const uint32_t so = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(soff));
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0v), "v"(voff), "s"(desc),
-                 "s"(so)
-                 : "memory", "m0");
+// 16-byte load per lane from byte voff + soff of a buffer into registers.
+__device__ __forceinline__ u32x4 gload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-// Barrier of the state pass: this wave's LDS accesses complete, then s_barrier.
-// The loading waves first wait for their direct loads (vm_wait). One asm statement
-// with a memory clobber, so the compiler keeps LDS accesses on their side of it.
+// Barrier of the state pass: this wave's LDS accesses complete, then s_barrier
+// (optionally after all of its vector-memory accesses). One asm statement with a
+// memory clobber, so the compiler keeps LDS accesses on their side of it.
 __device__ __forceinline__ void chunk_barrier(bool vm_wait) {
     if (vm_wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Loading wave (index among the loading waves) that issues load g of an iteration.
+// Waves w and w + 4 of a workgroup run on the same SIMD, and the rate at which one
+// SIMD issues direct loads bounds the loading; the deal gives every SIMD the same
+// share. With outputs, waves 0 and 1 (chain, output) each share their SIMD with one
+// loading wave (indices 2 and 3), which take two of every eight loads; otherwise
+// wave 0 shares its SIMD with loading wave 3.
+__host__ __device__ constexpr int load_owner(bool with_outputs, int g) {
+    const int p = g & 7;
+    if (with_outputs) return (p == 0 || p == 3) ? 2 : (p == 1 || p == 4) ? 3 : (p == 2) ? 0 : (p == 5) ? 1 : (p == 6) ? 4 : 5;
+    return p == 0 ? 3 : p - 1;
+}
+__host__ __device__ constexpr int loads_owned(bool with_outputs, int n, int me) {
+    int c = 0;
+    for (int g = 0; g < n; ++g) c += load_owner(with_outputs, g) == me ? 1 : 0;
+    return c;
 }
 
 template <bool kHasV, bool kSplit, bool kOut>
 __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk_groups) {
     constexpr bool outputs = kHasV && kOut;
     // K-side stage buffer: K, That, That remainder (split), V; Q-side: Q, P.
-    // K-side operands are loaded two chunks ahead (three buffers), Q-side operands
-    // one chunk ahead of the output wave, which runs one chunk behind (three buffers);
-    // the decay factors of a chunk live from their load to the output wave (ring of four).
+    // K-side operands of chunk n are written in iteration n - 1 and read in iteration
+    // n; Q-side operands in iteration n and read by the output wave, which runs one
+    // chunk behind, in iteration n + 1 (two buffers each); the decay factors of a
+    // chunk live from their write to the output wave (ring of four).
     constexpr int KB = 64 * DK * 2, TB = kTriRecord * 2, LB = kSplit ? kTriRecord * 2 : 0;
     constexpr int VB = kHasV ? 64 * 16 * 2 : 0;
     constexpr int KSB = KB + TB + LB + VB;
     constexpr int QSB = outputs ? KB + TB : 0;
     constexpr int HB = 6 * 1024;   // hand-off: S fragments (4 blocks), U fragments (2 blocks)
-    __shared__ __align__(16) unsigned char kst[3 * KSB];
-    __shared__ __align__(16) unsigned char qst[outputs ? 3 * QSB : 16];
+    __shared__ __align__(16) unsigned char kst[2 * KSB];
+    __shared__ __align__(16) unsigned char qst[outputs ? 2 * QSB : 16];
     __shared__ __align__(16) unsigned char gst[4 * 1024];
     __shared__ __align__(16) unsigned char hst[outputs ? 2 * HB : 16];
     __shared__ __align__(16) unsigned char pf_s[outputs ? 256 : 16];   // sink of the L2 prefetches
@@ -506,16 +509,16 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const uint16_t* kin = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(b) * a.T * qk_row;
         const uint16_t* qin = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.T * qk_row;
         const uint16_t* vin = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(b) * a.T * vo_row;
-        const u32x4 rk = make_desc(kin, nvalid * qk_row * 2);
-        const u32x4 rq = make_desc(outputs ? qin : kin, nvalid * qk_row * 2);
-        const u32x4 rv = make_desc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin, nvalid * qk_row * 2);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(outputs ? qin : kin, nvalid * qk_row * 2);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
         const int64_t rec = static_cast<int64_t>(a.NT) * kTriRecord * 2;   // bytes of one head's records
-        const u32x4 rth = make_desc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * kTriRecord, rec);
-        const u32x4 rpm = make_desc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * kTriRecord, rec);
-        const u32x4 rtl = make_desc(
+        const __amdgpu_buffer_rsrc_t rth = make_rsrc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * kTriRecord, rec);
+        const __amdgpu_buffer_rsrc_t rpm = make_rsrc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * kTriRecord, rec);
+        const __amdgpu_buffer_rsrc_t rtl = make_rsrc(
             kSplit ? static_cast<const uint16_t*>(a.ws.that_lo) + bh * a.NT * kTriRecord : static_cast<const uint16_t*>(a.ws.that),
             rec);
-        const u32x4 rgt = make_desc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
+        const __amdgpu_buffer_rsrc_t rgt = make_rsrc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
 
         // lane l of a quad-block load: slot l = 16 rho + c, row 4j + rho, granule c ^ (4 (j % 4) + rho)
         uint32_t voff_k[4];
@@ -528,75 +531,112 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 #pragma unroll
         for (int m = 0; m < 2; ++m)
             voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * vo_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
-        const uint32_t kbase = lds_addr(kst), qbase = lds_addr(qst), gbase = lds_addr(gst);
         constexpr int nl = 8 - (outputs ? 2 : 1);
         constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + (kHasV ? 2 : 0) + 1;
         constexpr int NQ = outputs ? 22 : 0;
-        constexpr int NI = NK + NQ;   // loads of one full iteration, dealt round-robin over the loading waves
+        constexpr int NI = NK + NQ;   // 1 KiB loads of one full iteration
+        static_assert(nl >= 6, "loading waves");
 
-        // The loads are dealt round-robin over the loading waves; the loop below is
-        // compiled once per wave index, so that each wave runs its own loads as
-        // straight-line code (a compare-and-branch per load slot costs the loading waves
-        // a large share of their time).
+        // Each 1 KiB load (lane l: 16 bytes, written to LDS at 16 l of its block) goes
+        // through registers. In iteration n a loading wave writes to LDS what it loaded
+        // in iteration n - 2 (the K-side operands of chunk n + 1 and the Q-side operands
+        // of chunk n) and then loads the K-side operands of chunk n + 3 and the Q-side
+        // operands of chunk n + 2: under the full load of the chip a load takes about
+        // one iteration to return, so two iterations of loads are in flight. Each
+        // operand spends a single iteration in LDS (two buffers per side).
+        // The loads are dealt over the loading waves by load_owner; the loop below is
+        // compiled once per wave index and unrolled by two, so that each wave runs its
+        // own loads as straight-line code with its registers indexed at compile time.
         auto loader = [&](auto me_tag) {
         constexpr int me = decltype(me_tag)::value;
-        // K-side operands of chunk n into stage buffer n % 3 (decay factors into ring slot n % 4)
-        auto issue_k = [&](int n) {
-            const uint32_t dst = kbase + static_cast<uint32_t>((n % 3) * KSB);
+        constexpr int NS = loads_owned(outputs, NI, me);
+        using Stage = u32x4[NS > 0 ? NS : 1];
+        Stage st0, st1;   // loads of even / odd iterations (relative to n0)
+        auto load_k = [&](int n, Stage& stage) {   // K-side operands of chunk n
             const uint32_t tr = static_cast<uint32_t>(n) * (kTriRecord * 2);
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
-                if (i % nl != me) continue;
+                if (load_owner(outputs, i) != me) continue;
+                u32x4& r = stage[loads_owned(outputs, i, me)];
                 if (i < 16) {
-                    lds_dma16(rk, dst + i * 1024, voff_k[i & 3],
-                              static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
+                    r = gload16(rk, voff_k[i & 3],
+                                static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
                 } else if (i < 22) {
-                    lds_dma16(rth, dst + KB + (i - 16) * 1024, voff_l, tr + (i - 16) * 1024);
+                    r = gload16(rth, voff_l, tr + (i - 16) * 1024);
                 } else if (kSplit && i < 28) {
-                    lds_dma16(rtl, dst + KB + TB + (i - 22) * 1024, voff_l, tr + (i - 22) * 1024);
+                    r = gload16(rtl, voff_l, tr + (i - 22) * 1024);
                 } else if (kHasV && i < NK - 1) {
-                    const int m = i - (NK - 3);
-                    lds_dma16(rv, dst + KB + TB + LB + m * 1024, voff_v[m], static_cast<uint32_t>(n) * vstep);
+                    r = gload16(rv, voff_v[i - (NK - 3)], static_cast<uint32_t>(n) * vstep);
                 } else {
-                    lds_dma16(rgt, gbase + (n % 4) * 1024, voff_l, static_cast<uint32_t>(n) * 512u);
+                    r = gload16(rgt, voff_l, static_cast<uint32_t>(n) * 512u);
                 }
             }
         };
-        // Q-side operands of chunk n into buffer n % 3
-        auto issue_q = [&](int n) {
-            const uint32_t dst = qbase + static_cast<uint32_t>((n % 3) * QSB);
+        auto store_k = [&](int n, const Stage& stage) {   // into stage buffer n % 2 (decay factors: slot n % 4)
+            unsigned char* dst = kst + (n & 1) * KSB + 16 * lane;
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                if (load_owner(outputs, i) != me) continue;
+                unsigned char* p;
+                if (i < 16) p = dst + i * 1024;
+                else if (i < 22) p = dst + KB + (i - 16) * 1024;
+                else if (kSplit && i < 28) p = dst + KB + TB + (i - 22) * 1024;
+                else if (kHasV && i < NK - 1) p = dst + KB + TB + LB + (i - (NK - 3)) * 1024;
+                else p = gst + (n % 4) * 1024 + 16 * lane;
+                *reinterpret_cast<u32x4*>(p) = stage[loads_owned(outputs, i, me)];
+            }
+        };
+        auto load_q = [&](int n, Stage& stage) {   // Q-side operands of chunk n
             const uint32_t tr = static_cast<uint32_t>(n) * (kTriRecord * 2);
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
-                if ((NK + j) % nl != me) continue;
+                if (load_owner(outputs, NK + j) != me) continue;
+                u32x4& r = stage[loads_owned(outputs, NK + j, me)];
                 if (j < 16) {
-                    lds_dma16(rq, dst + j * 1024, voff_k[j & 3],
-                              static_cast<uint32_t>(4 * j * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
+                    r = gload16(rq, voff_k[j & 3],
+                                static_cast<uint32_t>(4 * j * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
                 } else {
-                    lds_dma16(rpm, dst + KB + (j - 16) * 1024, voff_l, tr + (j - 16) * 1024);
+                    r = gload16(rpm, voff_l, tr + (j - 16) * 1024);
                 }
             }
         };
-        // In iteration m the waves issue K(m + 2) and Q(m + 1); the barrier that opens
-        // iteration n needs the loads issued in iteration n - 2, so each wave first waits
-        // until no more than its share of iteration n - 1 is outstanding (loads of one
-        // wave complete in order). A partial set (near the end) waits for everything.
-        constexpr int cnt = NI / nl + (me < NI % nl ? 1 : 0);
-        auto wait_older = [&](bool full) {
-            if (!full) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(cnt) : "memory");
+        auto store_q = [&](int n, const Stage& stage) {   // into buffer n % 2
+            unsigned char* dst = qst + (n & 1) * QSB + 16 * lane;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                if (load_owner(outputs, NK + j) != me) continue;
+                unsigned char* p = j < 16 ? dst + j * 1024 : dst + KB + (j - 16) * 1024;
+                *reinterpret_cast<u32x4*>(p) = stage[loads_owned(outputs, NK + j, me)];
+            }
         };
-        auto issue_iter = [&](int m) {   // the loads of iteration m
-            if (m + 2 < n1) issue_k(m + 2);
-            if (outputs && m + 1 < n1) issue_q(m + 1);
-        };
-        if (n0 < n1) issue_k(n0);
-        issue_iter(n0 - 1);
-        for (int n = n0; n <= n1; ++n) {
-            wait_older(n + 1 < n1);
+        // Iteration n: stores of the loads of iteration n - 2, then the loads of iteration
+        // n. The body has no branches, so that the compiler's wait for a store counts
+        // only the loads issued before it: loads past the last chunk fetch the last
+        // chunk again, and their stores land in buffers nobody reads any more (the
+        // K-side buffer of a chunk >= n1 and the Q-side buffer of chunk n1; the chain
+        // reads chunk n and the output wave chunk n - 1 in iteration n).
+        const int last = n1 > 0 ? n1 - 1 : 0;
+        auto step = [&](int n, Stage& stage) {
             chunk_barrier(false);
-            issue_iter(n);
+            store_k(n + 1, stage);
+            if constexpr (outputs) store_q(n, stage);
+            load_k(min(n + 3, last), stage);
+            if constexpr (outputs) load_q(min(n + 2, last), stage);
+        };
+        // the K-side operands of the first chunk are in LDS before the barrier that opens
+        // it; then the loads of iterations n0 - 2 (into st0) and n0 - 1 (into st1)
+        load_k(min(n0, last), st0);
+        store_k(n0, st0);
+        load_k(min(n0 + 1, last), st0);
+        if constexpr (outputs) load_q(min(n0, last), st0);
+        load_k(min(n0 + 2, last), st1);
+        if constexpr (outputs) load_q(min(n0 + 1, last), st1);
+        int n = n0;
+        for (; n + 1 <= n1; n += 2) {
+            step(n, st0);
+            step(n + 1, st1);
         }
+        if (n <= n1) step(n, st0);
         };
         switch (wave - first_loader) {
             case 0: loader(IntTag<0>{}); break;
@@ -670,7 +710,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             if (n == n0) continue;
             const int m = n - 1;
             const unsigned char* hb = hst + (m & 1) * HB;
-            const unsigned char* qs = qst + (m % 3) * QSB;
+            const unsigned char* qs = qst + (m & 1) * QSB;
             const unsigned char* ps = qs + KB;
             const float* gs = reinterpret_cast<const float*>(gst + (m % 4) * 1024);
             bf16x8 sb[4], ub[2];
@@ -710,6 +750,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     }
 
     // ---------------- chain wave ----------------
+    // Iteration n (between the barriers that open chunks n and n + 1) first applies the
+    // state update of chunk n - 1, whose operands (the transposed K fragments and V'')
+    // were read and formed in iteration n - 1, while the K fragments of chunk n stream in
+    // from LDS; then it runs K S, X and U of chunk n and reads the transposed K fragments
+    // of chunk n during the K S steps. Chunk n's K buffer is free once the barrier that
+    // opens chunk n + 1 has passed, and every read of it is complete by then.
     f32x4 S[8];
     {
         const int64_t blk = a.s_init_per_segment ? bh * a.P + seg : bh;
@@ -724,12 +770,6 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 S[t][j] = s0;
             }
     }
-    bf16x8 sb[4], sbl[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        if constexpr (kSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
-        else sb[s] = pack_frag(S[2 * s], S[2 * s + 1]);
-    }
     // Transposing reads of K: lane (c, g) of k-step s, half hf reads the 8-byte piece of
     // token 32s + 16hf + 4g + c / 4 at dk 32 (t / 2) + 8 (c % 4) + 4 (t % 2): quad block
     // 8s + 4hf + g, row c / 4 in it, granule 4 (t / 2) + c % 4, byte 8 (t % 2) of the granule.
@@ -739,20 +779,54 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         tr_lane[th] = g4 * 1024 + 256 * (l16 >> 2) + 16 * ((4 * th + (l16 & 3)) ^ (4 * g4 + (l16 >> 2)));
     const int v_lane = 2 * (16 * (4 * g4 + (l16 >> 2)) + 4 * (l16 & 3));
 
-    for (int n = n0; n <= n1; ++n) {
+    // operands of the pending state update (chunk n - 1): A fragments of K^T for state
+    // tile t and token k-step s, and V'' = diag(exp(Gam_C - Gam)) U as B fragments
+    u32x2 ktr[8][2][2];
+    bf16x8 vb[2], vbl[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) vb[s] = vbl[s] = bf16x8{};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ktr[t][s][0] = ktr[t][s][1] = u32x2{0u, 0u};
+
+    // state update of the last chunk, applied after the barrier that follows it
+    auto state_update = [&]() {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int s = i >> 3, t = i & 7;
+            const bf16x8 kt = __builtin_bit_cast(
+                bf16x8, u32x4{ktr[t][s][0][0], ktr[t][s][0][1], ktr[t][s][1][0], ktr[t][s][1][1]});
+            S[t] = mfma16(kt, vb[s], S[t]);
+            if constexpr (kSplit) S[t] = mfma16(kt, vbl[s], S[t]);
+        }
+    };
+    for (int n = n0; n < n1; ++n) {
         chunk_barrier(false);
-        if (n == n1) break;
-        const unsigned char* ks = kst + (n % 3) * KSB;
+        const unsigned char* ks = kst + (n & 1) * KSB;
         const unsigned char* ts = ks + KB;
         const unsigned char* tls = ks + KB + TB;
         const unsigned char* vs = ks + KB + TB + LB;
         const float* gs = reinterpret_cast<const float*>(gst + (n % 4) * 1024);
         unsigned char* hb = hst + (n & 1) * HB;
 
-        // Phase 0: every LDS operand of K S, X and U, read at once.
+        // State update of chunk n - 1 (S already holds exp(Gam_C) S): S += K^T V'', state
+        // tiles t, token k-steps s (zero operands before the first chunk, which adds
+        // exact zeros). Between the MFMAs, the K fragments of chunk n for K S are read in
+        // the order K S uses them (k-step major); kf[4 s + r] is token tile r.
         bf16x8 kf[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) kf[i] = lds_frag_b(ks + (i >> 2) * 4096 + frag_lane[i & 3]);
+        for (int i = 0; i < 16; ++i) {
+            const int s = i >> 3, t = i & 7;
+            const bf16x8 kt = __builtin_bit_cast(
+                bf16x8, u32x4{ktr[t][s][0][0], ktr[t][s][0][1], ktr[t][s][1][0], ktr[t][s][1][1]});
+            S[t] = mfma16(kt, vb[s], S[t]);
+            if constexpr (kSplit) S[t] = mfma16(kt, vbl[s], S[t]);
+            kf[i] = lds_frag_b(ks + (i & 3) * 4096 + frag_lane[i >> 2]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // the remaining LDS operands of chunk n
         f32x4 eg[4];
         u32x2 vraw[4];
 #pragma unroll
@@ -772,28 +846,42 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const float egC = gs[63];
         __builtin_amdgcn_sched_barrier(0);
 
-        // Phase 1: K S for token tiles r, one accumulator per tile; the k-steps go
-        // round the four tiles, so each MFMA's predecessor on its tile is four back.
-        f32x4 c0[4];
+        // the state of chunk n as bf16 B fragments of K S (and for the output wave)
+        bf16x8 sb[4], sbl[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * r], sb[0], zero4());
-#pragma unroll
-        for (int s = 1; s < 4; ++s)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * r + s], sb[s], c0[r]);
-        if constexpr (kSplit) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * r + s], sbl[s], c0[r]);
+        for (int s = 0; s < 4; ++s) {
+            if constexpr (kSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
+            else sb[s] = pack_frag(S[2 * s], S[2 * s + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
+
+        // K S for token tiles r, one accumulator per tile, k-steps s in turn; after each
+        // k-step, eight transposing reads of K for the state update go out (into the
+        // registers that k-step's fragments leave free).
+        f32x4 c0[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * s + r], sb[s], s == 0 ? zero4() : c0[r]);
+            if constexpr (kSplit) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * s + r], sbl[s], c0[r]);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = 2 * s + (q >> 1), ks2 = q & 1;
+                const int o0 = 8 * ks2 * 1024 + 8 * (t & 1) + tr_lane[t >> 1];
+                ktr[t][ks2][0] = lds_read_tr(ks + o0);
+                ktr[t][ks2][1] = lds_read_tr(ks + o0 + 4 * 1024);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (outputs) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(hb + s * 1024 + 16 * lane) = sb[s];
         }
 
-        // Phase 2: X = V - diag(exp Gam) K S for tokens 16r + 4g + j, column l16
+        // X = V - diag(exp Gam) K S for tokens 16r + 4g + j, column l16
         f32x4 x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -807,6 +895,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             if constexpr (kSplit) pack_frag_split(x[2 * s], x[2 * s + 1], xb[s], xbl[s]);
             else xb[s] = pack_frag(x[2 * s], x[2 * s + 1]);
         }
+        // the scaled old state, off the dependency chain (the fp32 S is next read by the
+        // state update that opens the next iteration)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S[t][j] *= egC;
         // U = That X (lower triangular: k-steps s <= r / 2)
         f32x4 u[4];
 #pragma unroll
@@ -821,33 +915,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // The transposing reads of K for the state update go out once U is issued. Issued
-        // earlier they would sit ahead of the That reads in the LDS counter, which counts
-        // at most 15 outstanding reads, and U would wait for them.
-        u32x2 ktr[8][2][2];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int o0 = 8 * s * 1024 + 8 * (t & 1) + tr_lane[t >> 1];
-                ktr[t][s][0] = lds_read_tr(ks + o0);
-                ktr[t][s][1] = lds_read_tr(ks + o0 + 4 * 1024);
-            }
-        __builtin_amdgcn_sched_barrier(0);
-        // the scaled old state, off the dependency chain
-        f32x4 sacc[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sacc[t][j] = egC * S[t][j];
         if constexpr (outputs) {
 #pragma unroll
             for (int s = 0; s < 2; ++s)
                 *reinterpret_cast<bf16x8*>(hb + (4 + s) * 1024 + 16 * lane) = pack_frag(u[2 * s], u[2 * s + 1]);
         }
-        // V'' = diag(exp(Gam_C - Gam)) U
-        bf16x8 vb[2], vbl[2];
+        // V'' = diag(exp(Gam_C - Gam)) U, the B operand of the pending state update
         {
             f32x4 w[4];
 #pragma unroll
@@ -860,24 +933,9 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 else vb[s] = pack_frag(w[2 * s], w[2 * s + 1]);
             }
         }
-        // S <- exp(Gam_C) S + K^T V'': state tiles t, token k-steps s
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const bf16x8 kt = __builtin_bit_cast(
-                    bf16x8, u32x4{ktr[t][s][0][0], ktr[t][s][0][1], ktr[t][s][1][0], ktr[t][s][1][1]});
-                sacc[t] = mfma16(kt, vb[s], sacc[t]);
-                if constexpr (kSplit) sacc[t] = mfma16(kt, vbl[s], sacc[t]);
-            }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = sacc[t];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            if constexpr (kSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
-            else sb[s] = pack_frag(S[2 * s], S[2 * s + 1]);
-        }
     }
+    chunk_barrier(false);
+    state_update();
 
     if (a.store_mode == kStoreNone) return;
     if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
