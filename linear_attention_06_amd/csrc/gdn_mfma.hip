@@ -330,15 +330,16 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
 //     wave O = diag(exp Gam) Q S + P U from the state and U the chain wave leaves in
 //     LDS, transposed (O^T = S^T Q^T + U^T P^T) so that each lane ends up holding
 //     four consecutive columns of one token, and writes o.
-//   the other waves load the chunk operands straight from global memory into LDS
-//     (buffer loads with the lds bit): K, That (and its remainder), V and the decay
-//     factors two chunks ahead of the chain wave, Q and P one chunk ahead of the
-//     output wave, in rings of three buffers.
+//   the other waves load the chunk operands into registers and write them to LDS
+//     an iteration later (K, That and its remainder, V and the decay factors of the
+//     next chunk for the chain wave; Q and P of the current chunk for the output
+//     wave, which reads them in the next iteration), with two iterations of loads in
+//     flight; two LDS buffers per side.
 // One barrier per chunk.
 //
 // Layouts. A 1 KiB fragment block holds one 16x32 bf16 MFMA operand, lane l's 16
 // bytes at byte 16 l (row l % 16, contraction slots 8 (l / 16) .. +7):
-//   K, Q: 4-row blocks, swizzled (see below) so that one direct load moves 4 whole rows;
+//   K, Q: 4-row blocks, swizzled (see below) so that one 1 KiB load moves 4 whole rows;
 //   That, P: blocks (r, s) of the lower triangle, (0,0) (1,0) (2,0) (2,1) (3,0) (3,1),
 //     rows = tokens 16r .., slot 8g + e = token 32s + 4g + (e % 4) + 16 (e / 4);
 //   V: [64 tokens][16 columns], read with transposing reads into accumulator order.
@@ -430,11 +431,10 @@ __device__ __forceinline__ void chunk_barrier(bool vm_wait) {
 }
 
 // Loading wave (index among the loading waves) that issues load g of an iteration.
-// Waves w and w + 4 of a workgroup run on the same SIMD, and the rate at which one
-// SIMD issues direct loads bounds the loading; the deal gives every SIMD the same
-// share. With outputs, waves 0 and 1 (chain, output) each share their SIMD with one
-// loading wave (indices 2 and 3), which take two of every eight loads; otherwise
-// wave 0 shares its SIMD with loading wave 3.
+// Waves w and w + 4 of a workgroup run on the same SIMD; the deal gives every SIMD
+// the same share of the loads. With outputs, waves 0 and 1 (chain, output) each
+// share their SIMD with one loading wave (indices 2 and 3), which take two of every
+// eight loads; otherwise wave 0 shares its SIMD with loading wave 3.
 __host__ __device__ constexpr int load_owner(bool with_outputs, int g) {
     const int p = g & 7;
     if (with_outputs) return (p == 0 || p == 3) ? 2 : (p == 1 || p == 4) ? 3 : (p == 2) ? 0 : (p == 5) ? 1 : (p == 6) ? 4 : 5;
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
     const int first_loader = outputs ? 2 : 1;
     // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
-    // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 (j % 4) + rho)). A direct load fills one
+    // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 (j % 4) + rho)). A 1 KiB load fills one
     // quad block with 16 lanes per row, so that each group of 4 lanes reads one 64-byte piece
     // (lanes of a quad spread over different rows cost the load path 3x as much); the
     // fragment reads and the transposing reads below are free of bank conflicts.
