@@ -332,9 +332,10 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
 //     four consecutive columns of one token, and writes o.
 //   the other waves load the chunk operands into registers and write them to LDS
 //     an iteration later (K, That and its remainder, V and the decay factors of the
-//     next chunk for the chain wave; Q and P of the current chunk for the output
-//     wave, which reads them in the next iteration), with two iterations of loads in
-//     flight; two LDS buffers per side.
+//     next chunk for the chain wave; Q of the current chunk for the output wave,
+//     which reads it in the next iteration), with two iterations of loads in flight;
+//     two LDS buffers per side. The output wave loads P itself, straight into
+//     registers.
 // One barrier per chunk.
 //
 // Layouts. A 1 KiB fragment block holds one 16x32 bf16 MFMA operand, lane l's 16
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     constexpr int KB = 64 * DK * 2, TB = kTriRecord * 2, LB = kSplit ? kTriRecord * 2 : 0;
     constexpr int VB = kHasV ? 64 * 16 * 2 : 0;
     constexpr int KSB = KB + TB + LB + VB;
-    constexpr int QSB = outputs ? KB + TB : 0;
+    constexpr int QSB = outputs ? KB : 0;
     constexpr int HB = 6 * 1024;   // hand-off: S fragments (4 blocks), U fragments (2 blocks)
     __shared__ __align__(16) unsigned char kst[2 * KSB];
     __shared__ __align__(16) unsigned char qst[outputs ? 2 * QSB : 16];
@@ -514,7 +515,6 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
         const int64_t rec = static_cast<int64_t>(a.NT) * kTriRecord * 2;   // bytes of one head's records
         const __amdgpu_buffer_rsrc_t rth = make_rsrc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * kTriRecord, rec);
-        const __amdgpu_buffer_rsrc_t rpm = make_rsrc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * kTriRecord, rec);
         const __amdgpu_buffer_rsrc_t rtl = make_rsrc(
             kSplit ? static_cast<const uint16_t*>(a.ws.that_lo) + bh * a.NT * kTriRecord : static_cast<const uint16_t*>(a.ws.that),
             rec);
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * vo_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
         constexpr int nl = 8 - (outputs ? 2 : 1);
         constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + (kHasV ? 2 : 0) + 1;
-        constexpr int NQ = outputs ? 22 : 0;
+        constexpr int NQ = outputs ? 16 : 0;
         constexpr int NI = NK + NQ;   // 1 KiB loads of one full iteration
         static_assert(nl >= 6, "loading waves");
 
@@ -586,18 +586,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 *reinterpret_cast<u32x4*>(p) = stage[loads_owned(outputs, i, me)];
             }
         };
-        auto load_q = [&](int n, Stage& stage) {   // Q-side operands of chunk n
-            const uint32_t tr = static_cast<uint32_t>(n) * (kTriRecord * 2);
+        auto load_q = [&](int n, Stage& stage) {   // Q of chunk n
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
                 if (load_owner(outputs, NK + j) != me) continue;
-                u32x4& r = stage[loads_owned(outputs, NK + j, me)];
-                if (j < 16) {
-                    r = gload16(rq, voff_k[j & 3],
-                                static_cast<uint32_t>(4 * j * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
-                } else {
-                    r = gload16(rpm, voff_l, tr + (j - 16) * 1024);
-                }
+                stage[loads_owned(outputs, NK + j, me)] =
+                    gload16(rq, voff_k[j & 3], static_cast<uint32_t>(4 * j * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
             }
         };
         auto store_q = [&](int n, const Stage& stage) {   // into buffer n % 2
@@ -605,8 +599,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
                 if (load_owner(outputs, NK + j) != me) continue;
-                unsigned char* p = j < 16 ? dst + j * 1024 : dst + KB + (j - 16) * 1024;
-                *reinterpret_cast<u32x4*>(p) = stage[loads_owned(outputs, NK + j, me)];
+                *reinterpret_cast<u32x4*>(dst + j * 1024) = stage[loads_owned(outputs, NK + j, me)];
             }
         };
         // Iteration n: stores of the loads of iteration n - 2, then the loads of iteration
@@ -704,14 +697,24 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         };
         if (kEnablePrefetch)
             for (int c = n0 + 2; c < n0 + kPrefetch && c < n1; ++c) prefetch(c);
-        for (int n = n0; n <= n1; ++n) {
-            chunk_barrier(false);
-            if (kEnablePrefetch && n + kPrefetch < n1) prefetch(n + kPrefetch);
-            if (n == n0) continue;
-            const int m = n - 1;
+        const int last = n1 > 0 ? n1 - 1 : 0;
+        // P goes from global memory straight into registers: its blocks are contiguous
+        // 1 KiB records (lane l: 16 bytes at 16 l), loaded two chunks ahead into the
+        // register set of the chunk's parity.
+        const __amdgpu_buffer_rsrc_t rpm = make_rsrc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * kTriRecord,
+                                                     static_cast<int64_t>(a.NT) * kTriRecord * 2);
+        const uint32_t voff_p = static_cast<uint32_t>(16 * lane);
+        using PSet = bf16x8[6];
+        PSet p0, p1;
+        auto load_p = [&](int c, PSet& pp) {
+#pragma unroll
+            for (int i = 0; i < 6; ++i)
+                pp[i] = __builtin_bit_cast(bf16x8, gload16(rpm, voff_p, static_cast<uint32_t>(c) * (kTriRecord * 2) +
+                                                                            static_cast<uint32_t>(i * 1024)));
+        };
+        auto compute = [&](int m, const PSet& pp) {   // outputs of chunk m
             const unsigned char* hb = hst + (m & 1) * HB;
             const unsigned char* qs = qst + (m & 1) * QSB;
-            const unsigned char* ps = qs + KB;
             const float* gs = reinterpret_cast<const float*>(gst + (m % 4) * 1024);
             bf16x8 sb[4], ub[2];
 #pragma unroll
@@ -730,8 +733,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 f32x4 o;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o[j] = e * (o0[j] + o1[j]);
-                o = mfma16(ub[0], lds_frag_b(ps + tri_block(r, 0) * 1024 + 16 * lane), o);
-                if (r >= 2) o = mfma16(ub[1], lds_frag_b(ps + tri_block(r, 1) * 1024 + 16 * lane), o);
+                o = mfma16(ub[0], pp[tri_block(r, 0)], o);
+                if (r >= 2) o = mfma16(ub[1], pp[tri_block(r, 1)], o);
                 const int64_t t = static_cast<int64_t>(m) * kChunk + 16 * r + l16;
                 const bool ok = t < nvalid;
                 const uint32_t w0 = ok ? pk2(o[0], o[1]) : 0u, w1 = ok ? pk2(o[2], o[3]) : 0u;
@@ -740,7 +743,26 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                                                           static_cast<uint32_t>(16 * r * vo_row * 2),
                                                       0, 0);
             }
+        };
+        // iteration n: outputs of chunk n - 1, then the P blocks of chunk n + 1 into the
+        // same registers; chunk indices past the end are clamped (a repeated prefetch or
+        // load of the last chunk), so that the body has no branches
+        auto step = [&](int n, PSet& pp) {
+            chunk_barrier(false);
+            if (kEnablePrefetch) prefetch(min(n + kPrefetch, last));
+            compute(n - 1, pp);
+            load_p(min(n + 1, last), pp);
+        };
+        load_p(min(n0, last), p0);
+        load_p(min(n0 + 1, last), p1);
+        chunk_barrier(false);   // iteration n0: no outputs yet
+        if (kEnablePrefetch) prefetch(min(n0 + kPrefetch, last));
+        int n = n0 + 1;
+        for (; n + 1 <= n1; n += 2) {
+            step(n, p0);
+            step(n + 1, p1);
         }
+        if (n <= n1) step(n, p0);
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
