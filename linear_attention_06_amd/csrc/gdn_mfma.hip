@@ -250,32 +250,57 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         for (int r = 0; r < 16; ++r) t_s[(o + r) * AP + o + c] = x[r];
     }
     lds_sync();
-    // off-diagonal blocks, one block row per level: T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj
+    // off-diagonal blocks: T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj (T_jj = D_j). Each wave
+    // runs one dependency chain with its earlier results kept in registers: wave 0
+    // T10, T20, T30; wave 1 T21, T31; wave 2 T32. A 16x16 block product takes four
+    // 16x16x4 f32 MFMAs; an operand in LDS is read in any order, and a result held in
+    // accumulator layout (lane (j, g) has rows 4g .. 4g+3 of column j) serves as the B
+    // operand with k-slot (s, g) standing for row 4g + s.
     const int l16 = lane & 15, g4 = lane >> 4;
-    for (int bi = 1; bi < 4; ++bi) {
-        if (wave < bi) {
-            const int bj = wave;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int bk = bj; bk < bi; ++bk) {
+    // acc += X_(bi,bk) Y_(bk,bj), both blocks in LDS (X from a_s or t_s, Y from t_s)
+    auto mm_ll = [&](const float* x, int bi, int bk, int bj, f32x4 acc) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const float av = a_s[(16 * bi + l16) * AP + 16 * bk + 4 * s + g4];
-                    const float bv = t_s[(16 * bk + 4 * s + g4) * AP + 16 * bj + l16];
-                    acc = mfma16f32(av, bv, acc);
-                }
-            }
-            // D_i X with X taken from the accumulator: k-slot (s, g4) is row 4*g4 + s
-            f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const float av = t_s[(16 * bi + l16) * AP + 16 * bi + 4 * g4 + s];
-                acc2 = mfma16f32(av, acc[s], acc2);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t_s[(16 * bi + 4 * g4 + i) * AP + 16 * bj + l16] = -acc2[i];
+        for (int s = 0; s < 4; ++s) {
+            const float av = x[(16 * bi + l16) * AP + 16 * bk + 4 * s + g4];
+            const float bv = t_s[(16 * bk + 4 * s + g4) * AP + 16 * bj + l16];
+            acc = mfma16f32(av, bv, acc);
         }
-        lds_sync();
+        return acc;
+    };
+    // acc += X_(bi,bk) R with X in LDS and R in accumulator layout
+    auto mm_lr = [&](const float* x, int bi, int bk, const f32x4& r, f32x4 acc) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma16f32(x[(16 * bi + l16) * AP + 16 * bk + 4 * g4 + s], r[s], acc);
+        return acc;
+    };
+    // -D_i Y
+    auto neg_d = [&](int bi, const f32x4& y) {
+        f32x4 r = mm_lr(t_s, bi, bi, y, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = -r[i];
+        return r;
+    };
+    auto put = [&](int bi, int bj, const f32x4& r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t_s[(16 * bi + 4 * g4 + i) * AP + 16 * bj + l16] = r[i];
+    };
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    if (wave == 0) {
+        const f32x4 t10 = neg_d(1, mm_ll(a_s, 1, 0, 0, z4));
+        const f32x4 t20 = neg_d(2, mm_lr(a_s, 2, 1, t10, mm_ll(a_s, 2, 0, 0, z4)));
+        const f32x4 t30 = neg_d(3, mm_lr(a_s, 3, 2, t20, mm_lr(a_s, 3, 1, t10, mm_ll(a_s, 3, 0, 0, z4))));
+        put(1, 0, t10);
+        put(2, 0, t20);
+        put(3, 0, t30);
+    } else if (wave == 1) {
+        const f32x4 t21 = neg_d(2, mm_ll(a_s, 2, 1, 1, z4));
+        const f32x4 t31 = neg_d(3, mm_lr(a_s, 3, 2, t21, mm_ll(a_s, 3, 1, 1, z4)));
+        put(2, 1, t21);
+        put(3, 1, t31);
+    } else if (wave == 2) {
+        put(3, 2, neg_d(3, mm_ll(a_s, 3, 2, 2, z4)));
     }
+    lds_sync();
     // P into the space of A
     if (has_p) {
         const int s = 32 * p_nj + lr;
