@@ -232,18 +232,22 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     // substitution, wave w inverts block w, lane c < 16 owns column c
     if (lane < 16) {
         // column sweep: once x[j] is final it is eliminated from every later row, so
-        // the dependency chain is 15 steps long instead of one FMA per matrix entry
+        // the dependency chain is 15 steps long instead of one FMA per matrix entry.
+        // The block is read in four batches of columns 4q .. 4q+3, one 16-byte read per
+        // row below the diagonal (at most 15 reads, so each batch waits once).
         const int c = lane, o = 16 * wave;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 0; j < 15; ++j) {
-            float col[16];
+        for (int q = 0; q < 4; ++q) {
+            f32x4 v[16];
 #pragma unroll
-            for (int r = j + 1; r < 16; ++r) col[r] = a_s[(o + r) * AP + o + j];
+            for (int r = 4 * q + 1; r < 16; ++r) v[r] = *reinterpret_cast<const f32x4*>(a_s + (o + r) * AP + o + 4 * q);
 #pragma unroll
-            for (int r = j + 1; r < 16; ++r) x[r] -= col[r] * x[j];
+            for (int j = 4 * q; j < 4 * q + 4 && j < 15; ++j)
+#pragma unroll
+                for (int r = j + 1; r < 16; ++r) x[r] -= v[r][j - 4 * q] * x[j];
         }
         // stored after the substitution, so that no store sits between its LDS reads
 #pragma unroll
