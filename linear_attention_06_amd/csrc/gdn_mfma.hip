@@ -523,14 +523,19 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
     const int first_loader = outputs ? 2 : 1;
     // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
-    // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 (j % 4) + rho)). A 1 KiB load fills one
+    // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 rho + j % 4)). A 1 KiB load fills one
     // quad block with 16 lanes per row, so that each group of 4 lanes reads one 64-byte piece
-    // (lanes of a quad spread over different rows cost the load path 3x as much); the
-    // fragment reads and the transposing reads below are free of bank conflicts.
+    // (lanes of a quad spread over different rows cost the load path 3x as much). The
+    // fragment reads are free of bank conflicts: the 16 lanes of a group read rows with 16
+    // different (rho, j % 4). A transposing read takes 4 granules of 4 rows per group; the
+    // row selects the upper two bits of the slot, so those 16 pieces fill 16 different
+    // slots (2-way conflicts remain between the two groups of a half-wave, which read the
+    // same 8-byte halves; with the row in the lower bits they were 4-way).
     // Fragment (r, s) of lane (l16, g4): byte 4096 r + frag_lane[s].
     int frag_lane[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) frag_lane[s] = (l16 >> 2) * 1024 + 256 * (l16 & 3) + 16 * ((4 * s + g4) ^ l16);
+    for (int s = 0; s < 4; ++s)
+        frag_lane[s] = (l16 >> 2) * 1024 + 256 * (l16 & 3) + 16 * ((4 * s + g4) ^ (4 * (l16 & 3) + (l16 >> 2)));
 
     if (wave >= first_loader) {
         // ---------------- loading waves ----------------
@@ -549,12 +554,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             rec);
         const __amdgpu_buffer_rsrc_t rgt = make_rsrc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
 
-        // lane l of a quad-block load: slot l = 16 rho + c, row 4j + rho, granule c ^ (4 (j % 4) + rho)
+        // lane l of a quad-block load: slot l = 16 rho + c, row 4j + rho, granule c ^ (4 rho + j % 4)
         uint32_t voff_k[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
             voff_k[jj] = static_cast<uint32_t>(((lane >> 4) * qk_row + hq * DK +
-                                                8 * ((lane & 15) ^ (4 * jj + (lane >> 4)))) * 2);
+                                                8 * ((lane & 15) ^ (4 * (lane >> 4) + jj))) * 2);
         const uint32_t voff_l = static_cast<uint32_t>(16 * lane);
         uint32_t voff_v[2];
 #pragma unroll
@@ -827,7 +832,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     int tr_lane[4];
 #pragma unroll
     for (int th = 0; th < 4; ++th)
-        tr_lane[th] = g4 * 1024 + 256 * (l16 >> 2) + 16 * ((4 * th + (l16 & 3)) ^ (4 * g4 + (l16 >> 2)));
+        tr_lane[th] = g4 * 1024 + 256 * (l16 >> 2) + 16 * ((4 * th + (l16 & 3)) ^ (4 * (l16 >> 2) + g4));
     const int v_lane = 2 * (16 * (4 * g4 + (l16 >> 2)) + 4 * (l16 & 3));
 
     // operands of the pending state update (chunk n - 1): A fragments of K^T for state
