@@ -137,7 +137,7 @@ gdn::StateArgs state_args(const gdn_problem& p, const Plan& pl, const void* q, c
     a.P = 1; a.Lc = static_cast<int>(pl.NT);
     a.q = q; a.k = k; a.v = v; a.valid_len = p.valid_len; a.ws = w;
     a.init_mode = gdn::kInitZero; a.s_init = nullptr; a.s_init_per_segment = 0;
-    a.o = nullptr; a.s_out = nullptr; a.store_mode = gdn::kStoreNone;
+    a.o = nullptr; a.s_out = nullptr; a.store_mode = gdn::kStoreNone; a.m_out = nullptr;
     return a;
 }
 
@@ -242,6 +242,14 @@ gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void
         a.P = static_cast<int>(P);
         a.Lc = seg_len / gdn::kChunk;
         a.store_mode = gdn::kStoreEverySegment;
+        if (S && M && use_mfma(*p) && p->dk == p->dv) {
+            // both summaries in one pass: the M and S chains of a column tile share
+            // every loaded operand
+            a.init_mode = gdn::kInitZero;
+            a.s_out = S;
+            a.m_out = M;
+            return run_state(*p, a, s);
+        }
         if (S) {
             a.init_mode = gdn::kInitZero;
             a.s_out = S;

@@ -56,6 +56,8 @@ struct StateArgs {
     void* o;                          // NULL: no token output
     float* s_out;
     int store_mode;
+    float* m_out;                     // matrix-core path: with v and no o, the M summary
+                                      // (ncols = dk) computed in the same pass as S; else NULL
 };
 
 struct ScanArgs {

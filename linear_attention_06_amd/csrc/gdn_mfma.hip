@@ -479,6 +479,12 @@ __host__ __device__ constexpr int loads_owned(bool with_outputs, int n, int me) 
 template <bool kHasV, bool kSplit, bool kOut>
 __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk_groups) {
     constexpr bool outputs = kHasV && kOut;
+    // Both summaries in one pass (values, split, no outputs): wave 0 runs the chain of
+    // the M tile (split operands, no values, identity start, written to a.m_out) and
+    // wave 1 the chain of the S tile (values, zero start, written to a.s_out); the two
+    // share every loaded operand. Requires ncols = dk.
+    constexpr bool dual = kHasV && kSplit && !kOut;
+    constexpr bool two_compute = outputs || dual;   // waves 0 and 1 compute, 2 .. 7 load
     // K-side stage buffer: K, That, That remainder (split), V; Q-side: Q, P.
     // K-side operands of chunk n are written in iteration n - 1 and read in iteration
     // n; Q-side operands in iteration n and read by the output wave, which runs one
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const int64_t vo_row = static_cast<int64_t>(a.H) * ncols;
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
-    const int first_loader = outputs ? 2 : 1;
+    const int first_loader = two_compute ? 2 : 1;
     // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
     // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 rho + j % 4)). A 1 KiB load fills one
     // quad block with 16 lanes per row, so that each group of 4 lanes reads one 64-byte piece
@@ -565,7 +571,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 #pragma unroll
         for (int m = 0; m < 2; ++m)
             voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * vo_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
-        constexpr int nl = 8 - (outputs ? 2 : 1);
+        constexpr int nl = 8 - (two_compute ? 2 : 1);
         constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + (kHasV ? 2 : 0) + 1;
         constexpr int NQ = outputs ? 16 : 0;
         constexpr int NI = NK + NQ;   // 1 KiB loads of one full iteration
@@ -583,15 +589,15 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // own loads as straight-line code with its registers indexed at compile time.
         auto loader = [&](auto me_tag) {
         constexpr int me = decltype(me_tag)::value;
-        constexpr int NS = loads_owned(outputs, NI, me);
+        constexpr int NS = loads_owned(two_compute, NI, me);
         using Stage = u32x4[NS > 0 ? NS : 1];
         Stage st0, st1;   // loads of even / odd iterations (relative to n0)
         auto load_k = [&](int n, Stage& stage) {   // K-side operands of chunk n
             const uint32_t tr = static_cast<uint32_t>(n) * (kTriRecord * 2);
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
-                if (load_owner(outputs, i) != me) continue;
-                u32x4& r = stage[loads_owned(outputs, i, me)];
+                if (load_owner(two_compute, i) != me) continue;
+                u32x4& r = stage[loads_owned(two_compute, i, me)];
                 if (i < 16) {
                     r = gload16(rk, voff_k[i & 3],
                                 static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
@@ -610,21 +616,21 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             unsigned char* dst = kst + (n & 1) * KSB + 16 * lane;
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
-                if (load_owner(outputs, i) != me) continue;
+                if (load_owner(two_compute, i) != me) continue;
                 unsigned char* p;
                 if (i < 16) p = dst + i * 1024;
                 else if (i < 22) p = dst + KB + (i - 16) * 1024;
                 else if (kSplit && i < 28) p = dst + KB + TB + (i - 22) * 1024;
                 else if (kHasV && i < NK - 1) p = dst + KB + TB + LB + (i - (NK - 3)) * 1024;
                 else p = gst + (n % 4) * 1024 + 16 * lane;
-                *reinterpret_cast<u32x4*>(p) = stage[loads_owned(outputs, i, me)];
+                *reinterpret_cast<u32x4*>(p) = stage[loads_owned(two_compute, i, me)];
             }
         };
         auto load_q = [&](int n, Stage& stage) {   // Q of chunk n
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
-                if (load_owner(outputs, NK + j) != me) continue;
-                stage[loads_owned(outputs, NK + j, me)] =
+                if (load_owner(two_compute, NK + j) != me) continue;
+                stage[loads_owned(two_compute, NK + j, me)] =
                     gload16(rq, voff_k[j & 3], static_cast<uint32_t>(4 * j * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
             }
         };
@@ -632,8 +638,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             unsigned char* dst = qst + (n & 1) * QSB + 16 * lane;
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
-                if (load_owner(outputs, NK + j) != me) continue;
-                *reinterpret_cast<u32x4*>(dst + j * 1024) = stage[loads_owned(outputs, NK + j, me)];
+                if (load_owner(two_compute, NK + j) != me) continue;
+                *reinterpret_cast<u32x4*>(dst + j * 1024) = stage[loads_owned(two_compute, NK + j, me)];
             }
         };
         // Iteration n: stores of the loads of iteration n - 2, then the loads of iteration
@@ -800,12 +806,15 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
-    if (wave != 0) {
+    if (wave != 0 && !dual) {
         for (int n = n0; n <= n1; ++n) chunk_barrier(false);
         return;
     }
 
-    // ---------------- chain wave ----------------
+    // ---------------- chain wave(s) ----------------
+    auto chain = [&](auto hv_tag, auto sp_tag, int init_mode, float* s_out) {
+    constexpr bool cHasV = decltype(hv_tag)::value != 0;
+    constexpr bool cSplit = decltype(sp_tag)::value != 0;
     // Iteration n (between the barriers that open chunks n and n + 1) first applies the
     // state update of chunk n - 1, whose operands (the transposed K fragments and V'')
     // were read and formed in iteration n - 1, while the K fragments of chunk n stream in
@@ -821,8 +830,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             for (int j = 0; j < 4; ++j) {
                 const int row = 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + j;
                 float s0 = 0.f;
-                if (a.init_mode == kInitLoad) s0 = a.s_init[blk * stile + static_cast<int64_t>(row) * ncols + col0 + l16];
-                else if (a.init_mode == kInitIdentity) s0 = (row == col0 + l16) ? 1.f : 0.f;
+                if (init_mode == kInitLoad) s0 = a.s_init[blk * stile + static_cast<int64_t>(row) * ncols + col0 + l16];
+                else if (init_mode == kInitIdentity) s0 = (row == col0 + l16) ? 1.f : 0.f;
                 S[t][j] = s0;
             }
     }
@@ -854,7 +863,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             const bf16x8 kt = __builtin_bit_cast(
                 bf16x8, u32x4{ktr[t][s][0][0], ktr[t][s][0][1], ktr[t][s][1][0], ktr[t][s][1][1]});
             S[t] = mfma16(kt, vb[s], S[t]);
-            if constexpr (kSplit) S[t] = mfma16(kt, vbl[s], S[t]);
+            if constexpr (cSplit) S[t] = mfma16(kt, vbl[s], S[t]);
         }
     };
     for (int n = n0; n < n1; ++n) {
@@ -877,7 +886,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             const bf16x8 kt = __builtin_bit_cast(
                 bf16x8, u32x4{ktr[t][s][0][0], ktr[t][s][0][1], ktr[t][s][1][0], ktr[t][s][1][1]});
             S[t] = mfma16(kt, vb[s], S[t]);
-            if constexpr (kSplit) S[t] = mfma16(kt, vbl[s], S[t]);
+            if constexpr (cSplit) S[t] = mfma16(kt, vbl[s], S[t]);
             kf[i] = lds_frag_b(ks + (i & 3) * 4096 + frag_lane[i >> 2]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -888,13 +897,13 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             eg[r] = *reinterpret_cast<const f32x4*>(gs + 16 * r + 4 * g4);
-            if constexpr (kHasV) vraw[r] = lds_read_tr(vs + 16 * r * 32 + v_lane);
+            if constexpr (cHasV) vraw[r] = lds_read_tr(vs + 16 * r * 32 + v_lane);
         }
         bf16x8 th[6], thl[6];
 #pragma unroll
         for (int j = 0; j < 6; ++j) {
             th[j] = lds_frag_b(ts + j * 1024 + 16 * lane);
-            if constexpr (kSplit) thl[j] = lds_frag_b(tls + j * 1024 + 16 * lane);
+            if constexpr (cSplit) thl[j] = lds_frag_b(tls + j * 1024 + 16 * lane);
         }
         f32x4 egc[4];
 #pragma unroll
@@ -906,7 +915,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         bf16x8 sb[4], sbl[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            if constexpr (kSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
+            if constexpr (cSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
             else sb[s] = pack_frag(S[2 * s], S[2 * s + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -919,7 +928,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * s + r], sb[s], s == 0 ? zero4() : c0[r]);
-            if constexpr (kSplit) {
+            if constexpr (cSplit) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) c0[r] = mfma16(kf[4 * s + r], sbl[s], c0[r]);
             }
@@ -941,14 +950,14 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         f32x4 x[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const f32x4 v4 = kHasV ? bf16x4_to_f32(vraw[r]) : zero4();
+            const f32x4 v4 = cHasV ? bf16x4_to_f32(vraw[r]) : zero4();
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[r][j] = v4[j] - eg[r][j] * c0[r][j];
         }
         bf16x8 xb[2], xbl[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            if constexpr (kSplit) pack_frag_split(x[2 * s], x[2 * s + 1], xb[s], xbl[s]);
+            if constexpr (cSplit) pack_frag_split(x[2 * s], x[2 * s + 1], xb[s], xbl[s]);
             else xb[s] = pack_frag(x[2 * s], x[2 * s + 1]);
         }
         // the scaled old state, off the dependency chain (the fp32 S is next read by the
@@ -965,7 +974,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 #pragma unroll
             for (int s = 0; s <= r / 2; ++s) {
                 u[r] = mfma16(th[tri_block(r, s)], xb[s], u[r]);
-                if constexpr (kSplit) {
+                if constexpr (cSplit) {
                     u[r] = mfma16(th[tri_block(r, s)], xbl[s], u[r]);
                     u[r] = mfma16(thl[tri_block(r, s)], xb[s], u[r]);
                 }
@@ -985,7 +994,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 for (int j = 0; j < 4; ++j) w[r][j] = egc[r][j] * u[r][j];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                if constexpr (kSplit) pack_frag_split(w[2 * s], w[2 * s + 1], vb[s], vbl[s]);
+                if constexpr (cSplit) pack_frag_split(w[2 * s], w[2 * s + 1], vb[s], vbl[s]);
                 else vb[s] = pack_frag(w[2 * s], w[2 * s + 1]);
             }
         }
@@ -1001,8 +1010,15 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + j;
-            a.s_out[blk * stile + static_cast<int64_t>(row) * ncols + col0 + l16] = S[t][j];
+            s_out[blk * stile + static_cast<int64_t>(row) * ncols + col0 + l16] = S[t][j];
         }
+    };
+    if constexpr (dual) {
+        if (wave == 0) chain(IntTag<0>{}, IntTag<1>{}, kInitIdentity, a.m_out);
+        else chain(IntTag<1>{}, IntTag<0>{}, kInitZero, a.s_out);
+    } else {
+        chain(IntTag<kHasV ? 1 : 0>{}, IntTag<kSplit ? 1 : 0>{}, a.init_mode, a.s_out);
+    }
 }
 
 }  // namespace
@@ -1019,10 +1035,12 @@ hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
     int qk_groups = a.Hqk * a.B * a.P;
     const unsigned nblk = static_cast<unsigned>(((qk_groups + 7) / 8) * 8 * (a.H / a.Hqk) * tiles);
     void* args[] = {const_cast<StateArgs*>(&a), &tiles, &qk_groups};
-    // Without values (the summary matrix M) the pass runs with split operands.
-    const void* fn = !a.v ? reinterpret_cast<const void*>(&state_mfma<false, true, false>)
-                   : a.o  ? reinterpret_cast<const void*>(&state_mfma<true, false, true>)
-                          : reinterpret_cast<const void*>(&state_mfma<true, false, false>);
+    // Without values (the summary matrix M) the pass runs with split operands; with
+    // values, no outputs and an M destination it computes M and S together.
+    const void* fn = !a.v      ? reinterpret_cast<const void*>(&state_mfma<false, true, false>)
+                   : a.o       ? reinterpret_cast<const void*>(&state_mfma<true, false, true>)
+                   : a.m_out   ? reinterpret_cast<const void*>(&state_mfma<true, true, false>)
+                               : reinterpret_cast<const void*>(&state_mfma<true, false, false>);
     return hipLaunchKernel(fn, dim3(nblk), dim3(512), args, 0, s);
 }
 

@@ -245,6 +245,26 @@ def test_summary_bf16_narrow_heads_matches_oracle():
         assert_close(np_f64(x), r, TOL_BF16, "bf16 dv32 segments " + n)
 
 
+def test_summary_bf16_both_summaries_in_one_pass():
+    """With dk = dv = 128 on the matrix-core path one pass computes M and S together
+    (the M and S chains of a column tile share their loaded operands). Both match the
+    oracle and, bit for bit, the passes that compute only M or only S; two batch rows,
+    five segments and three value heads per query/key head (so the grid's last XCD
+    slots stay empty)."""
+    inp = small_inputs("seg_bf16_dual", "bf16", 2, 640, 1, 3, 128, 128, seed=9)
+    q64, k64, v64, g64, b64, _ = inp.f64()
+    M_ref, S_ref = oracle.gdn_segment_summary(q64, k64, v64, g64, b64, 128)
+    q, k, v, g, beta, _, _ = to_dev(inp)
+    M, S, _ = gdn.gdn_segment_summary(q, k, v, g, beta, 128)
+    M1, _, _ = gdn.gdn_segment_summary(q, k, v, g, beta, 128, want_s=False)
+    _, S1, _ = gdn.gdn_segment_summary(q, k, v, g, beta, 128, want_m=False)
+    sync()
+    assert_close(np_f64(M), M_ref, TOL_BF16, "one-pass M")
+    assert_close(np_f64(S), S_ref, TOL_BF16, "one-pass S")
+    assert torch.equal(M, M1), "M differs from the M-only pass"
+    assert torch.equal(S, S1), "S differs from the S-only pass"
+
+
 def test_summary_f32_small_matches_oracle():
     inp = small_inputs("seg_f32", "f32", 2, 256, 2, 4, 32, 16, seed=7)
     q64, k64, v64, g64, b64, h064 = inp.f64()
