@@ -358,7 +358,9 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
 //   wave 1, the output wave (forward only), computes one chunk behind the chain
 //     wave O = diag(exp Gam) Q S + P U from the state and U the chain wave leaves in
 //     LDS, transposed (O^T = S^T Q^T + U^T P^T) so that each lane ends up holding
-//     four consecutive columns of one token, and writes o.
+//     four consecutive columns of one token, and writes o. When one pass computes
+//     both segment summaries, wave 0 runs the chain of the M tile and wave 1 the
+//     chain of the S tile instead.
 //   the other waves load the chunk operands into registers and write them to LDS
 //     an iteration later (K, That and its remainder, V and the decay factors of the
 //     next chunk for the chain wave; Q of the current chunk for the output wave,
