@@ -114,7 +114,17 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     // Loads are unconditional from a clamped, in-bounds token (row 0 of the
     // sequence for padded tokens) and masked afterwards, so that no load waits
     // behind a branch.
-    // the q/k loads go out first; the decay scan of wave 0 runs while they are in flight
+    // Wave 0's g and beta loads go out first, then everybody's q/k loads: loads return
+    // in issue order, so the decay scan of wave 0 starts while the q/k loads are still
+    // in flight (issued after them it would wait for all of them).
+    const int64_t tg = t0 + lane;
+    const bool gvalid = tg < nvalid;
+    float graw = 0.f, braw = 0.f;
+    if (wave == 0) {
+        const int64_t gi = (static_cast<int64_t>(b) * a.T + (gvalid ? tg : 0)) * a.H + h;
+        graw = a.g[gi];
+        braw = a.beta[gi];
+    }
     u32x4 kv[4], qv[4];
     {
 #pragma unroll
@@ -128,12 +138,8 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         }
     }
     if (wave == 0) {
-        const int64_t t = t0 + lane;
-        const bool valid = t < nvalid;
-        const int64_t gi = (static_cast<int64_t>(b) * a.T + (valid ? t : 0)) * a.H + h;
-        const float graw = a.g[gi], braw = a.beta[gi];
-        float gam = valid ? graw : 0.f;
-        const float bt = valid ? braw : 0.f;
+        float gam = gvalid ? graw : 0.f;
+        const float bt = gvalid ? braw : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(gam, off, 64);
