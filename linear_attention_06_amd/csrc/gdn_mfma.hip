@@ -41,6 +41,11 @@ __host__ __device__ constexpr int tri_block(int r, int s) { return r < 2 ? r : 2
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// A compile-time integer as a value (template arguments of generic lambdas).
+template <int V>
+struct IntTag {
+    static constexpr int value = V;
+};
 __device__ __forceinline__ f32x4 mfma16f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -140,14 +145,23 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     if (wave == 0) {
         float gam = gvalid ? graw : 0.f;
         const float bt = gvalid ? braw : 0.f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(gam, off, 64);
-            if (lane >= off) gam += y;
-        }
+        // inclusive scan over the 64 lanes with DPP moves: shifts by 1, 2, 4, 8 inside
+        // each row of 16 lanes (lanes shifted in from outside the row read 0), then lane
+        // 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3
+        const auto dpp_add = [](float x, auto ctrl_tag, auto rows_tag) {
+            const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl_tag)::value,
+                                                      decltype(rows_tag)::value, 0xf, true);
+            return x + __int_as_float(y);
+        };
+        gam = dpp_add(gam, IntTag<0x111>{}, IntTag<0xf>{});   // row_shr:1
+        gam = dpp_add(gam, IntTag<0x112>{}, IntTag<0xf>{});   // row_shr:2
+        gam = dpp_add(gam, IntTag<0x114>{}, IntTag<0xf>{});   // row_shr:4
+        gam = dpp_add(gam, IntTag<0x118>{}, IntTag<0xf>{});   // row_shr:8
+        gam = dpp_add(gam, IntTag<0x142>{}, IntTag<0xa>{});   // row_bcast:15
+        gam = dpp_add(gam, IntTag<0x143>{}, IntTag<0xc>{});   // row_bcast:31
         gam_s[lane] = gam;
         beta_s[lane] = bt;
-        const float gam_c = __shfl(gam, 63, 64);
+        const float gam_c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), 63));
         a.ws.gates[ch * 128 + lane] = __expf(gam);
         a.ws.gates[ch * 128 + 64 + lane] = __expf(gam_c - gam);
     }
@@ -398,10 +412,6 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-template <int V>
-struct IntTag {
-    static constexpr int value = V;
-};
 // Two accumulator tiles (4 rows each per lane) as one bf16 B fragment.
 __device__ __forceinline__ bf16x8 pack_frag(const f32x4& a, const f32x4& b) {
     bf16x8 f;
