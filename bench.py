@@ -132,6 +132,44 @@ def segmented_timing(gdn, q, k, v, g, beta, h0, stream, timed):
     return res
 
 
+def prologue_timing(gdn, inp, dev, stream, timed):
+    """The forward with the input prologue fused in (gdn_chunk_fwd_prologue on the raw
+    q/k draws and the gate inputs a, b, A_log, dt_bias of the same workload), beside the
+    same prologue as separate torch ops followed by gdn_chunk_fwd (for comparison only)."""
+    import torch
+
+    w = inp.w
+    r = inp.raw
+
+    def io(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.int16).view(torch.bfloat16).to(dev)
+
+    f = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    q_raw, k_raw, v = io(r["q_raw"]), io(r["k_raw"]), io(inp.v)
+    a, b, A_log, dt_bias, h0 = f(r["a"]), f(r["b"]), f(r["A_log"]), f(r["dt_bias"]), f(inp.h0)
+    p = gdn.problem(q_raw, v)
+    ws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
+    o = torch.empty_like(v)
+    hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    scale = w.dk ** -0.5
+
+    def fused():
+        gdn.gdn_chunk_fwd_prologue(q_raw, k_raw, v, a, b, A_log, dt_bias, scale, h0, o=o, hT=hT, ws=ws,
+                                   stream=stream)
+
+    def separate():
+        with torch.cuda.stream(stream):
+            qn = torch.nn.functional.normalize(q_raw.float(), dim=-1).mul_(scale).to(torch.bfloat16)
+            kn = torch.nn.functional.normalize(k_raw.float(), dim=-1).to(torch.bfloat16)
+            g = -torch.exp(A_log) * torch.nn.functional.softplus(a + dt_bias)
+            beta = torch.sigmoid(b)
+        gdn.gdn_chunk_fwd(qn, kn, v, g, beta, h0, o=o, hT=hT, ws=ws, stream=stream)
+
+    ms_f, ms_s = timed(fused, 10), timed(separate, 10)
+    return {"fused_ms": ms_f, "fused_tokens_per_s": w.B * w.T / (ms_f * 1e-3),
+            "torch_prologue_then_core_ms": ms_s}
+
+
 def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
     """gdn_chunk_fwd step time on the stateless 8K and padded 8K workloads."""
     import torch
@@ -307,6 +345,7 @@ def main():
     if not args.no_extra:
         line["segmented_32k"] = segmented_timing(gdn, q, k, v, g, beta, h0, stream, timed)
         line["other_workloads"] = other_workloads(gdn, WORKLOADS, make_inputs, dev, stream, timed)
+        line["fused_prologue_32k"] = prologue_timing(gdn, inp, dev, stream, timed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line))

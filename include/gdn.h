@@ -106,6 +106,33 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Forward with the layer's input prologue fused into the chunk prepare pass
+ * (PR #1035, section "What does this PR do": each rank projects Q/K/V/B/A and
+ * runs the Gated DeltaNet on them; issue #320's gradient checks name the A_log
+ * and dt_bias parameters of the decay gate). Per token t, query/key head and
+ * value head h:
+ *     q_t  = q_scale * q_raw_t / max(|q_raw_t|, 1e-12)      (L2 norm over dk)
+ *     k_t  = k_raw_t / max(|k_raw_t|, 1e-12)
+ *     g_t  = -exp(A_log[h]) * softplus(a_t + dt_bias[h]),   softplus(x) = log(1 + e^x)
+ *     beta_t = 1 / (1 + exp(-b_t))
+ * then the same forward as gdn_chunk_fwd on (q, k, v, g, beta). The norms are taken
+ * in fp32 over the bf16 inputs and applied to the fp32 products, so q and k are
+ * never rounded after normalisation.
+ *   q_raw, k_raw [B, T, Hqk, dk] bf16;  v, o [B, T, H, dv] bf16;
+ *   a, b [B, T, H] fp32;  A_log, dt_bias [H] fp32;  q_scale a finite float
+ *   (1/sqrt(dk) for the usual attention scale);  h0, hT as in gdn_chunk_fwd.
+ * Runs on the bf16 matrix-core path only (io_dtype GDN_BF16, dk == 128); other
+ * problems return GDN_EUNSUPPORTED. Padded tokens (valid_len) are treated as
+ * beta = 0, g = 0 whatever a and b hold. The workspace is gdn_chunk_fwd_workspace().
+ */
+gdn_status gdn_chunk_fwd_prologue(const gdn_problem* p,
+                                  const void* q_raw, const void* k_raw, const void* v,
+                                  const float* a, const float* b,
+                                  const float* A_log, const float* dt_bias, float q_scale,
+                                  const float* h0, void* o, float* hT,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace for the segment calls (gdn_segment_summary, then
  * gdn_apply_initial_state on the same workspace). seg_len must be a positive
  * multiple of 64 that divides T; P = T / seg_len segments.

@@ -56,7 +56,8 @@ Plan make_plan(const gdn_problem& p, bool segments) {
     pl.that_off = 0;
     pl.pmat_off = mat;
     pl.gates_off = 2 * mat;
-    pl.bytes = 2 * mat + align256(static_cast<size_t>(pl.nch) * 128 * sizeof(float));
+    const size_t gate = mfma ? gdn::kGateRecordMfma : gdn::kGateRecordF32;
+    pl.bytes = 2 * mat + align256(static_cast<size_t>(pl.nch) * gate * sizeof(float));
     pl.lo = mfma && segments;
     if (pl.lo) {
         pl.that_lo_off = pl.bytes;
@@ -119,11 +120,14 @@ gdn_status check_segments(const gdn_problem& p, int32_t seg_len, int64_t* P) {
 }
 
 gdn_status run_prep(const gdn_problem& p, const Plan& pl, const void* q, const void* k,
-                    const float* g, const float* beta, const gdn::Workspace& w, hipStream_t s) {
+                    const float* g, const float* beta, const gdn::Workspace& w, hipStream_t s,
+                    const gdn::Prologue* pro = nullptr) {
     if (pl.nch == 0) return GDN_OK;
     gdn::PrepArgs a;
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.NT = static_cast<int>(pl.NT);
     a.q = q; a.k = k; a.g = g; a.beta = beta; a.valid_len = p.valid_len; a.ws = w;
+    a.has_prologue = pro ? 1 : 0;
+    a.pro = pro ? *pro : gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
     hipError_t e = use_mfma(p) ? gdn::launch_prep_mfma(a, s)
                                : gdn::launch_prep_f32path(a, p.io_dtype == GDN_BF16, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "prepare kernel launch");
@@ -202,6 +206,42 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
         a.s_out = hT;
         a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
         return run_state(*p, a, s);
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_chunk_fwd_prologue(const gdn_problem* p, const void* q_raw, const void* k_raw, const void* v,
+                                  const float* a, const float* b, const float* A_log, const float* dt_bias,
+                                  float q_scale, const float* h0, void* o, float* hT, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        if (!use_mfma(*p))
+            return fail(GDN_EUNSUPPORTED, "the fused prologue runs on the bf16 matrix-core path only "
+                                          "(io_dtype GDN_BF16, dk = 128)");
+        if (!(q_scale == q_scale) || q_scale - q_scale != 0.f)
+            return fail(GDN_EINVAL, "q_scale must be finite");
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q_raw || !k_raw || !v || !a || !b || !A_log || !dt_bias || !o))
+            return fail(GDN_EINVAL, "q_raw, k_raw, v, a, b, A_log, dt_bias and o must be non-NULL");
+        const Plan pl = make_plan(*p, false);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (p->B == 0) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const gdn::Workspace w = carve(pl, ws);
+        const gdn::Prologue pro{a, b, A_log, dt_bias, q_scale};
+        st = run_prep(*p, pl, q_raw, k_raw, nullptr, nullptr, w, s, &pro);
+        if (st != GDN_OK) return st;
+        gdn::StateArgs sa = state_args(*p, pl, q_raw, k_raw, v, w);
+        sa.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+        sa.s_init = h0;
+        sa.o = o;
+        sa.s_out = hT;
+        sa.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+        return run_state(*p, sa, s);
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

@@ -11,6 +11,10 @@ namespace gdn {
 constexpr int kChunk = 64;
 // bf16 elements of one That or P record on the matrix-core path (6 blocks of 64 x 8)
 constexpr int kTriRecordElems = 6 * 512;
+// fp32 words of one decay record: 128 on the fp32 path (exp(Gam), exp(Gam_C - Gam)),
+// 256 on the matrix-core path (see prep_mfma)
+constexpr int kGateRecordF32 = 128;
+constexpr int kGateRecordMfma = 256;
 
 // How a state pass starts.
 enum InitMode : int { kInitZero = 0, kInitLoad = 1, kInitIdentity = 2 };
@@ -22,9 +26,13 @@ enum StoreMode : int { kStoreNone = 0, kStoreEverySegment = 1, kStoreLastSegment
 //   that  [64][64]  Tinv diag(beta), Tinv = (I + A)^{-1},
 //                   A_ij = beta_i exp(Gam_i - Gam_j) k_i.k_j (i > j)
 //   pmat  [64][64]  P_ij = (q_i.k_j) exp(Gam_i - Gam_j) for j <= i, else 0
-//   gates [2][64]   exp(Gam_i) and exp(Gam_C - Gam_i), Gam = chunk-local cumsum of g
+//   gates           fp32 decay factors, Gam = chunk-local cumsum of g:
+//                   fp32 path [2][64]: exp(Gam_i), exp(Gam_C - Gam_i);
+//                   matrix-core path [4][64]: exp(Gam_i) rk_i, exp(Gam_C - Gam_i) rk_i,
+//                   exp(Gam_i) rq_i, then exp(Gam_C) and zeros, where rk_i and rq_i are the
+//                   row factors of the fused prologue (1/|k_i|, q_scale/|q_i|) or 1
 // The element type of that/pmat is fp32 on the fp32 path and bf16 on the
-// matrix-core path; gates are always fp32.
+// matrix-core path.
 struct Workspace {
     void* that;
     void* pmat;
@@ -32,14 +40,27 @@ struct Workspace {
     void* that_lo;   // matrix-core path, segment calls only: bf16 remainder That - bf16(That), or NULL
 };
 
+// Input prologue of the layer, fused into the prepare pass (matrix-core path):
+// q = q_raw q_scale / |q_raw|, k = k_raw / |k_raw| per token and query/key head,
+// g = -exp(A_log[h]) softplus(a + dt_bias[h]), beta = sigmoid(b).
+struct Prologue {
+    const float* a;        // [B,T,H]
+    const float* b;        // [B,T,H]
+    const float* A_log;    // [H]
+    const float* dt_bias;  // [H]
+    float q_scale;
+};
+
 struct PrepArgs {
     int B, T, H, Hqk, dk, NT;
     const void* q;
     const void* k;
-    const float* g;
-    const float* beta;
+    const float* g;         // unused with a prologue
+    const float* beta;      // unused with a prologue
     const int32_t* valid_len;
     Workspace ws;
+    int has_prologue;       // 0: q, k, g, beta are used as given
+    Prologue pro;
 };
 
 struct StateArgs {

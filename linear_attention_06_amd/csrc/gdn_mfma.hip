@@ -55,6 +55,15 @@ __device__ __forceinline__ f32x16 zero16() {
     for (int i = 0; i < 16; ++i) z[i] = 0.f;
     return z;
 }
+// Inclusive prefix sum over each row of 16 lanes with DPP row shifts by 1, 2, 4, 8
+// (lanes shifted in from outside the row read 0): lane 15 of a row ends with the row total.
+__device__ __forceinline__ float row_prefix16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+    return x;
+}
 __device__ __forceinline__ int64_t valid_tokens(const int32_t* vl, int b, int64_t T) {
     if (!vl) return T;
     int64_t n = vl[b];
@@ -81,11 +90,14 @@ __device__ __forceinline__ void lds_sync() {
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     constexpr int AP = 68;  // fp32 pitch of the 64x64 A and Tinv tiles
-    // 34.5 KiB, four blocks per CU: K and Q (bf16, 256-byte rows) fill the first 32 KiB
+    // 35.8 KiB, four blocks per CU: K and Q (bf16, 256-byte rows) fill the first 32 KiB
     // until the products are done; then A lives at the start and Tinv behind it; once
-    // the solve is done P (bf16) takes the place of A. The decay scan and beta follow.
+    // the solve is done P (bf16) takes the place of A. Seven 64-float vectors follow:
+    // Gam, beta, the prologue's row factors rk = 1/|k_t| and rq = q_scale/|q_t| (1 without
+    // a prologue), and the exponents that fold them into the decay masks,
+    // Gam_t + ln rk_t, Gam_s - ln rk_s and Gam_t + ln rq_t.
     constexpr int TS_OFF = 64 * AP * 4, GB_OFF = 2 * 64 * AP * 4;
-    __shared__ __align__(16) unsigned char smem[GB_OFF + 512];
+    __shared__ __align__(16) unsigned char smem[GB_OFF + 7 * 256];
     uint16_t* k_s = reinterpret_cast<uint16_t*>(smem);
     uint16_t* q_s = k_s + 64 * DK;
     float* a_s = reinterpret_cast<float*>(smem);              // after the products
@@ -93,6 +105,11 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     uint16_t* p_s = reinterpret_cast<uint16_t*>(smem);        // after the solve
     float* gam_s = reinterpret_cast<float*>(smem + GB_OFF);
     float* beta_s = gam_s + 64;
+    float* rk_s = gam_s + 128;
+    float* rq_s = gam_s + 192;
+    float* gk_s = gam_s + 256;    // Gam_t + ln rk_t  (row side of A)
+    float* gks_s = gam_s + 320;   // Gam_s - ln rk_s  (column side of A and P)
+    float* gq_s = gam_s + 384;    // Gam_t + ln rq_t  (row side of P)
     // K / Q element offset of granule g (8 bf16) of row r: XOR-swizzled by the row so
     // that the fragment reads of 16 consecutive rows hit 16 different bank groups
     const auto kq_at = [](int r, int g) { return r * DK + 8 * (g ^ (r & 15)); };
@@ -124,11 +141,12 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     // in flight (issued after them it would wait for all of them).
     const int64_t tg = t0 + lane;
     const bool gvalid = tg < nvalid;
+    // With the prologue, a and b take the place of g and beta.
     float graw = 0.f, braw = 0.f;
     if (wave == 0) {
         const int64_t gi = (static_cast<int64_t>(b) * a.T + (gvalid ? tg : 0)) * a.H + h;
-        graw = a.g[gi];
-        braw = a.beta[gi];
+        graw = a.has_prologue ? a.pro.a[gi] : a.g[gi];
+        braw = a.has_prologue ? a.pro.b[gi] : a.beta[gi];
     }
     u32x4 kv[4], qv[4];
     {
@@ -143,8 +161,16 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         }
     }
     if (wave == 0) {
-        float gam = gvalid ? graw : 0.f;
-        const float bt = gvalid ? braw : 0.f;
+        float gv = graw, bv = braw;
+        if (a.has_prologue) {
+            // g = -exp(A_log) softplus(a + dt_bias), softplus(x) = max(x, 0) + log(1 + exp(-|x|));
+            // beta = sigmoid(b)
+            const float x = graw + a.pro.dt_bias[h];
+            gv = -__expf(a.pro.A_log[h]) * (fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));
+            bv = 1.f / (1.f + __expf(-braw));
+        }
+        float gam = gvalid ? gv : 0.f;
+        const float bt = gvalid ? bv : 0.f;
         // inclusive scan over the 64 lanes with DPP moves: shifts by 1, 2, 4, 8 inside
         // each row of 16 lanes (lanes shifted in from outside the row read 0), then lane
         // 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3
@@ -161,9 +187,6 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         gam = dpp_add(gam, IntTag<0x143>{}, IntTag<0xc>{});   // row_bcast:31
         gam_s[lane] = gam;
         beta_s[lane] = bt;
-        const float gam_c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), 63));
-        a.ws.gates[ch * 128 + lane] = __expf(gam);
-        a.ws.gates[ch * 128 + 64 + lane] = __expf(gam_c - gam);
     }
     {
         const u32x4 z = {0u, 0u, 0u, 0u};
@@ -171,11 +194,55 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         for (int u = 0; u < 4; ++u) {
             const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
             const bool valid = t0 + row < nvalid;
-            *reinterpret_cast<u32x4*>(k_s + kq_at(row, cb)) = valid ? kv[u] : z;
-            *reinterpret_cast<u32x4*>(q_s + kq_at(row, cb)) = valid ? qv[u] : z;
+            if (!valid) kv[u] = qv[u] = z;
+            *reinterpret_cast<u32x4*>(k_s + kq_at(row, cb)) = kv[u];
+            *reinterpret_cast<u32x4*>(q_s + kq_at(row, cb)) = qv[u];
         }
     }
+    if (a.has_prologue) {
+        // row norms: the 16 lanes of a row (a DPP row of consecutive lanes) each hold 8 of
+        // its values
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float k0 = __uint_as_float(kv[u][e] << 16), k1 = __uint_as_float(kv[u][e] & 0xFFFF0000u);
+                const float q0 = __uint_as_float(qv[u][e] << 16), q1 = __uint_as_float(qv[u][e] & 0xFFFF0000u);
+                sk += k0 * k0 + k1 * k1;
+                sq += q0 * q0 + q1 * q1;
+            }
+            // 1 / max(|x|, 1e-12) as the reciprocal square root of max(|x|^2, 1e-24)
+            const float rk = __builtin_amdgcn_rsqf(fmaxf(row_prefix16(sk), 1e-24f));
+            const float rq = a.pro.q_scale * __builtin_amdgcn_rsqf(fmaxf(row_prefix16(sq), 1e-24f));
+            if ((tid & 15) == 15) {
+                const int row = (tid >> 4) + 16 * u;
+                rk_s[row] = rk;
+                rq_s[row] = rq;
+            }
+        }
+    } else if (tid < 64) {
+        rk_s[tid] = 1.f;
+        rq_s[tid] = 1.f;
+    }
     lds_sync();
+    if (wave == 2) {
+        // the decay record: exp(Gam) rk, exp(Gam_C - Gam) rk, exp(Gam) rq, exp(Gam_C)
+        const float gam = gam_s[lane], gam_c = gam_s[63], rk = rk_s[lane], rq = rq_s[lane];
+        const float eg = __expf(gam);
+        float* gr = a.ws.gates + ch * kGateRecordMfma;
+        gr[lane] = eg * rk;
+        gr[64 + lane] = __expf(gam_c - gam) * rk;
+        gr[128 + lane] = eg * rq;
+        gr[192 + lane] = lane == 0 ? __expf(gam_c) : 0.f;
+    } else if (wave == 3) {
+        // the exponents of the decay masks of A and P with the row factors folded in
+        // (ln 1 = 0 exactly without a prologue)
+        const float gam = gam_s[lane], lk = __logf(rk_s[lane]);
+        gk_s[lane] = gam + lk;
+        gks_s[lane] = gam - lk;
+        gq_s[lane] = gam + __logf(rq_s[lane]);
+    }
 
     // K K^T and Q K^T on the lower 32x32 tiles: (row tile, col tile) in
     // {(0,0), (1,0), (1,1)} for each; six products over four waves.
@@ -206,11 +273,11 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     // between them would be issued one at a time.
     auto emit_a = [&](const f32x16& acc, int mi, int nj) {
         const int s = 32 * nj + lr;
-        const float gs = gam_s[s];
+        const float gs = gks_s[s];
         f32x4 gt[4], bt[4];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-            gt[i4] = *reinterpret_cast<const f32x4*>(gam_s + 32 * mi + 8 * i4 + 4 * q);
+            gt[i4] = *reinterpret_cast<const f32x4*>(gk_s + 32 * mi + 8 * i4 + 4 * q);
             bt[i4] = *reinterpret_cast<const f32x4*>(beta_s + 32 * mi + 8 * i4 + 4 * q);
         }
 #pragma unroll
@@ -230,10 +297,10 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     f32x16 pq = (wave == 0) ? acc1 : acc0;
     if (has_p) {
         const int s = 32 * p_nj + lr;
-        const float gs = gam_s[s];
+        const float gs = gks_s[s];
         f32x4 gt[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) gt[i4] = *reinterpret_cast<const f32x4*>(gam_s + 32 * p_mi + 8 * i4 + 4 * q);
+        for (int i4 = 0; i4 < 4; ++i4) gt[i4] = *reinterpret_cast<const f32x4*>(gq_s + 32 * p_mi + 8 * i4 + 4 * q);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 32 * p_mi + 8 * (i / 4) + 4 * q + (i % 4);
@@ -576,7 +643,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const __amdgpu_buffer_rsrc_t rtl = make_rsrc(
             kSplit ? static_cast<const uint16_t*>(a.ws.that_lo) + bh * a.NT * kTriRecord : static_cast<const uint16_t*>(a.ws.that),
             rec);
-        const __amdgpu_buffer_rsrc_t rgt = make_rsrc(a.ws.gates + bh * a.NT * 128, static_cast<int64_t>(a.NT) * 512);
+        const __amdgpu_buffer_rsrc_t rgt = make_rsrc(a.ws.gates + bh * a.NT * kGateRecordMfma,
+                                                     static_cast<int64_t>(a.NT) * kGateRecordMfma * 4);
 
         // lane l of a quad-block load: slot l = 16 rho + c, row 4j + rho, granule c ^ (4 rho + j % 4)
         uint32_t voff_k[4];
@@ -626,7 +694,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 } else if (kHasV && i < NK - 1) {
                     r = gload16(rv, voff_v[i - (NK - 3)], static_cast<uint32_t>(n) * vstep);
                 } else {
-                    r = gload16(rgt, voff_l, static_cast<uint32_t>(n) * 512u);
+                    r = gload16(rgt, voff_l, static_cast<uint32_t>(n) * (kGateRecordMfma * 4u));
                 }
             }
         };
@@ -736,8 +804,10 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 pf_base = reinterpret_cast<const unsigned char*>(rec + bh * a.NT * kTriRecord) + 128 * (lam % 48);
                 pf_stride = kTriRecord * 2;
             } else {
-                pf_base = reinterpret_cast<const unsigned char*>(a.ws.gates + bh * a.NT * 128) + 128 * (lane - 60);
-                pf_stride = 512;
+                // the first 768 bytes of the 1 KiB decay record; even and odd tiles split them
+                pf_base = reinterpret_cast<const unsigned char*>(a.ws.gates + bh * a.NT * kGateRecordMfma) +
+                          128 * (lane - 60) + 384 * (tile & 1);
+                pf_stride = kGateRecordMfma * 4;
             }
         }
         const uint32_t pf_lds = lds_addr(pf_s);
@@ -787,7 +857,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                     o0 = mfma16(sb[s], lds_frag_b(qs + r * 4096 + frag_lane[s]), o0);
                     o1 = mfma16(sb[s + 1], lds_frag_b(qs + r * 4096 + frag_lane[s + 1]), o1);
                 }
-                const float e = gs[16 * r + l16];
+                const float e = gs[128 + 16 * r + l16];   // exp(Gam) rq
                 f32x4 o;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o[j] = e * (o0[j] + o1[j]);
@@ -926,7 +996,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         f32x4 egc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) egc[r] = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
-        const float egC = gs[63];
+        const float egC = gs[192];   // exp(Gam_C)
         __builtin_amdgcn_sched_barrier(0);
 
         // the state of chunk n as bf16 B fragments of K S (and for the output wave)

@@ -23,7 +23,7 @@ CHUNK = 64
 
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
-           "gdn_chunk_fwd",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_prologue",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
            "gdn_apply_initial_state")
 
@@ -62,10 +62,13 @@ def lib():
         L.gdn_chunk_fwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
         L.gdn_segment_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
         L.gdn_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_chunk_fwd_prologue.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+                                             vp, sz, vp]
         L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd",
+                     "gdn_chunk_fwd_prologue",
                      "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -165,6 +168,34 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, valid_len=None, o=None, hT=None, wa
     _check(lib().gdn_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_chunk_fwd")
+    return o, hT
+
+
+def gdn_chunk_fwd_prologue(q_raw, k_raw, v, a, b, A_log, dt_bias, q_scale=None, h0=None,
+                           valid_len=None, o=None, hT=None, want_state=True, ws=None, stream=None):
+    """Forward with the input prologue fused in: q_raw, k_raw are normalised per token and
+    head (q also scaled by q_scale, default 1/sqrt(dk)), g = -exp(A_log) softplus(a + dt_bias),
+    beta = sigmoid(b). Returns (o, hT or None)."""
+    for t, n in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v, "v")):
+        _dev(t, n, q_raw.dtype)
+    for t, n in ((a, "a"), (b, "b"), (A_log, "A_log"), (dt_bias, "dt_bias"), (h0, "h0")):
+        _dev(t, n, torch.float32)
+    p = problem(q_raw, v, valid_len)
+    if q_scale is None:
+        q_scale = p.dk ** -0.5
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    _dev(o, "o", v.dtype)
+    if hT is None and want_state:
+        hT = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=v.device)
+    _dev(hT, "hT", torch.float32)
+    need = gdn_chunk_fwd_workspace(p)
+    if ws is None:
+        ws = workspace(need, v.device)
+    _check(lib().gdn_chunk_fwd_prologue(ctypes.byref(p), _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(a), _ptr(b),
+                                        _ptr(A_log), _ptr(dt_bias), ctypes.c_float(q_scale), _ptr(h0),
+                                        _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_chunk_fwd_prologue")
     return o, hT
 
 

@@ -15,6 +15,9 @@ Derived in float64: q = q_raw / |q_raw| / sqrt(dk), k = k_raw / |k_raw| (per tok
 and head), g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b). g and beta
 are stored as float32; q, k, v in the I/O dtype (bf16 by round-to-nearest-even
 from float32). Tokens at or past valid_len[b] get beta = 0 and g = 0.
+The raw draws (q_raw, k_raw in the I/O dtype; a, b, and A_log, dt_bias cast to
+float32) are kept too, as the inputs of the fused-prologue forward; there, pads
+keep their random a and b.
 
 The shapes follow the GDN-core workloads of hyper-parallel issue #320 (test
 report for PR #1114): section 4.1 (16 query/key heads copied to 32 value heads,
@@ -96,6 +99,7 @@ class Inputs:
     beta: np.ndarray         # [B,T,H] float32
     h0: Optional[np.ndarray]  # [B,H,dk,dv] float32 or None
     valid_len: Optional[np.ndarray]  # [B] int32 or None
+    raw: Optional[dict] = None       # q_raw, k_raw (I/O dtype), a, b [B,T,H], A_log, dt_bias [H] (float32)
 
     def io_f32(self, name: str) -> np.ndarray:
         x = getattr(self, name)
@@ -106,6 +110,16 @@ class Inputs:
         q, k, v = (self.io_f32(n).astype(np.float64) for n in ("q", "k", "v"))
         h0 = None if self.h0 is None else self.h0.astype(np.float64)
         return q, k, v, self.g.astype(np.float64), self.beta.astype(np.float64), h0
+
+    def raw_f64(self):
+        """Exact float64 copies of the fused-prologue inputs:
+        (q_raw, k_raw, v, a, b, A_log, dt_bias, h0)."""
+        r = self.raw
+        io = (lambda x: bf16_bits_to_f32(x)) if self.w.io == "bf16" else (lambda x: x)
+        h0 = None if self.h0 is None else self.h0.astype(np.float64)
+        return (io(r["q_raw"]).astype(np.float64), io(r["k_raw"]).astype(np.float64),
+                self.io_f32("v").astype(np.float64), r["a"].astype(np.float64), r["b"].astype(np.float64),
+                r["A_log"].astype(np.float64), r["dt_bias"].astype(np.float64), h0)
 
 
 def _softplus(x):
@@ -151,8 +165,12 @@ def make_inputs(w: Workload, T: Optional[int] = None, B: Optional[int] = None) -
     q32, k32 = q64.astype(np.float32), k64.astype(np.float32)
     if w.io == "bf16":
         qs, ks, vs = f32_to_bf16_bits(q32), f32_to_bf16_bits(k32), f32_to_bf16_bits(v)
+        qr, kr = f32_to_bf16_bits(q_raw), f32_to_bf16_bits(k_raw)
     elif w.io == "f32":
         qs, ks, vs = q32, k32, v
+        qr, kr = q_raw, k_raw
     else:
         raise ValueError(w.io)
-    return Inputs(w, qs, ks, vs, g, beta, h0, valid)
+    raw = {"q_raw": qr, "k_raw": kr, "a": a, "b": b, "A_log": a_log.astype(np.float32),
+           "dt_bias": dt_bias.astype(np.float32)}
+    return Inputs(w, qs, ks, vs, g, beta, h0, valid, raw)

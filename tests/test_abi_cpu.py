@@ -99,6 +99,30 @@ def test_fwd_argument_checks_return_before_launch():
     assert call_fwd(P(chunk=128), ws=256, nbytes=need) == gdn.GDN_EUNSUPPORTED
 
 
+def call_fwd_prologue(p, q=1, k=1, v=1, a=1, b=1, A_log=1, dt_bias=1, q_scale=0.125, o=1, ws=256,
+                      nbytes=1 << 40):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return gdn.lib().gdn_chunk_fwd_prologue(ctypes.byref(p), vp(q), vp(k), vp(v), vp(a), vp(b), vp(A_log),
+                                            vp(dt_bias), ctypes.c_float(q_scale), None, vp(o), None, vp(ws),
+                                            nbytes, None)
+
+
+def test_fwd_prologue_argument_checks_return_before_launch():
+    bf = P(H=4, Hqk=2, dk=128, dv=128, io_dtype=gdn.GDN_BF16)
+    assert call_fwd_prologue(P()) == gdn.GDN_EUNSUPPORTED                 # fp32 path
+    assert call_fwd_prologue(P(dk=64, dv=64, io_dtype=gdn.GDN_BF16)) == gdn.GDN_EUNSUPPORTED
+    for name in ("q", "k", "v", "a", "b", "A_log", "dt_bias", "o"):
+        assert call_fwd_prologue(bf, **{name: None}) == gdn.GDN_EINVAL, name
+    assert call_fwd_prologue(bf, q_scale=float("nan")) == gdn.GDN_EINVAL
+    assert call_fwd_prologue(bf, q_scale=float("inf")) == gdn.GDN_EINVAL
+    assert call_fwd_prologue(bf, ws=None, nbytes=0) == gdn.GDN_EWORKSPACE
+    _, need = ws_status(bf)
+    assert call_fwd_prologue(bf, nbytes=need - 1) == gdn.GDN_EWORKSPACE
+    # the decay record of the matrix-core path is 256 floats per chunk and head
+    nch = 1 * 4 * 2
+    assert need >= nch * (2 * 6 * 512 * 2 + 256 * 4)
+
+
 def test_segment_argument_checks():
     L = gdn.lib()
     n = ctypes.c_size_t(0)
