@@ -171,7 +171,8 @@ def prologue_timing(gdn, inp, dev, stream, timed):
 
 
 def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
-    """gdn_chunk_fwd step time on the stateless 8K and padded 8K workloads."""
+    """gdn_chunk_fwd step time on the stateless 8K and padded 8K workloads, and the padded
+    rows packed as variable-length sequences (gdn_chunk_fwd_varlen)."""
     import torch
 
     out = {}
@@ -196,6 +197,23 @@ def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
 
         ms = timed(step, 10)
         out[name] = {"B": w.B, "T": w.T, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
+        if name == "padded_8k":
+            # the same rows packed without their padding, as variable-length sequences
+            L = int(inp.valid_len[0])
+            pk = lambda x: torch.cat([x[r:r + 1, :L] for r in range(w.B)], dim=1).contiguous()
+            qp, kp, vp, gp, bp = pk(q), pk(k), pk(v), pk(g), pk(beta)
+            cu = torch.arange(0, (w.B + 1) * L, L, dtype=torch.int32, device=dev)
+            pp = gdn.problem(qp, vp)
+            pp.B = w.B
+            wsp = gdn.workspace(gdn.gdn_chunk_fwd_varlen_workspace(pp, L), dev)
+            op = torch.zeros_like(vp)
+
+            def step_varlen():
+                gdn.gdn_chunk_fwd_varlen(qp, kp, vp, gp, bp, cu, L, o=op, hT=hT, ws=wsp, stream=stream)
+
+            ms = timed(step_varlen, 10)
+            out["packed_varlen_2x7777"] = {"sequences": w.B, "T": w.B * L, "ms_per_step": ms,
+                                           "tokens_per_s": w.B * L / (ms * 1e-3)}
     return out
 
 

@@ -133,6 +133,29 @@ gdn_status gdn_chunk_fwd_prologue(const gdn_problem* p,
                                   void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Packed variable-length sequences (the general form of issue #320's variable-length
+ * case, section 5.2, where rows of one batch hold different numbers of valid tokens):
+ * instead of B rows of T tokens with padding, the B sequences lie back to back in one
+ * packed token dimension of p->T tokens,
+ *   q, k [1, T, Hqk, dk];  v, o [1, T, H, dv];  g, beta [1, T, H],
+ * sequence b at tokens cu_seqlens[b] .. cu_seqlens[b+1] - 1 (cu_seqlens: device
+ * int32[B + 1], non-decreasing from 0 to T). Each sequence runs its own recurrence from
+ * h0[b] (h0, hT [B, H, dk, dv]; h0 NULL = zero states) and its chunks start at its own
+ * first token, so the result for a sequence equals gdn_chunk_fwd on that sequence alone.
+ * max_seqlen (host) bounds every sequence's length and sizes the workspace; p->valid_len
+ * must be NULL. Only the tokens of the sequences are written. The kernels clamp the
+ * cu_seqlens values into [0, T] and each length to max_seqlen rounded up to 64, so that no
+ * value reads or writes outside the tensors; a sequence longer than that is cut there.
+ * Any head dims and dtypes gdn_chunk_fwd takes.
+ */
+gdn_status gdn_chunk_fwd_varlen_workspace(const gdn_problem* p, int32_t max_seqlen, size_t* bytes);
+gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens, int32_t max_seqlen,
+                                const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, const float* h0,
+                                void* o, float* hT,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace for the segment calls (gdn_segment_summary, then
  * gdn_apply_initial_state on the same workspace). seg_len must be a positive
  * multiple of 64 that divides T; P = T / seg_len segments.

@@ -46,9 +46,10 @@ struct Plan {
     bool lo = false;
 };
 
-Plan make_plan(const gdn_problem& p, bool segments) {
+// max_len: the longest row in tokens (T, or max_seqlen for packed sequences)
+Plan make_plan(const gdn_problem& p, bool segments, int64_t max_len = -1) {
     Plan pl;
-    pl.NT = (static_cast<int64_t>(p.T) + gdn::kChunk - 1) / gdn::kChunk;
+    pl.NT = ((max_len < 0 ? static_cast<int64_t>(p.T) : max_len) + gdn::kChunk - 1) / gdn::kChunk;
     pl.nch = static_cast<int64_t>(p.B) * p.H * pl.NT;
     const bool mfma = use_mfma(p);
     const size_t rec = mfma ? static_cast<size_t>(gdn::kTriRecordElems) * 2 : 64 * 64 * sizeof(float);
@@ -121,11 +122,12 @@ gdn_status check_segments(const gdn_problem& p, int32_t seg_len, int64_t* P) {
 
 gdn_status run_prep(const gdn_problem& p, const Plan& pl, const void* q, const void* k,
                     const float* g, const float* beta, const gdn::Workspace& w, hipStream_t s,
-                    const gdn::Prologue* pro = nullptr) {
+                    const gdn::Prologue* pro = nullptr, const int32_t* cu_seqlens = nullptr) {
     if (pl.nch == 0) return GDN_OK;
     gdn::PrepArgs a;
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.NT = static_cast<int>(pl.NT);
     a.q = q; a.k = k; a.g = g; a.beta = beta; a.valid_len = p.valid_len; a.ws = w;
+    a.cu_seqlens = cu_seqlens;
     a.has_prologue = pro ? 1 : 0;
     a.pro = pro ? *pro : gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
     hipError_t e = use_mfma(p) ? gdn::launch_prep_mfma(a, s)
@@ -139,7 +141,7 @@ gdn::StateArgs state_args(const gdn_problem& p, const Plan& pl, const void* q, c
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.ncols = p.dv;
     a.NT = static_cast<int>(pl.NT);
     a.P = 1; a.Lc = static_cast<int>(pl.NT);
-    a.q = q; a.k = k; a.v = v; a.valid_len = p.valid_len; a.ws = w;
+    a.q = q; a.k = k; a.v = v; a.valid_len = p.valid_len; a.cu_seqlens = nullptr; a.ws = w;
     a.init_mode = gdn::kInitZero; a.s_init = nullptr; a.s_init_per_segment = 0;
     a.o = nullptr; a.s_out = nullptr; a.store_mode = gdn::kStoreNone; a.m_out = nullptr;
     return a;
@@ -242,6 +244,51 @@ gdn_status gdn_chunk_fwd_prologue(const gdn_problem* p, const void* q_raw, const
         sa.s_out = hT;
         sa.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
         return run_state(*p, sa, s);
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_chunk_fwd_varlen_workspace(const gdn_problem* p, int32_t max_seqlen, size_t* bytes) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    if (max_seqlen < 0) return fail(GDN_EINVAL, "max_seqlen=%d must be >= 0", max_seqlen);
+    if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    *bytes = make_plan(*p, false, max_seqlen).bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens, int32_t max_seqlen,
+                                const void* q, const void* k, const void* v, const float* g,
+                                const float* beta, const float* h0, void* o, float* hT, void* ws,
+                                size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        if (p->valid_len)
+            return fail(GDN_EINVAL, "valid_len must be NULL with cu_seqlens (the lengths come from cu_seqlens)");
+        if (max_seqlen < 0) return fail(GDN_EINVAL, "max_seqlen=%d must be >= 0", max_seqlen);
+        if (p->B > 0 && !cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens must be non-NULL");
+        if (p->T > 0 && (!q || !k || !v || !g || !beta || !o))
+            return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+        const Plan pl = make_plan(*p, false, max_seqlen);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (p->B == 0) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const gdn::Workspace w = carve(pl, ws);
+        if (p->T > 0) {
+            st = run_prep(*p, pl, q, k, g, beta, w, s, nullptr, cu_seqlens);
+            if (st != GDN_OK) return st;
+        }
+        gdn::StateArgs a = state_args(*p, pl, q, k, v, w);
+        a.cu_seqlens = cu_seqlens;
+        a.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+        a.s_init = h0;
+        a.o = o;
+        a.s_out = hT;
+        a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+        return run_state(*p, a, s);
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

@@ -48,11 +48,12 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
     const int hq = h / (a.H / a.Hqk);
     const int i = threadIdx.x;
     const int64_t t = static_cast<int64_t>(n) * kChunk + i;
-    const bool valid = t < valid_tokens(a.valid_len, b, a.T);
+    const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
+    const bool valid = t < rs.valid;
     const IO* q = static_cast<const IO*>(a.q);
     const IO* k = static_cast<const IO*>(a.k);
 
-    const int64_t gi_idx = (static_cast<int64_t>(b) * a.T + t) * a.H + h;
+    const int64_t gi_idx = (rs.start + t) * a.H + h;
     const float gi = valid ? a.g[gi_idx] : 0.f;
     const float bi = valid ? a.beta[gi_idx] : 0.f;
     float gam = gi;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
         if (i >= off) gam += y;
     }
     gam_s[i] = gam;
-    const int64_t row = ((static_cast<int64_t>(b) * a.T + t) * a.Hqk + hq) * DK;
+    const int64_t row = ((rs.start + t) * a.Hqk + hq) * DK;
     float qreg[DK];
 #pragma unroll
     for (int d = 0; d < DK; ++d) {
@@ -124,7 +125,8 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     const int b = blockIdx.z / a.P, seg = blockIdx.z % a.P;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x;
-    const int64_t nvalid = valid_tokens(a.valid_len, b, a.T);
+    const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
+    const int64_t nvalid = rs.valid;
     const int ncols = a.ncols;
     const IO* q = static_cast<const IO*>(a.q);
     const IO* k = static_cast<const IO*>(a.k);
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     const int r = tid / 4;             // token row within the chunk
     const int c4 = (tid % 4) * 4;      // first of this thread's 4 columns
     const int n0 = seg * a.Lc;
-    const int n1 = min(n0 + a.Lc, a.NT);
+    const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
     for (int n = n0; n < n1; ++n) {
         const int64_t t0 = static_cast<int64_t>(n) * kChunk;
         const int64_t ch = bh * a.NT + n;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
             const int rr = e / DK, d = e % DK;
             const int64_t tok = t0 + rr;
             k_s[rr * KP + d] =
-                tok < nvalid ? ld_io(k, ((static_cast<int64_t>(b) * a.T + tok) * a.Hqk + hq) * DK + d)
+                tok < nvalid ? ld_io(k, ((rs.start + tok) * a.Hqk + hq) * DK + d)
                              : 0.f;
         }
         if (tid < 128) g_s[tid] = a.ws.gates[ch * 128 + tid];
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
 
         const int64_t tok = t0 + r;
         const bool valid = tok < nvalid;
-        const int64_t qrow = ((static_cast<int64_t>(b) * a.T + tok) * a.Hqk + hq) * DK;
+        const int64_t qrow = ((rs.start + tok) * a.Hqk + hq) * DK;
         float ks[4] = {0.f, 0.f, 0.f, 0.f}, qs[4] = {0.f, 0.f, 0.f, 0.f};
         for (int i = 0; i < DK; ++i) {
             const float kv = k_s[r * KP + i];
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
             }
         }
         const float eg = g_s[r];
-        const int64_t vrow = ((static_cast<int64_t>(b) * a.T + tok) * a.H + h) * ncols + col0 + c4;
+        const int64_t vrow = ((rs.start + tok) * a.H + h) * ncols + col0 + c4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float vv = (v && valid) ? ld_io(v, vrow + c) : 0.f;
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
         for (int c = 0; c < 4; ++c) u_s[r * (BV + 1) + c4 + c] = u[c];
         __syncthreads();
 
-        if (o && tok < a.T) {
+        if (o && tok < rs.extent) {
             const float* pm = static_cast<const float*>(a.ws.pmat) + ch * 4096;
             float ov[4];
 #pragma unroll

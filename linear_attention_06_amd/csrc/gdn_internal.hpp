@@ -16,6 +16,35 @@ constexpr int kTriRecordElems = 6 * 512;
 constexpr int kGateRecordF32 = 128;
 constexpr int kGateRecordMfma = 256;
 
+// Token range of batch row b. Without cu_seqlens the rows are T tokens each, one after
+// another, and token t of row b is valid when t < valid_len[b] (clamped to [0, T]); the
+// row's outputs cover all T tokens (padding written as zero). With cu_seqlens (packed
+// variable-length sequences, valid_len unused) row b is sequence b, tokens cu[b] ..
+// cu[b+1] - 1 of the packed tensor of T tokens; the ends are clamped into [0, T] and the
+// length to at most NT chunks, so that no value of cu_seqlens leads outside the tensors
+// or the workspace; a sequence's outputs cover its own tokens only.
+struct RowSpan {
+    int64_t start;    // first token of the row in the token dimension
+    int64_t valid;    // tokens that take part in the recurrence
+    int64_t extent;   // tokens whose outputs the row writes
+};
+__device__ __forceinline__ RowSpan row_span(const int32_t* cu, const int32_t* vl, int b, int64_t T, int NT) {
+    if (cu) {
+        int64_t s = cu[b], e = cu[b + 1];
+        s = s < 0 ? 0 : (s > T ? T : s);
+        e = e < s ? s : (e > T ? T : e);
+        const int64_t cap = static_cast<int64_t>(NT) * kChunk;
+        const int64_t n = e - s > cap ? cap : e - s;
+        return RowSpan{s, n, n};
+    }
+    int64_t n = T;
+    if (vl) {
+        n = vl[b];
+        n = n < 0 ? 0 : (n > T ? T : n);
+    }
+    return RowSpan{static_cast<int64_t>(b) * T, n, T};
+}
+
 // How a state pass starts.
 enum InitMode : int { kInitZero = 0, kInitLoad = 1, kInitIdentity = 2 };
 // Where a state pass leaves its final state.
@@ -58,6 +87,7 @@ struct PrepArgs {
     const float* g;         // unused with a prologue
     const float* beta;      // unused with a prologue
     const int32_t* valid_len;
+    const int32_t* cu_seqlens;  // packed sequences (see row_span), or NULL
     Workspace ws;
     int has_prologue;       // 0: q, k, g, beta are used as given
     Prologue pro;
@@ -70,6 +100,7 @@ struct StateArgs {
     const void* k;
     const void* v;                    // NULL: values are zero (M summary)
     const int32_t* valid_len;
+    const int32_t* cu_seqlens;        // packed sequences (see row_span), or NULL
     Workspace ws;
     int init_mode;
     const float* s_init;              // [B,H,Pin,dk,ncols], Pin = P when loading per segment, else 1

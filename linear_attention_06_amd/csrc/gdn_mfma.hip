@@ -129,7 +129,11 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 5, lr = lane & 31;
     const int64_t t0 = static_cast<int64_t>(n) * kChunk;
-    const int64_t nvalid = valid_tokens(a.valid_len, b, a.T);
+    const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
+    const int64_t nvalid = rs.valid;
+    // a packed sequence shorter than this chunk's start has nothing here (its state pass
+    // stops at its last chunk and never reads this record)
+    if (a.cu_seqlens && t0 >= nvalid) return;
     const uint16_t* kin = static_cast<const uint16_t*>(a.k);
     const uint16_t* qin = static_cast<const uint16_t*>(a.q);
 
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
     // With the prologue, a and b take the place of g and beta.
     float graw = 0.f, braw = 0.f;
     if (wave == 0) {
-        const int64_t gi = (static_cast<int64_t>(b) * a.T + (gvalid ? tg : 0)) * a.H + h;
+        const int64_t gi = (rs.start + (gvalid ? tg : 0)) * a.H + h;
         graw = a.has_prologue ? a.pro.a[gi] : a.g[gi];
         braw = a.has_prologue ? a.pro.b[gi] : a.beta[gi];
     }
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
             const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
             const int64_t t = t0 + row;
             const int64_t off =
-                ((static_cast<int64_t>(b) * a.T + (t < nvalid ? t : 0)) * a.Hqk + hq) * DK + 8 * cb;
+                ((rs.start + (t < nvalid ? t : 0)) * a.Hqk + hq) * DK + 8 * cb;
             kv[u] = *reinterpret_cast<const u32x4*>(kin + off);
             qv[u] = *reinterpret_cast<const u32x4*>(qin + off);
         }
@@ -603,10 +607,13 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int ncols = a.ncols;
-    const int64_t nvalid = valid_tokens(a.valid_len, b, a.T);
+    const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
+    const int64_t nvalid = rs.valid;
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     const int64_t stile = static_cast<int64_t>(DK) * ncols;
-    const int n0 = seg * a.Lc, n1 = min(n0 + a.Lc, a.NT);
+    // a packed sequence stops at its own last chunk
+    const int n0 = seg * a.Lc;
+    const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
 
     const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK;   // elements per token
     const int64_t vo_row = static_cast<int64_t>(a.H) * ncols;
@@ -632,9 +639,9 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // ---------------- loading waves ----------------
         // q/k/v descriptors over row b end at the last valid token: padded and
         // out-of-range tokens load as zero
-        const uint16_t* kin = static_cast<const uint16_t*>(a.k) + static_cast<int64_t>(b) * a.T * qk_row;
-        const uint16_t* qin = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(b) * a.T * qk_row;
-        const uint16_t* vin = static_cast<const uint16_t*>(a.v) + static_cast<int64_t>(b) * a.T * vo_row;
+        const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rs.start * qk_row;
+        const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rs.start * qk_row;
+        const uint16_t* vin = static_cast<const uint16_t*>(a.v) + rs.start * vo_row;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin, nvalid * qk_row * 2);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(outputs ? qin : kin, nvalid * qk_row * 2);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
@@ -772,8 +779,10 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 
     if (outputs && wave == 1) {
         // ---------------- output wave: chunk n - 1 during chunk n ----------------
-        uint16_t* oout = static_cast<uint16_t*>(a.o) + static_cast<int64_t>(b) * a.T * vo_row;
-        const __amdgpu_buffer_rsrc_t ro = make_rsrc(oout, static_cast<int64_t>(a.T) * vo_row * 2);
+        // stores past the row's extent (the tail of a packed sequence's last chunk) are
+        // dropped by the descriptor's range
+        uint16_t* oout = static_cast<uint16_t*>(a.o) + rs.start * vo_row;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(oout, rs.extent * vo_row * 2);
         const uint32_t ooff = static_cast<uint32_t>((l16 * vo_row + h * ncols + col0 + 4 * g4) * 2);
         // L2 prefetch, kPrefetch chunks ahead of the chain: the column tiles of a head
         // split the 128-byte lines of its chunk operands between them (lanes 0..31: k and
@@ -784,7 +793,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         int64_t pf_stride;      // bytes per chunk
         int pf_row = -1;        // token row inside the chunk for q/k/v lines, else -1
         {
-            const int64_t bT = static_cast<int64_t>(b) * a.T;
+            const int64_t bT = rs.start;
             if (lane < 32) {
                 const int lam = 32 * tile + lane;
                 const uint16_t* src = static_cast<const uint16_t*>(lam < 128 ? a.k : a.q);
@@ -815,7 +824,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             const unsigned char* p;
             if (pf_row >= 0) {
                 int64_t t = static_cast<int64_t>(c) * kChunk + pf_row;
-                if (t > a.T - 1) t = a.T - 1;
+                if (t > rs.extent - 1) t = rs.extent - 1;
                 p = pf_base + t * pf_stride;
             } else {
                 p = pf_base + static_cast<int64_t>(c) * pf_stride;
@@ -823,7 +832,10 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pf_lds));
             asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(p) : "memory", "m0");
         };
-        if (kEnablePrefetch)
+        // a row or segment without chunks has no line to prefetch (the clamped token
+        // index would fall before the row)
+        const bool pf_on = kEnablePrefetch && n1 > n0;
+        if (pf_on)
             for (int c = n0 + 2; c < n0 + kPrefetch && c < n1; ++c) prefetch(c);
         const int last = n1 > 0 ? n1 - 1 : 0;
         // P goes from global memory straight into registers: its blocks are contiguous
@@ -877,14 +889,14 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // load of the last chunk), so that the body has no branches
         auto step = [&](int n, PSet& pp) {
             chunk_barrier(false);
-            if (kEnablePrefetch) prefetch(min(n + kPrefetch, last));
+            if (pf_on) prefetch(min(n + kPrefetch, last));
             compute(n - 1, pp);
             load_p(min(n + 1, last), pp);
         };
         load_p(min(n0, last), p0);
         load_p(min(n0 + 1, last), p1);
         chunk_barrier(false);   // iteration n0: no outputs yet
-        if (kEnablePrefetch) prefetch(min(n0 + kPrefetch, last));
+        if (pf_on) prefetch(min(n0 + kPrefetch, last));
         int n = n0 + 1;
         for (; n + 1 <= n1; n += 2) {
             step(n, p0);

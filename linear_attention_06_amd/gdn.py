@@ -23,7 +23,8 @@ CHUNK = 64
 
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
-           "gdn_chunk_fwd", "gdn_chunk_fwd_prologue",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace",
+           "gdn_chunk_fwd_varlen",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
            "gdn_apply_initial_state")
 
@@ -64,11 +65,13 @@ def lib():
         L.gdn_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_chunk_fwd_prologue.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                              vp, sz, vp]
+        L.gdn_chunk_fwd_varlen_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
+        L.gdn_chunk_fwd_varlen.argtypes = [pp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd",
-                     "gdn_chunk_fwd_prologue",
+                     "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace", "gdn_chunk_fwd_varlen",
                      "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -196,6 +199,41 @@ def gdn_chunk_fwd_prologue(q_raw, k_raw, v, a, b, A_log, dt_bias, q_scale=None, 
                                         _ptr(A_log), _ptr(dt_bias), ctypes.c_float(q_scale), _ptr(h0),
                                         _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_chunk_fwd_prologue")
+    return o, hT
+
+
+def gdn_chunk_fwd_varlen_workspace(p: GdnProblem, max_seqlen: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_fwd_varlen_workspace(ctypes.byref(p), max_seqlen, ctypes.byref(n)),
+           "gdn_chunk_fwd_varlen_workspace")
+    return n.value
+
+
+def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen, h0=None, o=None, hT=None,
+                         want_state=True, ws=None, stream=None):
+    """Packed variable-length forward: q, k [1,T,Hqk,dk], v [1,T,H,dv], g, beta [1,T,H];
+    cu_seqlens int32 [N+1] on the device, max_seqlen an int. Returns (o, hT [N,H,dk,dv] or None)."""
+    _io_checks(q, k, v, g, beta)
+    _dev(h0, "h0", torch.float32)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    if q.shape[0] != 1:
+        raise ValueError("packed sequences use a batch dimension of 1")
+    N = cu_seqlens.numel() - 1
+    p = problem(q, v)
+    p.B = N
+    if o is None:
+        o = torch.zeros(v.shape, dtype=v.dtype, device=v.device)
+    _dev(o, "o", v.dtype)
+    if hT is None and want_state:
+        hT = torch.empty((N, p.H, p.dk, p.dv), dtype=torch.float32, device=v.device)
+    _dev(hT, "hT", torch.float32)
+    need = gdn_chunk_fwd_varlen_workspace(p, int(max_seqlen))
+    if ws is None:
+        ws = workspace(need, v.device)
+    _check(lib().gdn_chunk_fwd_varlen(ctypes.byref(p), _ptr(cu_seqlens), int(max_seqlen), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws),
+                                      ws.numel(), _stream(stream)),
+           "gdn_chunk_fwd_varlen")
     return o, hT
 
 

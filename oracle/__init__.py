@@ -189,3 +189,27 @@ def gdn_apply_initial_state(q, k, v, g, beta, H_in, seg_len, valid_len=None, _li
                                            _ptr(v), _ptr(g), _ptr(beta), _ptr(vl), _ptr(H_in),
                                            _ptr(o), _ptr(hT))
     return o, hT
+
+
+def gdn_fwd_varlen(q, k, v, g, beta, cu_seqlens, h0=None, want_state=True):
+    """Packed variable-length forward: sequence b is tokens cu_seqlens[b] .. cu_seqlens[b+1]-1
+    of the packed inputs (q, k [1,T,Hqk,dk], v [1,T,H,dv], g, beta [1,T,H]); each runs the
+    token-by-token forward on its own tokens from h0[b] (zero if h0 is None). The general
+    form of the pages' variable-length rows (issue #320, test report for PR #1114, section
+    5.2: rows of one batch with different valid lengths). Returns (o [1,T,H,dv] with zeros
+    outside every sequence, hT [N,H,dk,dv] or None)."""
+    q, k, v, g, beta, h0 = map(_f64, (q, k, v, g, beta, h0))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    H, dk, dv = v.shape[2], q.shape[3], v.shape[3]
+    o = np.zeros(v.shape, np.float64)
+    hT = np.empty((N, H, dk, dv), np.float64) if want_state else None
+    for b in range(N):
+        s, e = int(cu[b]), int(cu[b + 1])
+        sl = slice(s, e)
+        ob, hb = gdn_fwd(q[:, sl], k[:, sl], v[:, sl], g[:, sl], beta[:, sl],
+                         None if h0 is None else h0[b:b + 1], want_state=True)
+        o[:, sl] = ob
+        if want_state:
+            hT[b] = hb[0]
+    return o, hT
