@@ -170,6 +170,33 @@ def prologue_timing(gdn, inp, dev, stream, timed):
             "torch_prologue_then_core_ms": ms_s}
 
 
+def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
+    """gdn_chunk_bwd (all six gradients) on the stateless 8K workload with a seeded output
+    gradient, and its per-kernel split is in profiles/."""
+    import torch
+
+    w = workloads["stateless_8k"]
+    inp = make_inputs(w)
+
+    def io(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.int16).view(torch.bfloat16).to(dev)
+
+    q, k, v = io(inp.q), io(inp.k), io(inp.v)
+    g = torch.from_numpy(inp.g).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(8)
+    d_o = torch.randn(v.shape, device=dev, generator=gen).to(torch.bfloat16)
+    p = gdn.problem(q, v)
+    ws = gdn.workspace(gdn.gdn_chunk_bwd_workspace(p), dev)
+
+    def step():
+        gdn.gdn_chunk_bwd(q, k, v, g, beta, None, d_o, ws=ws, stream=stream)
+
+    ms = timed(step, 3)
+    return {"workload": "stateless_8k", "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+            "workspace_bytes": int(ws.numel())}
+
+
 def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
     """gdn_chunk_fwd step time on the stateless 8K and padded 8K workloads, and the padded
     rows packed as variable-length sequences (gdn_chunk_fwd_varlen)."""
@@ -364,6 +391,7 @@ def main():
         line["segmented_32k"] = segmented_timing(gdn, q, k, v, g, beta, h0, stream, timed)
         line["other_workloads"] = other_workloads(gdn, WORKLOADS, make_inputs, dev, stream, timed)
         line["fused_prologue_32k"] = prologue_timing(gdn, inp, dev, stream, timed)
+        line["backward_8k"] = backward_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line))

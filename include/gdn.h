@@ -156,6 +156,27 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Backward of gdn_chunk_fwd (the gradients issue #320, section 4 of the test report for
+ * PR #1114, checks: dq, dk, dv, dg, dbeta and dH0). Given the forward's inputs, the
+ * gradient d_o of o ([B, T, H, dv], io dtype) and, when non-NULL, the gradient dhT of the
+ * final state ([B, H, dk, dv] fp32; NULL = zero), writes
+ *   dq, dk [B, T, Hqk, dk],  dv [B, T, H, dv],  dg, dbeta [B, T, H]   (all fp32; dq and dk
+ *   summed over the value heads that read each query/key head)
+ *   dh0 [B, H, dk, dv] fp32 when non-NULL (the gradient of h0; h0 NULL = zero state).
+ * Padded tokens (valid_len) get zero gradients. Every head dim and dtype of the forward;
+ * the arithmetic is fp32 on the vector ALUs, token by token, with the forward state
+ * recomputed from checkpoints every 64 tokens. ws must be 256-byte aligned and at least
+ * gdn_chunk_bwd_workspace() bytes (B H ceil(T/64) dk dv + B T H (dv/16) 2 (dk + 1) fp32).
+ */
+gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);
+gdn_status gdn_chunk_bwd(const gdn_problem* p,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* h0,
+                         const void* d_o, const float* dhT,
+                         float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace for the segment calls (gdn_segment_summary, then
  * gdn_apply_initial_state on the same workspace). seg_len must be a positive
  * multiple of 64 that divides T; P = T / seg_len segments.

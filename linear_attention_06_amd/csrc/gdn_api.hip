@@ -294,6 +294,66 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
     }
 }
 
+// Backward workspace: chunk-start states, then the per-column-tile partials of dq, dk
+// and of dg, dbeta.
+struct BwdPlan {
+    int64_t NT = 0;
+    size_t ckpt_off = 0, dqk_off = 0, dgb_off = 0, bytes = 0;
+};
+
+BwdPlan make_bwd_plan(const gdn_problem& p) {
+    BwdPlan pl;
+    pl.NT = (static_cast<int64_t>(p.T) + gdn::kChunk - 1) / gdn::kChunk;
+    const size_t bt = static_cast<size_t>(p.B) * p.T, tiles = static_cast<size_t>(p.dv / 16);
+    pl.ckpt_off = 0;
+    pl.dqk_off = align256(static_cast<size_t>(p.B) * p.H * pl.NT * p.dk * p.dv * sizeof(float));
+    pl.dgb_off = pl.dqk_off + align256(bt * p.H * tiles * 2 * p.dk * sizeof(float));
+    pl.bytes = pl.dgb_off + align256(bt * p.H * tiles * 2 * sizeof(float));
+    return pl;
+}
+
+gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    *bytes = make_bwd_plan(*p).bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* h0, const void* d_o, const float* dhT, float* dq,
+                         float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
+                         void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+            return fail(GDN_EINVAL, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        const BwdPlan pl = make_bwd_plan(*p);
+        if (pl.bytes > 0) {
+            if (!ws) return fail(GDN_EWORKSPACE, "workspace is NULL, %zu bytes needed", pl.bytes);
+            if (ws_bytes < pl.bytes) return fail(GDN_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, pl.bytes);
+            if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
+        }
+        if (p->B == 0) return GDN_OK;
+        char* base = static_cast<char*>(ws);
+        gdn::BwdArgs a;
+        a.B = p->B; a.T = p->T; a.H = p->H; a.Hqk = p->Hqk; a.dk = p->dk; a.dv = p->dv;
+        a.NT = static_cast<int>(pl.NT);
+        a.q = q; a.k = k; a.v = v; a.d_o = d_o; a.g = g; a.beta = beta; a.h0 = h0; a.dhT = dhT;
+        a.valid_len = p->valid_len;
+        a.ckpt = reinterpret_cast<float*>(base + pl.ckpt_off);
+        a.dqk_part = reinterpret_cast<float*>(base + pl.dqk_off);
+        a.dgb_part = reinterpret_cast<float*>(base + pl.dgb_off);
+        a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta; a.dh0_out = dh0;
+        hipError_t e = gdn::launch_bwd(a, p->io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? GDN_OK : hip_fail(e, "backward kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
 gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;

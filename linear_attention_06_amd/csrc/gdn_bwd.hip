@@ -1,0 +1,305 @@
+// gdn_bwd.hip -- backward of the Gated DeltaNet recurrence for gfx950, fp32 on the
+// vector ALUs (any head dim of the forward; q, k, v and the output gradient may be
+// fp32 or bf16).
+//
+// Per batch row b and value head h, with the dk x dv state S and S_{-1} = h0:
+//   w_t = S_{t-1}^T k_t,   S_t = e^{g_t} (S_{t-1} - beta_t k_t w_t^T) + beta_t k_t v_t^T,
+//   o_t = S_t^T q_t
+// (the recurrence of include/gdn.h written with the delta error on the decayed state).
+// Given do_t and the gradient dhT of the final state, reverse mode gives, with
+// M = dS_t + q_t do_t^T the full gradient of S_t and z = M^T k_t:
+//   dq_t = S_t do_t                      dv_t = beta_t z
+//   dk_t = beta_t M v_t - e^{g_t} beta_t (M w_t + S_{t-1} z)
+//   dbeta_t = z . (v_t - e^{g_t} w_t)    dg_t = e^{g_t} (<M, S_{t-1}> - beta_t z . w_t)
+//   dS_{t-1} = e^{g_t} (M - beta_t k_t z^T),   dh0 = dS_{-1}.
+// The pages (hyper-parallel issue #320, the test report for PR #1114, section 4)
+// check dq, dk, dv, dg, dbeta and dH0 against a reference; this is that gradient.
+//
+// Three kernels, one block of 256 threads per (b, h, 16 state columns) for the first
+// two: thread 16 c + i holds column c of the tile at rows i + 16 j (j < dk / 16), so
+// that the 16 threads of a column are one DPP row and a column sum is four DPP
+// rotations.
+//   bwd_ckpt    the forward state at every chunk start (64 tokens) into the workspace;
+//   bwd_sweep   chunks in reverse: the chunk's states are recomputed from its
+//               checkpoint, with a second checkpoint every 8 tokens in LDS, and each
+//               8-token piece is recomputed into registers and run backwards; dv and
+//               dh0 are complete per tile, dq, dk, dg and dbeta are written as one
+//               partial per column tile;
+//   bwd_reduce  sums the partials over the column tiles and over the value heads that
+//               share a query/key head.
+// Tokens at or past valid_len[b] are identities of the recurrence (beta = g = 0) with
+// zero output: their gradients are zero.
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+__device__ __forceinline__ float ld_in(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ld_in(const uint16_t* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+// Sum over the 16 lanes of a DPP row (rotations by 8, 4, 2, 1); every lane gets it.
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
+    return x;
+}
+
+// Chunk operands in LDS (fp32): K, optionally Q, the tile's columns of V and of the
+// output gradient, g and beta; padded tokens read as zero.
+template <typename IO, int DK, bool kQ>
+struct ChunkLds {
+    float k[64][DK];
+    float q[kQ ? 64 : 1][DK];
+    float v[64][16];
+    float d[kQ ? 64 : 1][16];
+    float g[64];
+    float beta[64];
+};
+
+template <typename IO, int DK, bool kQ>
+__device__ __forceinline__ void load_chunk(ChunkLds<IO, DK, kQ>& L, const BwdArgs& a, const RowSpan& rs, int h,
+                                           int hq, int col0, int n, int tid) {
+    const IO* k = static_cast<const IO*>(a.k);
+    const IO* q = static_cast<const IO*>(a.q);
+    const IO* v = static_cast<const IO*>(a.v);
+    const IO* d = static_cast<const IO*>(a.d_o);
+    const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+    for (int e = tid; e < 64 * DK; e += 256) {
+        const int r = e / DK, x = e % DK;
+        const int64_t tok = t0 + r;
+        const bool ok = tok < rs.valid;
+        const int64_t idx = ((rs.start + tok) * a.Hqk + hq) * DK + x;
+        L.k[r][x] = ok ? ld_in(k, idx) : 0.f;
+        if (kQ) L.q[r][x] = ok ? ld_in(q, idx) : 0.f;
+    }
+    for (int e = tid; e < 64 * 16; e += 256) {
+        const int r = e / 16, c = e % 16;
+        const int64_t tok = t0 + r;
+        const bool ok = tok < rs.valid;
+        const int64_t idx = ((rs.start + tok) * a.H + h) * a.dv + col0 + c;
+        L.v[r][c] = ok ? ld_in(v, idx) : 0.f;
+        if (kQ) L.d[r][c] = ok ? ld_in(d, idx) : 0.f;
+    }
+    if (tid < 64) {
+        const int64_t tok = t0 + tid;
+        const bool ok = tok < rs.valid;
+        const int64_t gi = (rs.start + tok) * a.H + h;
+        L.g[tid] = ok ? a.g[gi] : 0.f;
+        L.beta[tid] = ok ? a.beta[gi] : 0.f;
+    }
+}
+
+// One forward token step on the thread's column slice S[j] = S[i + 16 j][c]; returns w_c.
+template <int RJ, typename Lds>
+__device__ __forceinline__ float fwd_step(float (&S)[RJ], const Lds& L, int u, int i, int c) {
+    float w = 0.f;
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) w += L.k[u][i + 16 * j] * S[j];
+    w = row_sum16(w);
+    const float eg = expf(L.g[u]), bt = L.beta[u], vc = L.v[u][c];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+        const float kr = L.k[u][i + 16 * j];
+        S[j] = eg * (S[j] - bt * kr * w) + bt * kr * vc;
+    }
+    return w;
+}
+
+template <typename IO, int DK>
+__global__ __launch_bounds__(256) void bwd_ckpt(BwdArgs a) {
+    constexpr int RJ = DK / 16;
+    __shared__ ChunkLds<IO, DK, false> L;
+    const int col0 = 16 * blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int hq = h / (a.H / a.Hqk);
+    const int tid = threadIdx.x, c = tid >> 4, i = tid & 15;
+    const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
+    const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    float S[RJ];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j)
+        S[j] = a.h0 ? a.h0[(bh * DK + i + 16 * j) * a.dv + col0 + c] : 0.f;
+    for (int n = 0; n < a.NT; ++n) {
+        float* ck = a.ckpt + (bh * a.NT + n) * DK * a.dv;
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) ck[static_cast<int64_t>(i + 16 * j) * a.dv + col0 + c] = S[j];
+        __syncthreads();
+        load_chunk<IO, DK, false>(L, a, rs, h, hq, col0, n, tid);
+        __syncthreads();
+        for (int u = 0; u < 64; ++u) fwd_step<RJ>(S, L, u, i, c);
+    }
+}
+
+template <typename IO, int DK>
+__global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
+    constexpr int RJ = DK / 16;
+    __shared__ ChunkLds<IO, DK, true> L;
+    __shared__ float sub_s[8][RJ][256];        // state every 8 tokens of the chunk
+    __shared__ float red_s[2][16][DK];         // per-column terms of dq and dk
+    __shared__ float red2_s[2][16];            // per-column terms of dg and dbeta
+    const int tiles = a.dv / 16;
+    const int tile = blockIdx.x, col0 = 16 * tile, h = blockIdx.y, b = blockIdx.z;
+    const int hq = h / (a.H / a.Hqk);
+    const int tid = threadIdx.x, c = tid >> 4, i = tid & 15;
+    const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
+    const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+
+    float dS[RJ];
+#pragma unroll
+    for (int j = 0; j < RJ; ++j)
+        dS[j] = a.dhT ? a.dhT[(bh * DK + i + 16 * j) * a.dv + col0 + c] : 0.f;
+
+    for (int n = a.NT - 1; n >= 0; --n) {
+        __syncthreads();
+        load_chunk<IO, DK, true>(L, a, rs, h, hq, col0, n, tid);
+        float S[RJ];
+        const float* ck = a.ckpt + (bh * a.NT + n) * DK * a.dv;
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) S[j] = ck[static_cast<int64_t>(i + 16 * j) * a.dv + col0 + c];
+        __syncthreads();
+        // forward through the chunk, keeping the state before every 8th token
+        for (int u = 0; u < 64; ++u) {
+            if ((u & 7) == 0) {
+#pragma unroll
+                for (int j = 0; j < RJ; ++j) sub_s[u >> 3][j][tid] = S[j];
+            }
+            fwd_step<RJ>(S, L, u, i, c);
+        }
+        for (int s = 7; s >= 0; --s) {
+            // the piece's states in registers: St[u] before token 8 s + u, St[u + 1] after it
+            float St[9][RJ], w[8];
+#pragma unroll
+            for (int j = 0; j < RJ; ++j) St[0][j] = sub_s[s][j][tid];
+#pragma unroll
+            for (int uu = 0; uu < 8; ++uu) {
+#pragma unroll
+                for (int j = 0; j < RJ; ++j) St[uu + 1][j] = St[uu][j];
+                w[uu] = fwd_step<RJ>(St[uu + 1], L, 8 * s + uu, i, c);
+            }
+#pragma unroll
+            for (int uu = 7; uu >= 0; --uu) {
+                const int u = 8 * s + uu;
+                const int64_t t = static_cast<int64_t>(n) * kChunk + u;
+                const bool valid = t < rs.valid;
+                const float eg = expf(L.g[u]), bt = L.beta[u], vc = L.v[u][c], doc = L.d[u][c];
+                float M[RJ];
+                float z = 0.f, ms = 0.f;
+#pragma unroll
+                for (int j = 0; j < RJ; ++j) {
+                    M[j] = dS[j] + L.q[u][i + 16 * j] * doc;
+                    z += M[j] * L.k[u][i + 16 * j];
+                    ms += M[j] * St[uu][j];
+                }
+                z = row_sum16(z);
+                ms = row_sum16(ms);
+                const bool inrow = t < rs.extent;      // the tail of the last chunk is past the row
+                const int64_t tokrow = rs.start + t;
+                if (i == 0 && inrow) a.dv_out[(tokrow * a.H + h) * a.dv + col0 + c] = valid ? bt * z : 0.f;
+#pragma unroll
+                for (int j = 0; j < RJ; ++j) {
+                    const int r = i + 16 * j;
+                    red_s[0][c][r] = St[uu + 1][j] * doc;
+                    red_s[1][c][r] = M[j] * (bt * vc - eg * bt * w[uu]) - eg * bt * St[uu][j] * z;
+                }
+                if (i == 0) {
+                    red2_s[0][c] = valid ? eg * (ms - bt * z * w[uu]) : 0.f;
+                    red2_s[1][c] = valid ? z * (vc - eg * w[uu]) : 0.f;
+                }
+                __syncthreads();
+                {
+                    float* part = a.dqk_part + ((tokrow * a.H + h) * tiles + tile) * 2 * DK;
+                    if (inrow && tid < 2 * DK) {
+                        const int which = tid / DK, r = tid % DK;
+                        float acc = 0.f;
+#pragma unroll
+                        for (int cc = 0; cc < 16; ++cc) acc += red_s[which][cc][r];
+                        part[tid] = valid ? acc : 0.f;
+                    }
+                    if (inrow && tid < 2) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int cc = 0; cc < 16; ++cc) acc += red2_s[tid][cc];
+                        a.dgb_part[((tokrow * a.H + h) * tiles + tile) * 2 + tid] = acc;
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < RJ; ++j) dS[j] = eg * (M[j] - bt * L.k[u][i + 16 * j] * z);
+            }
+        }
+    }
+    if (a.dh0_out) {
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) a.dh0_out[(bh * DK + i + 16 * j) * a.dv + col0 + c] = dS[j];
+    }
+}
+
+// One block per (t, b): dq, dk per query/key head (sum over column tiles and the
+// value heads of the group), dg and dbeta per value head (sum over column tiles).
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
+    const int64_t t = blockIdx.x;
+    const int b = blockIdx.y;
+    const int tiles = a.dv / 16, rep = a.H / a.Hqk;
+    const int64_t row = static_cast<int64_t>(b) * a.T + t;
+    for (int e = threadIdx.x; e < a.Hqk * DK; e += 256) {
+        const int hq = e / DK, r = e % DK;
+        float sq = 0.f, sk = 0.f;
+        for (int hh = 0; hh < rep; ++hh) {
+            const float* part = a.dqk_part + ((row * a.H + hq * rep + hh) * tiles) * 2 * DK;
+            for (int tl = 0; tl < tiles; ++tl) {
+                sq += part[tl * 2 * DK + r];
+                sk += part[tl * 2 * DK + DK + r];
+            }
+        }
+        a.dq_out[(row * a.Hqk + hq) * DK + r] = sq;
+        a.dk_out[(row * a.Hqk + hq) * DK + r] = sk;
+    }
+    for (int hh = threadIdx.x; hh < a.H; hh += 256) {
+        const float* part = a.dgb_part + (row * a.H + hh) * tiles * 2;
+        float sg = 0.f, sb = 0.f;
+        for (int tl = 0; tl < tiles; ++tl) {
+            sg += part[2 * tl];
+            sb += part[2 * tl + 1];
+        }
+        a.dg_out[row * a.H + hh] = sg;
+        a.dbeta_out[row * a.H + hh] = sb;
+    }
+}
+
+template <typename IO>
+hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
+    void* args[] = {const_cast<BwdArgs*>(&a)};
+    const void *f1 = nullptr, *f2 = nullptr, *f3 = nullptr;
+    switch (a.dk) {
+#define GDN_BWD_CASE(D)                                                   \
+        case D:                                                           \
+            f1 = reinterpret_cast<const void*>(&bwd_ckpt<IO, D>);         \
+            f2 = reinterpret_cast<const void*>(&bwd_sweep<IO, D>);        \
+            f3 = reinterpret_cast<const void*>(&bwd_reduce<D>);           \
+            break;
+        GDN_BWD_CASE(16)
+        GDN_BWD_CASE(32)
+        GDN_BWD_CASE(64)
+        GDN_BWD_CASE(128)
+#undef GDN_BWD_CASE
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipLaunchKernel(f1, grid, dim3(256), args, 0, s);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel(f2, grid, dim3(256), args, 0, s);
+    if (e != hipSuccess || a.T == 0) return e;
+    return hipLaunchKernel(f3, dim3(static_cast<unsigned>(a.T), static_cast<unsigned>(a.B)), dim3(256), args, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, bool io_bf16, hipStream_t s) {
+    return io_bf16 ? bwd_dispatch<uint16_t>(a, s) : bwd_dispatch<float>(a, s);
+}
+
+}  // namespace gdn

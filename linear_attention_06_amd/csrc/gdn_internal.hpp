@@ -124,11 +124,35 @@ struct ScanArgs {
     float* x_final;       // [B,H,dk,ncols]: X_{P-1}, or NULL
 };
 
+// Backward (fp32 vector-ALU kernels in gdn_bwd.hip).
+struct BwdArgs {
+    int B, T, H, Hqk, dk, dv, NT;
+    const void* q;            // [B,T,Hqk,dk]  io dtype
+    const void* k;
+    const void* v;            // [B,T,H,dv]    io dtype
+    const void* d_o;          // [B,T,H,dv]    io dtype: gradient of o
+    const float* g;           // [B,T,H]
+    const float* beta;
+    const float* h0;          // [B,H,dk,dv] or NULL
+    const float* dhT;         // [B,H,dk,dv] gradient of the final state, or NULL
+    const int32_t* valid_len;
+    float* ckpt;              // workspace [B,H,NT,dk,dv]: state at every chunk start
+    float* dqk_part;          // workspace [B,T,H,dv/16,2,dk]: dq, dk per column tile
+    float* dgb_part;          // workspace [B,T,H,dv/16,2]: dg, dbeta per column tile
+    float* dq_out;            // [B,T,Hqk,dk]
+    float* dk_out;            // [B,T,Hqk,dk]
+    float* dv_out;            // [B,T,H,dv]
+    float* dg_out;            // [B,T,H]
+    float* dbeta_out;         // [B,T,H]
+    float* dh0_out;           // [B,H,dk,dv] or NULL
+};
+
 // Launchers. Each returns the HIP status of its launches.
 hipError_t launch_prep_f32path(const PrepArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_state_f32path(const StateArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s);
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, bool io_bf16, hipStream_t s);
 
 }  // namespace gdn

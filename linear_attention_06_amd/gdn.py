@@ -24,7 +24,7 @@ CHUNK = 64
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
            "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace",
-           "gdn_chunk_fwd_varlen",
+           "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
            "gdn_apply_initial_state")
 
@@ -67,11 +67,14 @@ def lib():
                                              vp, sz, vp]
         L.gdn_chunk_fwd_varlen_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
         L.gdn_chunk_fwd_varlen.argtypes = [pp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_chunk_bwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
+        L.gdn_chunk_bwd.argtypes = [pp] + [vp] * 15 + [sz, vp]
         L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd",
                      "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace", "gdn_chunk_fwd_varlen",
+                     "gdn_chunk_bwd_workspace", "gdn_chunk_bwd",
                      "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -235,6 +238,36 @@ def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen, h0=None, o=No
                                       ws.numel(), _stream(stream)),
            "gdn_chunk_fwd_varlen")
     return o, hT
+
+
+def gdn_chunk_bwd_workspace(p: GdnProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)), "gdn_chunk_bwd_workspace")
+    return n.value
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, dhT=None, valid_len=None, want_dh0=True, ws=None, stream=None):
+    """Backward of gdn_chunk_fwd. Returns (dq, dk, dv, dg, dbeta, dh0 or None), all fp32."""
+    _io_checks(q, k, v, g, beta)
+    _dev(d_o, "d_o", v.dtype)
+    _dev(h0, "h0", torch.float32)
+    _dev(dhT, "dhT", torch.float32)
+    p = problem(q, v, valid_len)
+    f32 = dict(dtype=torch.float32, device=v.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    dg = torch.empty(g.shape, **f32)
+    dbeta = torch.empty(beta.shape, **f32)
+    dh0 = torch.empty((p.B, p.H, p.dk, p.dv), **f32) if want_dh0 else None
+    need = gdn_chunk_bwd_workspace(p)
+    if ws is None:
+        ws = workspace(need, v.device)
+    _check(lib().gdn_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+                               _ptr(d_o), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                               _ptr(dh0), _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_chunk_bwd")
+    return dq, dk, dv, dg, dbeta, dh0
 
 
 def gdn_segment_summary(q, k, v, g, beta, seg_len, M=None, S=None, want_m=True, want_s=True,
