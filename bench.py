@@ -197,6 +197,39 @@ def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
             "workspace_bytes": int(ws.numel())}
 
 
+def layer_ops_timing(gdn, dev, stream, timed):
+    """The streaming layer steps at the 32K layer's shapes: causal Conv1D (K = 4, SiLU) over
+    the projected q/k/v channels (16 + 16 query/key heads and 32 value heads of 128: C = 8192)
+    and the gated RMSNorm over o (32 heads of 128). Achieved GB/s counts each input read and
+    each output written once."""
+    import torch
+
+    gen = torch.Generator(device=dev).manual_seed(9)
+    T, C, K, H, D = 32768, 8192, 4, 32, 128
+    x = torch.randn((1, T, C), device=dev, generator=gen).to(torch.bfloat16)
+    w = torch.randn((C, K), device=dev, generator=gen) * 0.5
+    bias = torch.randn((C,), device=dev, generator=gen) * 0.1
+    y = torch.empty_like(x)
+    o = torch.randn((1, T, H, D), device=dev, generator=gen).to(torch.bfloat16)
+    z = torch.randn((1, T, H, D), device=dev, generator=gen).to(torch.bfloat16)
+    wt = torch.randn((D,), device=dev, generator=gen)
+    yn = torch.empty_like(o)
+
+    def conv():
+        gdn.gdn_causal_conv1d(x, w, bias, None, silu=True, y=y, stream=stream)
+
+    def norm():
+        gdn.gdn_gated_rmsnorm(o, z, wt, eps=1e-6, y=yn, stream=stream)
+
+    out = {}
+    for name, fn, nbytes in (("causal_conv1d_32k", conv, 2 * x.numel() * 2),
+                             ("gated_rmsnorm_32k", norm, 3 * o.numel() * 2)):
+        ms = timed(fn, 10)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": ms, "bytes": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
+    return out
+
+
 def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
     """gdn_chunk_fwd step time on the stateless 8K and padded 8K workloads, and the padded
     rows packed as variable-length sequences (gdn_chunk_fwd_varlen)."""
@@ -392,6 +425,7 @@ def main():
         line["other_workloads"] = other_workloads(gdn, WORKLOADS, make_inputs, dev, stream, timed)
         line["fused_prologue_32k"] = prologue_timing(gdn, inp, dev, stream, timed)
         line["backward_8k"] = backward_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
+        line["layer_ops"] = layer_ops_timing(gdn, dev, stream, timed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line))

@@ -177,6 +177,33 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The layer steps around the core (PR #1035, section "What does this PR do": a
+ * depthwise Conv1D on the projected Q/K/V before the Gated DeltaNet, whose left halo is
+ * all the p2p mode exchanges between neighbouring ranks; RMSNorm and gating on its
+ * output before the output projection). Both are single streaming passes in fp32
+ * arithmetic over io-dtype tensors (GDN_F32 or GDN_BF16; pointers 16-byte aligned for
+ * bf16, 32-byte for fp32).
+ *
+ * Causal depthwise Conv1D, channels last:
+ *   y[b,t,c] = act(bias[c] + sum_{j<K} w[c,j] x[b, t-K+1+j, c]),  act = SiLU if apply_silu
+ * x, y [B, T, C]; w [C, K] fp32; bias [C] fp32 or NULL; x_prev [B, K-1, C] or NULL: the
+ * K - 1 tokens before each sequence (a rank's left halo; zeros if NULL). K in {2, 3, 4},
+ * C % 8 == 0. y must not alias x.
+ */
+gdn_status gdn_causal_conv1d(int32_t B, int32_t T, int32_t C, int32_t K, int32_t io_dtype,
+                             const void* x, const float* w, const float* bias, const void* x_prev,
+                             int32_t apply_silu, void* y, void* stream);
+
+/*
+ * Gated RMSNorm over rows of D values (one token and value head of o):
+ *   y[r,:] = o[r,:] / sqrt(mean(o[r,:]^2) + eps) * weight * z[r,:] * sigmoid(z[r,:])
+ * o, z, y [rows, D]; weight [D] fp32 (shared by all rows); D in {16, 32, 64, 128}.
+ * y may alias o.
+ */
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t D, int32_t io_dtype, const void* o, const void* z,
+                             const float* weight, float eps, void* y, void* stream);
+
+/*
  * Workspace for the segment calls (gdn_segment_summary, then
  * gdn_apply_initial_state on the same workspace). seg_len must be a positive
  * multiple of 64 that divides T; P = T / seg_len segments.

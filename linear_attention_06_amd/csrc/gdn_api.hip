@@ -354,6 +354,53 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
     }
 }
 
+gdn_status gdn_causal_conv1d(int32_t B, int32_t T, int32_t C, int32_t K, int32_t io_dtype, const void* x,
+                             const float* w, const float* bias, const void* x_prev, int32_t apply_silu, void* y,
+                             void* stream) {
+    try {
+        if (B < 0 || T < 0 || C < 0) return fail(GDN_EINVAL, "B, T and C must be >= 0");
+        if (K < 2 || K > 4) return fail(GDN_EUNSUPPORTED, "K=%d: kernel widths 2, 3 and 4 are supported", K);
+        if (C % 8) return fail(GDN_EUNSUPPORTED, "C=%d must be a multiple of 8", C);
+        if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+            return fail(GDN_EUNSUPPORTED, "io_dtype=%d: only GDN_F32 and GDN_BF16", io_dtype);
+        if (B > 65535) return fail(GDN_EUNSUPPORTED, "B=%d exceeds 65535", B);
+        const int64_t n = static_cast<int64_t>(B) * T * C;
+        if (n == 0) return GDN_OK;
+        if (!x || !w || !y) return fail(GDN_EINVAL, "x, w and y must be non-NULL");
+        const size_t align = io_dtype == GDN_BF16 ? 16 : 32;
+        if (reinterpret_cast<uintptr_t>(x) % align || reinterpret_cast<uintptr_t>(y) % align ||
+            (x_prev && reinterpret_cast<uintptr_t>(x_prev) % align))
+            return fail(GDN_EINVAL, "x, x_prev and y must be %zu-byte aligned", align);
+        gdn::ConvArgs a{B, T, C, K, apply_silu ? 1 : 0, x, w, bias, x_prev, y};
+        hipError_t e = gdn::launch_causal_conv1d(a, io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? GDN_OK : hip_fail(e, "conv1d kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t D, int32_t io_dtype, const void* o, const void* z,
+                             const float* weight, float eps, void* y, void* stream) {
+    try {
+        if (rows < 0) return fail(GDN_EINVAL, "rows must be >= 0");
+        if (!head_dim_ok(D)) return fail(GDN_EUNSUPPORTED, "D=%d: 16, 32, 64 or 128", D);
+        if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
+            return fail(GDN_EUNSUPPORTED, "io_dtype=%d: only GDN_F32 and GDN_BF16", io_dtype);
+        if (!(eps >= 0.f) || eps - eps != 0.f) return fail(GDN_EINVAL, "eps must be finite and >= 0");
+        if (rows == 0) return GDN_OK;
+        if (!o || !z || !weight || !y) return fail(GDN_EINVAL, "o, z, weight and y must be non-NULL");
+        const size_t align = io_dtype == GDN_BF16 ? 16 : 32;
+        if (reinterpret_cast<uintptr_t>(o) % align || reinterpret_cast<uintptr_t>(z) % align ||
+            reinterpret_cast<uintptr_t>(y) % align)
+            return fail(GDN_EINVAL, "o, z and y must be %zu-byte aligned", align);
+        gdn::NormArgs a{rows, D, eps, o, z, weight, y};
+        hipError_t e = gdn::launch_gated_rmsnorm(a, io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? GDN_OK : hip_fail(e, "gated rmsnorm kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
 gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;

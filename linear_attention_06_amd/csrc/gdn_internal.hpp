@@ -147,6 +147,25 @@ struct BwdArgs {
     float* dh0_out;           // [B,H,dk,dv] or NULL
 };
 
+// Layer steps around the core (gdn_layer_ops.hip).
+struct ConvArgs {
+    int B, T, C, K, silu;
+    const void* x;        // [B,T,C] io dtype
+    const float* w;       // [C,K]
+    const float* bias;    // [C] or NULL
+    const void* x_prev;   // [B,K-1,C] io dtype (tokens before the sequence) or NULL
+    void* y;              // [B,T,C] io dtype
+};
+struct NormArgs {
+    int64_t rows;
+    int D;
+    float eps;
+    const void* o;        // [rows,D] io dtype
+    const void* z;        // [rows,D] io dtype
+    const float* weight;  // [D]
+    void* y;              // [rows,D] io dtype
+};
+
 // Launchers. Each returns the HIP status of its launches.
 hipError_t launch_prep_f32path(const PrepArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_state_f32path(const StateArgs& a, bool io_bf16, hipStream_t s);
@@ -154,5 +173,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s);
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, bool io_bf16, hipStream_t s);
+hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const NormArgs& a, bool io_bf16, hipStream_t s);
 
 }  // namespace gdn

@@ -24,7 +24,8 @@ CHUNK = 64
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
            "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace",
-           "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd",
+           "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d",
+           "gdn_gated_rmsnorm",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
            "gdn_apply_initial_state")
 
@@ -69,12 +70,14 @@ def lib():
         L.gdn_chunk_fwd_varlen.argtypes = [pp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_chunk_bwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
         L.gdn_chunk_bwd.argtypes = [pp] + [vp] * 15 + [sz, vp]
+        L.gdn_causal_conv1d.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
+        L.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp]
         L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd",
                      "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace", "gdn_chunk_fwd_varlen",
-                     "gdn_chunk_bwd_workspace", "gdn_chunk_bwd",
+                     "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d", "gdn_gated_rmsnorm",
                      "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -268,6 +271,41 @@ def gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, dhT=None, valid_len=None, want_dh0=
                                _ptr(dh0), _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_chunk_bwd")
     return dq, dk, dv, dg, dbeta, dh0
+
+
+def _io_code(t):
+    return {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}.get(t.dtype, -1)
+
+
+def gdn_causal_conv1d(x, w, bias=None, x_prev=None, silu=True, y=None, stream=None):
+    """Causal depthwise Conv1D over tokens: x [B,T,C], w [C,K] fp32, bias [C], x_prev
+    [B,K-1,C] (the tokens before the sequence). Returns y [B,T,C] in x's dtype."""
+    _dev(x, "x")
+    _dev(w, "w", torch.float32)
+    _dev(bias, "bias", torch.float32)
+    _dev(x_prev, "x_prev", x.dtype)
+    B, T, C = x.shape
+    K = w.shape[1]
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", x.dtype)
+    _check(lib().gdn_causal_conv1d(B, T, C, K, _io_code(x), _ptr(x), _ptr(w), _ptr(bias), _ptr(x_prev),
+                                   1 if silu else 0, _ptr(y), _stream(stream)), "gdn_causal_conv1d")
+    return y
+
+
+def gdn_gated_rmsnorm(o, z, weight, eps=1e-6, y=None, stream=None):
+    """Gated RMSNorm over the last dim D of o (rows = all leading dims)."""
+    _dev(o, "o")
+    _dev(z, "z", o.dtype)
+    _dev(weight, "weight", torch.float32)
+    D = o.shape[-1]
+    if y is None:
+        y = torch.empty_like(o)
+    _dev(y, "y", o.dtype)
+    _check(lib().gdn_gated_rmsnorm(o.numel() // max(D, 1), D, _io_code(o), _ptr(o), _ptr(z), _ptr(weight),
+                                   ctypes.c_float(eps), _ptr(y), _stream(stream)), "gdn_gated_rmsnorm")
+    return y
 
 
 def gdn_segment_summary(q, k, v, g, beta, seg_len, M=None, S=None, want_m=True, want_s=True,
