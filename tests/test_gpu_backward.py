@@ -9,7 +9,7 @@ import pytest
 import torch
 
 from oracle import backward
-from gpu_common import TOL_F32, dev, np_f64, sync, to_dev
+from gpu_common import TOL_F32, dev, np_f64, sync, to_dev, workload_inputs
 from helpers import rel_l2
 from linear_attention_06_amd import gdn
 from linear_attention_06_amd.inputs import WORKLOADS, make_inputs
@@ -74,3 +74,54 @@ def test_backward_is_deterministic():
     sync()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_backward_full_size_sampled_against_oracle():
+    """The stateless 8K workload (32 value heads, d = 128) in the launch configuration the
+    bench times, with the output gradient nonzero on the first 1024 tokens only and no
+    final-state gradient: then the gradients of those tokens depend on them alone and the
+    oracle checks query/key head 0 (value heads 0 and 1) on them, while every gradient of the
+    later tokens is exactly zero."""
+    inp = workload_inputs("stateless_8k")
+    q, k, v, g, beta, _, _ = to_dev(inp)
+    rng = np.random.default_rng(11)
+    L = 1024
+    d_o = np.zeros(v.shape, np.float32)
+    d_o[:, :L] = rng.standard_normal((1, L) + tuple(v.shape[2:]))
+    from linear_attention_06_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+    bits = f32_to_bf16_bits(d_o)
+    d_o_t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev())
+    dq, dk, dv, dg, db, dh0 = gdn.gdn_chunk_bwd(q, k, v, g, beta, None, d_o_t)
+    sync()
+    for x in (dq, dk, dv, dg, db):
+        assert torch.all(x[:, L:] == 0)
+    qf, kf, vf, gf, bf, _ = inp.f64()
+    ref = backward.gdn_bwd(qf[:, :L, :1], kf[:, :L, :1], vf[:, :L, :2], gf[:, :L, :2], bf[:, :L, :2], None,
+                           bf16_bits_to_f32(bits)[:, :L, :2].astype(np.float64))
+    got = (dq[:, :L, :1], dk[:, :L, :1], dv[:, :L, :2], dg[:, :L, :2], db[:, :L, :2], dh0[:, :2])
+    for nm, x, r in zip(NAMES, got, ref):
+        err = rel_l2(np_f64(x), r)
+        print("8k sampled %s rel-L2 %.3e" % (nm, err))
+        assert err <= TOL_F32, nm
+
+
+def test_initial_state_gradient_is_the_summary_transpose():
+    """With no output gradient, dh0 = M^T dhT where M is the sequence's state-transition
+    summary: the backward's reverse recurrence checked against the segment-summary pass
+    (split-bf16 matrix cores, an independent GPU path) on a slowly decaying 2048-token
+    problem at d = 128, where M is far from zero."""
+    from linear_attention_06_amd.inputs import slow_decay
+    w = dataclasses.replace(slow_decay(WORKLOADS["stateful_32k"], seed=606, seg_len=2048), T=2048, Hqk=2, H=4)
+    inp = make_inputs(w)
+    q, k, v, g, beta, h0, _ = to_dev(inp)
+    M, _, _ = gdn.gdn_segment_summary(q, k, v, g, beta, 2048, want_s=False)
+    dhT = torch.randn((1, 4, 128, 128), device=dev())
+    zero = torch.zeros_like(v)
+    *_, dh0 = gdn.gdn_chunk_bwd(q, k, v, g, beta, h0, zero, dhT)
+    sync()
+    want = torch.matmul(M[:, :, 0].transpose(-1, -2).contiguous(), dhT)
+    ratio = (want.norm() / dhT.norm()).item()
+    err = rel_l2(np_f64(dh0), np_f64(want))
+    print("dh0 vs M^T dhT rel-L2 %.3e (|M^T dhT| / |dhT| = %.3f)" % (err, ratio))
+    assert ratio > 0.05
+    assert err <= 1e-3
