@@ -169,3 +169,60 @@ def test_kernel_path_selection():
     assert path(io_dtype=gdn.GDN_F32, dk=128, dv=128) == "f32-valu"
     with pytest.raises(gdn.GdnError):
         path(chunk=32)
+
+
+def test_varlen_argument_checks():
+    L = gdn.lib()
+    n = ctypes.c_size_t(0)
+    bf = P(B=3, T=500, H=4, Hqk=2, dk=128, dv=128, io_dtype=gdn.GDN_BF16)
+    assert L.gdn_chunk_fwd_varlen_workspace(ctypes.byref(bf), -1, ctypes.byref(n)) == gdn.GDN_EINVAL
+    assert L.gdn_chunk_fwd_varlen_workspace(ctypes.byref(bf), 300, ctypes.byref(n)) == gdn.GDN_OK
+    # ceil(300 / 64) = 5 chunk records per sequence and head
+    assert n.value >= 3 * 4 * 5 * (2 * 6 * 512 * 2 + 256 * 4)
+    vp = ctypes.c_void_p
+    call = lambda p, cu=1, mx=300, q=1: L.gdn_chunk_fwd_varlen(ctypes.byref(p), vp(cu) if cu else None, mx,
+                                                                vp(q) if q else None, vp(1), vp(1), vp(1), vp(1),
+                                                                None, vp(1), None, vp(256), 1 << 40, None)
+    assert call(bf, cu=None) == gdn.GDN_EINVAL
+    assert call(bf, q=None) == gdn.GDN_EINVAL
+    assert call(bf, mx=-5) == gdn.GDN_EINVAL
+    assert call(P(B=3, T=500, H=4, Hqk=2, dk=128, dv=128, io_dtype=gdn.GDN_BF16, valid_len=1234)) == gdn.GDN_EINVAL
+
+
+def test_backward_argument_checks():
+    L = gdn.lib()
+    p = P()
+    n = ctypes.c_size_t(0)
+    assert L.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)) == gdn.GDN_OK
+    # checkpoints B H ceil(T/64) dk dv and per-tile partials B T H (dv/16) 2 (dk + 1), fp32
+    assert n.value >= 4 * (1 * 8 * 2 * 16 * 16 + 1 * 128 * 8 * 1 * 2 * (16 + 1))
+    vp = ctypes.c_void_p
+    args = [vp(1)] * 5 + [None, vp(1), None] + [vp(1)] * 5 + [None]
+    bad = list(args)
+    bad[8] = None                                   # dq
+    assert L.gdn_chunk_bwd(ctypes.byref(p), *bad, vp(256), n.value, None) == gdn.GDN_EINVAL
+    assert L.gdn_chunk_bwd(ctypes.byref(p), *args, vp(256), n.value - 1, None) == gdn.GDN_EWORKSPACE
+    assert L.gdn_chunk_bwd(ctypes.byref(p), *args, vp(258), n.value, None) == gdn.GDN_EWORKSPACE
+
+
+def test_layer_step_argument_checks():
+    L = gdn.lib()
+    vp = ctypes.c_void_p
+    conv = lambda B=1, T=10, C=16, K=4, io=gdn.GDN_BF16, x=256, w=1, y=512: L.gdn_causal_conv1d(
+        B, T, C, K, io, vp(x) if x else None, vp(w) if w else None, None, None, 1, vp(y) if y else None, None)
+    assert conv(K=5) == gdn.GDN_EUNSUPPORTED
+    assert conv(K=1) == gdn.GDN_EUNSUPPORTED
+    assert conv(C=12) == gdn.GDN_EUNSUPPORTED
+    assert conv(io=7) == gdn.GDN_EUNSUPPORTED
+    assert conv(T=-1) == gdn.GDN_EINVAL
+    assert conv(x=None) == gdn.GDN_EINVAL
+    assert conv(x=264) == gdn.GDN_EINVAL               # not 16-byte aligned
+    assert conv(T=0) == gdn.GDN_OK                      # nothing to do, nothing launched
+    norm = lambda rows=10, D=128, io=gdn.GDN_BF16, eps=1e-6, o=256: L.gdn_gated_rmsnorm(
+        rows, D, io, vp(o) if o else None, vp(256), vp(1), ctypes.c_float(eps), vp(512), None)
+    assert norm(D=48) == gdn.GDN_EUNSUPPORTED
+    assert norm(eps=float("nan")) == gdn.GDN_EINVAL
+    assert norm(eps=-1.0) == gdn.GDN_EINVAL
+    assert norm(o=None) == gdn.GDN_EINVAL
+    assert norm(rows=-1) == gdn.GDN_EINVAL
+    assert norm(rows=0) == gdn.GDN_OK
