@@ -15,10 +15,13 @@
 // The pages (hyper-parallel issue #320, the test report for PR #1114, section 4)
 // check dq, dk, dv, dg, dbeta and dH0 against a reference; this is that gradient.
 //
-// Three kernels, one block of 256 threads per (b, h, 16 state columns) for the first
-// two: thread 16 c + i holds column c of the tile at rows i + 16 j (j < dk / 16), so
-// that the 16 threads of a column are one DPP row and a column sum is four DPP
-// rotations.
+// Three kernels, one block of 16 x TPC threads per (b, h, 16 state columns) for the first
+// two: thread TPC c + i holds column c of the tile at rows i + TPC j (j < dk / TPC), so
+// that the TPC threads of a column are one DPP row (TPC = 16: four DPP rotations sum a
+// column) or two (TPC = 32, used for dk >= 32: then a v_permlane16_swap). With 32 the
+// SIMDs run two waves of a block and each thread's share of the token chain halves:
+// 12.5 against 15.1 ms at H = 32, d = 128, 8K tokens; 64 threads per column were slower
+// again (15.9 ms).
 //   bwd_ckpt    the forward state at every chunk start (64 tokens) into the workspace;
 //   bwd_sweep   chunks in reverse: the chunk's states are recomputed from its
 //               checkpoint, with a second checkpoint every 8 tokens in LDS, and each
@@ -48,6 +51,18 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Sum over the TPC lanes of a column (TPC = 16: one DPP row; TPC = 32: two DPP rows, the
+// second step v_permlane16_swap, whose pair of results sums odd and even rows).
+template <int TPC>
+__device__ __forceinline__ float col_sum(float x) {
+    x = row_sum16(x);
+    if constexpr (TPC == 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+
 // Chunk operands in LDS (fp32): K, optionally Q, the tile's columns of V and of the
 // output gradient, g and beta; padded tokens read as zero.
 template <typename IO, int DK, bool kQ>
@@ -60,7 +75,7 @@ struct ChunkLds {
     float beta[64];
 };
 
-template <typename IO, int DK, bool kQ>
+template <typename IO, int DK, bool kQ, int NTH>
 __device__ __forceinline__ void load_chunk(ChunkLds<IO, DK, kQ>& L, const BwdArgs& a, const RowSpan& rs, int h,
                                            int hq, int col0, int n, int tid) {
     const IO* k = static_cast<const IO*>(a.k);
@@ -68,7 +83,7 @@ __device__ __forceinline__ void load_chunk(ChunkLds<IO, DK, kQ>& L, const BwdArg
     const IO* v = static_cast<const IO*>(a.v);
     const IO* d = static_cast<const IO*>(a.d_o);
     const int64_t t0 = static_cast<int64_t>(n) * kChunk;
-    for (int e = tid; e < 64 * DK; e += 256) {
+    for (int e = tid; e < 64 * DK; e += NTH) {
         const int r = e / DK, x = e % DK;
         const int64_t tok = t0 + r;
         const bool ok = tok < rs.valid;
@@ -76,7 +91,7 @@ __device__ __forceinline__ void load_chunk(ChunkLds<IO, DK, kQ>& L, const BwdArg
         L.k[r][x] = ok ? ld_in(k, idx) : 0.f;
         if (kQ) L.q[r][x] = ok ? ld_in(q, idx) : 0.f;
     }
-    for (int e = tid; e < 64 * 16; e += 256) {
+    for (int e = tid; e < 64 * 16; e += NTH) {
         const int r = e / 16, c = e % 16;
         const int64_t tok = t0 + r;
         const bool ok = tok < rs.valid;
@@ -93,72 +108,72 @@ __device__ __forceinline__ void load_chunk(ChunkLds<IO, DK, kQ>& L, const BwdArg
     }
 }
 
-// One forward token step on the thread's column slice S[j] = S[i + 16 j][c]; returns w_c.
-template <int RJ, typename Lds>
+// One forward token step on the thread's column slice S[j] = S[i + TPC j][c]; returns w_c.
+template <int RJ, int TPC, typename Lds>
 __device__ __forceinline__ float fwd_step(float (&S)[RJ], const Lds& L, int u, int i, int c) {
     float w = 0.f;
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) w += L.k[u][i + 16 * j] * S[j];
-    w = row_sum16(w);
+    for (int j = 0; j < RJ; ++j) w += L.k[u][i + TPC * j] * S[j];
+    w = col_sum<TPC>(w);
     const float eg = expf(L.g[u]), bt = L.beta[u], vc = L.v[u][c];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
-        const float kr = L.k[u][i + 16 * j];
+        const float kr = L.k[u][i + TPC * j];
         S[j] = eg * (S[j] - bt * kr * w) + bt * kr * vc;
     }
     return w;
 }
 
-template <typename IO, int DK>
-__global__ __launch_bounds__(256) void bwd_ckpt(BwdArgs a) {
-    constexpr int RJ = DK / 16;
+template <typename IO, int DK, int TPC>
+__global__ __launch_bounds__(16 * TPC) void bwd_ckpt(BwdArgs a) {
+    constexpr int RJ = DK / TPC, NTH = 16 * TPC;
     __shared__ ChunkLds<IO, DK, false> L;
     const int col0 = 16 * blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int hq = h / (a.H / a.Hqk);
-    const int tid = threadIdx.x, c = tid >> 4, i = tid & 15;
+    const int tid = threadIdx.x, c = tid / TPC, i = tid % TPC;
     const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     float S[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j)
-        S[j] = a.h0 ? a.h0[(bh * DK + i + 16 * j) * a.dv + col0 + c] : 0.f;
+        S[j] = a.h0 ? a.h0[(bh * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
     for (int n = 0; n < a.NT; ++n) {
         float* ck = a.ckpt + (bh * a.NT + n) * DK * a.dv;
 #pragma unroll
-        for (int j = 0; j < RJ; ++j) ck[static_cast<int64_t>(i + 16 * j) * a.dv + col0 + c] = S[j];
+        for (int j = 0; j < RJ; ++j) ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c] = S[j];
         __syncthreads();
-        load_chunk<IO, DK, false>(L, a, rs, h, hq, col0, n, tid);
+        load_chunk<IO, DK, false, NTH>(L, a, rs, h, hq, col0, n, tid);
         __syncthreads();
-        for (int u = 0; u < 64; ++u) fwd_step<RJ>(S, L, u, i, c);
+        for (int u = 0; u < 64; ++u) fwd_step<RJ, TPC>(S, L, u, i, c);
     }
 }
 
-template <typename IO, int DK>
-__global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
-    constexpr int RJ = DK / 16;
+template <typename IO, int DK, int TPC>
+__global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
+    constexpr int RJ = DK / TPC, NTH = 16 * TPC;
     __shared__ ChunkLds<IO, DK, true> L;
-    __shared__ float sub_s[8][RJ][256];        // state every 8 tokens of the chunk
+    __shared__ float sub_s[8][RJ][NTH];        // state every 8 tokens of the chunk
     __shared__ float red_s[2][16][DK];         // per-column terms of dq and dk
     __shared__ float red2_s[2][16];            // per-column terms of dg and dbeta
     const int tiles = a.dv / 16;
     const int tile = blockIdx.x, col0 = 16 * tile, h = blockIdx.y, b = blockIdx.z;
     const int hq = h / (a.H / a.Hqk);
-    const int tid = threadIdx.x, c = tid >> 4, i = tid & 15;
+    const int tid = threadIdx.x, c = tid / TPC, i = tid % TPC;
     const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
 
     float dS[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j)
-        dS[j] = a.dhT ? a.dhT[(bh * DK + i + 16 * j) * a.dv + col0 + c] : 0.f;
+        dS[j] = a.dhT ? a.dhT[(bh * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
 
     for (int n = a.NT - 1; n >= 0; --n) {
         __syncthreads();
-        load_chunk<IO, DK, true>(L, a, rs, h, hq, col0, n, tid);
+        load_chunk<IO, DK, true, NTH>(L, a, rs, h, hq, col0, n, tid);
         float S[RJ];
         const float* ck = a.ckpt + (bh * a.NT + n) * DK * a.dv;
 #pragma unroll
-        for (int j = 0; j < RJ; ++j) S[j] = ck[static_cast<int64_t>(i + 16 * j) * a.dv + col0 + c];
+        for (int j = 0; j < RJ; ++j) S[j] = ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c];
         __syncthreads();
         // forward through the chunk, keeping the state before every 8th token
         for (int u = 0; u < 64; ++u) {
@@ -166,7 +181,7 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < RJ; ++j) sub_s[u >> 3][j][tid] = S[j];
             }
-            fwd_step<RJ>(S, L, u, i, c);
+            fwd_step<RJ, TPC>(S, L, u, i, c);
         }
         for (int s = 7; s >= 0; --s) {
             // the piece's states in registers: St[u] before token 8 s + u, St[u + 1] after it
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
             for (int uu = 0; uu < 8; ++uu) {
 #pragma unroll
                 for (int j = 0; j < RJ; ++j) St[uu + 1][j] = St[uu][j];
-                w[uu] = fwd_step<RJ>(St[uu + 1], L, 8 * s + uu, i, c);
+                w[uu] = fwd_step<RJ, TPC>(St[uu + 1], L, 8 * s + uu, i, c);
             }
 #pragma unroll
             for (int uu = 7; uu >= 0; --uu) {
@@ -189,18 +204,18 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
                 float z = 0.f, ms = 0.f;
 #pragma unroll
                 for (int j = 0; j < RJ; ++j) {
-                    M[j] = dS[j] + L.q[u][i + 16 * j] * doc;
-                    z += M[j] * L.k[u][i + 16 * j];
+                    M[j] = dS[j] + L.q[u][i + TPC * j] * doc;
+                    z += M[j] * L.k[u][i + TPC * j];
                     ms += M[j] * St[uu][j];
                 }
-                z = row_sum16(z);
-                ms = row_sum16(ms);
+                z = col_sum<TPC>(z);
+                ms = col_sum<TPC>(ms);
                 const bool inrow = t < rs.extent;      // the tail of the last chunk is past the row
                 const int64_t tokrow = rs.start + t;
                 if (i == 0 && inrow) a.dv_out[(tokrow * a.H + h) * a.dv + col0 + c] = valid ? bt * z : 0.f;
 #pragma unroll
                 for (int j = 0; j < RJ; ++j) {
-                    const int r = i + 16 * j;
+                    const int r = i + TPC * j;
                     red_s[0][c][r] = St[uu + 1][j] * doc;
                     red_s[1][c][r] = M[j] * (bt * vc - eg * bt * w[uu]) - eg * bt * St[uu][j] * z;
                 }
@@ -227,13 +242,13 @@ __global__ __launch_bounds__(256) void bwd_sweep(BwdArgs a) {
                 }
                 __syncthreads();
 #pragma unroll
-                for (int j = 0; j < RJ; ++j) dS[j] = eg * (M[j] - bt * L.k[u][i + 16 * j] * z);
+                for (int j = 0; j < RJ; ++j) dS[j] = eg * (M[j] - bt * L.k[u][i + TPC * j] * z);
             }
         }
     }
     if (a.dh0_out) {
 #pragma unroll
-        for (int j = 0; j < RJ; ++j) a.dh0_out[(bh * DK + i + 16 * j) * a.dv + col0 + c] = dS[j];
+        for (int j = 0; j < RJ; ++j) a.dh0_out[(bh * DK + i + TPC * j) * a.dv + col0 + c] = dS[j];
     }
 }
 
@@ -270,17 +285,23 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
     }
 }
 
+// Threads per state column: 32 (two DPP rows, 512-thread blocks, two waves per SIMD)
+// once dk >= 32, else 16.
+constexpr int kTpc(int dk) { return dk >= 32 ? 32 : 16; }
+
 template <typename IO>
 hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
     void* args[] = {const_cast<BwdArgs*>(&a)};
     const void *f1 = nullptr, *f2 = nullptr, *f3 = nullptr;
+    unsigned nth = 256;
     switch (a.dk) {
-#define GDN_BWD_CASE(D)                                                   \
-        case D:                                                           \
-            f1 = reinterpret_cast<const void*>(&bwd_ckpt<IO, D>);         \
-            f2 = reinterpret_cast<const void*>(&bwd_sweep<IO, D>);        \
-            f3 = reinterpret_cast<const void*>(&bwd_reduce<D>);           \
+#define GDN_BWD_CASE(D)                                                                  \
+        case D:                                                                          \
+            f1 = reinterpret_cast<const void*>(&bwd_ckpt<IO, D, kTpc(D)>);               \
+            f2 = reinterpret_cast<const void*>(&bwd_sweep<IO, D, kTpc(D)>);              \
+            f3 = reinterpret_cast<const void*>(&bwd_reduce<D>);                          \
+            nth = 16 * kTpc(D);                                                          \
             break;
         GDN_BWD_CASE(16)
         GDN_BWD_CASE(32)
@@ -289,9 +310,9 @@ hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t s) {
 #undef GDN_BWD_CASE
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipLaunchKernel(f1, grid, dim3(256), args, 0, s);
+    hipError_t e = hipLaunchKernel(f1, grid, dim3(nth), args, 0, s);
     if (e != hipSuccess) return e;
-    e = hipLaunchKernel(f2, grid, dim3(256), args, 0, s);
+    e = hipLaunchKernel(f2, grid, dim3(nth), args, 0, s);
     if (e != hipSuccess || a.T == 0) return e;
     return hipLaunchKernel(f3, dim3(static_cast<unsigned>(a.T), static_cast<unsigned>(a.B)), dim3(256), args, 0, s);
 }
