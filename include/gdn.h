@@ -216,7 +216,8 @@ gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* 
  *   M[b,h,p] = the product of the segment's token transitions
  *              exp(g_t)(I - beta_t k_t k_t^T), later tokens on the left.
  * Either output may be NULL to skip it. Leaves in ws the chunk intermediates that
- * gdn_apply_initial_state reuses. valid_len must be NULL (GDN_EUNSUPPORTED).
+ * gdn_apply_initial_state reuses. With valid_len, padded tokens are identities (M and S
+ * are those of the valid tokens; a segment of padding only has M = I, S = 0).
  */
 gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len,
                                const void* q, const void* k, const void* v,

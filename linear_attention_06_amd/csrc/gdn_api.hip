@@ -113,7 +113,6 @@ gdn_status check_segments(const gdn_problem& p, int32_t seg_len, int64_t* P) {
     if (seg_len <= 0 || seg_len % gdn::kChunk)
         return fail(GDN_EINVAL, "seg_len=%d must be a positive multiple of 64", seg_len);
     if (p.T % seg_len) return fail(GDN_EINVAL, "seg_len=%d does not divide T=%d", seg_len, p.T);
-    if (p.valid_len) return fail(GDN_EUNSUPPORTED, "valid_len is not supported by the segment calls");
     *P = p.T / seg_len;
     if (static_cast<int64_t>(p.B) * *P > 65535)
         return fail(GDN_EUNSUPPORTED, "B * P = %lld exceeds 65535", static_cast<long long>(p.B * *P));

@@ -309,10 +309,10 @@ def gdn_gated_rmsnorm(o, z, weight, eps=1e-6, y=None, stream=None):
 
 
 def gdn_segment_summary(q, k, v, g, beta, seg_len, M=None, S=None, want_m=True, want_s=True,
-                        ws=None, stream=None):
+                        ws=None, stream=None, valid_len=None):
     """Per-segment (M, S). Returns (M, S, ws); ws is needed by gdn_apply_initial_state."""
     _io_checks(q, k, v, g, beta)
-    p = problem(q, v)
+    p = problem(q, v, valid_len)
     P = p.T // seg_len if seg_len > 0 else 0
     dev = v.device
     if M is None and want_m:
@@ -351,11 +351,11 @@ def gdn_summary_combine(M, S, h0=None, H_in=None, want_prefix=False, M_prefix=No
 
 
 def gdn_apply_initial_state(q, k, v, g, beta, H_in, seg_len, ws, o=None, hT=None, want_state=True,
-                            stream=None):
+                            stream=None, valid_len=None):
     """Segment outputs from their incoming states. Returns (o, hT or None)."""
     _io_checks(q, k, v, g, beta)
     _dev(H_in, "H_in", torch.float32)
-    p = problem(q, v)
+    p = problem(q, v, valid_len)
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     if hT is None and want_state:

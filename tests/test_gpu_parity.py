@@ -89,6 +89,35 @@ def test_segmented_32k_matches_oracle_and_unsplit_run():
     assert_close(np_f64(hT), np_f64(hT_full), TOL_BF16, "segmented vs unsplit hT")
 
 
+def test_padded_8k_in_segments_matches_oracle():
+    """The padded 8K workload (two rows of 7777 valid tokens) through the segment calls in
+    4 segments of 2048: the last segment holds the padding, whose transitions are identities."""
+    inp = workload_inputs("padded_8k")
+    seg = 2048
+    q64, k64, v64, g64, b64, _ = inp.f64()
+    M_ref, S_ref = oracle.gdn_segment_summary(q64, k64, v64, g64, b64, seg, valid_len=inp.valid_len)
+    q, k, v, g, beta, _, vl = to_dev(inp)
+    M, S, ws = gdn.gdn_segment_summary(q, k, v, g, beta, seg, valid_len=vl)
+    H_in, _, hT_c = gdn.gdn_summary_combine(M, S, None)
+    o, hT = gdn.gdn_apply_initial_state(q, k, v, g, beta, H_in, seg, ws, valid_len=vl)
+    sync()
+    assert_close(np_f64(M), M_ref, TOL_BF16, "padded segment M")
+    assert_close(np_f64(S), S_ref, TOL_BF16, "padded segment S")
+    o_ref, hT_ref = oracle_fwd("padded_8k")
+    assert_close(np_f64(o), o_ref, TOL_BF16, "padded segmented o")
+    assert_close(np_f64(hT), hT_ref, TOL_BF16, "padded segmented hT")
+    assert_close(np_f64(hT_c), hT_ref, TOL_BF16, "padded combined hT")
+    tail = o[:, 7777:].float()
+    assert torch.all(tail == 0) and not torch.any(torch.signbit(tail))
+    # with 6000 valid tokens the last segment (tokens 6144..8191) is pure padding: its
+    # transitions are identities, so M = I and S = 0 exactly
+    vl2 = torch.full((2,), 6000, dtype=torch.int32, device=v.device)
+    M2, S2, _ = gdn.gdn_segment_summary(q, k, v, g, beta, seg, valid_len=vl2)
+    sync()
+    eye = torch.eye(128, device=M.device).expand_as(M2[:, :, -1])
+    assert torch.equal(M2[:, :, -1], eye) and torch.all(S2[:, :, -1] == 0)
+
+
 def test_padded_8k_matches_oracle_and_is_bit_exact():
     inp = workload_inputs("padded_8k")
     n = int(inp.valid_len[0])
