@@ -201,7 +201,7 @@ def layer_ops_timing(gdn, dev, stream, timed):
     """The streaming layer steps at the 32K layer's shapes: causal Conv1D (K = 4, SiLU) over
     the projected q/k/v channels (16 + 16 query/key heads and 32 value heads of 128: C = 8192)
     and the gated RMSNorm over o (32 heads of 128). Achieved GB/s counts each input read and
-    each output written once."""
+    each output written once. Then the three composed with the fused-prologue forward."""
     import torch
 
     gen = torch.Generator(device=dev).manual_seed(9)
@@ -227,6 +227,43 @@ def layer_ops_timing(gdn, dev, stream, timed):
         ms = timed(fn, 10)
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"ms": ms, "bytes": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
+
+    # the composed path: Conv1D over q/k/v channels, split, fused-prologue forward from a
+    # 0.1 N(0,1) initial state, gated RMSNorm (the split copies are torch plumbing)
+    Hqk = 16
+    a_g = torch.randn((1, T, H), device=dev, generator=gen)
+    b_g = torch.randn((1, T, H), device=dev, generator=gen)
+    A_log = torch.log(torch.rand((H,), device=dev, generator=gen) * 15 + 1)
+    dt = torch.exp(torch.rand((H,), device=dev, generator=gen) * (np.log(0.1) - np.log(1e-3)) + np.log(1e-3))
+    dt_bias = torch.log(torch.expm1(dt))
+    h0 = 0.1 * torch.randn((1, H, D, D), device=dev, generator=gen)
+    ov = torch.empty((1, T, H, D), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    p = gdn.problem(torch.empty((1, T, Hqk, D), dtype=torch.bfloat16, device=dev), ov)
+    ws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
+
+    def layer():
+        gdn.gdn_causal_conv1d(x, w, bias, None, silu=True, y=y, stream=stream)
+        with torch.cuda.stream(stream):
+            q_raw = y[..., :Hqk * D].reshape(1, T, Hqk, D).contiguous()
+            k_raw = y[..., Hqk * D:2 * Hqk * D].reshape(1, T, Hqk, D).contiguous()
+            v = y[..., 2 * Hqk * D:].reshape(1, T, H, D).contiguous()
+        gdn.gdn_chunk_fwd_prologue(q_raw, k_raw, v, a_g, b_g, A_log, dt_bias, D ** -0.5, h0, o=ov, hT=hT,
+                                   ws=ws, stream=stream)
+        gdn.gdn_gated_rmsnorm(ov, z, wt, eps=1e-6, y=yn, stream=stream)
+
+    ms = timed(layer, 5)
+    out["conv_prologue_core_norm_32k"] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                                          "note": "q/k/v split by torch copies"}
+
+    def layer_packed():   # the forward reads q_raw, k_raw, v straight out of the conv output
+        gdn.gdn_causal_conv1d(x, w, bias, None, silu=True, y=y, stream=stream)
+        gdn.gdn_chunk_fwd_prologue_qkv(y, Hqk, H, D, D, a_g, b_g, A_log, dt_bias, D ** -0.5, h0, o=ov, hT=hT,
+                                       ws=ws, stream=stream)
+        gdn.gdn_gated_rmsnorm(ov, z, wt, eps=1e-6, y=yn, stream=stream)
+
+    ms = timed(layer_packed, 5)
+    out["conv_prologue_core_norm_32k_packed_qkv"] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
     return out
 
 

@@ -133,6 +133,20 @@ gdn_status gdn_chunk_fwd_prologue(const gdn_problem* p,
                                   void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same fused-prologue forward reading q_raw, k_raw and v straight out of one packed
+ * tensor, as the Conv1D below produces it from the layer's projection:
+ *   qkv [B, T, C] bf16, C = 2 Hqk dk + H dv; token t holds q_raw (Hqk x dk), then k_raw
+ *   (Hqk x dk), then v (H x dv).
+ * No split copy is made: the kernels read the three parts with the token stride C.
+ * qkv must be 16-byte aligned. Everything else as gdn_chunk_fwd_prologue.
+ */
+gdn_status gdn_chunk_fwd_prologue_qkv(const gdn_problem* p, const void* qkv,
+                                      const float* a, const float* b,
+                                      const float* A_log, const float* dt_bias, float q_scale,
+                                      const float* h0, void* o, float* hT,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Packed variable-length sequences (the general form of issue #320's variable-length
  * case, section 5.2, where rows of one batch hold different numbers of valid tokens):
  * instead of B rows of T tokens with padding, the B sequences lie back to back in one

@@ -127,6 +127,7 @@ gdn_status run_prep(const gdn_problem& p, const Plan& pl, const void* q, const v
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.NT = static_cast<int>(pl.NT);
     a.q = q; a.k = k; a.g = g; a.beta = beta; a.valid_len = p.valid_len; a.ws = w;
     a.cu_seqlens = cu_seqlens;
+    a.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
     a.has_prologue = pro ? 1 : 0;
     a.pro = pro ? *pro : gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
     hipError_t e = use_mfma(p) ? gdn::launch_prep_mfma(a, s)
@@ -141,6 +142,8 @@ gdn::StateArgs state_args(const gdn_problem& p, const Plan& pl, const void* q, c
     a.NT = static_cast<int>(pl.NT);
     a.P = 1; a.Lc = static_cast<int>(pl.NT);
     a.q = q; a.k = k; a.v = v; a.valid_len = p.valid_len; a.cu_seqlens = nullptr; a.ws = w;
+    a.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
+    a.v_stride = static_cast<int64_t>(p.H) * p.dv;
     a.init_mode = gdn::kInitZero; a.s_init = nullptr; a.s_init_per_segment = 0;
     a.o = nullptr; a.s_out = nullptr; a.store_mode = gdn::kStoreNone; a.m_out = nullptr;
     return a;
@@ -396,6 +399,58 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t D, int32_t io_dtype, const vo
         gdn::NormArgs a{rows, D, eps, o, z, weight, y};
         hipError_t e = gdn::launch_gated_rmsnorm(a, io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? GDN_OK : hip_fail(e, "gated rmsnorm kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_chunk_fwd_prologue_qkv(const gdn_problem* p, const void* qkv, const float* a, const float* b,
+                                      const float* A_log, const float* dt_bias, float q_scale, const float* h0,
+                                      void* o, float* hT, void* ws, size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        if (!use_mfma(*p))
+            return fail(GDN_EUNSUPPORTED, "the fused prologue runs on the bf16 matrix-core path only "
+                                          "(io_dtype GDN_BF16, dk = 128)");
+        if (!(q_scale == q_scale) || q_scale - q_scale != 0.f)
+            return fail(GDN_EINVAL, "q_scale must be finite");
+        const int64_t C = 2 * static_cast<int64_t>(p->Hqk) * p->dk + static_cast<int64_t>(p->H) * p->dv;
+        if ((static_cast<int64_t>(p->T) + gdn::kChunk) * C * 2 >= (int64_t(1) << 31))
+            return fail(GDN_EUNSUPPORTED, "one batch row of qkv exceeds 2 GiB on the bf16 path");
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!qkv || !a || !b || !A_log || !dt_bias || !o))
+            return fail(GDN_EINVAL, "qkv, a, b, A_log, dt_bias and o must be non-NULL");
+        if (reinterpret_cast<uintptr_t>(qkv) % 16) return fail(GDN_EINVAL, "qkv must be 16-byte aligned");
+        const Plan pl = make_plan(*p, false);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (p->B == 0) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const gdn::Workspace w = carve(pl, ws);
+        const uint16_t* base = static_cast<const uint16_t*>(qkv);
+        const void* q = base;
+        const void* k = base + static_cast<int64_t>(p->Hqk) * p->dk;
+        const void* v = base + 2 * static_cast<int64_t>(p->Hqk) * p->dk;
+        const gdn::Prologue pro{a, b, A_log, dt_bias, q_scale};
+        if (pl.nch > 0) {
+            gdn::PrepArgs pa;
+            pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->Hqk; pa.dk = p->dk;
+            pa.NT = static_cast<int>(pl.NT);
+            pa.q = q; pa.k = k; pa.g = nullptr; pa.beta = nullptr; pa.valid_len = p->valid_len;
+            pa.cu_seqlens = nullptr; pa.qk_stride = C; pa.ws = w; pa.has_prologue = 1; pa.pro = pro;
+            const hipError_t e = gdn::launch_prep_mfma(pa, s);
+            if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
+        }
+        gdn::StateArgs sa = state_args(*p, pl, q, k, v, w);
+        sa.qk_stride = C;
+        sa.v_stride = C;
+        sa.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+        sa.s_init = h0;
+        sa.o = o;
+        sa.s_out = hT;
+        sa.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+        return run_state(*p, sa, s);
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

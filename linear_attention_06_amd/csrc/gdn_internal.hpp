@@ -88,6 +88,7 @@ struct PrepArgs {
     const float* beta;      // unused with a prologue
     const int32_t* valid_len;
     const int32_t* cu_seqlens;  // packed sequences (see row_span), or NULL
+    int64_t qk_stride;          // elements between consecutive tokens of q and k (Hqk dk if dense)
     Workspace ws;
     int has_prologue;       // 0: q, k, g, beta are used as given
     Prologue pro;
@@ -101,6 +102,8 @@ struct StateArgs {
     const void* v;                    // NULL: values are zero (M summary)
     const int32_t* valid_len;
     const int32_t* cu_seqlens;        // packed sequences (see row_span), or NULL
+    int64_t qk_stride, v_stride;      // elements between consecutive tokens of q/k and of v
+                                      // (Hqk dk and H ncols when dense; o is always dense)
     Workspace ws;
     int init_mode;
     const float* s_init;              // [B,H,Pin,dk,ncols], Pin = P when loading per segment, else 1

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
             const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
             const int64_t t = t0 + row;
             const int64_t off =
-                ((rs.start + (t < nvalid ? t : 0)) * a.Hqk + hq) * DK + 8 * cb;
+                (rs.start + (t < nvalid ? t : 0)) * a.qk_stride + hq * DK + 8 * cb;
             kv[u] = *reinterpret_cast<const u32x4*>(kin + off);
             qv[u] = *reinterpret_cast<const u32x4*>(qin + off);
         }
@@ -615,10 +615,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const int n0 = seg * a.Lc;
     const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
 
-    const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK;   // elements per token
-    const int64_t vo_row = static_cast<int64_t>(a.H) * ncols;
+    const int64_t qk_row = a.qk_stride;                          // elements between tokens of q, k
+    const int64_t v_row = a.v_stride;                            // ... of v
+    const int64_t vo_row = static_cast<int64_t>(a.H) * ncols;   // ... of o
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
-    const uint32_t vstep = static_cast<uint32_t>(kChunk * vo_row * 2);
+    const uint32_t vstep = static_cast<uint32_t>(kChunk * v_row * 2);
+    const uint32_t ostep = static_cast<uint32_t>(kChunk * vo_row * 2);
     const int first_loader = two_compute ? 2 : 1;
     // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
     // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 rho + j % 4)). A 1 KiB load fills one
@@ -641,10 +643,10 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // out-of-range tokens load as zero
         const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rs.start * qk_row;
         const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rs.start * qk_row;
-        const uint16_t* vin = static_cast<const uint16_t*>(a.v) + rs.start * vo_row;
+        const uint16_t* vin = static_cast<const uint16_t*>(a.v) + rs.start * v_row;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin, nvalid * qk_row * 2);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(outputs ? qin : kin, nvalid * qk_row * 2);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * vo_row * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * v_row * 2 : 0);
         const int64_t rec = static_cast<int64_t>(a.NT) * kTriRecord * 2;   // bytes of one head's records
         const __amdgpu_buffer_rsrc_t rth = make_rsrc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * kTriRecord, rec);
         const __amdgpu_buffer_rsrc_t rtl = make_rsrc(
@@ -663,7 +665,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         uint32_t voff_v[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * vo_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
+            voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * v_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
         constexpr int nl = 8 - (two_compute ? 2 : 1);
         constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + (kHasV ? 2 : 0) + 1;
         constexpr int NQ = outputs ? 16 : 0;
@@ -804,9 +806,9 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 const int lam = 16 * tile + lane - 32;
                 const int c = (64 * (lam & 1) < ncols) ? 64 * (lam & 1) : 0;
                 pf_row = lam >> 1;
-                pf_base = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.v) + bT * vo_row +
+                pf_base = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.v) + bT * v_row +
                                                                   h * ncols + c);
-                pf_stride = vo_row * 2;
+                pf_stride = v_row * 2;
             } else if (lane < 60) {
                 const int lam = (12 * tile + lane - 48) % 96;
                 const uint16_t* rec = static_cast<const uint16_t*>(lam < 48 ? a.ws.that : a.ws.pmat);
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 const bool ok = t < nvalid;
                 const uint32_t w0 = ok ? pk2(o[0], o[1]) : 0u, w1 = ok ? pk2(o[2], o[3]) : 0u;
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro,
-                                                      ooff + static_cast<uint32_t>(m) * vstep +
+                                                      ooff + static_cast<uint32_t>(m) * ostep +
                                                           static_cast<uint32_t>(16 * r * vo_row * 2),
                                                       0, 0);
             }

@@ -23,7 +23,7 @@ CHUNK = 64
 
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
-           "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
            "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d",
            "gdn_gated_rmsnorm",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
@@ -66,6 +66,7 @@ def lib():
         L.gdn_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_chunk_fwd_prologue.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                              vp, sz, vp]
+        L.gdn_chunk_fwd_prologue_qkv.argtypes = [pp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
         L.gdn_chunk_fwd_varlen_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
         L.gdn_chunk_fwd_varlen.argtypes = [pp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_chunk_bwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
@@ -76,7 +77,8 @@ def lib():
         L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd",
-                     "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_varlen_workspace", "gdn_chunk_fwd_varlen",
+                     "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
+                     "gdn_chunk_fwd_varlen",
                      "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d", "gdn_gated_rmsnorm",
                      "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state"):
             getattr(L, name).restype = ctypes.c_int
@@ -205,6 +207,39 @@ def gdn_chunk_fwd_prologue(q_raw, k_raw, v, a, b, A_log, dt_bias, q_scale=None, 
                                         _ptr(A_log), _ptr(dt_bias), ctypes.c_float(q_scale), _ptr(h0),
                                         _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_chunk_fwd_prologue")
+    return o, hT
+
+
+def gdn_chunk_fwd_prologue_qkv(qkv, Hqk, H, dk, dv, a, b, A_log, dt_bias, q_scale=None, h0=None,
+                               valid_len=None, o=None, hT=None, want_state=True, ws=None, stream=None):
+    """The fused-prologue forward reading q_raw, k_raw, v from one packed tensor qkv
+    [B, T, 2 Hqk dk + H dv] (bf16) without split copies. Returns (o, hT or None)."""
+    _dev(qkv, "qkv", torch.bfloat16)
+    for t_, n in ((a, "a"), (b, "b"), (A_log, "A_log"), (dt_bias, "dt_bias"), (h0, "h0")):
+        _dev(t_, n, torch.float32)
+    B, T, C = qkv.shape
+    if C != 2 * Hqk * dk + H * dv:
+        raise ValueError("qkv has %d channels, expected 2 Hqk dk + H dv = %d" % (C, 2 * Hqk * dk + H * dv))
+    vl = None
+    if valid_len is not None:
+        _dev(valid_len, "valid_len", torch.int32)
+        vl = valid_len.data_ptr()
+    p = GdnProblem(B, T, H, Hqk, dk, dv, CHUNK, GDN_BF16, vl)
+    if q_scale is None:
+        q_scale = dk ** -0.5
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=qkv.device)
+    _dev(o, "o", torch.bfloat16)
+    if hT is None and want_state:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=qkv.device)
+    _dev(hT, "hT", torch.float32)
+    need = gdn_chunk_fwd_workspace(p)
+    if ws is None:
+        ws = workspace(need, qkv.device)
+    _check(lib().gdn_chunk_fwd_prologue_qkv(ctypes.byref(p), _ptr(qkv), _ptr(a), _ptr(b), _ptr(A_log),
+                                            _ptr(dt_bias), ctypes.c_float(q_scale), _ptr(h0), _ptr(o), _ptr(hT),
+                                            _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_chunk_fwd_prologue_qkv")
     return o, hT
 
 
