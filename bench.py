@@ -337,7 +337,7 @@ def main():
                     help="skip the segmented-path and other-workload timings")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus,
+        print("bench.py: the library runs on one GPU; --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
