@@ -80,7 +80,7 @@ const char* gdn_last_error(void);
 
 /*
  * Kernel path a problem runs on (static string), or NULL for an invalid problem:
- *   "bf16-mfma" -- bf16 I/O with dk == 128 (and dv % 32 == 0): bf16 matrix-core
+ *   "bf16-mfma" -- bf16 I/O with dk == 128 (any dv of 16, 32, 64, 128): bf16 matrix-core
  *                  contractions with fp32 accumulation and an fp32 state;
  *   "f32-valu"  -- every other problem: fp32 arithmetic on the vector ALUs.
  */
