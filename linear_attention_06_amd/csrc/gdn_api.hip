@@ -141,6 +141,7 @@ gdn::StateArgs state_args(const gdn_problem& p, const Plan& pl, const void* q, c
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.ncols = p.dv;
     a.NT = static_cast<int>(pl.NT);
     a.P = 1; a.Lc = static_cast<int>(pl.NT);
+    a.pass = gdn::kPassOutputs;
     a.q = q; a.k = k; a.v = v; a.valid_len = p.valid_len; a.cu_seqlens = nullptr; a.ws = w;
     a.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
     a.v_stride = static_cast<int64_t>(p.H) * p.dv;
@@ -494,18 +495,21 @@ gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void
         if (S && M && use_mfma(*p) && p->dk == p->dv) {
             // both summaries in one pass: the M and S chains of a column tile share
             // every loaded operand
+            a.pass = gdn::kPassMS;
             a.init_mode = gdn::kInitZero;
             a.s_out = S;
             a.m_out = M;
             return run_state(*p, a, s);
         }
         if (S) {
+            a.pass = gdn::kPassS;
             a.init_mode = gdn::kInitZero;
             a.s_out = S;
             st = run_state(*p, a, s);
             if (st != GDN_OK) return st;
         }
         if (M) {
+            a.pass = gdn::kPassM;
             a.v = nullptr;
             a.ncols = p->dk;
             a.init_mode = gdn::kInitIdentity;

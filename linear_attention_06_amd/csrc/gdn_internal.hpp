@@ -47,6 +47,14 @@ __device__ __forceinline__ RowSpan row_span(const int32_t* cu, const int32_t* vl
 
 // How a state pass starts.
 enum InitMode : int { kInitZero = 0, kInitLoad = 1, kInitIdentity = 2 };
+// Which state pass to run. Stated by the caller, never inferred from NULL pointers: an
+// empty tensor's data pointer may be NULL.
+enum StatePass : int {
+    kPassOutputs = 0,   // values, token outputs (forward, apply)
+    kPassS = 1,         // values, no outputs (summary S)
+    kPassM = 2,         // no values, split operands (summary M)
+    kPassMS = 3         // M and S of each column tile in one pass
+};
 // Where a state pass leaves its final state.
 enum StoreMode : int { kStoreNone = 0, kStoreEverySegment = 1, kStoreLastSegment = 2 };
 
@@ -97,6 +105,7 @@ struct PrepArgs {
 struct StateArgs {
     int B, T, H, Hqk, dk, ncols, NT;  // ncols = dv, or dk for the M summary
     int P, Lc;                        // segments and chunks per segment (P = 1, Lc = NT: whole sequence)
+    int pass;                         // StatePass
     const void* q;
     const void* k;
     const void* v;                    // NULL: values are zero (M summary)

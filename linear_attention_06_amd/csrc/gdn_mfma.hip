@@ -1137,12 +1137,17 @@ hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
     int qk_groups = a.Hqk * a.B * a.P;
     const unsigned nblk = static_cast<unsigned>(((qk_groups + 7) / 8) * 8 * (a.H / a.Hqk) * tiles);
     void* args[] = {const_cast<StateArgs*>(&a), &tiles, &qk_groups};
-    // Without values (the summary matrix M) the pass runs with split operands; with
-    // values, no outputs and an M destination it computes M and S together.
-    const void* fn = !a.v      ? reinterpret_cast<const void*>(&state_mfma<false, true, false>)
-                   : a.o       ? reinterpret_cast<const void*>(&state_mfma<true, false, true>)
-                   : a.m_out   ? reinterpret_cast<const void*>(&state_mfma<true, true, false>)
-                               : reinterpret_cast<const void*>(&state_mfma<true, false, false>);
+    // The summary matrix M runs without values and with split operands; M and S together
+    // in one pass share the loads. The caller names the pass (an empty tensor's pointer
+    // may be NULL, so the pointers do not tell).
+    const void* fn = nullptr;
+    switch (a.pass) {
+        case kPassOutputs: fn = reinterpret_cast<const void*>(&state_mfma<true, false, true>); break;
+        case kPassS: fn = reinterpret_cast<const void*>(&state_mfma<true, false, false>); break;
+        case kPassM: fn = reinterpret_cast<const void*>(&state_mfma<false, true, false>); break;
+        case kPassMS: fn = reinterpret_cast<const void*>(&state_mfma<true, true, false>); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipLaunchKernel(fn, dim3(nblk), dim3(512), args, 0, s);
 }
 

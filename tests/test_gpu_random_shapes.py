@@ -1,0 +1,109 @@
+"""Seeded sweep of small random problems through the forward, the fused-prologue
+forward, the packed variable-length forward and the backward, each against the fp64
+oracle: batch, length (ragged tails, one-token and empty rows), head counts and ratio,
+head dims, dtype, padding and initial state drawn per case. The draw is fixed, so a
+failure names a reproducible case."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import backward, prologue
+from gpu_common import TOL_BF16, TOL_F32, dev, np_f64, sync, to_dev
+from helpers import rel_l2
+from linear_attention_06_amd import gdn
+from linear_attention_06_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def draw(seed):
+    r = np.random.default_rng(seed)
+    io = "bf16" if r.random() < 0.7 else "f32"
+    dk = 128 if (io == "bf16" and r.random() < 0.75) else int(r.choice([16, 32, 64, 128]))
+    dv = int(r.choice([16, 32, 64, 128]))
+    Hqk = int(r.choice([1, 2, 3]))
+    rep = int(r.choice([1, 2, 3]))
+    B = int(r.integers(1, 4))
+    T = int(r.choice([1, 63, 64, 65, 130, 191, 257]))
+    valid = int(r.integers(0, T + 1)) if r.random() < 0.4 else None
+    h0 = "normal" if r.random() < 0.6 else None
+    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="rand%d" % seed, B=B, T=T, Hqk=Hqk, H=Hqk * rep,
+                            dk=dk, dv=dv, io=io, h0=h0, seed=1000 + seed, valid_len=valid)
+    return w
+
+
+SEEDS = list(range(40))
+
+
+def check(x, ref, tol, what):
+    err = rel_l2(np_f64(x), ref)
+    assert np.all(np.isfinite(np_f64(x))), what
+    assert err <= tol, "%s rel-L2 %.3e > %.0e" % (what, err, tol)
+    return err
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_forward_and_backward(seed):
+    w = draw(seed)
+    inp = make_inputs(w)
+    if inp.valid_len is not None and w.B > 1:
+        inp.valid_len[-1] = max(0, inp.valid_len[-1] // 2)   # rows of different lengths
+    tol = TOL_BF16 if w.io == "bf16" else TOL_F32
+    print("case", seed, w)
+    q, k, v, g, beta, h0, vl = to_dev(inp)
+    qf, kf, vf, gf, bf, h0f = inp.f64()
+    # forward
+    o, hT = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, vl)
+    sync()
+    o_ref, hT_ref = oracle.gdn_fwd(qf, kf, vf, gf, bf, h0f, valid_len=inp.valid_len)
+    check(o, o_ref, tol, "o")
+    check(hT, hT_ref, tol, "hT")
+    # backward (fp32 arithmetic: the fp32 tolerance whatever the input dtype)
+    rng = np.random.default_rng(seed)
+    d_o = rng.standard_normal(v.shape).astype(np.float32)
+    if w.io == "bf16":
+        from linear_attention_06_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits
+        bits = f32_to_bf16_bits(d_o)
+        d_o = bf16_bits_to_f32(bits)
+        d_o_t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev())
+    else:
+        d_o_t = torch.from_numpy(d_o).to(dev())
+    got = gdn.gdn_chunk_bwd(q, k, v, g, beta, h0, d_o_t, None, vl)
+    sync()
+    ref = backward.gdn_bwd(qf, kf, vf, gf, bf, h0f, d_o.astype(np.float64), None, inp.valid_len)
+    for nm, x, r_ in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, ref):
+        if h0f is None and nm == "dh0":
+            continue
+        check(x, r_, TOL_F32, nm)
+    # packed variable-length sequences: each row's valid tokens back to back
+    lens = [int(inp.valid_len[b]) if inp.valid_len is not None else w.T for b in range(w.B)]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pk = lambda x: torch.cat([x[b:b + 1, :lens[b]] for b in range(w.B)], dim=1).contiguous()
+    ov, hTv = gdn.gdn_chunk_fwd_varlen(pk(q), pk(k), pk(v), pk(g), pk(beta),
+                                       torch.from_numpy(cu).to(dev()), max(max(lens), 1), h0)
+    sync()
+    for b in range(w.B):
+        assert torch.equal(ov[0, cu[b]:cu[b + 1]], o[b, :lens[b]]), ("varlen row", b)
+    assert torch.equal(hTv, hT)
+
+
+@pytest.mark.parametrize("seed", SEEDS[:16])
+def test_random_fused_prologue(seed):
+    w = draw(seed)
+    w = dataclasses.replace(w, io="bf16", dk=128)   # the prologue runs on the matrix-core path
+    inp = make_inputs(w)
+    r = inp.raw
+    d = dev()
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.int16).view(torch.bfloat16).to(d)
+    f = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(d)
+    o, hT = gdn.gdn_chunk_fwd_prologue(bf(r["q_raw"]), bf(r["k_raw"]), bf(inp.v), f(r["a"]), f(r["b"]),
+                                       f(r["A_log"]), f(r["dt_bias"]), w.dk ** -0.5, f(inp.h0), f(inp.valid_len))
+    sync()
+    qr, kr, v64, a, b, A_log, dt_bias, h064 = inp.raw_f64()
+    o_ref, hT_ref = prologue.gdn_fwd_prologue(qr, kr, v64, a, b, A_log, dt_bias, w.dk ** -0.5, h064,
+                                              inp.valid_len)
+    check(o, o_ref, TOL_BF16, "prologue o")
+    check(hT, hT_ref, TOL_BF16, "prologue hT")

@@ -77,13 +77,20 @@ def test_varlen_padded_8k_packed_equals_the_padded_run():
     assert torch.equal(hT, hT_pad)
 
 
-def test_varlen_all_empty_sequences_return_initial_states():
-    d = 128
-    q = torch.zeros((1, 0, 2, d), dtype=torch.bfloat16, device=dev())
-    v = torch.zeros((1, 0, 4, d), dtype=torch.bfloat16, device=dev())
+@pytest.mark.parametrize("max_seqlen", [0, 1, 64, 100])
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 32)])
+def test_varlen_all_empty_sequences_return_initial_states(max_seqlen, dtype, d):
+    """No tokens at all: every tensor is empty (its data pointer NULL) while max_seqlen may
+    still size one or more chunk records; each sequence returns its initial state. (A state
+    pass chosen from the NULL value pointer once read the summary-only records here.)"""
+    q = torch.zeros((1, 0, 2, d), dtype=dtype, device=dev())
+    v = torch.zeros((1, 0, 4, d), dtype=dtype, device=dev())
     g = torch.zeros((1, 0, 4), dtype=torch.float32, device=dev())
     h0 = torch.randn((3, 4, d, d), device=dev())
     cu = torch.zeros(4, dtype=torch.int32, device=dev())
-    o, hT = gdn.gdn_chunk_fwd_varlen(q, q, v, g, g, cu, 0, h0)
+    o, hT = gdn.gdn_chunk_fwd_varlen(q, q, v, g, g, cu, max_seqlen, h0)
     sync()
     assert torch.equal(hT, h0)
+    _, hT0 = gdn.gdn_chunk_fwd_varlen(q, q, v, g, g, cu, max_seqlen, None)
+    sync()
+    assert int(torch.count_nonzero(hT0)) == 0
