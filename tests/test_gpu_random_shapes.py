@@ -107,3 +107,53 @@ def test_random_fused_prologue(seed):
                                               inp.valid_len)
     check(o, o_ref, TOL_BF16, "prologue o")
     check(hT, hT_ref, TOL_BF16, "prologue hT")
+
+
+def draw_segments(seed):
+    r = np.random.default_rng(5000 + seed)
+    io = "bf16" if r.random() < 0.7 else "f32"
+    dk = 128 if (io == "bf16" and r.random() < 0.75) else int(r.choice([16, 32, 64, 128]))
+    dv = dk if r.random() < 0.6 else int(r.choice([16, 32, 64, 128]))
+    Hqk = int(r.choice([1, 2]))
+    rep = int(r.choice([1, 2, 3]))
+    seg = int(r.choice([64, 128, 192]))
+    P = int(r.integers(1, 4))
+    B = int(r.integers(1, 3))
+    T = seg * P
+    valid = int(r.integers(0, T + 1)) if r.random() < 0.4 else None
+    h0 = "normal" if r.random() < 0.6 else None
+    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="rseg%d" % seed, B=B, T=T, Hqk=Hqk, H=Hqk * rep,
+                            dk=dk, dv=dv, io=io, h0=h0, seed=2000 + seed, valid_len=valid, seg_len=seg)
+    return w
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_random_segments(seed):
+    """Summary (M and S), combine and apply on random shapes against the oracle, and the
+    segmented outputs against the unsplit forward."""
+    w = draw_segments(seed)
+    inp = make_inputs(w)
+    print("case", seed, w)
+    tol = TOL_BF16 if w.io == "bf16" else TOL_F32
+    q, k, v, g, beta, h0, vl = to_dev(inp)
+    qf, kf, vf, gf, bf, h0f = inp.f64()
+    M, S, ws = gdn.gdn_segment_summary(q, k, v, g, beta, w.seg_len, valid_len=vl)
+    H_in, Mp, hT_c = gdn.gdn_summary_combine(M, S, h0, want_prefix=True)
+    o, hT = gdn.gdn_apply_initial_state(q, k, v, g, beta, H_in, w.seg_len, ws, valid_len=vl)
+    sync()
+    M_ref, S_ref = oracle.gdn_segment_summary(qf, kf, vf, gf, bf, w.seg_len, valid_len=inp.valid_len)
+    # M is a product of decays e^{sum g} over the segment; blocks whose exact value lies below
+    # fp32's range (|M| < 1e-30, e.g. a log-decay sum of -150 gives ~1e-65) are zero in the
+    # fp32 result. Compare the blocks inside the range; bound the others in absolute terms.
+    Mg = np_f64(M).reshape(M.shape[0], M.shape[1], M.shape[2], -1)
+    Mr = M_ref.reshape(Mg.shape)
+    live = np.linalg.norm(Mr, axis=-1) >= 1e-30
+    if live.any():
+        err = rel_l2(Mg[live], Mr[live])
+        assert err <= tol, "M rel-L2 %.3e > %.0e over %d blocks" % (err, tol, int(live.sum()))
+    assert np.all(np.abs(Mg[~live]) <= 1e-30), "M outside the fp32 range is not ~0"
+    check(S, S_ref, tol, "S")
+    o_ref, hT_ref = oracle.gdn_fwd(qf, kf, vf, gf, bf, h0f, valid_len=inp.valid_len)
+    check(o, o_ref, tol, "segmented o")
+    check(hT, hT_ref, tol, "segmented hT")
+    check(hT_c, hT_ref, tol, "combined hT")
