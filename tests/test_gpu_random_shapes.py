@@ -157,3 +157,54 @@ def test_random_segments(seed):
     check(o, o_ref, tol, "segmented o")
     check(hT, hT_ref, tol, "segmented hT")
     check(hT_c, hT_ref, tol, "combined hT")
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_random_layer_steps(seed):
+    """Conv1D (random K, halo, bias, SiLU, dtype, C, T, B) and gated RMSNorm (random rows,
+    D, dtype, eps) against their oracles."""
+    from oracle import layer_ops
+    r = np.random.default_rng(7000 + seed)
+    io = "bf16" if r.random() < 0.6 else "f32"
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    tol = TOL_BF16 if io == "bf16" else 1e-5
+    B, T, C, K = int(r.integers(1, 4)), int(r.choice([1, 3, 63, 64, 65, 200])), 8 * int(r.integers(1, 70)), \
+        int(r.choice([2, 3, 4]))
+    x = torch.from_numpy(r.standard_normal((B, T, C)).astype(np.float32)).to(dev()).to(tdt)
+    w = torch.from_numpy((0.5 * r.standard_normal((C, K))).astype(np.float32)).to(dev())
+    bias = torch.from_numpy(r.standard_normal(C).astype(np.float32)).to(dev()) if r.random() < 0.5 else None
+    prev = torch.from_numpy(r.standard_normal((B, K - 1, C)).astype(np.float32)).to(dev()).to(tdt) \
+        if r.random() < 0.5 else None
+    silu = bool(r.random() < 0.7)
+    y = gdn.gdn_causal_conv1d(x, w, bias, prev, silu=silu)
+    sync()
+    ref = layer_ops.causal_conv1d(np_f64(x), np_f64(w), None if bias is None else np_f64(bias),
+                                  None if prev is None else np_f64(prev), silu)
+    check(y, ref, tol, "conv1d B=%d T=%d C=%d K=%d" % (B, T, C, K))
+    rows, D = int(r.integers(1, 3000)), int(r.choice([16, 32, 64, 128]))
+    eps = float(r.choice([0.0, 1e-6, 1e-2]))
+    o = torch.from_numpy(r.standard_normal((rows, D)).astype(np.float32)).to(dev()).to(tdt)
+    z = torch.from_numpy(r.standard_normal((rows, D)).astype(np.float32)).to(dev()).to(tdt)
+    wt = torch.from_numpy(r.standard_normal(D).astype(np.float32)).to(dev())
+    yn = gdn.gdn_gated_rmsnorm(o, z, wt, eps=eps)
+    sync()
+    check(yn, layer_ops.gated_rmsnorm(np_f64(o), np_f64(z), np_f64(wt), eps), tol, "norm rows=%d D=%d" % (rows, D))
+
+
+def test_empty_inputs_of_the_combine_and_backward():
+    """No segments: the combine returns the initial state; no tokens: the backward returns
+    the final-state gradient as dh0 and empty token gradients."""
+    d = 128
+    h0 = torch.randn((2, 4, d, d), device=dev())
+    M = torch.zeros((2, 4, 0, d, d), device=dev())
+    S = torch.zeros((2, 4, 0, d, d), device=dev())
+    H_in, _, hT = gdn.gdn_summary_combine(M, S, h0)
+    sync()
+    assert H_in.numel() == 0 and torch.equal(hT, h0)
+    q = torch.zeros((2, 0, 2, d), dtype=torch.bfloat16, device=dev())
+    v = torch.zeros((2, 0, 4, d), dtype=torch.bfloat16, device=dev())
+    g = torch.zeros((2, 0, 4), device=dev())
+    dhT = torch.randn((2, 4, d, d), device=dev())
+    dq, dk, dv, dg, db, dh0 = gdn.gdn_chunk_bwd(q, q, v, g, g, h0, v, dhT)
+    sync()
+    assert dq.numel() == 0 and torch.equal(dh0, dhT)
