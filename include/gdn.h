@@ -179,8 +179,8 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
  *   dh0 [B, H, dk, dv] fp32 when non-NULL (the gradient of h0; h0 NULL = zero state).
  * Padded tokens (valid_len) get zero gradients. Every head dim and dtype of the forward;
  * the arithmetic is fp32 on the vector ALUs, token by token, with the forward state
- * recomputed from checkpoints every 64 tokens. ws must be 256-byte aligned and at least
- * gdn_chunk_bwd_workspace() bytes (B H ceil(T/64) dk dv + B T H (dv/16) 2 (dk + 1) fp32).
+ * recomputed from checkpoints every 8 tokens. ws must be 256-byte aligned and at least
+ * gdn_chunk_bwd_workspace() bytes (8 B H ceil(T/64) dk dv + B T H (dv/16) 2 (dk + 1) fp32).
  */
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);
 gdn_status gdn_chunk_bwd(const gdn_problem* p,

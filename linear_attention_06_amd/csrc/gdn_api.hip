@@ -297,8 +297,8 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
     }
 }
 
-// Backward workspace: chunk-start states, then the per-column-tile partials of dq, dk
-// and of dg, dbeta.
+// Backward workspace: the states before every 8th token, then the per-column-tile
+// partials of dq, dk and of dg, dbeta.
 struct BwdPlan {
     int64_t NT = 0;
     size_t ckpt_off = 0, dqk_off = 0, dgb_off = 0, bytes = 0;
@@ -309,7 +309,7 @@ BwdPlan make_bwd_plan(const gdn_problem& p) {
     pl.NT = (static_cast<int64_t>(p.T) + gdn::kChunk - 1) / gdn::kChunk;
     const size_t bt = static_cast<size_t>(p.B) * p.T, tiles = static_cast<size_t>(p.dv / 16);
     pl.ckpt_off = 0;
-    pl.dqk_off = align256(static_cast<size_t>(p.B) * p.H * pl.NT * p.dk * p.dv * sizeof(float));
+    pl.dqk_off = align256(static_cast<size_t>(p.B) * p.H * 8 * pl.NT * p.dk * p.dv * sizeof(float));
     pl.dgb_off = pl.dqk_off + align256(bt * p.H * tiles * 2 * p.dk * sizeof(float));
     pl.bytes = pl.dgb_off + align256(bt * p.H * tiles * 2 * sizeof(float));
     return pl;

@@ -22,10 +22,10 @@
 // SIMDs run two waves of a block and each thread's share of the token chain halves:
 // 12.5 against 15.1 ms at H = 32, d = 128, 8K tokens; 64 threads per column were slower
 // again (15.9 ms).
-//   bwd_ckpt    the forward state at every chunk start (64 tokens) into the workspace;
-//   bwd_sweep   chunks in reverse: the chunk's states are recomputed from its
-//               checkpoint, with a second checkpoint every 8 tokens in LDS, and each
-//               8-token piece is recomputed into registers and run backwards; dv and
+//   bwd_ckpt    the forward state before every 8th token into the workspace;
+//   bwd_sweep   chunks in reverse, 8-token pieces in reverse: each piece's states are
+//               recomputed into registers from its checkpoint (loaded one piece ahead)
+//               and the piece is run backwards; dv and
 //               dh0 are complete per tile, dq, dk, dg and dbeta are written as one
 //               partial per column tile;
 //   bwd_reduce  sums the partials over the column tiles and over the value heads that
@@ -138,13 +138,17 @@ __global__ __launch_bounds__(16 * TPC) void bwd_ckpt(BwdArgs a) {
     for (int j = 0; j < RJ; ++j)
         S[j] = a.h0 ? a.h0[(bh * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
     for (int n = 0; n < a.NT; ++n) {
-        float* ck = a.ckpt + (bh * a.NT + n) * DK * a.dv;
-#pragma unroll
-        for (int j = 0; j < RJ; ++j) ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c] = S[j];
         __syncthreads();
         load_chunk<IO, DK, false, NTH>(L, a, rs, h, hq, col0, n, tid);
         __syncthreads();
-        for (int u = 0; u < 64; ++u) fwd_step<RJ, TPC>(S, L, u, i, c);
+        for (int u = 0; u < 64; ++u) {
+            if ((u & 7) == 0) {   // the state before every 8th token
+                float* ck = a.ckpt + (bh * 8 * a.NT + 8 * n + (u >> 3)) * DK * a.dv;
+#pragma unroll
+                for (int j = 0; j < RJ; ++j) ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c] = S[j];
+            }
+            fwd_step<RJ, TPC>(S, L, u, i, c);
+        }
     }
 }
 
@@ -152,7 +156,6 @@ template <typename IO, int DK, int TPC>
 __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     constexpr int RJ = DK / TPC, NTH = 16 * TPC;
     __shared__ ChunkLds<IO, DK, true> L;
-    __shared__ float sub_s[8][RJ][NTH];        // state every 8 tokens of the chunk
     __shared__ float red_s[2][16][DK];         // per-column terms of dq and dk
     __shared__ float red2_s[2][16];            // per-column terms of dg and dbeta
     const int tiles = a.dv / 16;
@@ -167,27 +170,25 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     for (int j = 0; j < RJ; ++j)
         dS[j] = a.dhT ? a.dhT[(bh * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
 
+    // the checkpoint of 8-token piece m (the state before token 8 m), loaded one piece ahead
+    const auto load_ck = [&](int m, float (&x)[RJ]) {
+        const float* ck = a.ckpt + (bh * 8 * a.NT + m) * DK * a.dv;
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) x[j] = ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c];
+    };
+    float nxt[RJ];
+    if (a.NT > 0) load_ck(8 * a.NT - 1, nxt);
+
     for (int n = a.NT - 1; n >= 0; --n) {
         __syncthreads();
         load_chunk<IO, DK, true, NTH>(L, a, rs, h, hq, col0, n, tid);
-        float S[RJ];
-        const float* ck = a.ckpt + (bh * a.NT + n) * DK * a.dv;
-#pragma unroll
-        for (int j = 0; j < RJ; ++j) S[j] = ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c];
         __syncthreads();
-        // forward through the chunk, keeping the state before every 8th token
-        for (int u = 0; u < 64; ++u) {
-            if ((u & 7) == 0) {
-#pragma unroll
-                for (int j = 0; j < RJ; ++j) sub_s[u >> 3][j][tid] = S[j];
-            }
-            fwd_step<RJ, TPC>(S, L, u, i, c);
-        }
         for (int s = 7; s >= 0; --s) {
             // the piece's states in registers: St[u] before token 8 s + u, St[u + 1] after it
             float St[9][RJ], w[8];
 #pragma unroll
-            for (int j = 0; j < RJ; ++j) St[0][j] = sub_s[s][j][tid];
+            for (int j = 0; j < RJ; ++j) St[0][j] = nxt[j];
+            if (8 * n + s > 0) load_ck(8 * n + s - 1, nxt);
 #pragma unroll
             for (int uu = 0; uu < 8; ++uu) {
 #pragma unroll

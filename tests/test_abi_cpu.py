@@ -194,8 +194,8 @@ def test_backward_argument_checks():
     p = P()
     n = ctypes.c_size_t(0)
     assert L.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)) == gdn.GDN_OK
-    # checkpoints B H ceil(T/64) dk dv and per-tile partials B T H (dv/16) 2 (dk + 1), fp32
-    assert n.value >= 4 * (1 * 8 * 2 * 16 * 16 + 1 * 128 * 8 * 1 * 2 * (16 + 1))
+    # checkpoints 8 B H ceil(T/64) dk dv and per-tile partials B T H (dv/16) 2 (dk + 1), fp32
+    assert n.value >= 4 * (8 * 1 * 8 * 2 * 16 * 16 + 1 * 128 * 8 * 1 * 2 * (16 + 1))
     vp = ctypes.c_void_p
     args = [vp(1)] * 5 + [None, vp(1), None] + [vp(1)] * 5 + [None]
     bad = list(args)
