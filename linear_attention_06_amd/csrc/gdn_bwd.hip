@@ -27,7 +27,8 @@
 //               recomputed into registers from its checkpoint (loaded one piece ahead)
 //               and the piece is run backwards; dv and
 //               dh0 are complete per tile, dq, dk, dg and dbeta are written as one
-//               partial per column tile;
+//               partial per column tile, their column sums taken through LDS once per
+//               pair of tokens (one barrier per pair);
 //   bwd_reduce  sums the partials over the column tiles and over the value heads that
 //               share a query/key head.
 // Tokens at or past valid_len[b] are identities of the recurrence (beta = g = 0) with
@@ -156,8 +157,11 @@ template <typename IO, int DK, int TPC>
 __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     constexpr int RJ = DK / TPC, NTH = 16 * TPC;
     __shared__ ChunkLds<IO, DK, true> L;
-    __shared__ float red_s[2][16][DK];         // per-column terms of dq and dk
-    __shared__ float red2_s[2][16];            // per-column terms of dg and dbeta
+    // per-column terms of dq and dk, of dg and dbeta, for four tokens in turn: a barrier
+    // after every second token, then the block sums that pair's terms; a pair's reads end
+    // before the next barrier, which every thread passes before the next pair writes
+    __shared__ float red_s[4][2][16][DK];
+    __shared__ float red2_s[4][2][16];
     const int tiles = a.dv / 16;
     const int tile = blockIdx.x, col0 = 16 * tile, h = blockIdx.y, b = blockIdx.z;
     const int hq = h / (a.H / a.Hqk);
@@ -217,31 +221,38 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
 #pragma unroll
                 for (int j = 0; j < RJ; ++j) {
                     const int r = i + TPC * j;
-                    red_s[0][c][r] = St[uu + 1][j] * doc;
-                    red_s[1][c][r] = M[j] * (bt * vc - eg * bt * w[uu]) - eg * bt * St[uu][j] * z;
+                    red_s[uu & 3][0][c][r] = St[uu + 1][j] * doc;
+                    red_s[uu & 3][1][c][r] = M[j] * (bt * vc - eg * bt * w[uu]) - eg * bt * St[uu][j] * z;
                 }
                 if (i == 0) {
-                    red2_s[0][c] = valid ? eg * (ms - bt * z * w[uu]) : 0.f;
-                    red2_s[1][c] = valid ? z * (vc - eg * w[uu]) : 0.f;
+                    red2_s[uu & 3][0][c] = valid ? eg * (ms - bt * z * w[uu]) : 0.f;
+                    red2_s[uu & 3][1][c] = valid ? z * (vc - eg * w[uu]) : 0.f;
                 }
-                __syncthreads();
-                {
-                    float* part = a.dqk_part + ((tokrow * a.H + h) * tiles + tile) * 2 * DK;
-                    if (inrow && tid < 2 * DK) {
-                        const int which = tid / DK, r = tid % DK;
-                        float acc = 0.f;
+                if ((uu & 1) == 0) {
+                    // the pair of tokens u + 1 (slot p = 0) and u (p = 1)
+                    __syncthreads();
+                    for (int e = tid; e < 4 * DK; e += NTH) {
+                        const int p = e / (2 * DK), which = (e / DK) & 1, r = e % DK;
+                        const int64_t tp = t + 1 - p;
+                        if (tp < rs.extent) {
+                            float acc = 0.f;
 #pragma unroll
-                        for (int cc = 0; cc < 16; ++cc) acc += red_s[which][cc][r];
-                        part[tid] = valid ? acc : 0.f;
+                            for (int cc = 0; cc < 16; ++cc) acc += red_s[(uu + 1 - p) & 3][which][cc][r];
+                            a.dqk_part[(((rs.start + tp) * a.H + h) * tiles + tile) * 2 * DK + which * DK + r] =
+                                tp < rs.valid ? acc : 0.f;
+                        }
                     }
-                    if (inrow && tid < 2) {
-                        float acc = 0.f;
+                    if (tid < 4) {
+                        const int p = tid / 2, which = tid & 1;
+                        const int64_t tp = t + 1 - p;
+                        if (tp < rs.extent) {
+                            float acc = 0.f;
 #pragma unroll
-                        for (int cc = 0; cc < 16; ++cc) acc += red2_s[tid][cc];
-                        a.dgb_part[((tokrow * a.H + h) * tiles + tile) * 2 + tid] = acc;
+                            for (int cc = 0; cc < 16; ++cc) acc += red2_s[(uu + 1 - p) & 3][which][cc];
+                            a.dgb_part[(((rs.start + tp) * a.H + h) * tiles + tile) * 2 + which] = acc;
+                        }
                     }
                 }
-                __syncthreads();
 #pragma unroll
                 for (int j = 0; j < RJ; ++j) dS[j] = eg * (M[j] - bt * L.k[u][i + TPC * j] * z);
             }
