@@ -65,47 +65,82 @@ __device__ __forceinline__ float col_sum(float x) {
 }
 
 // Chunk operands in LDS (fp32): K, optionally Q, the tile's columns of V and of the
-// output gradient, g and beta; padded tokens read as zero.
+// output gradient, e^g and beta; padded tokens read as zero (e^g as one).
 template <typename IO, int DK, bool kQ>
 struct ChunkLds {
     float k[64][DK];
     float q[kQ ? 64 : 1][DK];
     float v[64][16];
     float d[kQ ? 64 : 1][16];
-    float g[64];
+    float eg[64];      // e^{g}
     float beta[64];
 };
 
+// A chunk's operands in flight: every thread issues all its loads at once (addresses of
+// padded tokens clamped to the row's token 0, which exists whenever the row has a chunk;
+// their values are replaced by zero when stored), so one chunk can be fetched while the
+// previous one is processed.
 template <typename IO, int DK, bool kQ, int NTH>
-__device__ __forceinline__ void load_chunk(ChunkLds<IO, DK, kQ>& L, const BwdArgs& a, const RowSpan& rs, int h,
-                                           int hq, int col0, int n, int tid) {
+struct ChunkRegs {
+    static constexpr int EK = 64 * DK / NTH, EV = 64 * 16 / NTH;
+    static_assert(EK * NTH == 64 * DK && EV * NTH == 64 * 16, "chunk tiles must split evenly");
+    float k[EK], q[kQ ? EK : 1], v[EV], d[kQ ? EV : 1], g, beta;
+};
+
+template <typename IO, int DK, bool kQ, int NTH>
+__device__ __forceinline__ void fetch_chunk(ChunkRegs<IO, DK, kQ, NTH>& R, const BwdArgs& a, const RowSpan& rs, int h,
+                                            int hq, int col0, int n, int tid) {
+    using CR = ChunkRegs<IO, DK, kQ, NTH>;
     const IO* k = static_cast<const IO*>(a.k);
     const IO* q = static_cast<const IO*>(a.q);
     const IO* v = static_cast<const IO*>(a.v);
     const IO* d = static_cast<const IO*>(a.d_o);
     const int64_t t0 = static_cast<int64_t>(n) * kChunk;
-    for (int e = tid; e < 64 * DK; e += NTH) {
-        const int r = e / DK, x = e % DK;
-        const int64_t tok = t0 + r;
-        const bool ok = tok < rs.valid;
+#pragma unroll
+    for (int m = 0; m < CR::EK; ++m) {
+        const int e = tid + NTH * m, r = e / DK, x = e % DK;
+        const int64_t tok = t0 + r < rs.valid ? t0 + r : 0;
         const int64_t idx = ((rs.start + tok) * a.Hqk + hq) * DK + x;
-        L.k[r][x] = ok ? ld_in(k, idx) : 0.f;
-        if (kQ) L.q[r][x] = ok ? ld_in(q, idx) : 0.f;
+        R.k[m] = ld_in(k, idx);
+        if (kQ) R.q[m] = ld_in(q, idx);
     }
-    for (int e = tid; e < 64 * 16; e += NTH) {
-        const int r = e / 16, c = e % 16;
-        const int64_t tok = t0 + r;
-        const bool ok = tok < rs.valid;
+#pragma unroll
+    for (int m = 0; m < CR::EV; ++m) {
+        const int e = tid + NTH * m, r = e / 16, c = e % 16;
+        const int64_t tok = t0 + r < rs.valid ? t0 + r : 0;
         const int64_t idx = ((rs.start + tok) * a.H + h) * a.dv + col0 + c;
-        L.v[r][c] = ok ? ld_in(v, idx) : 0.f;
-        if (kQ) L.d[r][c] = ok ? ld_in(d, idx) : 0.f;
+        R.v[m] = ld_in(v, idx);
+        if (kQ) R.d[m] = ld_in(d, idx);
+    }
+    const int64_t tok = t0 + (tid & 63) < rs.valid ? t0 + (tid & 63) : 0;
+    const int64_t gi = (rs.start + tok) * a.H + h;
+    R.g = a.g[gi];
+    R.beta = a.beta[gi];
+}
+
+template <typename IO, int DK, bool kQ, int NTH>
+__device__ __forceinline__ void store_chunk(ChunkLds<IO, DK, kQ>& L, const ChunkRegs<IO, DK, kQ, NTH>& R,
+                                            const RowSpan& rs, int n, int tid) {
+    using CR = ChunkRegs<IO, DK, kQ, NTH>;
+    const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+#pragma unroll
+    for (int m = 0; m < CR::EK; ++m) {
+        const int e = tid + NTH * m, r = e / DK, x = e % DK;
+        const bool ok = t0 + r < rs.valid;
+        L.k[r][x] = ok ? R.k[m] : 0.f;
+        if (kQ) L.q[r][x] = ok ? R.q[m] : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < CR::EV; ++m) {
+        const int e = tid + NTH * m, r = e / 16, c = e % 16;
+        const bool ok = t0 + r < rs.valid;
+        L.v[r][c] = ok ? R.v[m] : 0.f;
+        if (kQ) L.d[r][c] = ok ? R.d[m] : 0.f;
     }
     if (tid < 64) {
-        const int64_t tok = t0 + tid;
-        const bool ok = tok < rs.valid;
-        const int64_t gi = (rs.start + tok) * a.H + h;
-        L.g[tid] = ok ? a.g[gi] : 0.f;
-        L.beta[tid] = ok ? a.beta[gi] : 0.f;
+        const bool ok = t0 + tid < rs.valid;
+        L.eg[tid] = ok ? expf(R.g) : 1.f;
+        L.beta[tid] = ok ? R.beta : 0.f;
     }
 }
 
@@ -116,12 +151,10 @@ __device__ __forceinline__ float fwd_step(float (&S)[RJ], const Lds& L, int u, i
 #pragma unroll
     for (int j = 0; j < RJ; ++j) w += L.k[u][i + TPC * j] * S[j];
     w = col_sum<TPC>(w);
-    const float eg = expf(L.g[u]), bt = L.beta[u], vc = L.v[u][c];
+    // e^g (S - beta k w^T) + beta k v^T = e^g S + k (beta (v - e^g w))^T
+    const float eg = L.eg[u], ac = L.beta[u] * (L.v[u][c] - eg * w);
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-        const float kr = L.k[u][i + TPC * j];
-        S[j] = eg * (S[j] - bt * kr * w) + bt * kr * vc;
-    }
+    for (int j = 0; j < RJ; ++j) S[j] = fmaf(L.k[u][i + TPC * j], ac, eg * S[j]);
     return w;
 }
 
@@ -138,10 +171,13 @@ __global__ __launch_bounds__(16 * TPC) void bwd_ckpt(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < RJ; ++j)
         S[j] = a.h0 ? a.h0[(bh * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
+    ChunkRegs<IO, DK, false, NTH> R;
+    if (a.NT > 0) fetch_chunk(R, a, rs, h, hq, col0, 0, tid);
     for (int n = 0; n < a.NT; ++n) {
         __syncthreads();
-        load_chunk<IO, DK, false, NTH>(L, a, rs, h, hq, col0, n, tid);
+        store_chunk(L, R, rs, n, tid);
         __syncthreads();
+        if (n + 1 < a.NT) fetch_chunk(R, a, rs, h, hq, col0, n + 1, tid);
         for (int u = 0; u < 64; ++u) {
             if ((u & 7) == 0) {   // the state before every 8th token
                 float* ck = a.ckpt + (bh * 8 * a.NT + 8 * n + (u >> 3)) * DK * a.dv;
@@ -183,10 +219,13 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     float nxt[RJ];
     if (a.NT > 0) load_ck(8 * a.NT - 1, nxt);
 
+    ChunkRegs<IO, DK, true, NTH> R;
+    if (a.NT > 0) fetch_chunk(R, a, rs, h, hq, col0, a.NT - 1, tid);
     for (int n = a.NT - 1; n >= 0; --n) {
         __syncthreads();
-        load_chunk<IO, DK, true, NTH>(L, a, rs, h, hq, col0, n, tid);
+        store_chunk(L, R, rs, n, tid);
         __syncthreads();
+        if (n > 0) fetch_chunk(R, a, rs, h, hq, col0, n - 1, tid);
         for (int s = 7; s >= 0; --s) {
             // the piece's states in registers: St[u] before token 8 s + u, St[u + 1] after it
             float St[9][RJ], w[8];
@@ -204,7 +243,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                 const int u = 8 * s + uu;
                 const int64_t t = static_cast<int64_t>(n) * kChunk + u;
                 const bool valid = t < rs.valid;
-                const float eg = expf(L.g[u]), bt = L.beta[u], vc = L.v[u][c], doc = L.d[u][c];
+                const float eg = L.eg[u], bt = L.beta[u], vc = L.v[u][c], doc = L.d[u][c];
                 float M[RJ];
                 float z = 0.f, ms = 0.f;
 #pragma unroll
@@ -218,11 +257,13 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                 const bool inrow = t < rs.extent;      // the tail of the last chunk is past the row
                 const int64_t tokrow = rs.start + t;
                 if (i == 0 && inrow) a.dv_out[(tokrow * a.H + h) * a.dv + col0 + c] = valid ? bt * z : 0.f;
+                // dk's column terms: M beta (v - e^g w) - e^g beta z S_{t-1}
+                const float am = bt * (vc - eg * w[uu]), bz = eg * bt * z;
 #pragma unroll
                 for (int j = 0; j < RJ; ++j) {
                     const int r = i + TPC * j;
                     red_s[uu & 3][0][c][r] = St[uu + 1][j] * doc;
-                    red_s[uu & 3][1][c][r] = M[j] * (bt * vc - eg * bt * w[uu]) - eg * bt * St[uu][j] * z;
+                    red_s[uu & 3][1][c][r] = fmaf(M[j], am, -bz * St[uu][j]);
                 }
                 if (i == 0) {
                     red2_s[uu & 3][0][c] = valid ? eg * (ms - bt * z * w[uu]) : 0.f;
@@ -254,7 +295,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                     }
                 }
 #pragma unroll
-                for (int j = 0; j < RJ; ++j) dS[j] = eg * (M[j] - bt * L.k[u][i + TPC * j] * z);
+                for (int j = 0; j < RJ; ++j) dS[j] = fmaf(-bz, L.k[u][i + TPC * j], eg * M[j]);
             }
         }
     }
