@@ -18,19 +18,24 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-// 8 values per lane: bf16 (16 bytes) or fp32 (32 bytes).
+// 8 values per lane: bf16 (16 bytes) or fp32 (32 bytes). fetch() issues the load and
+// unpack() widens it where it is used, so a load can stay in flight across iterations.
 template <typename IO>
 struct Vec8;
 template <>
 struct Vec8<uint16_t> {
-    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+    struct Raw {
+        u32x4 u;
+    };
+    static __device__ __forceinline__ Raw fetch(const uint16_t* p) { return Raw{*reinterpret_cast<const u32x4*>(p)}; }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&x)[8]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(u[e] << 16);
-            x[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+            x[2 * e] = __uint_as_float(r.u[e] << 16);
+            x[2 * e + 1] = __uint_as_float(r.u[e] & 0xFFFF0000u);
         }
     }
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) { unpack(fetch(p), x); }
     static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[8]) {
         u32x4 u;
 #pragma unroll
@@ -44,14 +49,20 @@ struct Vec8<uint16_t> {
 };
 template <>
 struct Vec8<float> {
-    static __device__ __forceinline__ void load(const float* p, float (&x)[8]) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(p), b = *reinterpret_cast<const u32x4*>(p + 4);
+    struct Raw {
+        u32x4 a, b;
+    };
+    static __device__ __forceinline__ Raw fetch(const float* p) {
+        return Raw{*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 4)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&x)[8]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            x[e] = __uint_as_float(a[e]);
-            x[4 + e] = __uint_as_float(b[e]);
+            x[e] = __uint_as_float(r.a[e]);
+            x[4 + e] = __uint_as_float(r.b[e]);
         }
     }
+    static __device__ __forceinline__ void load(const float* p, float (&x)[8]) { unpack(fetch(p), x); }
     static __device__ __forceinline__ void store(float* p, const float (&x)[8]) {
         *reinterpret_cast<u32x4*>(p) = u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
                                              __float_as_uint(x[3])};
@@ -60,7 +71,8 @@ struct Vec8<float> {
     }
 };
 
-__device__ __forceinline__ float silu(float x) { return x / (1.f + __expf(-x)); }
+// x sigmoid(x) with the hardware reciprocal (about 1 ulp) in place of a division
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // One thread per (b, group of 8 channels, run of kRun tokens); the K - 1 previous rows
 // of its channels stay in registers as the window slides.
@@ -99,8 +111,14 @@ __global__ __launch_bounds__(256) void causal_conv1d(ConvArgs a) {
         }
     }
     const int64_t t1 = t0 + kRun < a.T ? t0 + kRun : a.T;
+    // rows t + 1 and t + 2 in flight while row t is computed (t0 < T: the grid covers T)
+    typename Vec8<IO>::Raw n1 = Vec8<IO>::fetch(x + t0 * a.C);
+    typename Vec8<IO>::Raw n2 = t0 + 1 < t1 ? Vec8<IO>::fetch(x + (t0 + 1) * a.C) : n1;
     for (int64_t t = t0; t < t1; ++t) {
-        Vec8<IO>::load(x + t * a.C, win[K - 1]);
+        const typename Vec8<IO>::Raw cur = n1;
+        n1 = n2;
+        if (t + 2 < t1) n2 = Vec8<IO>::fetch(x + (t + 2) * a.C);
+        Vec8<IO>::unpack(cur, win[K - 1]);
         float out[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
