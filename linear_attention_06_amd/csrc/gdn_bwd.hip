@@ -221,12 +221,31 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
 
     ChunkRegs<IO, DK, true, NTH> R;
     if (a.NT > 0) fetch_chunk(R, a, rs, h, hq, col0, a.NT - 1, tid);
+    // token strides of dv and of the partials; this thread's output of the pair sums:
+    // token u + 1 - rp, the dq (rwhich = 0) or dk (1) term of row rr
+    static_assert(4 * DK <= NTH, "at most one pair-sum output per thread");
+    const int64_t sdv = static_cast<int64_t>(a.H) * a.dv;
+    const int64_t sqk = static_cast<int64_t>(a.H) * tiles * 2 * DK;
+    const int64_t sgb = static_cast<int64_t>(a.H) * tiles * 2;
+    const int rp = tid / (2 * DK), rwhich = (tid / DK) & 1, rr = tid % DK;
+
     for (int n = a.NT - 1; n >= 0; --n) {
         __syncthreads();
         store_chunk(L, R, rs, n, tid);
         __syncthreads();
         if (n > 0) fetch_chunk(R, a, rs, h, hq, col0, n - 1, tid);
+        // the chunk's tokens that take part and that the row writes (0..64), and its
+        // output addresses at its first token
+        const int64_t ct0 = static_cast<int64_t>(n) * kChunk, r0 = rs.start + ct0;
+        const int nvalid = static_cast<int>(rs.valid - ct0 < 0 ? 0 : (rs.valid - ct0 > 64 ? 64 : rs.valid - ct0));
+        const int nwrite = static_cast<int>(rs.extent - ct0 < 0 ? 0 : (rs.extent - ct0 > 64 ? 64 : rs.extent - ct0));
+        float* const dv_c = a.dv_out + (r0 * a.H + h) * a.dv + col0 + c;
+        float* const qk_c = a.dqk_part + ((r0 * a.H + h) * tiles + tile) * 2 * DK + (1 - rp) * sqk + rwhich * DK + rr;
+        float* const gb_c = a.dgb_part + ((r0 * a.H + h) * tiles + tile) * 2 + (1 - ((tid >> 1) & 1)) * sgb + (tid & 1);
         for (int s = 7; s >= 0; --s) {
+            float* const dv_s = dv_c + 8 * s * sdv;
+            float* const qk_s = qk_c + 8 * s * sqk;
+            float* const gb_s = gb_c + 8 * s * sgb;
             // the piece's states in registers: St[u] before token 8 s + u, St[u + 1] after it
             float St[9][RJ], w[8];
 #pragma unroll
@@ -241,8 +260,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
 #pragma unroll
             for (int uu = 7; uu >= 0; --uu) {
                 const int u = 8 * s + uu;
-                const int64_t t = static_cast<int64_t>(n) * kChunk + u;
-                const bool valid = t < rs.valid;
+                const bool valid = u < nvalid;
                 const float eg = L.eg[u], bt = L.beta[u], vc = L.v[u][c], doc = L.d[u][c];
                 float M[RJ];
                 float z = 0.f, ms = 0.f;
@@ -254,9 +272,8 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                 }
                 z = col_sum<TPC>(z);
                 ms = col_sum<TPC>(ms);
-                const bool inrow = t < rs.extent;      // the tail of the last chunk is past the row
-                const int64_t tokrow = rs.start + t;
-                if (i == 0 && inrow) a.dv_out[(tokrow * a.H + h) * a.dv + col0 + c] = valid ? bt * z : 0.f;
+                // the tail of the last chunk is past the row
+                if (i == 0 && u < nwrite) dv_s[uu * sdv] = valid ? bt * z : 0.f;
                 // dk's column terms: M beta (v - e^g w) - e^g beta z S_{t-1}
                 const float am = bt * (vc - eg * w[uu]), bz = eg * bt * z;
 #pragma unroll
@@ -272,25 +289,19 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                 if ((uu & 1) == 0) {
                     // the pair of tokens u + 1 (slot p = 0) and u (p = 1)
                     __syncthreads();
-                    for (int e = tid; e < 4 * DK; e += NTH) {
-                        const int p = e / (2 * DK), which = (e / DK) & 1, r = e % DK;
-                        const int64_t tp = t + 1 - p;
-                        if (tp < rs.extent) {
-                            float acc = 0.f;
+                    if (tid < 4 * DK && u + 1 - rp < nwrite) {
+                        float acc = 0.f;
 #pragma unroll
-                            for (int cc = 0; cc < 16; ++cc) acc += red_s[(uu + 1 - p) & 3][which][cc][r];
-                            a.dqk_part[(((rs.start + tp) * a.H + h) * tiles + tile) * 2 * DK + which * DK + r] =
-                                tp < rs.valid ? acc : 0.f;
-                        }
+                        for (int cc = 0; cc < 16; ++cc) acc += red_s[(uu + 1 - rp) & 3][rwhich][cc][rr];
+                        qk_s[uu * sqk] = u + 1 - rp < nvalid ? acc : 0.f;
                     }
                     if (tid < 4) {
                         const int p = tid / 2, which = tid & 1;
-                        const int64_t tp = t + 1 - p;
-                        if (tp < rs.extent) {
+                        if (u + 1 - p < nwrite) {
                             float acc = 0.f;
 #pragma unroll
                             for (int cc = 0; cc < 16; ++cc) acc += red2_s[(uu + 1 - p) & 3][which][cc];
-                            a.dgb_part[(((rs.start + tp) * a.H + h) * tiles + tile) * 2 + which] = acc;
+                            gb_s[uu * sgb] = acc;
                         }
                     }
                 }
