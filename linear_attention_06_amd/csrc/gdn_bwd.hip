@@ -22,7 +22,8 @@
 // SIMDs run two waves of a block and each thread's share of the token chain halves:
 // 12.5 against 15.1 ms at H = 32, d = 128, 8K tokens; 64 threads per column were slower
 // again (15.9 ms).
-//   bwd_ckpt    the forward state before every 8th token into the workspace;
+//   bwd_ckpt    the forward state before every 8th token into the workspace (each
+//               tile in thread order, so a wave's stores and loads are contiguous);
 //   bwd_sweep   chunks in reverse, 8-token pieces in reverse: each piece's states are
 //               recomputed into registers from its checkpoint (loaded one piece ahead)
 //               and the piece is run backwards; dv and
@@ -179,10 +180,10 @@ __global__ __launch_bounds__(16 * TPC) void bwd_ckpt(BwdArgs a) {
         __syncthreads();
         if (n + 1 < a.NT) fetch_chunk(R, a, rs, h, hq, col0, n + 1, tid);
         for (int u = 0; u < 64; ++u) {
-            if ((u & 7) == 0) {   // the state before every 8th token
-                float* ck = a.ckpt + (bh * 8 * a.NT + 8 * n + (u >> 3)) * DK * a.dv;
+            if ((u & 7) == 0) {   // the state before every 8th token, in thread order
+                float* ck = a.ckpt + ((bh * 8 * a.NT + 8 * n + (u >> 3)) * (a.dv / 16) + blockIdx.x) * (16 * DK);
 #pragma unroll
-                for (int j = 0; j < RJ; ++j) ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c] = S[j];
+                for (int j = 0; j < RJ; ++j) ck[j * NTH + tid] = S[j];
             }
             fwd_step<RJ, TPC>(S, L, u, i, c);
         }
@@ -212,9 +213,9 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
 
     // the checkpoint of 8-token piece m (the state before token 8 m), loaded one piece ahead
     const auto load_ck = [&](int m, float (&x)[RJ]) {
-        const float* ck = a.ckpt + (bh * 8 * a.NT + m) * DK * a.dv;
+        const float* ck = a.ckpt + ((bh * 8 * a.NT + m) * tiles + tile) * (16 * DK);
 #pragma unroll
-        for (int j = 0; j < RJ; ++j) x[j] = ck[static_cast<int64_t>(i + TPC * j) * a.dv + col0 + c];
+        for (int j = 0; j < RJ; ++j) x[j] = ck[j * NTH + tid];
     };
     float nxt[RJ];
     if (a.NT > 0) load_ck(8 * a.NT - 1, nxt);

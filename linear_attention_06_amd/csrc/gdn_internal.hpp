@@ -148,7 +148,8 @@ struct BwdArgs {
     const float* h0;          // [B,H,dk,dv] or NULL
     const float* dhT;         // [B,H,dk,dv] gradient of the final state, or NULL
     const int32_t* valid_len;
-    float* ckpt;              // workspace [B,H,NT,dk,dv]: state at every chunk start
+    float* ckpt;              // workspace [B,H,8 NT,dv/16,16 dk]: state before every 8th token,
+                              // each 16-column tile in the order of the threads holding it
     float* dqk_part;          // workspace [B,T,H,dv/16,2,dk]: dq, dk per column tile
     float* dgb_part;          // workspace [B,T,H,dv/16,2]: dg, dbeta per column tile
     float* dq_out;            // [B,T,Hqk,dk]
