@@ -114,6 +114,8 @@ __global__ __launch_bounds__(256) void causal_conv1d(ConvArgs a) {
     // rows t + 1 and t + 2 in flight while row t is computed (t0 < T: the grid covers T)
     typename Vec8<IO>::Raw n1 = Vec8<IO>::fetch(x + t0 * a.C);
     typename Vec8<IO>::Raw n2 = t0 + 1 < t1 ? Vec8<IO>::fetch(x + (t0 + 1) * a.C) : n1;
+    // unrolled so that the sliding window renames registers instead of copying them
+#pragma unroll 4
     for (int64_t t = t0; t < t1; ++t) {
         const typename Vec8<IO>::Raw cur = n1;
         n1 = n2;
