@@ -118,6 +118,8 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     __shared__ float s_s[DK * (BV + 1)];
     __shared__ float x_s[64 * (BV + 1)];
     __shared__ float u_s[64 * (BV + 1)];
+    __shared__ float t_s[64 * 65];     // the chunk's That
+    __shared__ float p_s[64 * 65];     // and P (when o is written)
     __shared__ float g_s[128];
 
     const int col0 = blockIdx.x * BV;
@@ -151,27 +153,66 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     const int c4 = (tid % 4) * 4;      // first of this thread's 4 columns
     const int n0 = seg * a.Lc;
     const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
-    for (int n = n0; n < n1; ++n) {
+
+    // A chunk's operands in flight: K rows, That, P and the decay factors. Every
+    // thread issues all its loads at once, one chunk ahead (addresses of padded tokens
+    // clamped to the row's first token, which exists whenever the row has a chunk; their
+    // values are replaced by zero when stored).
+    constexpr int EK = 64 * DK / 256;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    float kr[EK], gr = 0.f;
+    f32x4 tr[4], pr[4];
+    const auto fetch = [&](int n) {
         const int64_t t0 = static_cast<int64_t>(n) * kChunk;
         const int64_t ch = bh * a.NT + n;
-        __syncthreads();
-        for (int e = tid; e < 64 * DK; e += 256) {
-            const int rr = e / DK, d = e % DK;
-            const int64_t tok = t0 + rr;
-            k_s[rr * KP + d] =
-                tok < nvalid ? ld_io(k, ((rs.start + tok) * a.Hqk + hq) * DK + d)
-                             : 0.f;
+#pragma unroll
+        for (int m = 0; m < EK; ++m) {
+            const int e = tid + 256 * m, rr = e / DK, d = e % DK;
+            const int64_t idx = ((rs.start + (t0 + rr < nvalid ? t0 + rr : 0)) * a.Hqk + hq) * DK + d;
+            kr[m] = ld_io(k, idx);
         }
-        if (tid < 128) g_s[tid] = a.ws.gates[ch * 128 + tid];
+        const f32x4* tg = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws.that) + ch * 4096);
+        const f32x4* pg = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws.pmat) + ch * 4096);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            tr[m] = tg[tid + 256 * m];
+            if (o) pr[m] = pg[tid + 256 * m];
+        }
+        if (tid < 128) gr = a.ws.gates[ch * 128 + tid];
+    };
+    if (n0 < n1) fetch(n0);
+    for (int n = n0; n < n1; ++n) {
+        const int64_t t0 = static_cast<int64_t>(n) * kChunk;
         __syncthreads();
+#pragma unroll
+        for (int m = 0; m < EK; ++m) {
+            const int e = tid + 256 * m, rr = e / DK, d = e % DK;
+            k_s[rr * KP + d] = t0 + rr < nvalid ? kr[m] : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, rr = e / 16, cc = 4 * (e % 16);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                t_s[rr * 65 + cc + x] = tr[m][x];
+                if (o) p_s[rr * 65 + cc + x] = pr[m][x];
+            }
+        }
+        if (tid < 128) g_s[tid] = gr;
+        __syncthreads();
+        if (n + 1 < n1) fetch(n + 1);
 
         const int64_t tok = t0 + r;
         const bool valid = tok < nvalid;
-        const int64_t qrow = ((rs.start + tok) * a.Hqk + hq) * DK;
+        // q straight from memory (the row's four threads share it), addresses clamped so the
+        // unrolled loads issue together; only read when o is written
+        const int64_t qrow = ((rs.start + (valid ? tok : 0)) * a.Hqk + hq) * DK;
         float ks[4] = {0.f, 0.f, 0.f, 0.f}, qs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
         for (int i = 0; i < DK; ++i) {
             const float kv = k_s[r * KP + i];
-            const float qv = valid ? ld_io(q, qrow + i) : 0.f;
+            const float qm = o ? ld_io(q, qrow + i) : 0.f;
+            const float qv = valid ? qm : 0.f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float sv = s_s[i * (BV + 1) + c4 + c];
@@ -188,10 +229,9 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
         }
         __syncthreads();
 
-        const float* that = static_cast<const float*>(a.ws.that) + ch * 4096;
         float u[4] = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s <= r; ++s) {
-            const float tv = that[r * 64 + s];
+            const float tv = t_s[r * 65 + s];
 #pragma unroll
             for (int c = 0; c < 4; ++c) u[c] += tv * x_s[s * (BV + 1) + c4 + c];
         }
@@ -200,12 +240,11 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
         __syncthreads();
 
         if (o && tok < rs.extent) {
-            const float* pm = static_cast<const float*>(a.ws.pmat) + ch * 4096;
             float ov[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) ov[c] = eg * qs[c];
             for (int s = 0; s <= r; ++s) {
-                const float pv = pm[r * 64 + s];
+                const float pv = p_s[r * 65 + s];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) ov[c] += pv * u_s[s * (BV + 1) + c4 + c];
             }
