@@ -115,12 +115,15 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     constexpr int KP = DK + 1;
     constexpr int BV = 16;
     __shared__ float k_s[64 * KP];
-    __shared__ float s_s[DK * (BV + 1)];
-    __shared__ float x_s[64 * (BV + 1)];
-    __shared__ float u_s[64 * (BV + 1)];
+    // the state tile, X and U with rows of 16 floats: every read below is either the same
+    // row for the whole wave or consecutive columns, so 16-byte reads are conflict-free
+    __shared__ __align__(16) float s_s[DK * BV];
+    __shared__ __align__(16) float x_s[64 * BV];
+    __shared__ __align__(16) float u_s[64 * BV];
     __shared__ float t_s[64 * 65];     // the chunk's That
     __shared__ float p_s[64 * 65];     // and P (when o is written)
     __shared__ float g_s[128];
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
 
     const int col0 = blockIdx.x * BV;
     const int h = blockIdx.y;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
         } else if (a.init_mode == kInitIdentity) {
             s0 = (i == col0 + c) ? 1.f : 0.f;
         }
-        s_s[i * (BV + 1) + c] = s0;
+        s_s[i * BV + c] = s0;
     }
 
     const int r = tid / 4;             // token row within the chunk
@@ -159,7 +162,6 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     // clamped to the row's first token, which exists whenever the row has a chunk; their
     // values are replaced by zero when stored).
     constexpr int EK = 64 * DK / 256;
-    typedef float f32x4 __attribute__((ext_vector_type(4)));
     float kr[EK], gr = 0.f;
     f32x4 tr[4], pr[4];
     const auto fetch = [&](int n) {
@@ -213,30 +215,32 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
             const float kv = k_s[r * KP + i];
             const float qm = o ? ld_io(q, qrow + i) : 0.f;
             const float qv = valid ? qm : 0.f;
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_s[i * BV + c4]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const float sv = s_s[i * (BV + 1) + c4 + c];
-                ks[c] += kv * sv;
-                qs[c] += qv * sv;
+                ks[c] += kv * sv[c];
+                qs[c] += qv * sv[c];
             }
         }
         const float eg = g_s[r];
         const int64_t vrow = ((rs.start + tok) * a.H + h) * ncols + col0 + c4;
+        f32x4 xv;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float vv = (v && valid) ? ld_io(v, vrow + c) : 0.f;
-            x_s[r * (BV + 1) + c4 + c] = vv - eg * ks[c];
+            xv[c] = vv - eg * ks[c];
         }
+        *reinterpret_cast<f32x4*>(&x_s[r * BV + c4]) = xv;
         __syncthreads();
 
         float u[4] = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s <= r; ++s) {
             const float tv = t_s[r * 65 + s];
+            const f32x4 xs = *reinterpret_cast<const f32x4*>(&x_s[s * BV + c4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) u[c] += tv * x_s[s * (BV + 1) + c4 + c];
+            for (int c = 0; c < 4; ++c) u[c] += tv * xs[c];
         }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) u_s[r * (BV + 1) + c4 + c] = u[c];
+        *reinterpret_cast<f32x4*>(&u_s[r * BV + c4]) = f32x4{u[0], u[1], u[2], u[3]};
         __syncthreads();
 
         if (o && tok < rs.extent) {
@@ -245,20 +249,29 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
             for (int c = 0; c < 4; ++c) ov[c] = eg * qs[c];
             for (int s = 0; s <= r; ++s) {
                 const float pv = p_s[r * 65 + s];
+                const f32x4 us = *reinterpret_cast<const f32x4*>(&u_s[s * BV + c4]);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) ov[c] += pv * u_s[s * (BV + 1) + c4 + c];
+                for (int c = 0; c < 4; ++c) ov[c] += pv * us[c];
             }
 #pragma unroll
             for (int c = 0; c < 4; ++c) st_io(o, vrow + c, valid ? ov[c] : 0.f);
         }
 
+        // S <- e^{Gam_C} S + K^T (e^{Gam_C - Gam} U): the thread's elements are rows
+        // i0 + 16 m of column cs, so each step reads the column's scaled U value once
+        constexpr int ES = DK * BV / 256;
+        const int cs = tid % BV, i0 = tid / BV;
         const float egC = g_s[63];
-        for (int e = tid; e < DK * BV; e += 256) {
-            const int i = e / BV, c = e % BV;
-            float acc = egC * s_s[i * (BV + 1) + c];
-            for (int s = 0; s < 64; ++s) acc += g_s[64 + s] * k_s[s * KP + i] * u_s[s * (BV + 1) + c];
-            s_s[i * (BV + 1) + c] = acc;
+        float acc[ES];
+#pragma unroll
+        for (int m = 0; m < ES; ++m) acc[m] = egC * s_s[(i0 + 16 * m) * BV + cs];
+        for (int s = 0; s < 64; ++s) {
+            const float gu = g_s[64 + s] * u_s[s * BV + cs];
+#pragma unroll
+            for (int m = 0; m < ES; ++m) acc[m] = fmaf(k_s[s * KP + i0 + 16 * m], gu, acc[m]);
         }
+#pragma unroll
+        for (int m = 0; m < ES; ++m) s_s[(i0 + 16 * m) * BV + cs] = acc[m];
     }
     __syncthreads();
 
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     const int64_t blk = (a.store_mode == kStoreEverySegment) ? bh * a.P + seg : bh;
     for (int e = tid; e < DK * BV; e += 256) {
         const int i = e / BV, c = e % BV;
-        a.s_out[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = s_s[i * (BV + 1) + c];
+        a.s_out[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = s_s[i * BV + c];
     }
 }
 
