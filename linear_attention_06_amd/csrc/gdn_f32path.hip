@@ -78,7 +78,8 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
         float av = 0.f, pv = 0.f;
         if (j <= i) {
             float kk = 0.f, qk = 0.f;
-#pragma unroll 8
+            // fully unrolled, so that qreg stays in registers
+#pragma unroll
             for (int d = 0; d < DK; ++d) {
                 const float kj = kt_s[j * KP + d];
                 kk += kt_s[i * KP + d] * kj;
