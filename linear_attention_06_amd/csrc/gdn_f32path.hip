@@ -74,23 +74,40 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
 
     float* that = static_cast<float*>(a.ws.that) + ch * 4096;
     float* pm = static_cast<float*>(a.ws.pmat) + ch * 4096;
-    for (int j = 0; j < 64; ++j) {
-        float av = 0.f, pv = 0.f;
-        if (j <= i) {
-            float kk = 0.f, qk = 0.f;
+    // two columns j at a time: the lane's own K row is read once per two products, and its
+    // two P values leave in one 8-byte store (wider blocks spill registers at dk = 128)
+    for (int j0 = 0; j0 < 64; j0 += 2) {
+        float kk[2], qk[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) kk[jj] = qk[jj] = 0.f;
+        if (j0 <= i) {
             // fully unrolled, so that qreg stays in registers
 #pragma unroll
             for (int d = 0; d < DK; ++d) {
-                const float kj = kt_s[j * KP + d];
-                kk += kt_s[i * KP + d] * kj;
-                qk += qreg[d] * kj;
+                const float ki = kt_s[i * KP + d];
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+                    const float kj = kt_s[(j0 + jj) * KP + d];
+                    kk[jj] += ki * kj;
+                    qk[jj] += qreg[d] * kj;
+                }
             }
-            const float decay = expf(gam - gam_s[j]);
-            pv = decay * qk;
-            if (j < i) av = bi * decay * kk;
         }
-        a_s[i * 65 + j] = av;
-        pm[i * 64 + j] = pv;
+        float pv[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = j0 + jj;
+            float av = 0.f;
+            pv[jj] = 0.f;
+            if (j <= i) {
+                const float decay = expf(gam - gam_s[j]);
+                pv[jj] = decay * qk[jj];
+                if (j < i) av = bi * decay * kk[jj];
+            }
+            a_s[i * 65 + j] = av;
+        }
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<f32x2*>(pm + i * 64 + j0) = f32x2{pv[0], pv[1]};
     }
     __syncthreads();
 
