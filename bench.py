@@ -314,6 +314,41 @@ def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
     return out
 
 
+def vector_path_timing(gdn, workloads, make_inputs, dev, stream, timed):
+    """gdn_chunk_fwd on the problems the matrix-core kernels do not take, which run the fp32
+    vector-ALU kernels: the stateless 8K workload's shapes with heads of 64 (bf16) and with
+    fp32 inputs (heads of 128)."""
+    import dataclasses
+
+    import torch
+
+    out = {}
+    base = workloads["stateless_8k"]
+    for name, d, io in (("stateless_8k_bf16_d64", 64, "bf16"), ("stateless_8k_f32_d128", 128, "f32")):
+        w = dataclasses.replace(base, name=name, dk=d, dv=d, io=io)
+        inp = make_inputs(w)
+
+        def dev_io(x):
+            t = torch.from_numpy(np.ascontiguousarray(x))
+            return (t.view(torch.int16).view(torch.bfloat16) if io == "bf16" else t).to(dev)
+
+        q, k, v = dev_io(inp.q), dev_io(inp.k), dev_io(inp.v)
+        g = torch.from_numpy(inp.g).to(dev)
+        beta = torch.from_numpy(inp.beta).to(dev)
+        p = gdn.problem(q, v)
+        ws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
+        o = torch.empty_like(v)
+        hT = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+
+        def step():
+            gdn.gdn_chunk_fwd(q, k, v, g, beta, None, o=o, hT=hT, ws=ws, stream=stream)
+
+        ms = timed(step, 5)
+        out[name] = {"kernel_path": gdn.gdn_kernel_path(p), "T": w.T, "H": w.H, "d": d, "io": io,
+                     "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
+    return out
+
+
 def torch_empty(shape, dev):
     import torch
 
@@ -463,6 +498,7 @@ def main():
         line["fused_prologue_32k"] = prologue_timing(gdn, inp, dev, stream, timed)
         line["backward_8k"] = backward_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
         line["layer_ops"] = layer_ops_timing(gdn, dev, stream, timed)
+        line["vector_path"] = vector_path_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line))
