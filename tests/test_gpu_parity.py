@@ -52,6 +52,23 @@ def test_stateless_8k_matches_oracle():
     assert_close(np_f64(o), o_ref, TOL_BF16, "stateless_8k o")
 
 
+@pytest.mark.parametrize("d,io", [(64, "bf16"), (128, "f32")], ids=["bf16_d64", "f32_d128"])
+def test_vector_path_full_size_matches_oracle(d, io):
+    """The stateless 8K workload's shapes on the fp32 vector-ALU kernels (heads of 64 in
+    bf16, and fp32 inputs): the sizes bench.py times for that path."""
+    w = dataclasses.replace(WORKLOADS["stateless_8k"], name="vector_%s_d%d" % (io, d), dk=d, dv=d, io=io)
+    inp = make_inputs(w)
+    q, k, v, g, beta, _, _ = to_dev(inp)
+    assert gdn.gdn_kernel_path(gdn.problem(q, v)) == "f32-valu"
+    q64, k64, v64, g64, b64, _ = inp.f64()
+    o_ref, hT_ref = oracle.gdn_fwd(q64, k64, v64, g64, b64, None)
+    o, hT = gdn.gdn_chunk_fwd(q, k, v, g, beta, None)
+    sync()
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    assert_close(np_f64(o), o_ref, tol, "vector path %s d=%d o" % (io, d))
+    assert_close(np_f64(hT), hT_ref, tol, "vector path %s d=%d hT" % (io, d))
+
+
 def test_bf16_head_dim_128_uses_the_matrix_core_path():
     inp = workload_inputs("stateful_32k")
     q, k, v, g, beta, h0, _ = to_dev(inp)
