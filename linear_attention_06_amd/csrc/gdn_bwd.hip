@@ -242,7 +242,8 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
         const int nwrite = static_cast<int>(rs.extent - ct0 < 0 ? 0 : (rs.extent - ct0 > 64 ? 64 : rs.extent - ct0));
         float* const dv_c = a.dv_out + (r0 * a.H + h) * a.dv + col0 + c;
         float* const qk_c = a.dqk_part + ((r0 * a.H + h) * tiles + tile) * 2 * DK + (1 - rp) * sqk + rwhich * DK + rr;
-        float* const gb_c = a.dgb_part + ((r0 * a.H + h) * tiles + tile) * 2 + (1 - ((tid >> 1) & 1)) * sgb + (tid & 1);
+        float* const gb_c = a.dgb_part + ((r0 * a.H + h) * tiles + tile) * 2 + (1 - ((tid >> 5) & 1)) * sgb +
+                            ((tid >> 4) & 1);
         for (int s = 7; s >= 0; --s) {
             float* const dv_s = dv_c + 8 * s * sdv;
             float* const qk_s = qk_c + 8 * s * sqk;
@@ -296,14 +297,12 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                         for (int cc = 0; cc < 16; ++cc) acc += red_s[(uu + 1 - rp) & 3][rwhich][cc][rr];
                         qk_s[uu * sqk] = u + 1 - rp < nvalid ? acc : 0.f;
                     }
-                    if (tid < 4) {
-                        const int p = tid / 2, which = tid & 1;
-                        if (u + 1 - p < nwrite) {
-                            float acc = 0.f;
-#pragma unroll
-                            for (int cc = 0; cc < 16; ++cc) acc += red2_s[(uu + 1 - p) & 3][which][cc];
-                            gb_s[uu * sgb] = acc;
-                        }
+                    if (tid < 64) {
+                        // wave 0: lane 16 (2 p + which) + cc holds column cc's term, and the
+                        // 16 lanes of a DPP row sum them
+                        const int p = tid / 32, which = (tid / 16) & 1;
+                        const float acc = row_sum16(red2_s[(uu + 1 - p) & 3][which][tid & 15]);
+                        if ((tid & 15) == 0 && u + 1 - p < nwrite) gb_s[uu * sgb] = acc;
                     }
                 }
 #pragma unroll
