@@ -126,12 +126,15 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
     gates[64 + i] = expf(gam_c - gam);
 }
 
-// One block of 256 threads per (b, h, segment, 16 state columns): the
-// sequential pass over the segment's chunks with the state tile in LDS.
-template <typename IO, int DK>
-__global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
+// One block of 64 (16 / CPT) threads per (b, h, segment, 16 state columns): the
+// sequential pass over the segment's chunks with the state tile in LDS; thread t holds
+// token row t / (16 / CPT) and CPT columns from CPT (t % (16 / CPT)).
+template <typename IO, int DK, int CPT>
+__global__ __launch_bounds__(64 * (16 / CPT)) void state_f32path(StateArgs a) {
     constexpr int KP = DK + 1;
     constexpr int BV = 16;
+    constexpr int NTH = 64 * (BV / CPT);   // 64 token rows x BV / CPT groups of CPT columns
+    typedef float vecC __attribute__((ext_vector_type(CPT)));
     __shared__ float k_s[64 * KP];
     // the state tile, X and U with rows of 16 floats: every read below is either the same
     // row for the whole wave or consecutive columns, so 16-byte reads are conflict-free
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     const int64_t tile = static_cast<int64_t>(DK) * ncols;
 
-    for (int e = tid; e < DK * BV; e += 256) {
+    for (int e = tid; e < DK * BV; e += NTH) {
         const int i = e / BV, c = e % BV;
         float s0 = 0.f;
         if (a.init_mode == kInitLoad) {
@@ -170,8 +173,8 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
         s_s[i * BV + c] = s0;
     }
 
-    const int r = tid / 4;             // token row within the chunk
-    const int c4 = (tid % 4) * 4;      // first of this thread's 4 columns
+    const int r = tid / (BV / CPT);            // token row within the chunk
+    const int c4 = (tid % (BV / CPT)) * CPT;   // first of this thread's CPT columns
     const int n0 = seg * a.Lc;
     const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
 
@@ -179,24 +182,24 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
     // thread issues all its loads at once, one chunk ahead (addresses of padded tokens
     // clamped to the row's first token, which exists whenever the row has a chunk; their
     // values are replaced by zero when stored).
-    constexpr int EK = 64 * DK / 256;
+    constexpr int EK = 64 * DK / NTH, ET = 1024 / NTH;
     float kr[EK], gr = 0.f;
-    f32x4 tr[4], pr[4];
+    f32x4 tr[ET], pr[ET];
     const auto fetch = [&](int n) {
         const int64_t t0 = static_cast<int64_t>(n) * kChunk;
         const int64_t ch = bh * a.NT + n;
 #pragma unroll
         for (int m = 0; m < EK; ++m) {
-            const int e = tid + 256 * m, rr = e / DK, d = e % DK;
+            const int e = tid + NTH * m, rr = e / DK, d = e % DK;
             const int64_t idx = ((rs.start + (t0 + rr < nvalid ? t0 + rr : 0)) * a.Hqk + hq) * DK + d;
             kr[m] = ld_io(k, idx);
         }
         const f32x4* tg = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws.that) + ch * 4096);
         const f32x4* pg = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.ws.pmat) + ch * 4096);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            tr[m] = tg[tid + 256 * m];
-            if (o) pr[m] = pg[tid + 256 * m];
+        for (int m = 0; m < ET; ++m) {
+            tr[m] = tg[tid + NTH * m];
+            if (o) pr[m] = pg[tid + NTH * m];
         }
         if (tid < 128) gr = a.ws.gates[ch * 128 + tid];
     };
@@ -206,12 +209,12 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < EK; ++m) {
-            const int e = tid + 256 * m, rr = e / DK, d = e % DK;
+            const int e = tid + NTH * m, rr = e / DK, d = e % DK;
             k_s[rr * KP + d] = t0 + rr < nvalid ? kr[m] : 0.f;
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int e = tid + 256 * m, rr = e / 16, cc = 4 * (e % 16);
+        for (int m = 0; m < ET; ++m) {
+            const int e = tid + NTH * m, rr = e / 16, cc = 4 * (e % 16);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 t_s[rr * 65 + cc + x] = tr[m][x];
@@ -224,79 +227,86 @@ __global__ __launch_bounds__(256) void state_f32path(StateArgs a) {
 
         const int64_t tok = t0 + r;
         const bool valid = tok < nvalid;
-        // q straight from memory (the row's four threads share it), addresses clamped so the
+        // q straight from memory (the row's threads share it), addresses clamped so the
         // unrolled loads issue together; only read when o is written
         const int64_t qrow = ((rs.start + (valid ? tok : 0)) * a.Hqk + hq) * DK;
-        float ks[4] = {0.f, 0.f, 0.f, 0.f}, qs[4] = {0.f, 0.f, 0.f, 0.f};
+        float ks[CPT], qs[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) ks[c] = qs[c] = 0.f;
 #pragma unroll 8
         for (int i = 0; i < DK; ++i) {
             const float kv = k_s[r * KP + i];
             const float qm = o ? ld_io(q, qrow + i) : 0.f;
             const float qv = valid ? qm : 0.f;
-            const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_s[i * BV + c4]);
+            const vecC sv = *reinterpret_cast<const vecC*>(&s_s[i * BV + c4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < CPT; ++c) {
                 ks[c] += kv * sv[c];
                 qs[c] += qv * sv[c];
             }
         }
         const float eg = g_s[r];
         const int64_t vrow = ((rs.start + tok) * a.H + h) * ncols + col0 + c4;
-        f32x4 xv;
+        vecC xv;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < CPT; ++c) {
             const float vv = (v && valid) ? ld_io(v, vrow + c) : 0.f;
             xv[c] = vv - eg * ks[c];
         }
-        *reinterpret_cast<f32x4*>(&x_s[r * BV + c4]) = xv;
+        *reinterpret_cast<vecC*>(&x_s[r * BV + c4]) = xv;
         __syncthreads();
 
-        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        vecC u;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) u[c] = 0.f;
         for (int s = 0; s <= r; ++s) {
             const float tv = t_s[r * 65 + s];
-            const f32x4 xs = *reinterpret_cast<const f32x4*>(&x_s[s * BV + c4]);
+            const vecC xs = *reinterpret_cast<const vecC*>(&x_s[s * BV + c4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) u[c] += tv * xs[c];
+            for (int c = 0; c < CPT; ++c) u[c] += tv * xs[c];
         }
-        *reinterpret_cast<f32x4*>(&u_s[r * BV + c4]) = f32x4{u[0], u[1], u[2], u[3]};
+        *reinterpret_cast<vecC*>(&u_s[r * BV + c4]) = u;
         __syncthreads();
 
         if (o && tok < rs.extent) {
-            float ov[4];
+            float ov[CPT];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) ov[c] = eg * qs[c];
+            for (int c = 0; c < CPT; ++c) ov[c] = eg * qs[c];
             for (int s = 0; s <= r; ++s) {
                 const float pv = p_s[r * 65 + s];
-                const f32x4 us = *reinterpret_cast<const f32x4*>(&u_s[s * BV + c4]);
+                const vecC us = *reinterpret_cast<const vecC*>(&u_s[s * BV + c4]);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) ov[c] += pv * us[c];
+                for (int c = 0; c < CPT; ++c) ov[c] += pv * us[c];
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) st_io(o, vrow + c, valid ? ov[c] : 0.f);
+            for (int c = 0; c < CPT; ++c) st_io(o, vrow + c, valid ? ov[c] : 0.f);
         }
 
         // S <- e^{Gam_C} S + K^T (e^{Gam_C - Gam} U): the thread's elements are rows
-        // i0 + 16 m of column cs, so each step reads the column's scaled U value once
-        constexpr int ES = DK * BV / 256;
+        // i0 + RS m of column cs (RS = NTH / BV), so each step reads the column's scaled U
+        // value once; with more threads than elements (dk = 16, 512 threads) the rest idle
+        constexpr int RS = NTH / BV, ES = (DK + RS - 1) / RS;
         const int cs = tid % BV, i0 = tid / BV;
-        const float egC = g_s[63];
-        float acc[ES];
+        if (i0 < DK) {
+            const float egC = g_s[63];
+            float acc[ES];
 #pragma unroll
-        for (int m = 0; m < ES; ++m) acc[m] = egC * s_s[(i0 + 16 * m) * BV + cs];
-        for (int s = 0; s < 64; ++s) {
-            const float gu = g_s[64 + s] * u_s[s * BV + cs];
+            for (int m = 0; m < ES; ++m) acc[m] = egC * s_s[(i0 + RS * m) * BV + cs];
+            for (int s = 0; s < 64; ++s) {
+                const float gu = g_s[64 + s] * u_s[s * BV + cs];
 #pragma unroll
-            for (int m = 0; m < ES; ++m) acc[m] = fmaf(k_s[s * KP + i0 + 16 * m], gu, acc[m]);
+                for (int m = 0; m < ES; ++m) acc[m] = fmaf(k_s[s * KP + i0 + RS * m], gu, acc[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < ES; ++m) s_s[(i0 + RS * m) * BV + cs] = acc[m];
         }
-#pragma unroll
-        for (int m = 0; m < ES; ++m) s_s[(i0 + 16 * m) * BV + cs] = acc[m];
     }
     __syncthreads();
 
     if (a.store_mode == kStoreNone) return;
     if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
     const int64_t blk = (a.store_mode == kStoreEverySegment) ? bh * a.P + seg : bh;
-    for (int e = tid; e < DK * BV; e += 256) {
+    for (int e = tid; e < DK * BV; e += NTH) {
         const int i = e / BV, c = e % BV;
         a.s_out[blk * tile + static_cast<int64_t>(i) * ncols + col0 + c] = s_s[i * BV + c];
     }
@@ -386,6 +396,10 @@ hipError_t prep_dispatch(const PrepArgs& a, hipStream_t s) {
     return hipLaunchKernel(fn, grid, dim3(64), args, 0, s);
 }
 
+// Columns per thread of the state pass: 2 (512-thread blocks, two waves per SIMD) against
+// 4 and 1: 1.93 / 2.17 / 2.10 ms for bf16 heads of 64 at 8K tokens and 32 heads.
+constexpr int kStateCpt = 2;
+
 template <typename IO>
 hipError_t state_dispatch(const StateArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H),
@@ -393,13 +407,13 @@ hipError_t state_dispatch(const StateArgs& a, hipStream_t s) {
     void* args[] = {const_cast<StateArgs*>(&a)};
     const void* fn = nullptr;
     switch (a.dk) {
-        case 16: fn = reinterpret_cast<const void*>(&state_f32path<IO, 16>); break;
-        case 32: fn = reinterpret_cast<const void*>(&state_f32path<IO, 32>); break;
-        case 64: fn = reinterpret_cast<const void*>(&state_f32path<IO, 64>); break;
-        case 128: fn = reinterpret_cast<const void*>(&state_f32path<IO, 128>); break;
+        case 16: fn = reinterpret_cast<const void*>(&state_f32path<IO, 16, kStateCpt>); break;
+        case 32: fn = reinterpret_cast<const void*>(&state_f32path<IO, 32, kStateCpt>); break;
+        case 64: fn = reinterpret_cast<const void*>(&state_f32path<IO, 64, kStateCpt>); break;
+        case 128: fn = reinterpret_cast<const void*>(&state_f32path<IO, 128, kStateCpt>); break;
         default: return hipErrorInvalidValue;
     }
-    return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+    return hipLaunchKernel(fn, grid, dim3(64 * (16 / kStateCpt)), args, 0, s);
 }
 
 }  // namespace
