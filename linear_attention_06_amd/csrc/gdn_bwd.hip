@@ -19,9 +19,9 @@
 // two: thread TPC c + i holds column c of the tile at rows i + TPC j (j < dk / TPC), so
 // that the TPC threads of a column are one DPP row (TPC = 16: four DPP rotations sum a
 // column) or two (TPC = 32, used for dk >= 32: then a v_permlane16_swap). With 32 the
-// SIMDs run two waves of a block and each thread's share of the token chain halves:
-// 12.5 against 15.1 ms at H = 32, d = 128, 8K tokens; 64 threads per column were slower
-// again (15.9 ms).
+// SIMDs run two waves of a block and each thread's share of the token chain halves, which
+// measured faster than 16 threads per column; 64 were slower. The sweep's pair sums give
+// each thread at most one output, which needs 4 dk <= 16 TPC (true for both choices).
 //   bwd_ckpt    the forward state before every 8th token into the workspace (each
 //               tile in thread order, so a wave's stores and loads are contiguous);
 //   bwd_sweep   chunks in reverse, 8-token pieces in reverse: each piece's states are
