@@ -73,3 +73,37 @@ def test_gated_rmsnorm_matches_oracle(io, rows, D):
     tol = TOL_BF16 if io == "bf16" else 1e-5
     print("gated_rmsnorm %s rows=%d D=%d rel-L2 %.3e (bound %.0e)" % (io, rows, D, err, tol))
     assert err <= tol
+
+
+def test_layer_steps_at_the_timed_sizes_sampled():
+    """Both steps at the sizes bench.py times them (Conv1D over [1, 32768, 8192] bf16 with
+    K = 4 and SiLU; the gated RMSNorm over 32768 x 32 rows of 128), checked on sampled
+    channels and rows: each channel of the conv and each row of the norm is independent,
+    so the oracle on a sample is exact for it."""
+    gen = torch.Generator(device=dev()).manual_seed(11)
+    T, C, K = 32768, 8192, 4
+    x = torch.randn((1, T, C), device=dev(), generator=gen).to(torch.bfloat16)
+    w = torch.randn((C, K), device=dev(), generator=gen) * 0.5
+    bias = torch.randn((C,), device=dev(), generator=gen) * 0.1
+    y = gdn.gdn_causal_conv1d(x, w, bias, silu=True)
+    sync()
+    rng = np.random.default_rng(12)
+    # the first and last channel groups, and a random sample of the rest
+    chans = np.unique(np.concatenate([np.arange(8), np.arange(C - 8, C), rng.choice(C, 80, replace=False)]))
+    ci = torch.from_numpy(chans).to(dev())
+    ref = layer_ops.causal_conv1d(seen(x.index_select(2, ci)), np_f64(w[ci]), np_f64(bias[ci]), None, True)
+    err = rel_l2(np_f64(y.index_select(2, ci)), ref)
+    print("conv1d at 32768 x 8192, %d channels sampled: rel-L2 %.3e (bound %.0e)" % (len(chans), err, TOL_BF16))
+    assert err <= TOL_BF16
+
+    rows, D = 32768 * 32, 128
+    o = torch.randn((rows, D), device=dev(), generator=gen).to(torch.bfloat16)
+    z = torch.randn((rows, D), device=dev(), generator=gen).to(torch.bfloat16)
+    wt = torch.randn((D,), device=dev(), generator=gen)
+    yn = gdn.gdn_gated_rmsnorm(o, z, wt, eps=1e-6)
+    sync()
+    ri = torch.from_numpy(np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, 4096, replace=False)]))).to(dev())
+    ref = layer_ops.gated_rmsnorm(seen(o.index_select(0, ri)), seen(z.index_select(0, ri)), np_f64(wt), 1e-6)
+    err = rel_l2(np_f64(yn.index_select(0, ri)), ref)
+    print("gated_rmsnorm at %d rows of %d, %d rows sampled: rel-L2 %.3e (bound %.0e)" % (rows, D, len(ri), err, TOL_BF16))
+    assert err <= TOL_BF16
