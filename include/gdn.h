@@ -202,7 +202,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p,
  *   y[b,t,c] = act(bias[c] + sum_{j<K} w[c,j] x[b, t-K+1+j, c]),  act = SiLU if apply_silu
  * x, y [B, T, C]; w [C, K] fp32; bias [C] fp32 or NULL; x_prev [B, K-1, C] or NULL: the
  * K - 1 tokens before each sequence (a rank's left halo; zeros if NULL). K in {2, 3, 4},
- * C % 8 == 0. y must not alias x.
+ * C % 8 == 0, B <= 65535, T <= 65535 * 128. y must not alias x.
  */
 gdn_status gdn_causal_conv1d(int32_t B, int32_t T, int32_t C, int32_t K, int32_t io_dtype,
                              const void* x, const float* w, const float* bias, const void* x_prev,

@@ -367,7 +367,7 @@ gdn_status gdn_causal_conv1d(int32_t B, int32_t T, int32_t C, int32_t K, int32_t
         if (io_dtype != GDN_F32 && io_dtype != GDN_BF16)
             return fail(GDN_EUNSUPPORTED, "io_dtype=%d: only GDN_F32 and GDN_BF16", io_dtype);
         if (B > 65535) return fail(GDN_EUNSUPPORTED, "B=%d exceeds 65535", B);
-        if (T > 65535 * 64) return fail(GDN_EUNSUPPORTED, "T=%d exceeds 65535 runs of 64 tokens", T);
+        if (T > 65535 * 128) return fail(GDN_EUNSUPPORTED, "T=%d exceeds 65535 runs of 128 tokens", T);
         const int64_t n = static_cast<int64_t>(B) * T * C;
         if (n == 0) return GDN_OK;
         if (!x || !w || !y) return fail(GDN_EINVAL, "x, w and y must be non-NULL");
