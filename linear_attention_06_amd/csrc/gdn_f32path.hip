@@ -31,10 +31,10 @@ __device__ __forceinline__ int64_t valid_tokens(const int32_t* vl, int b, int64_
     return n < 0 ? 0 : (n > T ? T : n);
 }
 
-// One wave per (b, h, chunk): cumulative decay, A, the unit-lower-triangular
-// inverse by forward substitution, P and the decay factors.
+// Two waves per (b, h, chunk): cumulative decay, A, the unit-lower-triangular
+// inverse by forward substitution (wave 0), P and the decay factors.
 template <typename IO, int DK>
-__global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
+__global__ __launch_bounds__(128) void prep_f32path(PrepArgs a) {
     constexpr int KP = DK + 1;
     constexpr int KT = (64 * KP > 64 * 65) ? 64 * KP : 64 * 65;
     __shared__ float kt_s[KT];          // K rows, later the inverse
@@ -46,7 +46,9 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
     const int bh = static_cast<int>(ch / a.NT);
     const int h = bh % a.H, b = bh / a.H;
     const int hq = h / (a.H / a.Hqk);
-    const int i = threadIdx.x;
+    // two waves: both hold row i = lane of the chunk; wave `half` forms the column pairs
+    // j0 = 4 m + 2 half of A and P, and wave 0 alone runs the solve
+    const int i = threadIdx.x & 63, half = threadIdx.x >> 6;
     const int64_t t = static_cast<int64_t>(n) * kChunk + i;
     const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
     const bool valid = t < rs.valid;
@@ -62,12 +64,13 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
         const float y = __shfl_up(gam, off, 64);
         if (i >= off) gam += y;
     }
-    gam_s[i] = gam;
+    if (half == 0) gam_s[i] = gam;
     const int64_t row = ((rs.start + t) * a.Hqk + hq) * DK;
     float qreg[DK];
 #pragma unroll
     for (int d = 0; d < DK; ++d) {
-        kt_s[i * KP + d] = valid ? ld_io(k, row + d) : 0.f;
+        const float kv = valid ? ld_io(k, row + d) : 0.f;
+        if (half == 0) kt_s[i * KP + d] = kv;
         qreg[d] = valid ? ld_io(q, row + d) : 0.f;
     }
     __syncthreads();
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
     float* pm = static_cast<float*>(a.ws.pmat) + ch * 4096;
     // two columns j at a time: the lane's own K row is read once per two products, and its
     // two P values leave in one 8-byte store (wider blocks spill registers at dk = 128)
-    for (int j0 = 0; j0 < 64; j0 += 2) {
+    for (int j0 = 2 * half; j0 < 64; j0 += 4) {
         float kk[2], qk[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) kk[jj] = qk[jj] = 0.f;
@@ -110,6 +113,7 @@ __global__ __launch_bounds__(64) void prep_f32path(PrepArgs a) {
         *reinterpret_cast<f32x2*>(pm + i * 64 + j0) = f32x2{pv[0], pv[1]};
     }
     __syncthreads();
+    if (half != 0) return;   // no barrier follows
 
     // Forward substitution, lane c owns column c of Tinv.
     float* t_s = kt_s;
@@ -393,7 +397,7 @@ hipError_t prep_dispatch(const PrepArgs& a, hipStream_t s) {
         case 128: fn = reinterpret_cast<const void*>(&prep_f32path<IO, 128>); break;
         default: return hipErrorInvalidValue;
     }
-    return hipLaunchKernel(fn, grid, dim3(64), args, 0, s);
+    return hipLaunchKernel(fn, grid, dim3(128), args, 0, s);
 }
 
 // Columns per thread of the state pass: 2 (512-thread blocks, two waves per SIMD) against
