@@ -75,8 +75,8 @@ struct Vec8<float> {
 __device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // One thread per (b, group of 8 channels, run of kRun tokens); the K - 1 previous rows
-// of its channels stay in registers as the window slides. Runs of 128 tokens: one round of
-// four waves per SIMD at T = 32768, C = 8192 (64: 0.226 ms, 128: 0.221 ms).
+// of its channels stay in registers as the window slides. Runs of 128 tokens: every block
+// resident at once, four waves per SIMD, at T = 32768, C = 8192 (64: 0.226 ms, 128: 0.221 ms).
 constexpr int kRun = 128;
 
 template <typename IO, int K>
