@@ -159,7 +159,9 @@ gdn_status gdn_chunk_fwd_prologue_qkv(const gdn_problem* p, const void* qkv,
  * max_seqlen (host) bounds every sequence's length and sizes the workspace; p->valid_len
  * must be NULL. Only the tokens of the sequences are written. The kernels clamp the
  * cu_seqlens values into [0, T] and each length to max_seqlen rounded up to 64, so that no
- * value reads or writes outside the tensors; a sequence longer than that is cut there.
+ * value reads or writes outside the tensors; a sequence longer than that is cut there, and
+ * the outputs of its tokens past the cut are left unwritten (undefined): the caller must
+ * pass a max_seqlen of at least the longest sequence (the Python binding checks it).
  * Any head dims and dtypes gdn_chunk_fwd takes.
  */
 gdn_status gdn_chunk_fwd_varlen_workspace(const gdn_problem* p, int32_t max_seqlen, size_t* bytes);

@@ -152,6 +152,10 @@ gdn::StateArgs state_args(const gdn_problem& p, const Plan& pl, const void* q, c
 
 gdn_status run_state(const gdn_problem& p, const gdn::StateArgs& a, hipStream_t s) {
     if (p.B == 0 || a.P == 0) return GDN_OK;
+    // the summary-M passes read the bf16 remainder of That, which only a segment
+    // workspace holds
+    if (use_mfma(p) && (a.pass == gdn::kPassM || a.pass == gdn::kPassMS) && !a.ws.that_lo)
+        return fail(GDN_EWORKSPACE, "the summary-matrix pass needs a segment workspace");
     hipError_t e = use_mfma(p) ? gdn::launch_state_mfma(a, s)
                                : gdn::launch_state_f32path(a, p.io_dtype == GDN_BF16, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "state kernel launch");

@@ -537,9 +537,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
 #pragma clang diagnostic pop
 }
-// 16-byte load per lane from byte voff + soff of a buffer into registers.
-__device__ __forceinline__ u32x4 gload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+// 16-byte load per lane from byte voff + off of a buffer into registers. The whole
+// byte offset goes into the per-lane (VGPR) offset and the scalar offset is 0: the
+// range check of a raw buffer covers the VGPR and instruction offsets only, so an
+// offset placed in the scalar operand would let rows past the descriptor's end load
+// real memory instead of zero.
+__device__ __forceinline__ u32x4 gload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + off, 0, 0));
 }
 // Barrier of the state pass: this wave's LDS accesses complete, then s_barrier
 // (optionally after all of its vector-memory accesses). One asm statement with a
@@ -1148,6 +1152,8 @@ hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
         case kPassMS: fn = reinterpret_cast<const void*>(&state_mfma<true, true, false>); break;
         default: return hipErrorInvalidValue;
     }
+    // the split-operand passes read the bf16 remainder records of That
+    if ((a.pass == kPassM || a.pass == kPassMS) && !a.ws.that_lo) return hipErrorInvalidValue;
     return hipLaunchKernel(fn, dim3(nblk), dim3(512), args, 0, s);
 }
 

@@ -250,16 +250,24 @@ def gdn_chunk_fwd_varlen_workspace(p: GdnProblem, max_seqlen: int) -> int:
     return n.value
 
 
-def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen, h0=None, o=None, hT=None,
+def gdn_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, max_seqlen=None, h0=None, o=None, hT=None,
                          want_state=True, ws=None, stream=None):
     """Packed variable-length forward: q, k [1,T,Hqk,dk], v [1,T,H,dv], g, beta [1,T,H];
-    cu_seqlens int32 [N+1] on the device, max_seqlen an int. Returns (o, hT [N,H,dk,dv] or None)."""
+    cu_seqlens int32 [N+1] on the device; max_seqlen an int, or None to take it from
+    cu_seqlens. Returns (o, hT [N,H,dk,dv] or None). A max_seqlen below the longest
+    sequence would cut it (the library leaves the cut tokens unwritten), so it is checked
+    against cu_seqlens here (one read of the lengths)."""
     _io_checks(q, k, v, g, beta)
     _dev(h0, "h0", torch.float32)
     _dev(cu_seqlens, "cu_seqlens", torch.int32)
     if q.shape[0] != 1:
         raise ValueError("packed sequences use a batch dimension of 1")
     N = cu_seqlens.numel() - 1
+    longest = int((cu_seqlens[1:] - cu_seqlens[:-1]).max().item()) if N > 0 else 0
+    if max_seqlen is None:
+        max_seqlen = longest
+    elif int(max_seqlen) < longest:
+        raise ValueError("max_seqlen=%d is below the longest sequence (%d tokens)" % (int(max_seqlen), longest))
     p = problem(q, v)
     p.B = N
     if o is None:

@@ -19,6 +19,8 @@ TOL_BF16 = PAGE["rel_l2_bound_bf16"]["value"]
 # fp32 inputs: the arithmetic is fp32 throughout; 1e-4 leaves about two orders
 # of magnitude over the rounding of 64-term fp32 dot products chained over chunks.
 TOL_F32 = 1e-4
+# The pages' scaled check: max |x - ref| / max |ref| per tensor.
+TOL_MAXABS = PAGE["scaled_max_abs_bound"]["value"]
 
 
 def dev():

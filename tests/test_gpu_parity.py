@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_common import (TOL_BF16, TOL_F32, np_f64, oracle_fwd, sync, to_dev, workload_inputs)
-from helpers import rel_l2
+from gpu_common import (TOL_BF16, TOL_F32, TOL_MAXABS, np_f64, oracle_fwd, sync, to_dev, workload_inputs)
+from helpers import rel_l2, scaled_max_abs, worst_lead_block, worst_token_block
 from linear_attention_06_amd import gdn
 from linear_attention_06_amd.inputs import WORKLOADS, make_inputs, slow_decay
 
@@ -33,6 +33,24 @@ def assert_close(x, ref, tol, what):
     assert err <= tol, "%s rel-L2 %.3e > %.0e" % (what, err, tol)
 
 
+def assert_local(x, ref, tol, what, nlead=None):
+    """Localised gates on a full-size tensor: the whole-tensor bound must also hold on every
+    (b, 64-token chunk, h) block of a token tensor [B, T, H, D] (nlead None), or on every
+    block over the first nlead axes of a state or summary tensor; and the pages' scaled
+    max-abs check. One zeroed or garbage block of a 32K output is 1/16384 of the tensor and
+    would pass the whole-tensor bound."""
+    if nlead is None:
+        err, at = worst_token_block(x, ref)
+        where = "(b, chunk, h)"
+    else:
+        err, at = worst_lead_block(x, ref, nlead)
+        where = "block"
+    sma = scaled_max_abs(x, ref)
+    print("%s worst %s rel-L2 %.3e at %s; scaled max-abs %.3e" % (what, where, err, at, sma))
+    assert err <= tol, "%s worst %s rel-L2 %.3e at %s > %.0e" % (what, where, err, at, tol)
+    assert sma <= TOL_MAXABS, "%s scaled max-abs %.3e > %.0e" % (what, sma, TOL_MAXABS)
+
+
 # ------------------------------------------------------------------ full workloads
 def test_tiny_f32_matches_oracle():
     inp = workload_inputs("tiny_f32")
@@ -49,7 +67,9 @@ def test_stateless_8k_matches_oracle():
     inp = workload_inputs("stateless_8k")
     o_ref, _ = oracle_fwd("stateless_8k")
     o, _ = run_fwd(inp, want_state=False)
-    assert_close(np_f64(o), o_ref, TOL_BF16, "stateless_8k o")
+    on = np_f64(o)
+    assert_close(on, o_ref, TOL_BF16, "stateless_8k o")
+    assert_local(on, o_ref, TOL_BF16, "stateless_8k o")
 
 
 @pytest.mark.parametrize("d,io", [(64, "bf16"), (128, "f32")], ids=["bf16_d64", "f32_d128"])
@@ -79,8 +99,11 @@ def test_stateful_32k_matches_oracle():
     inp = workload_inputs("stateful_32k")
     o_ref, hT_ref = oracle_fwd("stateful_32k")
     o, hT = run_fwd(inp)
-    assert_close(np_f64(o), o_ref, TOL_BF16, "stateful_32k o")
-    assert_close(np_f64(hT), hT_ref, TOL_BF16, "stateful_32k hT")
+    on, hn = np_f64(o), np_f64(hT)
+    assert_close(on, o_ref, TOL_BF16, "stateful_32k o")
+    assert_close(hn, hT_ref, TOL_BF16, "stateful_32k hT")
+    assert_local(on, o_ref, TOL_BF16, "stateful_32k o")
+    assert_local(hn, hT_ref, TOL_BF16, "stateful_32k hT", nlead=2)
 
 
 def test_segmented_32k_matches_oracle_and_unsplit_run():
@@ -101,6 +124,11 @@ def test_segmented_32k_matches_oracle_and_unsplit_run():
     assert_close(np_f64(o), o_ref, TOL_BF16, "segmented o")
     assert_close(np_f64(hT), hT_ref, TOL_BF16, "segmented hT")
     assert_close(np_f64(hT_c), hT_ref, TOL_BF16, "combined hT")
+    assert_local(np_f64(M), M_ref, TOL_BF16, "segment M", nlead=3)
+    assert_local(np_f64(S), S_ref, TOL_BF16, "segment S", nlead=3)
+    assert_local(np_f64(H_in), Hin_ref, TOL_BF16, "H_in", nlead=3)
+    assert_local(np_f64(o), o_ref, TOL_BF16, "segmented o")
+    assert_local(np_f64(hT), hT_ref, TOL_BF16, "segmented hT", nlead=2)
     o_full, hT_full = run_fwd(inp)
     assert_close(np_f64(o), np_f64(o_full), TOL_BF16, "segmented vs unsplit o")
     assert_close(np_f64(hT), np_f64(hT_full), TOL_BF16, "segmented vs unsplit hT")
@@ -143,6 +171,8 @@ def test_padded_8k_matches_oracle_and_is_bit_exact():
     on = np_f64(o)
     assert_close(on[:, :n], o_ref[:, :n], TOL_BF16, "padded o (valid tokens)")
     assert_close(np_f64(hT), hT_ref, TOL_BF16, "padded hT")
+    assert_local(on[:, :n], o_ref[:, :n], TOL_BF16, "padded o (valid tokens)")
+    assert_local(np_f64(hT), hT_ref, TOL_BF16, "padded hT", nlead=2)
     # (i) padded outputs are +0.0, bitwise
     pad_bits = o[:, n:].contiguous().view(torch.int16)
     assert int(torch.count_nonzero(pad_bits)) == 0
