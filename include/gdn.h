@@ -106,6 +106,26 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * gdn_chunk_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * and results, without a workspace argument. The chunk records live in a static device
+ * array of 64 MiB that every GPU loading the library holds until the process ends; its
+ * device address is looked up once per device, on the first call made with that device
+ * current. The call allocates nothing and calls no allocating routine. A problem whose
+ * records exceed 64 MiB returns GDN_EWORKSPACE before anything is enqueued (the stateless
+ * 8K workload, B = 1, T = 8192, H = 32, dk = dv = 128 on the matrix-core path, needs
+ * 52 MiB); use gdn_chunk_fwd with a workspace for larger problems. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams, or host
+ * threads without ordering) race and give undefined results; calls on one stream are
+ * ordered. Nothing in the array has to start at zero (each call writes every record it
+ * reads).
+ */
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* h0,
+                                 void* o, float* hT, void* stream);
+
+/*
  * Forward with the layer's input prologue fused into the chunk prepare pass
  * (PR #1035, section "What does this PR do": each rank projects Q/K/V/B/A and
  * runs the Gated DeltaNet on them; issue #320's gradient checks name the A_log

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/gdn.h"
@@ -161,6 +162,62 @@ gdn_status run_state(const gdn_problem& p, const gdn::StateArgs& a, hipStream_t 
     return e == hipSuccess ? GDN_OK : hip_fail(e, "state kernel launch");
 }
 
+gdn_status check_fwd_args(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, const void* o) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+    if (tokens && (!q || !k || !v || !g || !beta || !o))
+        return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+    return GDN_OK;
+}
+
+// The forward on a checked problem with a workspace of at least pl.bytes.
+gdn_status run_fwd(const gdn_problem& p, const Plan& pl, const void* q, const void* k, const void* v,
+                   const float* g, const float* beta, const float* h0, void* o, float* hT, void* ws,
+                   hipStream_t s) {
+    if (p.B == 0) return GDN_OK;
+    const gdn::Workspace w = carve(pl, ws);
+    gdn_status st = run_prep(p, pl, q, k, g, beta, w, s);
+    if (st != GDN_OK) return st;
+    gdn::StateArgs a = state_args(p, pl, q, k, v, w);
+    a.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+    a.s_init = h0;
+    a.o = o;
+    a.s_out = hT;
+    a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+    return run_state(p, a, s);
+}
+
+// Chunk records of gdn_chunk_fwd_noalloc: a static device array, one copy per GPU that
+// loads the library, held until the process ends. Nothing in it has to start at zero:
+// the prepare pass writes every record the state pass reads. In host code the array's
+// name is not its device address; the address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in scratch_ptr.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+gdn_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256)
+            return fail(GDN_EHIP, "static scratch has no 256-byte aligned device address");
+        scratch_ptr[dev] = ptr;
+    }
+    *out = scratch_ptr[dev];
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,26 +252,33 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
                          const float* g, const float* beta, const float* h0, void* o, float* hT,
                          void* ws, size_t ws_bytes, void* stream) {
     try {
-        gdn_status st = check_problem(p);
+        gdn_status st = check_fwd_args(p, q, k, v, g, beta, o);
         if (st != GDN_OK) return st;
-        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
-        if (tokens && (!q || !k || !v || !g || !beta || !o))
-            return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
         const Plan pl = make_plan(*p, false);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
-        if (p->B == 0) return GDN_OK;
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        const gdn::Workspace w = carve(pl, ws);
-        st = run_prep(*p, pl, q, k, g, beta, w, s);
+        return run_fwd(*p, pl, q, k, v, g, beta, h0, o, hT, ws, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* h0, void* o, float* hT,
+                                 void* stream) {
+    try {
+        gdn_status st = check_fwd_args(p, q, k, v, g, beta, o);
         if (st != GDN_OK) return st;
-        gdn::StateArgs a = state_args(*p, pl, q, k, v, w);
-        a.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
-        a.s_init = h0;
-        a.o = o;
-        a.s_out = hT;
-        a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
-        return run_state(*p, a, s);
+        const Plan pl = make_plan(*p, false);
+        if (pl.bytes > kScratchBytes)
+            return fail(GDN_EWORKSPACE,
+                        "the problem needs %zu bytes of chunk records; the static scratch holds %zu "
+                        "(use gdn_chunk_fwd with a workspace)", pl.bytes, kScratchBytes);
+        if (p->B == 0) return GDN_OK;
+        void* ws = nullptr;
+        st = scratch_on_current_device(&ws);
+        if (st != GDN_OK) return st;
+        return run_fwd(*p, pl, q, k, v, g, beta, h0, o, hT, ws, static_cast<hipStream_t>(stream));
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

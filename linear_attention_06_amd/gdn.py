@@ -23,7 +23,7 @@ CHUNK = 64
 
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
-           "gdn_chunk_fwd", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
            "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d",
            "gdn_gated_rmsnorm",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
@@ -64,6 +64,7 @@ def lib():
         L.gdn_chunk_fwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
         L.gdn_segment_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
         L.gdn_chunk_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_chunk_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_chunk_fwd_prologue.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                              vp, sz, vp]
         L.gdn_chunk_fwd_prologue_qkv.argtypes = [pp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
@@ -76,7 +77,7 @@ def lib():
         L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd",
+        for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc",
                      "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
                      "gdn_chunk_fwd_varlen",
                      "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d", "gdn_gated_rmsnorm",
@@ -179,6 +180,21 @@ def gdn_chunk_fwd(q, k, v, g, beta, h0=None, valid_len=None, o=None, hT=None, wa
     _check(lib().gdn_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_chunk_fwd")
+    return o, hT
+
+
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, h0, o, hT=None, valid_len=None, stream=None):
+    """gdn_chunk_fwd without a workspace: the library's static 64 MiB scratch holds the
+    chunk records. The caller passes every output (o, and hT or None); nothing is
+    allocated here or in the library. Calls that overlap on one GPU race."""
+    _io_checks(q, k, v, g, beta)
+    _dev(h0, "h0", torch.float32)
+    _dev(o, "o", v.dtype)
+    _dev(hT, "hT", torch.float32)
+    p = problem(q, v, valid_len)
+    _check(lib().gdn_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                       _ptr(h0), _ptr(o), _ptr(hT), _stream(stream)),
+           "gdn_chunk_fwd_noalloc")
     return o, hT
 
 

@@ -226,3 +226,17 @@ def test_layer_step_argument_checks():
     assert norm(o=None) == gdn.GDN_EINVAL
     assert norm(rows=-1) == gdn.GDN_EINVAL
     assert norm(rows=0) == gdn.GDN_OK
+
+
+def test_noalloc_forward_rejects_oversized_problems_before_any_hip_call():
+    """The static scratch of gdn_chunk_fwd_noalloc holds 64 MiB of chunk records; the
+    stateful 32K workload needs 208 MiB and is refused before anything touches the GPU."""
+    p = P(B=1, T=32768, H=32, Hqk=16, dk=128, dv=128, io_dtype=gdn.GDN_BF16)
+    dummy = ctypes.c_void_p(256)
+    st = gdn.lib().gdn_chunk_fwd_noalloc(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, None, dummy,
+                                         None, None)
+    assert st == gdn.GDN_EWORKSPACE
+    assert "64" in gdn.lib().gdn_last_error().decode() or "scratch" in gdn.lib().gdn_last_error().decode()
+    # a problem of no batch rows is a no-op that needs no device
+    assert gdn.lib().gdn_chunk_fwd_noalloc(ctypes.byref(P(B=0)), None, None, None, None, None, None, None,
+                                           None, None) == gdn.GDN_OK
