@@ -32,13 +32,15 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 WORKLOAD = "stateful_32k"
 
 
-def algorithmic_bytes(B, T, H, Hqk, dk, dv, io_bytes=2, stateful=True):
+def algorithmic_bytes(B, T, H, Hqk, dk, dv, io_bytes=2, stateful=True, h0=None, hT=None):
     """Bytes the method must move: q, k (Hqk heads), v, g, beta read once, o written
-    once, h0 read and hT written once."""
+    once, h0 read and hT written once (each when present; `stateful` sets both)."""
+    h0 = stateful if h0 is None else h0
+    hT = stateful if hT is None else hT
     qk = 2 * B * T * Hqk * dk * io_bytes
     vo = 2 * B * T * H * dv * io_bytes
     gb = 2 * B * T * H * 4
-    st = (2 if stateful else 0) * B * H * dk * dv * 4
+    st = ((1 if h0 else 0) + (1 if hT else 0)) * B * H * dk * dv * 4
     return qk + vo + gb + st
 
 
@@ -47,6 +49,17 @@ def flops_per_token_head(C=64, d=128):
     triangles, 2 x C d), That X and P U (lower triangles, 2 x C d), K S, Q S and
     K^T V'' (3 x 2 d^2), ignoring the O(C^2) solve."""
     return 5 * C * d + 6 * d * d
+
+
+def dense_flops_per_token_head(C=64, d=128):
+    """The same products counted as dense 64-token tiles: A and P 2 x 2 C d, That X and
+    P U 2 x 2 C d, K S, Q S and K^T V'' 3 x 2 d^2 (180,224 at C = 64, d = 128)."""
+    return 8 * C * d + 6 * d * d
+
+
+def roofline_of(nbytes, ms):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"algorithmic_bytes": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gdn_state_and_prepare_stateful_32k_hbm_traffic.md")
@@ -67,6 +80,72 @@ def recorded_traffic(kernel):
             if kv.get("kernel") == kernel and kv.get("source_sha256_prefix") == sha:
                 return int(kv["traffic_bytes_per_launch"])
     return None
+
+
+def recorded_step_traffic():
+    """HBM bytes of one gdn_chunk_fwd step (prepare + state pass) from the committed
+    counter summary, or None when either kernel's figure is for another source version."""
+    a, b = recorded_traffic("prepare"), recorded_traffic("state")
+    return None if a is None or b is None else a + b
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_one_thread(workloads, make_inputs):
+    """The oracle on one value head of the stateless 8K workload (one (row, head) unit, so
+    one thread), repeated for about 3 s: tokens/s of the whole 32-head workload per core."""
+    import oracle
+
+    w = workloads["stateless_8k"]
+    inp = make_inputs(w)
+    q, k, v, g, beta, _ = inp.f64()
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gdn_fwd(q[:, :, :1], k[:, :, :1], v[:, :, :1], g[:, :, :1], beta[:, :, :1], None)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= 3.0:
+            break
+    return {"value": runs * w.B * w.T / w.H / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d run(s) of 1 of %d heads x %d tokens (stateless 8K), %.1f s" % (runs, w.H, w.T, dt)}
+
+
+def measured_peaks(dev, stream):
+    """Beside the spec peaks: a plain device copy of 1 GiB (HIP events, 10 copies) and a
+    dense bf16 GEMM of 8192^3 through torch.matmul (5 products)."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    a_ = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    b_ = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+
+    def timed(fn, reps):
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_copy = timed(lambda: dst.copy_(src), 10)
+    ms_mm = timed(lambda: torch.matmul(a_, b_), 5)
+    return {"copy_gbs": 2 * n / (ms_copy * 1e-3) / 1e9, "copy_bytes_read_and_written": 2 * n,
+            "bf16_gemm_tflops": 2 * 8192 ** 3 / (ms_mm * 1e-3) / 1e12, "gemm": "torch.matmul bf16 8192^3",
+            "spec_hbm_gbs": HBM_PEAK_GBS, "spec_bf16_tflops": BF16_PEAK_TFLOPS}
 
 
 def cpu_baseline(inp, budget_s=30.0, min_s=10.0):
@@ -101,7 +180,8 @@ def cpu_baseline(inp, budget_s=30.0, min_s=10.0):
     used = min(threads, w.B * heads)   # the oracle runs one (row, head) unit per thread
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": "%d run(s) of %d of %d heads x %d tokens (B=%d), fp64 token loop, %.1f s"
-                      % (runs, heads, w.H, w.T, w.B, dt)}
+                      % (runs, heads, w.H, w.T, w.B, dt),
+            "cpu_model": cpu_model(), "host_threads": threads}
 
 
 def segmented_timing(gdn, q, k, v, g, beta, h0, stream, timed):
@@ -135,6 +215,8 @@ def segmented_timing(gdn, q, k, v, g, beta, h0, stream, timed):
     res = {"segments": P, "seg_len": seg_len, "summary_ms": timed(summary, 5),
            "combine_ms": timed(combine, 5), "apply_ms": timed(apply, 5), "step_ms": timed(whole, 5)}
     res["tokens_per_s"] = B * T / (res["step_ms"] * 1e-3)
+    # the method's own bytes for the whole sequence (those of the unsplit forward)
+    res["roofline"] = roofline_of(algorithmic_bytes(B, T, H, q.shape[2], p.dk, p.dv), res["step_ms"])
     return res
 
 
@@ -299,7 +381,9 @@ def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
             gdn.gdn_chunk_fwd(q, k, v, g, beta, None, valid_len=vl, o=o, hT=hT, ws=ws, stream=stream)
 
         ms = timed(step, 10)
-        out[name] = {"B": w.B, "T": w.T, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3)}
+        out[name] = {"B": w.B, "T": w.T, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+                     "roofline": roofline_of(algorithmic_bytes(w.B, w.T, w.H, w.Hqk, w.dk, w.dv, h0=False,
+                                                               hT=True), ms)}
         if name == "padded_8k":
             # the same rows packed without their padding, as variable-length sequences
             L = int(inp.valid_len[0])
@@ -487,6 +571,10 @@ def main():
         "config": {"workload": WORKLOAD, "B": w.B, "T": w.T, "H": w.H, "Hqk": w.Hqk, "dk": w.dk,
                    "dv": w.dv, "chunk": 64, "h0": "0.1*N(0,1)", "kernel_path": path},
         "mfma_util_pct": 100.0 * flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "mfma_util_dense_pct": 100.0 * dense_flops_per_token_head(64, w.dk) * tokens * w.H / (ms * 1e-3)
+                               / (BF16_PEAK_TFLOPS * 1e12),
+        "step_roofline": dict(roofline_of(alg_bytes, ms), traffic=recorded_step_traffic(),
+                              traffic_unit="bytes/step"),
         "algorithmic_gbs_per_step": alg_bytes / (ms * 1e-3) / 1e9,
         "kernels_ms": {"prepare": prep_ms, "state": state_ms},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved_gbs,
@@ -505,8 +593,11 @@ def main():
         line["backward_8k"] = backward_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
         line["layer_ops"] = layer_ops_timing(gdn, dev, stream, timed)
         line["vector_path"] = vector_path_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
+    if not args.no_extra:
+        line["measured_peaks"] = measured_peaks(dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
+        line["cpu_baseline"]["one_thread_stateless_8k"] = cpu_one_thread(WORKLOADS, make_inputs)
     print(json.dumps(line))
 
 

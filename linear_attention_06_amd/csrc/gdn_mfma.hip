@@ -790,18 +790,25 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         uint16_t* oout = static_cast<uint16_t*>(a.o) + rs.start * vo_row;
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(oout, rs.extent * vo_row * 2);
         const uint32_t ooff = static_cast<uint32_t>((l16 * vo_row + h * ncols + col0 + 4 * g4) * 2);
-        // L2 prefetch, kPrefetch chunks ahead of the chain: the column tiles of a head
-        // split the 128-byte lines of its chunk operands between them (lanes 0..31: k and
-        // q rows, 32..47: v rows, 48..59: That and P records, 60..63: decay factors);
-        // the data lands in a scratch LDS word per lane that nothing reads.
+        // L2 prefetch, kPrefetch chunks ahead of the chain: the workgroups that read the
+        // same lines split them, so that each line is fetched once per XCD (every line
+        // costs an L1-to-L2 request slot for a full HBM latency). Lanes 0..31: the 256
+        // lines of a chunk's k and q rows, split over the rep x tiles workgroups of the
+        // query/key head (16 each when two value heads of 8 tiles share it); 32..47: v
+        // rows, 48..59: That and P records, 60..63: decay factors, split over the tiles of
+        // the value head. The data lands in a scratch LDS word per lane that nothing reads.
         constexpr int kPrefetch = 4;
         const unsigned char* pf_base;
         int64_t pf_stride;      // bytes per chunk
         int pf_row = -1;        // token row inside the chunk for q/k/v lines, else -1
+        bool pf_lane = true;    // this lane has a line to fetch
         {
             const int64_t bT = rs.start;
+            const int qk_share = rep * tiles, qk_rank = (kk % rep) * tiles + tile;
+            const int kq_lanes = min(32, (256 + qk_share - 1) / qk_share);
             if (lane < 32) {
-                const int lam = 32 * tile + lane;
+                const int lam = kq_lanes * qk_rank + lane;
+                pf_lane = lane < kq_lanes && lam < 256;
                 const uint16_t* src = static_cast<const uint16_t*>(lam < 128 ? a.k : a.q);
                 pf_row = (lam & 127) >> 1;
                 pf_base = reinterpret_cast<const unsigned char*>(src + bT * qk_row + hq * DK + 64 * (lam & 1));
@@ -836,7 +843,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 p = pf_base + static_cast<int64_t>(c) * pf_stride;
             }
             const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pf_lds));
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(p) : "memory", "m0");
+            if (pf_lane)
+                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(p) : "memory", "m0");
         };
         // a row or segment without chunks has no line to prefetch (the clamped token
         // index would fall before the row)
