@@ -281,8 +281,25 @@ def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
         gdn.gdn_chunk_bwd(q, k, v, g, beta, None, d_o, ws=ws, stream=stream)
 
     ms = timed(step, 3)
-    return {"workload": "stateless_8k", "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
-            "workspace_bytes": int(ws.numel())}
+    out = {"workload": "stateless_8k", "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+           "workspace_bytes": int(ws.numel())}
+
+    # the same gradients through the segment calls (4 segments of 2048): apply's backward,
+    # the combine's, then the summaries' accumulated onto apply's
+    L = 2048
+    M, S, seg_ws = gdn.gdn_segment_summary(q, k, v, g, beta, L)
+    H_in, _, _ = gdn.gdn_summary_combine(M, S, None)
+    bws = gdn.workspace(gdn.gdn_segment_bwd_workspace(p, L), dev)
+
+    def seg_step():
+        *grads, dH_in = gdn.gdn_apply_initial_state_bwd(q, k, v, g, beta, H_in, L, d_o, ws=bws, stream=stream)
+        dM, dS, _ = gdn.gdn_summary_combine_bwd(M, H_in, dH_in, stream=stream)
+        gdn.gdn_segment_summary_bwd(q, k, v, g, beta, L, dM, dS, grads=grads, ws=bws, stream=stream)
+
+    ms_seg = timed(seg_step, 2)
+    out["segments_4x2048"] = {"ms_per_step": ms_seg, "workspace_bytes": int(bws.numel()),
+                              "note": "apply, combine and summary backward composed"}
+    return out
 
 
 def layer_ops_timing(gdn, dev, stream, timed):

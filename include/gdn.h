@@ -284,6 +284,62 @@ gdn_status gdn_apply_initial_state(const gdn_problem* p, int32_t seg_len,
                                    const float* H_in, void* o, float* hT,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Backward through the segment calls. PR #1035's p2p mode passes the gradient of the
+ * state backwards across its autograd boundary between ranks; here the three forward
+ * calls each have a reverse, and composed they give the gradient of the unsplit forward:
+ *   1. gdn_apply_initial_state_bwd: each segment's backward from its incoming state, from
+ *      the output gradient d_o of its tokens (and, for the last segment, dhT): the inputs'
+ *      gradients of that segment and dH_in, the gradient of every incoming state;
+ *   2. gdn_summary_combine_bwd: from dH_in (and the combine's own hT gradient) to dM, dS
+ *      and dh0;
+ *   3. gdn_segment_summary_bwd with accumulate = 1: adds the summaries' share, through
+ *      dM and dS, to the inputs' gradients of step 1.
+ * All gradients are fp32 with the layouts of their forward tensors (dq, dk [B,T,Hqk,dk];
+ * dv [B,T,H,dv]; dg, dbeta [B,T,H]; dH_in, dS [B,H,P,dk,dv]; dM [B,H,P,dk,dk]). These run
+ * the fp32 vector-ALU backward (the kernels of gdn_chunk_bwd) on every segment as its own
+ * sequence. Padded tokens (valid_len) get zero gradients. seg_len as gdn_segment_summary.
+ *
+ * Workspace of the two backward calls that take one, in bytes (contents undefined on entry).
+ */
+gdn_status gdn_segment_bwd_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes);
+
+/*
+ * Backward of gdn_apply_initial_state: segment p runs from H_in[b,h,p]; d_o [B,T,H,dv]
+ * (io dtype) is the gradient of all token outputs, dhT [B,H,dk,dv] (nullable: zero) that
+ * of the last segment's end state. Writes dq, dk, dv, dg, dbeta and dH_in (nullable).
+ */
+gdn_status gdn_apply_initial_state_bwd(const gdn_problem* p, int32_t seg_len,
+                                       const void* q, const void* k, const void* v,
+                                       const float* g, const float* beta, const float* H_in,
+                                       const void* d_o, const float* dhT,
+                                       float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                                       float* dH_in, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of gdn_summary_combine: M and H_in as the combine used and produced them,
+ * dH_in the gradient of H_in, dhT (nullable: zero) that of the combine's hT. With G the
+ * gradient of H_p (G = dhT for p = P - 1): dS[p] = G, dM[p] = G H_in[p]^T, and the
+ * gradient of H_{p-1} is M_p^T G + dH_in[p]; dh0 (nullable) receives that of H_{-1} = h0.
+ */
+gdn_status gdn_summary_combine_bwd(int32_t B, int32_t H, int32_t P, int32_t dk, int32_t dv,
+                                   const float* M, const float* H_in, const float* dH_in,
+                                   const float* dhT, float* dM, float* dS, float* dh0, void* stream);
+
+/*
+ * Backward of gdn_segment_summary: the gradients of sum(M dM) + sum(S dS) with respect to
+ * k, v, g, beta (dq receives zeros: the summaries do not read q). dM or dS NULL is a zero
+ * gradient. accumulate = 0 writes dq, dk, dv, dg, dbeta; accumulate = 1 adds to them.
+ * S is the segment's recurrence from a zero state and M its homogeneous transition (zero
+ * values, identity start); each is run backwards from its final-state gradient.
+ */
+gdn_status gdn_segment_summary_bwd(const gdn_problem* p, int32_t seg_len,
+                                   const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta,
+                                   const float* dM, const float* dS,
+                                   float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

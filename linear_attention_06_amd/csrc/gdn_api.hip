@@ -372,15 +372,45 @@ struct BwdPlan {
     size_t ckpt_off = 0, dqk_off = 0, dgb_off = 0, bytes = 0;
 };
 
-BwdPlan make_bwd_plan(const gdn_problem& p) {
+// ncols: the widest state the workspace serves (dv, or max(dv, dk) for the segment
+// summaries' backward, whose M pass has dk columns); seg_len: segment length (or T).
+BwdPlan make_bwd_plan(const gdn_problem& p, int ncols = -1, int64_t seg_len = -1) {
     BwdPlan pl;
-    pl.NT = (static_cast<int64_t>(p.T) + gdn::kChunk - 1) / gdn::kChunk;
-    const size_t bt = static_cast<size_t>(p.B) * p.T, tiles = static_cast<size_t>(p.dv / 16);
+    if (ncols < 0) ncols = p.dv;
+    const int64_t L = seg_len < 0 ? p.T : seg_len;
+    const int64_t P = L > 0 ? p.T / L : 0;
+    pl.NT = (L + gdn::kChunk - 1) / gdn::kChunk;   // chunks per row or segment
+    const size_t bt = static_cast<size_t>(p.B) * p.T, tiles = static_cast<size_t>(ncols / 16);
     pl.ckpt_off = 0;
-    pl.dqk_off = align256(static_cast<size_t>(p.B) * p.H * 8 * pl.NT * p.dk * p.dv * sizeof(float));
+    pl.dqk_off = align256(static_cast<size_t>(p.B) * (P > 0 ? P : 1) * p.H * 8 * pl.NT * p.dk * ncols * sizeof(float));
     pl.dgb_off = pl.dqk_off + align256(bt * p.H * tiles * 2 * p.dk * sizeof(float));
     pl.bytes = pl.dgb_off + align256(bt * p.H * tiles * 2 * sizeof(float));
     return pl;
+}
+
+gdn::BwdArgs bwd_args(const gdn_problem& p, const BwdPlan& pl, void* ws) {
+    char* base = static_cast<char*>(ws);
+    gdn::BwdArgs a;
+    a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.dk = p.dk; a.dv = p.dv;
+    a.NT = static_cast<int>(pl.NT);
+    a.q = a.k = a.v = a.d_o = nullptr;
+    a.g = a.beta = a.h0 = a.dhT = nullptr;
+    a.valid_len = p.valid_len;
+    a.ckpt = reinterpret_cast<float*>(base + pl.ckpt_off);
+    a.dqk_part = reinterpret_cast<float*>(base + pl.dqk_off);
+    a.dgb_part = reinterpret_cast<float*>(base + pl.dgb_off);
+    a.dq_out = a.dk_out = a.dv_out = a.dg_out = a.dbeta_out = a.dh0_out = nullptr;
+    a.P = 1; a.L = p.T;
+    a.dhT_per_segment = 0; a.h0_identity = 0; a.v_zero = 0; a.do_zero = 0; a.write_dv = 1; a.accumulate = 0;
+    return a;
+}
+
+gdn_status check_bwd_ws(const BwdPlan& pl, void* ws, size_t ws_bytes) {
+    if (pl.bytes == 0) return GDN_OK;
+    if (!ws) return fail(GDN_EWORKSPACE, "workspace is NULL, %zu bytes needed", pl.bytes);
+    if (ws_bytes < pl.bytes) return fail(GDN_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, pl.bytes);
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
+    return GDN_OK;
 }
 
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
@@ -402,24 +432,120 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
         if (tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
         const BwdPlan pl = make_bwd_plan(*p);
-        if (pl.bytes > 0) {
-            if (!ws) return fail(GDN_EWORKSPACE, "workspace is NULL, %zu bytes needed", pl.bytes);
-            if (ws_bytes < pl.bytes) return fail(GDN_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, pl.bytes);
-            if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
-        }
+        st = check_bwd_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
         if (p->B == 0) return GDN_OK;
-        char* base = static_cast<char*>(ws);
-        gdn::BwdArgs a;
-        a.B = p->B; a.T = p->T; a.H = p->H; a.Hqk = p->Hqk; a.dk = p->dk; a.dv = p->dv;
-        a.NT = static_cast<int>(pl.NT);
+        gdn::BwdArgs a = bwd_args(*p, pl, ws);
         a.q = q; a.k = k; a.v = v; a.d_o = d_o; a.g = g; a.beta = beta; a.h0 = h0; a.dhT = dhT;
-        a.valid_len = p->valid_len;
-        a.ckpt = reinterpret_cast<float*>(base + pl.ckpt_off);
-        a.dqk_part = reinterpret_cast<float*>(base + pl.dqk_off);
-        a.dgb_part = reinterpret_cast<float*>(base + pl.dgb_off);
         a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta; a.dh0_out = dh0;
         hipError_t e = gdn::launch_bwd(a, p->io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? GDN_OK : hip_fail(e, "backward kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_segment_bwd_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    int64_t P = 0;
+    st = check_segments(*p, seg_len, &P);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    *bytes = make_bwd_plan(*p, p->dv > p->dk ? p->dv : p->dk, seg_len).bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_apply_initial_state_bwd(const gdn_problem* p, int32_t seg_len, const void* q, const void* k,
+                                       const void* v, const float* g, const float* beta, const float* H_in,
+                                       const void* d_o, const float* dhT, float* dq, float* dk, float* dv,
+                                       float* dg, float* dbeta, float* dH_in, void* ws, size_t ws_bytes,
+                                       void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        int64_t P = 0;
+        st = check_segments(*p, seg_len, &P);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !v || !g || !beta || !H_in || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+            return fail(GDN_EINVAL, "q, k, v, g, beta, H_in, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        const BwdPlan pl = make_bwd_plan(*p, p->dv > p->dk ? p->dv : p->dk, seg_len);
+        st = check_bwd_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (!tokens) return GDN_OK;
+        gdn::BwdArgs a = bwd_args(*p, pl, ws);
+        a.P = static_cast<int>(P); a.L = seg_len;
+        a.q = q; a.k = k; a.v = v; a.d_o = d_o; a.g = g; a.beta = beta; a.h0 = H_in; a.dhT = dhT;
+        a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta; a.dh0_out = dH_in;
+        hipError_t e = gdn::launch_bwd(a, p->io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? GDN_OK : hip_fail(e, "apply backward kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_summary_combine_bwd(int32_t B, int32_t H, int32_t P, int32_t dk, int32_t dv, const float* M,
+                                   const float* H_in, const float* dH_in, const float* dhT, float* dM, float* dS,
+                                   float* dh0, void* stream) {
+    try {
+        if (B < 0 || H < 0 || P < 0) return fail(GDN_EINVAL, "B, H and P must be >= 0");
+        if (!head_dim_ok(dk) || !head_dim_ok(dv))
+            return fail(GDN_EUNSUPPORTED, "dk=%d, dv=%d: head dims must be 16, 32, 64 or 128", dk, dv);
+        if (B > 65535 || H > 65535) return fail(GDN_EUNSUPPORTED, "B or H exceeds 65535");
+        const bool work = static_cast<int64_t>(B) * H > 0;
+        if (work && P > 0 && (!M || !H_in || !dH_in || !dM || !dS))
+            return fail(GDN_EINVAL, "M, H_in, dH_in, dM and dS must be non-NULL");
+        if (!work) return GDN_OK;
+        gdn::ScanBwdArgs a{B, H, P, dk, dv, M, H_in, dH_in, dhT, dM, dS, dh0};
+        hipError_t e = gdn::launch_scan_bwd(a, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? GDN_OK : hip_fail(e, "combine backward kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_segment_summary_bwd(const gdn_problem* p, int32_t seg_len, const void* q, const void* k,
+                                   const void* v, const float* g, const float* beta, const float* dM,
+                                   const float* dS, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                                   int32_t accumulate, void* ws, size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        int64_t P = 0;
+        st = check_segments(*p, seg_len, &P);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !v || !g || !beta || !dq || !dk || !dv || !dg || !dbeta))
+            return fail(GDN_EINVAL, "q, k, v, g, beta, dq, dk, dv, dg and dbeta must be non-NULL");
+        const BwdPlan pl = make_bwd_plan(*p, p->dv > p->dk ? p->dv : p->dk, seg_len);
+        st = check_bwd_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (!tokens) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        gdn::BwdArgs a = bwd_args(*p, pl, ws);
+        a.P = static_cast<int>(P); a.L = seg_len;
+        a.q = q; a.k = k; a.v = v; a.d_o = v; a.g = g; a.beta = beta;
+        a.do_zero = 1; a.dhT_per_segment = 1;
+        a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta;
+        // S: the segment's recurrence from a zero state with final-state gradient dS (a NULL
+        // dS is a zero gradient; the pass then writes zeros unless accumulating)
+        if (dS || !accumulate) {
+            a.dhT = dS; a.accumulate = accumulate ? 1 : 0;
+            hipError_t e = gdn::launch_bwd(a, p->io_dtype == GDN_BF16, s);
+            if (e != hipSuccess) return hip_fail(e, "summary S backward kernel launch");
+        }
+        // M: the homogeneous recurrence (zero values) from I, final-state gradient dM; M has
+        // dk columns and does not depend on v
+        if (dM) {
+            gdn::BwdArgs m = a;
+            m.dv = p->dk; m.v_zero = 1; m.h0_identity = 1; m.write_dv = 0;
+            m.dhT = dM;
+            m.accumulate = 1;   // onto the S pass's gradients, or the caller's when accumulating
+            hipError_t e = gdn::launch_bwd(m, p->io_dtype == GDN_BF16, s);
+            if (e != hipSuccess) return hip_fail(e, "summary M backward kernel launch");
+        }
+        return GDN_OK;
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

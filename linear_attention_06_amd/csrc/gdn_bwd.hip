@@ -65,6 +65,26 @@ __device__ __forceinline__ float col_sum(float x) {
     return x;
 }
 
+// Token range of grid row bz: segment p = bz % P of batch row b = bz / P, tokens p L ..
+// p L + L - 1 of the row, valid up to valid_len[b] (P = 1, L = T: the whole row).
+__device__ __forceinline__ RowSpan bwd_span(const BwdArgs& a, int bz) {
+    const int b = bz / a.P, p = bz % a.P;
+    int64_t n = a.T;
+    if (a.valid_len) {
+        n = a.valid_len[b];
+        n = n < 0 ? 0 : (n > a.T ? a.T : n);
+    }
+    const int64_t s = static_cast<int64_t>(p) * a.L;
+    n -= s;
+    n = n < 0 ? 0 : (n > a.L ? a.L : n);
+    return RowSpan{static_cast<int64_t>(b) * a.T + s, n, a.L};
+}
+// Index of the (row, segment, head) state block in a [B,H,P,dk,dv] array.
+__device__ __forceinline__ int64_t seg_state(const BwdArgs& a, int bz, int h) {
+    const int b = bz / a.P, p = bz % a.P;
+    return (static_cast<int64_t>(b) * a.H + h) * a.P + p;
+}
+
 // Chunk operands in LDS (fp32): K, optionally Q, the tile's columns of V and of the
 // output gradient, e^g and beta; padded tokens read as zero (e^g as one).
 template <typename IO, int DK, bool kQ>
@@ -110,8 +130,8 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<IO, DK, kQ, NTH>& R, const
         const int e = tid + NTH * m, r = e / 16, c = e % 16;
         const int64_t tok = t0 + r < rs.valid ? t0 + r : 0;
         const int64_t idx = ((rs.start + tok) * a.H + h) * a.dv + col0 + c;
-        R.v[m] = ld_in(v, idx);
-        if (kQ) R.d[m] = ld_in(d, idx);
+        R.v[m] = a.v_zero ? 0.f : ld_in(v, idx);
+        if (kQ) R.d[m] = a.do_zero ? 0.f : ld_in(d, idx);
     }
     const int64_t tok = t0 + (tid & 63) < rs.valid ? t0 + (tid & 63) : 0;
     const int64_t gi = (rs.start + tok) * a.H + h;
@@ -166,12 +186,15 @@ __global__ __launch_bounds__(16 * TPC) void bwd_ckpt(BwdArgs a) {
     const int col0 = 16 * blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, c = tid / TPC, i = tid % TPC;
-    const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
+    const RowSpan rs = bwd_span(a, b);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    const int64_t sb = seg_state(a, b, h);
     float S[RJ];
 #pragma unroll
-    for (int j = 0; j < RJ; ++j)
-        S[j] = a.h0 ? a.h0[(bh * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
+    for (int j = 0; j < RJ; ++j) {
+        const int r = i + TPC * j;
+        S[j] = a.h0_identity ? (r == col0 + c ? 1.f : 0.f) : (a.h0 ? a.h0[(sb * DK + r) * a.dv + col0 + c] : 0.f);
+    }
     ChunkRegs<IO, DK, false, NTH> R;
     if (a.NT > 0) fetch_chunk(R, a, rs, h, hq, col0, 0, tid);
     for (int n = 0; n < a.NT; ++n) {
@@ -203,13 +226,21 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     const int tile = blockIdx.x, col0 = 16 * tile, h = blockIdx.y, b = blockIdx.z;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, c = tid / TPC, i = tid % TPC;
-    const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
+    const RowSpan rs = bwd_span(a, b);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    const int64_t sb = seg_state(a, b, h);
+    // the final-state gradient: per segment, or the row's for its last segment only
+    const float* dhT = a.dhT;
+    int64_t dsb = sb;
+    if (!a.dhT_per_segment) {
+        dsb = static_cast<int64_t>(b / a.P) * a.H + h;
+        if (b % a.P != a.P - 1) dhT = nullptr;
+    }
 
     float dS[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j)
-        dS[j] = a.dhT ? a.dhT[(bh * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
+        dS[j] = dhT ? dhT[(dsb * DK + i + TPC * j) * a.dv + col0 + c] : 0.f;
 
     // the checkpoint of 8-token piece m (the state before token 8 m), loaded one piece ahead
     const auto load_ck = [&](int m, float (&x)[RJ]) {
@@ -275,7 +306,10 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                 z = col_sum<TPC>(z);
                 ms = col_sum<TPC>(ms);
                 // the tail of the last chunk is past the row
-                if (i == 0 && u < nwrite) dv_s[uu * sdv] = valid ? bt * z : 0.f;
+                if (a.write_dv && i == 0 && u < nwrite) {
+                    const float x = valid ? bt * z : 0.f;
+                    dv_s[uu * sdv] = a.accumulate ? dv_s[uu * sdv] + x : x;
+                }
                 // dk's column terms: M beta (v - e^g w) - e^g beta z S_{t-1}
                 const float am = bt * (vc - eg * w[uu]), bz = eg * bt * z;
 #pragma unroll
@@ -312,7 +346,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     }
     if (a.dh0_out) {
 #pragma unroll
-        for (int j = 0; j < RJ; ++j) a.dh0_out[(bh * DK + i + TPC * j) * a.dv + col0 + c] = dS[j];
+        for (int j = 0; j < RJ; ++j) a.dh0_out[(sb * DK + i + TPC * j) * a.dv + col0 + c] = dS[j];
     }
 }
 
@@ -341,8 +375,8 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
         float* dk = a.dk_out + (row * a.Hqk + hq) * DK + r;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            dq[x] = sq[x];
-            dk[x] = sk[x];
+            dq[x] = a.accumulate ? dq[x] + sq[x] : sq[x];
+            dk[x] = a.accumulate ? dk[x] + sk[x] : sk[x];
         }
     }
     for (int hh = threadIdx.x; hh < a.H; hh += 256) {
@@ -352,8 +386,8 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
             sg += part[2 * tl];
             sb += part[2 * tl + 1];
         }
-        a.dg_out[row * a.H + hh] = sg;
-        a.dbeta_out[row * a.H + hh] = sb;
+        a.dg_out[row * a.H + hh] = a.accumulate ? a.dg_out[row * a.H + hh] + sg : sg;
+        a.dbeta_out[row * a.H + hh] = a.accumulate ? a.dbeta_out[row * a.H + hh] + sb : sb;
     }
 }
 
@@ -363,7 +397,7 @@ constexpr int kTpc(int dk) { return dk >= 32 ? 32 : 16; }
 
 template <typename IO>
 hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
+    const dim3 grid(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B * a.P));
     void* args[] = {const_cast<BwdArgs*>(&a)};
     const void *f1 = nullptr, *f2 = nullptr, *f3 = nullptr;
     unsigned nth = 256;

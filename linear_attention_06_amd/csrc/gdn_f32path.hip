@@ -385,6 +385,83 @@ __global__ __launch_bounds__(256) void affine_scan(ScanArgs a) {
     }
 }
 
+// Reverse of the prefix combine, one block per (16 columns, h, b): the gradient G of the
+// running state (dk x 16, in LDS) from dhT (or 0); for p = P-1 .. 0 it is stored as dS_p,
+// then G <- M_p^T G + dH_in_p; the last G is dh0. Thread (i, half) computes row i of
+// M_p^T G for 8 columns, reading column i of M_p.
+template <int DKT>
+__global__ __launch_bounds__(256) void affine_scan_rev(ScanBwdArgs a) {
+    constexpr int BV = 16;
+    constexpr int dk = DKT;
+    __shared__ float g_s[DKT * BV];
+    const int col0 = blockIdx.x * BV;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int dv = a.dv;
+    const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    const int64_t tile = static_cast<int64_t>(dk) * dv;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < dk * BV; e += 256) {
+        const int i = e / BV, c = e % BV;
+        g_s[e] = a.dhT ? a.dhT[bh * tile + static_cast<int64_t>(i) * dv + col0 + c] : 0.f;
+    }
+    __syncthreads();
+    const bool active = tid < 2 * dk;
+    const int i = tid >> 1, c0 = 8 * (tid & 1);
+    const int64_t out0 = static_cast<int64_t>(i) * dv + col0 + c0;
+    for (int p = a.P - 1; p >= 0; --p) {
+        const int64_t blk = bh * a.P + p;
+        float acc[8];
+        if (active) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                a.dS[blk * tile + out0 + c] = g_s[i * BV + c0 + c];
+                acc[c] = a.dH_in[blk * tile + out0 + c];
+            }
+            const float* mcol = a.M + blk * static_cast<int64_t>(dk) * dk + i;
+            for (int l = 0; l < dk; ++l) {
+                const float m = mcol[static_cast<int64_t>(l) * dk];   // M_p[l][i]
+                const float* gr = g_s + l * BV + c0;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c] += m * gr[c];
+            }
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) g_s[i * BV + c0 + c] = acc[c];
+        }
+        __syncthreads();
+    }
+    if (a.dh0 && active) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a.dh0[bh * tile + out0 + c] = g_s[i * BV + c0 + c];
+    }
+}
+
+// dM_p = dS_p H_in_p^T, one block per (16 rows of dM, (b, h, p)): the block's 16 rows of
+// dS_p and all of H_in_p in LDS (fp32), thread (r, j0) sums over the dv columns for the
+// outputs (r, j0 + 16 u).
+__global__ __launch_bounds__(256) void summary_outer(ScanBwdArgs a) {
+    __shared__ float sm[(16 + 128) * 129];
+    const int dk = a.dk, dv = a.dv, pitch = dv + 1;
+    float* ds_s = sm;                 // [16][dv + 1]
+    float* hi_s = sm + 16 * pitch;    // [dk][dv + 1]
+    const int r0 = 16 * blockIdx.y;
+    const int64_t blk = blockIdx.x;   // (b h) P + p
+    const float* dS = a.dS + blk * static_cast<int64_t>(dk) * dv;
+    const float* Hi = a.H_in + blk * static_cast<int64_t>(dk) * dv;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < 16 * dv; e += 256) ds_s[(e / dv) * pitch + e % dv] = dS[static_cast<int64_t>(r0) * dv + e];
+    for (int e = tid; e < dk * dv; e += 256) hi_s[(e / dv) * pitch + e % dv] = Hi[e];
+    __syncthreads();
+    const int r = tid >> 4, j0 = tid & 15;
+    for (int j = j0; j < dk; j += 16) {
+        float acc = 0.f;
+        for (int c = 0; c < dv; ++c) acc += ds_s[r * pitch + c] * hi_s[j * pitch + c];
+        a.dM[blk * static_cast<int64_t>(dk) * dk + static_cast<int64_t>(r0 + r) * dk + j] = acc;
+    }
+}
+
 template <typename IO>
 hipError_t prep_dispatch(const PrepArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.NT));
@@ -443,6 +520,26 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
         default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+}
+
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s) {
+    void* args[] = {const_cast<ScanBwdArgs*>(&a)};
+    const void* fn = nullptr;
+    switch (a.dk) {
+        case 16: fn = reinterpret_cast<const void*>(&affine_scan_rev<16>); break;
+        case 32: fn = reinterpret_cast<const void*>(&affine_scan_rev<32>); break;
+        case 64: fn = reinterpret_cast<const void*>(&affine_scan_rev<64>); break;
+        case 128: fn = reinterpret_cast<const void*>(&affine_scan_rev<128>); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H),
+                                            static_cast<unsigned>(a.B)),
+                                   dim3(256), args, 0, s);
+    if (e != hipSuccess || a.P == 0) return e;
+    return hipLaunchKernel(reinterpret_cast<const void*>(&summary_outer),
+                           dim3(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.P),
+                                static_cast<unsigned>(a.dk / 16)),
+                           dim3(256), args, 0, s);
 }
 
 }  // namespace gdn

@@ -124,6 +124,19 @@ struct StateArgs {
                                       // (ncols = dk) computed in the same pass as S; else NULL
 };
 
+// Reverse of the prefix combine (gdn_summary_combine_bwd): G = dhT (or 0); for p = P-1
+// .. 0: dS_p = G, G <- M_p^T G + dH_in_p; dh0 = G. Then dM_p = dS_p H_in_p^T.
+struct ScanBwdArgs {
+    int B, H, P, dk, dv;
+    const float* M;       // [B,H,P,dk,dk]
+    const float* H_in;    // [B,H,P,dk,dv]
+    const float* dH_in;   // [B,H,P,dk,dv]
+    const float* dhT;     // [B,H,dk,dv] or NULL
+    float* dM;            // [B,H,P,dk,dk]
+    float* dS;            // [B,H,P,dk,dv]
+    float* dh0;           // [B,H,dk,dv] or NULL
+};
+
 struct ScanArgs {
     // X_p = M_p X_{p-1} + (S_p or 0), p = 0..P-1; X_{-1} = init
     int B, H, P, dk, ncols;
@@ -158,6 +171,17 @@ struct BwdArgs {
     float* dg_out;            // [B,T,H]
     float* dbeta_out;         // [B,T,H]
     float* dh0_out;           // [B,H,dk,dv] or NULL
+    // Segments: each batch row is P segments of L tokens (P = 1, L = T: the whole row),
+    // run as independent sequences (grid rows B P). h0 and dh0 are then [B,H,P,dk,dv]
+    // (segment p's incoming state and its gradient); dhT is [B,H,P,dk,dv] when
+    // dhT_per_segment, else [B,H,dk,dv] for the last segment only (zero for the others).
+    int P, L;
+    int dhT_per_segment;
+    int h0_identity;          // initial state I (dv == dk) instead of h0
+    int v_zero;               // values are zero (v unread)
+    int do_zero;              // output gradient is zero (d_o unread)
+    int write_dv;             // 0: the value gradient is not wanted (dv_out unread)
+    int accumulate;           // add into dq, dk, dv, dg, dbeta instead of writing them
 };
 
 // Layer steps around the core (gdn_layer_ops.hip).
@@ -186,6 +210,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s);
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, bool io_bf16, hipStream_t s);
+hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s);
 hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool io_bf16, hipStream_t s);
 

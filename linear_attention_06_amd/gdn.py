@@ -27,7 +27,8 @@ EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_
            "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d",
            "gdn_gated_rmsnorm",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
-           "gdn_apply_initial_state")
+           "gdn_apply_initial_state", "gdn_segment_bwd_workspace", "gdn_apply_initial_state_bwd",
+           "gdn_summary_combine_bwd", "gdn_segment_summary_bwd")
 
 
 class GdnProblem(ctypes.Structure):
@@ -77,11 +78,17 @@ def lib():
         L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_summary_combine.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         L.gdn_apply_initial_state.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_segment_bwd_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
+        L.gdn_apply_initial_state_bwd.argtypes = [pp, i32] + [vp] * 15 + [sz, vp]
+        L.gdn_summary_combine_bwd.argtypes = [i32, i32, i32, i32, i32] + [vp] * 8
+        L.gdn_segment_summary_bwd.argtypes = [pp, i32] + [vp] * 12 + [i32, vp, sz, vp]
         for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc",
                      "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
                      "gdn_chunk_fwd_varlen",
                      "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d", "gdn_gated_rmsnorm",
-                     "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state"):
+                     "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state",
+                     "gdn_segment_bwd_workspace", "gdn_apply_initial_state_bwd", "gdn_summary_combine_bwd",
+                     "gdn_segment_summary_bwd"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -426,3 +433,69 @@ def gdn_apply_initial_state(q, k, v, g, beta, H_in, seg_len, ws, o=None, hT=None
                                          _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_apply_initial_state")
     return o, hT
+
+
+def gdn_segment_bwd_workspace(p: GdnProblem, seg_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_segment_bwd_workspace(ctypes.byref(p), seg_len, ctypes.byref(n)), "gdn_segment_bwd_workspace")
+    return n.value
+
+
+def _grads_like(q, k, v, g, beta):
+    f32 = dict(dtype=torch.float32, device=v.device)
+    return (torch.empty(q.shape, **f32), torch.empty(k.shape, **f32), torch.empty(v.shape, **f32),
+            torch.empty(g.shape, **f32), torch.empty(beta.shape, **f32))
+
+
+def gdn_apply_initial_state_bwd(q, k, v, g, beta, H_in, seg_len, d_o, dhT=None, valid_len=None, want_dH_in=True,
+                                ws=None, stream=None):
+    """Backward of gdn_apply_initial_state. Returns (dq, dk, dv, dg, dbeta, dH_in or None), fp32."""
+    _io_checks(q, k, v, g, beta)
+    _dev(H_in, "H_in", torch.float32)
+    _dev(d_o, "d_o", v.dtype)
+    _dev(dhT, "dhT", torch.float32)
+    p = problem(q, v, valid_len)
+    dq, dk, dv, dg, db = _grads_like(q, k, v, g, beta)
+    dH_in = torch.empty_like(H_in) if want_dH_in else None
+    if ws is None:
+        ws = workspace(gdn_segment_bwd_workspace(p, seg_len), v.device)
+    _check(lib().gdn_apply_initial_state_bwd(ctypes.byref(p), seg_len, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                             _ptr(H_in), _ptr(d_o), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
+                                             _ptr(dg), _ptr(db), _ptr(dH_in), _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_apply_initial_state_bwd")
+    return dq, dk, dv, dg, db, dH_in
+
+
+def gdn_summary_combine_bwd(M, H_in, dH_in, dhT=None, want_dh0=True, stream=None):
+    """Backward of gdn_summary_combine. Returns (dM, dS, dh0 or None)."""
+    for t, n in ((M, "M"), (H_in, "H_in"), (dH_in, "dH_in"), (dhT, "dhT")):
+        _dev(t, n, torch.float32)
+    B, H, P, dk, dv = H_in.shape
+    dM = torch.empty_like(M)
+    dS = torch.empty_like(H_in)
+    dh0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=H_in.device) if want_dh0 else None
+    _check(lib().gdn_summary_combine_bwd(B, H, P, dk, dv, _ptr(M), _ptr(H_in), _ptr(dH_in), _ptr(dhT), _ptr(dM),
+                                         _ptr(dS), _ptr(dh0), _stream(stream)), "gdn_summary_combine_bwd")
+    return dM, dS, dh0
+
+
+def gdn_segment_summary_bwd(q, k, v, g, beta, seg_len, dM=None, dS=None, grads=None, valid_len=None, ws=None,
+                            stream=None):
+    """Backward of gdn_segment_summary: the gradients of sum(M dM) + sum(S dS). With grads =
+    (dq, dk, dv, dg, dbeta) given, the summaries' share is added to them in place (the
+    library accumulates); otherwise new tensors are returned."""
+    _io_checks(q, k, v, g, beta)
+    _dev(dM, "dM", torch.float32)
+    _dev(dS, "dS", torch.float32)
+    p = problem(q, v, valid_len)
+    accumulate = grads is not None
+    if grads is None:
+        grads = _grads_like(q, k, v, g, beta)
+    for t, n in zip(grads, ("dq", "dk", "dv", "dg", "dbeta")):
+        _dev(t, n, torch.float32)
+    if ws is None:
+        ws = workspace(gdn_segment_bwd_workspace(p, seg_len), v.device)
+    _check(lib().gdn_segment_summary_bwd(ctypes.byref(p), seg_len, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _ptr(dM), _ptr(dS), *(_ptr(t) for t in grads), 1 if accumulate else 0,
+                                         _ptr(ws), ws.numel(), _stream(stream)), "gdn_segment_summary_bwd")
+    return grads
