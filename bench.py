@@ -369,6 +369,23 @@ def layer_ops_timing(gdn, dev, stream, timed):
 
     ms = timed(layer_packed, 5)
     out["conv_prologue_core_norm_32k_packed_qkv"] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
+
+    def core_packed():   # the same without the Conv1D and the norm: the core alone on y
+        gdn.gdn_chunk_fwd_prologue_qkv(y, Hqk, H, D, D, a_g, b_g, A_log, dt_bias, D ** -0.5, h0, o=ov, hT=hT,
+                                       ws=ws, stream=stream)
+
+    def conv_in_prepare():   # the Conv1D inside the prepare pass (gdn_chunk_fwd_conv)
+        gdn.gdn_chunk_fwd_conv(x, w, bias, None, Hqk, H, D, D, a_g, b_g, A_log, dt_bias, D ** -0.5, h0, y=y,
+                               o=ov, hT=hT, ws=ws, stream=stream)
+
+    def layer_fused():
+        conv_in_prepare()
+        gdn.gdn_gated_rmsnorm(ov, z, wt, eps=1e-6, y=yn, stream=stream)
+
+    out["prologue_core_32k_packed_qkv"] = {"ms": timed(core_packed, 5)}
+    out["conv_prologue_core_32k_conv_in_prepare"] = {"ms": timed(conv_in_prepare, 5)}
+    ms = timed(layer_fused, 5)
+    out["conv_prologue_core_norm_32k_conv_in_prepare"] = {"ms": ms, "tokens_per_s": T / (ms * 1e-3)}
     return out
 
 

@@ -167,6 +167,30 @@ gdn_status gdn_chunk_fwd_prologue_qkv(const gdn_problem* p, const void* qkv,
                                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The same forward with the layer's causal depthwise Conv1D (kernel width conv_k in
+ * {2, 3, 4}, SiLU) fused into the chunk prepare pass (PR #1035, section "What does this PR
+ * do": the Conv1D runs on the projected Q, K and V before the Gated DeltaNet; its p2p mode
+ * exchanges the Conv1D's left halo between ranks):
+ *   x [B, T, C] bf16, C = 2 Hqk dk + H dv, the projected channels before the convolution
+ *   (per token: q_raw, then k_raw, then v, as in gdn_chunk_fwd_prologue_qkv);
+ *   conv_w [C, conv_k] fp32; conv_b [C] fp32 or NULL; x_prev [B, conv_k - 1, C] bf16 or
+ *   NULL: the tokens before the sequence (a rank's left halo), zero if NULL;
+ *   y [B, T, C] bf16 receives the convolution's output
+ *     y[b,t,c] = SiLU(conv_b[c] + sum_{j<conv_k} conv_w[c,j] x[b, t-conv_k+1+j, c])
+ *   (the arithmetic of gdn_causal_conv1d, bit for bit), which the state pass reads.
+ * Then the fused prologue and the forward of gdn_chunk_fwd_prologue on y's q, k and v
+ * parts; the prepare pass takes its q and k from the convolution in registers. Equal, bit
+ * for bit, to gdn_causal_conv1d followed by gdn_chunk_fwd_prologue_qkv. bf16 matrix-core
+ * path with dk = dv = 128 only; x, x_prev and y 16-byte aligned. y is written for every
+ * token t < T (padded tokens included, as the standalone convolution writes them).
+ */
+gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, const void* x, const float* conv_w,
+                              const float* conv_b, const void* x_prev, int32_t conv_k,
+                              const float* a, const float* b, const float* A_log,
+                              const float* dt_bias, float q_scale, const float* h0,
+                              void* y, void* o, float* hT, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Packed variable-length sequences (the general form of issue #320's variable-length
  * case, section 5.2, where rows of one batch hold different numbers of valid tokens):
  * instead of B rows of T tokens with padding, the B sequences lie back to back in one

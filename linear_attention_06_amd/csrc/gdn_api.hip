@@ -131,6 +131,8 @@ gdn_status run_prep(const gdn_problem& p, const Plan& pl, const void* q, const v
     a.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
     a.has_prologue = pro ? 1 : 0;
     a.pro = pro ? *pro : gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
+    a.has_conv = 0;
+    a.conv = gdn::PrepConv{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
     hipError_t e = use_mfma(p) ? gdn::launch_prep_mfma(a, s)
                                : gdn::launch_prep_f32path(a, p.io_dtype == GDN_BF16, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "prepare kernel launch");
@@ -634,6 +636,64 @@ gdn_status gdn_chunk_fwd_prologue_qkv(const gdn_problem* p, const void* qkv, con
             pa.NT = static_cast<int>(pl.NT);
             pa.q = q; pa.k = k; pa.g = nullptr; pa.beta = nullptr; pa.valid_len = p->valid_len;
             pa.cu_seqlens = nullptr; pa.qk_stride = C; pa.ws = w; pa.has_prologue = 1; pa.pro = pro;
+            pa.has_conv = 0; pa.conv = gdn::PrepConv{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+            const hipError_t e = gdn::launch_prep_mfma(pa, s);
+            if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
+        }
+        gdn::StateArgs sa = state_args(*p, pl, q, k, v, w);
+        sa.qk_stride = C;
+        sa.v_stride = C;
+        sa.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+        sa.s_init = h0;
+        sa.o = o;
+        sa.s_out = hT;
+        sa.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+        return run_state(*p, sa, s);
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, const void* x, const float* conv_w, const float* conv_b,
+                              const void* x_prev, int32_t conv_k, const float* a, const float* b,
+                              const float* A_log, const float* dt_bias, float q_scale, const float* h0, void* y,
+                              void* o, float* hT, void* ws, size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        if (!use_mfma(*p) || p->dv != 128)
+            return fail(GDN_EUNSUPPORTED, "the fused Conv1D runs on the bf16 matrix-core path with dk = dv = 128 only");
+        if (conv_k < 2 || conv_k > 4) return fail(GDN_EUNSUPPORTED, "conv_k=%d: kernel widths 2, 3 and 4", conv_k);
+        if (!(q_scale == q_scale) || q_scale - q_scale != 0.f) return fail(GDN_EINVAL, "q_scale must be finite");
+        const int64_t C = 2 * static_cast<int64_t>(p->Hqk) * p->dk + static_cast<int64_t>(p->H) * p->dv;
+        if ((static_cast<int64_t>(p->T) + gdn::kChunk) * C * 2 >= (int64_t(1) << 31))
+            return fail(GDN_EUNSUPPORTED, "one batch row of x exceeds 2 GiB");
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!x || !conv_w || !a || !b || !A_log || !dt_bias || !y || !o))
+            return fail(GDN_EINVAL, "x, conv_w, a, b, A_log, dt_bias, y and o must be non-NULL");
+        if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y) % 16 ||
+            (x_prev && reinterpret_cast<uintptr_t>(x_prev) % 16))
+            return fail(GDN_EINVAL, "x, x_prev and y must be 16-byte aligned");
+        const Plan pl = make_plan(*p, false);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (p->B == 0) return GDN_OK;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const gdn::Workspace w = carve(pl, ws);
+        const uint16_t* base = static_cast<const uint16_t*>(y);
+        const void* q = base;
+        const void* k = base + static_cast<int64_t>(p->Hqk) * p->dk;
+        const void* v = base + 2 * static_cast<int64_t>(p->Hqk) * p->dk;
+        if (pl.nch > 0) {
+            gdn::PrepArgs pa;
+            pa.B = p->B; pa.T = p->T; pa.H = p->H; pa.Hqk = p->Hqk; pa.dk = p->dk;
+            pa.NT = static_cast<int>(pl.NT);
+            pa.q = q; pa.k = k; pa.g = nullptr; pa.beta = nullptr; pa.valid_len = p->valid_len;
+            pa.cu_seqlens = nullptr; pa.qk_stride = C; pa.ws = w; pa.has_prologue = 1;
+            pa.pro = gdn::Prologue{a, b, A_log, dt_bias, q_scale};
+            pa.has_conv = 1;
+            pa.conv = gdn::PrepConv{static_cast<const uint16_t*>(x), conv_w, conv_b, static_cast<const uint16_t*>(x_prev),
+                                    static_cast<uint16_t*>(y), static_cast<int>(C), conv_k};
             const hipError_t e = gdn::launch_prep_mfma(pa, s);
             if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
         }

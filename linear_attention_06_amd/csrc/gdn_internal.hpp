@@ -88,6 +88,20 @@ struct Prologue {
     float q_scale;
 };
 
+// The layer's causal depthwise Conv1D fused into the prepare pass (matrix-core path, with
+// the prologue): the pass reads the projected channels before the convolution and writes
+// its output y, whose q, k and v parts the state pass then reads (token stride C):
+//   y[b,t,c] = SiLU(bias[c] + sum_{j<K} w[c,j] x[b, t-K+1+j, c]), tokens before t = 0
+//   from x_prev[b, 0..K-2, c] (zero if NULL); channels q (Hqk dk), k (Hqk dk), v (H dv).
+struct PrepConv {
+    const uint16_t* x;        // [B,T,C] bf16
+    const float* w;           // [C,K]
+    const float* bias;        // [C] or NULL
+    const uint16_t* x_prev;   // [B,K-1,C] bf16 or NULL
+    uint16_t* y;              // [B,T,C] bf16
+    int C, K;
+};
+
 struct PrepArgs {
     int B, T, H, Hqk, dk, NT;
     const void* q;
@@ -100,6 +114,8 @@ struct PrepArgs {
     Workspace ws;
     int has_prologue;       // 0: q, k, g, beta are used as given
     Prologue pro;
+    int has_conv;           // the Conv1D runs in the pass (requires the prologue; q, k unused)
+    PrepConv conv;
 };
 
 struct StateArgs {

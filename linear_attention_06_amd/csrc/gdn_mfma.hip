@@ -85,10 +85,68 @@ __device__ __forceinline__ void lds_sync() {
 }
 
 
+// Causal depthwise Conv1D of one 8-channel granule over 4 consecutive token rows t0 + r0
+// .. + 3 of batch row b, with SiLU and rounding to bf16, the same arithmetic as the
+// standalone convolution (acc = bias, then acc += w_j x_{t-K+1+j} for j = 0 .. K - 1):
+// out[u] is row r0 + u packed as bf16. The K - 1 rows before the first are read too (from
+// x_prev before the sequence). Rows at or past T are not computed (out zero, y untouched);
+// y receives the rows below T when write_y.
+template <int K>
+__device__ __forceinline__ void conv_granule(const PrepConv& cv, int b, int64_t T, int64_t t_first, int chan,
+                                             bool write_y, u32x4 (&out)[4]) {
+    const uint16_t* x = cv.x + static_cast<int64_t>(b) * T * cv.C + chan;
+    float w[8][K], bias[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) w[e][j] = cv.w[static_cast<int64_t>(chan + e) * K + j];
+        bias[e] = cv.bias ? cv.bias[chan + e] : 0.f;
+    }
+    // raw rows t_first - K + 1 .. t_first + 3, all loads issued before any is used
+    constexpr int NR = K + 3;
+    u32x4 raw[NR];
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+        const int64_t t = t_first - (K - 1) + j;
+        if (t >= 0) {
+            raw[j] = *reinterpret_cast<const u32x4*>(x + (t < T ? t : T - 1) * cv.C);
+        } else if (cv.x_prev) {
+            raw[j] = *reinterpret_cast<const u32x4*>(cv.x_prev + (static_cast<int64_t>(b) * (K - 1) + (K - 1) + t) * cv.C +
+                                                     chan);
+        } else {
+            raw[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float acc = bias[e];
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                const uint32_t wd = raw[u + j][e >> 1];
+                const float xv = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+                acc += w[e][j] * xv;
+            }
+            o[e] = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));
+        }
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            pk[e] = static_cast<uint32_t>(bf16_bits(o[2 * e])) | (static_cast<uint32_t>(bf16_bits(o[2 * e + 1])) << 16);
+        const int64_t t = t_first + u;
+        out[u] = t < T ? pk : u32x4{0u, 0u, 0u, 0u};
+        if (write_y && t < T) *reinterpret_cast<u32x4*>(cv.y + (static_cast<int64_t>(b) * T + t) * cv.C + chan) = pk;
+    }
+}
+
 // ----------------------------------------------------------------------------
-// Prepare: one block of 4 waves per (b, h, chunk).
+// Prepare: one block of 4 waves per (b, h, chunk). kConvK > 0: the Conv1D of width
+// kConvK runs in the pass (PrepConv).
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
+template <int kConvK>
+__global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
     constexpr int AP = 68;  // fp32 pitch of the 64x64 A and Tinv tiles
     // 35.8 KiB, four blocks per CU: K and Q (bf16, 256-byte rows) fill the first 32 KiB
     // until the products are done; then A lives at the start and Tinv behind it; once
@@ -152,11 +210,27 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         graw = a.has_prologue ? a.pro.a[gi] : a.g[gi];
         braw = a.has_prologue ? a.pro.b[gi] : a.beta[gi];
     }
+    // Rows of this thread's four K and Q granules (granule tid % 16): rows tid / 16 + 16 u,
+    // or with the Conv1D four consecutive rows 4 (tid / 16) + u, whose window each thread
+    // slides over the K - 1 rows before them.
+    const auto row_of = [&](int u) { return kConvK > 0 ? 4 * (tid >> 4) + u : (tid >> 4) + 16 * u; };
     u32x4 kv[4], qv[4];
-    {
+    if constexpr (kConvK > 0) {
+        // q, k and v channels of the convolution; the first value head of each query/key
+        // group writes the q and k output rows, every value head its own v rows
+        const int cb = tid & 15;
+        const int64_t tf = t0 + 4 * (tid >> 4);
+        const bool qk_owner = h % (a.H / a.Hqk) == 0;
+        {
+            u32x4 vv[4];   // written to y only
+            conv_granule<kConvK>(a.conv, b, a.T, tf, 2 * a.Hqk * DK + h * DK + 8 * cb, true, vv);
+        }
+        conv_granule<kConvK>(a.conv, b, a.T, tf, hq * DK + 8 * cb, qk_owner, qv);
+        conv_granule<kConvK>(a.conv, b, a.T, tf, a.Hqk * DK + hq * DK + 8 * cb, qk_owner, kv);
+    } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
+            const int row = row_of(u), cb = tid & 15;
             const int64_t t = t0 + row;
             const int64_t off =
                 (rs.start + (t < nvalid ? t : 0)) * a.qk_stride + hq * DK + 8 * cb;
@@ -196,7 +270,7 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int p = tid + 256 * u, row = p >> 4, cb = p & 15;
+            const int row = row_of(u), cb = tid & 15;
             const bool valid = t0 + row < nvalid;
             if (!valid) kv[u] = qv[u] = z;
             *reinterpret_cast<u32x4*>(k_s + kq_at(row, cb)) = kv[u];
@@ -220,7 +294,7 @@ __global__ __launch_bounds__(256) void prep_mfma(PrepArgs a) {
             const float rk = __builtin_amdgcn_rsqf(fmaxf(row_prefix16(sk), 1e-24f));
             const float rq = a.pro.q_scale * __builtin_amdgcn_rsqf(fmaxf(row_prefix16(sq), 1e-24f));
             if ((tid & 15) == 15) {
-                const int row = (tid >> 4) + 16 * u;
+                const int row = row_of(u);
                 rk_s[row] = rk;
                 rq_s[row] = rq;
             }
@@ -1141,7 +1215,16 @@ hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s) {
     const int64_t pairs = static_cast<int64_t>(a.B) * a.NT;
     const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * a.H));
     void* args[] = {const_cast<PrepArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&prep_mfma), grid, dim3(256), args, 0, s);
+    const void* fn = reinterpret_cast<const void*>(&prep_mfma<0>);
+    if (a.has_conv) {
+        switch (a.conv.K) {
+            case 2: fn = reinterpret_cast<const void*>(&prep_mfma<2>); break;
+            case 3: fn = reinterpret_cast<const void*>(&prep_mfma<3>); break;
+            case 4: fn = reinterpret_cast<const void*>(&prep_mfma<4>); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
 }
 
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {

@@ -23,7 +23,7 @@ CHUNK = 64
 
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
-           "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
+           "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_conv", "gdn_chunk_fwd_varlen_workspace",
            "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d",
            "gdn_gated_rmsnorm",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
@@ -69,6 +69,8 @@ def lib():
         L.gdn_chunk_fwd_prologue.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
                                              vp, sz, vp]
         L.gdn_chunk_fwd_prologue_qkv.argtypes = [pp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.gdn_chunk_fwd_conv.argtypes = [pp, vp, vp, vp, vp, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+                                         sz, vp]
         L.gdn_chunk_fwd_varlen_workspace.argtypes = [pp, i32, ctypes.POINTER(sz)]
         L.gdn_chunk_fwd_varlen.argtypes = [pp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_chunk_bwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
@@ -83,7 +85,7 @@ def lib():
         L.gdn_summary_combine_bwd.argtypes = [i32, i32, i32, i32, i32] + [vp] * 8
         L.gdn_segment_summary_bwd.argtypes = [pp, i32] + [vp] * 12 + [i32, vp, sz, vp]
         for name in ("gdn_chunk_fwd_workspace", "gdn_segment_workspace", "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc",
-                     "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_varlen_workspace",
+                     "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_conv", "gdn_chunk_fwd_varlen_workspace",
                      "gdn_chunk_fwd_varlen",
                      "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d", "gdn_gated_rmsnorm",
                      "gdn_segment_summary", "gdn_summary_combine", "gdn_apply_initial_state",
@@ -264,6 +266,44 @@ def gdn_chunk_fwd_prologue_qkv(qkv, Hqk, H, dk, dv, a, b, A_log, dt_bias, q_scal
                                             _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_chunk_fwd_prologue_qkv")
     return o, hT
+
+
+def gdn_chunk_fwd_conv(x, conv_w, conv_b, x_prev, Hqk, H, dk, dv, a, b, A_log, dt_bias, q_scale=None, h0=None,
+                       valid_len=None, y=None, o=None, hT=None, want_state=True, ws=None, stream=None):
+    """The fused-prologue forward with the layer's Conv1D (SiLU) fused into its prepare pass:
+    x [B, T, 2 Hqk dk + H dv] bf16 before the convolution, conv_w [C, K] fp32, conv_b [C] or
+    None, x_prev [B, K-1, C] or None. Returns (o, hT or None, y), y the convolution's output."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(x_prev, "x_prev", torch.bfloat16)
+    for t_, n in ((conv_w, "conv_w"), (conv_b, "conv_b"), (a, "a"), (b, "b"), (A_log, "A_log"),
+                  (dt_bias, "dt_bias"), (h0, "h0")):
+        _dev(t_, n, torch.float32)
+    B, T, C = x.shape
+    if C != 2 * Hqk * dk + H * dv:
+        raise ValueError("x has %d channels, expected 2 Hqk dk + H dv = %d" % (C, 2 * Hqk * dk + H * dv))
+    vl = None
+    if valid_len is not None:
+        _dev(valid_len, "valid_len", torch.int32)
+        vl = valid_len.data_ptr()
+    p = GdnProblem(B, T, H, Hqk, dk, dv, CHUNK, GDN_BF16, vl)
+    if q_scale is None:
+        q_scale = dk ** -0.5
+    if y is None:
+        y = torch.empty_like(x)
+    _dev(y, "y", torch.bfloat16)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=x.device)
+    _dev(o, "o", torch.bfloat16)
+    if hT is None and want_state:
+        hT = torch.empty((B, H, dk, dv), dtype=torch.float32, device=x.device)
+    _dev(hT, "hT", torch.float32)
+    if ws is None:
+        ws = workspace(gdn_chunk_fwd_workspace(p), x.device)
+    _check(lib().gdn_chunk_fwd_conv(ctypes.byref(p), _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(x_prev),
+                                    int(conv_w.shape[1]), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                    ctypes.c_float(q_scale), _ptr(h0), _ptr(y), _ptr(o), _ptr(hT), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "gdn_chunk_fwd_conv")
+    return o, hT, y
 
 
 def gdn_chunk_fwd_varlen_workspace(p: GdnProblem, max_seqlen: int) -> int:
