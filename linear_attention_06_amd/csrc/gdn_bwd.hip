@@ -67,7 +67,9 @@ __device__ __forceinline__ float col_sum(float x) {
 
 // Token range of grid row bz: segment p = bz % P of batch row b = bz / P, tokens p L ..
 // p L + L - 1 of the row, valid up to valid_len[b] (P = 1, L = T: the whole row).
+template <bool kSeg>
 __device__ __forceinline__ RowSpan bwd_span(const BwdArgs& a, int bz) {
+    if constexpr (!kSeg) return row_span(nullptr, a.valid_len, bz, a.T, a.NT);
     const int b = bz / a.P, p = bz % a.P;
     int64_t n = a.T;
     if (a.valid_len) {
@@ -80,7 +82,9 @@ __device__ __forceinline__ RowSpan bwd_span(const BwdArgs& a, int bz) {
     return RowSpan{static_cast<int64_t>(b) * a.T + s, n, a.L};
 }
 // Index of the (row, segment, head) state block in a [B,H,P,dk,dv] array.
+template <bool kSeg>
 __device__ __forceinline__ int64_t seg_state(const BwdArgs& a, int bz, int h) {
+    if constexpr (!kSeg) return static_cast<int64_t>(bz) * a.H + h;
     const int b = bz / a.P, p = bz % a.P;
     return (static_cast<int64_t>(b) * a.H + h) * a.P + p;
 }
@@ -108,7 +112,7 @@ struct ChunkRegs {
     float k[EK], q[kQ ? EK : 1], v[EV], d[kQ ? EV : 1], g, beta;
 };
 
-template <typename IO, int DK, bool kQ, int NTH>
+template <bool kSeg, typename IO, int DK, bool kQ, int NTH>
 __device__ __forceinline__ void fetch_chunk(ChunkRegs<IO, DK, kQ, NTH>& R, const BwdArgs& a, const RowSpan& rs, int h,
                                             int hq, int col0, int n, int tid) {
     using CR = ChunkRegs<IO, DK, kQ, NTH>;
@@ -130,8 +134,8 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<IO, DK, kQ, NTH>& R, const
         const int e = tid + NTH * m, r = e / 16, c = e % 16;
         const int64_t tok = t0 + r < rs.valid ? t0 + r : 0;
         const int64_t idx = ((rs.start + tok) * a.H + h) * a.dv + col0 + c;
-        R.v[m] = a.v_zero ? 0.f : ld_in(v, idx);
-        if (kQ) R.d[m] = a.do_zero ? 0.f : ld_in(d, idx);
+        R.v[m] = (kSeg && a.v_zero) ? 0.f : ld_in(v, idx);
+        if (kQ) R.d[m] = (kSeg && a.do_zero) ? 0.f : ld_in(d, idx);
     }
     const int64_t tok = t0 + (tid & 63) < rs.valid ? t0 + (tid & 63) : 0;
     const int64_t gi = (rs.start + tok) * a.H + h;
@@ -179,29 +183,31 @@ __device__ __forceinline__ float fwd_step(float (&S)[RJ], const Lds& L, int u, i
     return w;
 }
 
-template <typename IO, int DK, int TPC>
+// kSeg: the segment features of BwdArgs (segments, identity start, zero values or output
+// gradient, no dv, accumulation) are read; without it the kernels run the plain backward.
+template <typename IO, int DK, int TPC, bool kSeg>
 __global__ __launch_bounds__(16 * TPC) void bwd_ckpt(BwdArgs a) {
     constexpr int RJ = DK / TPC, NTH = 16 * TPC;
     __shared__ ChunkLds<IO, DK, false> L;
     const int col0 = 16 * blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, c = tid / TPC, i = tid % TPC;
-    const RowSpan rs = bwd_span(a, b);
+    const RowSpan rs = bwd_span<kSeg>(a, b);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
-    const int64_t sb = seg_state(a, b, h);
+    const int64_t sb = seg_state<kSeg>(a, b, h);
     float S[RJ];
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
         const int r = i + TPC * j;
-        S[j] = a.h0_identity ? (r == col0 + c ? 1.f : 0.f) : (a.h0 ? a.h0[(sb * DK + r) * a.dv + col0 + c] : 0.f);
+        S[j] = (kSeg && a.h0_identity) ? (r == col0 + c ? 1.f : 0.f) : (a.h0 ? a.h0[(sb * DK + r) * a.dv + col0 + c] : 0.f);
     }
     ChunkRegs<IO, DK, false, NTH> R;
-    if (a.NT > 0) fetch_chunk(R, a, rs, h, hq, col0, 0, tid);
+    if (a.NT > 0) fetch_chunk<kSeg>(R, a, rs, h, hq, col0, 0, tid);
     for (int n = 0; n < a.NT; ++n) {
         __syncthreads();
         store_chunk(L, R, rs, n, tid);
         __syncthreads();
-        if (n + 1 < a.NT) fetch_chunk(R, a, rs, h, hq, col0, n + 1, tid);
+        if (n + 1 < a.NT) fetch_chunk<kSeg>(R, a, rs, h, hq, col0, n + 1, tid);
         for (int u = 0; u < 64; ++u) {
             if ((u & 7) == 0) {   // the state before every 8th token, in thread order
                 float* ck = a.ckpt + ((bh * 8 * a.NT + 8 * n + (u >> 3)) * (a.dv / 16) + blockIdx.x) * (16 * DK);
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_ckpt(BwdArgs a) {
     }
 }
 
-template <typename IO, int DK, int TPC>
+template <typename IO, int DK, int TPC, bool kSeg>
 __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     constexpr int RJ = DK / TPC, NTH = 16 * TPC;
     __shared__ ChunkLds<IO, DK, true> L;
@@ -226,13 +232,13 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     const int tile = blockIdx.x, col0 = 16 * tile, h = blockIdx.y, b = blockIdx.z;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, c = tid / TPC, i = tid % TPC;
-    const RowSpan rs = bwd_span(a, b);
+    const RowSpan rs = bwd_span<kSeg>(a, b);
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
-    const int64_t sb = seg_state(a, b, h);
+    const int64_t sb = seg_state<kSeg>(a, b, h);
     // the final-state gradient: per segment, or the row's for its last segment only
     const float* dhT = a.dhT;
     int64_t dsb = sb;
-    if (!a.dhT_per_segment) {
+    if (kSeg && !a.dhT_per_segment) {
         dsb = static_cast<int64_t>(b / a.P) * a.H + h;
         if (b % a.P != a.P - 1) dhT = nullptr;
     }
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
     if (a.NT > 0) load_ck(8 * a.NT - 1, nxt);
 
     ChunkRegs<IO, DK, true, NTH> R;
-    if (a.NT > 0) fetch_chunk(R, a, rs, h, hq, col0, a.NT - 1, tid);
+    if (a.NT > 0) fetch_chunk<kSeg>(R, a, rs, h, hq, col0, a.NT - 1, tid);
     // token strides of dv and of the partials; this thread's output of the pair sums:
     // token u + 1 - rp, the dq (rwhich = 0) or dk (1) term of row rr
     static_assert(4 * DK <= NTH, "at most one pair-sum output per thread");
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
         __syncthreads();
         store_chunk(L, R, rs, n, tid);
         __syncthreads();
-        if (n > 0) fetch_chunk(R, a, rs, h, hq, col0, n - 1, tid);
+        if (n > 0) fetch_chunk<kSeg>(R, a, rs, h, hq, col0, n - 1, tid);
         // the chunk's tokens that take part and that the row writes (0..64), and its
         // output addresses at its first token
         const int64_t ct0 = static_cast<int64_t>(n) * kChunk, r0 = rs.start + ct0;
@@ -306,9 +312,9 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
                 z = col_sum<TPC>(z);
                 ms = col_sum<TPC>(ms);
                 // the tail of the last chunk is past the row
-                if (a.write_dv && i == 0 && u < nwrite) {
+                if ((!kSeg || a.write_dv) && i == 0 && u < nwrite) {
                     const float x = valid ? bt * z : 0.f;
-                    dv_s[uu * sdv] = a.accumulate ? dv_s[uu * sdv] + x : x;
+                    dv_s[uu * sdv] = (kSeg && a.accumulate) ? dv_s[uu * sdv] + x : x;
                 }
                 // dk's column terms: M beta (v - e^g w) - e^g beta z S_{t-1}
                 const float am = bt * (vc - eg * w[uu]), bz = eg * bt * z;
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(16 * TPC) void bwd_sweep(BwdArgs a) {
 
 // One block per (t, b): dq, dk per query/key head (sum over column tiles and the
 // value heads of the group), dg and dbeta per value head (sum over column tiles).
-template <int DK>
+template <int DK, bool kSeg>
 __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
     const int64_t t = blockIdx.x;
     const int b = blockIdx.y;
@@ -375,8 +381,8 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
         float* dk = a.dk_out + (row * a.Hqk + hq) * DK + r;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            dq[x] = a.accumulate ? dq[x] + sq[x] : sq[x];
-            dk[x] = a.accumulate ? dk[x] + sk[x] : sk[x];
+            dq[x] = (kSeg && a.accumulate) ? dq[x] + sq[x] : sq[x];
+            dk[x] = (kSeg && a.accumulate) ? dk[x] + sk[x] : sk[x];
         }
     }
     for (int hh = threadIdx.x; hh < a.H; hh += 256) {
@@ -386,8 +392,8 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
             sg += part[2 * tl];
             sb += part[2 * tl + 1];
         }
-        a.dg_out[row * a.H + hh] = a.accumulate ? a.dg_out[row * a.H + hh] + sg : sg;
-        a.dbeta_out[row * a.H + hh] = a.accumulate ? a.dbeta_out[row * a.H + hh] + sb : sb;
+        a.dg_out[row * a.H + hh] = (kSeg && a.accumulate) ? a.dg_out[row * a.H + hh] + sg : sg;
+        a.dbeta_out[row * a.H + hh] = (kSeg && a.accumulate) ? a.dbeta_out[row * a.H + hh] + sb : sb;
     }
 }
 
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(256) void bwd_reduce(BwdArgs a) {
 // once dk >= 32, else 16.
 constexpr int kTpc(int dk) { return dk >= 32 ? 32 : 16; }
 
-template <typename IO>
+template <typename IO, bool kSeg>
 hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B * a.P));
     void* args[] = {const_cast<BwdArgs*>(&a)};
@@ -404,9 +410,9 @@ hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t s) {
     switch (a.dk) {
 #define GDN_BWD_CASE(D)                                                                  \
         case D:                                                                          \
-            f1 = reinterpret_cast<const void*>(&bwd_ckpt<IO, D, kTpc(D)>);               \
-            f2 = reinterpret_cast<const void*>(&bwd_sweep<IO, D, kTpc(D)>);              \
-            f3 = reinterpret_cast<const void*>(&bwd_reduce<D>);                          \
+            f1 = reinterpret_cast<const void*>(&bwd_ckpt<IO, D, kTpc(D), kSeg>);         \
+            f2 = reinterpret_cast<const void*>(&bwd_sweep<IO, D, kTpc(D), kSeg>);        \
+            f3 = reinterpret_cast<const void*>(&bwd_reduce<D, kSeg>);                    \
             nth = 16 * kTpc(D);                                                          \
             break;
         GDN_BWD_CASE(16)
@@ -426,7 +432,10 @@ hipError_t bwd_dispatch(const BwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& a, bool io_bf16, hipStream_t s) {
-    return io_bf16 ? bwd_dispatch<uint16_t>(a, s) : bwd_dispatch<float>(a, s);
+    const bool seg = a.P != 1 || a.dhT_per_segment || a.h0_identity || a.v_zero || a.do_zero || !a.write_dv ||
+                     a.accumulate;
+    if (seg) return io_bf16 ? bwd_dispatch<uint16_t, true>(a, s) : bwd_dispatch<float, true>(a, s);
+    return io_bf16 ? bwd_dispatch<uint16_t, false>(a, s) : bwd_dispatch<float, false>(a, s);
 }
 
 }  // namespace gdn
