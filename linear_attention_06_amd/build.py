@@ -37,7 +37,7 @@ def hipcc() -> str:
 # Per-source flags. The matrix-core kernels keep MFMA accumulators in ordinary
 # VGPRs: their results feed VALU code every chunk, and accumulation registers
 # would cost a copy each way.
-SOURCE_FLAGS = {"gdn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+SOURCE_FLAGS = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for name in ("gdn_mfma.hip", "gdn_bwd_mfma.hip")}
 
 
 def _compile(src: str, extra: list) -> str:

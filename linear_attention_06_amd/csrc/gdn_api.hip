@@ -415,11 +415,85 @@ gdn_status check_bwd_ws(const BwdPlan& pl, void* ws, size_t ws_bytes) {
     return GDN_OK;
 }
 
+// The chunked matrix-core backward (bf16, dk = dv = 128): the prepare pass's records (That,
+// P, decay factors; That^T and P^T; Tinv and P row-major), then the state entering every
+// chunk and the gradient of the state leaving it (bf16, transposed).
+// The gradient pass reads one batch row of the fp32 dv output with 32-bit byte offsets.
+bool use_bwd_mfma(const gdn_problem& p) {
+    return use_mfma(p) && p.dv == 128 &&
+           static_cast<int64_t>(p.T + gdn::kChunk) * p.H * p.dv * 4 < (int64_t(1) << 31);
+}
+
+struct BwdMfmaPlan {
+    Plan fwd;
+    size_t thatT_off = 0, pT_off = 0, trm_off = 0, prm_off = 0, states_off = 0, dstates_off = 0, bytes = 0;
+};
+
+BwdMfmaPlan make_bwd_mfma_plan(const gdn_problem& p) {
+    BwdMfmaPlan pl;
+    pl.fwd = make_plan(p, false);
+    const size_t nch = static_cast<size_t>(pl.fwd.nch);
+    const size_t tri = align256(nch * gdn::kTriRecordElems * 2), rm = align256(nch * 64 * 64 * 2);
+    const size_t st = align256(nch * static_cast<size_t>(p.dk) * p.dv * 2);
+    pl.thatT_off = pl.fwd.bytes;
+    pl.pT_off = pl.thatT_off + tri;
+    pl.trm_off = pl.pT_off + tri;
+    pl.prm_off = pl.trm_off + rm;
+    pl.states_off = pl.prm_off + rm;
+    pl.dstates_off = pl.states_off + st;
+    pl.bytes = pl.dstates_off + st;
+    return pl;
+}
+
+gdn_status run_bwd_mfma(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, const void* d_o, const float* dhT,
+                        float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws, hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    const gdn::Workspace w = carve(pl.fwd, ws);
+    gdn::BwdRecords rec;
+    rec.thatT = base + pl.thatT_off;
+    rec.pT = base + pl.pT_off;
+    rec.t_rm = base + pl.trm_off;
+    rec.p_rm = base + pl.prm_off;
+    if (pl.fwd.nch > 0) {
+        gdn::PrepArgs pa;
+        pa.B = p.B; pa.T = p.T; pa.H = p.H; pa.Hqk = p.Hqk; pa.dk = p.dk; pa.NT = static_cast<int>(pl.fwd.NT);
+        pa.q = q; pa.k = k; pa.g = g; pa.beta = beta; pa.valid_len = p.valid_len; pa.cu_seqlens = nullptr; pa.ws = w;
+        pa.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
+        pa.has_prologue = 0;
+        pa.pro = gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
+        pa.has_conv = 0;
+        pa.conv = gdn::PrepConv{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+        pa.bwd = rec;
+        hipError_t e = gdn::launch_prep_mfma(pa, s);
+        if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
+        // the forward state pass, keeping the state entering every chunk
+        gdn::StateArgs sa = state_args(p, pl.fwd, q, k, v, w);
+        sa.pass = gdn::kPassS;
+        sa.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+        sa.s_init = h0;
+        sa.states = base + pl.states_off;
+        gdn_status st = run_state(p, sa, s);
+        if (st != GDN_OK) return st;
+    }
+    gdn::BwdMfmaArgs a;
+    a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.NT = static_cast<int>(pl.fwd.NT);
+    a.q = q; a.k = k; a.v = v; a.d_o = d_o; a.g = g; a.beta = beta; a.dhT = dhT; a.valid_len = p.valid_len;
+    a.ws = w; a.rec = rec;
+    a.states = base + pl.states_off;
+    a.dstates = base + pl.dstates_off;
+    a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta; a.dh0_out = dh0;
+    hipError_t e = gdn::launch_bwd_state_mfma(a, s);
+    if (e != hipSuccess) return hip_fail(e, "backward state kernel launch");
+    e = gdn::launch_bwd_grad_mfma(a, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "backward gradient kernel launch");
+}
+
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
-    *bytes = make_bwd_plan(*p).bytes;
+    *bytes = use_bwd_mfma(*p) ? make_bwd_mfma_plan(*p).bytes : make_bwd_plan(*p).bytes;
     return GDN_OK;
 }
 
@@ -433,6 +507,16 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (use_bwd_mfma(*p)) {
+            const BwdMfmaPlan pl = make_bwd_mfma_plan(*p);
+            Plan need;
+            need.bytes = pl.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            if (p->B == 0) return GDN_OK;
+            return run_bwd_mfma(*p, pl, q, k, v, g, beta, h0, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
+                                static_cast<hipStream_t>(stream));
+        }
         const BwdPlan pl = make_bwd_plan(*p);
         st = check_bwd_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;

@@ -1,0 +1,785 @@
+// gdn_bwd_mfma.hip -- chunked backward of the Gated DeltaNet recurrence on bf16 matrix
+// cores (gfx950), dk = dv = 128, in the chunk form of the forward (gdn_mfma.hip):
+//   X = V - diag(e^Gam) K S,   U = That X,   That = Tinv diag(beta),  Tinv = (I + A)^{-1}
+//   O = diag(e^Gam) Q S + P U, S' = e^{Gam_C} S + K^T diag(e^{Gam_C - Gam}) U
+// (Gam the chunk-local cumulative log-decay, Gam_C its last entry). Reverse mode, with dO
+// the output gradient of the chunk and dS' the gradient of the state leaving it:
+//   dU = P^T dO + diag(e^{Gam_C - Gam}) K dS',  dX = That^T dU (= dV)
+//   dS = e^{Gam_C} dS' + Q^T diag(e^Gam) dO - K^T diag(e^Gam) dX   (the state entering it)
+// and, with Zf = diag(e^Gam) dO S^T, Zg = -diag(e^Gam) dX S^T, Zh = diag(e^{Gam_C - Gam}) U dS'^T,
+// dP = (dO U^T) masked to j <= i, PD = dP . exp(Gam_i - Gam_j), dThat = dU X^T masked to
+// j <= i, dA = -Tinv^T (dThat diag(beta)) Tinv^T masked to j < i, E = dA . beta_i exp(Gam_i - Gam_j):
+//   dQ = Zf + PD K,   dK = Zg + Zh + PD^T Q + E K + E^T K
+//   dbeta_j = sum_i dThat_ij Tinv_ij + sum_l dA_jl (K K^T)_jl exp(Gam_j - Gam_l)
+//   dGam_t = <Zf_t, q_t> + <Zg_t, k_t> - W_t + sum_j (dP . P)_tj - sum_i (dP . P)_it
+//            + sum_j (E . K K^T)_tj - sum_i (E . K K^T)_it,   W_t = <Zh_t, k_t>,
+//   dGam_C += sum_t W_t + e^{Gam_C} <dS', S>,   dg_s = sum_{t >= s} dGam_t.
+// The token recurrence is in hyper-parallel issue #320 (test report for PR #1114, section
+// 4.1: the backward takes dO and the final-state gradient and returns the gradients of q,
+// k, v, g, beta and the initial state); the chunk form is the published UT/WY form of
+// Gated DeltaNet (Yang, Kautz and Hatamizadeh, 2025).
+//
+// Three passes after the prepare pass: the forward state pass stores the state S_n entering
+// every chunk (bf16, transposed); bwd_state_mfma runs the reverse chain above per (b, h,
+// 16 columns of dv), writing dv and the gradient dS'_n of the state leaving every chunk;
+// bwd_grad_mfma, one block per (b, query/key head, chunk), forms the rest from S_n and dS'_n
+// with every product on v_mfma_f32_16x16x32_bf16 and fp32 accumulation.
+#include "gdn_mfma_common.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int KPB = 272;   // LDS row pitch in bytes of 128 bf16 (256 B + 16)
+constexpr int SPB = 144;   // LDS row pitch in bytes of 64 bf16 (128 B + 16)
+
+// Block (r, s) of the upper-triangle records (That^T, P^T): (0,0) (0,1) (1,0) (1,1) (2,1) (3,1).
+__host__ __device__ constexpr int tri_up(int r, int s) { return r < 2 ? 2 * r + s : r + 2; }
+
+// Fragment of a matrix stored with its contraction index along LDS rows ("k-major": row
+// k0 + e holds the 16 output rows or columns at 2-byte steps from c0): two transposing
+// reads give lane (i, g) the values at rows k0 + 8 g .. + 7 of column c0 + i, the
+// 16x16x32 operand layout. Lane p of a group addresses row k0 + 8 g + 4 hh + p / 4 at
+// column c0 + 4 (p % 4).
+__device__ __forceinline__ bf16x8 frag_kmajor(const unsigned char* base, int pitch, int k0, int c0, int l16, int g4) {
+    const unsigned char* p = base + (k0 + 8 * g4 + (l16 >> 2)) * pitch + (c0 + 4 * (l16 & 3)) * 2;
+    const u32x2 a = lds_read_tr(p), b = lds_read_tr(p + 4 * pitch);
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+// Fragment of a matrix stored with its contraction index contiguous ("row-major"): lane
+// (i, g) reads row r0 + i at columns k0 + 8 g .. + 7.
+__device__ __forceinline__ bf16x8 frag_rowmajor(const unsigned char* base, int pitch, int r0, int k0, int l16, int g4) {
+    return lds_frag_b(base + (r0 + l16) * pitch + (k0 + 8 * g4) * 2);
+}
+// A 16x16 tile of a row-major bf16 matrix in accumulator order: lane (c, g) gets rows
+// r0 + 4 g .. + 3 of column c0 + c.
+__device__ __forceinline__ f32x4 tile_acc_order(const unsigned char* base, int pitch, int r0, int c0, int l16, int g4) {
+    return bf16x4_to_f32(lds_read_tr(base + (r0 + 4 * g4 + (l16 >> 2)) * pitch + (c0 + 4 * (l16 & 3)) * 2));
+}
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then row broadcasts).
+__device__ __forceinline__ float wave_scan64(float x) {
+    x = row_prefix16(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, true));   // row_bcast:15
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, true));   // row_bcast:31
+    return x;
+}
+// Sum over the 16 lanes of each row of the wave (all 16 lanes get it).
+__device__ __forceinline__ float row_sum16(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+// Sum over the four lanes l % 16 == c (lanes c, c + 16, c + 32, c + 48).
+__device__ __forceinline__ float col_sum4(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// ----------------------------------------------------------------------------
+// Reverse chain: one block of 8 waves per (b, h, 16 columns of dv). Wave 0 carries the
+// 128 x 16 slice of the state gradient in registers (the forward state pass's layout:
+// register t of lane (c, g), element j holds row 32 (t / 2) + 8 g + 4 (t % 2) + j of
+// column c) and walks the chunks from last to first; waves 1-7 stage each chunk's K, Q,
+// That^T and P^T records, output gradient and decay record in LDS two chunks ahead
+// (loads into registers, written to LDS one iteration later; one barrier per chunk).
+// ----------------------------------------------------------------------------
+constexpr int RB_Q = 64 * KPB, RB_TT = 2 * 64 * KPB, RB_PT = RB_TT + 6144, RB_DO = RB_PT + 6144,
+              RB_G = RB_DO + 2048, RB_SIZE = RB_G + 1024;
+constexpr int kRevLoads = 16 + 16 + 6 + 6 + 2 + 1;   // 1 KiB loads per chunk
+constexpr int kRevLoaders = 7;
+
+__host__ __device__ constexpr int rev_loads_owned(int me) {
+    int c = 0;
+    for (int i = 0; i < kRevLoads; ++i) c += (i % kRevLoaders == me) ? 1 : 0;
+    return c;
+}
+
+__global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_groups) {
+    constexpr int tiles = DK / 16;
+    __shared__ __align__(16) unsigned char stg[2 * RB_SIZE];
+
+    // XCD-aware order as in the forward state pass: the column tiles of the value heads
+    // that share a query/key head run on one XCD
+    const int L = blockIdx.x;
+    const int xcd = L & 7, slot = L >> 3;
+    const int tile = slot % tiles;
+    const int rep = a.H / a.Hqk;
+    const int kk = slot / tiles;
+    const int qg = (kk / rep) * 8 + xcd;
+    if (qg >= qk_groups) return;
+    const int b = qg / a.Hqk, hq = qg % a.Hqk;
+    const int h = hq * rep + kk % rep;
+    const int col0 = 16 * tile;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
+    const int64_t nvalid = rs.valid;
+    const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    const int NT = a.NT;
+    const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK, v_row = static_cast<int64_t>(a.H) * DK;
+
+    if (wave >= 1) {
+        if (NT == 0) return;
+        // ---------------- loading waves ----------------
+        const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rs.start * qk_row;
+        const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rs.start * qk_row;
+        const uint16_t* din = static_cast<const uint16_t*>(a.d_o) + rs.start * v_row;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin, nvalid * qk_row * 2);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qin, nvalid * qk_row * 2);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(din, nvalid * v_row * 2);
+        const int64_t rec = static_cast<int64_t>(NT) * kTriRecord * 2;
+        const __amdgpu_buffer_rsrc_t rtt = make_rsrc(static_cast<const uint16_t*>(a.rec.thatT) + bh * NT * kTriRecord, rec);
+        const __amdgpu_buffer_rsrc_t rpt = make_rsrc(static_cast<const uint16_t*>(a.rec.pT) + bh * NT * kTriRecord, rec);
+        const __amdgpu_buffer_rsrc_t rgt = make_rsrc(a.ws.gates + bh * NT * kGateRecordMfma,
+                                                     static_cast<int64_t>(NT) * kGateRecordMfma * 4);
+        // lane l of a K / Q load: row 4 j + l / 16 of the chunk, 16 bytes at column 8 (l % 16)
+        const uint32_t voff_kq = static_cast<uint32_t>(((lane >> 4) * qk_row + hq * DK + 8 * (lane & 15)) * 2);
+        const uint32_t voff_l = static_cast<uint32_t>(16 * lane);
+        const uint32_t voff_d = static_cast<uint32_t>(((lane >> 1) * v_row + h * DK + col0 + 8 * (lane & 1)) * 2);
+        const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2), dstep = static_cast<uint32_t>(kChunk * v_row * 2);
+        // load i of a chunk belongs to loading wave i % 7; each wave's loop is compiled for
+        // its own index, so that its stage registers are indexed at compile time
+        auto loader = [&](auto me_tag) {
+        constexpr int me = decltype(me_tag)::value;
+        constexpr int NS = rev_loads_owned(me);
+        using Stage = u32x4[NS];
+        Stage st0, st1;
+        auto load = [&](int n, Stage& st) {
+            n = n < 0 ? 0 : n;
+#pragma unroll
+            for (int i = me; i < kRevLoads; i += kRevLoaders) {
+                u32x4& r = st[i / kRevLoaders];
+                if (i < 16) r = gload16(rk, voff_kq, static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
+                else if (i < 32) r = gload16(rq, voff_kq, static_cast<uint32_t>(4 * (i - 16) * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
+                else if (i < 38) r = gload16(rtt, voff_l, static_cast<uint32_t>(n) * (kTriRecord * 2) + (i - 32) * 1024);
+                else if (i < 44) r = gload16(rpt, voff_l, static_cast<uint32_t>(n) * (kTriRecord * 2) + (i - 38) * 1024);
+                else if (i < 46) r = gload16(rd, voff_d, static_cast<uint32_t>(32 * (i - 44) * v_row * 2) + static_cast<uint32_t>(n) * dstep);
+                else r = gload16(rgt, voff_l, static_cast<uint32_t>(n) * (kGateRecordMfma * 4u));
+            }
+        };
+        auto store = [&](int n, const Stage& st) {   // into the buffer of the parity of n
+            unsigned char* dst = stg + (n & 1) * RB_SIZE;
+#pragma unroll
+            for (int i = me; i < kRevLoads; i += kRevLoaders) {
+                unsigned char* p;
+                if (i < 32) p = dst + (i < 16 ? 0 : RB_Q) + (4 * (i & 15) + (lane >> 4)) * KPB + 16 * (lane & 15);
+                else if (i < 38) p = dst + RB_TT + (i - 32) * 1024 + 16 * lane;
+                else if (i < 44) p = dst + RB_PT + (i - 38) * 1024 + 16 * lane;
+                else if (i < 46) p = dst + RB_DO + (i - 44) * 1024 + 16 * lane;
+                else p = dst + RB_G + 16 * lane;
+                *reinterpret_cast<u32x4*>(p) = st[i / kRevLoaders];
+            }
+        };
+        // chunks run from c = NT - 1 down to 0; in the iteration of chunk c the loaders write
+        // chunk c - 1 (loaded two iterations earlier) and load chunk c - 3. Every wave of the
+        // block passes one barrier per chunk.
+        const int c0 = NT - 1;
+        load(c0, st0);
+        store(c0, st0);
+        load(c0 - 1, st0);
+        load(c0 - 2, st1);
+        int c = c0;
+        for (; c >= 1; c -= 2) {
+            chunk_barrier(false);
+            store(c - 1, st0);
+            load(c - 3, st0);
+            chunk_barrier(false);
+            store(c - 2, st1);
+            load(c - 4, st1);
+        }
+        if (c == 0) {
+            chunk_barrier(false);
+            store(-1, st0);
+        }
+        };
+        switch (wave - 1) {
+            case 0: loader(IntTag<0>{}); break;
+            case 1: loader(IntTag<1>{}); break;
+            case 2: loader(IntTag<2>{}); break;
+            case 3: loader(IntTag<3>{}); break;
+            case 4: loader(IntTag<4>{}); break;
+            case 5: loader(IntTag<5>{}); break;
+            default: loader(IntTag<6>{}); break;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+
+    // ---------------- chain wave ----------------
+    f32x4 dS[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + j;
+            dS[t][j] = a.dhT ? a.dhT[bh * DK * DK + row * DK + col0 + l16] : 0.f;
+        }
+    float* dv_row = a.dv_out + rs.start * v_row + h * DK + col0 + l16;
+    for (int n = NT - 1; n >= 0; --n) {
+        chunk_barrier(false);
+        const unsigned char* sb_ = stg + (n & 1) * RB_SIZE;
+        const float* gs = reinterpret_cast<const float*>(sb_ + RB_G);
+        // dS' as B fragments of K dS' (k = dk), stored for the gradient pass (transposed)
+        bf16x8 sb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) sb[s] = pack_frag(dS[2 * s], dS[2 * s + 1]);
+        {
+            uint16_t* st = static_cast<uint16_t*>(a.dstates) + ((bh * NT + n) * DK + col0 + l16) * DK + 8 * g4;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(st + 32 * s) = sb[s];
+        }
+        // K dS' (token tiles r)
+        f32x4 c0[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            c0[r] = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) c0[r] = mfma16(frag_rowmajor(sb_, KPB, 16 * r, 32 * s, l16, g4), sb[s], c0[r]);
+        }
+        // dO in accumulator order (tokens 16 r + 4 g + j, column c) and P^T dO
+        u32x2 dor[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dor[r] = lds_read_tr(sb_ + RB_DO + (16 * r + 4 * g4 + (l16 >> 2)) * 32 + 8 * (l16 & 3));
+        bf16x8 dob[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            dob[s] = __builtin_bit_cast(bf16x8, u32x4{dor[2 * s][0], dor[2 * s][1], dor[2 * s + 1][0], dor[2 * s + 1][1]});
+        f32x4 du[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            f32x4 pd = zero4();
+#pragma unroll
+            for (int s = (r < 2 ? 0 : 1); s < 2; ++s) pd = mfma16(lds_frag_b(sb_ + RB_PT + tri_up(r, s) * 1024 + 16 * lane), dob[s], pd);
+            const f32x4 egc = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) du[r][j] = pd[j] + egc[j] * c0[r][j];
+        }
+        bf16x8 dub[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) dub[s] = pack_frag(du[2 * s], du[2 * s + 1]);
+        // dX = That^T dU, written as dv (zero past the valid tokens)
+        f32x4 dx[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dx[r] = zero4();
+#pragma unroll
+            for (int s = (r < 2 ? 0 : 1); s < 2; ++s) dx[r] = mfma16(lds_frag_b(sb_ + RB_TT + tri_up(r, s) * 1024 + 16 * lane), dub[s], dx[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t t = static_cast<int64_t>(n) * kChunk + 16 * r + 4 * g4 + j;
+                if (t < a.T) dv_row[t * v_row] = t < nvalid ? dx[r][j] : 0.f;
+            }
+        // dS = e^{Gam_C} dS' + Q^T diag(e^Gam) dO - K^T diag(e^Gam) dX
+        bf16x8 wb[2], qb[2];
+        {
+            f32x4 w[4], qv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 eg = *reinterpret_cast<const f32x4*>(gs + 16 * r + 4 * g4);
+                const f32x4 egq = *reinterpret_cast<const f32x4*>(gs + 128 + 16 * r + 4 * g4);
+                const f32x4 dof = bf16x4_to_f32(dor[r]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    w[r][j] = -eg[j] * dx[r][j];
+                    qv[r][j] = egq[j] * dof[j];
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                wb[s] = pack_frag(w[2 * s], w[2 * s + 1]);
+                qb[s] = pack_frag(qv[2 * s], qv[2 * s + 1]);
+            }
+        }
+        const float egC = gs[192];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dS[t][j] *= egC;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                // K^T and Q^T fragments of state tile t (rows 32 (t / 2) + 8 (i / 4) + 4 (t % 2) +
+                // i % 4 for lane i of a group) over tokens 32 s + 4 g + (e % 4) + 16 (e / 4)
+                const int off = (32 * s + 4 * g4 + (l16 >> 2)) * KPB + (32 * (t >> 1) + 8 * (l16 & 3) + 4 * (t & 1)) * 2;
+                const u32x2 k0 = lds_read_tr(sb_ + off), k1 = lds_read_tr(sb_ + off + 16 * KPB);
+                const u32x2 q0 = lds_read_tr(sb_ + RB_Q + off), q1 = lds_read_tr(sb_ + RB_Q + off + 16 * KPB);
+                dS[t] = mfma16(__builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), wb[s], dS[t]);
+                dS[t] = mfma16(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), qb[s], dS[t]);
+            }
+    }
+    if (a.dh0_out) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + j;
+                a.dh0_out[bh * DK * DK + row * DK + col0 + l16] = dS[t][j];
+            }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Gradient pass: one block of 8 waves per (b, query/key head, chunk); the value heads that
+// read the query/key head run in turn and their dq, dk are summed in registers (wave w
+// holds columns 16 w .. + 15 of dq and dk for the 64 tokens). Per value head, in two
+// panels of 64 columns of dv:
+//   B  (waves 0-3, one 16-column slice each) X = V - e^Gam K S and U = That X; (waves 4-7)
+//      dU = P^T dO + e^{Gam_C - Gam} K dS'; X, U, e^{Gam_C - Gam} U and dU go to LDS
+//      transposed (columns of dv as rows);
+//   C  Zf, Zg, Zh (contractions over the panel's columns) into dq, dk and, through their
+//      row products with q and k, into dGam; dP and dThat (lower 16x16 tiles) accumulated
+//      over both panels;
+// then D: PD, dT = dThat diag(beta) (Tinv and P read row-major), Y = dT Tinv^T,
+// dA = -Tinv^T Y, K K^T, E, and dq += PD K, dk += PD^T Q + E K + E^T K. Per-token sums
+// (dGam, dbeta) go through one LDS row per wave and are added in a fixed order, so the
+// result does not depend on timing.
+// ----------------------------------------------------------------------------
+constexpr int G_K = 0, G_Q = G_K + 64 * KPB, G_ST = G_Q + 64 * KPB, G_DST = G_ST + 64 * KPB,
+              G_V = G_DST + 64 * KPB, G_DO = G_V + 64 * SPB, G_DX = G_DO + 64 * SPB, G_XT = G_DX + 64 * SPB,
+              G_UET = G_XT + 64 * SPB, G_UT = G_UET + 64 * SPB, G_DUT = G_UT + 64 * SPB, G_VEC = G_DUT + 64 * SPB,
+              G_SIZE = G_VEC + (4 * 64 + 2 * 8 * 64 + 32) * 4;
+// Phase D reuses: Tinv (row-major) in G_ST, P in G_DST, PD^T in G_XT, dT^T in G_UT, Y^T in
+// G_UET, E^T in G_DUT.
+
+// The 10 lower-triangle 16x16 tiles (ri >= ci) of a 64x64 matrix.
+__device__ __forceinline__ void lower_tile(int q, int& ri, int& ci) {
+    ri = q < 1 ? 0 : q < 3 ? 1 : q < 6 ? 2 : 3;
+    ci = q - (ri * (ri + 1)) / 2;
+}
+__device__ __forceinline__ float wave_sum(float x) { return col_sum4(row_sum16(x)); }
+__device__ __forceinline__ u32x2 pack4(const f32x4& v) { return u32x2{pk2(v[0], v[1]), pk2(v[2], v[3])}; }
+
+// Lane index as a value the compiler must re-derive where it is used: the per-lane LDS
+// addresses of each phase are then formed in that phase instead of being hoisted out of
+// the loops and kept live (LDS offsets above 64 KiB do not fit the instruction's
+// immediate field, so every hoisted address would hold a register).
+__device__ __forceinline__ int fresh_lane(int lane) {
+    asm volatile("" : "+v"(lane));
+    return lane;
+}
+
+__global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
+    __shared__ __align__(16) unsigned char sm[G_SIZE];
+    const int NT = a.NT;
+    const int n = static_cast<int>(blockIdx.x % static_cast<unsigned>(NT));
+    const int bq = static_cast<int>(blockIdx.x / static_cast<unsigned>(NT));
+    const int hq = bq % a.Hqk, b = bq / a.Hqk;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, NT);
+    const int64_t nvalid = rs.valid;
+    const int rep = a.H / a.Hqk;
+    const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK, v_row = static_cast<int64_t>(a.H) * DK;
+    const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+    float* gam_s = reinterpret_cast<float*>(sm + G_VEC);
+    float* beta_s = gam_s + 64;
+    float* eg_s = gam_s + 128;
+    float* egc_s = gam_s + 192;
+    float* part_g = gam_s + 256;   // [8 waves][64 tokens]
+    float* part_b = gam_s + 768;
+    float* misc = gam_s + 1280;    // e^{Gam_C}, per-wave W sums, per-wave <dS', S>
+    const int m = wave;            // dq / dk column tile of this wave
+
+    // K and Q of the chunk, zero past the valid tokens
+    {
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(a.k) + rs.start * qk_row, nvalid * qk_row * 2);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(a.q) + rs.start * qk_row, nvalid * qk_row * 2);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = tid + 512 * u, mat = p >> 10, e = p & 1023, row = e >> 4, gr = e & 15;
+            const uint32_t off = static_cast<uint32_t>(((t0 + row) * qk_row + hq * DK + 8 * gr) * 2);
+            *reinterpret_cast<u32x4*>(sm + (mat ? G_Q : G_K) + row * KPB + 16 * gr) = gload16(mat ? rq : rk, off, 0);
+        }
+    }
+    f32x4 dq_acc[4], dk_acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dq_acc[r] = dk_acc[r] = zero4();
+
+    for (int kk = 0; kk < rep; ++kk) {
+        const int h = hq * rep + kk;
+        const int64_t bh = static_cast<int64_t>(b) * a.H + h, ch = bh * NT + n;
+        // decay vectors of the chunk
+        if (wave == 0) {
+            const int64_t t = t0 + lane;
+            const bool valid = t < nvalid;
+            const int64_t gi = (rs.start + (valid ? t : 0)) * a.H + h;
+            const float gv = valid ? a.g[gi] : 0.f, bv = valid ? a.beta[gi] : 0.f;
+            const float gam = wave_scan64(gv);
+            const float gamC = __shfl(gam, 63);
+            gam_s[lane] = gam;
+            beta_s[lane] = bv;
+            eg_s[lane] = __expf(gam);
+            egc_s[lane] = __expf(gamC - gam);
+            if (lane == 0) misc[0] = __expf(gamC);
+        }
+        for (int p = tid; p < 1024; p += 512) part_g[p] = 0.f;   // part_g and part_b
+        float sdot = 0.f, wsum = 0.f;
+        f32x4 acc_pt[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) acc_pt[i] = zero4();
+        __syncthreads();
+
+        for (int pn = 0; pn < 2; ++pn) {
+            // ---- A: the panel's rows of S^T and dS'^T, and its columns of V, dO, dX ----
+            {
+                const uint16_t* st = static_cast<const uint16_t*>(a.states) + (ch * DK + 64 * pn) * DK;
+                const uint16_t* dst = static_cast<const uint16_t*>(a.dstates) + (ch * DK + 64 * pn) * DK;
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int p = tid + 512 * u, row = p >> 4, gr = p & 15;
+                    const u32x4 s1 = *reinterpret_cast<const u32x4*>(st + row * DK + 8 * gr);
+                    const u32x4 s2 = *reinterpret_cast<const u32x4*>(dst + row * DK + 8 * gr);
+                    *reinterpret_cast<u32x4*>(sm + G_ST + row * KPB + 16 * gr) = s1;
+                    *reinterpret_cast<u32x4*>(sm + G_DST + row * KPB + 16 * gr) = s2;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sdot += __uint_as_float(s1[e] << 16) * __uint_as_float(s2[e] << 16) +
+                                __uint_as_float(s1[e] & 0xFFFF0000u) * __uint_as_float(s2[e] & 0xFFFF0000u);
+                }
+                const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(a.v) + rs.start * v_row, nvalid * v_row * 2);
+                const __amdgpu_buffer_rsrc_t rd = make_rsrc(static_cast<const uint16_t*>(a.d_o) + rs.start * v_row, nvalid * v_row * 2);
+                {
+                    const int row = tid >> 3, gr = tid & 7;
+                    const uint32_t off = static_cast<uint32_t>(((t0 + row) * v_row + h * DK + 64 * pn + 8 * gr) * 2);
+                    *reinterpret_cast<u32x4*>(sm + G_V + row * SPB + 16 * gr) = gload16(rv, off, 0);
+                    *reinterpret_cast<u32x4*>(sm + G_DO + row * SPB + 16 * gr) = gload16(rd, off, 0);
+                }
+                const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.dv_out + rs.start * v_row, nvalid * v_row * 4);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int p = tid + 512 * u, row = p >> 4, q4 = p & 15;
+                    const uint32_t off = static_cast<uint32_t>(((t0 + row) * v_row + h * DK + 64 * pn + 4 * q4) * 4);
+                    const f32x4 x = __builtin_bit_cast(f32x4, gload16(rx, off, 0));
+                    const float sc = -eg_s[row];
+                    *reinterpret_cast<u32x2*>(sm + G_DX + row * SPB + 8 * q4) =
+                        u32x2{pk2(sc * x[0], sc * x[1]), pk2(sc * x[2], sc * x[3])};
+                }
+            }
+            __syncthreads();
+            // ---- B ----
+            {
+                const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+                // That (waves 0-3) or P^T (waves 4-7) fragments of the chunk
+                bf16x8 rf[6];
+                {
+                    const uint16_t* rp = static_cast<const uint16_t*>(wave < 4 ? a.ws.that : a.rec.pT) + ch * kTriRecord;
+#pragma unroll
+                    for (int j = 0; j < 6; ++j) rf[j] = *reinterpret_cast<const bf16x8*>(rp + j * 512 + lane * 8);
+                }
+                const int sg = wave & 3;
+                f32x4 acc[4];
+                const int sel = wave < 4 ? G_ST : G_DST;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[r] = zero4();
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[r] = mfma16(frag_rowmajor(sm + G_K, KPB, 16 * r, 32 * s, l16, g4),
+                                        frag_rowmajor(sm + sel, KPB, 16 * sg, 32 * s, l16, g4), acc[r]);
+                }
+                unsigned char* colrow = sm + (16 * sg + l16) * SPB + 8 * g4;   // + region + 32 r
+                if (wave < 4) {
+                    f32x4 x[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const f32x4 vv = tile_acc_order(sm + G_V, SPB, 16 * r, 16 * sg, l16, g4);
+                        const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_s + 16 * r + 4 * g4);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) x[r][j] = vv[j] - eg[j] * acc[r][j];
+                    }
+                    bf16x8 xb[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) xb[s] = pack_frag(x[2 * s], x[2 * s + 1]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        f32x4 u = zero4();
+#pragma unroll
+                        for (int s = 0; s <= r / 2; ++s) u = mfma16(rf[tri_block(r, s)], xb[s], u);
+                        const f32x4 egc = *reinterpret_cast<const f32x4*>(egc_s + 16 * r + 4 * g4);
+                        f32x4 ue;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ue[j] = egc[j] * u[j];
+                        *reinterpret_cast<u32x2*>(colrow + G_XT + 32 * r) = pack4(x[r]);
+                        *reinterpret_cast<u32x2*>(colrow + G_UT + 32 * r) = pack4(u);
+                        *reinterpret_cast<u32x2*>(colrow + G_UET + 32 * r) = pack4(ue);
+                    }
+                } else {
+                    u32x2 dor[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dor[r] = lds_read_tr(sm + G_DO + (16 * r + 4 * g4 + (l16 >> 2)) * SPB + (16 * sg + 4 * (l16 & 3)) * 2);
+                    bf16x8 dob[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+                        dob[s] = __builtin_bit_cast(bf16x8, u32x4{dor[2 * s][0], dor[2 * s][1], dor[2 * s + 1][0], dor[2 * s + 1][1]});
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        f32x4 pd = zero4();
+#pragma unroll
+                        for (int s = (r < 2 ? 0 : 1); s < 2; ++s) pd = mfma16(rf[tri_up(r, s)], dob[s], pd);
+                        const f32x4 egc = *reinterpret_cast<const f32x4*>(egc_s + 16 * r + 4 * g4);
+                        f32x4 du;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) du[j] = pd[j] + egc[j] * acc[r][j];
+                        *reinterpret_cast<u32x2*>(colrow + G_DUT + 32 * r) = pack4(du);
+                    }
+                }
+            }
+            __syncthreads();
+            // ---- C ----
+            {
+                const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f32x4 zf = zero4(), zg = zero4(), zh = zero4();
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const bf16x8 stf = frag_kmajor(sm + G_ST, KPB, 32 * s, 16 * m, l16, g4);
+                        zf = mfma16(frag_rowmajor(sm + G_DO, SPB, 16 * r, 32 * s, l16, g4), stf, zf);
+                        zg = mfma16(frag_rowmajor(sm + G_DX, SPB, 16 * r, 32 * s, l16, g4), stf, zg);
+                        zh = mfma16(frag_kmajor(sm + G_UET, SPB, 32 * s, 16 * r, l16, g4),
+                                    frag_kmajor(sm + G_DST, KPB, 32 * s, 16 * m, l16, g4), zh);
+                    }
+                    const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_s + 16 * r + 4 * g4);
+                    const f32x4 qv = tile_acc_order(sm + G_Q, KPB, 16 * r, 16 * m, l16, g4);
+                    const f32x4 kv = tile_acc_order(sm + G_K, KPB, 16 * r, 16 * m, l16, g4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        zf[j] *= eg[j];
+                        wsum += zh[j] * kv[j];
+                        const float gp = row_sum16(zf[j] * qv[j] + (zg[j] - zh[j]) * kv[j]);
+                        if (l16 == 0) part_g[wave * 64 + 16 * r + 4 * g4 + j] += gp;
+                        dq_acc[r][j] += zf[j];
+                        dk_acc[r][j] += zg[j] + zh[j];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);   // keeps each tile's operand reads with it
+                }
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    const int item = wave + 8 * i;
+                    if (item >= 20) break;
+                    int ri, ci;
+                    lower_tile(item % 10, ri, ci);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        if (item < 10)
+                            acc_pt[i] = mfma16(frag_rowmajor(sm + G_DO, SPB, 16 * ri, 32 * s, l16, g4),
+                                               frag_kmajor(sm + G_UT, SPB, 32 * s, 16 * ci, l16, g4), acc_pt[i]);
+                        else
+                            acc_pt[i] = mfma16(frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * ri, l16, g4),
+                                               frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * ci, l16, g4), acc_pt[i]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+
+        // ---- D0: Tinv and P row-major; the upper tiles of PD^T, dT^T and E^T are zero ----
+        {
+            const int row = tid >> 3, gr = tid & 7;
+            *reinterpret_cast<u32x4*>(sm + G_ST + row * SPB + 16 * gr) =
+                *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.rec.t_rm) + ch * 4096 + row * 64 + 8 * gr);
+            *reinterpret_cast<u32x4*>(sm + G_DST + row * SPB + 16 * gr) =
+                *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.rec.p_rm) + ch * 4096 + row * 64 + 8 * gr);
+            // transposed storage [j][i]: tiles (row tile jt, column tile it) with it < jt
+            for (int p = tid; p < 3 * 6 * 32; p += 512) {
+                const int mat = p / 192, e = p % 192, tq = e >> 5, w16 = e & 31;
+                const int jt = tq < 1 ? 1 : tq < 3 ? 2 : 3, it = tq - (jt * (jt - 1)) / 2;
+                const int region = mat == 0 ? G_XT : mat == 1 ? G_UT : G_DUT;
+                *reinterpret_cast<u32x4*>(sm + region + (16 * jt + (w16 >> 1)) * SPB + 32 * it + 16 * (w16 & 1)) =
+                    u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        __syncthreads();
+        // ---- D1: PD and dT from the dP and dThat tiles ----
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+            const int item = wave + 8 * i;
+            if (item >= 20) break;
+            int ri, ci;
+            lower_tile(item % 10, ri, ci);
+            const int J = 16 * ci + l16;
+            const float gamJ = gam_s[J], betaJ = beta_s[J];
+            f32x4 outv;
+            float colacc = 0.f;
+            const f32x4 mv = tile_acc_order(sm + (item < 10 ? G_DST : G_ST), SPB, 16 * ri, 16 * ci, l16, g4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int I = 16 * ri + 4 * g4 + j;
+                const float d = I >= J ? acc_pt[i][j] : 0.f;
+                if (item < 10) {
+                    const float x = d * mv[j];   // dP . P
+                    const float rsum = row_sum16(x);
+                    if (l16 == 0) part_g[wave * 64 + I] += rsum;
+                    colacc += x;
+                    outv[j] = I >= J ? d * __expf(gam_s[I] - gamJ) : 0.f;
+                } else {
+                    colacc += d * mv[j];          // dThat . Tinv
+                    outv[j] = d * betaJ;
+                }
+            }
+            colacc = col_sum4(colacc);
+            if (g4 == 0) {
+                if (item < 10) part_g[wave * 64 + J] -= colacc;
+                else part_b[wave * 64 + J] += colacc;
+            }
+            *reinterpret_cast<u32x2*>(sm + (item < 10 ? G_XT : G_UT) + J * SPB + (16 * ri + 4 * g4) * 2) = pack4(outv);
+        }
+        __syncthreads();
+        // ---- D2: Y = dT Tinv^T (stored as Y^T), and K K^T on the tiles of D3 ----
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+            const int yt = 2 * wave + i, yi = yt >> 2, yj = yt & 3;
+            f32x4 y = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                y = mfma16(frag_kmajor(sm + G_UT, SPB, 32 * s, 16 * yi, l16, g4),
+                           frag_rowmajor(sm + G_ST, SPB, 16 * yj, 32 * s, l16, g4), y);
+            *reinterpret_cast<u32x2*>(sm + G_UET + (16 * yj + l16) * SPB + (16 * yi + 4 * g4) * 2) = pack4(y);
+        }
+        f32x4 kkt[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+            kkt[i] = zero4();
+            const int q = wave + 8 * i;
+            if (q >= 10) break;
+            int ri, ci;
+            lower_tile(q, ri, ci);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                kkt[i] = mfma16(frag_rowmajor(sm + G_K, KPB, 16 * ri, 32 * s, l16, g4),
+                                frag_rowmajor(sm + G_K, KPB, 16 * ci, 32 * s, l16, g4), kkt[i]);
+        }
+        __syncthreads();
+        // ---- D3: dA = -Tinv^T Y (strictly lower), E, and their dbeta / dGam terms ----
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+            const int q = wave + 8 * i;
+            if (q >= 10) break;
+            int ri, ci;
+            lower_tile(q, ri, ci);
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                acc = mfma16(frag_kmajor(sm + G_ST, SPB, 32 * s, 16 * ri, l16, g4),
+                             frag_rowmajor(sm + G_UET, SPB, 16 * ci, 32 * s, l16, g4), acc);
+            const int J = 16 * ci + l16;
+            const float gamJ = gam_s[J];
+            f32x4 ev;
+            float colacc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int I = 16 * ri + 4 * g4 + j;
+                const bool lower = I > J;
+                const float ex = lower ? __expf(gam_s[I] - gamJ) : 0.f;
+                const float da = lower ? -acc[j] : 0.f;
+                const float dbr = row_sum16(da * kkt[i][j] * ex);
+                const float e = da * beta_s[I] * ex;
+                const float x = e * kkt[i][j];
+                const float rsum = row_sum16(x);
+                if (l16 == 0) {
+                    part_b[wave * 64 + I] += dbr;
+                    part_g[wave * 64 + I] += rsum;
+                }
+                colacc += x;
+                ev[j] = e;
+            }
+            colacc = col_sum4(colacc);
+            if (g4 == 0) part_g[wave * 64 + J] -= colacc;
+            *reinterpret_cast<u32x2*>(sm + G_DUT + J * SPB + (16 * ri + 4 * g4) * 2) = pack4(ev);
+        }
+        __syncthreads();
+        // ---- D4: dq += PD K, dk += PD^T Q + E K + E^T K ----
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 kt = frag_kmajor(sm + G_K, KPB, 32 * s, 16 * m, l16, g4);
+                const bf16x8 qt = frag_kmajor(sm + G_Q, KPB, 32 * s, 16 * m, l16, g4);
+                dq_acc[r] = mfma16(frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * r, l16, g4), kt, dq_acc[r]);
+                dk_acc[r] = mfma16(frag_rowmajor(sm + G_XT, SPB, 16 * r, 32 * s, l16, g4), qt, dk_acc[r]);
+                dk_acc[r] = mfma16(frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * r, l16, g4), kt, dk_acc[r]);
+                dk_acc[r] = mfma16(frag_rowmajor(sm + G_DUT, SPB, 16 * r, 32 * s, l16, g4), kt, dk_acc[r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        {
+            const float ws = wave_sum(wsum), sd = wave_sum(sdot);
+            if (lane == 0) {
+                misc[1 + wave] = ws;
+                misc[9 + wave] = sd;
+            }
+        }
+        __syncthreads();
+        // ---- D5: dGam and dbeta per token, dg = reverse cumulative sum of dGam ----
+        if (wave == 0) {
+            float dgam = 0.f, db = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                dgam += part_g[w * 64 + lane];
+                db += part_b[w * 64 + lane];
+            }
+            if (lane == 63) {
+                float ws = 0.f, sd = 0.f;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    ws += misc[1 + w];
+                    sd += misc[9 + w];
+                }
+                dgam += ws + misc[0] * sd;
+            }
+            const float inc = wave_scan64(dgam);
+            const float dg = __shfl(inc, 63) - inc + dgam;
+            const int64_t t = t0 + lane;
+            if (t < a.T) {
+                const bool valid = t < nvalid;
+                a.dg_out[(rs.start + t) * a.H + h] = valid ? dg : 0.f;
+                a.dbeta_out[(rs.start + t) * a.H + h] = valid ? db : 0.f;
+            }
+        }
+        __syncthreads();
+    }
+    // dq and dk of the query/key head (zero past the valid tokens)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = t0 + 16 * r + 4 * g4 + j;
+            if (t < a.T) {
+                const bool valid = t < nvalid;
+                const int64_t o = ((rs.start + t) * a.Hqk + hq) * DK + 16 * m + l16;
+                a.dq_out[o] = valid ? dq_acc[r][j] : 0.f;
+                a.dk_out[o] = valid ? dk_acc[r][j] : 0.f;
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_state_mfma(const BwdMfmaArgs& a, hipStream_t s) {
+    int qk_groups = a.B * a.Hqk;
+    const unsigned nblk = static_cast<unsigned>(((qk_groups + 7) / 8) * 8 * (a.H / a.Hqk) * (DK / 16));
+    void* args[] = {const_cast<BwdMfmaArgs*>(&a), &qk_groups};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_state_mfma), dim3(nblk), dim3(512), args, 0, s);
+}
+
+hipError_t launch_bwd_grad_mfma(const BwdMfmaArgs& a, hipStream_t s) {
+    const int64_t nblk = static_cast<int64_t>(a.B) * a.Hqk * a.NT;
+    if (nblk == 0) return hipSuccess;
+    void* args[] = {const_cast<BwdMfmaArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_grad_mfma), dim3(static_cast<unsigned>(nblk)), dim3(512),
+                           args, 0, s);
+}
+
+}  // namespace gdn

@@ -102,6 +102,19 @@ struct PrepConv {
     int C, K;
 };
 
+// Records the prepare pass writes in addition for the matrix-core backward (all NULL in
+// the forward), bf16, one per (b, h, chunk):
+//   thatT, pT  That^T and P^T as the 6 upper-triangle 16x32 blocks (r, s) of the A operand of
+//              v_mfma_f32_16x16x32_bf16 (lane l: row 16r + l % 16 at tokens 32s + 4 (l / 16) +
+//              (e % 4) + 16 (e / 4), e = 0..7), blocks (0,0) (0,1) (1,0) (1,1) (2,1) (3,1);
+//   t_rm, p_rm Tinv = (I + A)^{-1} and P, row-major [64][64].
+struct BwdRecords {
+    void* thatT = nullptr;
+    void* pT = nullptr;
+    void* t_rm = nullptr;
+    void* p_rm = nullptr;
+};
+
 struct PrepArgs {
     int B, T, H, Hqk, dk, NT;
     const void* q;
@@ -116,6 +129,7 @@ struct PrepArgs {
     Prologue pro;
     int has_conv;           // the Conv1D runs in the pass (requires the prologue; q, k unused)
     PrepConv conv;
+    BwdRecords bwd;         // matrix-core backward only
 };
 
 struct StateArgs {
@@ -138,6 +152,8 @@ struct StateArgs {
     int store_mode;
     float* m_out;                     // matrix-core path: with v and no o, the M summary
                                       // (ncols = dk) computed in the same pass as S; else NULL
+    void* states = nullptr;           // matrix-core path, pass kPassS: bf16 [B,H,NT,ncols,dk], the
+                                      // state entering every chunk, transposed; or NULL
 };
 
 // Reverse of the prefix combine (gdn_summary_combine_bwd): G = dhT (or 0); for p = P-1
@@ -200,6 +216,33 @@ struct BwdArgs {
     int accumulate;           // add into dq, dk, dv, dg, dbeta instead of writing them
 };
 
+// Chunked matrix-core backward (gdn_bwd_mfma.hip; bf16, dk = dv = 128). The prepare pass
+// writes the forward records and BwdRecords; the forward state pass (kPassS with states)
+// writes the state S_n entering every chunk; bwd_state_mfma runs the reverse chain per
+// (b, h, 16 columns), writing dv and the gradient dS_n of the state leaving every chunk;
+// bwd_grad_mfma forms dq, dk, dg and dbeta per (b, query/key head, chunk).
+struct BwdMfmaArgs {
+    int B, T, H, Hqk, NT;
+    const void* q;            // [B,T,Hqk,128] bf16
+    const void* k;
+    const void* v;            // [B,T,H,128] bf16
+    const void* d_o;          // [B,T,H,128] bf16
+    const float* g;           // [B,T,H]
+    const float* beta;
+    const float* dhT;         // [B,H,128,128] or NULL
+    const int32_t* valid_len;
+    Workspace ws;             // that, pmat, gates of the prepare pass
+    BwdRecords rec;
+    const void* states;       // bf16 [B,H,NT,128 (dv),128 (dk)]: S_n^T
+    void* dstates;            // bf16 [B,H,NT,128,128]: the gradient of the state leaving chunk n, transposed
+    float* dq_out;            // [B,T,Hqk,128]
+    float* dk_out;
+    float* dv_out;            // [B,T,H,128]
+    float* dg_out;            // [B,T,H]
+    float* dbeta_out;
+    float* dh0_out;           // [B,H,128,128] or NULL
+};
+
 // Layer steps around the core (gdn_layer_ops.hip).
 struct ConvArgs {
     int B, T, C, K, silu;
@@ -226,6 +269,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s);
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, bool io_bf16, hipStream_t s);
+hipError_t launch_bwd_state_mfma(const BwdMfmaArgs& a, hipStream_t s);
+hipError_t launch_bwd_grad_mfma(const BwdMfmaArgs& a, hipStream_t s);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s);
 hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool io_bf16, hipStream_t s);

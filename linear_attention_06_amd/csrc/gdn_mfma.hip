@@ -19,33 +19,17 @@
 //   16x16x32 bf16 (state pass), g = l / 16: A row l%16, k = 8g .. 8g+7; B col l%16,
 //     k = 8g .. 8g+7; C register j holds row 4g + j, col l%16.
 //   16x16x4 f32: A row l%16, k = l/16;  B col l%16, k = l/16;  C rows 4(l/16)+j, col l%16.
-#include "gdn_internal.hpp"
+#include "gdn_mfma_common.hpp"
 
 namespace gdn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int DK = 128;
 constexpr int CP = 64 + 8;   // LDS pitch (bf16) of 64-wide rows: 144 B
-// That and P leave the prepare kernel as the 6 lower-triangle 16x32 blocks (r, s),
-// s <= r / 2, of 64 lanes x 8 bf16 each; block (r, s) sits at position tri_block(r, s).
-constexpr int kTriRecord = kTriRecordElems;
 constexpr bool kEnablePrefetch = true;   // L2 prefetch of chunk operands by the output wave
-__host__ __device__ constexpr int tri_block(int r, int s) { return r < 2 ? r : 2 + 2 * (r - 2) + s; }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-// A compile-time integer as a value (template arguments of generic lambdas).
-template <int V>
-struct IntTag {
-    static constexpr int value = V;
-};
 __device__ __forceinline__ f32x4 mfma16f32(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
@@ -55,25 +39,11 @@ __device__ __forceinline__ f32x16 zero16() {
     for (int i = 0; i < 16; ++i) z[i] = 0.f;
     return z;
 }
-// Inclusive prefix sum over each row of 16 lanes with DPP row shifts by 1, 2, 4, 8
-// (lanes shifted in from outside the row read 0): lane 15 of a row ends with the row total.
-__device__ __forceinline__ float row_prefix16(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
-    return x;
-}
 __device__ __forceinline__ int64_t valid_tokens(const int32_t* vl, int b, int64_t T) {
     if (!vl) return T;
     int64_t n = vl[b];
     return n < 0 ? 0 : (n > T ? T : n);
 }
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
-__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float(static_cast<uint32_t>(u) << 16); }
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 // Workgroup barrier that orders LDS only. __syncthreads() also waits for every
 // outstanding global load and store of the wave, which would stall the loads
 // issued one chunk ahead at every barrier; the waves here exchange data through
@@ -506,6 +476,42 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.pmat) + off) = wp;
         if (a.ws.that_lo) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.that_lo) + off) = wl;
     }
+    if (a.bwd.thatT) {
+        // backward records: That^T (That^T_ij = Tinv_ji beta_i) and P^T on the upper blocks
+        // (0,0) (0,1) (1,0) (1,1) (2,1) (3,1) in the same fragment order, then Tinv and P
+        // row-major (Tinv and P are exactly zero above their diagonals in LDS)
+        for (int p = tid; p < 6 * 64; p += 256) {
+            const int blk = p >> 6, l = p & 63;
+            const int r = blk < 4 ? blk >> 1 : blk - 2;
+            const int s = blk < 4 ? blk & 1 : 1;
+            const int i = 16 * r + (l & 15), g = l >> 4;
+            const float bi = beta_s[i];
+            u32x4 w, wp;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int j0 = 32 * s + 4 * g + 2 * (e2 & 1) + 16 * (e2 >> 1), j1 = j0 + 1;
+                w[e2] = pk2(t_s[j0 * AP + i] * bi, t_s[j1 * AP + i] * bi);
+                wp[e2] = p_s[j0 * CP + i] | (static_cast<uint32_t>(p_s[j1 * CP + i]) << 16);
+            }
+            const int64_t off = ch * kTriRecord + blk * 512 + l * 8;
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.bwd.thatT) + off) = w;
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.bwd.pT) + off) = wp;
+        }
+        for (int p = tid; p < 2 * 512; p += 256) {
+            const int row = (p & 511) >> 3, c0 = 8 * (p & 7);
+            u32x4 w;
+            if (p < 512) {
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) w[e2] = pk2(t_s[row * AP + c0 + 2 * e2], t_s[row * AP + c0 + 2 * e2 + 1]);
+            } else {
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2)
+                    w[e2] = p_s[row * CP + c0 + 2 * e2] | (static_cast<uint32_t>(p_s[row * CP + c0 + 2 * e2 + 1]) << 16);
+            }
+            void* dst = p < 512 ? a.bwd.t_rm : a.bwd.p_rm;
+            *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(dst) + ch * 4096 + row * 64 + c0) = w;
+        }
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -550,82 +556,6 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
 // V'' and That enter the MFMAs as bf16 hi + lo pairs (x = hi + lo, lo the bf16 of
 // the remainder), the products taken as hi*hi + hi*lo + lo*hi.
 // ----------------------------------------------------------------------------
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-// Two accumulator tiles (4 rows each per lane) as one bf16 B fragment.
-__device__ __forceinline__ bf16x8 pack_frag(const f32x4& a, const f32x4& b) {
-    bf16x8 f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        f[u] = static_cast<__bf16>(a[u]);
-        f[4 + u] = static_cast<__bf16>(b[u]);
-    }
-    return f;
-}
-// hi + lo split of the same pair: hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ void pack_frag_split(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const __bf16 ha = static_cast<__bf16>(a[u]), hb = static_cast<__bf16>(b[u]);
-        hi[u] = ha;
-        hi[4 + u] = hb;
-        lo[u] = static_cast<__bf16>(a[u] - static_cast<float>(ha));
-        lo[4 + u] = static_cast<__bf16>(b[u] - static_cast<float>(hb));
-    }
-}
-__device__ __forceinline__ uint32_t pk2(float a, float b) {
-    return bf16_bits(a) | (static_cast<uint32_t>(bf16_bits(b)) << 16);
-}
-__device__ __forceinline__ bf16x8 lds_frag_b(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane i receives element (i % 4) of the 8-byte pieces addressed by lanes
-// i/4, 4 + i/4, 8 + i/4, 12 + i/4 of its group.
-__device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* p) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-    lds_bf16x4* lp = (lds_bf16x4*)(const_cast<unsigned char*>(p));   // generic to LDS address space
-#pragma clang diagnostic pop
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lp));
-}
-__device__ __forceinline__ f32x4 bf16x4_to_f32(u32x2 v) {
-    return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
-                 __uint_as_float(v[1] & 0xFFFF0000u)};
-}
-
-constexpr int kBufferFlags = 0x00020000;   // raw buffer descriptor word 3 on gfx9-family GPUs
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-    const int32_t n = static_cast<int32_t>(bytes < 0 ? 0 : bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kBufferFlags);
-}
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-#pragma clang diagnostic pop
-}
-// 16-byte load per lane from byte voff + off of a buffer into registers. The whole
-// byte offset goes into the per-lane (VGPR) offset and the scalar offset is 0: the
-// range check of a raw buffer covers the VGPR and instruction offsets only, so an
-// offset placed in the scalar operand would let rows past the descriptor's end load
-// real memory instead of zero.
-__device__ __forceinline__ u32x4 gload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + off, 0, 0));
-}
-// Barrier of the state pass: this wave's LDS accesses complete, then s_barrier
-// (optionally after all of its vector-memory accesses). One asm statement with a
-// memory clobber, so the compiler keeps LDS accesses on their side of it.
-__device__ __forceinline__ void chunk_barrier(bool vm_wait) {
-    if (vm_wait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Loading wave (index among the loading waves) that issues load g of an iteration.
 // Waves w and w + 4 of a workgroup run on the same SIMD; the deal gives every SIMD
@@ -1105,6 +1035,16 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         for (int s = 0; s < 4; ++s) {
             if constexpr (cSplit) pack_frag_split(S[2 * s], S[2 * s + 1], sb[s], sbl[s]);
             else sb[s] = pack_frag(S[2 * s], S[2 * s + 1]);
+        }
+        if constexpr (cHasV && !cSplit) {
+            // for the backward: the state entering chunk n as bf16, transposed (lane (c, g)
+            // holds column c at rows 32 s + 8 g .. + 7)
+            if (a.states) {
+                uint16_t* st = static_cast<uint16_t*>(a.states) +
+                               ((bh * a.NT + n) * ncols + col0 + l16) * DK + 8 * g4;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(st + 32 * s) = sb[s];
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 

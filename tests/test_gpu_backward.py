@@ -1,7 +1,12 @@
 """GPU parity of the backward (gdn_chunk_bwd) against the fp64 autograd oracle on the
 same seeded inputs: all six gradients, with and without initial state and final-state
 gradient, padded rows, grouped heads, bf16 and fp32 inputs, head dims 16 to 128, and
-lengths that end inside a chunk."""
+lengths that end inside a chunk.
+
+bf16 inputs with heads of 128 run the chunked matrix-core backward (bf16 operands, fp32
+accumulation) and are held to the pages' bf16 bound on gradients (hyper-parallel issue
+#320, section 4.2); every other problem runs the fp32 token-level backward, held to the
+fp32 bound."""
 import dataclasses
 
 import numpy as np
@@ -9,7 +14,7 @@ import pytest
 import torch
 
 from oracle import backward
-from gpu_common import TOL_F32, dev, np_f64, sync, to_dev, workload_inputs
+from gpu_common import TOL_BF16, TOL_F32, dev, np_f64, sync, to_dev, workload_inputs
 from helpers import rel_l2
 from linear_attention_06_amd import gdn
 from linear_attention_06_amd.inputs import WORKLOADS, make_inputs
@@ -52,11 +57,12 @@ def test_backward_matches_oracle(case):
     qf, kf, vf, gf, bf, h0f = inp.f64()
     ref = backward.gdn_bwd(qf, kf, vf, gf, bf, h0f if with_h0 else None, d_o.astype(np.float64),
                            None if dhT is None else dhT.astype(np.float64), inp.valid_len)
+    tol = TOL_BF16 if (io == "bf16" and d == 128) else TOL_F32
     for nm, x, r in zip(NAMES, got, ref):
         err = rel_l2(np_f64(x), r)
         print("%s %s rel-L2 %.3e" % (name, nm, err))
         assert np.all(np.isfinite(np_f64(x))), nm
-        assert err <= TOL_F32, "%s %s rel-L2 %.3e > %.0e" % (name, nm, err, TOL_F32)
+        assert err <= tol, "%s %s rel-L2 %.3e > %.0e" % (name, nm, err, tol)
     if valid is not None:
         for r_ in range(B):
             n = int(inp.valid_len[r_])
@@ -102,7 +108,7 @@ def test_backward_full_size_sampled_against_oracle():
     for nm, x, r in zip(NAMES, got, ref):
         err = rel_l2(np_f64(x), r)
         print("8k sampled %s rel-L2 %.3e" % (nm, err))
-        assert err <= TOL_F32, nm
+        assert err <= TOL_BF16, nm
 
 
 def test_initial_state_gradient_is_the_summary_transpose():
@@ -124,7 +130,7 @@ def test_initial_state_gradient_is_the_summary_transpose():
     err = rel_l2(np_f64(dh0), np_f64(want))
     print("dh0 vs M^T dhT rel-L2 %.3e (|M^T dhT| / |dhT| = %.3f)" % (err, ratio))
     assert ratio > 0.05
-    assert err <= 1e-3
+    assert err <= TOL_BF16
 
 
 def test_backward_full_size_every_token_live():
@@ -155,5 +161,5 @@ def test_backward_full_size_every_token_live():
         sma = scaled_max_abs(xn, r)
         print("8k live %s rel-L2 %.3e (last 1024 tokens %.3e), scaled max-abs %.3e" % (nm, err, late, sma))
         assert np.all(np.isfinite(xn)), nm
-        assert err <= TOL_F32 and late <= TOL_F32, nm
+        assert err <= TOL_BF16 and late <= TOL_BF16, nm
         assert sma <= TOL_MAXABS, nm
