@@ -62,33 +62,53 @@ __device__ __forceinline__ float wave_scan64(float x) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, true));   // row_bcast:31
     return x;
 }
-// Sum over the 16 lanes of each row of the wave (all 16 lanes get it).
+// Sum over the 16 lanes of each row of the wave, every lane of the row gets it (DPP row
+// rotations by 8, 4, 2, 1: no LDS traffic).
 __device__ __forceinline__ float row_sum16(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
     return x;
 }
-// Sum over the four lanes l % 16 == c (lanes c, c + 16, c + 32, c + 48).
+// Sum over the four lanes l % 16 == c (lanes c, c + 16, c + 32, c + 48), every one of them
+// gets it: v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap the two halves (the
+// sum of a value and its swapped copy is the pair's sum in both lanes).
 __device__ __forceinline__ float col_sum4(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
 // ----------------------------------------------------------------------------
-// Reverse chain: one block of 8 waves per (b, h, 16 columns of dv). Wave 0 carries the
-// 128 x 16 slice of the state gradient in registers (the forward state pass's layout:
-// register t of lane (c, g), element j holds row 32 (t / 2) + 8 g + 4 (t % 2) + j of
-// column c) and walks the chunks from last to first; waves 1-7 stage each chunk's K, Q,
-// That^T and P^T records, output gradient and decay record in LDS two chunks ahead
-// (loads into registers, written to LDS one iteration later; one barrier per chunk).
+// Reverse chain: one block of 8 waves per (b, h, 16 columns of dv), chunks from last to
+// first, one barrier per iteration.
+//   wave 0 (chain) carries the 128 x 16 slice of the state gradient in registers (the
+//     forward state pass's layout: register t of lane (c, g), element j holds row
+//     32 (t / 2) + 8 g + 4 (t % 2) + j of column c) and runs the dependent part of each
+//     chunk: K dS', dU, dX = That^T dU and the update of dS (38 MFMAs);
+//   wave 1 (helper) computes one chunk ahead the terms that do not depend on the state
+//     gradient, P^T dO and Q^T diag(e^Gam) dO, and hands them over in LDS (fp32); one
+//     chunk behind it writes the chain's dX (as dv) and dS' (bf16) to memory, so that the
+//     chain wave issues no global memory instruction;
+//   waves 2-7 stage each chunk's operands two iterations ahead through registers: the
+//     chain's (K, That^T, decay record) and the helper's (Q, P^T, dO, decay record).
+// With c0 = NT - 1, iteration i has the helper on chunk c0 - i, the chain on c0 - i + 1
+// and the stores of chunk c0 - i + 2; there are NT + 2 iterations.
 // ----------------------------------------------------------------------------
-constexpr int RB_Q = 64 * KPB, RB_TT = 2 * 64 * KPB, RB_PT = RB_TT + 6144, RB_DO = RB_PT + 6144,
-              RB_G = RB_DO + 2048, RB_SIZE = RB_G + 1024;
-constexpr int kRevLoads = 16 + 16 + 6 + 6 + 2 + 1;   // 1 KiB loads per chunk
-constexpr int kRevLoaders = 7;
+// K and Q tiles in the forward state pass's layout (16 quad blocks of 4 token rows, 1 KiB
+// each; granule gk of row 4 j + rho at 16-byte slot 16 rho + (gk ^ (4 rho + j % 4))): its
+// fragment reads are free of bank conflicts and its transposing reads 2-way.
+constexpr int RK_TT = 64 * 256, RK_G = RK_TT + 6144, RK_SIZE = RK_G + 1024;             // chain side
+constexpr int RQ_PT = 64 * 256, RQ_DO = RQ_PT + 6144, RQ_G = RQ_DO + 2048, RQ_SIZE = RQ_G + 1024;   // helper side
+constexpr int RA_SIZE = 12 * 1024;   // hand-off ahead: P^T dO (4 x 1 KiB), Q^T e^Gam dO (8 x 1 KiB), fp32
+// hand-off behind: dX fp32 [64 rows][20] (a pitch of 20 floats puts the 64 lanes of each
+// write and the 16 x 4 lanes of each read on distinct banks), then dS' as [16 columns][128]
+// bf16 at a pitch of 272 bytes
+constexpr int RB_DXP = 20, RB_DX = 0, RB_DS = 64 * RB_DXP * 4, RB_SIZE2 = RB_DS + 16 * 272;
+constexpr int kRevLoadsK = 16 + 6 + 1, kRevLoadsQ = 16 + 6 + 2 + 1, kRevLoads = kRevLoadsK + kRevLoadsQ;
+constexpr int kRevLoaders = 6;
 
 __host__ __device__ constexpr int rev_loads_owned(int me) {
     int c = 0;
@@ -98,7 +118,10 @@ __host__ __device__ constexpr int rev_loads_owned(int me) {
 
 __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_groups) {
     constexpr int tiles = DK / 16;
-    __shared__ __align__(16) unsigned char stg[2 * RB_SIZE];
+    __shared__ __align__(16) unsigned char kst[2 * RK_SIZE];
+    __shared__ __align__(16) unsigned char qst[2 * RQ_SIZE];
+    __shared__ __align__(16) unsigned char ahd[2 * RA_SIZE];
+    __shared__ __align__(16) unsigned char bhd[2 * RB_SIZE2];
 
     // XCD-aware order as in the forward state pass: the column tiles of the value heads
     // that share a query/key head run on one XCD
@@ -117,10 +140,20 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
     const RowSpan rs = row_span(nullptr, a.valid_len, b, a.T, a.NT);
     const int64_t nvalid = rs.valid;
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
-    const int NT = a.NT;
+    const int NT = a.NT, c0 = NT - 1, iters = NT + 2;
     const int64_t qk_row = static_cast<int64_t>(a.Hqk) * DK, v_row = static_cast<int64_t>(a.H) * DK;
 
-    if (wave >= 1) {
+    // Fragment (token tile r, dk step s) of a K or Q tile: byte 4096 r + frag_lane[s]; the
+    // transposing read of state tile t over token step s: 8 KiB s + 8 (t % 2) + tr_lane[t / 2]
+    // and 4 KiB further for the second half of the step's tokens.
+    int frag_lane[4], tr_lane[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        frag_lane[q] = (l16 >> 2) * 1024 + 256 * (l16 & 3) + 16 * ((4 * q + g4) ^ (4 * (l16 & 3) + (l16 >> 2)));
+        tr_lane[q] = g4 * 1024 + 256 * (l16 >> 2) + 16 * ((4 * q + (l16 & 3)) ^ (4 * (l16 >> 2) + g4));
+    }
+
+    if (wave >= 2) {
         if (NT == 0) return;
         // ---------------- loading waves ----------------
         const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rs.start * qk_row;
@@ -134,80 +167,172 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
         const __amdgpu_buffer_rsrc_t rpt = make_rsrc(static_cast<const uint16_t*>(a.rec.pT) + bh * NT * kTriRecord, rec);
         const __amdgpu_buffer_rsrc_t rgt = make_rsrc(a.ws.gates + bh * NT * kGateRecordMfma,
                                                      static_cast<int64_t>(NT) * kGateRecordMfma * 4);
-        // lane l of a K / Q load: row 4 j + l / 16 of the chunk, 16 bytes at column 8 (l % 16)
-        const uint32_t voff_kq = static_cast<uint32_t>(((lane >> 4) * qk_row + hq * DK + 8 * (lane & 15)) * 2);
+        // lane l of the load of quad block j: row 4 j + l / 16, granule (l % 16) ^ (4 (l / 16) + j % 4)
+        uint32_t voff_kq[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            voff_kq[jj] = static_cast<uint32_t>(((lane >> 4) * qk_row + hq * DK + 8 * ((lane & 15) ^ (4 * (lane >> 4) + jj))) * 2);
         const uint32_t voff_l = static_cast<uint32_t>(16 * lane);
         const uint32_t voff_d = static_cast<uint32_t>(((lane >> 1) * v_row + h * DK + col0 + 8 * (lane & 1)) * 2);
         const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2), dstep = static_cast<uint32_t>(kChunk * v_row * 2);
-        // load i of a chunk belongs to loading wave i % 7; each wave's loop is compiled for
-        // its own index, so that its stage registers are indexed at compile time
+        // load i of an iteration belongs to loading wave i % 6 (i < 23: the chain side of one
+        // chunk, then the helper side of another); each wave's loop is compiled for its own
+        // index, so that its stage registers are indexed at compile time
         auto loader = [&](auto me_tag) {
         constexpr int me = decltype(me_tag)::value;
         constexpr int NS = rev_loads_owned(me);
         using Stage = u32x4[NS];
         Stage st0, st1;
-        auto load = [&](int n, Stage& st) {
-            n = n < 0 ? 0 : n;
+        // chain side of chunk ck, helper side of chunk cq (clamped to the first chunk)
+        auto load = [&](int ck, int cq, Stage& st) {
+            ck = ck < 0 ? 0 : ck;
+            cq = cq < 0 ? 0 : cq;
 #pragma unroll
             for (int i = me; i < kRevLoads; i += kRevLoaders) {
                 u32x4& r = st[i / kRevLoaders];
-                if (i < 16) r = gload16(rk, voff_kq, static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
-                else if (i < 32) r = gload16(rq, voff_kq, static_cast<uint32_t>(4 * (i - 16) * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
-                else if (i < 38) r = gload16(rtt, voff_l, static_cast<uint32_t>(n) * (kTriRecord * 2) + (i - 32) * 1024);
-                else if (i < 44) r = gload16(rpt, voff_l, static_cast<uint32_t>(n) * (kTriRecord * 2) + (i - 38) * 1024);
-                else if (i < 46) r = gload16(rd, voff_d, static_cast<uint32_t>(32 * (i - 44) * v_row * 2) + static_cast<uint32_t>(n) * dstep);
-                else r = gload16(rgt, voff_l, static_cast<uint32_t>(n) * (kGateRecordMfma * 4u));
+                if (i < 16) r = gload16(rk, voff_kq[i & 3], static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(ck) * kstep);
+                else if (i < 22) r = gload16(rtt, voff_l, static_cast<uint32_t>(ck) * (kTriRecord * 2) + (i - 16) * 1024);
+                else if (i < 23) r = gload16(rgt, voff_l, static_cast<uint32_t>(ck) * (kGateRecordMfma * 4u));
+                else if (i < 39) r = gload16(rq, voff_kq[(i - 23) & 3], static_cast<uint32_t>(4 * (i - 23) * qk_row * 2) + static_cast<uint32_t>(cq) * kstep);
+                else if (i < 45) r = gload16(rpt, voff_l, static_cast<uint32_t>(cq) * (kTriRecord * 2) + (i - 39) * 1024);
+                else if (i < 47) r = gload16(rd, voff_d, static_cast<uint32_t>(32 * (i - 45) * v_row * 2) + static_cast<uint32_t>(cq) * dstep);
+                else r = gload16(rgt, voff_l, static_cast<uint32_t>(cq) * (kGateRecordMfma * 4u));
             }
         };
-        auto store = [&](int n, const Stage& st) {   // into the buffer of the parity of n
-            unsigned char* dst = stg + (n & 1) * RB_SIZE;
+        // into the buffers of the parities of ck and cq; a side whose chunk is negative (past
+        // the first chunk) is not written
+        auto store = [&](int ck, int cq, const Stage& st) {
+            unsigned char* dk_ = kst + (ck & 1) * RK_SIZE;
+            unsigned char* dq_ = qst + (cq & 1) * RQ_SIZE;
 #pragma unroll
             for (int i = me; i < kRevLoads; i += kRevLoaders) {
+                if ((i < kRevLoadsK ? ck : cq) < 0) continue;
                 unsigned char* p;
-                if (i < 32) p = dst + (i < 16 ? 0 : RB_Q) + (4 * (i & 15) + (lane >> 4)) * KPB + 16 * (lane & 15);
-                else if (i < 38) p = dst + RB_TT + (i - 32) * 1024 + 16 * lane;
-                else if (i < 44) p = dst + RB_PT + (i - 38) * 1024 + 16 * lane;
-                else if (i < 46) p = dst + RB_DO + (i - 44) * 1024 + 16 * lane;
-                else p = dst + RB_G + 16 * lane;
+                if (i < 16) p = dk_ + i * 1024 + 16 * lane;
+                else if (i < 22) p = dk_ + RK_TT + (i - 16) * 1024 + 16 * lane;
+                else if (i < 23) p = dk_ + RK_G + 16 * lane;
+                else if (i < 39) p = dq_ + (i - 23) * 1024 + 16 * lane;
+                else if (i < 45) p = dq_ + RQ_PT + (i - 39) * 1024 + 16 * lane;
+                else if (i < 47) p = dq_ + RQ_DO + (i - 45) * 1024 + 16 * lane;
+                else p = dq_ + RQ_G + 16 * lane;
                 *reinterpret_cast<u32x4*>(p) = st[i / kRevLoaders];
             }
         };
-        // chunks run from c = NT - 1 down to 0; in the iteration of chunk c the loaders write
-        // chunk c - 1 (loaded two iterations earlier) and load chunk c - 3. Every wave of the
-        // block passes one barrier per chunk.
-        const int c0 = NT - 1;
-        load(c0, st0);
-        store(c0, st0);
-        load(c0 - 1, st0);
-        load(c0 - 2, st1);
-        int c = c0;
-        for (; c >= 1; c -= 2) {
-            chunk_barrier(false);
-            store(c - 1, st0);
-            load(c - 3, st0);
-            chunk_barrier(false);
-            store(c - 2, st1);
-            load(c - 4, st1);
+        // iteration i stores the chain side of chunk c0 - i and the helper side of chunk
+        // c0 - i - 1 (loaded two iterations before) and loads those of c0 - i - 2 and c0 - i - 3
+        {
+            Stage sq;
+            load(c0, c0, sq);
+            store(-1, c0, sq);   // the helper side of the first chunk, before the first barrier
         }
-        if (c == 0) {
+        load(c0, c0 - 1, st0);
+        load(c0 - 1, c0 - 2, st1);
+        for (int i = 0; i < iters; i += 2) {
             chunk_barrier(false);
-            store(-1, st0);
+            store(c0 - i, c0 - i - 1, st0);
+            load(c0 - i - 2, c0 - i - 3, st0);
+            if (i + 1 < iters) {
+                chunk_barrier(false);
+                store(c0 - i - 1, c0 - i - 2, st1);
+                load(c0 - i - 3, c0 - i - 4, st1);
+            }
         }
         };
-        switch (wave - 1) {
+        switch (wave - 2) {
             case 0: loader(IntTag<0>{}); break;
             case 1: loader(IntTag<1>{}); break;
             case 2: loader(IntTag<2>{}); break;
             case 3: loader(IntTag<3>{}); break;
             case 4: loader(IntTag<4>{}); break;
-            case 5: loader(IntTag<5>{}); break;
-            default: loader(IntTag<6>{}); break;
+            default: loader(IntTag<5>{}); break;
         }
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
 
+    if (wave == 1) {
+        // ---------------- helper wave ----------------
+        float* dv_base = a.dv_out + rs.start * v_row + h * DK + col0;
+        for (int i = 0; i < iters; ++i) {
+            chunk_barrier(false);
+            const int c = c0 - i;
+            if (c >= 0) {
+                const unsigned char* qs = qst + (c & 1) * RQ_SIZE;
+                const float* gs = reinterpret_cast<const float*>(qs + RQ_G);
+                // dO in accumulator order (tokens 16 r + 4 g + j, column c) and its fragments
+                u32x2 dor[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dor[r] = lds_read_tr(qs + RQ_DO + (16 * r + 4 * g4 + (l16 >> 2)) * 32 + 8 * (l16 & 3));
+                bf16x8 dob[2], qb[2];
+                {
+                    f32x4 qv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const f32x4 egq = *reinterpret_cast<const f32x4*>(gs + 128 + 16 * r + 4 * g4);
+                        const f32x4 dof = bf16x4_to_f32(dor[r]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) qv[r][j] = egq[j] * dof[j];
+                    }
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        dob[s] = __builtin_bit_cast(bf16x8, u32x4{dor[2 * s][0], dor[2 * s][1], dor[2 * s + 1][0], dor[2 * s + 1][1]});
+                        qb[s] = pack_frag(qv[2 * s], qv[2 * s + 1]);
+                    }
+                }
+                unsigned char* ah = ahd + (c & 1) * RA_SIZE + 16 * lane;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    f32x4 pd = zero4();
+#pragma unroll
+                    for (int s = (r < 2 ? 0 : 1); s < 2; ++s) pd = mfma16(lds_frag_b(qs + RQ_PT + tri_up(r, s) * 1024 + 16 * lane), dob[s], pd);
+                    *reinterpret_cast<f32x4*>(ah + r * 1024) = pd;
+                }
+                // Q^T diag(e^Gam) dO on the state tiles (the K^T fragments' row order)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        const int off = 8 * 1024 * s + 8 * (t & 1) + tr_lane[t >> 1];
+                        const u32x2 q0 = lds_read_tr(qs + off), q1 = lds_read_tr(qs + off + 4 * 1024);
+                        acc = mfma16(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), qb[s], acc);
+                    }
+                    *reinterpret_cast<f32x4*>(ah + (4 + t) * 1024) = acc;
+                }
+            }
+            const int cs = c0 - i + 2;   // the chain's outputs of chunk cs
+            if (i >= 2 && cs >= 0) {
+                const unsigned char* bh_ = bhd + (cs & 1) * RB_SIZE2;
+                // dS': store k writes the rows of columns 4 k + l / 16 whole (lane l: granule l % 16)
+                uint16_t* st = static_cast<uint16_t*>(a.dstates) + (bh * NT + cs) * DK * DK;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int c = 4 * k + (lane >> 4), gr = lane & 15;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(bh_ + RB_DS + c * 272 + 16 * gr);
+                    *reinterpret_cast<u32x4*>(st + (col0 + c) * DK + 8 * gr) = v;
+                }
+                // dv: store k writes rows 16 k + l / 4, lane l four consecutive columns 4 (l % 4) ..
+                const float* dxs = reinterpret_cast<const float*>(bh_ + RB_DX);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int row = 16 * k + (lane >> 2), c4 = 4 * (lane & 3);
+                    const int64_t t = static_cast<int64_t>(cs) * kChunk + row;
+                    if (t < a.T) {
+                        const f32x4 v = t < nvalid ? *reinterpret_cast<const f32x4*>(dxs + row * RB_DXP + c4) : zero4();
+                        *reinterpret_cast<f32x4*>(dv_base + t * v_row + c4) = v;
+                    }
+                }
+            }
+        }
+        return;
+    }
+
     // ---------------- chain wave ----------------
+    // The update of the state gradient by chunk n, dS -= K^T diag(e^Gam) dX, is applied at the
+    // start of the next iteration (or after the last chunk), interleaved with the reads of the
+    // next chunk's K fragments; its K^T fragments are read between the k-steps of K dS' (as in
+    // the forward state pass, so that LDS reads overlap MFMAs instead of sitting between
+    // dependent stages). Before the first chunk the pending operands are zero.
     f32x4 dS[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -216,103 +341,115 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
             const int row = 32 * (t >> 1) + 8 * g4 + 4 * (t & 1) + j;
             dS[t][j] = a.dhT ? a.dhT[bh * DK * DK + row * DK + col0 + l16] : 0.f;
         }
-    float* dv_row = a.dv_out + rs.start * v_row + h * DK + col0 + l16;
-    for (int n = NT - 1; n >= 0; --n) {
+    u32x2 ktr[8][2][2];
+    bf16x8 wb[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) wb[s] = bf16x8{};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) ktr[t][s][0] = ktr[t][s][1] = u32x2{0u, 0u};
+    auto kt_frag = [&](int t, int s) {
+        return __builtin_bit_cast(bf16x8, u32x4{ktr[t][s][0][0], ktr[t][s][0][1], ktr[t][s][1][0], ktr[t][s][1][1]});
+    };
+    for (int i = 0; i < iters; ++i) {
         chunk_barrier(false);
-        const unsigned char* sb_ = stg + (n & 1) * RB_SIZE;
-        const float* gs = reinterpret_cast<const float*>(sb_ + RB_G);
-        // dS' as B fragments of K dS' (k = dk), stored for the gradient pass (transposed)
+        const int n = c0 - i + 1;
+        if (i < 1 || n < 0) continue;
+        const unsigned char* ks = kst + (n & 1) * RK_SIZE;
+        const unsigned char* ah = ahd + (n & 1) * RA_SIZE + 16 * lane;
+        unsigned char* bh_ = bhd + (n & 1) * RB_SIZE2;
+        const float* gs = reinterpret_cast<const float*>(ks + RK_G);
+        // pending update of chunk n + 1, with the K fragments of chunk n read in between
+        // (kf[4 s + r]: token tile r, dk step s)
+        bf16x8 kf[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int s = q >> 3, t = q & 7;
+            dS[t] = mfma16(kt_frag(t, s), wb[s], dS[t]);
+            kf[q] = lds_frag_b(ks + (q & 3) * 4096 + frag_lane[q >> 2]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // dS' (the gradient of the state leaving chunk n) as B fragments of K dS', handed to
+        // the helper for the gradient pass
         bf16x8 sb[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) sb[s] = pack_frag(dS[2 * s], dS[2 * s + 1]);
-        {
-            uint16_t* st = static_cast<uint16_t*>(a.dstates) + ((bh * NT + n) * DK + col0 + l16) * DK + 8 * g4;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(st + 32 * s) = sb[s];
+        for (int s = 0; s < 4; ++s) {
+            sb[s] = pack_frag(dS[2 * s], dS[2 * s + 1]);
+            *reinterpret_cast<bf16x8*>(bh_ + RB_DS + l16 * 272 + 16 * (4 * s + g4)) = sb[s];
         }
-        // K dS' (token tiles r)
-        f32x4 c0[4];
+        f32x4 egc[4], eg[4], pd[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            c0[r] = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s) c0[r] = mfma16(frag_rowmajor(sb_, KPB, 16 * r, 32 * s, l16, g4), sb[s], c0[r]);
+            egc[r] = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
+            eg[r] = *reinterpret_cast<const f32x4*>(gs + 16 * r + 4 * g4);
+            pd[r] = *reinterpret_cast<const f32x4*>(ah + r * 1024);
         }
-        // dO in accumulator order (tokens 16 r + 4 g + j, column c) and P^T dO
-        u32x2 dor[4];
+        bf16x8 th[6];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dor[r] = lds_read_tr(sb_ + RB_DO + (16 * r + 4 * g4 + (l16 >> 2)) * 32 + 8 * (l16 & 3));
-        bf16x8 dob[2];
+        for (int q = 0; q < 6; ++q) th[q] = lds_frag_b(ks + RK_TT + q * 1024 + 16 * lane);
+        __builtin_amdgcn_sched_barrier(0);
+        // K dS' for token tiles r, dk steps s in turn; after each step eight transposing reads
+        // of K for the state update go out (into the registers that step frees)
+        f32x4 c0r[4];
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-            dob[s] = __builtin_bit_cast(bf16x8, u32x4{dor[2 * s][0], dor[2 * s][1], dor[2 * s + 1][0], dor[2 * s + 1][1]});
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) c0r[r] = mfma16(kf[4 * s + r], sb[s], s == 0 ? zero4() : c0r[r]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = 2 * s + (q >> 1), ts = q & 1;
+                const int off = 8 * 1024 * ts + 8 * (t & 1) + tr_lane[t >> 1];
+                ktr[t][ts][0] = lds_read_tr(ks + off);
+                ktr[t][ts][1] = lds_read_tr(ks + off + 4 * 1024);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the scaled state gradient plus the helper's Q^T diag(e^Gam) dO, off the dependency
+        // chain (the update that opens the next iteration adds -K^T diag(e^Gam) dX)
+        const float egC = gs[192];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 qd = *reinterpret_cast<const f32x4*>(ah + (4 + t) * 1024);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dS[t][j] = egC * dS[t][j] + qd[j];
+        }
+        // dU = P^T dO + e^{Gam_C - Gam} K dS', dX = That^T dU
         f32x4 du[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            f32x4 pd = zero4();
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int s = (r < 2 ? 0 : 1); s < 2; ++s) pd = mfma16(lds_frag_b(sb_ + RB_PT + tri_up(r, s) * 1024 + 16 * lane), dob[s], pd);
-            const f32x4 egc = *reinterpret_cast<const f32x4*>(gs + 64 + 16 * r + 4 * g4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) du[r][j] = pd[j] + egc[j] * c0[r][j];
-        }
+            for (int j = 0; j < 4; ++j) du[r][j] = pd[r][j] + egc[r][j] * c0r[r][j];
         bf16x8 dub[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) dub[s] = pack_frag(du[2 * s], du[2 * s + 1]);
-        // dX = That^T dU, written as dv (zero past the valid tokens)
         f32x4 dx[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             dx[r] = zero4();
 #pragma unroll
-            for (int s = (r < 2 ? 0 : 1); s < 2; ++s) dx[r] = mfma16(lds_frag_b(sb_ + RB_TT + tri_up(r, s) * 1024 + 16 * lane), dub[s], dx[r]);
+            for (int s = (r < 2 ? 0 : 1); s < 2; ++s) dx[r] = mfma16(th[tri_up(r, s)], dub[s], dx[r]);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t t = static_cast<int64_t>(n) * kChunk + 16 * r + 4 * g4 + j;
-                if (t < a.T) dv_row[t * v_row] = t < nvalid ? dx[r][j] : 0.f;
-            }
-        // dS = e^{Gam_C} dS' + Q^T diag(e^Gam) dO - K^T diag(e^Gam) dX
-        bf16x8 wb[2], qb[2];
+        // -diag(e^Gam) dX as the B operand of the pending update; dX to the helper, row by row
         {
-            f32x4 w[4], qv[4];
+            f32x4 w[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const f32x4 eg = *reinterpret_cast<const f32x4*>(gs + 16 * r + 4 * g4);
-                const f32x4 egq = *reinterpret_cast<const f32x4*>(gs + 128 + 16 * r + 4 * g4);
-                const f32x4 dof = bf16x4_to_f32(dor[r]);
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    w[r][j] = -eg[j] * dx[r][j];
-                    qv[r][j] = egq[j] * dof[j];
-                }
-            }
+                for (int j = 0; j < 4; ++j) w[r][j] = -eg[r][j] * dx[r][j];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                wb[s] = pack_frag(w[2 * s], w[2 * s + 1]);
-                qb[s] = pack_frag(qv[2 * s], qv[2 * s + 1]);
-            }
+            for (int s = 0; s < 2; ++s) wb[s] = pack_frag(w[2 * s], w[2 * s + 1]);
         }
-        const float egC = gs[192];
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int r = 0; r < 4; ++r) {
+            float* dxs = reinterpret_cast<float*>(bh_ + RB_DX) + (16 * r + 4 * g4) * RB_DXP + l16;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dS[t][j] *= egC;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                // K^T and Q^T fragments of state tile t (rows 32 (t / 2) + 8 (i / 4) + 4 (t % 2) +
-                // i % 4 for lane i of a group) over tokens 32 s + 4 g + (e % 4) + 16 (e / 4)
-                const int off = (32 * s + 4 * g4 + (l16 >> 2)) * KPB + (32 * (t >> 1) + 8 * (l16 & 3) + 4 * (t & 1)) * 2;
-                const u32x2 k0 = lds_read_tr(sb_ + off), k1 = lds_read_tr(sb_ + off + 16 * KPB);
-                const u32x2 q0 = lds_read_tr(sb_ + RB_Q + off), q1 = lds_read_tr(sb_ + RB_Q + off + 16 * KPB);
-                dS[t] = mfma16(__builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]}), wb[s], dS[t]);
-                dS[t] = mfma16(__builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]}), qb[s], dS[t]);
-            }
+            for (int j = 0; j < 4; ++j) dxs[j * RB_DXP] = dx[r][j];
+        }
     }
+    // the update of the first chunk
+#pragma unroll
+    for (int q = 0; q < 16; ++q) dS[q & 7] = mfma16(kt_frag(q & 7, q >> 3), wb[q >> 3], dS[q & 7]);
     if (a.dh0_out) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -535,16 +672,22 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             // ---- C ----
             {
                 const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+                // the B operands (columns 16 m .. of S and dS', contraction over the panel's
+                // columns of dv) serve all four token tiles
+                bf16x8 stf[2], dstf[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    stf[s] = frag_kmajor(sm + G_ST, KPB, 32 * s, 16 * m, l16, g4);
+                    dstf[s] = frag_kmajor(sm + G_DST, KPB, 32 * s, 16 * m, l16, g4);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     f32x4 zf = zero4(), zg = zero4(), zh = zero4();
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        const bf16x8 stf = frag_kmajor(sm + G_ST, KPB, 32 * s, 16 * m, l16, g4);
-                        zf = mfma16(frag_rowmajor(sm + G_DO, SPB, 16 * r, 32 * s, l16, g4), stf, zf);
-                        zg = mfma16(frag_rowmajor(sm + G_DX, SPB, 16 * r, 32 * s, l16, g4), stf, zg);
-                        zh = mfma16(frag_kmajor(sm + G_UET, SPB, 32 * s, 16 * r, l16, g4),
-                                    frag_kmajor(sm + G_DST, KPB, 32 * s, 16 * m, l16, g4), zh);
+                        zf = mfma16(frag_rowmajor(sm + G_DO, SPB, 16 * r, 32 * s, l16, g4), stf[s], zf);
+                        zg = mfma16(frag_rowmajor(sm + G_DX, SPB, 16 * r, 32 * s, l16, g4), stf[s], zg);
+                        zh = mfma16(frag_kmajor(sm + G_UET, SPB, 32 * s, 16 * r, l16, g4), dstf[s], zh);
                     }
                     const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_s + 16 * r + 4 * g4);
                     const f32x4 qv = tile_acc_order(sm + G_Q, KPB, 16 * r, 16 * m, l16, g4);
@@ -700,19 +843,25 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
         }
         __syncthreads();
         // ---- D4: dq += PD K, dk += PD^T Q + E K + E^T K ----
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        {
             const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+            bf16x8 kt[2], qt[2];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const bf16x8 kt = frag_kmajor(sm + G_K, KPB, 32 * s, 16 * m, l16, g4);
-                const bf16x8 qt = frag_kmajor(sm + G_Q, KPB, 32 * s, 16 * m, l16, g4);
-                dq_acc[r] = mfma16(frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * r, l16, g4), kt, dq_acc[r]);
-                dk_acc[r] = mfma16(frag_rowmajor(sm + G_XT, SPB, 16 * r, 32 * s, l16, g4), qt, dk_acc[r]);
-                dk_acc[r] = mfma16(frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * r, l16, g4), kt, dk_acc[r]);
-                dk_acc[r] = mfma16(frag_rowmajor(sm + G_DUT, SPB, 16 * r, 32 * s, l16, g4), kt, dk_acc[r]);
+                kt[s] = frag_kmajor(sm + G_K, KPB, 32 * s, 16 * m, l16, g4);
+                qt[s] = frag_kmajor(sm + G_Q, KPB, 32 * s, 16 * m, l16, g4);
             }
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    dq_acc[r] = mfma16(frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dq_acc[r]);
+                    dk_acc[r] = mfma16(frag_rowmajor(sm + G_XT, SPB, 16 * r, 32 * s, l16, g4), qt[s], dk_acc[r]);
+                    dk_acc[r] = mfma16(frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dk_acc[r]);
+                    dk_acc[r] = mfma16(frag_rowmajor(sm + G_DUT, SPB, 16 * r, 32 * s, l16, g4), kt[s], dk_acc[r]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         {
             const float ws = wave_sum(wsum), sd = wave_sum(sdot);
