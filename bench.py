@@ -259,30 +259,56 @@ def prologue_timing(gdn, inp, dev, stream, timed):
 
 
 def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
-    """gdn_chunk_bwd (all six gradients) on the stateless 8K workload with a seeded output
-    gradient, and its per-kernel split is in profiles/."""
+    """gdn_chunk_bwd (all six gradients; the chunked matrix-core backward on these bf16
+    heads of 128) on the stateless 8K workload with a seeded output gradient, beside the
+    forward on the same inputs, the fp32 token-level backward of the same problem (the
+    one-segment apply backward) and the stateful 32K workload; the per-kernel split is in
+    profiles/."""
     import torch
-
-    w = workloads["stateless_8k"]
-    inp = make_inputs(w)
 
     def io(x):
         return torch.from_numpy(np.ascontiguousarray(x)).view(torch.int16).view(torch.bfloat16).to(dev)
 
-    q, k, v = io(inp.q), io(inp.k), io(inp.v)
-    g = torch.from_numpy(inp.g).to(dev)
-    beta = torch.from_numpy(inp.beta).to(dev)
-    gen = torch.Generator(device=dev).manual_seed(8)
-    d_o = torch.randn(v.shape, device=dev, generator=gen).to(torch.bfloat16)
+    def setup(name):
+        w = workloads[name]
+        inp = make_inputs(w)
+        q, k, v = io(inp.q), io(inp.k), io(inp.v)
+        g = torch.from_numpy(inp.g).to(dev)
+        beta = torch.from_numpy(inp.beta).to(dev)
+        h0 = None if inp.h0 is None else torch.from_numpy(inp.h0).to(dev)
+        gen = torch.Generator(device=dev).manual_seed(8)
+        d_o = torch.randn(v.shape, device=dev, generator=gen).to(torch.bfloat16)
+        return w, q, k, v, g, beta, h0, d_o
+
+    w, q, k, v, g, beta, _, d_o = setup("stateless_8k")
     p = gdn.problem(q, v)
     ws = gdn.workspace(gdn.gdn_chunk_bwd_workspace(p), dev)
+    fws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
 
     def step():
         gdn.gdn_chunk_bwd(q, k, v, g, beta, None, d_o, ws=ws, stream=stream)
 
-    ms = timed(step, 3)
+    def fwd():
+        gdn.gdn_chunk_fwd(q, k, v, g, beta, None, ws=fws, stream=stream)
+
+    ms = timed(step, 5)
+    ms_fwd = timed(fwd, 5)
+    in_bytes = sum(int(x.numel()) * x.element_size() for x in (q, k, v, g, beta, d_o))
     out = {"workload": "stateless_8k", "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
-           "workspace_bytes": int(ws.numel())}
+           "forward_ms": ms_fwd, "ratio_to_forward": ms / ms_fwd,
+           "workspace_bytes": int(ws.numel()), "input_bytes": in_bytes,
+           "path": gdn.gdn_kernel_path(p)}
+
+    # the fp32 token-level backward of the same problem (one segment from a zero state)
+    H_in = torch.zeros((w.B, w.H, 1, w.dk, w.dv), device=dev)
+    tws = gdn.workspace(gdn.gdn_segment_bwd_workspace(p, w.T), dev)
+
+    def token_step():
+        gdn.gdn_apply_initial_state_bwd(q, k, v, g, beta, H_in, w.T, d_o, ws=tws, stream=stream)
+
+    out["token_level_fp32_ms"] = timed(token_step, 2)
+    out["token_level_workspace_bytes"] = int(tws.numel())
+    del tws
 
     # the same gradients through the segment calls (4 segments of 2048): apply's backward,
     # the combine's, then the summaries' accumulated onto apply's
@@ -298,7 +324,18 @@ def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
 
     ms_seg = timed(seg_step, 2)
     out["segments_4x2048"] = {"ms_per_step": ms_seg, "workspace_bytes": int(bws.numel()),
-                              "note": "apply, combine and summary backward composed"}
+                              "note": "apply, combine and summary backward composed (fp32 token level)"}
+    del bws, ws, fws
+
+    # the stateful 32K workload (initial state, 32 heads of 128)
+    w, q, k, v, g, beta, h0, d_o = setup("stateful_32k")
+    p = gdn.problem(q, v)
+    ws = gdn.workspace(gdn.gdn_chunk_bwd_workspace(p), dev)
+    fws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
+    ms = timed(lambda: gdn.gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, ws=ws, stream=stream), 3)
+    ms_fwd = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, ws=fws, stream=stream), 3)
+    out["stateful_32k"] = {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "forward_ms": ms_fwd,
+                           "ratio_to_forward": ms / ms_fwd, "workspace_bytes": int(ws.numel())}
     return out
 
 

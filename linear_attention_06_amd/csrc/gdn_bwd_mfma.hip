@@ -21,9 +21,10 @@
 //
 // Three passes after the prepare pass: the forward state pass stores the state S_n entering
 // every chunk (bf16, transposed); bwd_state_mfma runs the reverse chain above per (b, h,
-// 16 columns of dv), writing dv and the gradient dS'_n of the state leaving every chunk;
-// bwd_grad_mfma, one block per (b, query/key head, chunk), forms the rest from S_n and dS'_n
-// with every product on v_mfma_f32_16x16x32_bf16 and fp32 accumulation.
+// 16 columns of dv), writing the gradient dS'_n of the state leaving every chunk;
+// bwd_grad_mfma, one block per (b, query/key head, chunk), forms everything else (dv
+// included) from S_n and dS'_n, with every product on v_mfma_f32_16x16x32_bf16 and fp32
+// accumulation.
 #include "gdn_mfma_common.hpp"
 
 namespace gdn {
@@ -90,8 +91,9 @@ __device__ __forceinline__ float col_sum4(float x) {
 //     chunk: K dS', dU, dX = That^T dU and the update of dS (38 MFMAs);
 //   wave 1 (helper) computes one chunk ahead the terms that do not depend on the state
 //     gradient, P^T dO and Q^T diag(e^Gam) dO, and hands them over in LDS (fp32); one
-//     chunk behind it writes the chain's dX (as dv) and dS' (bf16) to memory, so that the
-//     chain wave issues no global memory instruction;
+//     chunk behind it writes the chain's dS' (bf16) to memory, so that the chain wave
+//     issues no global memory instruction (dv = dX is formed again in the gradient pass,
+//     which recomputes dU anyway);
 //   waves 2-7 stage each chunk's operands two iterations ahead through registers: the
 //     chain's (K, That^T, decay record) and the helper's (Q, P^T, dO, decay record).
 // With c0 = NT - 1, iteration i has the helper on chunk c0 - i, the chain on c0 - i + 1
@@ -103,10 +105,8 @@ __device__ __forceinline__ float col_sum4(float x) {
 constexpr int RK_TT = 64 * 256, RK_G = RK_TT + 6144, RK_SIZE = RK_G + 1024;             // chain side
 constexpr int RQ_PT = 64 * 256, RQ_DO = RQ_PT + 6144, RQ_G = RQ_DO + 2048, RQ_SIZE = RQ_G + 1024;   // helper side
 constexpr int RA_SIZE = 12 * 1024;   // hand-off ahead: P^T dO (4 x 1 KiB), Q^T e^Gam dO (8 x 1 KiB), fp32
-// hand-off behind: dX fp32 [64 rows][20] (a pitch of 20 floats puts the 64 lanes of each
-// write and the 16 x 4 lanes of each read on distinct banks), then dS' as [16 columns][128]
-// bf16 at a pitch of 272 bytes
-constexpr int RB_DXP = 20, RB_DX = 0, RB_DS = 64 * RB_DXP * 4, RB_SIZE2 = RB_DS + 16 * 272;
+// hand-off behind: dS' as [16 columns][128] bf16 at a pitch of 272 bytes
+constexpr int RB_DS = 0, RB_SIZE2 = 16 * 272;
 constexpr int kRevLoadsK = 16 + 6 + 1, kRevLoadsQ = 16 + 6 + 2 + 1, kRevLoads = kRevLoadsK + kRevLoadsQ;
 constexpr int kRevLoaders = 6;
 
@@ -252,7 +252,6 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
 
     if (wave == 1) {
         // ---------------- helper wave ----------------
-        float* dv_base = a.dv_out + rs.start * v_row + h * DK + col0;
         for (int i = 0; i < iters; ++i) {
             chunk_barrier(false);
             const int c = c0 - i;
@@ -310,17 +309,6 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
                     const int c = 4 * k + (lane >> 4), gr = lane & 15;
                     const u32x4 v = *reinterpret_cast<const u32x4*>(bh_ + RB_DS + c * 272 + 16 * gr);
                     *reinterpret_cast<u32x4*>(st + (col0 + c) * DK + 8 * gr) = v;
-                }
-                // dv: store k writes rows 16 k + l / 4, lane l four consecutive columns 4 (l % 4) ..
-                const float* dxs = reinterpret_cast<const float*>(bh_ + RB_DX);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int row = 16 * k + (lane >> 2), c4 = 4 * (lane & 3);
-                    const int64_t t = static_cast<int64_t>(cs) * kChunk + row;
-                    if (t < a.T) {
-                        const f32x4 v = t < nvalid ? *reinterpret_cast<const f32x4*>(dxs + row * RB_DXP + c4) : zero4();
-                        *reinterpret_cast<f32x4*>(dv_base + t * v_row + c4) = v;
-                    }
                 }
             }
         }
@@ -430,7 +418,7 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
 #pragma unroll
             for (int s = (r < 2 ? 0 : 1); s < 2; ++s) dx[r] = mfma16(th[tri_up(r, s)], dub[s], dx[r]);
         }
-        // -diag(e^Gam) dX as the B operand of the pending update; dX to the helper, row by row
+        // -diag(e^Gam) dX as the B operand of the pending update
         {
             f32x4 w[4];
 #pragma unroll
@@ -439,12 +427,6 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
                 for (int j = 0; j < 4; ++j) w[r][j] = -eg[r][j] * dx[r][j];
 #pragma unroll
             for (int s = 0; s < 2; ++s) wb[s] = pack_frag(w[2 * s], w[2 * s + 1]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float* dxs = reinterpret_cast<float*>(bh_ + RB_DX) + (16 * r + 4 * g4) * RB_DXP + l16;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dxs[j * RB_DXP] = dx[r][j];
         }
     }
     // the update of the first chunk
@@ -467,20 +449,23 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
 // holds columns 16 w .. + 15 of dq and dk for the 64 tokens). Per value head, in two
 // panels of 64 columns of dv:
 //   B  (waves 0-3, one 16-column slice each) X = V - e^Gam K S and U = That X; (waves 4-7)
-//      dU = P^T dO + e^{Gam_C - Gam} K dS'; X, U, e^{Gam_C - Gam} U and dU go to LDS
-//      transposed (columns of dv as rows);
+//      dU = P^T dO + e^{Gam_C - Gam} K dS' and dX = That^T dU, written as dv; X, U,
+//      e^{Gam_C - Gam} U, dU and -e^Gam dX go to LDS transposed (columns of dv as rows);
 //   C  Zf, Zg, Zh (contractions over the panel's columns) into dq, dk and, through their
 //      row products with q and k, into dGam; dP and dThat (lower 16x16 tiles) accumulated
 //      over both panels;
 // then D: PD, dT = dThat diag(beta) (Tinv and P read row-major), Y = dT Tinv^T,
-// dA = -Tinv^T Y, K K^T, E, and dq += PD K, dk += PD^T Q + E K + E^T K. Per-token sums
+// dA = -Tinv^T Y, K K^T, E; after the last value head dq += PD K, dk += PD^T Q + E K + E^T K
+// on PD and E summed over the value heads. Per-token sums
 // (dGam, dbeta) go through one LDS row per wave and are added in a fixed order, so the
 // result does not depend on timing.
 // ----------------------------------------------------------------------------
 constexpr int G_K = 0, G_Q = G_K + 64 * KPB, G_ST = G_Q + 64 * KPB, G_DST = G_ST + 64 * KPB,
               G_V = G_DST + 64 * KPB, G_DO = G_V + 64 * SPB, G_DX = G_DO + 64 * SPB, G_XT = G_DX + 64 * SPB,
               G_UET = G_XT + 64 * SPB, G_UT = G_UET + 64 * SPB, G_DUT = G_UT + 64 * SPB, G_VEC = G_DUT + 64 * SPB,
-              G_SIZE = G_VEC + (4 * 64 + 2 * 8 * 64 + 32) * 4;
+              G_DVP = 68, G_DV = G_VEC + (4 * 64 + 2 * 8 * 64 + 32) * 4, G_SIZE = G_DV + 64 * G_DVP * 4;
+// G_DV stages the panel's dv (fp32 [64 tokens][64 columns] at a pitch of 68 floats: the
+// writes of a wave's accumulator tiles and the 16-byte row reads are free of bank conflicts)
 // Phase D reuses: Tinv (row-major) in G_ST, P in G_DST, PD^T in G_XT, dT^T in G_UT, Y^T in
 // G_UET, E^T in G_DUT.
 
@@ -499,6 +484,14 @@ __device__ __forceinline__ u32x2 pack4(const f32x4& v) { return u32x2{pk2(v[0], 
 __device__ __forceinline__ int fresh_lane(int lane) {
     asm volatile("" : "+v"(lane));
     return lane;
+}
+
+// Zero granule e (0..191) of the six upper 16x16 tiles of a [j][i] (transposed) 64x64 bf16
+// matrix at pitch SPB: tiles (row tile jt, column tile it) with it < jt.
+__device__ __forceinline__ void zero_upper_tiles_t(unsigned char* base, int e) {
+    const int tq = e >> 5, w16 = e & 31;
+    const int jt = tq < 1 ? 1 : tq < 3 ? 2 : 3, it = tq - (jt * (jt - 1)) / 2;
+    *reinterpret_cast<u32x4*>(base + (16 * jt + (w16 >> 1)) * SPB + 32 * it + 16 * (w16 & 1)) = u32x4{0u, 0u, 0u, 0u};
 }
 
 __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
@@ -538,6 +531,13 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) dq_acc[r] = dk_acc[r] = zero4();
 
+    // PD and E of the wave's lower 16x16 tiles (tile wave, and wave + 8 for waves 0 and 1),
+    // summed over the value heads: dq += PD K and dk += PD^T Q + E K + E^T K are linear in
+    // them, so those products run once per block
+    f32x4 pd_acc[2], e_acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pd_acc[i] = e_acc[i] = zero4();
+
     for (int kk = 0; kk < rep; ++kk) {
         const int h = hq * rep + kk;
         const int64_t bh = static_cast<int64_t>(b) * a.H + h, ch = bh * NT + n;
@@ -560,10 +560,10 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
         f32x4 acc_pt[3];
 #pragma unroll
         for (int i = 0; i < 3; ++i) acc_pt[i] = zero4();
-        __syncthreads();
+        chunk_barrier(false);
 
         for (int pn = 0; pn < 2; ++pn) {
-            // ---- A: the panel's rows of S^T and dS'^T, and its columns of V, dO, dX ----
+            // ---- A: the panel's rows of S^T and dS'^T, and its columns of V and dO ----
             {
                 const uint16_t* st = static_cast<const uint16_t*>(a.states) + (ch * DK + 64 * pn) * DK;
                 const uint16_t* dst = static_cast<const uint16_t*>(a.dstates) + (ch * DK + 64 * pn) * DK;
@@ -587,18 +587,8 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                     *reinterpret_cast<u32x4*>(sm + G_V + row * SPB + 16 * gr) = gload16(rv, off, 0);
                     *reinterpret_cast<u32x4*>(sm + G_DO + row * SPB + 16 * gr) = gload16(rd, off, 0);
                 }
-                const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.dv_out + rs.start * v_row, nvalid * v_row * 4);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int p = tid + 512 * u, row = p >> 4, q4 = p & 15;
-                    const uint32_t off = static_cast<uint32_t>(((t0 + row) * v_row + h * DK + 64 * pn + 4 * q4) * 4);
-                    const f32x4 x = __builtin_bit_cast(f32x4, gload16(rx, off, 0));
-                    const float sc = -eg_s[row];
-                    *reinterpret_cast<u32x2*>(sm + G_DX + row * SPB + 8 * q4) =
-                        u32x2{pk2(sc * x[0], sc * x[1]), pk2(sc * x[2], sc * x[3])};
-                }
             }
-            __syncthreads();
+            chunk_barrier(false);
             // ---- B ----
             {
                 const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
@@ -655,20 +645,56 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
 #pragma unroll
                     for (int s = 0; s < 2; ++s)
                         dob[s] = __builtin_bit_cast(bf16x8, u32x4{dor[2 * s][0], dor[2 * s][1], dor[2 * s + 1][0], dor[2 * s + 1][1]});
+                    f32x4 du[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         f32x4 pd = zero4();
 #pragma unroll
                         for (int s = (r < 2 ? 0 : 1); s < 2; ++s) pd = mfma16(rf[tri_up(r, s)], dob[s], pd);
                         const f32x4 egc = *reinterpret_cast<const f32x4*>(egc_s + 16 * r + 4 * g4);
-                        f32x4 du;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) du[j] = pd[j] + egc[j] * acc[r][j];
-                        *reinterpret_cast<u32x2*>(colrow + G_DUT + 32 * r) = pack4(du);
+                        for (int j = 0; j < 4; ++j) du[r][j] = pd[j] + egc[j] * acc[r][j];
+                        *reinterpret_cast<u32x2*>(colrow + G_DUT + 32 * r) = pack4(du[r]);
+                    }
+                    // dX = That^T dU (the value gradient): to LDS as -e^Gam dX, transposed, and
+                    // to dv (zero past the valid tokens)
+                    {
+                        const uint16_t* rp = static_cast<const uint16_t*>(a.rec.thatT) + ch * kTriRecord;
+#pragma unroll
+                        for (int j = 0; j < 6; ++j) rf[j] = *reinterpret_cast<const bf16x8*>(rp + j * 512 + lane * 8);
+                    }
+                    bf16x8 dub[2];
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) dub[s] = pack_frag(du[2 * s], du[2 * s + 1]);
+                    float* dvs = reinterpret_cast<float*>(sm + G_DV) + 16 * sg + l16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        f32x4 dx = zero4();
+#pragma unroll
+                        for (int s = (r < 2 ? 0 : 1); s < 2; ++s) dx = mfma16(rf[tri_up(r, s)], dub[s], dx);
+                        const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_s + 16 * r + 4 * g4);
+                        f32x4 dxe;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            dxe[j] = -eg[j] * dx[j];
+                            dvs[(16 * r + 4 * g4 + j) * G_DVP] = dx[j];
+                        }
+                        *reinterpret_cast<u32x2*>(colrow + G_DX + 32 * r) = pack4(dxe);
                     }
                 }
             }
-            __syncthreads();
+            chunk_barrier(false);
+            // the panel's dv, whole rows of 64 columns (zero past the valid tokens)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int p = tid + 512 * u, row = p >> 4, q4 = p & 15;
+                const int64_t t = t0 + row;
+                if (t < a.T) {
+                    const f32x4 x = t < nvalid ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(sm + G_DV) + row * G_DVP + 4 * q4)
+                                               : zero4();
+                    *reinterpret_cast<f32x4*>(a.dv_out + (rs.start + t) * v_row + h * DK + 64 * pn + 4 * q4) = x;
+                }
+            }
             // ---- C ----
             {
                 const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
@@ -686,7 +712,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
                         zf = mfma16(frag_rowmajor(sm + G_DO, SPB, 16 * r, 32 * s, l16, g4), stf[s], zf);
-                        zg = mfma16(frag_rowmajor(sm + G_DX, SPB, 16 * r, 32 * s, l16, g4), stf[s], zg);
+                        zg = mfma16(frag_kmajor(sm + G_DX, SPB, 32 * s, 16 * r, l16, g4), stf[s], zg);
                         zh = mfma16(frag_kmajor(sm + G_UET, SPB, 32 * s, 16 * r, l16, g4), dstf[s], zh);
                     }
                     const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_s + 16 * r + 4 * g4);
@@ -720,26 +746,19 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                     }
                 }
             }
-            __syncthreads();
+            chunk_barrier(false);
         }
 
-        // ---- D0: Tinv and P row-major; the upper tiles of PD^T, dT^T and E^T are zero ----
+        // ---- D0: Tinv and P row-major; the upper tiles of dT^T are zero ----
         {
             const int row = tid >> 3, gr = tid & 7;
             *reinterpret_cast<u32x4*>(sm + G_ST + row * SPB + 16 * gr) =
                 *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.rec.t_rm) + ch * 4096 + row * 64 + 8 * gr);
             *reinterpret_cast<u32x4*>(sm + G_DST + row * SPB + 16 * gr) =
                 *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.rec.p_rm) + ch * 4096 + row * 64 + 8 * gr);
-            // transposed storage [j][i]: tiles (row tile jt, column tile it) with it < jt
-            for (int p = tid; p < 3 * 6 * 32; p += 512) {
-                const int mat = p / 192, e = p % 192, tq = e >> 5, w16 = e & 31;
-                const int jt = tq < 1 ? 1 : tq < 3 ? 2 : 3, it = tq - (jt * (jt - 1)) / 2;
-                const int region = mat == 0 ? G_XT : mat == 1 ? G_UT : G_DUT;
-                *reinterpret_cast<u32x4*>(sm + region + (16 * jt + (w16 >> 1)) * SPB + 32 * it + 16 * (w16 & 1)) =
-                    u32x4{0u, 0u, 0u, 0u};
-            }
+            if (tid < 192) zero_upper_tiles_t(sm + G_UT, tid);
         }
-        __syncthreads();
+        chunk_barrier(false);
         // ---- D1: PD and dT from the dP and dThat tiles ----
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
@@ -773,9 +792,14 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 if (item < 10) part_g[wave * 64 + J] -= colacc;
                 else part_b[wave * 64 + J] += colacc;
             }
-            *reinterpret_cast<u32x2*>(sm + (item < 10 ? G_XT : G_UT) + J * SPB + (16 * ri + 4 * g4) * 2) = pack4(outv);
+            if (item < 10) {
+                if (i == 0) pd_acc[0] += outv;
+                else pd_acc[1] += outv;
+            } else {
+                *reinterpret_cast<u32x2*>(sm + G_UT + J * SPB + (16 * ri + 4 * g4) * 2) = pack4(outv);
+            }
         }
-        __syncthreads();
+        chunk_barrier(false);
         // ---- D2: Y = dT Tinv^T (stored as Y^T), and K K^T on the tiles of D3 ----
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -802,7 +826,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 kkt[i] = mfma16(frag_rowmajor(sm + G_K, KPB, 16 * ri, 32 * s, l16, g4),
                                 frag_rowmajor(sm + G_K, KPB, 16 * ci, 32 * s, l16, g4), kkt[i]);
         }
-        __syncthreads();
+        chunk_barrier(false);
         // ---- D3: dA = -Tinv^T Y (strictly lower), E, and their dbeta / dGam terms ----
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -839,30 +863,10 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             }
             colacc = col_sum4(colacc);
             if (g4 == 0) part_g[wave * 64 + J] -= colacc;
-            *reinterpret_cast<u32x2*>(sm + G_DUT + J * SPB + (16 * ri + 4 * g4) * 2) = pack4(ev);
+            if (i == 0) e_acc[0] += ev;
+            else e_acc[1] += ev;
         }
-        __syncthreads();
-        // ---- D4: dq += PD K, dk += PD^T Q + E K + E^T K ----
-        {
-            const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
-            bf16x8 kt[2], qt[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                kt[s] = frag_kmajor(sm + G_K, KPB, 32 * s, 16 * m, l16, g4);
-                qt[s] = frag_kmajor(sm + G_Q, KPB, 32 * s, 16 * m, l16, g4);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    dq_acc[r] = mfma16(frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dq_acc[r]);
-                    dk_acc[r] = mfma16(frag_rowmajor(sm + G_XT, SPB, 16 * r, 32 * s, l16, g4), qt[s], dk_acc[r]);
-                    dk_acc[r] = mfma16(frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dk_acc[r]);
-                    dk_acc[r] = mfma16(frag_rowmajor(sm + G_DUT, SPB, 16 * r, 32 * s, l16, g4), kt[s], dk_acc[r]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+        chunk_barrier(false);
         {
             const float ws = wave_sum(wsum), sd = wave_sum(sdot);
             if (lane == 0) {
@@ -870,7 +874,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 misc[9 + wave] = sd;
             }
         }
-        __syncthreads();
+        chunk_barrier(false);
         // ---- D5: dGam and dbeta per token, dg = reverse cumulative sum of dGam ----
         if (wave == 0) {
             float dgam = 0.f, db = 0.f;
@@ -897,7 +901,47 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 a.dbeta_out[(rs.start + t) * a.H + h] = valid ? db : 0.f;
             }
         }
-        __syncthreads();
+        chunk_barrier(false);
+    }
+    // ---- D4, once per block: PD^T and E^T of all value heads, then dq += PD K,
+    // dk += PD^T Q + E K + E^T K ----
+    {
+        const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+        if (tid < 192) {
+            zero_upper_tiles_t(sm + G_XT, tid);
+            zero_upper_tiles_t(sm + G_DUT, tid);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = wave + 8 * i;
+            if (q >= 10) break;
+            int ri, ci;
+            lower_tile(q, ri, ci);
+            const int off = (16 * ci + l16) * SPB + (16 * ri + 4 * g4) * 2;
+            *reinterpret_cast<u32x2*>(sm + G_XT + off) = pack4(pd_acc[i]);
+            *reinterpret_cast<u32x2*>(sm + G_DUT + off) = pack4(e_acc[i]);
+        }
+    }
+    chunk_barrier(false);
+    {
+        const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
+        bf16x8 kt[2], qt[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            kt[s] = frag_kmajor(sm + G_K, KPB, 32 * s, 16 * m, l16, g4);
+            qt[s] = frag_kmajor(sm + G_Q, KPB, 32 * s, 16 * m, l16, g4);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                dq_acc[r] = mfma16(frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dq_acc[r]);
+                dk_acc[r] = mfma16(frag_rowmajor(sm + G_XT, SPB, 16 * r, 32 * s, l16, g4), qt[s], dk_acc[r]);
+                dk_acc[r] = mfma16(frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dk_acc[r]);
+                dk_acc[r] = mfma16(frag_rowmajor(sm + G_DUT, SPB, 16 * r, 32 * s, l16, g4), kt[s], dk_acc[r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     // dq and dk of the query/key head (zero past the valid tokens)
 #pragma unroll
