@@ -223,10 +223,16 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
  *   dq, dk [B, T, Hqk, dk],  dv [B, T, H, dv],  dg, dbeta [B, T, H]   (all fp32; dq and dk
  *   summed over the value heads that read each query/key head)
  *   dh0 [B, H, dk, dv] fp32 when non-NULL (the gradient of h0; h0 NULL = zero state).
- * Padded tokens (valid_len) get zero gradients. Every head dim and dtype of the forward;
- * the arithmetic is fp32 on the vector ALUs, token by token, with the forward state
- * recomputed from checkpoints every 8 tokens. ws must be 256-byte aligned and at least
- * gdn_chunk_bwd_workspace() bytes (8 B H ceil(T/64) dk dv + B T H (dv/16) 2 (dk + 1) fp32).
+ * Padded tokens (valid_len) get zero gradients. Every head dim and dtype of the forward.
+ * bf16 inputs with dk = dv = 128 run the chunked matrix-core backward (the transposes of the
+ * chunk form's products on bf16 MFMAs with fp32 accumulation, relative error a few 1e-3,
+ * within the bf16 bound issue #320 section 4.2 states for gradients): workspace per
+ * (b, h, 64-token chunk) of 105 KiB (the prepare pass's records, the state entering the chunk
+ * and the gradient of the state leaving it, bf16). Every other problem runs the fp32
+ * token-level backward on the vector ALUs, with the forward state recomputed from
+ * checkpoints every 8 tokens (workspace 8 B H ceil(T/64) dk dv + B T H (dv/16) 2 (dk + 1)
+ * fp32). ws must be 256-byte aligned and at least gdn_chunk_bwd_workspace() bytes; results
+ * are deterministic (the same bits on every run).
  */
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes);
 gdn_status gdn_chunk_bwd(const gdn_problem* p,
