@@ -291,13 +291,23 @@ def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
     def fwd():
         gdn.gdn_chunk_fwd(q, k, v, g, beta, None, ws=fws, stream=stream)
 
+    def train_step():
+        # forward keeping its records and states, then the backward from them
+        gdn.gdn_chunk_fwd_save(q, k, v, g, beta, None, ws=ws, stream=stream)
+        gdn.gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, stream=stream)
+
     ms = timed(step, 5)
     ms_fwd = timed(fwd, 5)
+    ms_train = timed(train_step, 5)
+    ms_bwd_saved = timed(lambda: gdn.gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, stream=stream), 5)
     in_bytes = sum(int(x.numel()) * x.element_size() for x in (q, k, v, g, beta, d_o))
     out = {"workload": "stateless_8k", "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
            "forward_ms": ms_fwd, "ratio_to_forward": ms / ms_fwd,
            "workspace_bytes": int(ws.numel()), "input_bytes": in_bytes,
-           "path": gdn.gdn_kernel_path(p)}
+           "path": gdn.gdn_kernel_path(p),
+           "kept_forward": {"fwd_save_plus_bwd_saved_ms": ms_train, "bwd_saved_ms": ms_bwd_saved,
+                            "bwd_saved_ratio_to_forward": ms_bwd_saved / ms_fwd,
+                            "fwd_plus_bwd_ms": ms_fwd + ms}}
 
     # the fp32 token-level backward of the same problem (one segment from a zero state)
     H_in = torch.zeros((w.B, w.H, 1, w.dk, w.dv), device=dev)
@@ -334,8 +344,11 @@ def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
     fws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(p), dev)
     ms = timed(lambda: gdn.gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, ws=ws, stream=stream), 3)
     ms_fwd = timed(lambda: gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, ws=fws, stream=stream), 3)
+    gdn.gdn_chunk_fwd_save(q, k, v, g, beta, h0, ws=ws, stream=stream)
+    ms_saved = timed(lambda: gdn.gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, stream=stream), 3)
     out["stateful_32k"] = {"ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "forward_ms": ms_fwd,
-                           "ratio_to_forward": ms / ms_fwd, "workspace_bytes": int(ws.numel())}
+                           "ratio_to_forward": ms / ms_fwd, "workspace_bytes": int(ws.numel()),
+                           "bwd_saved_ms": ms_saved}
     return out
 
 

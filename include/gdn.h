@@ -243,6 +243,31 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The forward and backward of a training step with the forward's intermediates kept: the
+ * backward of gdn_chunk_bwd (issue #320, section 4 of the test report for PR #1114) reruns
+ * the chunk prepare pass and the forward state pass to rebuild what it needs; here the
+ * forward keeps both in the caller's workspace.
+ *   gdn_chunk_fwd_save: gdn_chunk_fwd (the same o and hT, bit for bit) that also leaves in ws
+ *     the backward's chunk records and the state entering every chunk.
+ *   gdn_chunk_bwd_saved: gdn_chunk_bwd (the same gradients, bit for bit) from that ws, for
+ *     the same problem and inputs (q, k, v, g, beta unchanged since the forward; h0 is not
+ *     needed again: the kept states hold it).
+ * Only on the chunked matrix-core path (bf16 inputs, dk = dv = 128, gdn_chunk_bwd's
+ * condition); other problems get GDN_EUNSUPPORTED. ws: 256-byte aligned, at least
+ * gdn_chunk_fwd_save_workspace() bytes (the size gdn_chunk_bwd_workspace gives for the same
+ * problem), owned by the caller between the two calls. Arguments as for gdn_chunk_fwd and
+ * gdn_chunk_bwd.
+ */
+gdn_status gdn_chunk_fwd_save_workspace(const gdn_problem* p, size_t* bytes);
+gdn_status gdn_chunk_fwd_save(const gdn_problem* p, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, const float* h0, void* o, float* hT,
+                              void* ws, size_t ws_bytes, void* stream);
+gdn_status gdn_chunk_bwd_saved(const gdn_problem* p, const void* q, const void* k, const void* v,
+                               const float* g, const float* beta, const void* d_o, const float* dhT,
+                               float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
  * The layer steps around the core (PR #1035, section "What does this PR do": a
  * depthwise Conv1D on the projected Q/K/V before the Gated DeltaNet, whose left halo is
  * all the p2p mode exchanges between neighbouring ranks; RMSNorm and gating on its

@@ -445,41 +445,57 @@ BwdMfmaPlan make_bwd_mfma_plan(const gdn_problem& p) {
     return pl;
 }
 
-gdn_status run_bwd_mfma(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const float* h0, const void* d_o, const float* dhT,
-                        float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws, hipStream_t s) {
+gdn::BwdRecords bwd_records(const BwdMfmaPlan& pl, void* ws) {
     char* base = static_cast<char*>(ws);
-    const gdn::Workspace w = carve(pl.fwd, ws);
     gdn::BwdRecords rec;
     rec.thatT = base + pl.thatT_off;
     rec.pT = base + pl.pT_off;
     rec.t_rm = base + pl.trm_off;
     rec.p_rm = base + pl.prm_off;
-    if (pl.fwd.nch > 0) {
-        gdn::PrepArgs pa;
-        pa.B = p.B; pa.T = p.T; pa.H = p.H; pa.Hqk = p.Hqk; pa.dk = p.dk; pa.NT = static_cast<int>(pl.fwd.NT);
-        pa.q = q; pa.k = k; pa.g = g; pa.beta = beta; pa.valid_len = p.valid_len; pa.cu_seqlens = nullptr; pa.ws = w;
-        pa.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
-        pa.has_prologue = 0;
-        pa.pro = gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
-        pa.has_conv = 0;
-        pa.conv = gdn::PrepConv{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
-        pa.bwd = rec;
-        hipError_t e = gdn::launch_prep_mfma(pa, s);
-        if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
-        // the forward state pass, keeping the state entering every chunk
-        gdn::StateArgs sa = state_args(p, pl.fwd, q, k, v, w);
-        sa.pass = gdn::kPassS;
-        sa.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
-        sa.s_init = h0;
-        sa.states = base + pl.states_off;
-        gdn_status st = run_state(p, sa, s);
-        if (st != GDN_OK) return st;
-    }
+    return rec;
+}
+
+// The prepare pass with the backward's records and the forward state pass keeping the state
+// entering every chunk; with outputs (o non-NULL) the state pass also writes o and hT.
+gdn_status run_fwd_keep(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, void* o, float* hT, void* ws,
+                        hipStream_t s) {
+    if (pl.fwd.nch == 0) return GDN_OK;
+    char* base = static_cast<char*>(ws);
+    const gdn::Workspace w = carve(pl.fwd, ws);
+    gdn::PrepArgs pa;
+    pa.B = p.B; pa.T = p.T; pa.H = p.H; pa.Hqk = p.Hqk; pa.dk = p.dk; pa.NT = static_cast<int>(pl.fwd.NT);
+    pa.q = q; pa.k = k; pa.g = g; pa.beta = beta; pa.valid_len = p.valid_len; pa.cu_seqlens = nullptr; pa.ws = w;
+    pa.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
+    pa.has_prologue = 0;
+    pa.pro = gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
+    pa.has_conv = 0;
+    pa.conv = gdn::PrepConv{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
+    pa.bwd = bwd_records(pl, ws);
+    pa.bwd.keep_pmat = o ? 1 : 0;
+    hipError_t e = gdn::launch_prep_mfma(pa, s);
+    if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
+    gdn::StateArgs sa = state_args(p, pl.fwd, q, k, v, w);
+    sa.pass = o ? gdn::kPassOutputs : gdn::kPassS;
+    sa.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+    sa.s_init = h0;
+    sa.o = o;
+    sa.s_out = hT;
+    sa.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+    sa.states = base + pl.states_off;
+    return run_state(p, sa, s);
+}
+
+// The reverse chain and the gradient pass on a workspace that holds the records and states.
+gdn_status run_bwd_from_saved(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k,
+                              const void* v, const float* g, const float* beta, const void* d_o, const float* dhT,
+                              float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws,
+                              hipStream_t s) {
+    char* base = static_cast<char*>(ws);
     gdn::BwdMfmaArgs a;
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.NT = static_cast<int>(pl.fwd.NT);
     a.q = q; a.k = k; a.v = v; a.d_o = d_o; a.g = g; a.beta = beta; a.dhT = dhT; a.valid_len = p.valid_len;
-    a.ws = w; a.rec = rec;
+    a.ws = carve(pl.fwd, ws); a.rec = bwd_records(pl, ws);
     a.states = base + pl.states_off;
     a.dstates = base + pl.dstates_off;
     a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta; a.dh0_out = dh0;
@@ -487,6 +503,14 @@ gdn_status run_bwd_mfma(const gdn_problem& p, const BwdMfmaPlan& pl, const void*
     if (e != hipSuccess) return hip_fail(e, "backward state kernel launch");
     e = gdn::launch_bwd_grad_mfma(a, s);
     return e == hipSuccess ? GDN_OK : hip_fail(e, "backward gradient kernel launch");
+}
+
+gdn_status run_bwd_mfma(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, const void* d_o, const float* dhT,
+                        float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws, hipStream_t s) {
+    gdn_status st = run_fwd_keep(p, pl, q, k, v, g, beta, h0, nullptr, nullptr, ws, s);
+    if (st != GDN_OK) return st;
+    return run_bwd_from_saved(p, pl, q, k, v, g, beta, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws, s);
 }
 
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
@@ -526,6 +550,64 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
         a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta; a.dh0_out = dh0;
         hipError_t e = gdn::launch_bwd(a, p->io_dtype == GDN_BF16, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? GDN_OK : hip_fail(e, "backward kernel launch");
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_chunk_fwd_save_workspace(const gdn_problem* p, size_t* bytes) {
+    gdn_status st = check_problem(p);
+    if (st != GDN_OK) return st;
+    if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    if (!use_bwd_mfma(*p))
+        return fail(GDN_EUNSUPPORTED, "keeping the forward for the backward needs bf16 inputs with dk = dv = 128");
+    *bytes = make_bwd_mfma_plan(*p).bytes;
+    return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_save(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, const float* h0, void* o, float* hT, void* ws, size_t ws_bytes,
+                              void* stream) {
+    try {
+        gdn_status st = check_fwd_args(p, q, k, v, g, beta, o);
+        if (st != GDN_OK) return st;
+        if (!use_bwd_mfma(*p))
+            return fail(GDN_EUNSUPPORTED, "keeping the forward for the backward needs bf16 inputs with dk = dv = 128");
+        const BwdMfmaPlan pl = make_bwd_mfma_plan(*p);
+        Plan need;
+        need.bytes = pl.bytes;
+        st = check_ws(need, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (p->B == 0) return GDN_OK;
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        // no chunks: the plain forward (hT = h0, or zero) keeps nothing
+        if (pl.fwd.nch == 0) return run_fwd(*p, pl.fwd, q, k, v, g, beta, h0, o, hT, ws, s);
+        return run_fwd_keep(*p, pl, q, k, v, g, beta, h0, o, hT, ws, s);
+    } catch (...) {
+        return fail(GDN_EHIP, "unexpected exception");
+    }
+}
+
+gdn_status gdn_chunk_bwd_saved(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
+                               const float* beta, const void* d_o, const float* dhT, float* dq, float* dk,
+                               float* dv, float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
+                               void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+            return fail(GDN_EINVAL, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (!use_bwd_mfma(*p))
+            return fail(GDN_EUNSUPPORTED, "the backward from a kept forward needs bf16 inputs with dk = dv = 128");
+        const BwdMfmaPlan pl = make_bwd_mfma_plan(*p);
+        Plan need;
+        need.bytes = pl.bytes;
+        st = check_ws(need, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (p->B == 0) return GDN_OK;
+        return run_bwd_from_saved(*p, pl, q, k, v, g, beta, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
+                                  static_cast<hipStream_t>(stream));
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

@@ -113,6 +113,7 @@ struct BwdRecords {
     void* pT = nullptr;
     void* t_rm = nullptr;
     void* p_rm = nullptr;
+    int keep_pmat = 0;      // with the backward records, also the forward's P record (for outputs)
 };
 
 struct PrepArgs {

@@ -473,7 +473,8 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
         }
         const int64_t off = ch * kTriRecord + blk * 512 + l * 8;
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.that) + off) = w;
-        if (!a.bwd.thatT) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.pmat) + off) = wp;   // unread by the backward
+        // the backward alone does not read the forward's P record
+        if (!a.bwd.thatT || a.bwd.keep_pmat) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.pmat) + off) = wp;
         if (a.ws.that_lo) *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.ws.that_lo) + off) = wl;
     }
     if (a.bwd.thatT) {

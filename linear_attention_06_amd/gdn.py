@@ -24,7 +24,8 @@ CHUNK = 64
 # The functions include/gdn.h declares.
 EXPORTS = ("gdn_status_string", "gdn_last_error", "gdn_kernel_path", "gdn_chunk_fwd_workspace",
            "gdn_chunk_fwd", "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_prologue", "gdn_chunk_fwd_prologue_qkv", "gdn_chunk_fwd_conv", "gdn_chunk_fwd_varlen_workspace",
-           "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_causal_conv1d",
+           "gdn_chunk_fwd_varlen", "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_chunk_fwd_save_workspace",
+           "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_causal_conv1d",
            "gdn_gated_rmsnorm",
            "gdn_segment_workspace", "gdn_segment_summary", "gdn_summary_combine",
            "gdn_apply_initial_state", "gdn_segment_bwd_workspace", "gdn_apply_initial_state_bwd",
@@ -75,6 +76,9 @@ def lib():
         L.gdn_chunk_fwd_varlen.argtypes = [pp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gdn_chunk_bwd_workspace.argtypes = [pp, ctypes.POINTER(sz)]
         L.gdn_chunk_bwd.argtypes = [pp] + [vp] * 15 + [sz, vp]
+        L.gdn_chunk_fwd_save_workspace.argtypes = [pp, ctypes.POINTER(sz)]
+        L.gdn_chunk_fwd_save.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gdn_chunk_bwd_saved.argtypes = [pp] + [vp] * 14 + [sz, vp]
         L.gdn_causal_conv1d.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp]
         L.gdn_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, ctypes.c_float, vp, vp]
         L.gdn_segment_summary.argtypes = [pp, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -376,6 +380,56 @@ def gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, dhT=None, valid_len=None, want_dh0=
                                _ptr(d_o), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
                                _ptr(dh0), _ptr(ws), ws.numel(), _stream(stream)),
            "gdn_chunk_bwd")
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+def gdn_chunk_fwd_save_workspace(p: GdnProblem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().gdn_chunk_fwd_save_workspace(ctypes.byref(p), ctypes.byref(n)), "gdn_chunk_fwd_save_workspace")
+    return n.value
+
+
+def gdn_chunk_fwd_save(q, k, v, g, beta, h0=None, valid_len=None, o=None, hT=None, want_state=True,
+                       ws=None, stream=None):
+    """gdn_chunk_fwd that keeps, in ws, what gdn_chunk_bwd_saved needs. Returns (o, hT or
+    None, ws); ws must stay untouched until the backward has run."""
+    _io_checks(q, k, v, g, beta)
+    _dev(h0, "h0", torch.float32)
+    p = problem(q, v, valid_len)
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    _dev(o, "o", v.dtype)
+    if hT is None and want_state:
+        hT = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=v.device)
+    _dev(hT, "hT", torch.float32)
+    need = gdn_chunk_fwd_save_workspace(p)
+    if ws is None:
+        ws = workspace(need, v.device)
+    _check(lib().gdn_chunk_fwd_save(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(h0), _ptr(o), _ptr(hT), _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_chunk_fwd_save")
+    return o, hT, ws
+
+
+def gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, dhT=None, valid_len=None, want_dh0=True, stream=None):
+    """Backward from the workspace of gdn_chunk_fwd_save on the same inputs. Returns
+    (dq, dk, dv, dg, dbeta, dh0 or None), all fp32."""
+    _io_checks(q, k, v, g, beta)
+    _dev(d_o, "d_o", v.dtype)
+    _dev(dhT, "dhT", torch.float32)
+    _dev(ws, "ws", torch.uint8)
+    p = problem(q, v, valid_len)
+    f32 = dict(dtype=torch.float32, device=v.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    dg = torch.empty(g.shape, **f32)
+    dbeta = torch.empty(beta.shape, **f32)
+    dh0 = torch.empty((p.B, p.H, p.dk, p.dv), **f32) if want_dh0 else None
+    _check(lib().gdn_chunk_bwd_saved(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(d_o), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                     _ptr(dbeta), _ptr(dh0), _ptr(ws), ws.numel(), _stream(stream)),
+           "gdn_chunk_bwd_saved")
     return dq, dk, dv, dg, dbeta, dh0
 
 

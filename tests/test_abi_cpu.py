@@ -205,6 +205,33 @@ def test_backward_argument_checks():
     assert L.gdn_chunk_bwd(ctypes.byref(p), *args, vp(258), n.value, None) == gdn.GDN_EWORKSPACE
 
 
+def test_saved_forward_argument_checks():
+    """gdn_chunk_fwd_save / gdn_chunk_bwd_saved: only the chunked matrix-core problem, a
+    workspace as large as gdn_chunk_bwd's, and every check before any launch."""
+    L = gdn.lib()
+    vp = ctypes.c_void_p
+    n = ctypes.c_size_t(0)
+    assert L.gdn_chunk_fwd_save_workspace(ctypes.byref(P()), ctypes.byref(n)) == gdn.GDN_EUNSUPPORTED
+    p = P(B=1, T=300, H=4, Hqk=2, dk=128, dv=128, io_dtype=gdn.GDN_BF16)
+    assert L.gdn_chunk_fwd_save_workspace(ctypes.byref(p), ctypes.byref(n)) == gdn.GDN_OK
+    nb = ctypes.c_size_t(0)
+    assert L.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(nb)) == gdn.GDN_OK
+    assert n.value == nb.value
+    fwd = lambda q=vp(1), o=vp(1), ws=vp(256), nbytes=n.value, pp=p: L.gdn_chunk_fwd_save(
+        ctypes.byref(pp), q, vp(1), vp(1), vp(1), vp(1), None, o, None, ws, nbytes, None)
+    assert fwd(q=None) == gdn.GDN_EINVAL
+    assert fwd(o=None) == gdn.GDN_EINVAL
+    assert fwd(nbytes=n.value - 1) == gdn.GDN_EWORKSPACE
+    assert fwd(ws=vp(258)) == gdn.GDN_EWORKSPACE
+    assert fwd(pp=P()) == gdn.GDN_EUNSUPPORTED
+    args = [vp(1)] * 6 + [None] + [vp(1)] * 5 + [None]
+    bad = list(args)
+    bad[7] = None                                   # dq
+    assert L.gdn_chunk_bwd_saved(ctypes.byref(p), *bad, vp(256), n.value, None) == gdn.GDN_EINVAL
+    assert L.gdn_chunk_bwd_saved(ctypes.byref(p), *args, vp(256), n.value - 1, None) == gdn.GDN_EWORKSPACE
+    assert L.gdn_chunk_bwd_saved(ctypes.byref(P()), *args, vp(256), 1 << 40, None) == gdn.GDN_EUNSUPPORTED
+
+
 def test_layer_step_argument_checks():
     L = gdn.lib()
     vp = ctypes.c_void_p

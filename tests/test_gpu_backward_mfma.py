@@ -159,3 +159,39 @@ def test_chunked_backward_matches_token_level_stateful_2k():
         print("2k stateful %s rel-L2 %.3e scaled max-abs %.3e" % (nm, err, sma))
         assert np.all(np.isfinite(xn)), nm
         assert err <= TOL_BF16 and sma <= TOL_MAXABS, nm
+
+
+SAVED_CASES = [
+    # name, B, T, Hqk, H, valid, h0, dhT
+    ("ragged_stateful", 1, 150, 2, 4, None, True, True),
+    ("padded_rows", 2, 300, 2, 4, 173, False, True),
+    ("stateful_2k_rep2", 1, 2048, 16, 32, None, True, True),
+    ("empty", 1, 0, 1, 2, None, True, True),
+]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=[c[0] for c in SAVED_CASES])
+def test_saved_forward_and_backward_match_the_plain_calls(case):
+    """gdn_chunk_fwd_save gives gdn_chunk_fwd's o and hT bit for bit, and
+    gdn_chunk_bwd_saved on its workspace gives gdn_chunk_bwd's gradients bit for bit (the
+    same kernels on the same records and states); the backward runs twice on one kept
+    forward, as a caller that recomputes a gradient would."""
+    name, B, T, Hqk, H, valid, with_h0, with_dhT = case
+    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="saved_" + name, B=B, T=T, Hqk=Hqk, H=H,
+                            seed=840 + T + H, valid_len=valid)
+    inp = make_inputs(w)
+    q, k, v, g, beta, h0, vl = to_dev(inp)
+    if not with_h0:
+        h0 = None
+    d_o, _ = output_grad(tuple(v.shape), 841 + T)
+    dhT = 0.1 * torch.randn((B, H, 128, 128), device=dev()) if with_dhT else None
+    o_ref, hT_ref = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, vl)
+    ref = gdn.gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, dhT, vl)
+    o, hT, ws = gdn.gdn_chunk_fwd_save(q, k, v, g, beta, h0, vl)
+    got = gdn.gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, dhT, vl)
+    again = gdn.gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, dhT, vl)
+    sync()
+    assert torch.equal(o, o_ref) and torch.equal(hT, hT_ref)
+    for nm, x, y, z in zip(NAMES, got, again, ref):
+        assert torch.equal(x, z), "%s %s differs from gdn_chunk_bwd" % (name, nm)
+        assert torch.equal(y, z), "%s %s differs on the second backward" % (name, nm)
