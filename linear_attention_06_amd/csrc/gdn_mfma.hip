@@ -145,14 +145,16 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
     // Block order: chunk-major, the heads of one (b, chunk) back to back on one XCD
     // (workgroups go round-robin over the 8 XCDs), so that its L2 serves the q/k rows
     // shared by the value heads of a query/key head and the g / beta lines shared by
-    // all heads. ch is the (b, h, chunk) record index.
+    // all heads. Chunks run from the last to the first: the state pass that follows
+    // starts with the records written last, which the memory-side cache still holds.
+    // ch is the (b, h, chunk) record index.
     const int64_t L = blockIdx.x;
     const int xcd = static_cast<int>(L & 7);
     const int64_t u = L >> 3;
     const int h = static_cast<int>(u % a.H);
     const int64_t pair = (u / a.H) * 8 + xcd;
     if (pair >= static_cast<int64_t>(a.B) * a.NT) return;
-    const int b = static_cast<int>(pair / a.NT), n = static_cast<int>(pair % a.NT);
+    const int b = static_cast<int>(pair / a.NT), n = a.NT - 1 - static_cast<int>(pair % a.NT);
     const int64_t ch = (static_cast<int64_t>(b) * a.H + h) * a.NT + n;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 5, lr = lane & 31;
