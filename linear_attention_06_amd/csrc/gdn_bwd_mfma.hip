@@ -122,6 +122,7 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
     __shared__ __align__(16) unsigned char qst[2 * RQ_SIZE];
     __shared__ __align__(16) unsigned char ahd[2 * RA_SIZE];
     __shared__ __align__(16) unsigned char bhd[2 * RB_SIZE2];
+    __shared__ __align__(16) unsigned char pf_s[256];   // sink of the L2 prefetches
 
     // XCD-aware order as in the forward state pass: the column tiles of the value heads
     // that share a query/key head run on one XCD
@@ -252,8 +253,74 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
 
     if (wave == 1) {
         // ---------------- helper wave ----------------
+        // L2 prefetch, a few chunks ahead of the loading waves: the workgroups that read the
+        // same lines split them, so that each line is fetched from memory once per XCD and the
+        // loading waves' requests hit the L2. Lanes 0..15: the 256 lines of a chunk's k and q
+        // rows, split over the rep x 8 workgroups of the query/key head; 16..31: the 128 lines
+        // of the value head's dO rows, 32..44: its That^T and P^T records (96 lines), 45..47:
+        // its decay record, each split over the head's 8 column tiles. The data lands in a
+        // scratch LDS word per lane that nothing reads.
+        const unsigned char* pf_base = nullptr;
+        int64_t pf_stride = 0;   // bytes per chunk
+        int pf_row = -1;         // token row inside the chunk for q/k/dO lines, else -1
+        bool pf_lane = true;
+        {
+            const int64_t bT = rs.start;
+            const int qk_share = rep * tiles, qk_rank = (kk % rep) * tiles + tile;
+            const int kq_lanes = min(16, (256 + qk_share - 1) / qk_share);
+            if (lane < 16) {
+                const int lam = kq_lanes * qk_rank + lane;
+                pf_lane = lane < kq_lanes && lam < 256;
+                const uint16_t* src = static_cast<const uint16_t*>(lam < 128 ? a.k : a.q);
+                pf_row = (lam & 127) >> 1;
+                pf_base = reinterpret_cast<const unsigned char*>(src + bT * qk_row + hq * DK + 64 * (lam & 1));
+                pf_stride = qk_row * 2;
+            } else if (lane < 32) {
+                const int lam = 16 * tile + lane - 16;
+                pf_row = lam >> 1;
+                pf_base = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.d_o) + bT * v_row +
+                                                                  h * DK + 64 * (lam & 1));
+                pf_stride = v_row * 2;
+            } else if (lane < 45) {
+                const int lam = 13 * tile + lane - 32;
+                pf_lane = lam < 96;
+                const uint16_t* rec = static_cast<const uint16_t*>(lam < 48 ? a.rec.thatT : a.rec.pT);
+                pf_base = reinterpret_cast<const unsigned char*>(rec + bh * NT * kTriRecord) + 128 * (lam % 48);
+                pf_stride = kTriRecord * 2;
+            } else if (lane < 48) {
+                // the 1 KiB decay record: 8 lines over the 8 tiles' three lanes
+                const int lam = 3 * tile + lane - 45;
+                pf_lane = lam < 8;
+                pf_base = reinterpret_cast<const unsigned char*>(a.ws.gates + bh * NT * kGateRecordMfma) + 128 * (lam & 7);
+                pf_stride = kGateRecordMfma * 4;
+            } else {
+                pf_lane = false;
+            }
+        }
+        const uint32_t pf_lds = lds_addr(pf_s);
+        auto prefetch = [&](int c) {
+            const unsigned char* p;
+            if (pf_row >= 0) {
+                int64_t t = static_cast<int64_t>(c) * kChunk + pf_row;
+                if (t > rs.extent - 1) t = rs.extent - 1;
+                p = pf_base + t * pf_stride;
+            } else {
+                p = pf_base + static_cast<int64_t>(c) * pf_stride;
+            }
+            const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pf_lds));
+            if (pf_lane)
+                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(p) : "memory", "m0");
+        };
+        // a row without chunks has no line to prefetch (the clamped token index would fall
+        // before the row)
+        const bool pf_on = NT > 0 && rs.extent > 0;
+        if (pf_on) {
+            prefetch(max(c0 - 2, 0));
+            prefetch(max(c0 - 3, 0));
+        }
         for (int i = 0; i < iters; ++i) {
             chunk_barrier(false);
+            if (pf_on) prefetch(max(c0 - i - 4, 0));
             const int c = c0 - i;
             if (c >= 0) {
                 const unsigned char* qs = qst + (c & 1) * RQ_SIZE;
@@ -312,6 +379,7 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);
         return;
     }
 
