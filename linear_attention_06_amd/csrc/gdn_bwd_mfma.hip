@@ -818,25 +818,31 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
+                    // transposed products (the S-side fragments as the A operand): lane
+                    // (l16, g4) holds token 16 r + l16 at dk columns 16 m + 4 g4 .. + 3, so
+                    // that the dGam sum over dk is three adds and a sum over the lane groups
                     f32x4 zf = zero4(), zg = zero4(), zh = zero4();
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {
-                        zf = mfma16(frag_rowmajor(sm + G_DO, SPB, 16 * r, 32 * s, l16, g4), stf[s], zf);
-                        zg = mfma16(frag_kmajor(sm + G_DX, SPB, 32 * s, 16 * r, l16, g4), stf[s], zg);
-                        zh = mfma16(frag_kmajor(sm + G_UET, SPB, 32 * s, 16 * r, l16, g4), dstf[s], zh);
+                        zf = mfma16(stf[s], frag_rowmajor(sm + G_DO, SPB, 16 * r, 32 * s, l16, g4), zf);
+                        zg = mfma16(stf[s], frag_kmajor(sm + G_DX, SPB, 32 * s, 16 * r, l16, g4), zg);
+                        zh = mfma16(dstf[s], frag_kmajor(sm + G_UET, SPB, 32 * s, 16 * r, l16, g4), zh);
                     }
-                    const f32x4 eg = *reinterpret_cast<const f32x4*>(eg_s + 16 * r + 4 * g4);
-                    const f32x4 qv = tile_acc_order(sm + G_Q, KPB, 16 * r, 16 * m, l16, g4);
-                    const f32x4 kv = tile_acc_order(sm + G_K, KPB, 16 * r, 16 * m, l16, g4);
+                    const float eg = eg_s[16 * r + l16];
+                    const int qk_off = (16 * r + l16) * KPB + (16 * m + 4 * g4) * 2;
+                    const f32x4 qv = bf16x4_to_f32(*reinterpret_cast<const u32x2*>(sm + G_Q + qk_off));
+                    const f32x4 kv = bf16x4_to_f32(*reinterpret_cast<const u32x2*>(sm + G_K + qk_off));
+                    float gp = 0.f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        zf[j] *= eg[j];
+                        zf[j] *= eg;
                         wsum += zh[j] * kv[j];
-                        const float gp = row_sum16(zf[j] * qv[j] + (zg[j] - zh[j]) * kv[j]);
-                        if (l16 == 0) part_g[wave * 64 + 16 * r + 4 * g4 + j] += gp;
+                        gp += zf[j] * qv[j] + (zg[j] - zh[j]) * kv[j];
                         dq_acc[r][j] += zf[j];
                         dk_acc[r][j] += zg[j] + zh[j];
                     }
+                    gp = col_sum4(gp);
+                    if (g4 == 0) part_g[wave * 64 + 16 * r + l16] += gp;
                     __builtin_amdgcn_sched_barrier(0);   // keeps each tile's operand reads with it
                 }
 #pragma unroll
@@ -1045,27 +1051,27 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                dq_acc[r] = mfma16(frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dq_acc[r]);
-                dk_acc[r] = mfma16(frag_rowmajor(sm + G_XT, SPB, 16 * r, 32 * s, l16, g4), qt[s], dk_acc[r]);
-                dk_acc[r] = mfma16(frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * r, l16, g4), kt[s], dk_acc[r]);
-                dk_acc[r] = mfma16(frag_rowmajor(sm + G_DUT, SPB, 16 * r, 32 * s, l16, g4), kt[s], dk_acc[r]);
+                // transposed like the accumulators (the K / Q side as the A operand)
+                dq_acc[r] = mfma16(kt[s], frag_kmajor(sm + G_XT, SPB, 32 * s, 16 * r, l16, g4), dq_acc[r]);
+                dk_acc[r] = mfma16(qt[s], frag_rowmajor(sm + G_XT, SPB, 16 * r, 32 * s, l16, g4), dk_acc[r]);
+                dk_acc[r] = mfma16(kt[s], frag_kmajor(sm + G_DUT, SPB, 32 * s, 16 * r, l16, g4), dk_acc[r]);
+                dk_acc[r] = mfma16(kt[s], frag_rowmajor(sm + G_DUT, SPB, 16 * r, 32 * s, l16, g4), dk_acc[r]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // dq and dk of the query/key head (zero past the valid tokens)
+    // dq and dk of the query/key head (zero past the valid tokens): lane (l16, g4) holds
+    // token 16 r + l16 at dk columns 16 m + 4 g4 .. + 3
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t t = t0 + 16 * r + 4 * g4 + j;
-            if (t < a.T) {
-                const bool valid = t < nvalid;
-                const int64_t o = ((rs.start + t) * a.Hqk + hq) * DK + 16 * m + l16;
-                a.dq_out[o] = valid ? dq_acc[r][j] : 0.f;
-                a.dk_out[o] = valid ? dk_acc[r][j] : 0.f;
-            }
+    for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 16 * r + l16;
+        if (t < a.T) {
+            const bool valid = t < nvalid;
+            const int64_t o = ((rs.start + t) * a.Hqk + hq) * DK + 16 * m + 4 * g4;
+            *reinterpret_cast<f32x4*>(a.dq_out + o) = valid ? dq_acc[r] : zero4();
+            *reinterpret_cast<f32x4*>(a.dk_out + o) = valid ? dk_acc[r] : zero4();
         }
+    }
     __builtin_amdgcn_s_waitcnt(0);   // every prefetch has landed in the sink
 }
 
