@@ -634,8 +634,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
     for (int kk = 0; kk < rep; ++kk) {
         const int h = hq * rep + kk;
         const int64_t bh = static_cast<int64_t>(b) * a.H + h, ch = bh * NT + n;
-        // decay vectors of the chunk (the other waves prefetch the first panel's lines)
-        if (kk == 0 && wave > 0) pf_panel(h, ch, 0, fresh_lane(tid) - 64);
+        // decay vectors of the chunk
         if (wave == 0) {
             const int64_t t = t0 + lane;
             const bool valid = t < nvalid;
@@ -791,20 +790,17 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             }
             // ---- C ----
             // prefetch: the next panel's phase A lines and the row-major records of phase D0,
-            // or after the last panel the next value head's first panel and decay inputs
-            // (the thread index re-derived here, so that no address is kept live across phases)
+            // or after the last panel the next value head's first panel, by waves 1-6 (wave 0's
+            // own loads of the next decay inputs would otherwise wait behind them; those
+            // lines, shared by all heads of a token, are in the L2 already). The thread index
+            // is re-derived here, so that no address is kept live across phases.
             if (pn == 0) {
                 const int pt = fresh_lane(tid);
                 if (pt < 384) pf_panel(h, ch, 1, pt);
                 else pf_line(static_cast<const uint16_t*>(pt < 448 ? a.rec.t_rm : a.rec.p_rm) + ch * 4096 + (pt & 63) * 64);
             } else if (kk + 1 < rep) {
                 const int pt = fresh_lane(tid);
-                if (pt < 384) {
-                    pf_panel(h + 1, ch + NT, 0, pt);
-                } else {
-                    const int64_t t = min(t0 + (pt & 63), static_cast<int64_t>(a.T) - 1);
-                    pf_line((pt < 448 ? a.g : a.beta) + (rs.start + t) * a.H + h + 1);
-                }
+                if (pt >= 64 && pt < 448) pf_panel(h + 1, ch + NT, 0, pt - 64);
             }
             {
                 const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
