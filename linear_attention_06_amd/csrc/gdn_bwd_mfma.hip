@@ -882,7 +882,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             const int J = 16 * ci + l16;
             const float gamJ = gam_s[J], betaJ = beta_s[J];
             f32x4 outv;
-            float colacc = 0.f;
+            float colacc = 0.f, rmine = 0.f;   // lane l16 < 4 keeps the row sum of row 4 g4 + l16
             const f32x4 mv = tile_acc_order(sm + (item < 10 ? G_DST : G_ST), SPB, 16 * ri, 16 * ci, l16, g4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -891,7 +891,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 if (item < 10) {
                     const float x = d * mv[j];   // dP . P
                     const float rsum = row_sum16(x);
-                    if (l16 == 0) part_g[wave * 64 + I] += rsum;
+                    rmine = l16 == j ? rsum : rmine;
                     colacc += x;
                     outv[j] = I >= J ? d * __expf(gam_s[I] - gamJ) : 0.f;
                 } else {
@@ -899,6 +899,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                     outv[j] = d * betaJ;
                 }
             }
+            if (item < 10 && l16 < 4) part_g[wave * 64 + 16 * ri + 4 * g4 + l16] += rmine;
             colacc = col_sum4(colacc);
             if (g4 == 0) {
                 if (item < 10) part_g[wave * 64 + J] -= colacc;
@@ -955,7 +956,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             const int J = 16 * ci + l16;
             const float gamJ = gam_s[J];
             f32x4 ev;
-            float colacc = 0.f;
+            float colacc = 0.f, bmine = 0.f, gmine = 0.f;   // row sums of row 4 g4 + l16, lanes l16 < 4
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int I = 16 * ri + 4 * g4 + j;
@@ -966,12 +967,14 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 const float e = da * beta_s[I] * ex;
                 const float x = e * kkt[i][j];
                 const float rsum = row_sum16(x);
-                if (l16 == 0) {
-                    part_b[wave * 64 + I] += dbr;
-                    part_g[wave * 64 + I] += rsum;
-                }
+                bmine = l16 == j ? dbr : bmine;
+                gmine = l16 == j ? rsum : gmine;
                 colacc += x;
                 ev[j] = e;
+            }
+            if (l16 < 4) {
+                part_b[wave * 64 + 16 * ri + 4 * g4 + l16] += bmine;
+                part_g[wave * 64 + 16 * ri + 4 * g4 + l16] += gmine;
             }
             colacc = col_sum4(colacc);
             if (g4 == 0) part_g[wave * 64 + J] -= colacc;
