@@ -562,36 +562,43 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
 
 // Loading wave (index among the loading waves) that issues load g of an iteration.
 // Waves w and w + 4 of a workgroup run on the same SIMD; the deal gives every SIMD
-// the same share of the loads. With outputs, waves 0 and 1 (chain, output) each
-// share their SIMD with one loading wave (indices 2 and 3), which take two of every
-// eight loads; otherwise wave 0 shares its SIMD with loading wave 3.
-__host__ __device__ constexpr int load_owner(bool with_outputs, int g) {
+// the same share of the loads. Mode 1 (outputs: chain and output waves 0 and 1, loading
+// waves 2 .. 7): waves 0 and 1 each share their SIMD with one loading wave (indices 2
+// and 3), which take two of every eight loads. Mode 2 (two tiles of both summaries: M
+// chains on waves 0 and 1, S chains on waves 2 and 3, loading waves 4 .. 7): the loading
+// waves beside the S chains (indices 2 and 3) take three of every four loads. Mode 0
+// (one chain wave, loading waves 1 .. 7): wave 0 shares its SIMD with loading wave 3.
+__host__ __device__ constexpr int load_owner(int mode, int g) {
     const int p = g & 7;
-    if (with_outputs) return (p == 0 || p == 3) ? 2 : (p == 1 || p == 4) ? 3 : (p == 2) ? 0 : (p == 5) ? 1 : (p == 6) ? 4 : 5;
+    if (mode == 1) return (p == 0 || p == 3) ? 2 : (p == 1 || p == 4) ? 3 : (p == 2) ? 0 : (p == 5) ? 1 : (p == 6) ? 4 : 5;
+    if (mode == 2) return (p == 0) ? 0 : (p == 4) ? 1 : (p & 1) ? 2 : 3;
     return p == 0 ? 3 : p - 1;
 }
-__host__ __device__ constexpr int loads_owned(bool with_outputs, int n, int me) {
+__host__ __device__ constexpr int loads_owned(int mode, int n, int me) {
     int c = 0;
-    for (int g = 0; g < n; ++g) c += load_owner(with_outputs, g) == me ? 1 : 0;
+    for (int g = 0; g < n; ++g) c += load_owner(mode, g) == me ? 1 : 0;
     return c;
 }
 
 template <bool kHasV, bool kSplit, bool kOut>
 __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk_groups) {
     constexpr bool outputs = kHasV && kOut;
-    // Both summaries in one pass (values, split, no outputs): wave 0 runs the chain of
-    // the M tile (split operands, no values, identity start, written to a.m_out) and
-    // wave 1 the chain of the S tile (values, zero start, written to a.s_out); the two
-    // share every loaded operand. Requires ncols = dk.
+    // Both summaries in one pass (values, split, no outputs) on two column tiles: waves 0
+    // and 1 run the chains of the M tiles (split operands, no values, identity start,
+    // written to a.m_out), waves 2 and 3 the chains of the S tiles (values, zero start,
+    // written to a.s_out); the four share every loaded operand, each M chain on a SIMD of
+    // its own. Requires ncols = dk; `tiles` counts pairs of column tiles.
     constexpr bool dual = kHasV && kSplit && !kOut;
-    constexpr bool two_compute = outputs || dual;   // waves 0 and 1 compute, 2 .. 7 load
+    constexpr bool two_compute = outputs || dual;   // compute waves first, then loading waves
+    constexpr int load_mode = dual ? 2 : (outputs ? 1 : 0);
+    constexpr int vtiles = dual ? 2 : 1;   // column tiles of V per workgroup
     // K-side stage buffer: K, That, That remainder (split), V; Q-side: Q, P.
     // K-side operands of chunk n are written in iteration n - 1 and read in iteration
     // n; Q-side operands in iteration n and read by the output wave, which runs one
     // chunk behind, in iteration n + 1 (two buffers each); the decay factors of a
     // chunk live from their write to the output wave (ring of four).
     constexpr int KB = 64 * DK * 2, TB = kTriRecord * 2, LB = kSplit ? kTriRecord * 2 : 0;
-    constexpr int VB = kHasV ? 64 * 16 * 2 : 0;
+    constexpr int VB = kHasV ? 64 * 16 * 2 * vtiles : 0;
     constexpr int KSB = KB + TB + LB + VB;
     constexpr int QSB = outputs ? KB : 0;
     constexpr int HB = 6 * 1024;   // hand-off: S fragments (4 blocks), U fragments (2 blocks)
@@ -614,9 +621,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const int bz = qg / a.Hqk, hq = qg % a.Hqk;
     const int h = hq * rep + kk % rep;
     const int b = bz / a.P, seg = bz % a.P;
-    const int col0 = 16 * tile;
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    // the workgroup's first column; a chain wave's own tile (two per workgroup in the
+    // one-pass summary: waves w and w + 2 share tile w % 2)
+    const int colp = 16 * vtiles * tile;
+    const int col0 = colp + (dual ? 16 * (wave & 1) : 0);
     const int ncols = a.ncols;
     const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
     const int64_t nvalid = rs.valid;
@@ -632,7 +642,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * v_row * 2);
     const uint32_t ostep = static_cast<uint32_t>(kChunk * vo_row * 2);
-    const int first_loader = two_compute ? 2 : 1;
+    const int first_loader = dual ? 4 : (two_compute ? 2 : 1);
     // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
     // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 rho + j % 4)). A 1 KiB load fills one
     // quad block with 16 lanes per row, so that each group of 4 lanes reads one 64-byte piece
@@ -673,15 +683,18 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             voff_k[jj] = static_cast<uint32_t>(((lane >> 4) * qk_row + hq * DK +
                                                 8 * ((lane & 15) ^ (4 * (lane >> 4) + jj))) * 2);
         const uint32_t voff_l = static_cast<uint32_t>(16 * lane);
-        uint32_t voff_v[2];
+        // V load m: tile m / 2 of the workgroup, tokens 32 (m % 2) + lane / 2
+        constexpr int NV = kHasV ? 2 * vtiles : 0;
+        uint32_t voff_v[2 * vtiles];
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-            voff_v[m] = static_cast<uint32_t>(((32 * m + (lane >> 1)) * v_row + h * ncols + col0 + 8 * (lane & 1)) * 2);
-        constexpr int nl = 8 - (two_compute ? 2 : 1);
-        constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + (kHasV ? 2 : 0) + 1;
+        for (int m = 0; m < 2 * vtiles; ++m)
+            voff_v[m] = static_cast<uint32_t>(((32 * (m & 1) + (lane >> 1)) * v_row + h * ncols + colp + 16 * (m >> 1) +
+                                               8 * (lane & 1)) * 2);
+        constexpr int nl = 8 - (dual ? 4 : (two_compute ? 2 : 1));
+        constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + NV + 1;
         constexpr int NQ = outputs ? 16 : 0;
         constexpr int NI = NK + NQ;   // 1 KiB loads of one full iteration
-        static_assert(nl >= 6, "loading waves");
+        static_assert(nl >= 4, "loading waves");
 
         // Each 1 KiB load (lane l: 16 bytes, written to LDS at 16 l of its block) goes
         // through registers. In iteration n a loading wave writes to LDS what it loaded
@@ -695,15 +708,15 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // own loads as straight-line code with its registers indexed at compile time.
         auto loader = [&](auto me_tag) {
         constexpr int me = decltype(me_tag)::value;
-        constexpr int NS = loads_owned(two_compute, NI, me);
+        constexpr int NS = loads_owned(load_mode, NI, me);
         using Stage = u32x4[NS > 0 ? NS : 1];
         Stage st0, st1;   // loads of even / odd iterations (relative to n0)
         auto load_k = [&](int n, Stage& stage) {   // K-side operands of chunk n
             const uint32_t tr = static_cast<uint32_t>(n) * (kTriRecord * 2);
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
-                if (load_owner(two_compute, i) != me) continue;
-                u32x4& r = stage[loads_owned(two_compute, i, me)];
+                if (load_owner(load_mode, i) != me) continue;
+                u32x4& r = stage[loads_owned(load_mode, i, me)];
                 if (i < 16) {
                     r = gload16(rk, voff_k[i & 3],
                                 static_cast<uint32_t>(4 * i * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
@@ -712,7 +725,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 } else if (kSplit && i < 28) {
                     r = gload16(rtl, voff_l, tr + (i - 22) * 1024);
                 } else if (kHasV && i < NK - 1) {
-                    r = gload16(rv, voff_v[i - (NK - 3)], static_cast<uint32_t>(n) * vstep);
+                    r = gload16(rv, voff_v[i - (NK - 1 - NV)], static_cast<uint32_t>(n) * vstep);
                 } else {
                     r = gload16(rgt, voff_l, static_cast<uint32_t>(n) * (kGateRecordMfma * 4u));
                 }
@@ -722,21 +735,21 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             unsigned char* dst = kst + (n & 1) * KSB + 16 * lane;
 #pragma unroll
             for (int i = 0; i < NK; ++i) {
-                if (load_owner(two_compute, i) != me) continue;
+                if (load_owner(load_mode, i) != me) continue;
                 unsigned char* p;
                 if (i < 16) p = dst + i * 1024;
                 else if (i < 22) p = dst + KB + (i - 16) * 1024;
                 else if (kSplit && i < 28) p = dst + KB + TB + (i - 22) * 1024;
-                else if (kHasV && i < NK - 1) p = dst + KB + TB + LB + (i - (NK - 3)) * 1024;
+                else if (kHasV && i < NK - 1) p = dst + KB + TB + LB + (i - (NK - 1 - NV)) * 1024;
                 else p = gst + (n % 4) * 1024 + 16 * lane;
-                *reinterpret_cast<u32x4*>(p) = stage[loads_owned(two_compute, i, me)];
+                *reinterpret_cast<u32x4*>(p) = stage[loads_owned(load_mode, i, me)];
             }
         };
         auto load_q = [&](int n, Stage& stage) {   // Q of chunk n
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
-                if (load_owner(two_compute, NK + j) != me) continue;
-                stage[loads_owned(two_compute, NK + j, me)] =
+                if (load_owner(load_mode, NK + j) != me) continue;
+                stage[loads_owned(load_mode, NK + j, me)] =
                     gload16(rq, voff_k[j & 3], static_cast<uint32_t>(4 * j * qk_row * 2) + static_cast<uint32_t>(n) * kstep);
             }
         };
@@ -744,8 +757,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             unsigned char* dst = qst + (n & 1) * QSB + 16 * lane;
 #pragma unroll
             for (int j = 0; j < NQ; ++j) {
-                if (load_owner(two_compute, NK + j) != me) continue;
-                *reinterpret_cast<u32x4*>(dst + j * 1024) = stage[loads_owned(two_compute, NK + j, me)];
+                if (load_owner(load_mode, NK + j) != me) continue;
+                *reinterpret_cast<u32x4*>(dst + j * 1024) = stage[loads_owned(load_mode, NK + j, me)];
             }
         };
         // Iteration n: stores of the loads of iteration n - 2, then the loads of iteration
@@ -992,7 +1005,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const unsigned char* ks = kst + (n & 1) * KSB;
         const unsigned char* ts = ks + KB;
         const unsigned char* tls = ks + KB + TB;
-        const unsigned char* vs = ks + KB + TB + LB;
+        const unsigned char* vs = ks + KB + TB + LB + (dual ? 2048 * (wave & 1) : 0);   // this chain's V tile
         const float* gs = reinterpret_cast<const float*>(gst + (n % 4) * 1024);
         unsigned char* hb = hst + (n & 1) * HB;
 
@@ -1145,7 +1158,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         }
     };
     if constexpr (dual) {
-        if (wave == 0) chain(IntTag<0>{}, IntTag<1>{}, kInitIdentity, a.m_out);
+        if (wave < 2) chain(IntTag<0>{}, IntTag<1>{}, kInitIdentity, a.m_out);
         else chain(IntTag<1>{}, IntTag<0>{}, kInitZero, a.s_out);
     } else {
         chain(IntTag<kHasV ? 1 : 0>{}, IntTag<kSplit ? 1 : 0>{}, a.init_mode, a.s_out);
@@ -1171,7 +1184,10 @@ hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
-    int tiles = a.ncols / 16;
+    // workgroups per value head: one per 16-column tile, or per pair of tiles for M and S
+    // in one pass
+    int tiles = a.ncols / (a.pass == kPassMS ? 32 : 16);
+    if (a.pass == kPassMS && a.ncols % 32 != 0) return hipErrorInvalidValue;
     int qk_groups = a.Hqk * a.B * a.P;
     const unsigned nblk = static_cast<unsigned>(((qk_groups + 7) / 8) * 8 * (a.H / a.Hqk) * tiles);
     void* args[] = {const_cast<StateArgs*>(&a), &tiles, &qk_groups};
