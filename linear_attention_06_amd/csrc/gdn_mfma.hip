@@ -566,12 +566,15 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
 // waves 2 .. 7): waves 0 and 1 each share their SIMD with one loading wave (indices 2
 // and 3), which take two of every eight loads. Mode 2 (two tiles of both summaries: M
 // chains on waves 0 and 1, S chains on waves 2 and 3, loading waves 4 .. 7): the loading
-// waves beside the S chains (indices 2 and 3) take three of every four loads. Mode 0
+// waves beside the S chains (indices 2 and 3) take three of every four loads. Mode 3 (two
+// tiles with outputs: chain, output, chain, output on waves 0 .. 3, loading waves 4 .. 7,
+// one beside each): round-robin. Mode 0
 // (one chain wave, loading waves 1 .. 7): wave 0 shares its SIMD with loading wave 3.
 __host__ __device__ constexpr int load_owner(int mode, int g) {
     const int p = g & 7;
     if (mode == 1) return (p == 0 || p == 3) ? 2 : (p == 1 || p == 4) ? 3 : (p == 2) ? 0 : (p == 5) ? 1 : (p == 6) ? 4 : 5;
     if (mode == 2) return (p == 0) ? 0 : (p == 4) ? 1 : (p & 1) ? 2 : 3;
+    if (mode == 3) return p & 3;
     return p == 0 ? 3 : p - 1;
 }
 __host__ __device__ constexpr int loads_owned(int mode, int n, int me) {
@@ -580,9 +583,12 @@ __host__ __device__ constexpr int loads_owned(int mode, int n, int me) {
     return c;
 }
 
-template <bool kHasV, bool kSplit, bool kOut>
+template <bool kHasV, bool kSplit, bool kOut, bool kPair = false>
 __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk_groups) {
     constexpr bool outputs = kHasV && kOut;
+    // Two column tiles per workgroup with outputs (kPair): waves 0 and 2 run the chains of
+    // tiles 0 and 1, waves 1 and 3 their outputs; the four share the loaded operands.
+    constexpr bool pair = outputs && kPair;
     // Both summaries in one pass (values, split, no outputs) on two column tiles: waves 0
     // and 1 run the chains of the M tiles (split operands, no values, identity start,
     // written to a.m_out), waves 2 and 3 the chains of the S tiles (values, zero start,
@@ -590,8 +596,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     // its own. Requires ncols = dk; `tiles` counts pairs of column tiles.
     constexpr bool dual = kHasV && kSplit && !kOut;
     constexpr bool two_compute = outputs || dual;   // compute waves first, then loading waves
-    constexpr int load_mode = dual ? 2 : (outputs ? 1 : 0);
-    constexpr int vtiles = dual ? 2 : 1;   // column tiles of V per workgroup
+    constexpr int load_mode = dual ? 2 : (pair ? 3 : (outputs ? 1 : 0));
+    constexpr int vtiles = (dual || pair) ? 2 : 1;   // column tiles per workgroup
     // K-side stage buffer: K, That, That remainder (split), V; Q-side: Q, P.
     // K-side operands of chunk n are written in iteration n - 1 and read in iteration
     // n; Q-side operands in iteration n and read by the output wave, which runs one
@@ -605,7 +611,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     __shared__ __align__(16) unsigned char kst[2 * KSB];
     __shared__ __align__(16) unsigned char qst[outputs ? 2 * QSB : 16];
     __shared__ __align__(16) unsigned char gst[4 * 1024];
-    __shared__ __align__(16) unsigned char hst[outputs ? 2 * HB : 16];
+    __shared__ __align__(16) unsigned char hst[outputs ? 2 * HB * vtiles : 16];
     __shared__ __align__(16) unsigned char pf_s[outputs ? 256 : 16];   // sink of the L2 prefetches
 
     // XCD-aware block order (workgroups go round-robin over the 8 XCDs): every column
@@ -623,10 +629,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const int b = bz / a.P, seg = bz % a.P;
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
-    // the workgroup's first column; a chain wave's own tile (two per workgroup in the
-    // one-pass summary: waves w and w + 2 share tile w % 2)
+    // the workgroup's first column and a compute wave's own tile: in the one-pass summary
+    // waves w and w + 2 share tile w % 2, with outputs on two tiles waves 2 t and 2 t + 1
+    // work on tile t
+    const int sub = dual ? (wave & 1) : (pair ? ((wave >> 1) & 1) : 0);
     const int colp = 16 * vtiles * tile;
-    const int col0 = colp + (dual ? 16 * (wave & 1) : 0);
+    const int col0 = colp + 16 * sub;
     const int ncols = a.ncols;
     const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
     const int64_t nvalid = rs.valid;
@@ -642,7 +650,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * v_row * 2);
     const uint32_t ostep = static_cast<uint32_t>(kChunk * vo_row * 2);
-    const int first_loader = dual ? 4 : (two_compute ? 2 : 1);
+    const int first_loader = (dual || pair) ? 4 : (two_compute ? 2 : 1);
     // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
     // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 rho + j % 4)). A 1 KiB load fills one
     // quad block with 16 lanes per row, so that each group of 4 lanes reads one 64-byte piece
@@ -690,7 +698,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         for (int m = 0; m < 2 * vtiles; ++m)
             voff_v[m] = static_cast<uint32_t>(((32 * (m & 1) + (lane >> 1)) * v_row + h * ncols + colp + 16 * (m >> 1) +
                                                8 * (lane & 1)) * 2);
-        constexpr int nl = 8 - (dual ? 4 : (two_compute ? 2 : 1));
+        constexpr int nl = 8 - ((dual || pair) ? 4 : (two_compute ? 2 : 1));
         constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + NV + 1;
         constexpr int NQ = outputs ? 16 : 0;
         constexpr int NI = NK + NQ;   // 1 KiB loads of one full iteration
@@ -803,7 +811,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         return;
     }
 
-    if (outputs && wave == 1) {
+    if (outputs && (wave == 1 || (pair && wave == 3))) {
         // ---------------- output wave: chunk n - 1 during chunk n ----------------
         // stores past the row's extent (the tail of a packed sequence's last chunk) are
         // dropped by the descriptor's range
@@ -824,7 +832,9 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         bool pf_lane = true;    // this lane has a line to fetch
         {
             const int64_t bT = rs.start;
-            const int qk_share = rep * tiles, qk_rank = (kk % rep) * tiles + tile;
+            // (with two tiles per workgroup each output wave takes the share of one tile)
+            const int vt = vtiles * tile + sub, vts = vtiles * tiles;
+            const int qk_share = rep * vts, qk_rank = (kk % rep) * vts + vt;
             const int kq_lanes = min(32, (256 + qk_share - 1) / qk_share);
             if (lane < 32) {
                 const int lam = kq_lanes * qk_rank + lane;
@@ -834,21 +844,21 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 pf_base = reinterpret_cast<const unsigned char*>(src + bT * qk_row + hq * DK + 64 * (lam & 1));
                 pf_stride = qk_row * 2;
             } else if (lane < 48) {
-                const int lam = 16 * tile + lane - 32;
+                const int lam = 16 * vt + lane - 32;
                 const int c = (64 * (lam & 1) < ncols) ? 64 * (lam & 1) : 0;
                 pf_row = lam >> 1;
                 pf_base = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.v) + bT * v_row +
                                                                   h * ncols + c);
                 pf_stride = v_row * 2;
             } else if (lane < 60) {
-                const int lam = (12 * tile + lane - 48) % 96;
+                const int lam = (12 * vt + lane - 48) % 96;
                 const uint16_t* rec = static_cast<const uint16_t*>(lam < 48 ? a.ws.that : a.ws.pmat);
                 pf_base = reinterpret_cast<const unsigned char*>(rec + bh * a.NT * kTriRecord) + 128 * (lam % 48);
                 pf_stride = kTriRecord * 2;
             } else {
                 // the first 768 bytes of the 1 KiB decay record; even and odd tiles split them
                 pf_base = reinterpret_cast<const unsigned char*>(a.ws.gates + bh * a.NT * kGateRecordMfma) +
-                          128 * (lane - 60) + 384 * (tile & 1);
+                          128 * (lane - 60) + 384 * (vt & 1);
                 pf_stride = kGateRecordMfma * 4;
             }
         }
@@ -887,7 +897,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                                                                             static_cast<uint32_t>(i * 1024)));
         };
         auto compute = [&](int m, const PSet& pp) {   // outputs of chunk m
-            const unsigned char* hb = hst + (m & 1) * HB;
+            const unsigned char* hb = hst + (2 * sub + (m & 1)) * HB;
             const unsigned char* qs = qst + (m & 1) * QSB;
             const float* gs = reinterpret_cast<const float*>(gst + (m % 4) * 1024);
             bf16x8 sb[4], ub[2];
@@ -940,7 +950,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
-    if (wave != 0 && !dual) {
+    if (wave != 0 && !dual && !(pair && wave == 2)) {
         for (int n = n0; n <= n1; ++n) chunk_barrier(false);
         return;
     }
@@ -1005,9 +1015,9 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const unsigned char* ks = kst + (n & 1) * KSB;
         const unsigned char* ts = ks + KB;
         const unsigned char* tls = ks + KB + TB;
-        const unsigned char* vs = ks + KB + TB + LB + (dual ? 2048 * (wave & 1) : 0);   // this chain's V tile
+        const unsigned char* vs = ks + KB + TB + LB + 2048 * sub;   // this chain's V tile
         const float* gs = reinterpret_cast<const float*>(gst + (n % 4) * 1024);
-        unsigned char* hb = hst + (n & 1) * HB;
+        unsigned char* hb = hst + (2 * sub + (n & 1)) * HB;
 
         // State update of chunk n - 1 (S already holds exp(Gam_C) S): S += K^T V'', state
         // tiles t, token k-steps s (zero operands before the first chunk, which adds
@@ -1184,19 +1194,34 @@ hipError_t launch_prep_mfma(const PrepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_state_mfma(const StateArgs& a, hipStream_t s) {
-    // workgroups per value head: one per 16-column tile, or per pair of tiles for M and S
-    // in one pass
-    int tiles = a.ncols / (a.pass == kPassMS ? 32 : 16);
-    if (a.pass == kPassMS && a.ncols % 32 != 0) return hipErrorInvalidValue;
     int qk_groups = a.Hqk * a.B * a.P;
-    const unsigned nblk = static_cast<unsigned>(((qk_groups + 7) / 8) * 8 * (a.H / a.Hqk) * tiles);
+    const int64_t groups = static_cast<int64_t>((qk_groups + 7) / 8) * 8 * (a.H / a.Hqk);
+    // Workgroups per value head: one per 16-column tile, or per pair of tiles for M and S
+    // in one pass. With outputs, pairs of tiles share their loads when one-tile
+    // workgroups would take at least two rounds of the compute units (one workgroup runs
+    // per unit): a pair's chunk costs well under two tiles' chunks.
+    bool paired = false;
+    if (a.pass == kPassOutputs && a.ncols % 32 == 0) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        paired = cus > 0 && groups * (a.ncols / 16) >= 2 * static_cast<int64_t>(cus);
+    }
+    int tiles = a.ncols / ((a.pass == kPassMS || paired) ? 32 : 16);
+    if (a.pass == kPassMS && a.ncols % 32 != 0) return hipErrorInvalidValue;
+    const unsigned nblk = static_cast<unsigned>(groups * tiles);
     void* args[] = {const_cast<StateArgs*>(&a), &tiles, &qk_groups};
     // The summary matrix M runs without values and with split operands; M and S together
     // in one pass share the loads. The caller names the pass (an empty tensor's pointer
     // may be NULL, so the pointers do not tell).
     const void* fn = nullptr;
     switch (a.pass) {
-        case kPassOutputs: fn = reinterpret_cast<const void*>(&state_mfma<true, false, true>); break;
+        case kPassOutputs:
+            fn = paired ? reinterpret_cast<const void*>(&state_mfma<true, false, true, true>)
+                        : reinterpret_cast<const void*>(&state_mfma<true, false, true>);
+            break;
         case kPassS: fn = reinterpret_cast<const void*>(&state_mfma<true, false, false>); break;
         case kPassM: fn = reinterpret_cast<const void*>(&state_mfma<false, true, false>); break;
         case kPassMS: fn = reinterpret_cast<const void*>(&state_mfma<true, true, false>); break;
