@@ -351,9 +351,11 @@ gdn_status gdn_apply_initial_state(const gdn_problem* p, int32_t seg_len,
  *   3. gdn_segment_summary_bwd with accumulate = 1: adds the summaries' share, through
  *      dM and dS, to the inputs' gradients of step 1.
  * All gradients are fp32 with the layouts of their forward tensors (dq, dk [B,T,Hqk,dk];
- * dv [B,T,H,dv]; dg, dbeta [B,T,H]; dH_in, dS [B,H,P,dk,dv]; dM [B,H,P,dk,dk]). These run
- * the fp32 vector-ALU backward (the kernels of gdn_chunk_bwd) on every segment as its own
- * sequence. Padded tokens (valid_len) get zero gradients. seg_len as gdn_segment_summary.
+ * dv [B,T,H,dv]; dg, dbeta [B,T,H]; dH_in, dS [B,H,P,dk,dv]; dM [B,H,P,dk,dk]). Each segment
+ * runs as a sequence of its own through gdn_chunk_bwd's kernels: the chunked matrix-core
+ * backward for bf16 heads of 128 (gradients within the bf16 bound of issue #320 section
+ * 4.2), the fp32 vector-ALU backward otherwise. Padded tokens (valid_len) get zero
+ * gradients. seg_len as gdn_segment_summary.
  *
  * Workspace of the two backward calls that take one, in bytes (contents undefined on entry).
  */

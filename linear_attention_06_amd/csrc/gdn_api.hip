@@ -455,29 +455,35 @@ gdn::BwdRecords bwd_records(const BwdMfmaPlan& pl, void* ws) {
     return rec;
 }
 
-// The prepare pass with the backward's records and the forward state pass keeping the state
-// entering every chunk; with outputs (o non-NULL) the state pass also writes o and hT.
-gdn_status run_fwd_keep(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const void* v,
-                        const float* g, const float* beta, const float* h0, void* o, float* hT, void* ws,
-                        hipStream_t s) {
+// The prepare pass with the backward's records (and the forward's P record when the
+// forward's outputs are wanted too).
+gdn_status run_prep_keep(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const float* g,
+                         const float* beta, bool keep_pmat, void* ws, hipStream_t s) {
     if (pl.fwd.nch == 0) return GDN_OK;
-    char* base = static_cast<char*>(ws);
-    const gdn::Workspace w = carve(pl.fwd, ws);
     gdn::PrepArgs pa;
     pa.B = p.B; pa.T = p.T; pa.H = p.H; pa.Hqk = p.Hqk; pa.dk = p.dk; pa.NT = static_cast<int>(pl.fwd.NT);
-    pa.q = q; pa.k = k; pa.g = g; pa.beta = beta; pa.valid_len = p.valid_len; pa.cu_seqlens = nullptr; pa.ws = w;
+    pa.q = q; pa.k = k; pa.g = g; pa.beta = beta; pa.valid_len = p.valid_len; pa.cu_seqlens = nullptr;
+    pa.ws = carve(pl.fwd, ws);
     pa.qk_stride = static_cast<int64_t>(p.Hqk) * p.dk;
     pa.has_prologue = 0;
     pa.pro = gdn::Prologue{nullptr, nullptr, nullptr, nullptr, 1.f};
     pa.has_conv = 0;
     pa.conv = gdn::PrepConv{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
     pa.bwd = bwd_records(pl, ws);
-    pa.bwd.keep_pmat = o ? 1 : 0;
+    pa.bwd.keep_pmat = keep_pmat ? 1 : 0;
     hipError_t e = gdn::launch_prep_mfma(pa, s);
-    if (e != hipSuccess) return hip_fail(e, "prepare kernel launch");
-    gdn::StateArgs sa = state_args(p, pl.fwd, q, k, v, w);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "prepare kernel launch");
+}
+
+// The forward state pass keeping the state entering every chunk, from h0 (init_mode) and
+// values v (NULL: zero values); with outputs (o non-NULL) it also writes o and hT.
+gdn_status run_state_keep(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const void* v,
+                          int init_mode, const float* h0, void* o, float* hT, void* ws, hipStream_t s) {
+    if (pl.fwd.nch == 0) return GDN_OK;
+    char* base = static_cast<char*>(ws);
+    gdn::StateArgs sa = state_args(p, pl.fwd, q, k, v, carve(pl.fwd, ws));
     sa.pass = o ? gdn::kPassOutputs : gdn::kPassS;
-    sa.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+    sa.init_mode = init_mode;
     sa.s_init = h0;
     sa.o = o;
     sa.s_out = hT;
@@ -486,11 +492,23 @@ gdn_status run_fwd_keep(const gdn_problem& p, const BwdMfmaPlan& pl, const void*
     return run_state(p, sa, s);
 }
 
+// The prepare pass with the backward's records and the forward state pass keeping the state
+// entering every chunk; with outputs (o non-NULL) the state pass also writes o and hT.
+gdn_status run_fwd_keep(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k, const void* v,
+                        const float* g, const float* beta, const float* h0, void* o, float* hT, void* ws,
+                        hipStream_t s) {
+    gdn_status st = run_prep_keep(p, pl, q, k, g, beta, o != nullptr, ws, s);
+    if (st != GDN_OK) return st;
+    return run_state_keep(p, pl, q, k, v, h0 ? gdn::kInitLoad : gdn::kInitZero, h0, o, hT, ws, s);
+}
+
 // The reverse chain and the gradient pass on a workspace that holds the records and states.
+// v or d_o NULL: zero values / output gradient; dv NULL: not written; accumulate: the
+// gradients are added to what dq, dk, dv, dg and dbeta hold.
 gdn_status run_bwd_from_saved(const gdn_problem& p, const BwdMfmaPlan& pl, const void* q, const void* k,
                               const void* v, const float* g, const float* beta, const void* d_o, const float* dhT,
                               float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws,
-                              hipStream_t s) {
+                              hipStream_t s, bool accumulate = false) {
     char* base = static_cast<char*>(ws);
     gdn::BwdMfmaArgs a;
     a.B = p.B; a.T = p.T; a.H = p.H; a.Hqk = p.Hqk; a.NT = static_cast<int>(pl.fwd.NT);
@@ -499,6 +517,7 @@ gdn_status run_bwd_from_saved(const gdn_problem& p, const BwdMfmaPlan& pl, const
     a.states = base + pl.states_off;
     a.dstates = base + pl.dstates_off;
     a.dq_out = dq; a.dk_out = dk; a.dv_out = dv; a.dg_out = dg; a.dbeta_out = dbeta; a.dh0_out = dh0;
+    a.accumulate = accumulate ? 1 : 0;
     hipError_t e = gdn::launch_bwd_state_mfma(a, s);
     if (e != hipSuccess) return hip_fail(e, "backward state kernel launch");
     e = gdn::launch_bwd_grad_mfma(a, s);
@@ -511,6 +530,60 @@ gdn_status run_bwd_mfma(const gdn_problem& p, const BwdMfmaPlan& pl, const void*
     gdn_status st = run_fwd_keep(p, pl, q, k, v, g, beta, h0, nullptr, nullptr, ws, s);
     if (st != GDN_OK) return st;
     return run_bwd_from_saved(p, pl, q, k, v, g, beta, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws, s);
+}
+
+// The backward through the segment calls on the matrix cores: the P segments of each of the
+// B rows run as B * P rows of their own (the token-major tensors [B, T, ...] are
+// [B * P, L, ...] as they lie), each from its own incoming state; the state blocks move
+// between the segment calls' [B, H, P, D, D] and the rows' [B * P, H, D, D] layouts in the
+// workspace, behind the chunked backward's own records.
+struct SegBwdMfmaPlan {
+    gdn_problem rows;
+    BwdMfmaPlan bwd;
+    size_t h0_off = 0, dhT_off = 0, dh0_off = 0, vl_off = 0, bytes = 0;
+};
+
+SegBwdMfmaPlan make_seg_bwd_mfma_plan(const gdn_problem& p, int64_t P, int32_t L) {
+    SegBwdMfmaPlan sp;
+    sp.rows = p;
+    sp.rows.B = static_cast<int32_t>(p.B * P);
+    sp.rows.T = L;
+    sp.rows.valid_len = nullptr;
+    sp.bwd = make_bwd_mfma_plan(sp.rows);
+    const size_t blocks = align256(static_cast<size_t>(p.B) * P * p.H * p.dk * p.dv * 4);
+    sp.h0_off = align256(sp.bwd.bytes);
+    sp.dhT_off = sp.h0_off + blocks;
+    sp.dh0_off = sp.dhT_off + blocks;
+    sp.vl_off = sp.dh0_off + blocks;
+    sp.bytes = sp.vl_off + align256(static_cast<size_t>(p.B) * P * 4);
+    return sp;
+}
+
+bool use_seg_bwd_mfma(const gdn_problem& p, int64_t P, int32_t L) {
+    if (!use_bwd_mfma(p) || P == 0 || p.B * P > 65535) return false;
+    gdn_problem rows = p;
+    rows.B = static_cast<int32_t>(p.B * P);
+    rows.T = L;
+    return use_bwd_mfma(rows);
+}
+
+// The rows' problem with their valid tokens (from the padded rows' valid_len) in ws.
+gdn_problem seg_rows(const SegBwdMfmaPlan& sp, const gdn_problem& p, int64_t P, int32_t L, void* ws, hipStream_t s,
+                     hipError_t* e) {
+    gdn_problem rows = sp.rows;
+    *e = hipSuccess;
+    if (p.valid_len) {
+        int32_t* vl = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + sp.vl_off);
+        *e = gdn::launch_seg_valid_len(p.valid_len, p.B, static_cast<int>(P), L, p.T, vl, s);
+        rows.valid_len = vl;
+    }
+    return rows;
+}
+
+hipError_t seg_blocks(const gdn_problem& p, int64_t P, const float* src, float* dst, bool to_rows, bool last_only,
+                      hipStream_t s) {
+    gdn::SegBlocksArgs a{p.B, p.H, static_cast<int>(P), p.dk, src, dst, to_rows ? 1 : 0, last_only ? 1 : 0};
+    return gdn::launch_seg_state_blocks(a, s);
 }
 
 gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
@@ -620,7 +693,8 @@ gdn_status gdn_segment_bwd_workspace(const gdn_problem* p, int32_t seg_len, size
     st = check_segments(*p, seg_len, &P);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
-    *bytes = make_bwd_plan(*p, p->dv > p->dk ? p->dv : p->dk, seg_len).bytes;
+    *bytes = use_seg_bwd_mfma(*p, P, seg_len) ? make_seg_bwd_mfma_plan(*p, P, seg_len).bytes
+                                              : make_bwd_plan(*p, p->dv > p->dk ? p->dv : p->dk, seg_len).bytes;
     return GDN_OK;
 }
 
@@ -638,6 +712,31 @@ gdn_status gdn_apply_initial_state_bwd(const gdn_problem* p, int32_t seg_len, co
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !H_in || !d_o || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, H_in, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (use_seg_bwd_mfma(*p, P, seg_len)) {
+            // every segment as a row of its own, from its incoming state, through the chunked
+            // matrix-core backward; the final-state gradient enters the last segment of a row
+            const SegBwdMfmaPlan sp = make_seg_bwd_mfma_plan(*p, P, seg_len);
+            Plan need;
+            need.bytes = sp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            if (!tokens) return GDN_OK;
+            hipStream_t s = static_cast<hipStream_t>(stream);
+            char* base = static_cast<char*>(ws);
+            float* h0r = reinterpret_cast<float*>(base + sp.h0_off);
+            float* dhTr = reinterpret_cast<float*>(base + sp.dhT_off);
+            float* dh0r = reinterpret_cast<float*>(base + sp.dh0_off);
+            hipError_t e;
+            const gdn_problem rows = seg_rows(sp, *p, P, seg_len, ws, s, &e);
+            if (e == hipSuccess) e = seg_blocks(*p, P, H_in, h0r, true, false, s);
+            if (e == hipSuccess) e = seg_blocks(*p, P, dhT, dhTr, true, true, s);
+            if (e != hipSuccess) return hip_fail(e, "segment state layout kernel launch");
+            st = run_bwd_mfma(rows, sp.bwd, q, k, v, g, beta, h0r, d_o, dhTr, dq, dk, dv, dg, dbeta,
+                              dH_in ? dh0r : nullptr, ws, s);
+            if (st != GDN_OK || !dH_in) return st;
+            e = seg_blocks(*p, P, dh0r, dH_in, false, false, s);
+            return e == hipSuccess ? GDN_OK : hip_fail(e, "segment state layout kernel launch");
+        }
         const BwdPlan pl = make_bwd_plan(*p, p->dv > p->dk ? p->dv : p->dk, seg_len);
         st = check_bwd_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
@@ -686,6 +785,43 @@ gdn_status gdn_segment_summary_bwd(const gdn_problem* p, int32_t seg_len, const 
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (use_seg_bwd_mfma(*p, P, seg_len)) {
+            // every segment as a row of its own through the chunked matrix-core backward, the
+            // chunk records prepared once: S from a zero state with values, M from the
+            // identity without values (its value gradient dropped), neither with outputs
+            const SegBwdMfmaPlan sp = make_seg_bwd_mfma_plan(*p, P, seg_len);
+            Plan need;
+            need.bytes = sp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            if (!tokens) return GDN_OK;
+            hipStream_t s = static_cast<hipStream_t>(stream);
+            float* dhTr = reinterpret_cast<float*>(static_cast<char*>(ws) + sp.dhT_off);
+            hipError_t e;
+            const gdn_problem rows = seg_rows(sp, *p, P, seg_len, ws, s, &e);
+            if (e != hipSuccess) return hip_fail(e, "segment valid-length kernel launch");
+            st = run_prep_keep(rows, sp.bwd, q, k, g, beta, false, ws, s);
+            if (st != GDN_OK) return st;
+            if (dS || !accumulate) {
+                e = seg_blocks(*p, P, dS, dhTr, true, false, s);
+                if (e != hipSuccess) return hip_fail(e, "segment state layout kernel launch");
+                st = run_state_keep(rows, sp.bwd, q, k, v, gdn::kInitZero, nullptr, nullptr, nullptr, ws, s);
+                if (st == GDN_OK)
+                    st = run_bwd_from_saved(rows, sp.bwd, q, k, v, g, beta, nullptr, dhTr, dq, dk, dv, dg, dbeta, nullptr,
+                                            ws, s, accumulate != 0);
+                if (st != GDN_OK) return st;
+            }
+            if (dM) {
+                e = seg_blocks(*p, P, dM, dhTr, true, false, s);
+                if (e != hipSuccess) return hip_fail(e, "segment state layout kernel launch");
+                st = run_state_keep(rows, sp.bwd, q, k, nullptr, gdn::kInitIdentity, nullptr, nullptr, nullptr, ws, s);
+                if (st == GDN_OK)
+                    st = run_bwd_from_saved(rows, sp.bwd, q, k, nullptr, g, beta, nullptr, dhTr, dq, dk, nullptr, dg, dbeta,
+                                            nullptr, ws, s, true);
+                if (st != GDN_OK) return st;
+            }
+            return GDN_OK;
+        }
         const BwdPlan pl = make_bwd_plan(*p, p->dv > p->dk ? p->dv : p->dk, seg_len);
         st = check_bwd_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;

@@ -159,10 +159,11 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
         // ---------------- loading waves ----------------
         const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rs.start * qk_row;
         const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rs.start * qk_row;
-        const uint16_t* din = static_cast<const uint16_t*>(a.d_o) + rs.start * v_row;
+        // a NULL output gradient is zero: its descriptor holds no records, so its loads read 0
+        const uint16_t* din = static_cast<const uint16_t*>(a.d_o ? a.d_o : a.k) + rs.start * v_row;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin, nvalid * qk_row * 2);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qin, nvalid * qk_row * 2);
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc(din, nvalid * v_row * 2);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(din, a.d_o ? nvalid * v_row * 2 : 0);
         const int64_t rec = static_cast<int64_t>(NT) * kTriRecord * 2;
         const __amdgpu_buffer_rsrc_t rtt = make_rsrc(static_cast<const uint16_t*>(a.rec.thatT) + bh * NT * kTriRecord, rec);
         const __amdgpu_buffer_rsrc_t rpt = make_rsrc(static_cast<const uint16_t*>(a.rec.pT) + bh * NT * kTriRecord, rec);
@@ -277,8 +278,9 @@ __global__ __launch_bounds__(512) void bwd_state_mfma(BwdMfmaArgs a, int qk_grou
                 pf_stride = qk_row * 2;
             } else if (lane < 32) {
                 const int lam = 16 * tile + lane - 16;
+                pf_lane = a.d_o != nullptr;
                 pf_row = lam >> 1;
-                pf_base = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.d_o) + bT * v_row +
+                pf_base = reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(a.d_o ? a.d_o : a.k) + bT * v_row +
                                                                   h * DK + 64 * (lam & 1));
                 pf_stride = v_row * 2;
             } else if (lane < 45) {
@@ -605,7 +607,7 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
         } else if (L < 384) {
             const int64_t t = min(t0 + r, static_cast<int64_t>(a.T) - 1);
             const uint16_t* base = static_cast<const uint16_t*>(L < 320 ? a.v : a.d_o);
-            pf_line(base + (rs.start + t) * v_row + hh * DK + 64 * pp);
+            if (base) pf_line(base + (rs.start + t) * v_row + hh * DK + 64 * pp);
         }
     };
 
@@ -672,8 +674,11 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                         sdot += __uint_as_float(s1[e] << 16) * __uint_as_float(s2[e] << 16) +
                                 __uint_as_float(s1[e] & 0xFFFF0000u) * __uint_as_float(s2[e] & 0xFFFF0000u);
                 }
-                const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(a.v) + rs.start * v_row, nvalid * v_row * 2);
-                const __amdgpu_buffer_rsrc_t rd = make_rsrc(static_cast<const uint16_t*>(a.d_o) + rs.start * v_row, nvalid * v_row * 2);
+                // NULL values or output gradient read as zero (descriptors without records)
+                const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(a.v ? a.v : a.k) + rs.start * v_row,
+                                                            a.v ? nvalid * v_row * 2 : 0);
+                const __amdgpu_buffer_rsrc_t rd = make_rsrc(static_cast<const uint16_t*>(a.d_o ? a.d_o : a.k) + rs.start * v_row,
+                                                            a.d_o ? nvalid * v_row * 2 : 0);
                 {
                     const int row = tid >> 3, gr = tid & 7;
                     const uint32_t off = static_cast<uint32_t>(((t0 + row) * v_row + h * DK + 64 * pn + 8 * gr) * 2);
@@ -778,14 +783,18 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             }
             chunk_barrier(false);
             // the panel's dv, whole rows of 64 columns (zero past the valid tokens)
+            if (a.dv_out) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int p = tid + 512 * u, row = p >> 4, q4 = p & 15;
-                const int64_t t = t0 + row;
-                if (t < a.T) {
-                    const f32x4 x = t < nvalid ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(sm + G_DV) + row * G_DVP + 4 * q4)
-                                               : zero4();
-                    *reinterpret_cast<f32x4*>(a.dv_out + (rs.start + t) * v_row + h * DK + 64 * pn + 4 * q4) = x;
+                for (int u = 0; u < 2; ++u) {
+                    const int p = tid + 512 * u, row = p >> 4, q4 = p & 15;
+                    const int64_t t = t0 + row;
+                    if (t < a.T) {
+                        f32x4 x = t < nvalid ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(sm + G_DV) + row * G_DVP + 4 * q4)
+                                             : zero4();
+                        f32x4* out = reinterpret_cast<f32x4*>(a.dv_out + (rs.start + t) * v_row + h * DK + 64 * pn + 4 * q4);
+                        if (a.accumulate) x += *out;
+                        *out = x;
+                    }
                 }
             }
             // ---- C ----
@@ -1012,8 +1021,10 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             const int64_t t = t0 + lane;
             if (t < a.T) {
                 const bool valid = t < nvalid;
-                a.dg_out[(rs.start + t) * a.H + h] = valid ? dg : 0.f;
-                a.dbeta_out[(rs.start + t) * a.H + h] = valid ? db : 0.f;
+                const int64_t o = (rs.start + t) * a.H + h;
+                const float base_g = a.accumulate ? a.dg_out[o] : 0.f, base_b = a.accumulate ? a.dbeta_out[o] : 0.f;
+                a.dg_out[o] = base_g + (valid ? dg : 0.f);
+                a.dbeta_out[o] = base_b + (valid ? db : 0.f);
             }
         }
         chunk_barrier(false);
@@ -1067,14 +1078,75 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
         if (t < a.T) {
             const bool valid = t < nvalid;
             const int64_t o = ((rs.start + t) * a.Hqk + hq) * DK + 16 * m + 4 * g4;
-            *reinterpret_cast<f32x4*>(a.dq_out + o) = valid ? dq_acc[r] : zero4();
-            *reinterpret_cast<f32x4*>(a.dk_out + o) = valid ? dk_acc[r] : zero4();
+            f32x4 xq = valid ? dq_acc[r] : zero4(), xk = valid ? dk_acc[r] : zero4();
+            if (a.accumulate) {
+                xq += *reinterpret_cast<const f32x4*>(a.dq_out + o);
+                xk += *reinterpret_cast<const f32x4*>(a.dk_out + o);
+            }
+            *reinterpret_cast<f32x4*>(a.dq_out + o) = xq;
+            *reinterpret_cast<f32x4*>(a.dk_out + o) = xk;
         }
     }
     __builtin_amdgcn_s_waitcnt(0);   // every prefetch has landed in the sink
 }
 
+// Segments of B rows as rows of their own. State blocks (D x D fp32, 16 KiB at D = 128)
+// move between the segment-major layout [B, H, P, D, D] of the segment calls and the
+// row-major layout [B * P, H, D, D] of the backward on segments as rows: dst block
+// (b P + p, h) is src block (b, h, p) (to_rows), or the reverse. src NULL gives zero
+// blocks. With last_only, src is [B, H, D, D] and lands at p = P - 1, the other blocks zero.
+__global__ __launch_bounds__(256) void seg_state_blocks(SegBlocksArgs a) {
+    const int64_t n4 = static_cast<int64_t>(a.B) * a.P * a.H * a.D * a.D / 4;
+    const int64_t blk4 = static_cast<int64_t>(a.D) * a.D / 4;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t blk = i / blk4, e = i % blk4;
+        // blk in the row-major order: (b P + p) H + h
+        const int h = static_cast<int>(blk % a.H);
+        const int64_t bp = blk / a.H;
+        const int p = static_cast<int>(bp % a.P), b = static_cast<int>(bp / a.P);
+        const int64_t seg_blk = (static_cast<int64_t>(b) * a.H + h) * a.P + p;
+        if (a.to_rows) {
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (a.src) {
+                if (!a.last_only) x = reinterpret_cast<const float4*>(a.src)[seg_blk * blk4 + e];
+                else if (p == a.P - 1) x = reinterpret_cast<const float4*>(a.src)[(static_cast<int64_t>(b) * a.H + h) * blk4 + e];
+            }
+            reinterpret_cast<float4*>(a.dst)[blk * blk4 + e] = x;
+        } else {
+            reinterpret_cast<float4*>(a.dst)[seg_blk * blk4 + e] = reinterpret_cast<const float4*>(a.src)[blk * blk4 + e];
+        }
+    }
+}
+
+// Valid tokens of every segment as a row: clamp(valid_len[b] - p L, 0, L).
+__global__ __launch_bounds__(256) void seg_valid_len(const int32_t* vl, int B, int P, int L, int T, int32_t* out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= B * P) return;
+    const int b = i / P, p = i % P;
+    int n = vl[b];
+    n = n < 0 ? 0 : (n > T ? T : n);
+    n -= p * L;
+    out[i] = n < 0 ? 0 : (n > L ? L : n);
+}
+
 }  // namespace
+
+hipError_t launch_seg_state_blocks(const SegBlocksArgs& a, hipStream_t s) {
+    const int64_t n4 = static_cast<int64_t>(a.B) * a.P * a.H * a.D * a.D / 4;
+    if (n4 == 0) return hipSuccess;
+    const int64_t nblk = (n4 + 255) / 256;
+    const unsigned grid = static_cast<unsigned>(nblk < 4096 ? nblk : 4096);
+    void* args[] = {const_cast<SegBlocksArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&seg_state_blocks), dim3(grid), dim3(256), args, 0, s);
+}
+
+hipError_t launch_seg_valid_len(const int32_t* vl, int B, int P, int L, int T, int32_t* out, hipStream_t s) {
+    const int n = B * P;
+    if (n == 0) return hipSuccess;
+    void* args[] = {const_cast<int32_t**>(&vl), &B, &P, &L, &T, &out};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&seg_valid_len), dim3((n + 255) / 256), dim3(256), args, 0, s);
+}
 
 hipError_t launch_bwd_state_mfma(const BwdMfmaArgs& a, hipStream_t s) {
     int qk_groups = a.B * a.Hqk;

@@ -242,7 +242,22 @@ struct BwdMfmaArgs {
     float* dg_out;            // [B,T,H]
     float* dbeta_out;
     float* dh0_out;           // [B,H,128,128] or NULL
+    // v or d_o NULL: zero values / output gradient; dv_out NULL: dv not written;
+    // accumulate: dq, dk, dv, dg, dbeta added to what the buffers hold
+    int accumulate = 0;
 };
+
+// State blocks between the segment calls' layout [B, H, P, D, D] and segments as rows
+// [B * P, H, D, D] (gdn_bwd_mfma.hip).
+struct SegBlocksArgs {
+    int B, H, P, D;
+    const float* src;   // NULL: zero blocks (to_rows)
+    float* dst;
+    int to_rows;        // 1: segment-major to row-major; 0: back
+    int last_only;      // to_rows with src [B, H, D, D] placed at the last segment
+};
+hipError_t launch_seg_state_blocks(const SegBlocksArgs& a, hipStream_t s);
+hipError_t launch_seg_valid_len(const int32_t* vl, int B, int P, int L, int T, int32_t* out, hipStream_t s);
 
 // Layer steps around the core (gdn_layer_ops.hip).
 struct ConvArgs {

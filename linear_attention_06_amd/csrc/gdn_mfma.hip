@@ -672,10 +672,11 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         // out-of-range tokens load as zero
         const uint16_t* kin = static_cast<const uint16_t*>(a.k) + rs.start * qk_row;
         const uint16_t* qin = static_cast<const uint16_t*>(a.q) + rs.start * qk_row;
-        const uint16_t* vin = static_cast<const uint16_t*>(a.v) + rs.start * v_row;
+        const uint16_t* vin = static_cast<const uint16_t*>(a.v ? a.v : a.k) + rs.start * v_row;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kin, nvalid * qk_row * 2);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(outputs ? qin : kin, nvalid * qk_row * 2);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(kHasV ? vin : kin, kHasV ? nvalid * v_row * 2 : 0);
+        // NULL values (the homogeneous chain's backward) read as zero: no records
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc((kHasV && a.v) ? vin : kin, (kHasV && a.v) ? nvalid * v_row * 2 : 0);
         const int64_t rec = static_cast<int64_t>(a.NT) * kTriRecord * 2;   // bytes of one head's records
         const __amdgpu_buffer_rsrc_t rth = make_rsrc(static_cast<const uint16_t*>(a.ws.that) + bh * a.NT * kTriRecord, rec);
         const __amdgpu_buffer_rsrc_t rtl = make_rsrc(

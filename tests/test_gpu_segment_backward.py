@@ -48,6 +48,14 @@ CASES = [
 ]
 
 
+def call_tol(case):
+    """The apply and summary backward of bf16 heads of 128 run the chunked matrix-core backward
+    (bf16 operands, fp32 accumulation): the pages' bf16 bound on gradients (issue #320,
+    section 4.2). Every other shape runs fp32 arithmetic: 1e-4. The combine is fp32 always."""
+    _, io, dk, dv = case[:4]
+    return TOL_BF16 if (io == "bf16" and dk == 128 and dv == 128) else TOL_F32
+
+
 def case_inputs(case, seed):
     name, io, dk, dv, B, T, Hqk, H, L, valid = case
     w = dataclasses.replace(slow_decay(WORKLOADS["stateful_32k"], seed=seed, seg_len=L), name="segbwd_" + name, B=B,
@@ -74,8 +82,9 @@ def test_each_backward_call_matches_the_oracle(case):
     got = gdn.gdn_apply_initial_state_bwd(q, k, v, g, beta, H_in, L, d_o_t, torch.from_numpy(dhT).to(dev()), vl)
     sync()
     ref = sb.apply_initial_state_bwd(qf, kf, vf, gf, bf, Hf, L, d_o, dhT.astype(np.float64), inp.valid_len)
+    tol = call_tol(case)
     for nm, x, r in zip(NAMES + ("dH_in",), got, ref):
-        check(x, r, TOL_F32, case[0] + " apply " + nm)
+        check(x, r, tol, case[0] + " apply " + nm)
     dH_in = got[5]
     # 2. combine
     dM, dS, dh0 = gdn.gdn_summary_combine_bwd(M, H_in, dH_in)
@@ -89,7 +98,7 @@ def test_each_backward_call_matches_the_oracle(case):
     ref = sb.segment_summary_bwd(qf, kf, vf, gf, bf, L, np_f64(dM), np_f64(dS), inp.valid_len)
     assert int(torch.count_nonzero(got[0])) == 0, "the summaries do not read q"
     for nm, x, r in zip(NAMES[1:], got[1:], ref[1:]):
-        check(x, r, TOL_F32, case[0] + " summary " + nm)
+        check(x, r, tol, case[0] + " summary " + nm)
     if inp.valid_len is not None:
         for b in range(inp.w.B):
             n = int(inp.valid_len[b])
@@ -101,10 +110,9 @@ def test_each_backward_call_matches_the_oracle(case):
 def test_composed_segment_backward_equals_the_unsplit_backward(case):
     """apply_bwd, then combine_bwd, then summary_bwd accumulating onto apply's gradients:
     the gradient of the unsplit forward (fp64 oracle and gdn_chunk_bwd), the summaries'
-    share nonzero (slow decay keeps the carried state's weight large). Each backward call
-    is fp32 (checked at 1e-4 above), but the incoming states H_in it starts from come out
-    of the bf16 matrix-core summaries, so on bf16 inputs the composition carries their
-    error: the bf16 bound applies."""
+    share nonzero (slow decay keeps the carried state's weight large). On bf16 heads of 128
+    the backward calls run the matrix-core backward and the incoming states H_in come out
+    of the bf16 matrix-core summaries: the bf16 bound applies; fp32 shapes stay at 1e-4."""
     L = case[8]
     inp = case_inputs(case, 710)
     q, k, v, g, beta, h0, vl = to_dev(inp)
