@@ -261,8 +261,8 @@ def prologue_timing(gdn, inp, dev, stream, timed):
 def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
     """gdn_chunk_bwd (all six gradients; the chunked matrix-core backward on these bf16
     heads of 128) on the stateless 8K workload with a seeded output gradient, beside the
-    forward on the same inputs, the fp32 token-level backward of the same problem (the
-    one-segment apply backward) and the stateful 32K workload; the per-kernel split is in
+    forward on the same inputs, the training step with the forward kept, the same gradients
+    through the segment calls and the stateful 32K workload; the per-kernel split is in
     profiles/."""
     import torch
 
@@ -309,17 +309,6 @@ def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
                             "bwd_saved_ratio_to_forward": ms_bwd_saved / ms_fwd,
                             "fwd_plus_bwd_ms": ms_fwd + ms}}
 
-    # the fp32 token-level backward of the same problem (one segment from a zero state)
-    H_in = torch.zeros((w.B, w.H, 1, w.dk, w.dv), device=dev)
-    tws = gdn.workspace(gdn.gdn_segment_bwd_workspace(p, w.T), dev)
-
-    def token_step():
-        gdn.gdn_apply_initial_state_bwd(q, k, v, g, beta, H_in, w.T, d_o, ws=tws, stream=stream)
-
-    out["token_level_fp32_ms"] = timed(token_step, 2)
-    out["token_level_workspace_bytes"] = int(tws.numel())
-    del tws
-
     # the same gradients through the segment calls (4 segments of 2048): apply's backward,
     # the combine's, then the summaries' accumulated onto apply's
     L = 2048
@@ -334,7 +323,8 @@ def backward_timing(gdn, workloads, make_inputs, dev, stream, timed):
 
     ms_seg = timed(seg_step, 2)
     out["segments_4x2048"] = {"ms_per_step": ms_seg, "workspace_bytes": int(bws.numel()),
-                              "note": "apply, combine and summary backward composed (fp32 token level)"}
+                              "note": "apply, combine and summary backward composed, each segment a row "
+                                      "of the matrix-core backward"}
     del bws, ws, fws
 
     # the stateful 32K workload (initial state, 32 heads of 128)
