@@ -568,13 +568,16 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
 // chains on waves 0 and 1, S chains on waves 2 and 3, loading waves 4 .. 7): the loading
 // waves beside the S chains (indices 2 and 3) take three of every four loads. Mode 3 (two
 // tiles with outputs: chain, output, chain, output on waves 0 .. 3, loading waves 4 .. 7,
-// one beside each): round-robin. Mode 0
+// one beside each): round-robin. Mode 4 (one tile with outputs split over two waves: chain,
+// output, output on waves 0 .. 2, loading waves 3 .. 7): the two loading waves of the SIMD
+// without a compute wave (indices 0 and 4) take five of every eight loads. Mode 0
 // (one chain wave, loading waves 1 .. 7): wave 0 shares its SIMD with loading wave 3.
 __host__ __device__ constexpr int load_owner(int mode, int g) {
     const int p = g & 7;
     if (mode == 1) return (p == 0 || p == 3) ? 2 : (p == 1 || p == 4) ? 3 : (p == 2) ? 0 : (p == 5) ? 1 : (p == 6) ? 4 : 5;
     if (mode == 2) return (p == 0) ? 0 : (p == 4) ? 1 : (p & 1) ? 2 : 3;
     if (mode == 3) return p & 3;
+    if (mode == 4) return (p == 0 || p == 2 || p == 7) ? 0 : (p == 1 || p == 3) ? 4 : p - 3;
     return p == 0 ? 3 : p - 1;
 }
 __host__ __device__ constexpr int loads_owned(int mode, int n, int me) {
@@ -589,6 +592,9 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     // Two column tiles per workgroup with outputs (kPair): waves 0 and 2 run the chains of
     // tiles 0 and 1, waves 1 and 3 their outputs; the four share the loaded operands.
     constexpr bool pair = outputs && kPair;
+    // One tile with outputs: the outputs of a chunk's four 16-token tiles are split over
+    // waves 1 (tiles 0 and 3) and 2 (tiles 1 and 2), halving each wave's reads of Q.
+    constexpr bool split_out = outputs && !kPair;
     // Both summaries in one pass (values, split, no outputs) on two column tiles: waves 0
     // and 1 run the chains of the M tiles (split operands, no values, identity start,
     // written to a.m_out), waves 2 and 3 the chains of the S tiles (values, zero start,
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     // its own. Requires ncols = dk; `tiles` counts pairs of column tiles.
     constexpr bool dual = kHasV && kSplit && !kOut;
     constexpr bool two_compute = outputs || dual;   // compute waves first, then loading waves
-    constexpr int load_mode = dual ? 2 : (pair ? 3 : (outputs ? 1 : 0));
+    constexpr int load_mode = dual ? 2 : (pair ? 3 : (split_out ? 4 : (outputs ? 1 : 0)));
     constexpr int vtiles = (dual || pair) ? 2 : 1;   // column tiles per workgroup
     // K-side stage buffer: K, That, That remainder (split), V; Q-side: Q, P.
     // K-side operands of chunk n are written in iteration n - 1 and read in iteration
@@ -650,7 +656,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
     const uint32_t kstep = static_cast<uint32_t>(kChunk * qk_row * 2);   // bytes per chunk
     const uint32_t vstep = static_cast<uint32_t>(kChunk * v_row * 2);
     const uint32_t ostep = static_cast<uint32_t>(kChunk * vo_row * 2);
-    const int first_loader = (dual || pair) ? 4 : (two_compute ? 2 : 1);
+    const int first_loader = (dual || pair) ? 4 : (split_out ? 3 : (two_compute ? 2 : 1));
     // K / Q tile layout: quad block j (rows 4j .. 4j+3, 1 KiB) holds granule gk (dk 8gk .. +7)
     // of row 4j + rho at 16-byte slot 16 rho + (gk ^ (4 rho + j % 4)). A 1 KiB load fills one
     // quad block with 16 lanes per row, so that each group of 4 lanes reads one 64-byte piece
@@ -699,7 +705,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         for (int m = 0; m < 2 * vtiles; ++m)
             voff_v[m] = static_cast<uint32_t>(((32 * (m & 1) + (lane >> 1)) * v_row + h * ncols + colp + 16 * (m >> 1) +
                                                8 * (lane & 1)) * 2);
-        constexpr int nl = 8 - ((dual || pair) ? 4 : (two_compute ? 2 : 1));
+        constexpr int nl = 8 - ((dual || pair) ? 4 : (split_out ? 3 : (two_compute ? 2 : 1)));
         constexpr int NK = 16 + 6 + (kSplit ? 6 : 0) + NV + 1;
         constexpr int NQ = outputs ? 16 : 0;
         constexpr int NI = NK + NQ;   // 1 KiB loads of one full iteration
@@ -812,7 +818,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         return;
     }
 
-    if (outputs && (wave == 1 || (pair && wave == 3))) {
+    if (outputs && (wave == 1 || (pair && wave == 3) || (split_out && wave == 2))) {
+        const int half = (split_out && wave == 2) ? 1 : 0;   // which two token tiles (split outputs)
         // ---------------- output wave: chunk n - 1 during chunk n ----------------
         // stores past the row's extent (the tail of a packed sequence's last chunk) are
         // dropped by the descriptor's range
@@ -879,7 +886,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         };
         // a row or segment without chunks has no line to prefetch (the clamped token
         // index would fall before the row)
-        const bool pf_on = kEnablePrefetch && n1 > n0;
+        const bool pf_on = kEnablePrefetch && n1 > n0 && half == 0;   // the tile's share: one wave
         if (pf_on)
             for (int c = n0 + 2; c < n0 + kPrefetch && c < n1; ++c) prefetch(c);
         const int last = n1 > 0 ? n1 - 1 : 0;
@@ -889,13 +896,19 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const __amdgpu_buffer_rsrc_t rpm = make_rsrc(static_cast<const uint16_t*>(a.ws.pmat) + bh * a.NT * kTriRecord,
                                                      static_cast<int64_t>(a.NT) * kTriRecord * 2);
         const uint32_t voff_p = static_cast<uint32_t>(16 * lane);
-        using PSet = bf16x8[6];
+        // with split outputs a wave loads the P blocks of its own token tiles: tiles 0 and 3
+        // (blocks 0, 4, 5) or 1 and 2 (blocks 1, 2, 3); its first tile uses pp[0], its
+        // second pp[1] and pp[2]
+        constexpr int NPB = split_out ? 3 : 6;
+        using PSet = bf16x8[NPB];
         PSet p0, p1;
         auto load_p = [&](int c, PSet& pp) {
 #pragma unroll
-            for (int i = 0; i < 6; ++i)
+            for (int i = 0; i < NPB; ++i) {
+                const int blk = split_out ? (half ? 1 + i : (i == 0 ? 0 : 3 + i)) : i;
                 pp[i] = __builtin_bit_cast(bf16x8, gload16(rpm, voff_p, static_cast<uint32_t>(c) * (kTriRecord * 2) +
-                                                                            static_cast<uint32_t>(i * 1024)));
+                                                                            static_cast<uint32_t>(blk * 1024)));
+            }
         };
         auto compute = [&](int m, const PSet& pp) {   // outputs of chunk m
             const unsigned char* hb = hst + (2 * sub + (m & 1)) * HB;
@@ -907,7 +920,8 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
 #pragma unroll
             for (int s = 0; s < 2; ++s) ub[s] = lds_frag_b(hb + (4 + s) * 1024 + 16 * lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int ri = 0; ri < (split_out ? 2 : 4); ++ri) {
+                const int r = split_out ? (half ? 1 + ri : 3 * ri) : ri;
                 f32x4 o0 = zero4(), o1 = zero4();
 #pragma unroll
                 for (int s = 0; s < 4; s += 2) {
@@ -918,8 +932,13 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
                 f32x4 o;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o[j] = e * (o0[j] + o1[j]);
-                o = mfma16(ub[0], pp[tri_block(r, 0)], o);
-                if (r >= 2) o = mfma16(ub[1], pp[tri_block(r, 1)], o);
+                if constexpr (split_out) {
+                    o = mfma16(ub[0], pp[ri == 0 ? 0 : 1], o);
+                    if (ri == 1) o = mfma16(ub[1], pp[2], o);
+                } else {
+                    o = mfma16(ub[0], pp[tri_block(ri, 0)], o);
+                    if (ri >= 2) o = mfma16(ub[1], pp[tri_block(ri, 1)], o);
+                }
                 const int64_t t = static_cast<int64_t>(m) * kChunk + 16 * r + l16;
                 const bool ok = t < nvalid;
                 const uint32_t w0 = ok ? pk2(o[0], o[1]) : 0u, w1 = ok ? pk2(o[2], o[3]) : 0u;
@@ -951,7 +970,7 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
-    if (wave != 0 && !dual && !(pair && wave == 2)) {
+    if (wave != 0 && !dual && !(pair && wave == 2)) {   // (with split outputs waves 1 and 2 returned above)
         for (int n = n0; n <= n1; ++n) chunk_barrier(false);
         return;
     }
