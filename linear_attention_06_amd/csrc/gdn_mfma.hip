@@ -785,6 +785,13 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
         const int last = n1 > 0 ? n1 - 1 : 0;
         auto step = [&](int n, Stage& stage) {
             chunk_barrier(false);
+            // The chain wave reads the chunk's K fragments right after the barrier, between
+            // the MFMAs of the pending state update; LDS stores issued at that moment delay
+            // those reads on the chain's critical path. With outputs (and in the one-pass
+            // summary) the stores wait ~770 cycles, the operands still land an iteration
+            // before their use (stateful 32K forward 0.612 -> 0.575 ms; delays of 384 to
+            // 1,024 cycles all help, 768 the most; the state pass alone is slower with it).
+            if constexpr (outputs || dual) __builtin_amdgcn_s_sleep(12);
             store_k(n + 1, stage);
             if constexpr (outputs) store_q(n, stage);
             load_k(min(n + 3, last), stage);
