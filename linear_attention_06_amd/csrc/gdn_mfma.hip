@@ -26,6 +26,7 @@ namespace {
 
 constexpr int CP = 64 + 8;   // LDS pitch (bf16) of 64-wide rows: 144 B
 constexpr bool kEnablePrefetch = true;   // L2 prefetch of chunk operands by the output wave
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -276,7 +277,11 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
         rq_s[tid] = 1.f;
     }
     lds_sync();
-    if (wave == 2) {
+    // Waves 0-2 form the Gram tiles, wave 3 the decay record and the mask exponents.
+    // (mi, nj): the lower 32x32 tile of K K^T and of Q K^T that wave w < 3 owns.
+    const int mi = wave == 0 ? 1 : wave - 1, nj = wave == 0 ? 0 : wave - 1;
+    f32x16 acc0 = zero16(), acc1 = zero16();
+    if (wave == 3) {
         // the decay record: exp(Gam) rk, exp(Gam_C - Gam) rk, exp(Gam) rq, exp(Gam_C)
         const float gam = gam_s[lane], gam_c = gam_s[63], rk = rk_s[lane], rq = rq_s[lane];
         const float eg = __expf(gam);
@@ -285,37 +290,23 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
         gr[64 + lane] = __expf(gam_c - gam) * rk;
         gr[128 + lane] = eg * rq;
         gr[192 + lane] = lane == 0 ? __expf(gam_c) : 0.f;
-    } else if (wave == 3) {
         // the exponents of the decay masks of A and P with the row factors folded in
-        // (ln 1 = 0 exactly without a prologue)
-        const float gam = gam_s[lane], lk = __logf(rk_s[lane]);
-        gk_s[lane] = gam + lk;
-        gks_s[lane] = gam - lk;
-        gq_s[lane] = gam + __logf(rq_s[lane]);
-    }
-
-    // K K^T and Q K^T on the lower 32x32 tiles: (row tile, col tile) in
-    // {(0,0), (1,0), (1,1)} for each; six products over four waves.
-    auto tile = [&](const uint16_t* X, int mi, int nj) {
-        f32x16 acc = zero16();
+        // (ln 1 = 0 exactly without a prologue), in base 2 for v_exp_f32
+        const float lk = __logf(rk);
+        gk_s[lane] = (gam + lk) * kLog2e;
+        gks_s[lane] = (gam - lk) * kLog2e;
+        gq_s[lane] = (gam + __logf(rq)) * kLog2e;
+    } else {
+        // K K^T and Q K^T of tile (mi, nj) in one k-loop over the shared K fragments:
+        // wave 0 (1,0), wave 1 (0,0), wave 2 (1,1)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const bf16x8 av = lds_frag(X + kq_at(32 * mi + lr, 2 * c + q));
+            const bf16x8 ak = lds_frag(k_s + kq_at(32 * mi + lr, 2 * c + q));
+            const bf16x8 aq = lds_frag(q_s + kq_at(32 * mi + lr, 2 * c + q));
             const bf16x8 bv = lds_frag(k_s + kq_at(32 * nj + lr, 2 * c + q));
-            acc = mfma32(av, bv, acc);
+            acc0 = mfma32(ak, bv, acc0);
+            acc1 = mfma32(aq, bv, acc1);
         }
-        return acc;
-    };
-    // wave 0: KK(1,0), QK(1,0);  wave 1: KK(0,0), KK(1,1);  waves 2,3: QK(w-2, w-2)
-    f32x16 acc0, acc1 = zero16();
-    if (wave == 0) {
-        acc0 = tile(k_s, 1, 0);
-        acc1 = tile(q_s, 1, 0);
-    } else if (wave == 1) {
-        acc0 = tile(k_s, 0, 0);
-        acc1 = tile(k_s, 1, 1);
-    } else {
-        acc0 = tile(q_s, wave - 2, wave - 2);
     }
     lds_sync();   // K and Q are dead from here on; A takes their place
     // A (fp32) into LDS. The decay and beta values of the lane's 16 rows are read
@@ -333,46 +324,39 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = 32 * mi + 8 * (i / 4) + 4 * q + (i % 4);
-            a_s[t * AP + s] = (t > s) ? bt[i / 4][i % 4] * __expf(gt[i / 4][i % 4] - gs) * acc[i] : 0.f;
+            a_s[t * AP + s] = (t > s) ? bt[i / 4][i % 4] * __builtin_amdgcn_exp2f(gt[i / 4][i % 4] - gs) * acc[i] : 0.f;
         }
     };
-    if (wave == 0) emit_a(acc0, 1, 0);
-    if (wave == 1) {
-        emit_a(acc0, 0, 0);
-        emit_a(acc1, 1, 1);
-    }
-    // P stays in registers until K and Q are no longer read
-    const bool has_p = (wave != 1);
-    const int p_mi = (wave == 0) ? 1 : wave - 2, p_nj = (wave == 0) ? 0 : wave - 2;
-    f32x16 pq = (wave == 0) ? acc1 : acc0;
-    if (has_p) {
-        const int s = 32 * p_nj + lr;
+    if (wave < 3) emit_a(acc0, mi, nj);
+    lds_sync();   // A is complete; P stays in registers until A is dead
+    if (wave < 3) {
+        // the decay mask of the wave's P tile, while wave 3 inverts the diagonal blocks
+        const int s = 32 * nj + lr;
         const float gs = gks_s[s];
         f32x4 gt[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) gt[i4] = *reinterpret_cast<const f32x4*>(gq_s + 32 * p_mi + 8 * i4 + 4 * q);
+        for (int i4 = 0; i4 < 4; ++i4) gt[i4] = *reinterpret_cast<const f32x4*>(gq_s + 32 * mi + 8 * i4 + 4 * q);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int t = 32 * p_mi + 8 * (i / 4) + 4 * q + (i % 4);
-            pq[i] = (t >= s) ? __expf(gt[i / 4][i % 4] - gs) * pq[i] : 0.f;
+            const int t = 32 * mi + 8 * (i / 4) + 4 * q + (i % 4);
+            acc1[i] = (t >= s) ? __builtin_amdgcn_exp2f(gt[i / 4][i % 4] - gs) * acc1[i] : 0.f;
         }
-    }
-    lds_sync();   // A is complete; P stays in registers until A is dead
-    // zero the strictly upper 16x16 blocks of Tinv
-    for (int e = tid; e < 6 * 256; e += 256) {
-        const int blk = e >> 8, w = e & 255;
-        const int bi = (blk < 3) ? 0 : (blk < 5 ? 1 : 2);
-        const int bj = (blk < 3) ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-        t_s[(16 * bi + (w >> 4)) * AP + 16 * bj + (w & 15)] = 0.f;
-    }
-    // diagonal 16x16 blocks: unit lower-triangular inverse by forward
-    // substitution, wave w inverts block w, lane c < 16 owns column c
-    if (lane < 16) {
-        // column sweep: once x[j] is final it is eliminated from every later row, so
+        // zero the strictly upper 16x16 blocks of Tinv, 16 bytes a store
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int e = tid; e < 6 * 64; e += 192) {
+            const int blk = e >> 6, w = e & 63;
+            const int bi = (blk < 3) ? 0 : (blk < 5 ? 1 : 2);
+            const int bj = (blk < 3) ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+            *reinterpret_cast<f32x4*>(t_s + (16 * bi + (w >> 2)) * AP + 16 * bj + 4 * (w & 3)) = z;
+        }
+    } else {
+        // diagonal 16x16 blocks: unit lower-triangular inverse by forward substitution,
+        // lane (blk, c) of wave 3 owns column c of diagonal block blk.
+        // Column sweep: once x[j] is final it is eliminated from every later row, so
         // the dependency chain is 15 steps long instead of one FMA per matrix entry.
         // The block is read in four batches of columns 4q .. 4q+3, one 16-byte read per
         // row below the diagonal (at most 15 reads, so each batch waits once).
-        const int c = lane, o = 16 * wave;
+        const int c = lane & 15, o = 16 * (lane >> 4);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
@@ -443,15 +427,15 @@ __global__ __launch_bounds__(256, 4) void prep_mfma(PrepArgs a) {
     }
     lds_sync();
     // P into the space of A
-    if (has_p) {
-        const int s = 32 * p_nj + lr;
+    if (wave < 3) {
+        const int s = 32 * nj + lr;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int t = 32 * p_mi + 8 * (i / 4) + 4 * q + (i % 4);
-            p_s[t * CP + s] = bf16_bits(pq[i]);
+            const int t = 32 * mi + 8 * (i / 4) + 4 * q + (i % 4);
+            p_s[t * CP + s] = bf16_bits(acc1[i]);
         }
     } else {
-        // wave 1: the all-zero upper tile of P (rows 0..31, cols 32..63)
+        // wave 3: the all-zero upper tile of P (rows 0..31, cols 32..63)
         for (int e = lane; e < 32 * 32; e += 64) p_s[(e >> 5) * CP + 32 + (e & 31)] = 0;
     }
     lds_sync();
