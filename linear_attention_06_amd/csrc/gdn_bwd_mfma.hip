@@ -566,7 +566,6 @@ __device__ __forceinline__ void zero_upper_tiles_t(unsigned char* base, int e) {
 
 __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
     __shared__ __align__(16) unsigned char sm[G_SIZE];
-    __shared__ __align__(16) unsigned char pf_s[256];   // sink of the L2 prefetches
     const int NT = a.NT;
     const int n = static_cast<int>(blockIdx.x % static_cast<unsigned>(NT));
     const int bq = static_cast<int>(blockIdx.x / static_cast<unsigned>(NT));
@@ -586,30 +585,6 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
     float* part_b = gam_s + 768;
     float* misc = gam_s + 1280;    // e^{Gam_C}, per-wave W sums, per-wave <dS', S>
     const int m = wave;            // dq / dk column tile of this wave
-
-    // L2 prefetch of the lines a later load phase reads, one line per lane, issued where the
-    // wave has no loads of its own in flight: the loads of phase A (a panel's state and
-    // state-gradient rows, its V and dO columns) otherwise wait for memory with every block
-    // of the grid loading at once. The data lands in a scratch LDS word per lane that nothing
-    // reads.
-    const uint32_t pf_lds = lds_addr(pf_s);
-    const auto pf_line = [&](const void* p) {
-        const uint32_t m0v = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pf_lds));
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(m0v), "v"(p) : "memory", "m0");
-    };
-    // the 384 lines of phase A for value head hh (chunk record chh), panel pp: thread L < 128
-    // a state row half, < 256 a state-gradient row half, < 320 a V row, < 384 a dO row
-    const auto pf_panel = [&](int hh, int64_t chh, int pp, int L) {
-        const int r = L & 63;
-        if (L < 256) {
-            const uint16_t* base = static_cast<const uint16_t*>(L < 128 ? a.states : a.dstates);
-            pf_line(base + (chh * DK + 64 * pp + ((L & 127) >> 1)) * DK + 64 * (L & 1));
-        } else if (L < 384) {
-            const int64_t t = min(t0 + r, static_cast<int64_t>(a.T) - 1);
-            const uint16_t* base = static_cast<const uint16_t*>(L < 320 ? a.v : a.d_o);
-            if (base) pf_line(base + (rs.start + t) * v_row + hh * DK + 64 * pp);
-        }
-    };
 
     // K and Q of the chunk, zero past the valid tokens
     {
@@ -798,19 +773,6 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
                 }
             }
             // ---- C ----
-            // prefetch: the next panel's phase A lines and the row-major records of phase D0,
-            // or after the last panel the next value head's first panel, by waves 1-6 (wave 0's
-            // own loads of the next decay inputs would otherwise wait behind them; those
-            // lines, shared by all heads of a token, are in the L2 already). The thread index
-            // is re-derived here, so that no address is kept live across phases.
-            if (pn == 0) {
-                const int pt = fresh_lane(tid);
-                if (pt < 384) pf_panel(h, ch, 1, pt);
-                else pf_line(static_cast<const uint16_t*>(pt < 448 ? a.rec.t_rm : a.rec.p_rm) + ch * 4096 + (pt & 63) * 64);
-            } else if (kk + 1 < rep) {
-                const int pt = fresh_lane(tid);
-                if (pt >= 64 && pt < 448) pf_panel(h + 1, ch + NT, 0, pt - 64);
-            }
             {
                 const int ln = fresh_lane(lane), l16 = ln & 15, g4 = ln >> 4;
                 // the B operands (columns 16 m .. of S and dS', contraction over the panel's
@@ -1087,7 +1049,6 @@ __global__ __launch_bounds__(512) void bwd_grad_mfma(BwdMfmaArgs a) {
             *reinterpret_cast<f32x4*>(a.dk_out + o) = xk;
         }
     }
-    __builtin_amdgcn_s_waitcnt(0);   // every prefetch has landed in the sink
 }
 
 // Segments of B rows as rows of their own. State blocks (D x D fp32, 16 KiB at D = 128)
