@@ -438,6 +438,179 @@ __global__ __launch_bounds__(256) void affine_scan_rev(ScanBwdArgs a) {
     }
 }
 
+// The two scans above for dk = 128 on v_mfma_f32_16x16x4_f32 (fp32 products, fp32
+// accumulation), one block of four waves per (16 columns, h, b); wave w owns rows 32 w ..
+// 32 w + 31 of the running state (two 16-row tiles in accumulator layout: lane (c, g) holds
+// rows 16 rt + 4 g .. + 3 of column c). The state is exchanged through LDS transposed
+// (column c at x_t + c * kScanPitch), so that a lane reads its four rows of a k-tile with one
+// 16-byte read. k-step (t, s) of a tile product has lane (., g) supply contraction index
+// 16 t + 4 g + s on both sides; over t = 0..7 and s = 0..3 that covers each of the 128 once.
+// Each step's M_p fragments are loaded during the previous step's products.
+constexpr int kScanPitch = 128 + 4;
+typedef float f32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4s mfma_f32_4(float a, float b, f32x4s c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// The fragments of M_p (forward) or M_p^T (reverse) of rows 32 w .. + 31 for k-tile t:
+// element s of m[rt][t] is M_p[16 (2w + rt) + l16][16 t + 4 g + s] (forward) or
+// M_p[16 t + 4 g + s][16 (2w + rt) + l16] (reverse).
+template <bool kTrans>
+__device__ __forceinline__ void scan_load_m(const float* Mp, int wave, int l16, int g4, f32x4s (&m)[2][8]) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int row = 16 * (2 * wave + rt) + l16;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if constexpr (!kTrans) {
+                m[rt][t] = *reinterpret_cast<const f32x4s*>(Mp + row * 128 + 16 * t + 4 * g4);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[rt][t][e] = Mp[(16 * t + 4 * g4 + e) * 128 + row];
+            }
+        }
+    }
+}
+
+// acc[rt] += (M_p or M_p^T) X for the wave's two row tiles, X^T in LDS
+__device__ __forceinline__ void scan_products(const float* x_t, int l16, int g4, const f32x4s (&m)[2][8],
+                                              f32x4s (&acc)[2]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const f32x4s xb = *reinterpret_cast<const f32x4s*>(x_t + l16 * kScanPitch + 16 * t + 4 * g4);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) acc[rt] = mfma_f32_4(m[rt][t][s], xb[s], acc[rt]);
+    }
+}
+
+// XCD-aware block order of the scans (workgroups go round-robin over the 8 XCDs): the
+// 16-column tiles of one (b, h) run on one XCD, so that its L2 reads each M_p from memory
+// once for all of them. Returns false for the padding blocks of the last group.
+__device__ __forceinline__ bool scan_block(int ntiles, int nbh, int& tile, int& bhi) {
+    const int L = blockIdx.x, xcd = L & 7, slot = L >> 3;
+    tile = slot % ntiles;
+    bhi = (slot / ntiles) * 8 + xcd;
+    return bhi < nbh;
+}
+
+__global__ __launch_bounds__(256) void affine_scan_mfma(ScanArgs a) {
+    __shared__ __align__(16) float x_t[16 * kScanPitch];
+    const int ncols = a.ncols;
+    int ct, bhi;
+    if (!scan_block(ncols / 16, a.B * a.H, ct, bhi)) return;
+    const int col0 = 16 * ct;
+    const int64_t bh = bhi;
+    const int64_t tile = static_cast<int64_t>(128) * ncols;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    for (int e = tid; e < 128 * 16; e += 256) {
+        const int i = e >> 4, c = e & 15;
+        float x0 = 0.f;
+        if (a.init_mode == kInitLoad) x0 = a.init[bh * tile + static_cast<int64_t>(i) * ncols + col0 + c];
+        else if (a.init_mode == kInitIdentity) x0 = (i == col0 + c) ? 1.f : 0.f;
+        x_t[c * kScanPitch + i] = x0;
+    }
+    f32x4s m[2][8], mn[2][8];
+    if (a.P > 0) scan_load_m<false>(a.M + bh * a.P * 128 * 128, wave, l16, g4, m);
+    __syncthreads();
+    for (int p = 0; p < a.P; ++p) {
+        // the next step's fragments are in flight during this step's products
+        if (p + 1 < a.P) scan_load_m<false>(a.M + (bh * a.P + p + 1) * 128 * 128, wave, l16, g4, mn);
+        const int64_t blk = bh * a.P + p;
+        // S_p is added after the products, so that its loads are in flight during them
+        f32x4s acc[2], sv[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int row0 = 16 * (2 * wave + rt) + 4 * g4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                sv[rt][j] = a.S ? a.S[blk * tile + static_cast<int64_t>(row0 + j) * ncols + col0 + l16] : 0.f;
+            if (a.x_before) {
+                const f32x4s xo = *reinterpret_cast<const f32x4s*>(x_t + l16 * kScanPitch + row0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a.x_before[blk * tile + static_cast<int64_t>(row0 + j) * ncols + col0 + l16] = xo[j];
+            }
+            acc[rt] = f32x4s{0.f, 0.f, 0.f, 0.f};
+        }
+        scan_products(x_t, l16, g4, m, acc);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt] += sv[rt];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) m[rt][t] = mn[rt][t];
+        __syncthreads();   // every read of X_{p-1} is done
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int row0 = 16 * (2 * wave + rt) + 4 * g4;
+            *reinterpret_cast<f32x4s*>(x_t + l16 * kScanPitch + row0) = acc[rt];
+            if (a.x_after)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a.x_after[blk * tile + static_cast<int64_t>(row0 + j) * ncols + col0 + l16] = acc[rt][j];
+        }
+        __syncthreads();
+    }
+    if (a.x_final)
+        for (int e = tid; e < 128 * 16; e += 256) {
+            const int i = e >> 4, c = e & 15;
+            a.x_final[bh * tile + static_cast<int64_t>(i) * ncols + col0 + c] = x_t[c * kScanPitch + i];
+        }
+}
+
+__global__ __launch_bounds__(256) void affine_scan_rev_mfma(ScanBwdArgs a) {
+    __shared__ __align__(16) float x_t[16 * kScanPitch];
+    const int dv = a.dv;
+    int ct, bhi;
+    if (!scan_block(dv / 16, a.B * a.H, ct, bhi)) return;
+    const int col0 = 16 * ct;
+    const int64_t bh = bhi;
+    const int64_t tile = static_cast<int64_t>(128) * dv;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    for (int e = tid; e < 128 * 16; e += 256) {
+        const int i = e >> 4, c = e & 15;
+        x_t[c * kScanPitch + i] = a.dhT ? a.dhT[bh * tile + static_cast<int64_t>(i) * dv + col0 + c] : 0.f;
+    }
+    f32x4s m[2][8], mn[2][8];
+    if (a.P > 0) scan_load_m<true>(a.M + (bh * a.P + a.P - 1) * 128 * 128, wave, l16, g4, m);
+    __syncthreads();
+    for (int p = a.P - 1; p >= 0; --p) {
+        if (p > 0) scan_load_m<true>(a.M + (bh * a.P + p - 1) * 128 * 128, wave, l16, g4, mn);
+        const int64_t blk = bh * a.P + p;
+        // dH_in_p is added after the products, so that its loads are in flight during them
+        f32x4s acc[2], dv_in[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int row0 = 16 * (2 * wave + rt) + 4 * g4;
+            const f32x4s go = *reinterpret_cast<const f32x4s*>(x_t + l16 * kScanPitch + row0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t o = blk * tile + static_cast<int64_t>(row0 + j) * dv + col0 + l16;
+                dv_in[rt][j] = a.dH_in[o];
+                a.dS[o] = go[j];
+            }
+            acc[rt] = f32x4s{0.f, 0.f, 0.f, 0.f};
+        }
+        scan_products(x_t, l16, g4, m, acc);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc[rt] += dv_in[rt];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) m[rt][t] = mn[rt][t];
+        __syncthreads();
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+            *reinterpret_cast<f32x4s*>(x_t + l16 * kScanPitch + 16 * (2 * wave + rt) + 4 * g4) = acc[rt];
+        __syncthreads();
+    }
+    if (a.dh0)
+        for (int e = tid; e < 128 * 16; e += 256) {
+            const int i = e >> 4, c = e & 15;
+            a.dh0[bh * tile + static_cast<int64_t>(i) * dv + col0 + c] = x_t[c * kScanPitch + i];
+        }
+}
+
 // dM_p = dS_p H_in_p^T, one block per (16 rows of dM, (b, h, p)): the block's 16 rows of
 // dS_p and all of H_in_p in LDS (fp32), thread (r, j0) sums over the dv columns for the
 // outputs (r, j0 + 16 u).
@@ -459,6 +632,39 @@ __global__ __launch_bounds__(256) void summary_outer(ScanBwdArgs a) {
         float acc = 0.f;
         for (int c = 0; c < dv; ++c) acc += ds_s[r * pitch + c] * hi_s[j * pitch + c];
         a.dM[blk * static_cast<int64_t>(dk) * dk + static_cast<int64_t>(r0 + r) * dk + j] = acc;
+    }
+}
+
+// dM_p = dS_p H_in_p^T for dk = dv = 128 on v_mfma_f32_16x16x4_f32: one block of eight
+// waves per (b, h, p); H_in_p is staged in LDS (rows at a pitch of 132 floats) and wave w
+// forms the 16 x 128 row tile w of dM_p. k-step (t, s) has lane (., g) supply dv index
+// 16 t + 4 g + s of both operands, each read as 16 contiguous bytes of a row of dS_p or
+// H_in_p.
+__global__ __launch_bounds__(512) void summary_outer_mfma(ScanBwdArgs a) {
+    __shared__ __align__(16) float hi_s[128 * kScanPitch];
+    const int64_t blk = blockIdx.x;   // (b h) P + p
+    const float* dS = a.dS + blk * 128 * 128;
+    const float* Hi = a.H_in + blk * 128 * 128;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    f32x4s af[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) af[t] = *reinterpret_cast<const f32x4s*>(dS + (16 * wave + l16) * 128 + 16 * t + 4 * g4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int e = tid + 512 * u, row = e >> 5, c4 = e & 31;
+        *reinterpret_cast<f32x4s*>(hi_s + row * kScanPitch + 4 * c4) = *reinterpret_cast<const f32x4s*>(Hi + row * 128 + 4 * c4);
+    }
+    __syncthreads();
+    for (int jt = 0; jt < 8; ++jt) {
+        f32x4s acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4s bf = *reinterpret_cast<const f32x4s*>(hi_s + (16 * jt + l16) * kScanPitch + 16 * t + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) acc = mfma_f32_4(af[t][s], bf[s], acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a.dM[blk * 128 * 128 + (16 * wave + 4 * g4 + j) * 128 + 16 * jt + l16] = acc[j];
     }
 }
 
@@ -507,16 +713,24 @@ hipError_t launch_state_f32path(const StateArgs& a, bool io_bf16, hipStream_t s)
     return io_bf16 ? state_dispatch<uint16_t>(a, s) : state_dispatch<float>(a, s);
 }
 
+// blocks of the XCD-aware scan order: ceil(B H / 8) groups of 8 (b, h) x the column tiles
+static dim3 scan_grid_xcd(int B, int H, int ncols) {
+    const int64_t groups = (static_cast<int64_t>(B) * H + 7) / 8;
+    return dim3(static_cast<unsigned>(groups * 8 * (ncols / 16)));
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H),
-                    static_cast<unsigned>(a.B));
+    dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
     void* args[] = {const_cast<ScanArgs*>(&a)};
     const void* fn = nullptr;
     switch (a.dk) {
         case 16: fn = reinterpret_cast<const void*>(&affine_scan<16>); break;
         case 32: fn = reinterpret_cast<const void*>(&affine_scan<32>); break;
         case 64: fn = reinterpret_cast<const void*>(&affine_scan<64>); break;
-        case 128: fn = reinterpret_cast<const void*>(&affine_scan<128>); break;
+        case 128:
+            fn = reinterpret_cast<const void*>(&affine_scan_mfma);
+            grid = scan_grid_xcd(a.B, a.H, a.ncols);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
@@ -525,20 +739,23 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s) {
     void* args[] = {const_cast<ScanBwdArgs*>(&a)};
     const void* fn = nullptr;
+    dim3 grid(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H), static_cast<unsigned>(a.B));
     switch (a.dk) {
         case 16: fn = reinterpret_cast<const void*>(&affine_scan_rev<16>); break;
         case 32: fn = reinterpret_cast<const void*>(&affine_scan_rev<32>); break;
         case 64: fn = reinterpret_cast<const void*>(&affine_scan_rev<64>); break;
-        case 128: fn = reinterpret_cast<const void*>(&affine_scan_rev<128>); break;
+        case 128:
+            fn = reinterpret_cast<const void*>(&affine_scan_rev_mfma);
+            grid = scan_grid_xcd(a.B, a.H, a.dv);
+            break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipLaunchKernel(fn, dim3(static_cast<unsigned>(a.dv / 16), static_cast<unsigned>(a.H),
-                                            static_cast<unsigned>(a.B)),
-                                   dim3(256), args, 0, s);
+    hipError_t e = hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
     if (e != hipSuccess || a.P == 0) return e;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&summary_outer),
-                           dim3(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.P),
-                                static_cast<unsigned>(a.dk / 16)),
+    const unsigned nbhp = static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.P);
+    if (a.dk == 128 && a.dv == 128)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&summary_outer_mfma), dim3(nbhp), dim3(512), args, 0, s);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&summary_outer), dim3(nbhp, static_cast<unsigned>(a.dk / 16)),
                            dim3(256), args, 0, s);
 }
 
