@@ -772,10 +772,12 @@ __global__ __launch_bounds__(512) void state_mfma(StateArgs a, int tiles, int qk
             // The chain wave reads the chunk's K fragments right after the barrier, between
             // the MFMAs of the pending state update; LDS stores issued at that moment delay
             // those reads on the chain's critical path. With outputs (and in the one-pass
-            // summary) the stores wait ~770 cycles, the operands still land an iteration
-            // before their use (stateful 32K forward 0.612 -> 0.575 ms; delays of 384 to
-            // 1,024 cycles all help, 768 the most; the state pass alone is slower with it).
-            if constexpr (outputs || dual) __builtin_amdgcn_s_sleep(12);
+            // summary) the stores wait ~770 cycles, with two tiles of outputs ~1,280, and
+            // the operands still land an iteration before their use (stateful 32K forward
+            // 0.612 -> 0.575 ms; delays of 384 to 1,024 cycles all help, 768 the most; the
+            // segment apply of 8 x 4096 tokens, paired, is best at 1,280; the state pass
+            // alone is slower with a delay).
+            if constexpr (outputs || dual) __builtin_amdgcn_s_sleep(pair ? 20 : 12);
             store_k(n + 1, stage);
             if constexpr (outputs) store_q(n, stage);
             load_k(min(n + 3, last), stage);
