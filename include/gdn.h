@@ -80,16 +80,22 @@ const char* gdn_last_error(void);
 
 /*
  * Kernel path a problem runs on (static string), or NULL for an invalid problem:
- *   "bf16-mfma" -- bf16 I/O with dk == 128 (any dv of 16, 32, 64, 128): bf16 matrix-core
- *                  contractions with fp32 accumulation and an fp32 state;
- *   "f32-valu"  -- every other problem: fp32 arithmetic on the vector ALUs.
+ *   "bf16-mfma"        -- bf16 I/O with dk == 128 (any dv of 16, 32, 64, 128): bf16
+ *                         matrix-core contractions with fp32 accumulation and an fp32 state;
+ *   "bf16-mfma-padded" -- bf16 I/O with dk < 128: gdn_chunk_fwd runs the dk == 128
+ *                         matrix-core kernels on q and k zero-padded to 128 columns (exact:
+ *                         the padded columns add zeros to every product); every other call
+ *                         runs such a problem on the fp32 vector-ALU kernels;
+ *   "f32-valu"         -- every other problem: fp32 arithmetic on the vector ALUs.
  */
 const char* gdn_kernel_path(const gdn_problem* p);
 
 /*
  * Workspace for gdn_chunk_fwd, in bytes, written to *bytes. The workspace holds
  * the per-chunk intermediates (the triangular-solve factor, the masked intra-chunk
- * q.k block and the chunk decay factors); its contents are undefined on entry.
+ * q.k block and the chunk decay factors), and for bf16 heads with dk < 128 also q and k
+ * padded to 128 columns and the initial and final states padded to 128 rows; its
+ * contents are undefined on entry.
  */
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes);
 
@@ -118,7 +124,9 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p,
  * shares that GPU's array: calls that overlap on one GPU (different streams, or host
  * threads without ordering) race and give undefined results; calls on one stream are
  * ordered. Nothing in the array has to start at zero (each call writes every record it
- * reads).
+ * reads). bf16 heads with dk < 128 run here on the fp32 vector-ALU kernels (gdn_chunk_fwd
+ * runs them on the matrix cores through padded copies of q and k, which this call has no
+ * room for), so for them the two calls agree to the bf16 bound, not bit for bit.
  */
 gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p,
                                  const void* q, const void* k, const void* v,

@@ -36,6 +36,18 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // other problem runs on the fp32 vector-ALU kernels.
 bool use_mfma(const gdn_problem& p) { return p.io_dtype == GDN_BF16 && p.dk == 128; }
 
+// gdn_chunk_fwd on bf16 heads with dk < 128 runs the dk = 128 matrix-core kernels on q and
+// k zero-padded to 128 columns (and h0 to 128 rows): the padded columns add exact zeros to
+// every q.k and k.k product and to K S, and the state's padded rows start at zero and stay
+// zero (their transition is a pure decay), so o and the first dk rows of the final state are
+// those of the unpadded problem.
+bool use_mfma_padded(const gdn_problem& p) { return p.io_dtype == GDN_BF16 && p.dk < 128; }
+gdn_problem padded_problem(const gdn_problem& p) {
+    gdn_problem w = p;
+    w.dk = 128;
+    return w;
+}
+
 // Chunk intermediates: one record per (b, h, chunk). The two 64x64 matrices take
 // their 6 lower-triangle 16x32 blocks in bf16 on the matrix-core path, and are
 // stored whole in fp32 otherwise.
@@ -191,6 +203,78 @@ gdn_status run_fwd(const gdn_problem& p, const Plan& pl, const void* q, const vo
     return run_state(p, a, s);
 }
 
+// Workspace of the padded forward: the dk = 128 problem's chunk records, then q and k
+// padded to 128 columns ([B, T, Hqk, 128] bf16), h0 and the final state padded to 128 rows
+// ([B, H, 128, dv] fp32).
+struct PadPlan {
+    Plan rec;
+    size_t q_off = 0, k_off = 0, h0_off = 0, hT_off = 0, bytes = 0;
+};
+
+// packed: the tokens of B packed sequences lie in one row of T (cu_seqlens)
+PadPlan make_pad_plan(const gdn_problem& p, int64_t max_len = -1, bool packed = false) {
+    PadPlan pp;
+    pp.rec = make_plan(padded_problem(p), false, max_len);
+    const size_t tokens = packed ? static_cast<size_t>(p.T) : static_cast<size_t>(p.B) * p.T;
+    const size_t qk = align256(tokens * p.Hqk * 128 * 2);
+    const size_t st = align256(static_cast<size_t>(p.B) * p.H * 128 * p.dv * 4);
+    pp.q_off = align256(pp.rec.bytes);
+    pp.k_off = pp.q_off + qk;
+    pp.h0_off = pp.k_off + qk;
+    pp.hT_off = pp.h0_off + st;
+    pp.bytes = pp.hT_off + st;
+    return pp;
+}
+
+gdn_status run_varlen(const gdn_problem& p, const Plan& pl, const int32_t* cu_seqlens, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta, const float* h0, void* o, float* hT, void* ws,
+                      hipStream_t s);
+
+// The forward of a bf16 problem with dk < 128 on padded copies (cu_seqlens: packed
+// sequences, through the varlen body).
+gdn_status run_fwd_padded(const gdn_problem& p, const PadPlan& pp, const int32_t* cu_seqlens, const void* q,
+                          const void* k, const void* v, const float* g, const float* beta, const float* h0,
+                          void* o, float* hT, void* ws, hipStream_t s) {
+    if (p.B == 0) return GDN_OK;
+    char* base = static_cast<char*>(ws);
+    const int64_t qk_rows = (cu_seqlens ? static_cast<int64_t>(p.T) : static_cast<int64_t>(p.B) * p.T) * p.Hqk;
+    const int64_t blocks = static_cast<int64_t>(p.B) * p.H;
+    const int64_t st_in = static_cast<int64_t>(p.dk) * p.dv * 4, st_pad = static_cast<int64_t>(128) * p.dv * 4;
+    hipError_t e = gdn::launch_copy_rows(q, p.dk * 2, base + pp.q_off, 256, qk_rows, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(k, p.dk * 2, base + pp.k_off, 256, qk_rows, s);
+    if (e == hipSuccess && h0) e = gdn::launch_copy_rows(h0, st_in, base + pp.h0_off, st_pad, blocks, s);
+    if (e != hipSuccess) return hip_fail(e, "padding copy launch");
+    float* hT_pad = hT ? reinterpret_cast<float*>(base + pp.hT_off) : nullptr;
+    const float* h0_pad = h0 ? reinterpret_cast<const float*>(base + pp.h0_off) : nullptr;
+    gdn_status st = cu_seqlens ? run_varlen(padded_problem(p), pp.rec, cu_seqlens, base + pp.q_off, base + pp.k_off,
+                                            v, g, beta, h0_pad, o, hT_pad, ws, s)
+                               : run_fwd(padded_problem(p), pp.rec, base + pp.q_off, base + pp.k_off, v, g, beta,
+                                         h0_pad, o, hT_pad, ws, s);
+    if (st != GDN_OK || !hT) return st;
+    e = gdn::launch_copy_rows(hT_pad, st_pad, hT, st_in, blocks, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "final-state copy launch");
+}
+
+// The packed-sequence forward on a checked problem with a workspace of at least pl.bytes.
+gdn_status run_varlen(const gdn_problem& p, const Plan& pl, const int32_t* cu_seqlens, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta, const float* h0, void* o, float* hT, void* ws,
+                      hipStream_t s) {
+    if (p.B == 0) return GDN_OK;
+    const gdn::Workspace w = carve(pl, ws);
+    if (p.T > 0) {
+        gdn_status st = run_prep(p, pl, q, k, g, beta, w, s, nullptr, cu_seqlens);
+        if (st != GDN_OK) return st;
+    }
+    gdn::StateArgs a = state_args(p, pl, q, k, v, w);
+    a.cu_seqlens = cu_seqlens;
+    a.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
+    a.s_init = h0;
+    a.o = o;
+    a.s_out = hT;
+    a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
+    return run_state(p, a, s);
+}
+
 // Chunk records of gdn_chunk_fwd_noalloc: a static device array, one copy per GPU that
 // loads the library, held until the process ends. Nothing in it has to start at zero:
 // the prepare pass writes every record the state pass reads. In host code the array's
@@ -239,13 +323,20 @@ const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
 const char* gdn_kernel_path(const gdn_problem* p) {
     if (check_problem(p) != GDN_OK) return nullptr;
-    return use_mfma(*p) ? "bf16-mfma" : "f32-valu";
+    return use_mfma(*p) ? "bf16-mfma" : (use_mfma_padded(*p) ? "bf16-mfma-padded" : "f32-valu");
 }
 
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    if (use_mfma_padded(*p)) {
+        const gdn_problem w = padded_problem(*p);
+        st = check_problem(&w);
+        if (st != GDN_OK) return st;
+        *bytes = make_pad_plan(*p).bytes;
+        return GDN_OK;
+    }
     *bytes = make_plan(*p, false).bytes;
     return GDN_OK;
 }
@@ -256,6 +347,17 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p, const void* q, const void* k, con
     try {
         gdn_status st = check_fwd_args(p, q, k, v, g, beta, o);
         if (st != GDN_OK) return st;
+        if (use_mfma_padded(*p)) {
+            const gdn_problem w = padded_problem(*p);
+            st = check_problem(&w);
+            if (st != GDN_OK) return st;
+            const PadPlan pp = make_pad_plan(*p);
+            Plan need;
+            need.bytes = pp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            return run_fwd_padded(*p, pp, nullptr, q, k, v, g, beta, h0, o, hT, ws, static_cast<hipStream_t>(stream));
+        }
         const Plan pl = make_plan(*p, false);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
@@ -327,6 +429,13 @@ gdn_status gdn_chunk_fwd_varlen_workspace(const gdn_problem* p, int32_t max_seql
     if (st != GDN_OK) return st;
     if (max_seqlen < 0) return fail(GDN_EINVAL, "max_seqlen=%d must be >= 0", max_seqlen);
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    if (use_mfma_padded(*p)) {
+        const gdn_problem w = padded_problem(*p);
+        st = check_problem(&w);
+        if (st != GDN_OK) return st;
+        *bytes = make_pad_plan(*p, max_seqlen, true).bytes;
+        return GDN_OK;
+    }
     *bytes = make_plan(*p, false, max_seqlen).bytes;
     return GDN_OK;
 }
@@ -344,24 +453,22 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
         if (p->B > 0 && !cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens must be non-NULL");
         if (p->T > 0 && (!q || !k || !v || !g || !beta || !o))
             return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+        if (use_mfma_padded(*p)) {
+            const gdn_problem w = padded_problem(*p);
+            st = check_problem(&w);
+            if (st != GDN_OK) return st;
+            const PadPlan pp = make_pad_plan(*p, max_seqlen, true);
+            Plan need;
+            need.bytes = pp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            return run_fwd_padded(*p, pp, cu_seqlens, q, k, v, g, beta, h0, o, hT, ws,
+                                  static_cast<hipStream_t>(stream));
+        }
         const Plan pl = make_plan(*p, false, max_seqlen);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
-        if (p->B == 0) return GDN_OK;
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        const gdn::Workspace w = carve(pl, ws);
-        if (p->T > 0) {
-            st = run_prep(*p, pl, q, k, g, beta, w, s, nullptr, cu_seqlens);
-            if (st != GDN_OK) return st;
-        }
-        gdn::StateArgs a = state_args(*p, pl, q, k, v, w);
-        a.cu_seqlens = cu_seqlens;
-        a.init_mode = h0 ? gdn::kInitLoad : gdn::kInitZero;
-        a.s_init = h0;
-        a.o = o;
-        a.s_out = hT;
-        a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
-        return run_state(*p, a, s);
+        return run_varlen(*p, pl, cu_seqlens, q, k, v, g, beta, h0, o, hT, ws, static_cast<hipStream_t>(stream));
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

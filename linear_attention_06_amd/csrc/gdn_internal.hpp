@@ -290,5 +290,7 @@ hipError_t launch_bwd_grad_mfma(const BwdMfmaArgs& a, hipStream_t s);
 hipError_t launch_scan_bwd(const ScanBwdArgs& a, hipStream_t s);
 hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool io_bf16, hipStream_t s);
+// rows of in_row bytes into rows of out_row bytes, zero-padded or cut (multiples of 16)
+hipError_t launch_copy_rows(const void* in, int64_t in_row, void* out, int64_t out_row, int64_t rows, hipStream_t s);
 
 }  // namespace gdn

@@ -201,7 +201,35 @@ hipError_t norm_dispatch(const NormArgs& a, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, s);
 }
 
+// Rows of in_row bytes copied into rows of out_row bytes (both multiples of 16), 16 bytes a
+// thread: the part of an output row past in_row is zero (padding), and an input row longer
+// than out_row is cut (cropping).
+__global__ __launch_bounds__(256) void copy_rows(const unsigned char* in, int64_t in_row, unsigned char* out,
+                                                 int64_t out_row, int64_t rows) {
+    const int64_t per_row = out_row / 16;
+    const int64_t n = rows * per_row;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t r = i / per_row, c = (i % per_row) * 16;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (c < in_row) x = *reinterpret_cast<const u32x4*>(in + r * in_row + c);
+        *reinterpret_cast<u32x4*>(out + r * out_row + c) = x;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_rows(const void* in, int64_t in_row, void* out, int64_t out_row, int64_t rows, hipStream_t s) {
+    if (rows <= 0 || out_row <= 0) return hipSuccess;
+    if (in_row % 16 || out_row % 16) return hipErrorInvalidValue;
+    const int64_t n = rows * (out_row / 16);
+    const int64_t need = (n + 255) / 256;
+    const unsigned blocks = static_cast<unsigned>(need < 65536 ? need : 65536);
+    const unsigned char* src = static_cast<const unsigned char*>(in);
+    unsigned char* dst = static_cast<unsigned char*>(out);
+    void* args[] = {&src, &in_row, &dst, &out_row, &rows};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&copy_rows), dim3(blocks), dim3(256), args, 0, s);
+}
 
 hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s) {
     return io_bf16 ? conv_dispatch<uint16_t>(a, s) : conv_dispatch<float>(a, s);

@@ -1,0 +1,59 @@
+"""bf16 heads with dk < 128 in gdn_chunk_fwd: the dk = 128 matrix-core kernels on q and k
+zero-padded to 128 columns and h0 to 128 rows. Checked against the fp64 oracle (the pages'
+1e-2 bound, issue #320 section 4.2), and bit for bit against the same call made by hand on
+padded tensors: the padded columns add exact zeros to every product, and the final state's
+padded rows come out zero."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_common import TOL_BF16, dev, np_f64, sync, to_dev
+from helpers import rel_l2
+from linear_attention_06_amd import gdn
+from linear_attention_06_amd.inputs import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, B, T, Hqk, H, dk, dv, valid_len
+    ("d64", 1, 1000, 2, 4, 64, 64, None),
+    ("d32_dv16_padded_rows", 2, 300, 1, 3, 32, 16, 211),
+    ("d16_dv128", 1, 129, 2, 2, 16, 128, None),
+    ("d64_one_chunk_tail", 1, 63, 1, 1, 64, 32, None),
+]
+
+
+def inputs(case):
+    name, B, T, Hqk, H, dk, dv, vl = case
+    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="narrow_" + name, B=B, T=T, Hqk=Hqk, H=H, dk=dk,
+                            dv=dv, io="bf16", h0="normal", seed=300 + dk + dv, valid_len=vl)
+    return make_inputs(w)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_narrow_bf16_heads_run_padded_on_the_matrix_cores(case):
+    name, B, T, Hqk, H, dk, dv, vl = case
+    inp = inputs(case)
+    q, k, v, g, beta, h0, vl_t = to_dev(inp)
+    p = gdn.problem(q, v, vl_t)
+    assert gdn.gdn_kernel_path(p) == "bf16-mfma-padded"
+    o, hT = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, valid_len=vl_t)
+    sync()
+    q64, k64, v64, g64, b64, h064 = inp.f64()
+    o_ref, hT_ref = oracle.gdn_fwd(q64, k64, v64, g64, b64, h064, valid_len=inp.valid_len)
+    for nm, x, r in (("o", o, o_ref), ("hT", hT, hT_ref)):
+        err = rel_l2(np_f64(x), r)
+        print("%s %s rel-L2 %.3e" % (name, nm, err))
+        assert err <= TOL_BF16, "%s %s rel-L2 %.3e" % (name, nm, err)
+    # the same forward by hand on padded tensors through the dk = 128 path
+    pad = lambda x: torch.nn.functional.pad(x, (0, 128 - dk)).contiguous()
+    h0p = torch.nn.functional.pad(h0, (0, 0, 0, 128 - dk)).contiguous()
+    assert gdn.gdn_kernel_path(gdn.problem(pad(q), v, vl_t)) == "bf16-mfma"
+    o2, hT2 = gdn.gdn_chunk_fwd(pad(q), pad(k), v, g, beta, h0p, valid_len=vl_t)
+    sync()
+    assert torch.equal(o, o2), "o differs from the hand-padded call"
+    assert torch.equal(hT, hT2[:, :, :dk]), "hT differs from the hand-padded call"
+    assert int(torch.count_nonzero(hT2[:, :, dk:])) == 0, "padded state rows are not zero"

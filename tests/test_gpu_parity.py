@@ -74,12 +74,13 @@ def test_stateless_8k_matches_oracle():
 
 @pytest.mark.parametrize("d,io", [(64, "bf16"), (128, "f32")], ids=["bf16_d64", "f32_d128"])
 def test_vector_path_full_size_matches_oracle(d, io):
-    """The stateless 8K workload's shapes on the fp32 vector-ALU kernels (heads of 64 in
-    bf16, and fp32 inputs): the sizes bench.py times for that path."""
+    """The stateless 8K workload's shapes off the d = 128 bf16 path (heads of 64 in bf16, run
+    by gdn_chunk_fwd on the matrix cores with q and k padded to 128 columns, and fp32 inputs on
+    the fp32 vector-ALU kernels): the sizes bench.py times for those paths."""
     w = dataclasses.replace(WORKLOADS["stateless_8k"], name="vector_%s_d%d" % (io, d), dk=d, dv=d, io=io)
     inp = make_inputs(w)
     q, k, v, g, beta, _, _ = to_dev(inp)
-    assert gdn.gdn_kernel_path(gdn.problem(q, v)) == "f32-valu"
+    assert gdn.gdn_kernel_path(gdn.problem(q, v)) == ("bf16-mfma-padded" if io == "bf16" else "f32-valu")
     q64, k64, v64, g64, b64, _ = inp.f64()
     o_ref, hT_ref = oracle.gdn_fwd(q64, k64, v64, g64, b64, None)
     o, hT = gdn.gdn_chunk_fwd(q, k, v, g, beta, None)
