@@ -236,7 +236,10 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
  * chunk form's products on bf16 MFMAs with fp32 accumulation, relative error a few 1e-3,
  * within the bf16 bound issue #320 section 4.2 states for gradients): workspace per
  * (b, h, 64-token chunk) of 105 KiB (the prepare pass's records, the state entering the chunk
- * and the gradient of the state leaving it, bf16). Every other problem runs the fp32
+ * and the gradient of the state leaving it, bf16). bf16 inputs with dk or dv under 128 and
+ * T >= 256 run the same backward on copies of q, k, v, d_o zero-padded to 128 columns and
+ * of h0, dhT padded to 128 x 128 blocks, in the workspace (the padded columns add exact
+ * zeros; the gradients are cut back to dk and dv). Every other problem runs the fp32
  * token-level backward on the vector ALUs, with the forward state recomputed from
  * checkpoints every 8 tokens (workspace 8 B H ceil(T/64) dk dv + B T H (dv/16) 2 (dk + 1)
  * fp32). ws must be 256-byte aligned and at least gdn_chunk_bwd_workspace() bytes; results

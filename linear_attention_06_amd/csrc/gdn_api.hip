@@ -639,6 +639,85 @@ gdn_status run_bwd_mfma(const gdn_problem& p, const BwdMfmaPlan& pl, const void*
     return run_bwd_from_saved(p, pl, q, k, v, g, beta, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws, s);
 }
 
+// The backward of bf16 problems with dk or dv under 128 on the matrix cores: the chunked
+// backward of the problem padded to dk = dv = 128 (q, k, v, d_o zero-padded to 128 columns,
+// h0 and dhT to 128 x 128 blocks), whose gradients in the padded columns are cut off. The
+// padded columns add exact zeros to every product and sum, so the kept gradients are those
+// of the unpadded problem, at the bf16 operand precision of that backward. Rows shorter than
+// kPadBwdMinT tokens keep the fp32 token-level backward: it costs little there, and a few
+// tokens' gradients can cancel to a small fraction of their terms, where the bf16-rounded
+// operands of the chunked backward would leave a large relative error (a one-token row:
+// 0.27 on dk, whose norm was 4e-4 of dq's).
+constexpr int32_t kPadBwdMinT = 256;
+gdn_problem padded_bwd_problem(const gdn_problem& p) {
+    gdn_problem w = p;
+    w.dk = 128;
+    w.dv = 128;
+    return w;
+}
+bool use_bwd_mfma_padded(const gdn_problem& p) {
+    return p.io_dtype == GDN_BF16 && (p.dk < 128 || p.dv < 128) && p.T >= kPadBwdMinT &&
+           use_bwd_mfma(padded_bwd_problem(p));
+}
+
+struct BwdPadPlan {
+    BwdMfmaPlan bwd;
+    size_t q_off = 0, k_off = 0, v_off = 0, do_off = 0, h0_off = 0, dhT_off = 0, dh0_off = 0;
+    size_t dq_off = 0, dk_off = 0, dv_off = 0, bytes = 0;
+};
+
+BwdPadPlan make_bwd_pad_plan(const gdn_problem& p) {
+    BwdPadPlan pp;
+    pp.bwd = make_bwd_mfma_plan(padded_bwd_problem(p));
+    const size_t tq = static_cast<size_t>(p.B) * p.T * p.Hqk, tv = static_cast<size_t>(p.B) * p.T * p.H;
+    const size_t st = align256(static_cast<size_t>(p.B) * p.H * 128 * 128 * 4);
+    size_t off = align256(pp.bwd.bytes);
+    pp.q_off = off; off += align256(tq * 256);
+    pp.k_off = off; off += align256(tq * 256);
+    pp.v_off = off; off += align256(tv * 256);
+    pp.do_off = off; off += align256(tv * 256);
+    pp.h0_off = off; off += st;
+    pp.dhT_off = off; off += st;
+    pp.dh0_off = off; off += st;
+    pp.dq_off = off; off += align256(tq * 512);
+    pp.dk_off = off; off += align256(tq * 512);
+    pp.dv_off = off; off += align256(tv * 512);
+    pp.bytes = off;
+    return pp;
+}
+
+gdn_status run_bwd_padded(const gdn_problem& p, const BwdPadPlan& pp, const void* q, const void* k, const void* v,
+                          const float* g, const float* beta, const float* h0, const void* d_o, const float* dhT,
+                          float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws,
+                          hipStream_t s) {
+    if (p.B == 0) return GDN_OK;
+    char* base = static_cast<char*>(ws);
+    const int64_t tq = static_cast<int64_t>(p.B) * p.T * p.Hqk, tv = static_cast<int64_t>(p.B) * p.T * p.H;
+    const int64_t nbh = static_cast<int64_t>(p.B) * p.H;
+    const int64_t kb = p.dk * 2, vb = p.dv * 2, kf = p.dk * 4, vf = p.dv * 4;
+    hipError_t e = gdn::launch_copy_rows(q, kb, base + pp.q_off, 256, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(k, kb, base + pp.k_off, 256, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(v, vb, base + pp.v_off, 256, tv, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(d_o, vb, base + pp.do_off, 256, tv, s);
+    if (e == hipSuccess && h0) e = gdn::launch_copy_blocks(h0, p.dk, vf, base + pp.h0_off, 128, 512, nbh, s);
+    if (e == hipSuccess && dhT) e = gdn::launch_copy_blocks(dhT, p.dk, vf, base + pp.dhT_off, 128, 512, nbh, s);
+    if (e != hipSuccess) return hip_fail(e, "padding copy launch");
+    float* dq_p = reinterpret_cast<float*>(base + pp.dq_off);
+    float* dk_p = reinterpret_cast<float*>(base + pp.dk_off);
+    float* dv_p = reinterpret_cast<float*>(base + pp.dv_off);
+    float* dh0_p = dh0 ? reinterpret_cast<float*>(base + pp.dh0_off) : nullptr;
+    gdn_status st = run_bwd_mfma(padded_bwd_problem(p), pp.bwd, base + pp.q_off, base + pp.k_off, base + pp.v_off, g,
+                                 beta, h0 ? reinterpret_cast<const float*>(base + pp.h0_off) : nullptr,
+                                 base + pp.do_off, dhT ? reinterpret_cast<const float*>(base + pp.dhT_off) : nullptr,
+                                 dq_p, dk_p, dv_p, dg, dbeta, dh0_p, ws, s);
+    if (st != GDN_OK) return st;
+    e = gdn::launch_copy_rows(dq_p, 512, dq, kf, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(dk_p, 512, dk, kf, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(dv_p, 512, dv, vf, tv, s);
+    if (e == hipSuccess && dh0) e = gdn::launch_copy_blocks(dh0_p, 128, 512, dh0, p.dk, vf, nbh, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "gradient copy launch");
+}
+
 // The backward through the segment calls on the matrix cores: the P segments of each of the
 // B rows run as B * P rows of their own (the token-major tensors [B, T, ...] are
 // [B * P, L, ...] as they lie), each from its own incoming state; the state blocks move
@@ -697,7 +776,8 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_problem* p, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
-    *bytes = use_bwd_mfma(*p) ? make_bwd_mfma_plan(*p).bytes : make_bwd_plan(*p).bytes;
+    *bytes = use_bwd_mfma(*p) ? make_bwd_mfma_plan(*p).bytes
+                              : (use_bwd_mfma_padded(*p) ? make_bwd_pad_plan(*p).bytes : make_bwd_plan(*p).bytes);
     return GDN_OK;
 }
 
@@ -720,6 +800,15 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
             if (p->B == 0) return GDN_OK;
             return run_bwd_mfma(*p, pl, q, k, v, g, beta, h0, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
                                 static_cast<hipStream_t>(stream));
+        }
+        if (use_bwd_mfma_padded(*p)) {
+            const BwdPadPlan pp = make_bwd_pad_plan(*p);
+            Plan need;
+            need.bytes = pp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            return run_bwd_padded(*p, pp, q, k, v, g, beta, h0, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
+                                  static_cast<hipStream_t>(stream));
         }
         const BwdPlan pl = make_bwd_plan(*p);
         st = check_bwd_ws(pl, ws, ws_bytes);

@@ -292,5 +292,9 @@ hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool io_bf16, hipStream_t s);
 // rows of in_row bytes into rows of out_row bytes, zero-padded or cut (multiples of 16)
 hipError_t launch_copy_rows(const void* in, int64_t in_row, void* out, int64_t out_row, int64_t rows, hipStream_t s);
+// nblk blocks of in_rows x in_row bytes into blocks of out_rows x out_row bytes, zero-padded
+// or cut in both directions (row sizes multiples of 16)
+hipError_t launch_copy_blocks(const void* in, int64_t in_rows, int64_t in_row, void* out, int64_t out_rows,
+                              int64_t out_row, int64_t nblk, hipStream_t s);
 
 }  // namespace gdn

@@ -201,34 +201,41 @@ hipError_t norm_dispatch(const NormArgs& a, hipStream_t s) {
     return hipLaunchKernel(fn, dim3(blocks), dim3(256), args, 0, s);
 }
 
-// Rows of in_row bytes copied into rows of out_row bytes (both multiples of 16), 16 bytes a
-// thread: the part of an output row past in_row is zero (padding), and an input row longer
-// than out_row is cut (cropping).
-__global__ __launch_bounds__(256) void copy_rows(const unsigned char* in, int64_t in_row, unsigned char* out,
-                                                 int64_t out_row, int64_t rows) {
-    const int64_t per_row = out_row / 16;
-    const int64_t n = rows * per_row;
+// nblk blocks of in_rows rows of in_row bytes copied into blocks of out_rows rows of out_row
+// bytes (row sizes multiples of 16), 16 bytes a thread: output rows and row parts past the
+// input's are zero (padding), input rows and row parts past the output's are dropped
+// (cropping).
+__global__ __launch_bounds__(256) void copy_blocks(const unsigned char* in, int64_t in_rows, int64_t in_row,
+                                                   unsigned char* out, int64_t out_rows, int64_t out_row,
+                                                   int64_t nblk) {
+    const int64_t per_row = out_row / 16, per_blk = out_rows * per_row;
+    const int64_t n = nblk * per_blk;
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const int64_t r = i / per_row, c = (i % per_row) * 16;
+        const int64_t blk = i / per_blk, e = i % per_blk, r = e / per_row, c = (e % per_row) * 16;
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (c < in_row) x = *reinterpret_cast<const u32x4*>(in + r * in_row + c);
-        *reinterpret_cast<u32x4*>(out + r * out_row + c) = x;
+        if (r < in_rows && c < in_row) x = *reinterpret_cast<const u32x4*>(in + (blk * in_rows + r) * in_row + c);
+        *reinterpret_cast<u32x4*>(out + (blk * out_rows + r) * out_row + c) = x;
     }
 }
 
 }  // namespace
 
-hipError_t launch_copy_rows(const void* in, int64_t in_row, void* out, int64_t out_row, int64_t rows, hipStream_t s) {
-    if (rows <= 0 || out_row <= 0) return hipSuccess;
+hipError_t launch_copy_blocks(const void* in, int64_t in_rows, int64_t in_row, void* out, int64_t out_rows,
+                              int64_t out_row, int64_t nblk, hipStream_t s) {
+    if (nblk <= 0 || out_rows <= 0 || out_row <= 0) return hipSuccess;
     if (in_row % 16 || out_row % 16) return hipErrorInvalidValue;
-    const int64_t n = rows * (out_row / 16);
+    const int64_t n = nblk * out_rows * (out_row / 16);
     const int64_t need = (n + 255) / 256;
     const unsigned blocks = static_cast<unsigned>(need < 65536 ? need : 65536);
     const unsigned char* src = static_cast<const unsigned char*>(in);
     unsigned char* dst = static_cast<unsigned char*>(out);
-    void* args[] = {&src, &in_row, &dst, &out_row, &rows};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&copy_rows), dim3(blocks), dim3(256), args, 0, s);
+    void* args[] = {&src, &in_rows, &in_row, &dst, &out_rows, &out_row, &nblk};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&copy_blocks), dim3(blocks), dim3(256), args, 0, s);
+}
+
+hipError_t launch_copy_rows(const void* in, int64_t in_row, void* out, int64_t out_row, int64_t rows, hipStream_t s) {
+    return launch_copy_blocks(in, 1, in_row, out, 1, out_row, rows, s);
 }
 
 hipError_t launch_causal_conv1d(const ConvArgs& a, bool io_bf16, hipStream_t s) {

@@ -3,10 +3,10 @@ same seeded inputs: all six gradients, with and without initial state and final-
 gradient, padded rows, grouped heads, bf16 and fp32 inputs, head dims 16 to 128, and
 lengths that end inside a chunk.
 
-bf16 inputs with heads of 128 run the chunked matrix-core backward (bf16 operands, fp32
-accumulation) and are held to the pages' bf16 bound on gradients (hyper-parallel issue
-#320, section 4.2); every other problem runs the fp32 token-level backward, held to the
-fp32 bound."""
+bf16 inputs with heads of 128 (and narrower heads on rows of at least 256 tokens, padded to
+128) run the chunked matrix-core backward (bf16 operands, fp32 accumulation) and are held to
+the pages' bf16 bound on gradients (hyper-parallel issue #320, section 4.2); every other
+problem runs the fp32 token-level backward, held to the fp32 bound."""
 import dataclasses
 
 import numpy as np
@@ -57,7 +57,7 @@ def test_backward_matches_oracle(case):
     qf, kf, vf, gf, bf, h0f = inp.f64()
     ref = backward.gdn_bwd(qf, kf, vf, gf, bf, h0f if with_h0 else None, d_o.astype(np.float64),
                            None if dhT is None else dhT.astype(np.float64), inp.valid_len)
-    tol = TOL_BF16 if (io == "bf16" and d == 128) else TOL_F32
+    tol = TOL_BF16 if (io == "bf16" and (d == 128 or T >= 256)) else TOL_F32
     for nm, x, r in zip(NAMES, got, ref):
         err = rel_l2(np_f64(x), r)
         print("%s %s rel-L2 %.3e" % (name, nm, err))

@@ -1,8 +1,9 @@
-"""bf16 heads with dk < 128 in gdn_chunk_fwd: the dk = 128 matrix-core kernels on q and k
-zero-padded to 128 columns and h0 to 128 rows. Checked against the fp64 oracle (the pages'
-1e-2 bound, issue #320 section 4.2), and bit for bit against the same call made by hand on
-padded tensors: the padded columns add exact zeros to every product, and the final state's
-padded rows come out zero."""
+"""bf16 heads under 128: gdn_chunk_fwd runs the dk = 128 matrix-core kernels on q and k
+zero-padded to 128 columns and h0 to 128 rows, and gdn_chunk_bwd the chunked matrix-core
+backward on q, k, v, d_o padded to 128 columns and h0, dhT to 128 x 128 blocks. Checked
+against the fp64 oracles (the pages' 1e-2 bound, issue #320 section 4.2), and bit for bit
+against the same calls made by hand on padded tensors: the padded columns add exact zeros to
+every product, and the final state's padded rows come out zero."""
 import dataclasses
 
 import numpy as np
@@ -10,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import backward
 from gpu_common import TOL_BF16, dev, np_f64, sync, to_dev
 from helpers import rel_l2
 from linear_attention_06_amd import gdn
@@ -57,3 +59,39 @@ def test_narrow_bf16_heads_run_padded_on_the_matrix_cores(case):
     assert torch.equal(o, o2), "o differs from the hand-padded call"
     assert torch.equal(hT, hT2[:, :, :dk]), "hT differs from the hand-padded call"
     assert int(torch.count_nonzero(hT2[:, :, dk:])) == 0, "padded state rows are not zero"
+
+
+# the backward pads rows of at least 256 tokens (shorter ones keep the fp32 token-level kernels)
+BWD_CASES = [
+    ("d64", 1, 1000, 2, 4, 64, 64, None),
+    ("d32_dv16_padded_rows", 2, 300, 1, 3, 32, 16, 211),
+    ("d128_dv32", 1, 257, 2, 2, 128, 32, None),
+    ("d16_dv128_ratio1", 1, 640, 2, 2, 16, 128, None),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_narrow_bf16_heads_backward_runs_padded_on_the_matrix_cores(case):
+    name, B, T, Hqk, H, dk, dv, vl = case
+    inp = inputs(case)
+    q, k, v, g, beta, h0, vl_t = to_dev(inp)
+    rng = np.random.default_rng(400 + dk)
+    d_o = torch.from_numpy(rng.standard_normal(tuple(v.shape)).astype(np.float32)).to(dev()).to(torch.bfloat16)
+    dhT = torch.from_numpy(0.1 * rng.standard_normal((B, H, dk, dv)).astype(np.float32)).to(dev())
+    got = gdn.gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, dhT, vl_t)
+    sync()
+    q64, k64, v64, g64, b64, h064 = inp.f64()
+    ref = backward.gdn_bwd(q64, k64, v64, g64, b64, h064, np_f64(d_o), np_f64(dhT), inp.valid_len)
+    for nm, x, r in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, ref):
+        err = rel_l2(np_f64(x), r)
+        print("%s %s rel-L2 %.3e" % (name, nm, err))
+        assert err <= TOL_BF16, "%s %s rel-L2 %.3e" % (name, nm, err)
+    # the same backward by hand on padded tensors through the dk = dv = 128 path
+    pad = lambda x, n: torch.nn.functional.pad(x, (0, 128 - n)).contiguous()
+    blk = lambda x: torch.nn.functional.pad(x, (0, 128 - dv, 0, 128 - dk)).contiguous()
+    hand = gdn.gdn_chunk_bwd(pad(q, dk), pad(k, dk), pad(v, dv), g, beta, blk(h0), pad(d_o, dv), blk(dhT), vl_t)
+    sync()
+    for nm, x, y in zip(("dq", "dk", "dv", "dg", "dbeta"), got, hand):
+        w = x.shape[-1]
+        assert torch.equal(x, y[..., :w]), "%s differs from the hand-padded call" % nm
+    assert torch.equal(got[5], hand[5][:, :, :dk, :dv]), "dh0 differs from the hand-padded call"

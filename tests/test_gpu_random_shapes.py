@@ -62,14 +62,14 @@ def test_random_forward_and_backward(seed):
     o_ref, hT_ref = oracle.gdn_fwd(qf, kf, vf, gf, bf, h0f, valid_len=inp.valid_len)
     check(o, o_ref, tol, "o")
     check(hT, hT_ref, tol, "hT")
-    # backward: bf16 heads of 128 run the chunked matrix-core backward (bf16 operands),
-    # every other shape the fp32 token-level backward (the fp32 tolerance whatever the input
-    # dtype). The pages' bf16 bound on gradients (issue #320 section 4.2) is stated at their
+    # backward: bf16 heads of 128, and narrower bf16 heads on rows of at least 256 tokens
+    # (padded to 128), run the chunked matrix-core backward (bf16 operands); everything else
+    # the fp32 token-level backward (the fp32 tolerance whatever the input dtype). The pages' bf16 bound on gradients (issue #320 section 4.2) is stated at their
     # sizes (8K-32K tokens); this sweep draws rows of one token, whose dq and dbeta are each a
     # single dot product of bf16-rounded operands (U, dU, X), so that cancellation can
     # multiply the 2^-9 rounding several-fold (2.0e-2 measured on a one-token row). The sweep
     # holds that path to TOL_BWD_SMALL; the full-size and per-path backward tests hold it to 1e-2.
-    btol = TOL_BWD_SMALL if (w.io == "bf16" and w.dk == 128 and w.dv == 128) else TOL_F32
+    btol = TOL_BWD_SMALL if (w.io == "bf16" and ((w.dk == 128 and w.dv == 128) or w.T >= 256)) else TOL_F32
     rng = np.random.default_rng(seed)
     d_o = rng.standard_normal(v.shape).astype(np.float32)
     if w.io == "bf16":
