@@ -479,9 +479,9 @@ def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
 
 
 def vector_path_timing(gdn, workloads, make_inputs, dev, stream, timed):
-    """gdn_chunk_fwd on the problems the matrix-core kernels do not take, which run the fp32
-    vector-ALU kernels: the stateless 8K workload's shapes with heads of 64 (bf16) and with
-    fp32 inputs (heads of 128)."""
+    """gdn_chunk_fwd off the d = 128 bf16 shapes, on the stateless 8K workload's sizes: heads
+    of 64 in bf16 (the matrix-core kernels on q and k padded to 128 columns) and fp32 inputs
+    with heads of 128 (the fp32 vector-ALU kernels); kernel_path names the path."""
     import dataclasses
 
     import torch
