@@ -268,3 +268,38 @@ def test_noalloc_forward_rejects_oversized_problems_before_any_hip_call():
     # a problem of no batch rows is a no-op that needs no device
     assert gdn.lib().gdn_chunk_fwd_noalloc(ctypes.byref(P(B=0)), None, None, None, None, None, None, None,
                                            None, None) == gdn.GDN_OK
+
+
+def test_padded_narrow_head_workspaces_and_checks():
+    """bf16 heads under 128: the forward's workspace holds the dk = 128 problem's records plus
+    q and k padded to 128 columns and two 128-row state blocks; the backward pads from 256
+    tokens per row on (shorter rows keep the token-level backward's workspace); the checks
+    still come before any launch."""
+    L = gdn.lib()
+    n = ctypes.c_size_t(0)
+    B, T, H, Hqk, dk, dv = 2, 300, 4, 2, 64, 32
+    p = P(B=B, T=T, H=H, Hqk=Hqk, dk=dk, dv=dv, io_dtype=gdn.GDN_BF16)
+    p128 = P(B=B, T=T, H=H, Hqk=Hqk, dk=128, dv=dv, io_dtype=gdn.GDN_BF16)
+    st, n_pad = ws_status(p)
+    st128, n128 = ws_status(p128)
+    assert st == gdn.GDN_OK and st128 == gdn.GDN_OK
+    assert n_pad >= n128 + 2 * B * T * Hqk * 128 * 2 + 2 * B * H * 128 * dv * 4
+    assert call_fwd(p, ws=256, nbytes=n_pad - 1) == gdn.GDN_EWORKSPACE
+    assert call_fwd(p, q=None, ws=256, nbytes=n_pad) == gdn.GDN_EINVAL
+    # the fp32 problem of the same shape keeps the vector-ALU workspace
+    assert ws_status(P(B=B, T=T, H=H, Hqk=Hqk, dk=dk, dv=dv))[1] < n_pad
+    # backward: padded (T >= 256) needs the dk = dv = 128 problem's workspace and more
+    assert L.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)) == gdn.GDN_OK
+    n_bwd = n.value
+    full = P(B=B, T=T, H=H, Hqk=Hqk, dk=128, dv=128, io_dtype=gdn.GDN_BF16)
+    assert L.gdn_chunk_bwd_workspace(ctypes.byref(full), ctypes.byref(n)) == gdn.GDN_OK
+    assert n_bwd > n.value
+    short = P(B=B, T=100, H=H, Hqk=Hqk, dk=dk, dv=dv, io_dtype=gdn.GDN_BF16)
+    short_f32 = P(B=B, T=100, H=H, Hqk=Hqk, dk=dk, dv=dv)
+    assert L.gdn_chunk_bwd_workspace(ctypes.byref(short), ctypes.byref(n)) == gdn.GDN_OK
+    n_short = n.value
+    assert L.gdn_chunk_bwd_workspace(ctypes.byref(short_f32), ctypes.byref(n)) == gdn.GDN_OK
+    assert n_short == n.value
+    vp = ctypes.c_void_p
+    args = [vp(1)] * 5 + [None, vp(1), None] + [vp(1)] * 5 + [None]
+    assert L.gdn_chunk_bwd(ctypes.byref(p), *args, vp(256), n_bwd - 1, None) == gdn.GDN_EWORKSPACE
