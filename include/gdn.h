@@ -263,8 +263,12 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p,
  *   gdn_chunk_bwd_saved: gdn_chunk_bwd (the same gradients, bit for bit) from that ws, for
  *     the same problem and inputs (q, k, v, g, beta unchanged since the forward; h0 is not
  *     needed again: the kept states hold it).
- * Only on the chunked matrix-core path (bf16 inputs, dk = dv = 128, gdn_chunk_bwd's
- * condition); other problems get GDN_EUNSUPPORTED. ws: 256-byte aligned, at least
+ * Only on the problems gdn_chunk_bwd runs on the chunked matrix-core kernels: bf16 inputs
+ * with dk = dv = 128, or bf16 heads with dk or dv under 128 on rows of 256 tokens or more
+ * (then q, k, v and h0 are padded to 128 columns / 128 x 128 blocks in ws, the padded problem's
+ * forward is kept, o and hT are cut back, and the backward pads d_o and dhT and cuts the
+ * gradients back, as gdn_chunk_bwd does); other problems get GDN_EUNSUPPORTED. ws: 256-byte
+ * aligned, at least
  * gdn_chunk_fwd_save_workspace() bytes (the size gdn_chunk_bwd_workspace gives for the same
  * problem), owned by the caller between the two calls. Arguments as for gdn_chunk_fwd and
  * gdn_chunk_bwd.

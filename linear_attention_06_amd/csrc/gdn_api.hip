@@ -686,6 +686,60 @@ BwdPadPlan make_bwd_pad_plan(const gdn_problem& p) {
     return pp;
 }
 
+// The kept forward of a padded problem: q, k, v and h0 padded into the workspace (where the
+// backward from it reads them), the dk = dv = 128 forward that keeps its records and states,
+// o and the final state cut back. The padded o and final state pass through the slots of the
+// padded d_o and dhT, which the forward does not use.
+gdn_status run_fwd_save_padded(const gdn_problem& p, const BwdPadPlan& pp, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, const float* h0, void* o, float* hT,
+                               void* ws, hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    const int64_t tq = static_cast<int64_t>(p.B) * p.T * p.Hqk, tv = static_cast<int64_t>(p.B) * p.T * p.H;
+    const int64_t nbh = static_cast<int64_t>(p.B) * p.H, vf = p.dv * 4;
+    hipError_t e = gdn::launch_copy_rows(q, p.dk * 2, base + pp.q_off, 256, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(k, p.dk * 2, base + pp.k_off, 256, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(v, p.dv * 2, base + pp.v_off, 256, tv, s);
+    if (e == hipSuccess && h0) e = gdn::launch_copy_blocks(h0, p.dk, vf, base + pp.h0_off, 128, 512, nbh, s);
+    if (e != hipSuccess) return hip_fail(e, "padding copy launch");
+    const gdn_problem w = padded_bwd_problem(p);
+    float* hT_p = hT ? reinterpret_cast<float*>(base + pp.dhT_off) : nullptr;
+    const float* h0_p = h0 ? reinterpret_cast<const float*>(base + pp.h0_off) : nullptr;
+    gdn_status st = run_fwd_keep(w, pp.bwd, base + pp.q_off, base + pp.k_off, base + pp.v_off, g, beta, h0_p,
+                                 base + pp.do_off, hT_p, ws, s);
+    if (st != GDN_OK) return st;
+    e = gdn::launch_copy_rows(base + pp.do_off, 256, o, p.dv * 2, tv, s);
+    if (e == hipSuccess && hT) e = gdn::launch_copy_blocks(hT_p, 128, 512, hT, p.dk, vf, nbh, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "output copy launch");
+}
+
+// The backward from a padded kept forward: d_o and dhT padded, the backward from the kept
+// records and states on the padded q, k, v the forward left in the workspace, the gradients
+// cut back.
+gdn_status run_bwd_saved_padded(const gdn_problem& p, const BwdPadPlan& pp, const float* g, const float* beta,
+                                const void* d_o, const float* dhT, float* dq, float* dk, float* dv, float* dg,
+                                float* dbeta, float* dh0, void* ws, hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    const int64_t tq = static_cast<int64_t>(p.B) * p.T * p.Hqk, tv = static_cast<int64_t>(p.B) * p.T * p.H;
+    const int64_t nbh = static_cast<int64_t>(p.B) * p.H, kf = p.dk * 4, vf = p.dv * 4;
+    hipError_t e = gdn::launch_copy_rows(d_o, p.dv * 2, base + pp.do_off, 256, tv, s);
+    if (e == hipSuccess && dhT) e = gdn::launch_copy_blocks(dhT, p.dk, vf, base + pp.dhT_off, 128, 512, nbh, s);
+    if (e != hipSuccess) return hip_fail(e, "padding copy launch");
+    float* dq_p = reinterpret_cast<float*>(base + pp.dq_off);
+    float* dk_p = reinterpret_cast<float*>(base + pp.dk_off);
+    float* dv_p = reinterpret_cast<float*>(base + pp.dv_off);
+    float* dh0_p = dh0 ? reinterpret_cast<float*>(base + pp.dh0_off) : nullptr;
+    gdn_status st = run_bwd_from_saved(padded_bwd_problem(p), pp.bwd, base + pp.q_off, base + pp.k_off,
+                                       base + pp.v_off, g, beta, base + pp.do_off,
+                                       dhT ? reinterpret_cast<const float*>(base + pp.dhT_off) : nullptr, dq_p, dk_p,
+                                       dv_p, dg, dbeta, dh0_p, ws, s);
+    if (st != GDN_OK) return st;
+    e = gdn::launch_copy_rows(dq_p, 512, dq, kf, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(dk_p, 512, dk, kf, tq, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(dv_p, 512, dv, vf, tv, s);
+    if (e == hipSuccess && dh0) e = gdn::launch_copy_blocks(dh0_p, 128, 512, dh0, p.dk, vf, nbh, s);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "gradient copy launch");
+}
+
 gdn_status run_bwd_padded(const gdn_problem& p, const BwdPadPlan& pp, const void* q, const void* k, const void* v,
                           const float* g, const float* beta, const float* h0, const void* d_o, const float* dhT,
                           float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0, void* ws,
@@ -828,8 +882,13 @@ gdn_status gdn_chunk_fwd_save_workspace(const gdn_problem* p, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    if (use_bwd_mfma_padded(*p)) {
+        *bytes = make_bwd_pad_plan(*p).bytes;
+        return GDN_OK;
+    }
     if (!use_bwd_mfma(*p))
-        return fail(GDN_EUNSUPPORTED, "keeping the forward for the backward needs bf16 inputs with dk = dv = 128");
+        return fail(GDN_EUNSUPPORTED, "keeping the forward for the backward needs the chunked matrix-core backward's "
+                                      "problems (bf16 inputs, dk = dv = 128, or narrower heads on rows of 256 tokens or more)");
     *bytes = make_bwd_mfma_plan(*p).bytes;
     return GDN_OK;
 }
@@ -840,8 +899,18 @@ gdn_status gdn_chunk_fwd_save(const gdn_problem* p, const void* q, const void* k
     try {
         gdn_status st = check_fwd_args(p, q, k, v, g, beta, o);
         if (st != GDN_OK) return st;
+        if (use_bwd_mfma_padded(*p)) {
+            const BwdPadPlan pp = make_bwd_pad_plan(*p);
+            Plan need;
+            need.bytes = pp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            if (p->B == 0) return GDN_OK;
+            return run_fwd_save_padded(*p, pp, q, k, v, g, beta, h0, o, hT, ws, static_cast<hipStream_t>(stream));
+        }
         if (!use_bwd_mfma(*p))
-            return fail(GDN_EUNSUPPORTED, "keeping the forward for the backward needs bf16 inputs with dk = dv = 128");
+            return fail(GDN_EUNSUPPORTED, "keeping the forward for the backward needs the chunked matrix-core backward's "
+                                          "problems (bf16 inputs, dk = dv = 128, or narrower heads on rows of 256 tokens or more)");
         const BwdMfmaPlan pl = make_bwd_mfma_plan(*p);
         Plan need;
         need.bytes = pl.bytes;
@@ -867,8 +936,19 @@ gdn_status gdn_chunk_bwd_saved(const gdn_problem* p, const void* q, const void* 
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (use_bwd_mfma_padded(*p)) {
+            const BwdPadPlan pp = make_bwd_pad_plan(*p);
+            Plan need;
+            need.bytes = pp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            if (p->B == 0) return GDN_OK;
+            return run_bwd_saved_padded(*p, pp, g, beta, d_o, dhT, dq, dk, dv, dg, dbeta, dh0, ws,
+                                        static_cast<hipStream_t>(stream));
+        }
         if (!use_bwd_mfma(*p))
-            return fail(GDN_EUNSUPPORTED, "the backward from a kept forward needs bf16 inputs with dk = dv = 128");
+            return fail(GDN_EUNSUPPORTED, "the backward from a kept forward needs the chunked matrix-core backward's "
+                                          "problems (bf16 inputs, dk = dv = 128, or narrower heads on rows of 256 tokens or more)");
         const BwdMfmaPlan pl = make_bwd_mfma_plan(*p);
         Plan need;
         need.bytes = pl.bytes;

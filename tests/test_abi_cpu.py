@@ -207,8 +207,8 @@ def test_backward_argument_checks():
 
 
 def test_saved_forward_argument_checks():
-    """gdn_chunk_fwd_save / gdn_chunk_bwd_saved: only the chunked matrix-core problem, a
-    workspace as large as gdn_chunk_bwd's, and every check before any launch."""
+    """gdn_chunk_fwd_save / gdn_chunk_bwd_saved: only the chunked matrix-core backward's
+    problems, a workspace as large as gdn_chunk_bwd's, and every check before any launch."""
     L = gdn.lib()
     vp = ctypes.c_void_p
     n = ctypes.c_size_t(0)
@@ -231,6 +231,20 @@ def test_saved_forward_argument_checks():
     assert L.gdn_chunk_bwd_saved(ctypes.byref(p), *bad, vp(256), n.value, None) == gdn.GDN_EINVAL
     assert L.gdn_chunk_bwd_saved(ctypes.byref(p), *args, vp(256), n.value - 1, None) == gdn.GDN_EWORKSPACE
     assert L.gdn_chunk_bwd_saved(ctypes.byref(P()), *args, vp(256), 1 << 40, None) == gdn.GDN_EUNSUPPORTED
+    # narrow bf16 heads: kept through the padded problem on rows of 256 tokens or more, with
+    # gdn_chunk_bwd's workspace; shorter rows keep the token-level backward and nothing
+    for T, ok in ((256, True), (1000, True), (255, False)):
+        pn = P(B=2, T=T, H=3, Hqk=1, dk=32, dv=16, io_dtype=gdn.GDN_BF16)
+        st = L.gdn_chunk_fwd_save_workspace(ctypes.byref(pn), ctypes.byref(n))
+        assert st == (gdn.GDN_OK if ok else gdn.GDN_EUNSUPPORTED), T
+        if ok:
+            assert L.gdn_chunk_bwd_workspace(ctypes.byref(pn), ctypes.byref(nb)) == gdn.GDN_OK
+            assert n.value == nb.value
+            assert fwd(pp=pn, nbytes=n.value - 1) == gdn.GDN_EWORKSPACE
+            assert L.gdn_chunk_bwd_saved(ctypes.byref(pn), *args, vp(256), n.value - 1, None) == gdn.GDN_EWORKSPACE
+        else:
+            assert fwd(pp=pn, nbytes=1 << 40) == gdn.GDN_EUNSUPPORTED
+            assert L.gdn_chunk_bwd_saved(ctypes.byref(pn), *args, vp(256), 1 << 40, None) == gdn.GDN_EUNSUPPORTED
 
 
 def test_layer_step_argument_checks():

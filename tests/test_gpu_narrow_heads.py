@@ -95,3 +95,28 @@ def test_narrow_bf16_heads_backward_runs_padded_on_the_matrix_cores(case):
         w = x.shape[-1]
         assert torch.equal(x, y[..., :w]), "%s differs from the hand-padded call" % nm
     assert torch.equal(got[5], hand[5][:, :, :dk, :dv]), "dh0 differs from the hand-padded call"
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_narrow_bf16_heads_kept_forward_matches_the_plain_calls(case):
+    """gdn_chunk_fwd_save on a narrow bf16 head keeps the padded problem's records and
+    states; its o and hT are gdn_chunk_fwd's bit for bit (each value column and each state
+    row of the padded forward is computed as in the forward padded on dk alone), and
+    gdn_chunk_bwd_saved on its workspace gives gdn_chunk_bwd's gradients bit for bit, twice."""
+    name, B, T, Hqk, H, dk, dv, vl = case
+    inp = inputs(case)
+    q, k, v, g, beta, h0, vl_t = to_dev(inp)
+    rng = np.random.default_rng(500 + dk)
+    d_o = torch.from_numpy(rng.standard_normal(tuple(v.shape)).astype(np.float32)).to(dev()).to(torch.bfloat16)
+    dhT = torch.from_numpy(0.1 * rng.standard_normal((B, H, dk, dv)).astype(np.float32)).to(dev())
+    o_ref, hT_ref = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, valid_len=vl_t)
+    ref = gdn.gdn_chunk_bwd(q, k, v, g, beta, h0, d_o, dhT, vl_t)
+    o, hT, ws = gdn.gdn_chunk_fwd_save(q, k, v, g, beta, h0, vl_t)
+    got = gdn.gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, dhT, vl_t)
+    again = gdn.gdn_chunk_bwd_saved(q, k, v, g, beta, d_o, ws, dhT, vl_t)
+    sync()
+    assert torch.equal(o, o_ref), "%s o differs from gdn_chunk_fwd" % name
+    assert torch.equal(hT, hT_ref), "%s hT differs from gdn_chunk_fwd" % name
+    for nm, x, y, z in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, again, ref):
+        assert torch.equal(x, z), "%s %s differs from gdn_chunk_bwd" % (name, nm)
+        assert torch.equal(y, z), "%s %s differs on the second backward" % (name, nm)
