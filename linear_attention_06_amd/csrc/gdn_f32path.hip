@@ -668,6 +668,283 @@ __global__ __launch_bounds__(512) void summary_outer_mfma(ScanBwdArgs a) {
     }
 }
 
+// The state pass for fp32 inputs with dk = 128 on v_mfma_f32_16x16x4_f32 (fp32 products,
+// fp32 accumulation): one block of four waves per (b, h, segment, 16 state columns), the
+// column tiles of one (b, h, segment) on one XCD (the order of the scans above). Wave w
+// keeps rows 32 w .. 32 w + 31 of the state in two accumulator tiles and owns token tile w
+// (tokens 16 w .. 16 w + 15) of every chunk:
+//   P1  K S and Q S of its tokens over all 128 state rows (the state read back from LDS,
+//       transposed), X = V - e^Gam K S;
+//   P2  U = That X over the token tiles up to its own (X exchanged through LDS);
+//   P3  O = e^Gam Q S + P U (U through LDS), and its state rows
+//       S <- e^{Gam_C} S + K^T (e^{Gam_C - Gam} U), the K^T fragments read as single floats
+//       from the row-major K tile (conflict-free at a pitch of 132 floats).
+// Three barriers per chunk; K and Q in LDS, two buffers each, at a pitch of 132 floats.
+// A chunk's ~88 KiB of loads take the CU's load path longer to accept than its products
+// take, and a wave stalls while its loads issue; so they are issued between products: the
+// next chunk's K and Q between P1's (into registers, written to the free LDS buffers in
+// P3), its V, That, P and decay factors between the update's (straight into the registers
+// the next chunk reads; this chunk is done with them). Each k-tile's LDS operands are read
+// during the previous one's products, and the scheduling barriers pin that order.
+// k-step s of a 16x16x4 product has lane (l16, g4) supply contraction index 4 g4 + s of a
+// 16-wide slice, so that one 16-byte LDS read gives a lane its operand for four steps.
+constexpr int kRawBufferWord3 = 0x00020000;   // raw buffer descriptor word 3 on gfx9-family GPUs
+
+template <bool kOut>
+__global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
+    constexpr int KPf = 132, TP = 68, KQT = 64 * KPf;
+    __shared__ __align__(16) float k_s[2 * KQT];
+    __shared__ __align__(16) float q_s[kOut ? 2 * KQT : 4];
+    __shared__ __align__(16) float s_t[16 * KPf];   // the state transposed: S[i][c] at c KPf + i
+    __shared__ __align__(16) float x_t[16 * TP];    // X, U and e^{Gam_C - Gam} U transposed
+    __shared__ __align__(16) float u_t[16 * TP];
+    __shared__ __align__(16) float ug_t[16 * TP];
+
+    const int ncols = a.ncols;
+    int ct, bhi;
+    if (!scan_block(ncols / 16, a.B * a.P * a.H, ct, bhi)) return;
+    const int h = bhi % a.H, bz = bhi / a.H, b = bz / a.P, seg = bz % a.P;
+    const int col0 = 16 * ct;
+    const int hq = h / (a.H / a.Hqk);
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
+    const int64_t nvalid = rs.valid;
+    const float* q = static_cast<const float*>(a.q);
+    const float* k = static_cast<const float*>(a.k);
+    const float* v = static_cast<const float*>(a.v);
+    float* o = static_cast<float*>(a.o);
+    const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+    const int64_t tile = static_cast<int64_t>(128) * ncols;
+    const f32x4s zero = {0.f, 0.f, 0.f, 0.f};
+
+    f32x4s st[2];   // state rows 32 w + 16 rt + 4 g4 + j, column col0 + l16
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 32 * w + 16 * rt + 4 * g4 + j;
+            float s0 = 0.f;
+            if (a.init_mode == kInitLoad) {
+                const int64_t blk = a.s_init_per_segment ? bh * a.P + seg : bh;
+                s0 = a.s_init[blk * tile + static_cast<int64_t>(i) * ncols + col0 + l16];
+            } else if (a.init_mode == kInitIdentity) {
+                s0 = (i == col0 + l16) ? 1.f : 0.f;
+            }
+            st[rt][j] = s0;
+        }
+        *reinterpret_cast<f32x4s*>(s_t + l16 * KPf + 32 * w + 16 * rt + 4 * g4) = st[rt];
+    }
+
+    const int n0 = seg * a.Lc;
+    const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
+
+    // float4 m of K and Q (lane tid) is row (tid + 256 m) / 32, columns 4 ((tid + 256 m) % 32)
+    // .. + 3; addresses of padded tokens are clamped to the row's first token (which exists
+    // whenever the row has a chunk) and their values replaced by zero when stored
+    f32x4s kr[8], qr[8];
+    const auto kq_at = [&](int64_t t0, int m) -> int64_t {
+        const int e = tid + 256 * m, rr = e >> 5;
+        const int64_t tok = t0 + rr < nvalid ? t0 + rr : 0;
+        return ((rs.start + tok) * a.Hqk + hq) * 128 + 4 * (e & 31);
+    };
+    const auto load_k = [&](int64_t t0, int m) { kr[m] = *reinterpret_cast<const f32x4s*>(k + kq_at(t0, m)); };
+    const auto load_q = [&](int64_t t0, int m) {
+        if constexpr (kOut) qr[m] = *reinterpret_cast<const f32x4s*>(q + kq_at(t0, m));
+    };
+    const auto store_kq = [&](int64_t t0, int buf) {
+        float* kb = k_s + buf * KQT;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int e = tid + 256 * m, rr = e >> 5, c4 = 4 * (e & 31);
+            const bool ok = t0 + rr < nvalid;
+            *reinterpret_cast<f32x4s*>(kb + rr * KPf + c4) = ok ? kr[m] : zero;
+            if constexpr (kOut) *reinterpret_cast<f32x4s*>(q_s + buf * KQT + rr * KPf + c4) = ok ? qr[m] : zero;
+        }
+    };
+    // a chunk's V of rows 16 w + 4 g4 + j (replaced by zero past the valid length where it
+    // is used: a select here would wait for the load), That and P rows 16 w + l16, columns
+    // 16 r + 4 g4 .. + 3 for the token tiles r <= w, e^Gam and e^{Gam_C - Gam} of rows
+    // 16 w + 4 g4 .. + 3, and e^{Gam_C}; loaded in four pieces
+    f32x4s tc[4], pc[4], egv, egcv;
+    float vc[4], egC = 1.f;
+    const auto load_rest = [&](int n, int piece) {
+        const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+        const int64_t ch = bh * a.NT + n;
+        if (piece == 0) {
+            const float* gg = a.ws.gates + ch * 128 + 16 * w + 4 * g4;
+            egv = *reinterpret_cast<const f32x4s*>(gg);
+            egcv = *reinterpret_cast<const f32x4s*>(gg + 64);
+            egC = a.ws.gates[ch * 128 + 63];
+        }
+        const int64_t tok = t0 + 16 * w + 4 * g4 + piece;
+        const int64_t tcl = tok < nvalid ? tok : 0;
+        vc[piece] = v ? v[((rs.start + tcl) * a.H + h) * ncols + col0 + l16] : 0.f;
+        if (piece <= w) {
+            const int64_t off = ch * 4096 + (16 * w + l16) * 64 + 16 * piece + 4 * g4;
+            tc[piece] = *reinterpret_cast<const f32x4s*>(static_cast<const float*>(a.ws.that) + off);
+            if constexpr (kOut) pc[piece] = *reinterpret_cast<const f32x4s*>(static_cast<const float*>(a.ws.pmat) + off);
+        }
+    };
+    if (n0 < n1) {
+        const int64_t t0 = static_cast<int64_t>(n0) * kChunk;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            load_k(t0, m);
+            load_q(t0, m);
+        }
+#pragma unroll
+        for (int piece = 0; piece < 4; ++piece) load_rest(n0, piece);
+        store_kq(t0, n0 & 1);
+    }
+    __syncthreads();
+
+    // The loop body has no branches around its loads and stores but wave-uniform ones, so
+    // that the compiler's wait counts stay tight: the last chunk re-fetches itself (into
+    // registers and the free LDS buffers, read by nobody).
+    for (int n = n0; n < n1; ++n) {
+        const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+        const int nf = n + 1 < n1 ? n + 1 : n;
+        const int64_t tf = static_cast<int64_t>(nf) * kChunk;
+        const float* kb = k_s + (n & 1) * KQT;
+        const float* qb = q_s + (n & 1) * KQT;
+
+        // P1: K S and Q S of token tile w, the next chunk's K and Q loads between the
+        // products; even and odd k-tiles accumulate in separate chains
+        f32x4s ks2[2] = {zero, zero}, qs2[2] = {zero, zero};
+        f32x4s sb[2], ka[2], qa[2];
+        const auto rd1 = [&](int t, int i) {
+            sb[i] = *reinterpret_cast<const f32x4s*>(s_t + l16 * KPf + 16 * t + 4 * g4);
+            ka[i] = *reinterpret_cast<const f32x4s*>(kb + (16 * w + l16) * KPf + 16 * t + 4 * g4);
+            if constexpr (kOut) qa[i] = *reinterpret_cast<const f32x4s*>(qb + (16 * w + l16) * KPf + 16 * t + 4 * g4);
+        };
+        rd1(0, 0);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int i = t & 1;
+            if (t + 1 < 8) rd1(t + 1, i ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                ks2[i] = mfma_f32_4(ka[i][s], sb[i][s], ks2[i]);
+                if constexpr (kOut) qs2[i] = mfma_f32_4(qa[i][s], sb[i][s], qs2[i]);
+                if (s == 0) load_k(tf, t);
+                if (s == 2) load_q(tf, t);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        const f32x4s ks = ks2[0] + ks2[1], qs = qs2[0] + qs2[1];
+        f32x4s xw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xw[j] = (t0 + 16 * w + 4 * g4 + j < nvalid ? vc[j] : 0.f) - egv[j] * ks[j];
+        *reinterpret_cast<f32x4s*>(x_t + l16 * TP + 16 * w + 4 * g4) = xw;
+        __syncthreads();
+
+        // P2: U of token tile w (all four X tiles read at once; the products stop at w;
+        // even and odd token tiles in two chains)
+        f32x4s u2[2] = {zero, zero}, xb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xb[r] = *reinterpret_cast<const f32x4s*>(x_t + l16 * TP + 16 * r + 4 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (r <= w) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) u2[r & 1] = mfma_f32_4(tc[r][s], xb[r][s], u2[r & 1]);
+            }
+        }
+        const f32x4s u = u2[0] + u2[1];
+        *reinterpret_cast<f32x4s*>(u_t + l16 * TP + 16 * w + 4 * g4) = u;
+        *reinterpret_cast<f32x4s*>(ug_t + l16 * TP + 16 * w + 4 * g4) = egcv * u;
+        __syncthreads();
+
+        // P3: the output of token tile w
+        const float egCn = egC;
+        f32x4s ov = zero;
+        if constexpr (kOut) {
+            f32x4s ov2[2] = {egv * qs, zero}, ub[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ub[r] = *reinterpret_cast<const f32x4s*>(u_t + l16 * TP + 16 * r + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (r <= w) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) ov2[r & 1] = mfma_f32_4(pc[r][s], ub[r][s], ov2[r & 1]);
+                }
+            }
+            ov = ov2[0] + ov2[1];
+        }
+        // the next chunk's K and Q into the buffers the previous chunk used
+        store_kq(tf, (n + 1) & 1);
+
+        // the state rows of the wave, the next chunk's other loads between the products;
+        // each token tile's K^T values and scaled U are read during the previous tile's
+        // products; even and odd token tiles in separate chains
+        f32x4s sto[2] = {zero, zero};
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) st[rt] *= egCn;
+        float kt[2][8];
+        f32x4s gb[2];
+        const auto rd3 = [&](int r, int i) {
+            gb[i] = *reinterpret_cast<const f32x4s*>(ug_t + l16 * TP + 16 * r + 4 * g4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float* kc = kb + (16 * r + 4 * g4 + s) * KPf + 32 * w + l16;
+                kt[i][2 * s] = kc[0];
+                kt[i][2 * s + 1] = kc[16];
+            }
+        };
+        rd3(0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = r & 1;
+            if (r + 1 < 4) rd3(r + 1, i ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    if (i == 0) st[rt] = mfma_f32_4(kt[i][2 * s + rt], gb[i][s], st[rt]);
+                    else sto[rt] = mfma_f32_4(kt[i][2 * s + rt], gb[i][s], sto[rt]);
+                }
+                if (s == 1) load_rest(nf, r);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            st[rt] += sto[rt];
+            *reinterpret_cast<f32x4s*>(s_t + l16 * KPf + 32 * w + 16 * rt + 4 * g4) = st[rt];
+        }
+        if constexpr (kOut) {
+            // unconditional stores through a descriptor that ends at the row's last token
+            // (stores past it are dropped), after this chunk's loads: a later wait for one
+            // of those loads need not wait for the stores
+            const int64_t trow = static_cast<int64_t>(a.H) * ncols;
+            const int64_t left = rs.extent - t0;
+            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                o + (rs.start + t0) * trow, 0, static_cast<int32_t>((left < 64 ? left : 64) * trow * 4),
+                kRawBufferWord3);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 16 * w + 4 * g4 + j;
+                const float x = t0 + row < nvalid ? ov[j] : 0.f;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), ro,
+                                                      static_cast<uint32_t>((row * trow + h * ncols + col0 + l16) * 4), 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+    if (a.store_mode == kStoreNone) return;
+    if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
+    const int64_t blk = (a.store_mode == kStoreEverySegment) ? bh * a.P + seg : bh;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            a.s_out[blk * tile + static_cast<int64_t>(32 * w + 16 * rt + 4 * g4 + j) * ncols + col0 + l16] = st[rt][j];
+}
+
 template <typename IO>
 hipError_t prep_dispatch(const PrepArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.NT));
@@ -689,9 +966,19 @@ constexpr int kStateCpt = 2;
 
 template <typename IO>
 hipError_t state_dispatch(const StateArgs& a, hipStream_t s) {
+    void* args[] = {const_cast<StateArgs*>(&a)};
+    if constexpr (sizeof(IO) == 4) {
+        if (a.dk == 128) {
+            // fp32 matrix cores; blocks in the scans' XCD-aware order over (b, segment, h)
+            const int64_t groups = (static_cast<int64_t>(a.B) * a.P * a.H + 7) / 8;
+            const dim3 grid(static_cast<unsigned>(groups * 8 * (a.ncols / 16)));
+            const void* fn = a.o ? reinterpret_cast<const void*>(&state_f32mfma<true>)
+                                 : reinterpret_cast<const void*>(&state_f32mfma<false>);
+            return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+        }
+    }
     const dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H),
                     static_cast<unsigned>(a.B * a.P));
-    void* args[] = {const_cast<StateArgs*>(&a)};
     const void* fn = nullptr;
     switch (a.dk) {
         case 16: fn = reinterpret_cast<const void*>(&state_f32path<IO, 16, kStateCpt>); break;
