@@ -481,7 +481,7 @@ def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
 def vector_path_timing(gdn, workloads, make_inputs, dev, stream, timed):
     """gdn_chunk_fwd off the d = 128 bf16 shapes, on the stateless 8K workload's sizes: heads
     of 64 in bf16 (the matrix-core kernels on q and k padded to 128 columns) and fp32 inputs
-    with heads of 128 (the fp32 vector-ALU kernels); kernel_path names the path."""
+    with heads of 128 (the fp32 matrix-core kernels); kernel_path names the path."""
     import dataclasses
 
     import torch

@@ -86,6 +86,9 @@ const char* gdn_last_error(void);
  *                         matrix-core kernels on q and k zero-padded to 128 columns (exact:
  *                         the padded columns add zeros to every product); every other call
  *                         runs such a problem on the fp32 vector-ALU kernels;
+ *   "f32-mfma"         -- fp32 I/O with dk == 128: the forward calls' prepare and state
+ *                         passes on fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32 products
+ *                         and accumulation); the backward runs the fp32 token-level kernels;
  *   "f32-valu"         -- every other problem: fp32 arithmetic on the vector ALUs.
  */
 const char* gdn_kernel_path(const gdn_problem* p);

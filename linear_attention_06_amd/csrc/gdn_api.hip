@@ -323,7 +323,11 @@ const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
 const char* gdn_kernel_path(const gdn_problem* p) {
     if (check_problem(p) != GDN_OK) return nullptr;
-    return use_mfma(*p) ? "bf16-mfma" : (use_mfma_padded(*p) ? "bf16-mfma-padded" : "f32-valu");
+    if (use_mfma(*p)) return "bf16-mfma";
+    if (use_mfma_padded(*p)) return "bf16-mfma-padded";
+    // fp32 inputs with dk = 128: the fp32 prepare and state kernels dispatch to their
+    // matrix-core versions by dk
+    return p->io_dtype == GDN_F32 && p->dk == 128 ? "f32-mfma" : "f32-valu";
 }
 
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {

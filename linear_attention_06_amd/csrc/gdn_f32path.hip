@@ -681,17 +681,20 @@ __global__ __launch_bounds__(512) void summary_outer_mfma(ScanBwdArgs a) {
 //       from the row-major K tile (conflict-free at a pitch of 132 floats).
 // Three barriers per chunk; K and Q in LDS, two buffers each, at a pitch of 132 floats.
 // A chunk's ~88 KiB of loads take the CU's load path longer to accept than its products
-// take, and a wave stalls while its loads issue; so they are issued between products: the
-// next chunk's K and Q between P1's (into registers, written to the free LDS buffers in
-// P3), its V, That, P and decay factors between the update's (straight into the registers
-// the next chunk reads; this chunk is done with them). Each k-tile's LDS operands are read
-// during the previous one's products, and the scheduling barriers pin that order.
+// take, and a wave stalls while its loads issue. Four more waves (one more per SIMD) load
+// the next chunk's K and Q (64 KiB) while the computing waves run P1, which issues no
+// memory instruction, and write them to the LDS buffers the chunk before used after the
+// second barrier (issued over P1 and the later phases instead, they slow the computing
+// waves' own loads: 0.65 against 0.62 ms at 8K tokens and 32 heads). The computing waves
+// load their V, That, P and decay factors between the update's products (straight into the
+// registers the next chunk reads; this chunk is done with them). Each k-tile's LDS operands are read during
+// the previous one's products, and the scheduling barriers pin that order.
 // k-step s of a 16x16x4 product has lane (l16, g4) supply contraction index 4 g4 + s of a
 // 16-wide slice, so that one 16-byte LDS read gives a lane its operand for four steps.
 constexpr int kRawBufferWord3 = 0x00020000;   // raw buffer descriptor word 3 on gfx9-family GPUs
 
 template <bool kOut>
-__global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
+__global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
     constexpr int KPf = 132, TP = 68, KQT = 64 * KPf;
     __shared__ __align__(16) float k_s[2 * KQT];
     __shared__ __align__(16) float q_s[kOut ? 2 * KQT : 4];
@@ -707,7 +710,9 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
     const int col0 = 16 * ct;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0-3 compute, 4-7 load K and Q
+    const bool loader = w >= 4;
+    const int ltid = tid & 255;
     const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
     const int64_t nvalid = rs.valid;
     const float* q = static_cast<const float*>(a.q);
@@ -718,9 +723,9 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
     const int64_t tile = static_cast<int64_t>(128) * ncols;
     const f32x4s zero = {0.f, 0.f, 0.f, 0.f};
 
-    f32x4s st[2];   // state rows 32 w + 16 rt + 4 g4 + j, column col0 + l16
+    f32x4s st[2] = {zero, zero};   // state rows 32 w + 16 rt + 4 g4 + j, column col0 + l16
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < 2 && !loader; ++rt) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int i = 32 * w + 16 * rt + 4 * g4 + j;
@@ -739,27 +744,35 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
     const int n0 = seg * a.Lc;
     const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
 
-    // float4 m of K and Q (lane tid) is row (tid + 256 m) / 32, columns 4 ((tid + 256 m) % 32)
-    // .. + 3; addresses of padded tokens are clamped to the row's first token (which exists
-    // whenever the row has a chunk) and their values replaced by zero when stored
+    // float4 m of K and Q (loading thread ltid) is row (ltid + 256 m) / 32, columns
+    // 4 ((ltid + 256 m) % 32) .. + 3, loaded through a descriptor per chunk that ends at the
+    // chunk's last valid row (rows past it read as zero; the whole offset is in the vector
+    // offset, which the range check covers)
     f32x4s kr[8], qr[8];
-    const auto kq_at = [&](int64_t t0, int m) -> int64_t {
-        const int e = tid + 256 * m, rr = e >> 5;
-        const int64_t tok = t0 + rr < nvalid ? t0 + rr : 0;
-        return ((rs.start + tok) * a.Hqk + hq) * 128 + 4 * (e & 31);
+    const int64_t qk_row = static_cast<int64_t>(a.Hqk) * 128;   // floats between tokens
+    const uint32_t kq_voff = static_cast<uint32_t>(((ltid >> 5) * qk_row + 4 * (ltid & 31)) * 4);
+    const auto kq_rsrc = [&](const float* base, int64_t t0) {
+        const int64_t rows = nvalid - t0 < 0 ? 0 : (nvalid - t0 > 64 ? 64 : nvalid - t0);
+        const int64_t bytes = rows > 0 ? ((rows - 1) * qk_row + 128) * 4 : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base + ((rs.start + t0) * a.Hqk + hq) * 128), 0,
+                                                 static_cast<int32_t>(bytes), kRawBufferWord3);
     };
-    const auto load_k = [&](int64_t t0, int m) { kr[m] = *reinterpret_cast<const f32x4s*>(k + kq_at(t0, m)); };
-    const auto load_q = [&](int64_t t0, int m) {
-        if constexpr (kOut) qr[m] = *reinterpret_cast<const f32x4s*>(q + kq_at(t0, m));
+    const auto load_kq = [&](int64_t t0) {
+        const __amdgpu_buffer_rsrc_t rk = kq_rsrc(k, t0), rq = kq_rsrc(q, t0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t off = kq_voff + static_cast<uint32_t>(m * 8 * qk_row * 4);
+            kr[m] = __builtin_bit_cast(f32x4s, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+            if constexpr (kOut) qr[m] = __builtin_bit_cast(f32x4s, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+        }
     };
-    const auto store_kq = [&](int64_t t0, int buf) {
+    const auto store_kq = [&](int buf) {
         float* kb = k_s + buf * KQT;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-            const int e = tid + 256 * m, rr = e >> 5, c4 = 4 * (e & 31);
-            const bool ok = t0 + rr < nvalid;
-            *reinterpret_cast<f32x4s*>(kb + rr * KPf + c4) = ok ? kr[m] : zero;
-            if constexpr (kOut) *reinterpret_cast<f32x4s*>(q_s + buf * KQT + rr * KPf + c4) = ok ? qr[m] : zero;
+            const int e = ltid + 256 * m, rr = e >> 5, c4 = 4 * (e & 31);
+            *reinterpret_cast<f32x4s*>(kb + rr * KPf + c4) = kr[m];
+            if constexpr (kOut) *reinterpret_cast<f32x4s*>(q_s + buf * KQT + rr * KPf + c4) = qr[m];
         }
     };
     // a chunk's V of rows 16 w + 4 g4 + j (replaced by zero past the valid length where it
@@ -788,20 +801,31 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
     };
     if (n0 < n1) {
         const int64_t t0 = static_cast<int64_t>(n0) * kChunk;
+        if (loader) {
+            load_kq(t0);
+            store_kq(n0 & 1);
+        } else {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            load_k(t0, m);
-            load_q(t0, m);
+            for (int piece = 0; piece < 4; ++piece) load_rest(n0, piece);
         }
-#pragma unroll
-        for (int piece = 0; piece < 4; ++piece) load_rest(n0, piece);
-        store_kq(t0, n0 & 1);
     }
     __syncthreads();
 
+    if (loader) {
+        // three barriers per chunk, as the computing waves below: the next chunk's K and Q
+        // (the last chunk re-fetches itself) into the LDS buffers the chunk before used
+        for (int n = n0; n < n1; ++n) {
+            load_kq(static_cast<int64_t>(n + 1 < n1 ? n + 1 : n) * kChunk);
+            __syncthreads();
+            __syncthreads();
+            store_kq((n + 1) & 1);
+            __syncthreads();
+        }
+        return;
+    }
+
     // The loop body has no branches around its loads and stores but wave-uniform ones, so
-    // that the compiler's wait counts stay tight: the last chunk re-fetches itself (into
-    // registers and the free LDS buffers, read by nobody).
+    // that the compiler's wait counts stay tight.
     for (int n = n0; n < n1; ++n) {
         const int64_t t0 = static_cast<int64_t>(n) * kChunk;
         const int nf = n + 1 < n1 ? n + 1 : n;
@@ -809,8 +833,7 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
         const float* kb = k_s + (n & 1) * KQT;
         const float* qb = q_s + (n & 1) * KQT;
 
-        // P1: K S and Q S of token tile w, the next chunk's K and Q loads between the
-        // products; even and odd k-tiles accumulate in separate chains
+        // P1: K S and Q S of token tile w; even and odd k-tiles accumulate in separate chains
         f32x4s ks2[2] = {zero, zero}, qs2[2] = {zero, zero};
         f32x4s sb[2], ka[2], qa[2];
         const auto rd1 = [&](int t, int i) {
@@ -828,8 +851,6 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
             for (int s = 0; s < 4; ++s) {
                 ks2[i] = mfma_f32_4(ka[i][s], sb[i][s], ks2[i]);
                 if constexpr (kOut) qs2[i] = mfma_f32_4(qa[i][s], sb[i][s], qs2[i]);
-                if (s == 0) load_k(tf, t);
-                if (s == 2) load_q(tf, t);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -873,9 +894,6 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
             }
             ov = ov2[0] + ov2[1];
         }
-        // the next chunk's K and Q into the buffers the previous chunk used
-        store_kq(tf, (n + 1) & 1);
-
         // the state rows of the wave, the next chunk's other loads between the products;
         // each token tile's K^T values and scaled U are read during the previous tile's
         // products; even and odd token tiles in separate chains
@@ -935,7 +953,7 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
         __syncthreads();
     }
 
-    if (a.store_mode == kStoreNone) return;
+    if (loader || a.store_mode == kStoreNone) return;
     if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
     const int64_t blk = (a.store_mode == kStoreEverySegment) ? bh * a.P + seg : bh;
 #pragma unroll
@@ -945,8 +963,202 @@ __global__ __launch_bounds__(256) void state_f32mfma(StateArgs a) {
             a.s_out[blk * tile + static_cast<int64_t>(32 * w + 16 * rt + 4 * g4 + j) * ncols + col0 + l16] = st[rt][j];
 }
 
+// The prepare pass for fp32 inputs with dk = 128 on v_mfma_f32_16x16x4_f32: one block of
+// four waves per (b, h, chunk), chunk-major with the heads of one chunk back to back on one
+// XCD (its L2 serves the q/k rows the value heads of a query/key head share). It writes the
+// records of prep_f32path: That = (I + A)^{-1} diag(beta) and P (64 x 64 fp32, row-major,
+// zero above the diagonal) and the decay factors.
+//   Gram products: the ten lower 16x16 tiles of K K^T and of Q K^T, five per wave, over the
+//   128 columns (K and Q in LDS, 16-byte granules XOR-swizzled by the row so that the
+//   fragment reads of 16 consecutive rows are conflict-free); A = beta_i e^{Gam_i - Gam_j}
+//   (K K^T)_ij below the diagonal into LDS, P = e^{Gam_i - Gam_j} (Q K^T)_ij on and below it
+//   to memory.
+//   Solve: the four diagonal blocks D_b = (I + A_bb)^{-1} by column sweep on one wave (lane =
+//   (block, column)); the blocks below them T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj as three
+//   per-wave chains of 16x16x16 products (T10 T20 T30 / T21 T31 / T32), each result kept in
+//   accumulators and entering the next product as its B operand.
+__device__ __forceinline__ int kq_slot(int r, int c4) { return r * 128 + 4 * (c4 ^ (r & 15)); }
+
+__global__ __launch_bounds__(256) void prep_f32mfma(PrepArgs a) {
+    constexpr int BP = 20;           // pitch of the 16x16 blocks in LDS (16-byte aligned rows)
+    constexpr int BS = 16 * BP;      // floats per block
+    __shared__ __align__(16) float kq_s[2 * 64 * 128];   // K, Q; later the diagonal inverses
+    __shared__ __align__(16) float a_s[10 * BS];          // the lower blocks of A, (i, j) at i (i + 1) / 2 + j
+    __shared__ float gam_s[64], beta_s[64];
+    float* k_s = kq_s;
+    float* q_s = kq_s + 64 * 128;
+    float* dr_s = kq_s;              // D_b row-major (after the Gram products)
+    float* dc_s = kq_s + 4 * BS;     // D_b transposed
+
+    const int64_t L = blockIdx.x;
+    const int xcd = static_cast<int>(L & 7);
+    const int64_t u = L >> 3;
+    const int h = static_cast<int>(u % a.H);
+    const int64_t pair = (u / a.H) * 8 + xcd;
+    if (pair >= static_cast<int64_t>(a.B) * a.NT) return;
+    const int b = static_cast<int>(pair / a.NT), n = static_cast<int>(pair % a.NT);
+    const int64_t ch = (static_cast<int64_t>(b) * a.H + h) * a.NT + n;
+    const int hq = h / (a.H / a.Hqk);
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+    const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
+    const float* kin = static_cast<const float*>(a.k);
+    const float* qin = static_cast<const float*>(a.q);
+    float* that = static_cast<float*>(a.ws.that) + ch * 4096;
+    float* pm = static_cast<float*>(a.ws.pmat) + ch * 4096;
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const f32x4v zero = {0.f, 0.f, 0.f, 0.f};
+
+    // K and Q rows (zero past the valid length), g and beta with the chunk-local cumulative sum
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int e = tid + 256 * m, rr = e >> 5, c4 = e & 31;
+        const bool ok = t0 + rr < rs.valid;
+        const int64_t idx = ((rs.start + (ok ? t0 + rr : 0)) * a.Hqk + hq) * 128 + 4 * c4;
+        const f32x4v kv = *reinterpret_cast<const f32x4v*>(kin + idx);
+        const f32x4v qv = *reinterpret_cast<const f32x4v*>(qin + idx);
+        *reinterpret_cast<f32x4v*>(k_s + kq_slot(rr, c4)) = ok ? kv : zero;
+        *reinterpret_cast<f32x4v*>(q_s + kq_slot(rr, c4)) = ok ? qv : zero;
+    }
+    if (w == 0) {
+        const bool ok = t0 + lane < rs.valid;
+        const int64_t gi = (rs.start + (ok ? t0 + lane : 0)) * a.H + h;
+        const float gv = a.g[gi], bv = a.beta[gi];
+        float gam = ok ? gv : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(gam, off, 64);
+            if (lane >= off) gam += y;
+        }
+        gam_s[lane] = gam;
+        beta_s[lane] = ok ? bv : 0.f;
+        // decay factors e^{Gam_t} and e^{Gam_C - Gam_t}
+        const float gam_c = __shfl(gam, 63, 64);
+        a.ws.gates[ch * 128 + lane] = expf(gam);
+        a.ws.gates[ch * 128 + 64 + lane] = expf(gam_c - gam);
+    }
+    // the blocks above the diagonal of That and P are zero
+    for (int e = tid; e < 6 * 64; e += 256) {
+        // block (i, j), i < j, element quad e % 64: rows 16 i + (e % 64) / 4, columns 16 j + 4 (e % 4)
+        const int blk = e >> 6, qd = e & 63;
+        const int i = blk < 3 ? 0 : (blk < 5 ? 1 : 2), j = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+        const int off = (16 * i + (qd >> 2)) * 64 + 16 * j + 4 * (qd & 3);
+        *reinterpret_cast<f32x4v*>(that + off) = zero;
+        *reinterpret_cast<f32x4v*>(pm + off) = zero;
+    }
+    __syncthreads();
+
+    // ---- Gram products: tile item w + 4 v of [K K^T lower tiles, Q K^T lower tiles] ----
+#pragma unroll 1
+    for (int v = 0; v < 5; ++v) {
+        const int item = w + 4 * v;
+        const int li = item < 10 ? item : item - 10;
+        const int bi = li == 0 ? 0 : (li < 3 ? 1 : (li < 6 ? 2 : 3));
+        const int bj = li - bi * (bi + 1) / 2;
+        const float* left = item < 10 ? k_s : q_s;
+        const int ra = 16 * bi + l16, rb = 16 * bj + l16;
+        f32x4v acc2[2] = {zero, zero};
+        f32x4v fa[2], fb[2];
+        fa[0] = *reinterpret_cast<const f32x4v*>(left + kq_slot(ra, g4));
+        fb[0] = *reinterpret_cast<const f32x4v*>(k_s + kq_slot(rb, g4));
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int i = t & 1;
+            if (t + 1 < 8) {
+                fa[i ^ 1] = *reinterpret_cast<const f32x4v*>(left + kq_slot(ra, 4 * (t + 1) + g4));
+                fb[i ^ 1] = *reinterpret_cast<const f32x4v*>(k_s + kq_slot(rb, 4 * (t + 1) + g4));
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) acc2[i] = mfma_f32_4(fa[i][s2], fb[i][s2], acc2[i]);
+        }
+        const f32x4v acc = acc2[0] + acc2[1];
+        const int jc = 16 * bj + l16;
+        const float gj = gam_s[jc];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ii = 16 * bi + 4 * g4 + r;
+            const float d = gam_s[ii] - gj;
+            const float dec = expf(d < 0.f ? d : 0.f);
+            if (item < 10) a_s[li * BS + (4 * g4 + r) * BP + l16] = ii > jc ? beta_s[ii] * dec * acc[r] : 0.f;
+            else pm[ii * 64 + jc] = ii >= jc ? dec * acc[r] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- the diagonal blocks: lane (blk, c) sweeps column c of (I + A_bb)^{-1} ----
+    if (w == 0) {
+        const int blk = lane >> 4, c = l16;
+        const float* ab = a_s + (blk * (blk + 1) / 2 + blk) * BS;
+        float tcol[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = r == c ? 1.f : 0.f;
+#pragma unroll
+            for (int j = 0; j < r; ++j) acc -= ab[r * BP + j] * tcol[j];
+            tcol[r] = acc;
+        }
+        const float bc = beta_s[16 * blk + c];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dr_s[blk * BS + r * BP + c] = tcol[r];
+            that[(16 * blk + r) * 64 + 16 * blk + c] = tcol[r] * bc;
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<f32x4v*>(dc_s + blk * BS + c * BP + 4 * r4) =
+                f32x4v{tcol[4 * r4], tcol[4 * r4 + 1], tcol[4 * r4 + 2], tcol[4 * r4 + 3]};
+    }
+    __syncthreads();
+
+    // ---- the blocks below the diagonal ----
+    if (w < 3) {
+        // A operand: rows l16 of a row-major block, columns 4 g4 .. + 3; B operand from a
+        // transposed block: its rows 4 g4 .. + 3 of column l16
+        const auto fr = [&](const float* blk) { return *reinterpret_cast<const f32x4v*>(blk + l16 * BP + 4 * g4); };
+        const auto mm = [&](const f32x4v& x, const f32x4v& y, f32x4v acc) {
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) acc = mfma_f32_4(x[s2], y[s2], acc);
+            return acc;
+        };
+        const auto ablk = [&](int i, int j) { return a_s + (i * (i + 1) / 2 + j) * BS; };
+        const auto put = [&](int i, int j, const f32x4v& tv) {
+            const float bc = beta_s[16 * j + l16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) that[(16 * i + 4 * g4 + r) * 64 + 16 * j + l16] = tv[r] * bc;
+        };
+        const int j0 = w;                      // the chain of column block w
+        // T_{j0+1, j0} = -D_{j0+1} A_{j0+1, j0} D_{j0}
+        f32x4v tprev[3];
+        f32x4v y = mm(fr(ablk(j0 + 1, j0)), fr(dc_s + j0 * BS), zero);
+        tprev[0] = -mm(fr(dr_s + (j0 + 1) * BS), y, zero);
+        put(j0 + 1, j0, tprev[0]);
+        // T_{i, j0} = -D_i (A_{i, j0} D_{j0} + sum_{k = j0+1}^{i-1} A_{i, k} T_{k, j0})
+#pragma unroll
+        for (int i = 2; i < 4; ++i) {
+            if (i > j0 + 1) {
+                y = mm(fr(ablk(i, j0)), fr(dc_s + j0 * BS), zero);
+#pragma unroll
+                for (int kk = 1; kk < 3; ++kk)
+                    if (j0 + kk < i) y = mm(fr(ablk(i, j0 + kk)), tprev[kk - 1], y);
+                tprev[i - j0 - 1] = -mm(fr(dr_s + i * BS), y, zero);
+                put(i, j0, tprev[i - j0 - 1]);
+            }
+        }
+    }
+}
+
 template <typename IO>
 hipError_t prep_dispatch(const PrepArgs& a, hipStream_t s) {
+    if constexpr (sizeof(IO) == 4) {
+        if (a.dk == 128) {
+            // fp32 matrix cores; (b, chunk) groups of 8 x the heads
+            const int64_t pairs = static_cast<int64_t>(a.B) * a.NT;
+            const dim3 grid(static_cast<unsigned>((pairs + 7) / 8 * 8 * a.H));
+            void* args[] = {const_cast<PrepArgs*>(&a)};
+            return hipLaunchKernel(reinterpret_cast<const void*>(&prep_f32mfma), grid, dim3(256), args, 0, s);
+        }
+    }
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.B) * a.H * a.NT));
     void* args[] = {const_cast<PrepArgs*>(&a)};
     const void* fn = nullptr;
@@ -974,7 +1186,7 @@ hipError_t state_dispatch(const StateArgs& a, hipStream_t s) {
             const dim3 grid(static_cast<unsigned>(groups * 8 * (a.ncols / 16)));
             const void* fn = a.o ? reinterpret_cast<const void*>(&state_f32mfma<true>)
                                  : reinterpret_cast<const void*>(&state_f32mfma<false>);
-            return hipLaunchKernel(fn, grid, dim3(256), args, 0, s);
+            return hipLaunchKernel(fn, grid, dim3(512), args, 0, s);
         }
     }
     const dim3 grid(static_cast<unsigned>(a.ncols / 16), static_cast<unsigned>(a.H),

@@ -167,7 +167,8 @@ def test_kernel_path_selection():
     assert path(io_dtype=gdn.GDN_BF16, dk=128, dv=64) == "bf16-mfma"
     assert path(io_dtype=gdn.GDN_BF16, dk=64, dv=64) == "bf16-mfma-padded"
     assert path(io_dtype=gdn.GDN_F32, dk=64, dv=64) == "f32-valu"
-    assert path(io_dtype=gdn.GDN_F32, dk=128, dv=128) == "f32-valu"
+    assert path(io_dtype=gdn.GDN_F32, dk=128, dv=128) == "f32-mfma"
+    assert path(io_dtype=gdn.GDN_F32, dk=128, dv=32) == "f32-mfma"
     with pytest.raises(gdn.GdnError):
         path(chunk=32)
 

@@ -76,11 +76,11 @@ def test_stateless_8k_matches_oracle():
 def test_vector_path_full_size_matches_oracle(d, io):
     """The stateless 8K workload's shapes off the d = 128 bf16 path (heads of 64 in bf16, run
     by gdn_chunk_fwd on the matrix cores with q and k padded to 128 columns, and fp32 inputs on
-    the fp32 vector-ALU kernels): the sizes bench.py times for those paths."""
+    the fp32 matrix-core kernels): the sizes bench.py times for those paths."""
     w = dataclasses.replace(WORKLOADS["stateless_8k"], name="vector_%s_d%d" % (io, d), dk=d, dv=d, io=io)
     inp = make_inputs(w)
     q, k, v, g, beta, _, _ = to_dev(inp)
-    assert gdn.gdn_kernel_path(gdn.problem(q, v)) == ("bf16-mfma-padded" if io == "bf16" else "f32-valu")
+    assert gdn.gdn_kernel_path(gdn.problem(q, v)) == ("bf16-mfma-padded" if io == "bf16" else "f32-mfma")
     q64, k64, v64, g64, b64, _ = inp.f64()
     o_ref, hT_ref = oracle.gdn_fwd(q64, k64, v64, g64, b64, None)
     o, hT = gdn.gdn_chunk_fwd(q, k, v, g, beta, None)
