@@ -669,37 +669,40 @@ __global__ __launch_bounds__(512) void summary_outer_mfma(ScanBwdArgs a) {
 }
 
 // The state pass for fp32 inputs with dk = 128 on v_mfma_f32_16x16x4_f32 (fp32 products,
-// fp32 accumulation): one block of four waves per (b, h, segment, 16 state columns), the
-// column tiles of one (b, h, segment) on one XCD (the order of the scans above). Wave w
-// keeps rows 32 w .. 32 w + 31 of the state in two accumulator tiles and owns token tile w
-// (tokens 16 w .. 16 w + 15) of every chunk:
+// fp32 accumulation): one block of eight waves per (b, h, segment, 16 state columns), the
+// column tiles of one (b, h, segment) on one XCD (the order of the scans above). Computing
+// wave w (0-3) keeps rows 32 w .. 32 w + 31 of the state in two accumulator tiles and owns
+// token tile w (tokens 16 w .. 16 w + 15) of every chunk:
 //   P1  K S and Q S of its tokens over all 128 state rows (the state read back from LDS,
 //       transposed), X = V - e^Gam K S;
 //   P2  U = That X over the token tiles up to its own (X exchanged through LDS);
 //   P3  O = e^Gam Q S + P U (U through LDS), and its state rows
 //       S <- e^{Gam_C} S + K^T (e^{Gam_C - Gam} U), the K^T fragments read as single floats
 //       from the row-major K tile (conflict-free at a pitch of 132 floats).
-// Three barriers per chunk; K and Q in LDS, two buffers each, at a pitch of 132 floats.
-// A chunk's ~88 KiB of loads take the CU's load path longer to accept than its products
-// take, and a wave stalls while its loads issue. Four more waves (one more per SIMD) load
-// the next chunk's K and Q (64 KiB) while the computing waves run P1, which issues no
-// memory instruction, and write them to the LDS buffers the chunk before used after the
-// second barrier (issued over P1 and the later phases instead, they slow the computing
-// waves' own loads: 0.65 against 0.62 ms at 8K tokens and 32 heads). The computing waves
-// load their V, That, P and decay factors between the update's products (straight into the
-// registers the next chunk reads; this chunk is done with them). Each k-tile's LDS operands are read during
-// the previous one's products, and the scheduling barriers pin that order.
-// k-step s of a 16x16x4 product has lane (l16, g4) supply contraction index 4 g4 + s of a
-// 16-wide slice, so that one 16-byte LDS read gives a lane its operand for four steps.
+// Three barriers per chunk. Waves 4-7 stage every operand in LDS, so that the computing
+// waves issue no load (a CU's load path accepts a chunk's ~100 KiB more slowly than the
+// products take, and a wave stalls while its loads issue): the next chunk's K and Q are
+// loaded while P1 runs; its That, V, P and decay factors after the first barrier; Q is
+// written after the first barrier (P1 has read this chunk's), That, V, K and the decay
+// factors after the second (P2 has read That), P at the start of the next chunk (P3 has
+// read this one's). K and the decay factors have two buffers; padded tokens' K and V are
+// zero. Each k-tile's LDS operands are read during the previous one's products, and the
+// scheduling barriers pin that order. k-step s of a 16x16x4 product has lane (l16, g4)
+// supply contraction index 4 g4 + s of a 16-wide slice, so that one 16-byte LDS read gives
+// a lane its operand for four steps.
 constexpr int kRawBufferWord3 = 0x00020000;   // raw buffer descriptor word 3 on gfx9-family GPUs
 
 template <bool kOut>
 __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
     constexpr int KPf = 132, TP = 68, KQT = 64 * KPf;
     __shared__ __align__(16) float k_s[2 * KQT];
-    __shared__ __align__(16) float q_s[kOut ? 2 * KQT : 4];
-    __shared__ __align__(16) float s_t[16 * KPf];   // the state transposed: S[i][c] at c KPf + i
-    __shared__ __align__(16) float x_t[16 * TP];    // X, U and e^{Gam_C - Gam} U transposed
+    __shared__ __align__(16) float q_s[kOut ? KQT : 4];
+    __shared__ __align__(16) float t_s[64 * TP];           // That, row-major
+    __shared__ __align__(16) float p_s[kOut ? 64 * TP : 4];  // P, row-major
+    __shared__ __align__(16) float v_t[16 * TP];           // V transposed: V[t][c] at c TP + t
+    __shared__ __align__(16) float g_s[2 * 128];           // e^Gam, e^{Gam_C - Gam}
+    __shared__ __align__(16) float s_t[16 * KPf];          // the state transposed: S[i][c] at c KPf + i
+    __shared__ __align__(16) float x_t[16 * TP];           // X, U and e^{Gam_C - Gam} U transposed
     __shared__ __align__(16) float u_t[16 * TP];
     __shared__ __align__(16) float ug_t[16 * TP];
 
@@ -710,7 +713,7 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
     const int col0 = 16 * ct;
     const int hq = h / (a.H / a.Hqk);
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0-3 compute, 4-7 load K and Q
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0-3 compute, 4-7 stage operands
     const bool loader = w >= 4;
     const int ltid = tid & 255;
     const RowSpan rs = row_span(a.cu_seqlens, a.valid_len, b, a.T, a.NT);
@@ -722,10 +725,111 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
     const int64_t bh = static_cast<int64_t>(b) * a.H + h;
     const int64_t tile = static_cast<int64_t>(128) * ncols;
     const f32x4s zero = {0.f, 0.f, 0.f, 0.f};
+    const int n0 = seg * a.Lc;
+    const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
 
-    f32x4s st[2] = {zero, zero};   // state rows 32 w + 16 rt + 4 g4 + j, column col0 + l16
+    if (loader) {
+        // float4 m of K and Q is row (ltid + 256 m) / 32, columns 4 ((ltid + 256 m) % 32) .. + 3,
+        // loaded through a descriptor per chunk that ends at the chunk's last valid row (rows
+        // past it read as zero; the whole offset is in the vector offset, which the range
+        // check covers). float4 m of That and P is row (ltid + 256 m) / 16, columns
+        // 4 ((ltid + 256 m) % 16) .. + 3; of V, token ltid / 4, columns 4 (ltid % 4) .. + 3.
+        f32x4s kr[8], qr[8], tr[4], pr[4], vr, gr;
+        const int64_t qk_row = static_cast<int64_t>(a.Hqk) * 128;
+        const uint32_t kq_voff = static_cast<uint32_t>(((ltid >> 5) * qk_row + 4 * (ltid & 31)) * 4);
+        const auto kq_rsrc = [&](const float* base, int64_t t0) {
+            const int64_t rows = nvalid - t0 < 0 ? 0 : (nvalid - t0 > 64 ? 64 : nvalid - t0);
+            const int64_t bytes = rows > 0 ? ((rows - 1) * qk_row + 128) * 4 : 0;
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base + ((rs.start + t0) * a.Hqk + hq) * 128), 0,
+                                                     static_cast<int32_t>(bytes), kRawBufferWord3);
+        };
+        const auto load_kq = [&](int n) {
+            const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+            const __amdgpu_buffer_rsrc_t rk = kq_rsrc(k, t0), rq = kq_rsrc(q, t0);
 #pragma unroll
-    for (int rt = 0; rt < 2 && !loader; ++rt) {
+            for (int m = 0; m < 8; ++m) {
+                const uint32_t off = kq_voff + static_cast<uint32_t>(m * 8 * qk_row * 4);
+                kr[m] = __builtin_bit_cast(f32x4s, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                if constexpr (kOut)
+                    qr[m] = __builtin_bit_cast(f32x4s, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+            }
+        };
+        const auto load_rest = [&](int n) {
+            const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+            const int64_t ch = bh * a.NT + n;
+            const float* tg = static_cast<const float*>(a.ws.that) + ch * 4096;
+            const float* pg = static_cast<const float*>(a.ws.pmat) + ch * 4096;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                tr[m] = *reinterpret_cast<const f32x4s*>(tg + 4 * (ltid + 256 * m));
+                if constexpr (kOut) pr[m] = *reinterpret_cast<const f32x4s*>(pg + 4 * (ltid + 256 * m));
+            }
+            const int64_t tok = t0 + (ltid >> 2);
+            const int64_t tcl = tok < nvalid ? tok : 0;
+            vr = v ? *reinterpret_cast<const f32x4s*>(v + ((rs.start + tcl) * a.H + h) * ncols + col0 + 4 * (ltid & 3))
+                   : zero;
+            if (ltid < 32) gr = *reinterpret_cast<const f32x4s*>(a.ws.gates + ch * 128 + 4 * ltid);
+        };
+        const auto store_q = [&]() {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int e = ltid + 256 * m;
+                if constexpr (kOut) *reinterpret_cast<f32x4s*>(q_s + (e >> 5) * KPf + 4 * (e & 31)) = qr[m];
+            }
+        };
+        // That, V (padded tokens zero) of chunk n, its K and decay factors into buffer buf
+        const auto store_tvkg = [&](int n, int buf) {
+            const int64_t t0 = static_cast<int64_t>(n) * kChunk;
+            float* kb = k_s + buf * KQT;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int e = ltid + 256 * m;
+                *reinterpret_cast<f32x4s*>(t_s + (e >> 4) * TP + 4 * (e & 15)) = tr[m];
+            }
+            const int tk = ltid >> 2, c4 = 4 * (ltid & 3);
+            const f32x4s vv = t0 + tk < nvalid ? vr : zero;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v_t[(c4 + i) * TP + tk] = vv[i];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int e = ltid + 256 * m;
+                *reinterpret_cast<f32x4s*>(kb + (e >> 5) * KPf + 4 * (e & 31)) = kr[m];
+            }
+            if (ltid < 32) *reinterpret_cast<f32x4s*>(g_s + buf * 128 + 4 * ltid) = gr;
+        };
+        const auto store_p = [&]() {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int e = ltid + 256 * m;
+                if constexpr (kOut) *reinterpret_cast<f32x4s*>(p_s + (e >> 4) * TP + 4 * (e & 15)) = pr[m];
+            }
+        };
+        if (n0 < n1) {
+            load_kq(n0);
+            load_rest(n0);
+            store_q();
+            store_tvkg(n0, n0 & 1);
+        }
+        __syncthreads();
+        // three barriers per chunk, as the computing waves below (the last chunk re-fetches
+        // itself where a later one is due; nobody reads what it stores)
+        for (int n = n0; n < n1; ++n) {
+            const int nf = n + 1 < n1 ? n + 1 : n;
+            store_p();                       // this chunk's P (loaded during the previous one)
+            load_kq(nf);
+            __syncthreads();
+            store_q();
+            load_rest(nf);
+            __syncthreads();
+            store_tvkg(nf, (n + 1) & 1);
+            __syncthreads();
+        }
+        return;
+    }
+
+    f32x4s st[2];   // state rows 32 w + 16 rt + 4 g4 + j, column col0 + l16
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int i = 32 * w + 16 * rt + 4 * g4 + j;
@@ -740,98 +844,13 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
         }
         *reinterpret_cast<f32x4s*>(s_t + l16 * KPf + 32 * w + 16 * rt + 4 * g4) = st[rt];
     }
-
-    const int n0 = seg * a.Lc;
-    const int n1 = min(min(n0 + a.Lc, a.NT), static_cast<int>((rs.extent + kChunk - 1) / kChunk));
-
-    // float4 m of K and Q (loading thread ltid) is row (ltid + 256 m) / 32, columns
-    // 4 ((ltid + 256 m) % 32) .. + 3, loaded through a descriptor per chunk that ends at the
-    // chunk's last valid row (rows past it read as zero; the whole offset is in the vector
-    // offset, which the range check covers)
-    f32x4s kr[8], qr[8];
-    const int64_t qk_row = static_cast<int64_t>(a.Hqk) * 128;   // floats between tokens
-    const uint32_t kq_voff = static_cast<uint32_t>(((ltid >> 5) * qk_row + 4 * (ltid & 31)) * 4);
-    const auto kq_rsrc = [&](const float* base, int64_t t0) {
-        const int64_t rows = nvalid - t0 < 0 ? 0 : (nvalid - t0 > 64 ? 64 : nvalid - t0);
-        const int64_t bytes = rows > 0 ? ((rows - 1) * qk_row + 128) * 4 : 0;
-        return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base + ((rs.start + t0) * a.Hqk + hq) * 128), 0,
-                                                 static_cast<int32_t>(bytes), kRawBufferWord3);
-    };
-    const auto load_kq = [&](int64_t t0) {
-        const __amdgpu_buffer_rsrc_t rk = kq_rsrc(k, t0), rq = kq_rsrc(q, t0);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const uint32_t off = kq_voff + static_cast<uint32_t>(m * 8 * qk_row * 4);
-            kr[m] = __builtin_bit_cast(f32x4s, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-            if constexpr (kOut) qr[m] = __builtin_bit_cast(f32x4s, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-        }
-    };
-    const auto store_kq = [&](int buf) {
-        float* kb = k_s + buf * KQT;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int e = ltid + 256 * m, rr = e >> 5, c4 = 4 * (e & 31);
-            *reinterpret_cast<f32x4s*>(kb + rr * KPf + c4) = kr[m];
-            if constexpr (kOut) *reinterpret_cast<f32x4s*>(q_s + buf * KQT + rr * KPf + c4) = qr[m];
-        }
-    };
-    // a chunk's V of rows 16 w + 4 g4 + j (replaced by zero past the valid length where it
-    // is used: a select here would wait for the load), That and P rows 16 w + l16, columns
-    // 16 r + 4 g4 .. + 3 for the token tiles r <= w, e^Gam and e^{Gam_C - Gam} of rows
-    // 16 w + 4 g4 .. + 3, and e^{Gam_C}; loaded in four pieces
-    f32x4s tc[4], pc[4], egv, egcv;
-    float vc[4], egC = 1.f;
-    const auto load_rest = [&](int n, int piece) {
-        const int64_t t0 = static_cast<int64_t>(n) * kChunk;
-        const int64_t ch = bh * a.NT + n;
-        if (piece == 0) {
-            const float* gg = a.ws.gates + ch * 128 + 16 * w + 4 * g4;
-            egv = *reinterpret_cast<const f32x4s*>(gg);
-            egcv = *reinterpret_cast<const f32x4s*>(gg + 64);
-            egC = a.ws.gates[ch * 128 + 63];
-        }
-        const int64_t tok = t0 + 16 * w + 4 * g4 + piece;
-        const int64_t tcl = tok < nvalid ? tok : 0;
-        vc[piece] = v ? v[((rs.start + tcl) * a.H + h) * ncols + col0 + l16] : 0.f;
-        if (piece <= w) {
-            const int64_t off = ch * 4096 + (16 * w + l16) * 64 + 16 * piece + 4 * g4;
-            tc[piece] = *reinterpret_cast<const f32x4s*>(static_cast<const float*>(a.ws.that) + off);
-            if constexpr (kOut) pc[piece] = *reinterpret_cast<const f32x4s*>(static_cast<const float*>(a.ws.pmat) + off);
-        }
-    };
-    if (n0 < n1) {
-        const int64_t t0 = static_cast<int64_t>(n0) * kChunk;
-        if (loader) {
-            load_kq(t0);
-            store_kq(n0 & 1);
-        } else {
-#pragma unroll
-            for (int piece = 0; piece < 4; ++piece) load_rest(n0, piece);
-        }
-    }
     __syncthreads();
 
-    if (loader) {
-        // three barriers per chunk, as the computing waves below: the next chunk's K and Q
-        // (the last chunk re-fetches itself) into the LDS buffers the chunk before used
-        for (int n = n0; n < n1; ++n) {
-            load_kq(static_cast<int64_t>(n + 1 < n1 ? n + 1 : n) * kChunk);
-            __syncthreads();
-            __syncthreads();
-            store_kq((n + 1) & 1);
-            __syncthreads();
-        }
-        return;
-    }
-
-    // The loop body has no branches around its loads and stores but wave-uniform ones, so
-    // that the compiler's wait counts stay tight.
     for (int n = n0; n < n1; ++n) {
         const int64_t t0 = static_cast<int64_t>(n) * kChunk;
-        const int nf = n + 1 < n1 ? n + 1 : n;
-        const int64_t tf = static_cast<int64_t>(nf) * kChunk;
         const float* kb = k_s + (n & 1) * KQT;
-        const float* qb = q_s + (n & 1) * KQT;
+        const float* gb_s = g_s + (n & 1) * 128;
+        const f32x4s egv = *reinterpret_cast<const f32x4s*>(gb_s + 16 * w + 4 * g4);
 
         // P1: K S and Q S of token tile w; even and odd k-tiles accumulate in separate chains
         f32x4s ks2[2] = {zero, zero}, qs2[2] = {zero, zero};
@@ -839,7 +858,7 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
         const auto rd1 = [&](int t, int i) {
             sb[i] = *reinterpret_cast<const f32x4s*>(s_t + l16 * KPf + 16 * t + 4 * g4);
             ka[i] = *reinterpret_cast<const f32x4s*>(kb + (16 * w + l16) * KPf + 16 * t + 4 * g4);
-            if constexpr (kOut) qa[i] = *reinterpret_cast<const f32x4s*>(qb + (16 * w + l16) * KPf + 16 * t + 4 * g4);
+            if constexpr (kOut) qa[i] = *reinterpret_cast<const f32x4s*>(q_s + (16 * w + l16) * KPf + 16 * t + 4 * g4);
         };
         rd1(0, 0);
 #pragma unroll
@@ -851,21 +870,21 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
             for (int s = 0; s < 4; ++s) {
                 ks2[i] = mfma_f32_4(ka[i][s], sb[i][s], ks2[i]);
                 if constexpr (kOut) qs2[i] = mfma_f32_4(qa[i][s], sb[i][s], qs2[i]);
-                __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         const f32x4s ks = ks2[0] + ks2[1], qs = qs2[0] + qs2[1];
-        f32x4s xw;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xw[j] = (t0 + 16 * w + 4 * g4 + j < nvalid ? vc[j] : 0.f) - egv[j] * ks[j];
-        *reinterpret_cast<f32x4s*>(x_t + l16 * TP + 16 * w + 4 * g4) = xw;
+        const f32x4s vc = *reinterpret_cast<const f32x4s*>(v_t + l16 * TP + 16 * w + 4 * g4);
+        *reinterpret_cast<f32x4s*>(x_t + l16 * TP + 16 * w + 4 * g4) = vc - egv * ks;
         __syncthreads();
 
-        // P2: U of token tile w (all four X tiles read at once; the products stop at w;
-        // even and odd token tiles in two chains)
-        f32x4s u2[2] = {zero, zero}, xb[4];
+        // P2: U of token tile w (the products stop at w; even and odd token tiles in two chains)
+        f32x4s u2[2] = {zero, zero}, xb[4], tc[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xb[r] = *reinterpret_cast<const f32x4s*>(x_t + l16 * TP + 16 * r + 4 * g4);
+        for (int r = 0; r < 4; ++r) {
+            xb[r] = *reinterpret_cast<const f32x4s*>(x_t + l16 * TP + 16 * r + 4 * g4);
+            tc[r] = *reinterpret_cast<const f32x4s*>(t_s + (16 * w + l16) * TP + 16 * r + 4 * g4);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             if (r <= w) {
@@ -874,17 +893,20 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
             }
         }
         const f32x4s u = u2[0] + u2[1];
+        const f32x4s egcv = *reinterpret_cast<const f32x4s*>(gb_s + 64 + 16 * w + 4 * g4);
         *reinterpret_cast<f32x4s*>(u_t + l16 * TP + 16 * w + 4 * g4) = u;
         *reinterpret_cast<f32x4s*>(ug_t + l16 * TP + 16 * w + 4 * g4) = egcv * u;
         __syncthreads();
 
         // P3: the output of token tile w
-        const float egCn = egC;
         f32x4s ov = zero;
         if constexpr (kOut) {
-            f32x4s ov2[2] = {egv * qs, zero}, ub[4];
+            f32x4s ov2[2] = {egv * qs, zero}, ub[4], pc[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ub[r] = *reinterpret_cast<const f32x4s*>(u_t + l16 * TP + 16 * r + 4 * g4);
+            for (int r = 0; r < 4; ++r) {
+                ub[r] = *reinterpret_cast<const f32x4s*>(u_t + l16 * TP + 16 * r + 4 * g4);
+                pc[r] = *reinterpret_cast<const f32x4s*>(p_s + (16 * w + l16) * TP + 16 * r + 4 * g4);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if (r <= w) {
@@ -894,9 +916,10 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
             }
             ov = ov2[0] + ov2[1];
         }
-        // the state rows of the wave, the next chunk's other loads between the products;
-        // each token tile's K^T values and scaled U are read during the previous tile's
-        // products; even and odd token tiles in separate chains
+
+        // the state rows of the wave; each token tile's K^T values and scaled U are read
+        // during the previous tile's products; even and odd token tiles in separate chains
+        const float egCn = gb_s[63];
         f32x4s sto[2] = {zero, zero};
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) st[rt] *= egCn;
@@ -924,9 +947,8 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
                     if (i == 0) st[rt] = mfma_f32_4(kt[i][2 * s + rt], gb[i][s], st[rt]);
                     else sto[rt] = mfma_f32_4(kt[i][2 * s + rt], gb[i][s], sto[rt]);
                 }
-                if (s == 1) load_rest(nf, r);
-                __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -935,8 +957,7 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
         }
         if constexpr (kOut) {
             // unconditional stores through a descriptor that ends at the row's last token
-            // (stores past it are dropped), after this chunk's loads: a later wait for one
-            // of those loads need not wait for the stores
+            // (stores past it are dropped)
             const int64_t trow = static_cast<int64_t>(a.H) * ncols;
             const int64_t left = rs.extent - t0;
             const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
@@ -953,7 +974,7 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
         __syncthreads();
     }
 
-    if (loader || a.store_mode == kStoreNone) return;
+    if (a.store_mode == kStoreNone) return;
     if (a.store_mode == kStoreLastSegment && seg != a.P - 1) return;
     const int64_t blk = (a.store_mode == kStoreEverySegment) ? bh * a.P + seg : bh;
 #pragma unroll
