@@ -89,14 +89,17 @@ const char* gdn_last_error(void);
  *   "f32-mfma"         -- fp32 I/O with dk == 128: the forward calls' prepare and state
  *                         passes on fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32 products
  *                         and accumulation); the backward runs the fp32 token-level kernels;
- *   "f32-valu"         -- every other problem: fp32 arithmetic on the vector ALUs.
+ *   "f32-mfma-padded"  -- fp32 I/O with dk < 128: gdn_chunk_fwd and gdn_chunk_fwd_varlen
+ *                         run the fp32 matrix-core kernels on q and k zero-padded to 128
+ *                         columns; every other call runs such a problem on the fp32
+ *                         vector-ALU kernels.
  */
 const char* gdn_kernel_path(const gdn_problem* p);
 
 /*
  * Workspace for gdn_chunk_fwd, in bytes, written to *bytes. The workspace holds
  * the per-chunk intermediates (the triangular-solve factor, the masked intra-chunk
- * q.k block and the chunk decay factors), and for bf16 heads with dk < 128 also q and k
+ * q.k block and the chunk decay factors), and for heads with dk < 128 also q and k
  * padded to 128 columns and the initial and final states padded to 128 rows; its
  * contents are undefined on entry.
  */
@@ -127,9 +130,10 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p,
  * shares that GPU's array: calls that overlap on one GPU (different streams, or host
  * threads without ordering) race and give undefined results; calls on one stream are
  * ordered. Nothing in the array has to start at zero (each call writes every record it
- * reads). bf16 heads with dk < 128 run here on the fp32 vector-ALU kernels (gdn_chunk_fwd
+ * reads). Heads with dk < 128 run here on the fp32 vector-ALU kernels (gdn_chunk_fwd
  * runs them on the matrix cores through padded copies of q and k, which this call has no
- * room for), so for them the two calls agree to the bf16 bound, not bit for bit.
+ * room for), so for them the two calls agree to the bound of the input type (bf16 or
+ * fp32), not bit for bit.
  */
 gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p,
                                  const void* q, const void* k, const void* v,

@@ -36,12 +36,14 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // other problem runs on the fp32 vector-ALU kernels.
 bool use_mfma(const gdn_problem& p) { return p.io_dtype == GDN_BF16 && p.dk == 128; }
 
-// gdn_chunk_fwd on bf16 heads with dk < 128 runs the dk = 128 matrix-core kernels on q and
-// k zero-padded to 128 columns (and h0 to 128 rows): the padded columns add exact zeros to
-// every q.k and k.k product and to K S, and the state's padded rows start at zero and stay
-// zero (their transition is a pure decay), so o and the first dk rows of the final state are
-// those of the unpadded problem.
-bool use_mfma_padded(const gdn_problem& p) { return p.io_dtype == GDN_BF16 && p.dk < 128; }
+// gdn_chunk_fwd on heads with dk < 128 runs the dk = 128 matrix-core kernels (bf16, or fp32
+// for fp32 inputs) on q and k zero-padded to 128 columns (and h0 to 128 rows): the padded
+// columns add exact zeros to every q.k and k.k product and to K S, and the state's padded
+// rows start at zero and stay zero (their transition is a pure decay), so o and the first
+// dk rows of the final state are those of the unpadded problem. Without tokens there is
+// nothing to pad (hT = h0 or zero needs no workspace).
+bool use_mfma_padded(const gdn_problem& p) { return p.dk < 128 && p.T > 0; }
+int64_t io_bytes(const gdn_problem& p) { return p.io_dtype == GDN_BF16 ? 2 : 4; }
 gdn_problem padded_problem(const gdn_problem& p) {
     gdn_problem w = p;
     w.dk = 128;
@@ -216,7 +218,7 @@ PadPlan make_pad_plan(const gdn_problem& p, int64_t max_len = -1, bool packed = 
     PadPlan pp;
     pp.rec = make_plan(padded_problem(p), false, max_len);
     const size_t tokens = packed ? static_cast<size_t>(p.T) : static_cast<size_t>(p.B) * p.T;
-    const size_t qk = align256(tokens * p.Hqk * 128 * 2);
+    const size_t qk = align256(tokens * p.Hqk * 128 * io_bytes(p));
     const size_t st = align256(static_cast<size_t>(p.B) * p.H * 128 * p.dv * 4);
     pp.q_off = align256(pp.rec.bytes);
     pp.k_off = pp.q_off + qk;
@@ -230,8 +232,8 @@ gdn_status run_varlen(const gdn_problem& p, const Plan& pl, const int32_t* cu_se
                       const void* v, const float* g, const float* beta, const float* h0, void* o, float* hT, void* ws,
                       hipStream_t s);
 
-// The forward of a bf16 problem with dk < 128 on padded copies (cu_seqlens: packed
-// sequences, through the varlen body).
+// The forward of a problem with dk < 128 on padded copies (cu_seqlens: packed sequences,
+// through the varlen body).
 gdn_status run_fwd_padded(const gdn_problem& p, const PadPlan& pp, const int32_t* cu_seqlens, const void* q,
                           const void* k, const void* v, const float* g, const float* beta, const float* h0,
                           void* o, float* hT, void* ws, hipStream_t s) {
@@ -240,8 +242,9 @@ gdn_status run_fwd_padded(const gdn_problem& p, const PadPlan& pp, const int32_t
     const int64_t qk_rows = (cu_seqlens ? static_cast<int64_t>(p.T) : static_cast<int64_t>(p.B) * p.T) * p.Hqk;
     const int64_t blocks = static_cast<int64_t>(p.B) * p.H;
     const int64_t st_in = static_cast<int64_t>(p.dk) * p.dv * 4, st_pad = static_cast<int64_t>(128) * p.dv * 4;
-    hipError_t e = gdn::launch_copy_rows(q, p.dk * 2, base + pp.q_off, 256, qk_rows, s);
-    if (e == hipSuccess) e = gdn::launch_copy_rows(k, p.dk * 2, base + pp.k_off, 256, qk_rows, s);
+    const int64_t es = io_bytes(p);
+    hipError_t e = gdn::launch_copy_rows(q, p.dk * es, base + pp.q_off, 128 * es, qk_rows, s);
+    if (e == hipSuccess) e = gdn::launch_copy_rows(k, p.dk * es, base + pp.k_off, 128 * es, qk_rows, s);
     if (e == hipSuccess && h0) e = gdn::launch_copy_rows(h0, st_in, base + pp.h0_off, st_pad, blocks, s);
     if (e != hipSuccess) return hip_fail(e, "padding copy launch");
     float* hT_pad = hT ? reinterpret_cast<float*>(base + pp.hT_off) : nullptr;
@@ -323,11 +326,10 @@ const char* gdn_last_error(void) { return g_last_error.c_str(); }
 
 const char* gdn_kernel_path(const gdn_problem* p) {
     if (check_problem(p) != GDN_OK) return nullptr;
-    if (use_mfma(*p)) return "bf16-mfma";
-    if (use_mfma_padded(*p)) return "bf16-mfma-padded";
-    // fp32 inputs with dk = 128: the fp32 prepare and state kernels dispatch to their
-    // matrix-core versions by dk
-    return p->io_dtype == GDN_F32 && p->dk == 128 ? "f32-mfma" : "f32-valu";
+    // (fp32 inputs: the fp32 prepare and state kernels dispatch to their matrix-core
+    // versions by dk)
+    if (p->io_dtype == GDN_BF16) return p->dk == 128 ? "bf16-mfma" : "bf16-mfma-padded";
+    return p->dk == 128 ? "f32-mfma" : "f32-mfma-padded";
 }
 
 gdn_status gdn_chunk_fwd_workspace(const gdn_problem* p, size_t* bytes) {

@@ -166,7 +166,8 @@ def test_kernel_path_selection():
     assert path(io_dtype=gdn.GDN_BF16, dk=128, dv=128) == "bf16-mfma"
     assert path(io_dtype=gdn.GDN_BF16, dk=128, dv=64) == "bf16-mfma"
     assert path(io_dtype=gdn.GDN_BF16, dk=64, dv=64) == "bf16-mfma-padded"
-    assert path(io_dtype=gdn.GDN_F32, dk=64, dv=64) == "f32-valu"
+    assert path(io_dtype=gdn.GDN_F32, dk=64, dv=64) == "f32-mfma-padded"
+    assert path(io_dtype=gdn.GDN_F32, dk=16, dv=16) == "f32-mfma-padded"
     assert path(io_dtype=gdn.GDN_F32, dk=128, dv=128) == "f32-mfma"
     assert path(io_dtype=gdn.GDN_F32, dk=128, dv=32) == "f32-mfma"
     with pytest.raises(gdn.GdnError):
@@ -286,8 +287,8 @@ def test_noalloc_forward_rejects_oversized_problems_before_any_hip_call():
 
 
 def test_padded_narrow_head_workspaces_and_checks():
-    """bf16 heads under 128: the forward's workspace holds the dk = 128 problem's records plus
-    q and k padded to 128 columns and two 128-row state blocks; the backward pads from 256
+    """Heads under 128: the forward's workspace holds the dk = 128 problem's records plus q
+    and k padded to 128 columns and two 128-row state blocks (bf16 and fp32); the backward pads from 256
     tokens per row on (shorter rows keep the token-level backward's workspace); the checks
     still come before any launch."""
     L = gdn.lib()
@@ -301,8 +302,10 @@ def test_padded_narrow_head_workspaces_and_checks():
     assert n_pad >= n128 + 2 * B * T * Hqk * 128 * 2 + 2 * B * H * 128 * dv * 4
     assert call_fwd(p, ws=256, nbytes=n_pad - 1) == gdn.GDN_EWORKSPACE
     assert call_fwd(p, q=None, ws=256, nbytes=n_pad) == gdn.GDN_EINVAL
-    # the fp32 problem of the same shape keeps the vector-ALU workspace
-    assert ws_status(P(B=B, T=T, H=H, Hqk=Hqk, dk=dk, dv=dv))[1] < n_pad
+    # the fp32 problem of the same shape pads too, onto the fp32 dk = 128 records
+    n_f32 = ws_status(P(B=B, T=T, H=H, Hqk=Hqk, dk=dk, dv=dv))[1]
+    n_f32_128 = ws_status(P(B=B, T=T, H=H, Hqk=Hqk, dk=128, dv=dv))[1]
+    assert n_f32 >= n_f32_128 + 2 * B * T * Hqk * 128 * 4 + 2 * B * H * 128 * dv * 4
     # backward: padded (T >= 256) needs the dk = dv = 128 problem's workspace and more
     assert L.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(n)) == gdn.GDN_OK
     n_bwd = n.value

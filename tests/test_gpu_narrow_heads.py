@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from oracle import backward
-from gpu_common import TOL_BF16, dev, np_f64, sync, to_dev
+from gpu_common import TOL_BF16, TOL_F32, dev, np_f64, sync, to_dev
 from helpers import rel_l2
 from linear_attention_06_amd import gdn
 from linear_attention_06_amd.inputs import WORKLOADS, make_inputs
@@ -120,3 +120,39 @@ def test_narrow_bf16_heads_kept_forward_matches_the_plain_calls(case):
     for nm, x, y, z in zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), got, again, ref):
         assert torch.equal(x, z), "%s %s differs from gdn_chunk_bwd" % (name, nm)
         assert torch.equal(y, z), "%s %s differs on the second backward" % (name, nm)
+
+
+F32_CASES = [
+    # name, B, T, Hqk, H, dk, dv, valid_len (the first: the tiny fp32 workload's shape)
+    ("f32_d16_tiny", 1, 128, 4, 8, 16, 16, None),
+    ("f32_d64_dv32_padded_rows", 2, 300, 2, 4, 64, 32, 211),
+    ("f32_d32_dv128", 1, 200, 1, 2, 32, 128, None),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_narrow_f32_heads_run_padded_on_the_fp32_matrix_cores(case):
+    """fp32 heads under 128: gdn_chunk_fwd runs the fp32 matrix-core kernels on q and k
+    zero-padded to 128 columns; the fp32 bound against the oracle, and bit for bit the same
+    call made by hand on padded tensors."""
+    name, B, T, Hqk, H, dk, dv, vl = case
+    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="narrow_" + name, B=B, T=T, Hqk=Hqk, H=H, dk=dk,
+                            dv=dv, io="f32", h0="normal", seed=600 + dk + dv, valid_len=vl)
+    inp = make_inputs(w)
+    q, k, v, g, beta, h0, vl_t = to_dev(inp)
+    assert gdn.gdn_kernel_path(gdn.problem(q, v, vl_t)) == "f32-mfma-padded"
+    o, hT = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, valid_len=vl_t)
+    sync()
+    q64, k64, v64, g64, b64, h064 = inp.f64()
+    o_ref, hT_ref = oracle.gdn_fwd(q64, k64, v64, g64, b64, h064, valid_len=inp.valid_len)
+    for nm, x, r in (("o", o, o_ref), ("hT", hT, hT_ref)):
+        err = rel_l2(np_f64(x), r)
+        print("%s %s rel-L2 %.3e" % (name, nm, err))
+        assert err <= TOL_F32, "%s %s rel-L2 %.3e" % (name, nm, err)
+    pad = lambda x: torch.nn.functional.pad(x, (0, 128 - dk)).contiguous()
+    h0p = torch.nn.functional.pad(h0, (0, 0, 0, 128 - dk)).contiguous()
+    assert gdn.gdn_kernel_path(gdn.problem(pad(q), v, vl_t)) == "f32-mfma"
+    o2, hT2 = gdn.gdn_chunk_fwd(pad(q), pad(k), v, g, beta, h0p, valid_len=vl_t)
+    sync()
+    assert torch.equal(o, o2), "o differs from the hand-padded call"
+    assert torch.equal(hT, hT2[:, :, :dk]), "hT differs from the hand-padded call"

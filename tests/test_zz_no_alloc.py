@@ -35,11 +35,24 @@ def test_noalloc_equals_workspace_forward_twice_second_smaller():
                             seed=991, valid_len=517)
     (o2, hT2), (o2_ref, hT2_ref) = _run_both(make_inputs(w))
     assert torch.equal(o2, o2_ref) and torch.equal(hT2, hT2_ref)
-    # and the vector-ALU path (fp32 records in the same scratch)
-    w3 = dataclasses.replace(WORKLOADS["stateful_32k"], name="noalloc_f32", B=1, T=300, Hqk=2, H=4, dk=32, dv=32,
+    # and the fp32 path (fp32 records in the same scratch)
+    w3 = dataclasses.replace(WORKLOADS["stateful_32k"], name="noalloc_f32", B=1, T=300, Hqk=2, H=4, dk=128, dv=32,
                              io="f32", seed=992)
     (o3, hT3), (o3_ref, hT3_ref) = _run_both(make_inputs(w3))
     assert torch.equal(o3, o3_ref) and torch.equal(hT3, hT3_ref)
+
+
+def test_noalloc_narrow_heads_match_to_the_input_bound():
+    """Heads under 128 run on the vector-ALU kernels here and on padded copies in
+    gdn_chunk_fwd (no room for the copies in the scratch): equal to the bound of the input
+    type, fp32 and bf16."""
+    for io, tol in (("f32", 1e-4), ("bf16", 1e-2)):
+        w = dataclasses.replace(WORKLOADS["stateful_32k"], name="noalloc_narrow_" + io, B=1, T=300, Hqk=2, H=4,
+                                dk=32, dv=32, io=io, seed=993)
+        (o, hT), (o_ref, hT_ref) = _run_both(make_inputs(w))
+        for x, y in ((o, o_ref), (hT, hT_ref)):
+            x, y = x.float(), y.float()
+            assert float(torch.linalg.vector_norm(x - y) / torch.linalg.vector_norm(y)) <= tol
 
 
 def test_noalloc_rejects_problems_beyond_the_scratch():
