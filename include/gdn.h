@@ -29,7 +29,9 @@
  *     issue #320, section 4.1 describes, done as an index map instead of a copy.
  *   - Every pointer is device memory owned by the caller (except `p` and `bytes`,
  *     which are host pointers). The library allocates no memory and keeps no
- *     state between calls; calls are reentrant.
+ *     state between calls; calls are reentrant. The token tensors (q, k, v, o, d_o
+ *     and the gradients dq, dk, dv) are 16-byte aligned (the kernels move them in
+ *     16-byte pieces); a misaligned one is GDN_EINVAL.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
  *     the call returns after enqueueing. Results are visible after the caller
  *     synchronises that stream.

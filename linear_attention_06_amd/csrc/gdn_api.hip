@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -178,6 +179,13 @@ gdn_status run_state(const gdn_problem& p, const gdn::StateArgs& a, hipStream_t 
     return e == hipSuccess ? GDN_OK : hip_fail(e, "state kernel launch");
 }
 
+// The kernels read and write the token tensors with 16-byte accesses.
+bool aligned16(std::initializer_list<const void*> ptrs) {
+    for (const void* x : ptrs)
+        if (reinterpret_cast<uintptr_t>(x) % 16) return false;
+    return true;
+}
+
 gdn_status check_fwd_args(const gdn_problem* p, const void* q, const void* k, const void* v, const float* g,
                           const float* beta, const void* o) {
     gdn_status st = check_problem(p);
@@ -185,6 +193,7 @@ gdn_status check_fwd_args(const gdn_problem* p, const void* q, const void* k, co
     const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
     if (tokens && (!q || !k || !v || !g || !beta || !o))
         return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+    if (tokens && !aligned16({q, k, v, o})) return fail(GDN_EINVAL, "q, k, v and o must be 16-byte aligned");
     return GDN_OK;
 }
 
@@ -409,6 +418,8 @@ gdn_status gdn_chunk_fwd_prologue(const gdn_problem* p, const void* q_raw, const
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q_raw || !k_raw || !v || !a || !b || !A_log || !dt_bias || !o))
             return fail(GDN_EINVAL, "q_raw, k_raw, v, a, b, A_log, dt_bias and o must be non-NULL");
+        if (tokens && !aligned16({q_raw, k_raw, v, o}))
+            return fail(GDN_EINVAL, "q_raw, k_raw, v and o must be 16-byte aligned");
         const Plan pl = make_plan(*p, false);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
@@ -459,6 +470,7 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
         if (p->B > 0 && !cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens must be non-NULL");
         if (p->T > 0 && (!q || !k || !v || !g || !beta || !o))
             return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+        if (p->T > 0 && !aligned16({q, k, v, o})) return fail(GDN_EINVAL, "q, k, v and o must be 16-byte aligned");
         if (use_mfma_padded(*p)) {
             const gdn_problem w = padded_problem(*p);
             st = check_problem(&w);
@@ -851,6 +863,8 @@ gdn_status gdn_chunk_bwd(const gdn_problem* p, const void* q, const void* k, con
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (tokens && !aligned16({q, k, v, d_o, dq, dk, dv}))
+            return fail(GDN_EINVAL, "q, k, v, d_o, dq, dk and dv must be 16-byte aligned");
         if (use_bwd_mfma(*p)) {
             const BwdMfmaPlan pl = make_bwd_mfma_plan(*p);
             Plan need;
@@ -942,6 +956,8 @@ gdn_status gdn_chunk_bwd_saved(const gdn_problem* p, const void* q, const void* 
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (tokens && !aligned16({q, k, v, d_o, dq, dk, dv}))
+            return fail(GDN_EINVAL, "q, k, v, d_o, dq, dk and dv must be 16-byte aligned");
         if (use_bwd_mfma_padded(*p)) {
             const BwdPadPlan pp = make_bwd_pad_plan(*p);
             Plan need;
@@ -994,6 +1010,8 @@ gdn_status gdn_apply_initial_state_bwd(const gdn_problem* p, int32_t seg_len, co
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !H_in || !d_o || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, H_in, d_o, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (tokens && !aligned16({q, k, v, d_o, dq, dk, dv}))
+            return fail(GDN_EINVAL, "q, k, v, d_o, dq, dk and dv must be 16-byte aligned");
         if (use_seg_bwd_mfma(*p, P, seg_len)) {
             // every segment as a row of its own, from its incoming state, through the chunked
             // matrix-core backward; the final-state gradient enters the last segment of a row
@@ -1067,6 +1085,8 @@ gdn_status gdn_segment_summary_bwd(const gdn_problem* p, int32_t seg_len, const 
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !g || !beta || !dq || !dk || !dv || !dg || !dbeta))
             return fail(GDN_EINVAL, "q, k, v, g, beta, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (tokens && !aligned16({q, k, v, dq, dk, dv}))
+            return fail(GDN_EINVAL, "q, k, v, dq, dk and dv must be 16-byte aligned");
         if (use_seg_bwd_mfma(*p, P, seg_len)) {
             // every segment as a row of its own through the chunked matrix-core backward, the
             // chunk records prepared once: S from a zero state with values, M from the
@@ -1318,6 +1338,7 @@ gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !g || !beta || (S && !v)))
             return fail(GDN_EINVAL, "q, k, g, beta (and v when S is wanted) must be non-NULL");
+        if (tokens && !aligned16({q, k, v})) return fail(GDN_EINVAL, "q, k and v must be 16-byte aligned");
         const Plan pl = make_plan(*p, true);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;
@@ -1409,6 +1430,7 @@ gdn_status gdn_apply_initial_state(const gdn_problem* p, int32_t seg_len, const 
         const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
         if (tokens && (!q || !k || !v || !H_in || !o))
             return fail(GDN_EINVAL, "q, k, v, H_in and o must be non-NULL");
+        if (tokens && !aligned16({q, k, v, o})) return fail(GDN_EINVAL, "q, k, v and o must be 16-byte aligned");
         const Plan pl = make_plan(*p, true);
         st = check_ws(pl, ws, ws_bytes);
         if (st != GDN_OK) return st;

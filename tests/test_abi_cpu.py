@@ -81,7 +81,7 @@ def test_workspace_sizes():
     assert st == gdn.GDN_OK and n0 == 0
 
 
-def call_fwd(p, q=1, k=1, v=1, g=1, b=1, h0=None, o=1, hT=None, ws=None, nbytes=0):
+def call_fwd(p, q=16, k=16, v=16, g=16, b=16, h0=None, o=16, hT=None, ws=None, nbytes=0):
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return gdn.lib().gdn_chunk_fwd(ctypes.byref(p) if p is not None else None, vp(q), vp(k), vp(v),
                                    vp(g), vp(b), vp(h0), vp(o), vp(hT), vp(ws), nbytes, None)
@@ -97,9 +97,15 @@ def test_fwd_argument_checks_return_before_launch():
     assert call_fwd(p, ws=256, nbytes=need - 1) == gdn.GDN_EWORKSPACE
     assert call_fwd(p, ws=258, nbytes=need) == gdn.GDN_EWORKSPACE       # misaligned
     assert call_fwd(P(chunk=128), ws=256, nbytes=need) == gdn.GDN_EUNSUPPORTED
+    # token tensors must be 16-byte aligned (moved in 16-byte pieces); without tokens
+    # nothing is read
+    for name in ("q", "k", "v", "o"):
+        assert call_fwd(p, ws=256, nbytes=need, **{name: 24}) == gdn.GDN_EINVAL, name
+    assert "16-byte aligned" in gdn.lib().gdn_last_error().decode()
+    assert call_fwd(P(T=0), q=24, ws=256, nbytes=need) == gdn.GDN_OK
 
 
-def call_fwd_prologue(p, q=1, k=1, v=1, a=1, b=1, A_log=1, dt_bias=1, q_scale=0.125, o=1, ws=256,
+def call_fwd_prologue(p, q=16, k=16, v=16, a=16, b=16, A_log=16, dt_bias=16, q_scale=0.125, o=16, ws=256,
                       nbytes=1 << 40):
     vp = lambda x: None if x is None else ctypes.c_void_p(x)
     return gdn.lib().gdn_chunk_fwd_prologue(ctypes.byref(p), vp(q), vp(k), vp(v), vp(a), vp(b), vp(A_log),
@@ -133,22 +139,22 @@ def test_segment_argument_checks():
     p = P(valid_len=1234)                      # padded rows are allowed in the segment calls
     assert L.gdn_segment_workspace(ctypes.byref(p), 64, ctypes.byref(n)) == gdn.GDN_OK
     vp = ctypes.c_void_p
-    st = L.gdn_segment_summary(ctypes.byref(P()), 64, None, vp(1), vp(1), vp(1), vp(1), vp(1), vp(1),
+    st = L.gdn_segment_summary(ctypes.byref(P()), 64, None, vp(16), vp(16), vp(16), vp(16), vp(16), vp(16),
                                vp(256), 1 << 30, None)
     assert st == gdn.GDN_EINVAL
-    st = L.gdn_apply_initial_state(ctypes.byref(P()), 64, vp(1), vp(1), vp(1), vp(1), vp(1), None,
-                                   vp(1), None, vp(256), 1 << 30, None)
+    st = L.gdn_apply_initial_state(ctypes.byref(P()), 64, vp(16), vp(16), vp(16), vp(16), vp(16), None,
+                                   vp(16), None, vp(256), 1 << 30, None)
     assert st == gdn.GDN_EINVAL
 
 
 def test_combine_argument_checks():
     L = gdn.lib()
     vp = ctypes.c_void_p
-    assert L.gdn_summary_combine(1, 2, 3, 24, 16, vp(1), vp(1), None, vp(1), None, None, None) == \
+    assert L.gdn_summary_combine(1, 2, 3, 24, 16, vp(16), vp(16), None, vp(16), None, None, None) == \
         gdn.GDN_EUNSUPPORTED
-    assert L.gdn_summary_combine(1, 2, 3, 16, 16, None, vp(1), None, vp(1), None, None, None) == \
+    assert L.gdn_summary_combine(1, 2, 3, 16, 16, None, vp(16), None, vp(16), None, None, None) == \
         gdn.GDN_EINVAL
-    assert L.gdn_summary_combine(-1, 2, 3, 16, 16, vp(1), vp(1), None, vp(1), None, None, None) == \
+    assert L.gdn_summary_combine(-1, 2, 3, 16, 16, vp(16), vp(16), None, vp(16), None, None, None) == \
         gdn.GDN_EINVAL
     # nothing to do: no launch, OK
     assert L.gdn_summary_combine(0, 2, 3, 16, 16, None, None, None, None, None, None, None) == gdn.GDN_OK
@@ -184,8 +190,8 @@ def test_varlen_argument_checks():
     assert n.value >= 3 * 4 * 5 * (2 * 6 * 512 * 2 + 256 * 4)
     vp = ctypes.c_void_p
     call = lambda p, cu=1, mx=300, q=1: L.gdn_chunk_fwd_varlen(ctypes.byref(p), vp(cu) if cu else None, mx,
-                                                                vp(q) if q else None, vp(1), vp(1), vp(1), vp(1),
-                                                                None, vp(1), None, vp(256), 1 << 40, None)
+                                                                vp(q) if q else None, vp(16), vp(16), vp(16), vp(16),
+                                                                None, vp(16), None, vp(256), 1 << 40, None)
     assert call(bf, cu=None) == gdn.GDN_EINVAL
     assert call(bf, q=None) == gdn.GDN_EINVAL
     assert call(bf, mx=-5) == gdn.GDN_EINVAL
@@ -200,7 +206,7 @@ def test_backward_argument_checks():
     # checkpoints 8 B H ceil(T/64) dk dv and per-tile partials B T H (dv/16) 2 (dk + 1), fp32
     assert n.value >= 4 * (8 * 1 * 8 * 2 * 16 * 16 + 1 * 128 * 8 * 1 * 2 * (16 + 1))
     vp = ctypes.c_void_p
-    args = [vp(1)] * 5 + [None, vp(1), None] + [vp(1)] * 5 + [None]
+    args = [vp(16)] * 5 + [None, vp(16), None] + [vp(16)] * 5 + [None]
     bad = list(args)
     bad[8] = None                                   # dq
     assert L.gdn_chunk_bwd(ctypes.byref(p), *bad, vp(256), n.value, None) == gdn.GDN_EINVAL
@@ -220,14 +226,14 @@ def test_saved_forward_argument_checks():
     nb = ctypes.c_size_t(0)
     assert L.gdn_chunk_bwd_workspace(ctypes.byref(p), ctypes.byref(nb)) == gdn.GDN_OK
     assert n.value == nb.value
-    fwd = lambda q=vp(1), o=vp(1), ws=vp(256), nbytes=n.value, pp=p: L.gdn_chunk_fwd_save(
-        ctypes.byref(pp), q, vp(1), vp(1), vp(1), vp(1), None, o, None, ws, nbytes, None)
+    fwd = lambda q=vp(16), o=vp(16), ws=vp(256), nbytes=n.value, pp=p: L.gdn_chunk_fwd_save(
+        ctypes.byref(pp), q, vp(16), vp(16), vp(16), vp(16), None, o, None, ws, nbytes, None)
     assert fwd(q=None) == gdn.GDN_EINVAL
     assert fwd(o=None) == gdn.GDN_EINVAL
     assert fwd(nbytes=n.value - 1) == gdn.GDN_EWORKSPACE
     assert fwd(ws=vp(258)) == gdn.GDN_EWORKSPACE
     assert fwd(pp=P()) == gdn.GDN_EUNSUPPORTED
-    args = [vp(1)] * 6 + [None] + [vp(1)] * 5 + [None]
+    args = [vp(16)] * 6 + [None] + [vp(16)] * 5 + [None]
     bad = list(args)
     bad[7] = None                                   # dq
     assert L.gdn_chunk_bwd_saved(ctypes.byref(p), *bad, vp(256), n.value, None) == gdn.GDN_EINVAL
@@ -263,7 +269,7 @@ def test_layer_step_argument_checks():
     assert conv(x=264) == gdn.GDN_EINVAL               # not 16-byte aligned
     assert conv(T=0) == gdn.GDN_OK                      # nothing to do, nothing launched
     norm = lambda rows=10, D=128, io=gdn.GDN_BF16, eps=1e-6, o=256: L.gdn_gated_rmsnorm(
-        rows, D, io, vp(o) if o else None, vp(256), vp(1), ctypes.c_float(eps), vp(512), None)
+        rows, D, io, vp(o) if o else None, vp(256), vp(16), ctypes.c_float(eps), vp(512), None)
     assert norm(D=48) == gdn.GDN_EUNSUPPORTED
     assert norm(eps=float("nan")) == gdn.GDN_EINVAL
     assert norm(eps=-1.0) == gdn.GDN_EINVAL
@@ -319,5 +325,5 @@ def test_padded_narrow_head_workspaces_and_checks():
     assert L.gdn_chunk_bwd_workspace(ctypes.byref(short_f32), ctypes.byref(n)) == gdn.GDN_OK
     assert n_short == n.value
     vp = ctypes.c_void_p
-    args = [vp(1)] * 5 + [None, vp(1), None] + [vp(1)] * 5 + [None]
+    args = [vp(16)] * 5 + [None, vp(16), None] + [vp(16)] * 5 + [None]
     assert L.gdn_chunk_bwd(ctypes.byref(p), *args, vp(256), n_bwd - 1, None) == gdn.GDN_EWORKSPACE
