@@ -102,7 +102,7 @@ def test_fwd_argument_checks_return_before_launch():
     for name in ("q", "k", "v", "o"):
         assert call_fwd(p, ws=256, nbytes=need, **{name: 24}) == gdn.GDN_EINVAL, name
     assert "16-byte aligned" in gdn.lib().gdn_last_error().decode()
-    assert call_fwd(P(T=0), q=24, ws=256, nbytes=need) == gdn.GDN_OK
+    assert call_fwd(P(B=0), q=24, ws=256, nbytes=need) == gdn.GDN_OK
 
 
 def call_fwd_prologue(p, q=16, k=16, v=16, a=16, b=16, A_log=16, dt_bias=16, q_scale=0.125, o=16, ws=256,
