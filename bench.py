@@ -478,7 +478,7 @@ def other_workloads(gdn, workloads, make_inputs, dev, stream, timed):
     return out
 
 
-def vector_path_timing(gdn, workloads, make_inputs, dev, stream, timed):
+def other_paths_timing(gdn, workloads, make_inputs, dev, stream, timed):
     """gdn_chunk_fwd off the d = 128 bf16 shapes, on the stateless 8K workload's sizes: heads
     of 64 in bf16 (the matrix-core kernels on q and k padded to 128 columns) and fp32 inputs
     with heads of 128 (the fp32 matrix-core kernels); kernel_path names the path."""
@@ -666,7 +666,7 @@ def main():
         line["fused_prologue_32k"] = prologue_timing(gdn, inp, dev, stream, timed)
         line["backward_8k"] = backward_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
         line["layer_ops"] = layer_ops_timing(gdn, dev, stream, timed)
-        line["vector_path"] = vector_path_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
+        line["other_paths"] = other_paths_timing(gdn, WORKLOADS, make_inputs, dev, stream, timed)
     if not args.no_extra:
         line["measured_peaks"] = measured_peaks(dev, stream)
     if not args.no_cpu_baseline:

@@ -73,7 +73,7 @@ def test_stateless_8k_matches_oracle():
 
 
 @pytest.mark.parametrize("d,io", [(64, "bf16"), (128, "f32")], ids=["bf16_d64", "f32_d128"])
-def test_vector_path_full_size_matches_oracle(d, io):
+def test_other_paths_full_size_match_oracle(d, io):
     """The stateless 8K workload's shapes off the d = 128 bf16 path (heads of 64 in bf16, run
     by gdn_chunk_fwd on the matrix cores with q and k padded to 128 columns, and fp32 inputs on
     the fp32 matrix-core kernels): the sizes bench.py times for those paths."""
