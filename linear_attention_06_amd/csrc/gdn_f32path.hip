@@ -990,24 +990,26 @@ __global__ __launch_bounds__(512) void state_f32mfma(StateArgs a) {
 // records of prep_f32path: That = (I + A)^{-1} diag(beta) and P (64 x 64 fp32, row-major,
 // zero above the diagonal) and the decay factors.
 //   Gram products: the ten lower 16x16 tiles of K K^T and of Q K^T, five per wave, over the
-//   128 columns (K and Q in LDS, 16-byte granules XOR-swizzled by the row so that the
-//   fragment reads of 16 consecutive rows are conflict-free); A = beta_i e^{Gam_i - Gam_j}
+//   128 columns in two halves of 64 (K and Q halves in LDS, 16-byte granules XOR-swizzled by
+//   the row so that the fragment reads of 16 consecutive rows are conflict-free; the second
+//   half is loaded into registers during the first half's products, and the halves keep the
+//   LDS at 45 KiB, three blocks per CU); A = beta_i e^{Gam_i - Gam_j}
 //   (K K^T)_ij below the diagonal into LDS, P = e^{Gam_i - Gam_j} (Q K^T)_ij on and below it
 //   to memory.
 //   Solve: the four diagonal blocks D_b = (I + A_bb)^{-1} by column sweep on one wave (lane =
 //   (block, column)); the blocks below them T_ij = -D_i sum_{k=j}^{i-1} A_ik T_kj as three
 //   per-wave chains of 16x16x16 products (T10 T20 T30 / T21 T31 / T32), each result kept in
 //   accumulators and entering the next product as its B operand.
-__device__ __forceinline__ int kq_slot(int r, int c4) { return r * 128 + 4 * (c4 ^ (r & 15)); }
+__device__ __forceinline__ int kq_slot(int r, int c4) { return r * 64 + 4 * (c4 ^ (r & 15)); }
 
 __global__ __launch_bounds__(256) void prep_f32mfma(PrepArgs a) {
     constexpr int BP = 20;           // pitch of the 16x16 blocks in LDS (16-byte aligned rows)
     constexpr int BS = 16 * BP;      // floats per block
-    __shared__ __align__(16) float kq_s[2 * 64 * 128];   // K, Q; later the diagonal inverses
+    __shared__ __align__(16) float kq_s[2 * 64 * 64];    // a half of K and of Q; later the diagonal inverses
     __shared__ __align__(16) float a_s[10 * BS];          // the lower blocks of A, (i, j) at i (i + 1) / 2 + j
     __shared__ float gam_s[64], beta_s[64];
     float* k_s = kq_s;
-    float* q_s = kq_s + 64 * 128;
+    float* q_s = kq_s + 64 * 64;
     float* dr_s = kq_s;              // D_b row-major (after the Gram products)
     float* dc_s = kq_s + 4 * BS;     // D_b transposed
 
@@ -1031,17 +1033,31 @@ __global__ __launch_bounds__(256) void prep_f32mfma(PrepArgs a) {
     typedef float f32x4v __attribute__((ext_vector_type(4)));
     const f32x4v zero = {0.f, 0.f, 0.f, 0.f};
 
-    // K and Q rows (zero past the valid length), g and beta with the chunk-local cumulative sum
+    // K and Q rows (zero past the valid length) in two halves of 64 columns: float4 m of a
+    // half is row (tid + 256 m) / 16, columns 4 ((tid + 256 m) % 16) .. + 3 of the half
+    f32x4v kh[4], qh[4];
+    const auto load_half = [&](int half) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int e = tid + 256 * m, rr = e >> 5, c4 = e & 31;
-        const bool ok = t0 + rr < rs.valid;
-        const int64_t idx = ((rs.start + (ok ? t0 + rr : 0)) * a.Hqk + hq) * 128 + 4 * c4;
-        const f32x4v kv = *reinterpret_cast<const f32x4v*>(kin + idx);
-        const f32x4v qv = *reinterpret_cast<const f32x4v*>(qin + idx);
-        *reinterpret_cast<f32x4v*>(k_s + kq_slot(rr, c4)) = ok ? kv : zero;
-        *reinterpret_cast<f32x4v*>(q_s + kq_slot(rr, c4)) = ok ? qv : zero;
-    }
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, rr = e >> 4;
+            const bool ok = t0 + rr < rs.valid;
+            const int64_t idx = ((rs.start + (ok ? t0 + rr : 0)) * a.Hqk + hq) * 128 + 64 * half + 4 * (e & 15);
+            kh[m] = *reinterpret_cast<const f32x4v*>(kin + idx);
+            qh[m] = *reinterpret_cast<const f32x4v*>(qin + idx);
+        }
+    };
+    const auto store_half = [&]() {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = tid + 256 * m, rr = e >> 4, c4 = e & 15;
+            const bool ok = t0 + rr < rs.valid;
+            *reinterpret_cast<f32x4v*>(k_s + kq_slot(rr, c4)) = ok ? kh[m] : zero;
+            *reinterpret_cast<f32x4v*>(q_s + kq_slot(rr, c4)) = ok ? qh[m] : zero;
+        }
+    };
+    load_half(0);
+    store_half();
+    load_half(1);
     if (w == 0) {
         const bool ok = t0 + lane < rs.valid;
         const int64_t gi = (rs.start + (ok ? t0 + lane : 0)) * a.H + h;
@@ -1070,30 +1086,47 @@ __global__ __launch_bounds__(256) void prep_f32mfma(PrepArgs a) {
     }
     __syncthreads();
 
-    // ---- Gram products: tile item w + 4 v of [K K^T lower tiles, Q K^T lower tiles] ----
-#pragma unroll 1
+    // ---- Gram products: tile item w + 4 v of [K K^T lower tiles, Q K^T lower tiles], each
+    // over the two halves of the columns; even and odd k-tiles in separate chains ----
+    f32x4v acc2[5][2];
+#pragma unroll
+    for (int v = 0; v < 5; ++v) acc2[v][0] = acc2[v][1] = zero;
+    const auto gram_half = [&]() {
+#pragma unroll
+        for (int v = 0; v < 5; ++v) {
+            const int item = w + 4 * v;
+            const int li = item < 10 ? item : item - 10;
+            const int bi = li == 0 ? 0 : (li < 3 ? 1 : (li < 6 ? 2 : 3));
+            const int bj = li - bi * (bi + 1) / 2;
+            const float* left = item < 10 ? k_s : q_s;
+            const int ra = 16 * bi + l16, rb = 16 * bj + l16;
+            f32x4v fa[2], fb[2];
+            fa[0] = *reinterpret_cast<const f32x4v*>(left + kq_slot(ra, g4));
+            fb[0] = *reinterpret_cast<const f32x4v*>(k_s + kq_slot(rb, g4));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int i = t & 1;
+                if (t + 1 < 4) {
+                    fa[i ^ 1] = *reinterpret_cast<const f32x4v*>(left + kq_slot(ra, 4 * (t + 1) + g4));
+                    fb[i ^ 1] = *reinterpret_cast<const f32x4v*>(k_s + kq_slot(rb, 4 * (t + 1) + g4));
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) acc2[v][i] = mfma_f32_4(fa[i][s2], fb[i][s2], acc2[v][i]);
+            }
+        }
+    };
+    gram_half();
+    __syncthreads();   // every read of the first half is done
+    store_half();
+    __syncthreads();
+    gram_half();
+#pragma unroll
     for (int v = 0; v < 5; ++v) {
         const int item = w + 4 * v;
         const int li = item < 10 ? item : item - 10;
         const int bi = li == 0 ? 0 : (li < 3 ? 1 : (li < 6 ? 2 : 3));
         const int bj = li - bi * (bi + 1) / 2;
-        const float* left = item < 10 ? k_s : q_s;
-        const int ra = 16 * bi + l16, rb = 16 * bj + l16;
-        f32x4v acc2[2] = {zero, zero};
-        f32x4v fa[2], fb[2];
-        fa[0] = *reinterpret_cast<const f32x4v*>(left + kq_slot(ra, g4));
-        fb[0] = *reinterpret_cast<const f32x4v*>(k_s + kq_slot(rb, g4));
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int i = t & 1;
-            if (t + 1 < 8) {
-                fa[i ^ 1] = *reinterpret_cast<const f32x4v*>(left + kq_slot(ra, 4 * (t + 1) + g4));
-                fb[i ^ 1] = *reinterpret_cast<const f32x4v*>(k_s + kq_slot(rb, 4 * (t + 1) + g4));
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) acc2[i] = mfma_f32_4(fa[i][s2], fb[i][s2], acc2[i]);
-        }
-        const f32x4v acc = acc2[0] + acc2[1];
+        const f32x4v acc = acc2[v][0] + acc2[v][1];
         const int jc = 16 * bj + l16;
         const float gj = gam_s[jc];
 #pragma unroll
