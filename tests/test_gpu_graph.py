@@ -3,6 +3,8 @@ replayed: the library enqueues kernels only (no allocation, no memset, no host
 synchronisation), so a captured call must give, on every replay, exactly what the same call
 gives eagerly. Between replays the test writes new inputs into the captured tensors and runs
 the eager reference on them, with synchronisations in between."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -16,9 +18,10 @@ pytestmark = pytest.mark.gpu
 REPLAYS = 3
 
 
-def inputs(seed):
-    # bf16, heads of 128 (the matrix-core path), a ragged tail, an initial state
-    inp = make_inputs(WORKLOADS["stateful_32k"], T=1000, B=1)
+def inputs(seed, **kw):
+    # bf16, heads of 128 (the matrix-core path), a ragged tail, an initial state (kw: other
+    # dtypes and head dims)
+    inp = make_inputs(dataclasses.replace(WORKLOADS["stateful_32k"], **kw), T=1000, B=1)
     rng = np.random.default_rng(seed)
     q, k, v, g, beta, h0, _ = to_dev(inp)
     # fresh values per replay: permute tokens of the seeded inputs and scale the state
@@ -28,10 +31,12 @@ def inputs(seed):
         g[:, perm].contiguous(), beta[:, perm].contiguous(), (h0 * s).contiguous()
 
 
-def test_forward_graph_replays_match_eager_calls():
-    q, k, v, g, beta, h0 = inputs(0)
+@pytest.mark.parametrize("kw", [{}, {"io": "f32"}, {"io": "f32", "dk": 64, "dv": 64}],
+                         ids=["bf16_d128", "f32_d128", "f32_d64_padded"])
+def test_forward_graph_replays_match_eager_calls(kw):
+    q, k, v, g, beta, h0 = inputs(0, **kw)
     o = torch.empty_like(v)
-    hT = torch.empty((1, v.shape[2], 128, 128), dtype=torch.float32, device=dev())
+    hT = torch.empty(h0.shape, dtype=torch.float32, device=dev())
     ws = gdn.workspace(gdn.gdn_chunk_fwd_workspace(gdn.problem(q, v)), dev())
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -42,7 +47,7 @@ def test_forward_graph_replays_match_eager_calls():
     with torch.cuda.graph(graph):
         gdn.gdn_chunk_fwd(q, k, v, g, beta, h0, o=o, hT=hT, ws=ws)
     for r in range(REPLAYS):
-        new = inputs(10 + r)
+        new = inputs(10 + r, **kw)
         for dst, src in zip((q, k, v, g, beta, h0), new):
             dst.copy_(src)
         torch.cuda.synchronize()
