@@ -44,7 +44,7 @@ def test_padded_8k_nan_pads_give_the_same_bits():
     assert int(torch.count_nonzero(o2[:, n:].contiguous().view(torch.int16))) == 0
 
 
-@pytest.mark.parametrize("io,d", [("bf16", 128), ("bf16", 64), ("f32", 32)])
+@pytest.mark.parametrize("io,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 32)])
 def test_padded_rows_nan_pads_small(io, d):
     """Both kernel paths, rows with different valid lengths (one ending inside a chunk,
     one with none valid), NaN at every padded token."""
@@ -64,12 +64,12 @@ def test_padded_rows_nan_pads_small(io, d):
     assert torch.equal(o, o2) and torch.equal(hT, hT2)
 
 
-@pytest.mark.parametrize("T", [1000, 63, 4097])
-def test_ragged_tensor_end_followed_by_nan_memory(T):
+@pytest.mark.parametrize("T,io", [(1000, "bf16"), (63, "bf16"), (4097, "bf16"), (1000, "f32"), (63, "f32")])
+def test_ragged_tensor_end_followed_by_nan_memory(T, io):
     """A B = 1 problem whose T ends inside a chunk, passed as a view of the start of a
     longer buffer filled with NaN: the rows the last chunk covers past T must read as
     zero, not as the memory behind the tensor."""
-    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="ragged_view", B=1, T=T, Hqk=2, H=4, seed=902)
+    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="ragged_view", B=1, T=T, Hqk=2, H=4, seed=902, io=io)
     inp = make_inputs(w)
     q, k, v, g, beta, h0, _ = to_dev(inp)
     o, hT = gdn.gdn_chunk_fwd(q, k, v, g, beta, h0)
