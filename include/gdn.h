@@ -84,17 +84,17 @@ const char* gdn_last_error(void);
  * Kernel path a problem runs on (static string), or NULL for an invalid problem:
  *   "bf16-mfma"        -- bf16 I/O with dk == 128 (any dv of 16, 32, 64, 128): bf16
  *                         matrix-core contractions with fp32 accumulation and an fp32 state;
- *   "bf16-mfma-padded" -- bf16 I/O with dk < 128: gdn_chunk_fwd runs the dk == 128
- *                         matrix-core kernels on q and k zero-padded to 128 columns (exact:
- *                         the padded columns add zeros to every product); every other call
- *                         runs such a problem on the fp32 vector-ALU kernels;
+ *   "bf16-mfma-padded" -- bf16 I/O with dk < 128: gdn_chunk_fwd, gdn_chunk_fwd_varlen and
+ *                         the segment calls run the dk == 128 matrix-core kernels on q and k
+ *                         zero-padded to 128 columns (exact: the padded columns add zeros to
+ *                         every product); the allocation-free forward and the segment
+ *                         backward calls run such a problem on the fp32 vector-ALU kernels
+ *                         (gdn_chunk_bwd pads too, on rows of 256 tokens or more);
  *   "f32-mfma"         -- fp32 I/O with dk == 128: the forward calls' prepare and state
  *                         passes on fp32 matrix cores (v_mfma_f32_16x16x4_f32: fp32 products
  *                         and accumulation); the backward runs the fp32 token-level kernels;
- *   "f32-mfma-padded"  -- fp32 I/O with dk < 128: gdn_chunk_fwd and gdn_chunk_fwd_varlen
- *                         run the fp32 matrix-core kernels on q and k zero-padded to 128
- *                         columns; every other call runs such a problem on the fp32
- *                         vector-ALU kernels.
+ *   "f32-mfma-padded"  -- fp32 I/O with dk < 128: likewise on the fp32 matrix-core kernels
+ *                         (the backward calls run the fp32 token-level kernels).
  */
 const char* gdn_kernel_path(const gdn_problem* p);
 
@@ -321,7 +321,11 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t D, int32_t io_dtype, const vo
 /*
  * Workspace for the segment calls (gdn_segment_summary, then
  * gdn_apply_initial_state on the same workspace). seg_len must be a positive
- * multiple of 64 that divides T; P = T / seg_len segments.
+ * multiple of 64 that divides T; P = T / seg_len segments. Heads with dk < 128 run the
+ * segment calls as the dk = 128 problem on q and k zero-padded to 128 columns (a padded
+ * segment's transition is block-diagonal, so M's first dk rows and columns and S's first
+ * dk rows are exact; H_in enters with zero rows below dk and hT is cut back); the
+ * workspace then also holds the padded q and k and 128-row staging blocks.
  */
 gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes);
 

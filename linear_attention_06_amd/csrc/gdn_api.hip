@@ -1315,6 +1315,39 @@ gdn_status gdn_chunk_fwd_conv(const gdn_problem* p, const void* x, const float* 
     }
 }
 
+// The segment calls on heads with dk < 128 run the dk = 128 problem on q and k zero-padded to
+// 128 columns, as the padded forward does. A padded segment's transition is block-diagonal
+// (the padded state rows only decay and stay apart from the rest), so the first dk rows and
+// columns of its M and the first dk rows of its S are the unpadded problem's; H_in enters
+// with zero rows below dk, and the final state is cut back. The workspace holds the padded
+// problem's segment records (shared by the summary and apply calls, as the plain segment
+// workspace is), the padded q and k, and staging for the 128-row M, S / H_in and hT blocks.
+struct SegPadPlan {
+    Plan rec;
+    size_t q_off = 0, k_off = 0, m_off = 0, s_off = 0, h_off = 0, bytes = 0;
+};
+SegPadPlan make_seg_pad_plan(const gdn_problem& p, int64_t P) {
+    SegPadPlan sp;
+    sp.rec = make_plan(padded_problem(p), true);
+    const size_t qk = align256(static_cast<size_t>(p.B) * p.T * p.Hqk * 128 * io_bytes(p));
+    const size_t blocks = static_cast<size_t>(p.B) * p.H * static_cast<size_t>(P);
+    sp.q_off = align256(sp.rec.bytes);
+    sp.k_off = sp.q_off + qk;
+    sp.m_off = sp.k_off + qk;
+    sp.s_off = sp.m_off + align256(blocks * 128 * 128 * 4);
+    sp.h_off = sp.s_off + align256(blocks * 128 * p.dv * 4);
+    sp.bytes = sp.h_off + align256(static_cast<size_t>(p.B) * p.H * 128 * p.dv * 4);
+    return sp;
+}
+// q and k into their padded copies in the workspace
+hipError_t pad_qk(const gdn_problem& p, const SegPadPlan& sp, const void* q, const void* k, void* ws,
+                  hipStream_t s) {
+    char* base = static_cast<char*>(ws);
+    const int64_t rows = static_cast<int64_t>(p.B) * p.T * p.Hqk, es = io_bytes(p);
+    hipError_t e = gdn::launch_copy_rows(q, p.dk * es, base + sp.q_off, 128 * es, rows, s);
+    return e == hipSuccess ? gdn::launch_copy_rows(k, p.dk * es, base + sp.k_off, 128 * es, rows, s) : e;
+}
+
 gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* bytes) {
     gdn_status st = check_problem(p);
     if (st != GDN_OK) return st;
@@ -1322,28 +1355,24 @@ gdn_status gdn_segment_workspace(const gdn_problem* p, int32_t seg_len, size_t* 
     st = check_segments(*p, seg_len, &P);
     if (st != GDN_OK) return st;
     if (!bytes) return fail(GDN_EINVAL, "bytes pointer is NULL");
+    if (use_mfma_padded(*p)) {
+        const gdn_problem w = padded_problem(*p);
+        st = check_problem(&w);
+        if (st != GDN_OK) return st;
+        *bytes = make_seg_pad_plan(*p, P).bytes;
+        return GDN_OK;
+    }
     *bytes = make_plan(*p, true).bytes;
     return GDN_OK;
 }
 
-gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void* q, const void* k,
-                               const void* v, const float* g, const float* beta, float* M, float* S,
-                               void* ws, size_t ws_bytes, void* stream) {
-    try {
-        gdn_status st = check_problem(p);
-        if (st != GDN_OK) return st;
-        int64_t P = 0;
-        st = check_segments(*p, seg_len, &P);
-        if (st != GDN_OK) return st;
-        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
-        if (tokens && (!q || !k || !g || !beta || (S && !v)))
-            return fail(GDN_EINVAL, "q, k, g, beta (and v when S is wanted) must be non-NULL");
-        if (tokens && !aligned16({q, k, v})) return fail(GDN_EINVAL, "q, k and v must be 16-byte aligned");
-        const Plan pl = make_plan(*p, true);
-        st = check_ws(pl, ws, ws_bytes);
-        if (st != GDN_OK) return st;
-        if (!tokens) return GDN_OK;
-        hipStream_t s = static_cast<hipStream_t>(stream);
+// The segment summaries of a checked problem with a workspace of at least pl.bytes.
+gdn_status run_summary(const gdn_problem& pr, const Plan& pl, int64_t P, int32_t seg_len, const void* q,
+                       const void* k, const void* v, const float* g, const float* beta, float* M, float* S,
+                       void* ws, hipStream_t s) {
+    {
+        const gdn_problem* p = &pr;
+        gdn_status st;
         const gdn::Workspace w = carve(pl, ws);
         st = run_prep(*p, pl, q, k, g, beta, w, s);
         if (st != GDN_OK) return st;
@@ -1377,10 +1406,55 @@ gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void
             if (st != GDN_OK) return st;
         }
         return GDN_OK;
+    }
+}
+
+gdn_status gdn_segment_summary(const gdn_problem* p, int32_t seg_len, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta, float* M, float* S,
+                               void* ws, size_t ws_bytes, void* stream) {
+    try {
+        gdn_status st = check_problem(p);
+        if (st != GDN_OK) return st;
+        int64_t P = 0;
+        st = check_segments(*p, seg_len, &P);
+        if (st != GDN_OK) return st;
+        const bool tokens = static_cast<int64_t>(p->B) * p->T > 0;
+        if (tokens && (!q || !k || !g || !beta || (S && !v)))
+            return fail(GDN_EINVAL, "q, k, g, beta (and v when S is wanted) must be non-NULL");
+        if (tokens && !aligned16({q, k, v})) return fail(GDN_EINVAL, "q, k and v must be 16-byte aligned");
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (use_mfma_padded(*p)) {
+            const gdn_problem wp = padded_problem(*p);
+            st = check_problem(&wp);
+            if (st != GDN_OK) return st;
+            const SegPadPlan sp = make_seg_pad_plan(*p, P);
+            Plan need;
+            need.bytes = sp.bytes;
+            st = check_ws(need, ws, ws_bytes);
+            if (st != GDN_OK) return st;
+            if (!tokens) return GDN_OK;
+            hipError_t e = pad_qk(*p, sp, q, k, ws, s);
+            if (e != hipSuccess) return hip_fail(e, "padding copy launch");
+            char* base = static_cast<char*>(ws);
+            float* m_pad = M ? reinterpret_cast<float*>(base + sp.m_off) : nullptr;
+            float* s_pad = S ? reinterpret_cast<float*>(base + sp.s_off) : nullptr;
+            st = run_summary(wp, sp.rec, P, seg_len, base + sp.q_off, base + sp.k_off, v, g, beta, m_pad, s_pad, ws, s);
+            if (st != GDN_OK) return st;
+            const int64_t blocks = static_cast<int64_t>(p->B) * p->H * P;
+            if (M) e = gdn::launch_copy_blocks(m_pad, 128, 512, M, p->dk, p->dk * 4, blocks, s);
+            if (e == hipSuccess && S) e = gdn::launch_copy_blocks(s_pad, 128, p->dv * 4, S, p->dk, p->dv * 4, blocks, s);
+            return e == hipSuccess ? GDN_OK : hip_fail(e, "summary copy launch");
+        }
+        const Plan pl = make_plan(*p, true);
+        st = check_ws(pl, ws, ws_bytes);
+        if (st != GDN_OK) return st;
+        if (!tokens) return GDN_OK;
+        return run_summary(*p, pl, P, seg_len, q, k, v, g, beta, M, S, ws, s);
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }
 }
+
 
 gdn_status gdn_summary_combine(int32_t B, int32_t H, int32_t P, int32_t dk, int32_t dv, const float* M,
                                const float* S, const float* h0, float* H_in, float* M_prefix, float* hT,
@@ -1431,22 +1505,53 @@ gdn_status gdn_apply_initial_state(const gdn_problem* p, int32_t seg_len, const 
         if (tokens && (!q || !k || !v || !H_in || !o))
             return fail(GDN_EINVAL, "q, k, v, H_in and o must be non-NULL");
         if (tokens && !aligned16({q, k, v, o})) return fail(GDN_EINVAL, "q, k, v and o must be 16-byte aligned");
-        const Plan pl = make_plan(*p, true);
-        st = check_ws(pl, ws, ws_bytes);
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const bool padded = use_mfma_padded(*p);
+        const gdn_problem wp = padded ? padded_problem(*p) : *p;
+        if (padded) {
+            st = check_problem(&wp);
+            if (st != GDN_OK) return st;
+        }
+        const SegPadPlan sp = padded ? make_seg_pad_plan(*p, P) : SegPadPlan{};
+        const Plan pl = padded ? sp.rec : make_plan(*p, true);
+        Plan need;
+        need.bytes = padded ? sp.bytes : pl.bytes;
+        st = check_ws(need, ws, ws_bytes);
         if (st != GDN_OK) return st;
         if (!tokens) return GDN_OK;
-        hipStream_t s = static_cast<hipStream_t>(stream);
+        char* base = static_cast<char*>(ws);
+        const void* qw = q;
+        const void* kw = k;
+        const float* h_in = H_in;
+        float* h_out = hT;
+        if (padded) {
+            // the padded q, k (again: this call may not follow the summary on the same
+            // stream) and H_in with zero rows below dk
+            hipError_t e = pad_qk(*p, sp, q, k, ws, s);
+            if (e == hipSuccess)
+                e = gdn::launch_copy_blocks(H_in, p->dk, p->dv * 4, base + sp.s_off, 128, p->dv * 4,
+                                            static_cast<int64_t>(p->B) * p->H * P, s);
+            if (e != hipSuccess) return hip_fail(e, "padding copy launch");
+            qw = base + sp.q_off;
+            kw = base + sp.k_off;
+            h_in = reinterpret_cast<const float*>(base + sp.s_off);
+            h_out = hT ? reinterpret_cast<float*>(base + sp.h_off) : nullptr;
+        }
         const gdn::Workspace w = carve(pl, ws);
-        gdn::StateArgs a = state_args(*p, pl, q, k, v, w);
+        gdn::StateArgs a = state_args(wp, pl, qw, kw, v, w);
         a.P = static_cast<int>(P);
         a.Lc = seg_len / gdn::kChunk;
         a.init_mode = gdn::kInitLoad;
-        a.s_init = H_in;
+        a.s_init = h_in;
         a.s_init_per_segment = 1;
         a.o = o;
-        a.s_out = hT;
-        a.store_mode = hT ? gdn::kStoreLastSegment : gdn::kStoreNone;
-        return run_state(*p, a, s);
+        a.s_out = h_out;
+        a.store_mode = h_out ? gdn::kStoreLastSegment : gdn::kStoreNone;
+        st = run_state(wp, a, s);
+        if (st != GDN_OK || !padded || !hT) return st;
+        const hipError_t e = gdn::launch_copy_blocks(h_out, 128, p->dv * 4, hT, p->dk, p->dv * 4,
+                                                     static_cast<int64_t>(p->B) * p->H, s);
+        return e == hipSuccess ? GDN_OK : hip_fail(e, "final state copy launch");
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }

@@ -156,3 +156,34 @@ def test_narrow_f32_heads_run_padded_on_the_fp32_matrix_cores(case):
     sync()
     assert torch.equal(o, o2), "o differs from the hand-padded call"
     assert torch.equal(hT, hT2[:, :, :dk]), "hT differs from the hand-padded call"
+
+
+@pytest.mark.parametrize("io,dk,dv", [("bf16", 64, 64), ("bf16", 32, 16), ("f32", 16, 32)])
+def test_narrow_heads_segment_calls_run_padded(io, dk, dv):
+    """The segment calls on heads under 128 run the dk = 128 problem on padded q and k: M's
+    first dk rows and columns, S's first dk rows, and apply's o and final state are bit for
+    bit those of the same calls made by hand on padded tensors (H_in padded with zero rows),
+    and the composed path matches the oracle's unsplit forward."""
+    seg = 128
+    w = dataclasses.replace(WORKLOADS["stateful_32k"], name="narrow_seg", B=2, T=3 * seg, Hqk=2, H=4, dk=dk,
+                            dv=dv, io=io, h0="normal", seed=700 + dk + dv, valid_len=300)
+    inp = make_inputs(w)
+    q, k, v, g, beta, h0, vl = to_dev(inp)
+    M, S, ws = gdn.gdn_segment_summary(q, k, v, g, beta, seg, valid_len=vl)
+    H_in, _, _ = gdn.gdn_summary_combine(M, S, h0)
+    o, hT = gdn.gdn_apply_initial_state(q, k, v, g, beta, H_in, seg, ws, valid_len=vl)
+    pad = lambda x: torch.nn.functional.pad(x, (0, 128 - dk)).contiguous()
+    rows = lambda x: torch.nn.functional.pad(x, (0, 0, 0, 128 - dk)).contiguous()
+    M2, S2, ws2 = gdn.gdn_segment_summary(pad(q), pad(k), v, g, beta, seg, valid_len=vl)
+    o2, hT2 = gdn.gdn_apply_initial_state(pad(q), pad(k), v, g, beta, rows(H_in), seg, ws2, valid_len=vl)
+    sync()
+    assert torch.equal(M, M2[..., :dk, :dk]), "M differs from the hand-padded call"
+    assert torch.equal(S, S2[..., :dk, :]), "S differs from the hand-padded call"
+    assert torch.equal(o, o2), "o differs from the hand-padded call"
+    assert torch.equal(hT, hT2[:, :, :dk]), "hT differs from the hand-padded call"
+    q64, k64, v64, g64, b64, h064 = inp.f64()
+    o_ref, hT_ref = oracle.gdn_fwd(q64, k64, v64, g64, b64, h064, valid_len=inp.valid_len)
+    tol = TOL_BF16 if io == "bf16" else TOL_F32
+    for nm, x, r in (("o", o, o_ref), ("hT", hT, hT_ref)):
+        err = rel_l2(np_f64(x), r)
+        assert err <= tol, "%s %s rel-L2 %.3e" % (io, nm, err)
