@@ -308,6 +308,16 @@ def test_padded_narrow_head_workspaces_and_checks():
     assert n_pad >= n128 + 2 * B * T * Hqk * 128 * 2 + 2 * B * H * 128 * dv * 4
     assert call_fwd(p, ws=256, nbytes=n_pad - 1) == gdn.GDN_EWORKSPACE
     assert call_fwd(p, q=None, ws=256, nbytes=n_pad) == gdn.GDN_EINVAL
+    # the segment calls pad too: the dk = 128 problem's segment records, padded q and k,
+    # and 128-row staging for M (128 x 128), S / H_in and hT
+    nseg, nseg128 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.gdn_segment_workspace(ctypes.byref(p), 64, ctypes.byref(nseg)) == gdn.GDN_EINVAL  # 64 does not divide 300
+    ps = P(B=B, T=256, H=H, Hqk=Hqk, dk=dk, dv=dv, io_dtype=gdn.GDN_BF16)
+    ps128 = P(B=B, T=256, H=H, Hqk=Hqk, dk=128, dv=dv, io_dtype=gdn.GDN_BF16)
+    assert L.gdn_segment_workspace(ctypes.byref(ps), 64, ctypes.byref(nseg)) == gdn.GDN_OK
+    assert L.gdn_segment_workspace(ctypes.byref(ps128), 64, ctypes.byref(nseg128)) == gdn.GDN_OK
+    blocks = B * H * 4
+    assert nseg.value >= nseg128.value + 2 * B * 256 * Hqk * 128 * 2 + blocks * 128 * (128 + dv) * 4
     # the fp32 problem of the same shape pads too, onto the fp32 dk = 128 records
     n_f32 = ws_status(P(B=B, T=T, H=H, Hqk=Hqk, dk=dk, dv=dv))[1]
     n_f32_128 = ws_status(P(B=B, T=T, H=H, Hqk=Hqk, dk=128, dv=dv))[1]
