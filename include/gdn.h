@@ -87,7 +87,7 @@ const char* gdn_last_error(void);
  *   "bf16-mfma-padded" -- bf16 I/O with dk < 128: gdn_chunk_fwd, gdn_chunk_fwd_varlen and
  *                         the segment calls run the dk == 128 matrix-core kernels on q and k
  *                         zero-padded to 128 columns (exact: the padded columns add zeros to
- *                         every product); the allocation-free forward and the segment
+ *                         every product), the allocation-free forward included; the segment
  *                         backward calls run such a problem on the fp32 vector-ALU kernels
  *                         (gdn_chunk_bwd pads too, on rows of 256 tokens or more);
  *   "f32-mfma"         -- fp32 I/O with dk == 128: the forward calls' prepare and state
@@ -132,10 +132,8 @@ gdn_status gdn_chunk_fwd(const gdn_problem* p,
  * shares that GPU's array: calls that overlap on one GPU (different streams, or host
  * threads without ordering) race and give undefined results; calls on one stream are
  * ordered. Nothing in the array has to start at zero (each call writes every record it
- * reads). Heads with dk < 128 run here on the fp32 vector-ALU kernels (gdn_chunk_fwd
- * runs them on the matrix cores through padded copies of q and k, which this call has no
- * room for), so for them the two calls agree to the bound of the input type (bf16 or
- * fp32), not bit for bit.
+ * reads). Heads with dk < 128 run, as in gdn_chunk_fwd, on padded copies of q and k, which
+ * share the array with the records (so the limit counts them too).
  */
 gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p,
                                  const void* q, const void* k, const void* v,

@@ -388,16 +388,27 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_problem* p, const void* q, const void
     try {
         gdn_status st = check_fwd_args(p, q, k, v, g, beta, o);
         if (st != GDN_OK) return st;
-        const Plan pl = make_plan(*p, false);
-        if (pl.bytes > kScratchBytes)
+        // heads under 128: the padded q, k and state blocks share the array with the records
+        const bool padded = use_mfma_padded(*p);
+        if (padded) {
+            const gdn_problem w = padded_problem(*p);
+            st = check_problem(&w);
+            if (st != GDN_OK) return st;
+        }
+        const PadPlan pp = padded ? make_pad_plan(*p) : PadPlan{};
+        const Plan pl = padded ? pp.rec : make_plan(*p, false);
+        const size_t need = padded ? pp.bytes : pl.bytes;
+        if (need > kScratchBytes)
             return fail(GDN_EWORKSPACE,
                         "the problem needs %zu bytes of chunk records; the static scratch holds %zu "
-                        "(use gdn_chunk_fwd with a workspace)", pl.bytes, kScratchBytes);
+                        "(use gdn_chunk_fwd with a workspace)", need, kScratchBytes);
         if (p->B == 0) return GDN_OK;
         void* ws = nullptr;
         st = scratch_on_current_device(&ws);
         if (st != GDN_OK) return st;
-        return run_fwd(*p, pl, q, k, v, g, beta, h0, o, hT, ws, static_cast<hipStream_t>(stream));
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if (padded) return run_fwd_padded(*p, pp, nullptr, q, k, v, g, beta, h0, o, hT, ws, s);
+        return run_fwd(*p, pl, q, k, v, g, beta, h0, o, hT, ws, s);
     } catch (...) {
         return fail(GDN_EHIP, "unexpected exception");
     }
