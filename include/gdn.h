@@ -239,7 +239,8 @@ gdn_status gdn_chunk_fwd_varlen(const gdn_problem* p, const int32_t* cu_seqlens,
  *   summed over the value heads that read each query/key head)
  *   dh0 [B, H, dk, dv] fp32 when non-NULL (the gradient of h0; h0 NULL = zero state).
  * Padded tokens (valid_len) get zero gradients. Every head dim and dtype of the forward.
- * bf16 inputs with dk = dv = 128 run the chunked matrix-core backward (the transposes of the
+ * bf16 inputs with dk = dv = 128 on rows of 64 tokens or more (T >= 64, or T = 0) run the
+ * chunked matrix-core backward (the transposes of the
  * chunk form's products on bf16 MFMAs with fp32 accumulation, relative error a few 1e-3,
  * within the bf16 bound issue #320 section 4.2 states for gradients): workspace per
  * (b, h, 64-token chunk) of 105 KiB (the prepare pass's records, the state entering the chunk

@@ -555,8 +555,13 @@ gdn_status check_bwd_ws(const BwdPlan& pl, void* ws, size_t ws_bytes) {
 // P, decay factors; That^T and P^T; Tinv and P row-major), then the state entering every
 // chunk and the gradient of the state leaving it (bf16, transposed).
 // The gradient pass reads one batch row of the fp32 dv output with 32-bit byte offsets.
+// Rows shorter than one chunk keep the fp32 token-level backward: a few tokens' gradients can
+// cancel to a small fraction of their terms, where the bf16-rounded operands of the chunked
+// backward leave a large relative error (a one-token row: 3.5e-2 on dk), and such rows cost
+// little there. Without tokens there is nothing to compute either way.
+constexpr int32_t kMfmaBwdMinT = gdn::kChunk;
 bool use_bwd_mfma(const gdn_problem& p) {
-    return use_mfma(p) && p.dv == 128 &&
+    return use_mfma(p) && p.dv == 128 && (p.T == 0 || p.T >= kMfmaBwdMinT) &&
            static_cast<int64_t>(p.T + gdn::kChunk) * p.H * p.dv * 4 < (int64_t(1) << 31);
 }
 

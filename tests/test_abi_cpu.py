@@ -239,6 +239,11 @@ def test_saved_forward_argument_checks():
     assert L.gdn_chunk_bwd_saved(ctypes.byref(p), *bad, vp(256), n.value, None) == gdn.GDN_EINVAL
     assert L.gdn_chunk_bwd_saved(ctypes.byref(p), *args, vp(256), n.value - 1, None) == gdn.GDN_EWORKSPACE
     assert L.gdn_chunk_bwd_saved(ctypes.byref(P()), *args, vp(256), 1 << 40, None) == gdn.GDN_EUNSUPPORTED
+    # heads of 128: the chunked backward (and so the kept forward) on rows of a chunk or more
+    for T, ok in ((0, True), (63, False), (64, True)):
+        p128 = P(B=1, T=T, H=4, Hqk=2, dk=128, dv=128, io_dtype=gdn.GDN_BF16)
+        st = L.gdn_chunk_fwd_save_workspace(ctypes.byref(p128), ctypes.byref(n))
+        assert st == (gdn.GDN_OK if ok else gdn.GDN_EUNSUPPORTED), T
     # narrow bf16 heads: kept through the padded problem on rows of 256 tokens or more, with
     # gdn_chunk_bwd's workspace; shorter rows keep the token-level backward and nothing
     for T, ok in ((256, True), (1000, True), (255, False)):
